@@ -1,0 +1,278 @@
+"""CPU oracle of block-scaled quantization and the block-scaled GEMM (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``oracle.c`` (plain C, built
+with gcc) through ctypes and works on numpy arrays; it shares nothing with the
+HIP library.  See ``oracle.c`` for the definitions and their sources.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+
+ROW, COL = 1, 2
+RNE, SR = 0, 1
+FMT_NVFP4, FMT_MXFP8 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into _build/liboracle.so with gcc (OpenMP, strict IEEE binary32)."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = build(force=False)
+        L = C.CDLL(path)
+        u8p = C.POINTER(C.c_uint8)
+        u16p = C.POINTER(C.c_uint16)
+        f32p = C.POINTER(C.c_float)
+        f64p = C.POINTER(C.c_double)
+        i8p = C.POINTER(C.c_int8)
+        i64p = C.POINTER(C.c_int64)
+        u32p = C.POINTER(C.c_uint32)
+        L.or_bf16_to_f32.argtypes = [C.c_uint16]; L.or_bf16_to_f32.restype = C.c_float
+        L.or_f32_to_bf16_rne.argtypes = [C.c_float]; L.or_f32_to_bf16_rne.restype = C.c_uint16
+        L.or_e2m1_decode.argtypes = [C.c_uint8]; L.or_e2m1_decode.restype = C.c_float
+        L.or_e2m1_encode_rne.argtypes = [C.c_float]; L.or_e2m1_encode_rne.restype = C.c_uint8
+        L.or_e2m1_encode_sr.argtypes = [C.c_float, C.c_uint32]; L.or_e2m1_encode_sr.restype = C.c_uint8
+        L.or_e4m3_decode.argtypes = [C.c_uint8]; L.or_e4m3_decode.restype = C.c_float
+        L.or_e4m3_encode_rne_sat.argtypes = [C.c_float]; L.or_e4m3_encode_rne_sat.restype = C.c_uint8
+        L.or_e8m0_decode.argtypes = [C.c_uint8]; L.or_e8m0_decode.restype = C.c_float
+        L.or_philox4x32_10.argtypes = [u32p, u32p, u32p]; L.or_philox4x32_10.restype = None
+        L.or_sr_word.argtypes = [C.c_uint64, C.c_uint32, C.c_uint32, C.c_uint64]
+        L.or_sr_word.restype = C.c_uint32
+        L.or_rht16.argtypes = [f32p, i8p, f32p]; L.or_rht16.restype = None
+        L.or_nvfp4_tensor_scale.argtypes = [C.c_float]; L.or_nvfp4_tensor_scale.restype = C.c_float
+        L.or_nvfp4_block_scale.argtypes = [C.c_float, C.c_float]; L.or_nvfp4_block_scale.restype = C.c_uint8
+        L.or_mxfp8_scale_byte.argtypes = [C.c_float]; L.or_mxfp8_scale_byte.restype = C.c_uint8
+        L.or_nvfp4_quantize.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_uint64,
+                                        C.c_uint32, i8p, u8p, u8p, u8p, u8p, f32p, f32p]
+        L.or_nvfp4_quantize.restype = C.c_int
+        L.or_nvfp4_dequantize.argtypes = [u8p, u8p, C.c_float, C.c_int64, C.c_int64, u16p]
+        L.or_nvfp4_dequantize.restype = None
+        L.or_mxfp8_quantize.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int, u8p, u8p, u8p, u8p]
+        L.or_mxfp8_quantize.restype = C.c_int
+        L.or_rht_apply.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int, i8p, f32p]
+        L.or_rht_apply.restype = C.c_int
+        L.or_blockscaled_gemm.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64,
+                                          u8p, u8p, C.c_float, u8p, u8p, C.c_float,
+                                          i64p, C.c_int64, i64p, C.c_int64, f64p]
+        L.or_blockscaled_gemm.restype = C.c_int
+        L.or_num_threads.argtypes = []; L.or_num_threads.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ctype):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+def _bits(x) -> np.ndarray:
+    """bf16 input as a contiguous uint16 numpy array (accepts a torch bf16 tensor or uint16 array)."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch  # only for accepting torch CPU tensors
+    assert x.dtype == torch.bfloat16
+    return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _signs(signs):
+    if signs is None:
+        return None
+    s = np.ascontiguousarray(np.asarray(signs, dtype=np.int8).reshape(16))
+    assert np.all(np.abs(s.astype(np.int32)) == 1), "sign vector entries must be +-1"
+    return s
+
+
+def num_threads() -> int:
+    return lib().or_num_threads()
+
+
+# ---------------------------------------------------------------- scalar codecs
+
+def e2m1_decode(code: int) -> float:
+    return lib().or_e2m1_decode(code)
+
+
+def e2m1_encode_rne(v: float) -> int:
+    return lib().or_e2m1_encode_rne(v)
+
+
+def e2m1_encode_sr(v: float, u: int) -> int:
+    return lib().or_e2m1_encode_sr(v, u)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().or_e4m3_decode(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().or_e4m3_encode_rne_sat(v)
+
+
+def e8m0_decode(b: int) -> float:
+    return lib().or_e8m0_decode(b)
+
+
+def philox4x32_10(counter, key):
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint32).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+    out = np.zeros(4, dtype=np.uint32)
+    lib().or_philox4x32_10(_p(c, C.c_uint32), _p(k, C.c_uint32), _p(out, C.c_uint32))
+    return out
+
+
+def sr_word(seed: int, stream: int, direction: int, i: int) -> int:
+    return lib().or_sr_word(seed & (2**64 - 1), stream, direction, i)
+
+
+def rht16(x, signs) -> np.ndarray:
+    xi = np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(16))
+    out = np.zeros(16, dtype=np.float32)
+    lib().or_rht16(_p(xi, C.c_float), _p(_signs(signs), C.c_int8), _p(out, C.c_float))
+    return out
+
+
+def nvfp4_tensor_scale(amax: float) -> float:
+    return lib().or_nvfp4_tensor_scale(amax)
+
+
+def nvfp4_block_scale(block_amax: float, s_enc: float) -> int:
+    return lib().or_nvfp4_block_scale(block_amax, s_enc)
+
+
+def mxfp8_scale_byte(block_amax: float) -> int:
+    return lib().or_mxfp8_scale_byte(block_amax)
+
+
+def f32_to_bf16_rne(v: float) -> int:
+    return lib().or_f32_to_bf16_rne(v)
+
+
+# ---------------------------------------------------------------- tensor ops
+
+def nvfp4_quantize(x, direction: int = ROW, rounding: int = RNE, sr_seed: int = 0,
+                   sr_stream: int = 0, signs=None) -> dict:
+    """NVFP4 quantization of bf16 x[R][C].  Returns a dict with the requested
+    directions' codes/scales and amax[2], s_enc[2] ([0] rowwise, [1] columnwise)."""
+    xb = _bits(x)
+    R, Cc = xb.shape
+    out = {}
+    rc = rs = cc = cs = None
+    if direction & ROW:
+        rc = np.zeros((R, Cc // 2), np.uint8); rs = np.zeros((R, Cc // 16), np.uint8)
+    if direction & COL:
+        cc = np.zeros((Cc, R // 2), np.uint8); cs = np.zeros((Cc, R // 16), np.uint8)
+    amax = np.zeros(2, np.float32)
+    s_enc = np.zeros(2, np.float32)
+    sg = _signs(signs)
+    u8 = C.c_uint8
+    nullu8 = C.POINTER(C.c_uint8)()
+    st = lib().or_nvfp4_quantize(
+        _p(xb, C.c_uint16), R, Cc, direction, rounding, sr_seed & (2**64 - 1), sr_stream,
+        _p(sg, C.c_int8) if sg is not None else C.POINTER(C.c_int8)(),
+        _p(rc, u8) if rc is not None else nullu8, _p(rs, u8) if rs is not None else nullu8,
+        _p(cc, u8) if cc is not None else nullu8, _p(cs, u8) if cs is not None else nullu8,
+        _p(amax, C.c_float), _p(s_enc, C.c_float))
+    if st != 0:
+        raise ValueError("oracle nvfp4_quantize failed with status %d" % st)
+    if rc is not None:
+        out["row_codes"], out["row_scales"] = rc, rs
+    if cc is not None:
+        out["col_codes"], out["col_scales"] = cc, cs
+    out["amax"], out["s_enc"] = amax, s_enc
+    return out
+
+
+def nvfp4_dequantize(codes: np.ndarray, scales: np.ndarray, s_enc: float) -> np.ndarray:
+    """bf16 bits [rows][cols] of the dequantized NVFP4 tensor."""
+    rows, half = codes.shape
+    cols = half * 2
+    out = np.zeros((rows, cols), np.uint16)
+    lib().or_nvfp4_dequantize(_p(np.ascontiguousarray(codes), C.c_uint8),
+                              _p(np.ascontiguousarray(scales), C.c_uint8), float(s_enc),
+                              rows, cols, _p(out, C.c_uint16))
+    return out
+
+
+def mxfp8_quantize(x, direction: int = ROW) -> dict:
+    xb = _bits(x)
+    R, Cc = xb.shape
+    rc = rs = cc = cs = None
+    if direction & ROW:
+        rc = np.zeros((R, Cc), np.uint8); rs = np.zeros((R, Cc // 32), np.uint8)
+    if direction & COL:
+        cc = np.zeros((Cc, R), np.uint8); cs = np.zeros((Cc, R // 32), np.uint8)
+    u8 = C.c_uint8
+    nullu8 = C.POINTER(C.c_uint8)()
+    st = lib().or_mxfp8_quantize(
+        _p(xb, C.c_uint16), R, Cc, direction,
+        _p(rc, u8) if rc is not None else nullu8, _p(rs, u8) if rs is not None else nullu8,
+        _p(cc, u8) if cc is not None else nullu8, _p(cs, u8) if cs is not None else nullu8)
+    if st != 0:
+        raise ValueError("oracle mxfp8_quantize failed with status %d" % st)
+    out = {}
+    if rc is not None:
+        out["row_codes"], out["row_scales"] = rc, rs
+    if cc is not None:
+        out["col_codes"], out["col_scales"] = cc, cs
+    return out
+
+
+def rht_apply(x, axis: int, signs) -> np.ndarray:
+    xb = _bits(x)
+    R, Cc = xb.shape
+    out = np.zeros((R, Cc), np.float32)
+    st = lib().or_rht_apply(_p(xb, C.c_uint16), R, Cc, axis, _p(_signs(signs), C.c_int8),
+                            _p(out, C.c_float))
+    if st != 0:
+        raise ValueError("oracle rht_apply failed with status %d" % st)
+    return out
+
+
+def blockscaled_gemm(fmt: int, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc,
+                     rows=None, cols=None) -> np.ndarray:
+    """binary64 C = A B^T of the dequantized operands (optionally only rows x cols of C)."""
+    M = a_codes.shape[0]
+    N = b_codes.shape[0]
+    K = a_codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
+    mi = np.ascontiguousarray(np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, np.int64))
+    ni = np.ascontiguousarray(np.arange(N, dtype=np.int64) if cols is None else np.asarray(cols, np.int64))
+    out = np.zeros((mi.size, ni.size), np.float64)
+    u8 = C.c_uint8
+    st = lib().or_blockscaled_gemm(
+        fmt, M, N, K,
+        _p(np.ascontiguousarray(a_codes), u8), _p(np.ascontiguousarray(a_scales), u8), float(a_s_enc),
+        _p(np.ascontiguousarray(b_codes), u8), _p(np.ascontiguousarray(b_scales), u8), float(b_s_enc),
+        _p(mi, C.c_int64), mi.size, _p(ni, C.c_int64), ni.size, _p(out, C.c_double))
+    if st != 0:
+        raise ValueError("oracle blockscaled_gemm failed with status %d" % st)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(force=True), file=sys.stderr)
