@@ -1,0 +1,195 @@
+"""Benchmark: one training step of a block-scaled quantized linear layer at the Llama-3-8B
+FFN up-projection shape (tokens M = 16384, out features N = 14336, in features K = 4096)
+on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic bf16 inputs already
+resident in HBM:
+  fwd    NVFP4 rowwise (RNE) of X[16384,4096] and W[14336,4096]; Y = X W^T (bf16)
+  wgrad  16-point RHT + Philox SR, NVFP4 columnwise of dY[16384,14336] and X;
+         dW = dY^T X (fp32)
+  dgrad  per-direction (hybrid) recipe: MXFP8 rowwise of dY, MXFP8 columnwise of
+         bf16(dequant(NVFP4 rowwise W)); dX = dY W (bf16)
+value = the step's GEMM FLOPs (3 x 2MNK) / step time, in TFLOP/s.  The line also carries
+the NVFP4 quantize GB/s and the NVFP4 GEMM TFLOP/s of the forward pass, the roofline of
+the dominant kernel (the NVFP4 GEMM) timed with HIP events on its own stream, and the CPU
+oracle timed on a token-sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+M_TOK, N_OUT, K_IN = 16384, 14336, 4096
+HBM_PEAK_GBPS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+
+# algorithmic bytes per element of one NVFP4 quantization direction: 2 B bf16 read,
+# 0.5 B codes + 1/16 B scale written.
+NVFP4_BYTES_PER_ELT = 2.0 + 0.5 + 1.0 / 16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    return p.parse_args()
+
+
+class Step:
+    """Buffers and launches of one step; every kernel runs on torch's current stream."""
+
+    def __init__(self, dev):
+        import torch
+        import block_scaled_precision_nvfp4_amd as bsq
+        from synthetic import (SEED_DY, SEED_SIGNS, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16, rht_signs)
+        self.bsq, self.torch = bsq, torch
+        self.X = gaussian_bf16((M_TOK, K_IN), 1.0, SEED_X).to(dev)
+        self.W = gaussian_bf16((N_OUT, K_IN), STD_W, SEED_W).to(dev)
+        self.dY = gaussian_bf16((M_TOK, N_OUT), STD_DY, SEED_DY).to(dev)
+        self.signs = rht_signs(SEED_SIGNS).to(dev)
+        self.seed = 42
+        self.dev = dev
+        self.ev = {}
+
+    def _ev(self, name):
+        torch = self.torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.ev.setdefault(name, []).append(e)
+
+    def run(self, timed=False):
+        bsq, torch = self.bsq, self.torch
+        mark = self._ev if timed else (lambda name: None)
+        # fwd
+        mark("q_fwd0")
+        qx = bsq.nvfp4_quantize(self.X, direction=bsq.ROW)
+        qw = bsq.nvfp4_quantize(self.W, direction=bsq.ROW)
+        mark("q_fwd1")
+        mark("g_fwd0")
+        y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qx["row_codes"], qx["row_scales"], qx["s_enc"][0:1],
+                                 qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], out_dtype=torch.bfloat16)
+        mark("g_fwd1")
+        # wgrad
+        qdy = bsq.nvfp4_quantize(self.dY, direction=bsq.COL, rounding=bsq.SR, sr_seed=self.seed, sr_stream=0,
+                                 rht_signs=self.signs)
+        qxc = bsq.nvfp4_quantize(self.X, direction=bsq.COL, rounding=bsq.SR, sr_seed=self.seed, sr_stream=1,
+                                 rht_signs=self.signs)
+        mark("g_wgrad0")
+        dw = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qdy["col_codes"], qdy["col_scales"], qdy["s_enc"][1:2],
+                                  qxc["col_codes"], qxc["col_scales"], qxc["s_enc"][1:2], out_dtype=torch.float32)
+        mark("g_wgrad1")
+        # dgrad (MXFP8 backward operands; W from its rowwise-dequantized NVFP4 value)
+        mdy = bsq.mxfp8_quantize(self.dY, direction=bsq.ROW)
+        wdq = bsq.nvfp4_dequantize(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1])
+        mw = bsq.mxfp8_quantize(wdq, direction=bsq.COL)
+        mark("g_dgrad0")
+        dx = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["row_codes"], mdy["row_scales"], None,
+                                  mw["col_codes"], mw["col_scales"], None, out_dtype=torch.bfloat16)
+        mark("g_dgrad1")
+        return y, dw, dx
+
+    def avg_ms(self, name):
+        a, b = self.ev[name + "0"], self.ev[name + "1"]
+        return sum(x.elapsed_time(y) for x, y in zip(a, b)) / len(a)
+
+
+def cpu_baseline(tokens: int):
+    """The oracle on a token-sample of the step: the same operations with M = tokens."""
+    import numpy as np
+    import oracle
+    from synthetic import (SEED_DY, SEED_SIGNS, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16, rht_signs)
+    X = gaussian_bf16((tokens, K_IN), 1.0, SEED_X)
+    W = gaussian_bf16((N_OUT, K_IN), STD_W, SEED_W)
+    dY = gaussian_bf16((tokens, N_OUT), STD_DY, SEED_DY)
+    d = rht_signs(SEED_SIGNS).numpy()
+    t0 = time.perf_counter()
+    qx = oracle.nvfp4_quantize(X, direction=oracle.ROW)
+    qw = oracle.nvfp4_quantize(W, direction=oracle.ROW)
+    oracle.blockscaled_gemm(oracle.FMT_NVFP4, qx["row_codes"], qx["row_scales"], qx["s_enc"][0],
+                            qw["row_codes"], qw["row_scales"], qw["s_enc"][0])
+    qdy = oracle.nvfp4_quantize(dY, direction=oracle.COL, rounding=oracle.SR, sr_seed=42, sr_stream=0, signs=d)
+    qxc = oracle.nvfp4_quantize(X, direction=oracle.COL, rounding=oracle.SR, sr_seed=42, sr_stream=1, signs=d)
+    oracle.blockscaled_gemm(oracle.FMT_NVFP4, qdy["col_codes"], qdy["col_scales"], qdy["s_enc"][1],
+                            qxc["col_codes"], qxc["col_scales"], qxc["s_enc"][1])
+    mdy = oracle.mxfp8_quantize(dY, direction=oracle.ROW)
+    wdq = oracle.nvfp4_dequantize(qw["row_codes"], qw["row_scales"], float(qw["s_enc"][0]))
+    mw = oracle.mxfp8_quantize(wdq, direction=oracle.COL)
+    oracle.blockscaled_gemm(oracle.FMT_MXFP8, mdy["row_codes"], mdy["row_scales"], 1.0,
+                            mw["col_codes"], mw["col_scales"], 1.0)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * tokens * N_OUT * K_IN
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "the full step with %d of %d tokens (M = %d); %.1f s on the host" % (tokens, M_TOK, tokens, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import block_scaled_precision_nvfp4_amd as bsq
+    bsq.lib()
+    dev = torch.device("cuda:0")
+    step = Step(dev)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(args.steps):
+        step.run(timed=True)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    gemm_flops = 2.0 * M_TOK * N_OUT * K_IN
+    value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
+
+    g_fwd = step.avg_ms("g_fwd")
+    g_wgrad = step.avg_ms("g_wgrad")
+    g_dgrad = step.avg_ms("g_dgrad")
+    q_fwd = step.avg_ms("q_fwd")
+    q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
+    fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fwd_tflops / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_nvfp4 (fwd, f16 MFMA with in-register dequant)"}
+    line = {
+        "metric": "NVFP4 quant GB/s + block-scaled GEMM TFLOP/s at Llama-3-8B FFN shape",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4/mxfp8 operands, f16/fp8 MFMA, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "quantized linear fwd+wgrad+dgrad step, Llama-3-8B FFN up-proj",
+                   "tokens": M_TOK, "in_features": K_IN, "out_features": N_OUT,
+                   "fwd": "NVFP4 row RNE", "wgrad": "NVFP4 col RHT16+SR", "dgrad": "MXFP8 (W from rowwise-dequantized)"},
+        "nvfp4_quant_GBps": round(q_bytes / (q_fwd * 1e-3) / 1e9, 1),
+        "nvfp4_gemm_TFLOPs": round(fwd_tflops, 2),
+        "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "gemm_fwd_nvfp4": round(g_fwd, 4),
+                      "gemm_wgrad_nvfp4": round(g_wgrad, 4), "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
+        "mxfp8_gemm_TFLOPs": round(gemm_flops / (g_dgrad * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+"""Python binding of libbsq: block-scaled (NVFP4 / MXFP8) quantization and GEMM on MI355X.
+
+Thin ctypes marshalling over the C ABI in include/bsq.h: every step of the computation
+runs in the library's HIP kernels.  PyTorch only provides device memory (output
+tensors are allocated with torch.empty) and the current HIP stream.  The functions
+have the names of the C entry points.  Importing works without a GPU; calling a
+compute function needs libbsq.so (built by ``python -m
+block_scaled_precision_nvfp4_amd.build``) and fails loudly if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+import torch
+
+ROW, COL = 1, 2
+RNE, SR = 0, 1
+FMT_NVFP4, FMT_MXFP8 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsq.so")
+
+_ERRORS = {1: "null pointer", 2: "shape", 3: "argument", 4: "unsupported", 5: "HIP", 6: "alignment"}
+
+
+class BsqError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed (%s error %d): %s" % (fn, _ERRORS.get(status, "?"), status, msg))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libbsq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libbsq.so not found at %s; build it with "
+                               "`python -m block_scaled_precision_nvfp4_amd.build`" % LIB_PATH)
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32, u32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64
+        L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+        L.mxfp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
+        L.rht_apply.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.blockscaled_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+        for f in ("nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "rht_apply", "blockscaled_gemm",
+                  "bsq_version"):
+            getattr(L, f).restype = C.c_int
+        L.bsq_last_error.argtypes = []
+        L.bsq_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise BsqError(fn, status, lib().bsq_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev_tensor(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA/HIP tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _signs(rht_signs, device):
+    if rht_signs is None:
+        return None
+    s = rht_signs
+    if not isinstance(s, torch.Tensor):
+        s = torch.tensor(s, dtype=torch.int8)
+    s = s.to(device=device, dtype=torch.int8).contiguous()
+    if s.numel() != 16:
+        raise ValueError("rht_signs must have 16 entries")
+    return s
+
+
+def nvfp4_quantize(x: torch.Tensor, direction: int = ROW, rounding: int = RNE, sr_seed: int = 0,
+                   sr_stream: int = 0, rht_signs=None) -> Dict[str, torch.Tensor]:
+    """NVFP4-quantize a bf16 [rows, cols] device tensor.  Returns the requested directions'
+    ``{row,col}_codes`` / ``{row,col}_scales`` (uint8) and ``amax`` / ``s_enc`` (float32[2],
+    index 0 rowwise, 1 columnwise), all on x's device."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    R, Cc = x.shape
+    dev = x.device
+    out: Dict[str, torch.Tensor] = {}
+    u8 = dict(dtype=torch.uint8, device=dev)
+    if direction & ROW:
+        out["row_codes"] = torch.empty((R, Cc // 2), **u8)
+        out["row_scales"] = torch.empty((R, Cc // 16), **u8)
+    if direction & COL:
+        out["col_codes"] = torch.empty((Cc, R // 2), **u8)
+        out["col_scales"] = torch.empty((Cc, R // 16), **u8)
+    out["amax"] = torch.empty(2, dtype=torch.float32, device=dev)
+    out["s_enc"] = torch.empty(2, dtype=torch.float32, device=dev)
+    sg = _signs(rht_signs, dev)
+    _check("nvfp4_quantize", lib().nvfp4_quantize(
+        x.data_ptr(), R, Cc, direction, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg),
+        _ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
+        _ptr(out.get("col_scales")), out["amax"].data_ptr(), out["s_enc"].data_ptr(), _stream(dev)))
+    return out
+
+
+def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, s_enc: torch.Tensor) -> torch.Tensor:
+    """bf16 [rows, cols] value of NVFP4 codes [rows, cols/2] with scales [rows, cols/16] and
+    tensor scale ``s_enc`` (a 1-element float32 device tensor)."""
+    _dev_tensor(codes, torch.uint8, "codes")
+    _dev_tensor(scales, torch.uint8, "scales")
+    _dev_tensor(s_enc, torch.float32, "s_enc")
+    rows, half = codes.shape
+    out = torch.empty((rows, half * 2), dtype=torch.bfloat16, device=codes.device)
+    _check("nvfp4_dequantize", lib().nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), s_enc.data_ptr(),
+                                                      rows, half * 2, out.data_ptr(), _stream(codes.device)))
+    return out
+
+
+def mxfp8_quantize(x: torch.Tensor, direction: int = ROW) -> Dict[str, torch.Tensor]:
+    """MXFP8-cast a bf16 [rows, cols] device tensor (E4M3 codes, E8M0 scale per 32)."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    R, Cc = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out: Dict[str, torch.Tensor] = {}
+    if direction & ROW:
+        out["row_codes"] = torch.empty((R, Cc), **u8)
+        out["row_scales"] = torch.empty((R, Cc // 32), **u8)
+    if direction & COL:
+        out["col_codes"] = torch.empty((Cc, R), **u8)
+        out["col_scales"] = torch.empty((Cc, R // 32), **u8)
+    _check("mxfp8_quantize", lib().mxfp8_quantize(
+        x.data_ptr(), R, Cc, direction, _ptr(out.get("row_codes")), _ptr(out.get("row_scales")),
+        _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _stream(dev)))
+    return out
+
+
+def rht_apply(x: torch.Tensor, axis: int, rht_signs) -> torch.Tensor:
+    """float32 16-point random Hadamard transform of a bf16 tensor along ``axis``."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    R, Cc = x.shape
+    sg = _signs(rht_signs, x.device)
+    out = torch.empty((R, Cc), dtype=torch.float32, device=x.device)
+    _check("rht_apply", lib().rht_apply(x.data_ptr(), R, Cc, axis, sg.data_ptr(), out.data_ptr(),
+                                        _stream(x.device)))
+    return out
+
+
+def blockscaled_gemm(fmt: int, a_codes: torch.Tensor, a_scales: torch.Tensor, a_s_enc: Optional[torch.Tensor],
+                     b_codes: torch.Tensor, b_scales: torch.Tensor, b_s_enc: Optional[torch.Tensor],
+                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[M, N] = A[M, K] B[N, K]^T on NVFP4 (fmt 0) or MXFP8 (fmt 1) operands, fp32 accumulate."""
+    _dev_tensor(a_codes, torch.uint8, "a_codes")
+    _dev_tensor(b_codes, torch.uint8, "b_codes")
+    _dev_tensor(a_scales, torch.uint8, "a_scales")
+    _dev_tensor(b_scales, torch.uint8, "b_scales")
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    K = a_codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
+    if b_codes.shape[1] != a_codes.shape[1]:
+        raise ValueError("operands disagree on K")
+    c_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    else:
+        _dev_tensor(out, out_dtype, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (M, N)))
+    _check("blockscaled_gemm", lib().blockscaled_gemm(
+        fmt, M, N, K, a_codes.data_ptr(), a_scales.data_ptr(), _ptr(a_s_enc), b_codes.data_ptr(),
+        b_scales.data_ptr(), _ptr(b_s_enc), out.data_ptr(), c_dtype, _stream(a_codes.device)))
+    return out

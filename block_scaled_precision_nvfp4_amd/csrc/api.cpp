@@ -1,0 +1,133 @@
+// api.cpp -- the C ABI of libbsq (declared in include/bsq.h): argument validation on the
+// host, then one launcher call.  Validation runs before any HIP call, so a rejected call
+// never touches the device and works on a machine without a GPU.
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/bsq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return BSQ_OK;
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int launched(int hip_code, const char* what) {
+    if (hip_code != 0)
+        return fail(BSQ_ERR_HIP, "%s: kernel launch failed: %s", what, bsq::hip_error_string(hip_code));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsq_version(void) { return 100; }
+
+const char* bsq_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding, uint64_t sr_seed,
+                   uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
+                   uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out,
+                   void* hip_stream) {
+    static const char* fn = "nvfp4_quantize";
+    if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
+    if (rounding != BSQ_RNE && rounding != BSQ_SR) return fail(BSQ_ERR_ARG, "%s: rounding must be 0 (RNE) or 1 (SR), got %d", fn, rounding);
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape [%lld, %lld]", fn, (long long)rows, (long long)cols);
+    if (cols % 8 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
+    if ((direction & BSQ_ROW) && cols % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: rowwise needs cols %% 16 == 0, got %lld", fn, (long long)cols);
+    if ((direction & BSQ_COL) && rows % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: columnwise needs rows %% 16 == 0, got %lld", fn, (long long)rows);
+    if (!amax_out || !s_enc_out) return fail(BSQ_ERR_NULL, "%s: amax_out and s_enc_out are required", fn);
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty && !x) return fail(BSQ_ERR_NULL, "%s: x is NULL", fn);
+    if ((direction & BSQ_ROW) && !empty && (!row_codes || !row_scales)) return fail(BSQ_ERR_NULL, "%s: rowwise outputs are NULL", fn);
+    if ((direction & BSQ_COL) && !empty && (!col_codes || !col_scales)) return fail(BSQ_ERR_NULL, "%s: columnwise outputs are NULL", fn);
+    if (misaligned(x) || misaligned(row_codes) || misaligned(col_codes) || misaligned(rht_signs))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_nvfp4_quantize(x, rows, cols, direction, rounding, sr_seed, sr_stream, rht_signs,
+                                               row_codes, row_scales, col_codes, col_scales, amax_out, s_enc_out,
+                                               hip_stream), fn);
+}
+
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows, int64_t cols,
+                     void* out, void* hip_stream) {
+    static const char* fn = "nvfp4_dequantize";
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (cols % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 16", fn, (long long)cols);
+    if (rows * cols == 0) return ok();
+    if (!codes || !scales || !s_enc || !out) return fail(BSQ_ERR_NULL, "%s: NULL argument", fn);
+    if (misaligned(codes) || misaligned(out)) return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_nvfp4_dequantize(codes, scales, s_enc, rows, cols, out, hip_stream), fn);
+}
+
+int mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int direction, uint8_t* row_codes,
+                   uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
+    static const char* fn = "mxfp8_quantize";
+    if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (cols % 8 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
+    if ((direction & BSQ_ROW) && cols % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: rowwise needs cols %% 32 == 0, got %lld", fn, (long long)cols);
+    if ((direction & BSQ_COL) && rows % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: columnwise needs rows %% 32 == 0, got %lld", fn, (long long)rows);
+    if (rows == 0 || cols == 0) return ok();
+    if (!x) return fail(BSQ_ERR_NULL, "%s: x is NULL", fn);
+    if ((direction & BSQ_ROW) && (!row_codes || !row_scales)) return fail(BSQ_ERR_NULL, "%s: rowwise outputs are NULL", fn);
+    if ((direction & BSQ_COL) && (!col_codes || !col_scales)) return fail(BSQ_ERR_NULL, "%s: columnwise outputs are NULL", fn);
+    if (misaligned(x) || misaligned(row_codes) || misaligned(col_codes))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_mxfp8_quantize(x, rows, cols, direction, row_codes, row_scales, col_codes,
+                                               col_scales, hip_stream), fn);
+}
+
+int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t* signs, float* out,
+              void* hip_stream) {
+    static const char* fn = "rht_apply";
+    if (axis != 0 && axis != 1) return fail(BSQ_ERR_ARG, "%s: axis must be 0 or 1, got %d", fn, axis);
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (cols % 8 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
+    if (axis == 1 && cols % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: axis 1 needs cols %% 16 == 0", fn);
+    if (axis == 0 && rows % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: axis 0 needs rows %% 16 == 0", fn);
+    if (!signs) return fail(BSQ_ERR_NULL, "%s: signs is NULL", fn);
+    if (rows == 0 || cols == 0) return ok();
+    if (!x || !out) return fail(BSQ_ERR_NULL, "%s: NULL argument", fn);
+    if (misaligned(x) || misaligned(out) || misaligned(signs)) return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_rht_apply(x, rows, cols, axis, signs, out, hip_stream), fn);
+}
+
+int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                     const float* a_s_enc, const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
+                     void* c, int c_dtype, void* hip_stream) {
+    static const char* fn = "blockscaled_gemm";
+    if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), got %d", fn, fmt);
+    if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
+    if (M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    if (!c) return fail(BSQ_ERR_NULL, "%s: c is NULL", fn);
+    if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return fail(BSQ_ERR_NULL, "%s: operand pointer is NULL", fn);
+    if (fmt == BSQ_FMT_NVFP4 && (!a_s_enc || !b_s_enc)) return fail(BSQ_ERR_NULL, "%s: NVFP4 needs both tensor scales", fn);
+    if (misaligned(a_codes) || misaligned(b_codes) || misaligned(c)) return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_blockscaled_gemm(fmt, M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales,
+                                                 b_s_enc, c, c_dtype, hip_stream), fn);
+}
+
+}  // extern "C"

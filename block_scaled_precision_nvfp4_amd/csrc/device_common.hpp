@@ -1,0 +1,201 @@
+// device_common.hpp -- gfx950 device helpers shared by the quantization and GEMM kernels:
+// bf16 widening, E4M3 / E2M1 encoders, Philox4x32-10, the 16-point Hadamard butterfly.
+//
+// Every floating-point step is a single binary32 operation in round-to-nearest-even
+// (the library is built with -ffp-contract=off and correctly rounded division), so the
+// results are bit-identical to any implementation performing the same operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace bsq {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).  Used where a loop
+// body indexes a register array and must see constant indices even when it is too large
+// for the unroller's heuristics.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the data is read once).
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    const u32v4 v = __builtin_nontemporal_load((const u32v4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight bf16 values packed in a uint4 -> eight floats (exact).
+__device__ __forceinline__ void unpack_bf16x8(const uint4 q, float v[8]) {
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+    v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+}
+
+// binary32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------- E4M3 (OCP "fn")
+// Non-negative t -> E4M3 code, nearest-even, saturating at 448 (code 0x7E).
+// Subnormal range [0, 2^-6): code = rint(t * 2^9) (0..8; 8 is the first normal).
+// Normal range: round the binary32 mantissa to 3 bits (ties to even) and rebias the
+// exponent from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float t) {
+    if (!(t < 448.0f)) return 0x7Eu;
+    if (t < 0x1p-6f) return (uint32_t)__builtin_rintf(t * 512.0f);
+    uint32_t u = __float_as_uint(t);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    return (u >> 20) - (120u << 3);
+}
+
+// Signed value -> E4M3 code (sign bit copied, including -0).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    return e4m3_encode_nonneg(__builtin_fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+// Non-negative E4M3 code (<= 0x7E) -> float.
+__device__ __forceinline__ float e4m3_decode_nonneg(uint32_t c) {
+    if (c < 8u) return (float)c * 0x1p-9f;
+    return __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
+}
+
+// ---------------------------------------------------------------- E2M1
+// Round-to-nearest-even onto {0, .5, 1, 1.5, 2, 3, 4, 6} with saturation: the code is
+// the number of decision boundaries below |v|; a boundary that is a tie rounds toward
+// the even code, hence '>' where the lower neighbour has an even code and '>=' where
+// it is odd.
+__device__ __forceinline__ uint32_t e2m1_encode_rne(float v) {
+    float a = __builtin_fabsf(v);
+    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Stochastic rounding onto the E2M1 grid: lo = largest grid value <= |v| (|v| < 6),
+// p = (|v| - lo) / (hi - lo) exactly (the spacing is a power of two), round up iff
+// (u >> 8) * 2^-24 < p.  |v| >= 6 saturates.
+__device__ __forceinline__ uint32_t e2m1_encode_sr(float v, uint32_t u) {
+    float a = __builtin_fabsf(v);
+    uint32_t s = (__float_as_uint(v) >> 28) & 8u;
+    if (a >= 6.0f) return 7u | s;
+    uint32_t lo = (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) +
+                  (uint32_t)(a >= 2.0f) + (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f);
+    // grid value of lo and the inverse spacing to the next grid value
+    float lov = lo <= 4u ? 0.5f * (float)lo : (lo == 5u ? 3.0f : 4.0f);
+    float inv = lo <= 3u ? 2.0f : (lo <= 5u ? 1.0f : 0.5f);
+    float p = (a - lov) * inv;
+    float r = (float)(u >> 8) * 0x1p-24f;
+    return (lo + (uint32_t)(r < p)) | s;
+}
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon et al., "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
+        uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+        u32x4 n;
+        n.x = hi1 ^ c.y ^ k0;
+        n.y = lo1;
+        n.z = hi0 ^ c.w ^ k1;
+        n.w = lo0;
+        c = n;
+        k0 += W0;
+        k1 += W1;
+    }
+    return c;
+}
+
+// The four SR words of output elements 4q .. 4q+3 of direction dir.
+__device__ __forceinline__ u32x4 sr_words(uint64_t q, uint64_t seed, uint32_t stream, uint32_t dir) {
+    u32x4 c{(uint32_t)q, (uint32_t)(q >> 32), stream, dir};
+    return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t word_of(const u32x4& w, int i) {
+    return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
+}
+
+// ---------------------------------------------------------------- Hadamard
+// In-place y = v diag(d) H16 / 4 on 16 registers: sign flip, butterfly strides 1, 2, 4,
+// 8 with (a, b) -> (a + b, a - b), then the exact scaling by 1/4.  d is a bitmask:
+// bit i set means d_i = -1.
+__device__ __forceinline__ void rht16(float v[16], uint32_t negmask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = ((negmask >> i) & 1u) ? -v[i] : v[i];
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * h) {
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+                float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
+}
+
+// Half of a 16-point transform held by a lane pair: this lane holds elements
+// 8*upper .. 8*upper+7 of the block and its partner (lane ^ 1) the other half.
+// Strides 1, 2, 4 are local; stride 8 pairs element j of the lower half with
+// element j of the upper half.
+__device__ __forceinline__ void rht16_pair(float v[8], uint32_t negmask, bool upper) {
+    const int off = upper ? 8 : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ((negmask >> (i + off)) & 1u) ? -v[i] : v[i];
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < 8; i += 2 * h) {
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+                float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float other = __shfl_xor(v[j], 1);
+        // lower lane: a + b with a = own; upper lane: a - b with a = partner's
+        v[j] = upper ? (other - v[j]) : (v[j] + other);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= 0.25f;
+}
+
+// NVFP4 per-tensor scale from the amax: 2688 / A, A = 0 -> 1, overflow -> FLT_MAX.
+__device__ __forceinline__ float nvfp4_tensor_scale(float amax) {
+    if (amax == 0.0f) return 1.0f;
+    float s = 2688.0f / amax;
+    if (__builtin_isinf(s)) s = 3.40282347e38f;
+    return s;
+}
+
+}  // namespace bsq

@@ -1,0 +1,25 @@
+// launch.hpp -- internal host-side launchers of the HIP kernels.  The C ABI (api.cpp)
+// validates every argument before calling one of these; the launchers only enqueue
+// kernels and return 0 or a hipError_t code.  Streams travel as void* so that api.cpp
+// needs no HIP header.
+#pragma once
+
+#include <stdint.h>
+
+namespace bsq {
+
+int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
+                          uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
+                          uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, void* hip_stream);
+int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, uint8_t* row_codes,
+                          uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream);
+int launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows,
+                            int64_t cols, void* out, void* hip_stream);
+int launch_rht_apply(const void* x, int64_t R, int64_t C, int axis, const int8_t* signs, float* out,
+                     void* hip_stream);
+int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const float* a_s_enc, const uint8_t* b_codes,
+                            const uint8_t* b_scales, const float* b_s_enc, void* c, int c_dtype, void* hip_stream);
+const char* hip_error_string(int e);
+
+}  // namespace bsq

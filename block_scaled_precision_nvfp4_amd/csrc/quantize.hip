@@ -1,0 +1,538 @@
+// quantize.hip -- NVFP4 / MXFP8 quantization, NVFP4 dequantization and the standalone
+// 16-point Hadamard transform for gfx950.
+//
+// Work decomposition (all quantize kernels).  A workgroup of 256 threads owns a tile of
+// 256 rows x 128 columns of the bf16 input.  Thread t = 16*rb + cc loads the 16 x 8
+// sub-tile rows [16rb, 16rb+16) x columns [8cc, 8cc+8) with sixteen 16-byte loads; one
+// wave therefore reads four 256-byte row segments per load instruction (coalesced).
+//   * Rowwise 16-blocks span a lane pair (cc, cc^1); their amax and the stride-8
+//     Hadamard stage use one cross-lane exchange.  Rowwise 32-blocks (MXFP8) span four
+//     lanes.
+//   * Columnwise 16-blocks are entirely inside one thread (its 16 rows of one column);
+//     columnwise 32-blocks span the lanes t and t^16.  Columnwise codes are transposed
+//     through LDS so that every output row (= input column) receives a full 128-byte
+//     (NVFP4) or 256-byte (MXFP8) segment from one wave.
+// The NVFP4 path runs an amax pass (atomic max of the binary32 bit pattern, which orders
+// like the value for non-negative floats) before the encode pass, because every block
+// scale depends on the per-tensor scale.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace bsq {
+
+constexpr int TILE_R = 256;
+constexpr int TILE_C = 128;
+constexpr int NTHREADS = 256;
+
+struct TileCoord {
+    int64_t r0, c0;   // origin of this thread's 16 x 8 sub-tile
+    int rb, cc;       // sub-tile coordinates inside the workgroup tile
+};
+
+__device__ __forceinline__ TileCoord tile_coord() {
+    TileCoord t;
+    t.rb = threadIdx.x >> 4;
+    t.cc = threadIdx.x & 15;
+    t.r0 = (int64_t)blockIdx.y * TILE_R + 16 * t.rb;
+    t.c0 = (int64_t)blockIdx.x * TILE_C + 8 * t.cc;
+    return t;
+}
+
+// Load the thread's 16 x 8 bf16 sub-tile; rows >= R or a column chunk >= C read as zero
+// (C % 8 == 0, so a chunk is either entirely inside or entirely outside).
+// The sub-tile lives in registers as q[row][word], word w holding columns 2w and 2w+1;
+// every loop that indexes it is fully unrolled so that all indices are constants.
+typedef uint32_t SubTile[16][4];
+
+__device__ __forceinline__ void load_subtile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                             const TileCoord& t, SubTile q) {
+    const bool colok = t.c0 < C;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int64_t r = t.r0 + j;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (colok && r < R) v = load16_stream(x + r * C + t.c0);
+        q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
+    }
+}
+
+// Row j of the sub-tile as 8 floats.
+__device__ __forceinline__ void row_of(const SubTile q, int j, float v[8]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        v[2 * w] = bf16_lo(q[j][w]);
+        v[2 * w + 1] = bf16_hi(q[j][w]);
+    }
+}
+
+// Column k of the sub-tile as 16 floats.
+__device__ __forceinline__ void col_of(const SubTile q, int k, float v[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = (k & 1) ? bf16_hi(q[j][k >> 1]) : bf16_lo(q[j][k >> 1]);
+}
+
+__device__ __forceinline__ uint32_t sign_mask16(const int8_t* __restrict__ signs) {
+    if (!signs) return 0u;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m |= (signs[i] < 0 ? 1u : 0u) << i;
+    return m;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+    atomicMax((unsigned int*)p, __float_as_uint(v));
+}
+
+// ------------------------------------------------------------------ amax pass
+
+__global__ void reset_amax_kernel(float* amax) {
+    if (threadIdx.x < 2) amax[threadIdx.x] = 0.0f;
+}
+
+// DIRS: which slots to fill (bit 0 rowwise, bit 1 columnwise).  Without RHT both
+// directions share the plain amax; with RHT each direction takes the amax of its own
+// transformed values.
+template <int DIRS, bool RHT>
+__global__ __launch_bounds__(NTHREADS) void nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                              int64_t C, const int8_t* __restrict__ signs,
+                                                              float* __restrict__ amax) {
+    const TileCoord t = tile_coord();
+    SubTile q;
+    load_subtile(x, R, C, t, q);
+    float mrow = 0.0f, mcol = 0.0f;
+    if (!RHT) {
+        static_for<0, 16>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            float v[8];
+            row_of(q, j, v);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) mrow = __builtin_fmaxf(mrow, __builtin_fabsf(v[k]));
+        });
+        mcol = mrow;
+    } else {
+        const uint32_t neg = sign_mask16(signs);
+        if (DIRS & 1) {
+            const bool upper = (t.cc & 1) != 0;
+        static_for<0, 16>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+                float v[8];
+                row_of(q, j, v);
+                rht16_pair(v, neg, upper);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) mrow = __builtin_fmaxf(mrow, __builtin_fabsf(v[k]));
+            });
+        }
+        if (DIRS & 2) {
+        static_for<0, 8>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+                float v[16];
+            col_of(q, k, v);
+                rht16(v, neg);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mcol = __builtin_fmaxf(mcol, __builtin_fabsf(v[j]));
+            });
+        }
+    }
+    __shared__ float red[2][NTHREADS / 64];
+    mrow = wave_max(mrow);
+    mcol = wave_max(mcol);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        red[0][wave] = mrow;
+        red[1][wave] = mcol;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0][0], b = red[1][0];
+#pragma unroll
+        for (int w = 1; w < NTHREADS / 64; ++w) {
+            a = __builtin_fmaxf(a, red[0][w]);
+            b = __builtin_fmaxf(b, red[1][w]);
+        }
+        if (DIRS & 1) atomic_max_nonneg(amax + 0, a);
+        if (DIRS & 2) atomic_max_nonneg(amax + 1, b);
+    }
+}
+
+// ------------------------------------------------------------------ NVFP4 encode
+
+struct NvEncodeArgs {
+    const uint16_t* x;
+    int64_t R, C;
+    const int8_t* signs;
+    uint8_t* row_codes;
+    uint8_t* row_scales;
+    uint8_t* col_codes;
+    uint8_t* col_scales;
+    const float* amax;
+    float* s_enc_out;
+    uint64_t seed;
+    uint32_t stream;
+};
+
+// Encode one 16-block's worth of values held by this thread (n = 8 or 16 values) with the
+// block amax already known.  Writes the packed codes (n/2 bytes as n/8 words) into w[].
+// first_index: output-layout index of v[0]; consecutive values are consecutive indices.
+template <int N, bool SR>
+__device__ __forceinline__ uint32_t encode_block(const float* v, float bmax, float S, uint64_t first_index,
+                                                 uint64_t seed, uint32_t stream, uint32_t dir, uint32_t* w) {
+    float tt = bmax * S;
+    tt = tt / 6.0f;
+    const uint32_t sb = e4m3_encode_nonneg(tt);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) w[i] = 0u;
+    if (sb != 0u) {
+        const float enc = S / e4m3_decode_nonneg(sb);
+        if (SR) {
+#pragma unroll
+            for (int g = 0; g < N / 4; ++g) {
+                const u32x4 rw = sr_words((first_index >> 2) + g, seed, stream, dir);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * g + e;
+                    const uint32_t c = e2m1_encode_sr(v[j] * enc, word_of(rw, e));
+                    w[j >> 3] |= c << (4 * (j & 7));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                const uint32_t c = e2m1_encode_rne(v[j] * enc);
+                w[j >> 3] |= c << (4 * (j & 7));
+            }
+        }
+    }
+    return sb;
+}
+
+template <int DIRS, bool RHT, bool SR>
+__global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) {
+    const TileCoord t = tile_coord();
+    const int64_t R = a.R, C = a.C;
+    SubTile q;
+    load_subtile(a.x, R, C, t, q);
+    const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
+    const float Srow = nvfp4_tensor_scale(a.amax[0]);
+    const float Scol = nvfp4_tensor_scale(a.amax[1]);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        if (DIRS & 1) a.s_enc_out[0] = Srow;
+        if (DIRS & 2) a.s_enc_out[1] = Scol;
+    }
+    const bool colok = t.c0 < C;
+
+    if (DIRS & 1) {
+        const bool upper = (t.cc & 1) != 0;
+        static_for<0, 16>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            const int64_t r = t.r0 + j;
+            float v[8];
+            row_of(q, j, v);
+            if (RHT) rht16_pair(v, neg, upper);
+            float m = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            uint32_t w;
+            const uint32_t sb = encode_block<8, SR>(v, m, Srow, (uint64_t)r * (uint64_t)C + (uint64_t)t.c0,
+                                                    a.seed, a.stream, 0u, &w);
+            if (colok && r < R) {
+                *(uint32_t*)(a.row_codes + r * (C / 2) + t.c0 / 2) = w;
+                if (!upper) a.row_scales[r * (C / 16) + t.c0 / 16] = (uint8_t)sb;
+            }
+        });
+    }
+
+    if (DIRS & 2) {
+        // codes of column (8cc + k), row block rb -> lds_codes[8cc + k][rb]
+        __shared__ uint2 lds_codes[TILE_C][TILE_R / 16];
+        __shared__ uint8_t lds_sc[TILE_C][TILE_R / 16];
+        static_for<0, 8>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            float v[16];
+            col_of(q, k, v);
+            if (RHT) rht16(v, neg);
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+            uint32_t w[2];
+            const uint64_t c = (uint64_t)(t.c0 + k);
+            const uint32_t sb = encode_block<16, SR>(v, m, Scol, c * (uint64_t)R + (uint64_t)t.r0,
+                                                     a.seed, a.stream, 1u, w);
+            lds_codes[8 * t.cc + k][t.rb] = make_uint2(w[0], w[1]);
+            lds_sc[8 * t.cc + k][t.rb] = (uint8_t)sb;
+        });
+        __syncthreads();
+        const int64_t tr0 = (int64_t)blockIdx.y * TILE_R;
+        const int64_t tc0 = (int64_t)blockIdx.x * TILE_C;
+#pragma unroll
+        for (int p = 0; p < (TILE_C * TILE_R / 16) / NTHREADS; ++p) {
+            const int idx = threadIdx.x + NTHREADS * p;
+            const int col = idx >> 4, rbk = idx & 15;
+            const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
+            if (c < C && r < R) {
+                *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk];
+                a.col_scales[c * (R / 16) + r / 16] = lds_sc[col][rbk];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ MXFP8 cast
+
+// Scale byte of a 32-block with amax m: X = floor(log2 m) - 8 clamped at -127, byte X+127;
+// for a normal binary32 m that is max(exponent_field - 8, 0), and 0 for subnormal or zero m.
+__device__ __forceinline__ uint32_t mx_scale_byte(float m) {
+    const int e = (int)(__float_as_uint(m) >> 23);
+    return (uint32_t)(e > 8 ? e - 8 : 0);
+}
+
+// 2^-X for scale byte b (X = b - 127): binary32 with exponent field 254 - b (b <= 246).
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
+
+struct MxArgs {
+    const uint16_t* x;
+    int64_t R, C;
+    uint8_t* row_codes;
+    uint8_t* row_scales;
+    uint8_t* col_codes;
+    uint8_t* col_scales;
+};
+
+template <int DIRS>
+__global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
+    const TileCoord t = tile_coord();
+    const int64_t R = a.R, C = a.C;
+    SubTile q;
+    load_subtile(a.x, R, C, t, q);
+    const bool colok = t.c0 < C;
+
+    if (DIRS & 1) {
+        static_for<0, 16>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            const int64_t r = t.r0 + j;
+            float v[8];
+            row_of(q, j, v);
+            float m = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 2));
+            uint32_t lo = 0, hi = 0, sb = 0;
+            if (m != 0.0f) {
+                sb = mx_scale_byte(m);
+                const float inv = mx_inv_scale(sb);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) lo |= e4m3_encode(v[k] * inv) << (8 * k);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) hi |= e4m3_encode(v[4 + k] * inv) << (8 * k);
+            }
+            if (colok && r < R) {
+                *(uint2*)(a.row_codes + r * C + t.c0) = make_uint2(lo, hi);
+                if ((t.cc & 3) == 0) a.row_scales[r * (C / 32) + t.c0 / 32] = (uint8_t)sb;
+            }
+        });
+    }
+
+    if (DIRS & 2) {
+        __shared__ uint4 lds_codes[TILE_C][TILE_R / 16];
+        __shared__ uint8_t lds_sc[TILE_C][TILE_R / 32];
+        const bool upper = (t.rb & 1) != 0;
+        static_for<0, 8>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            float v[16];
+            col_of(q, k, v);
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+            uint32_t w[4] = {0, 0, 0, 0}, sb = 0;
+            if (m != 0.0f) {
+                sb = mx_scale_byte(m);
+                const float inv = mx_inv_scale(sb);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) w[j >> 2] |= e4m3_encode(v[j] * inv) << (8 * (j & 3));
+            }
+            lds_codes[8 * t.cc + k][t.rb] = make_uint4(w[0], w[1], w[2], w[3]);
+            if (!upper) lds_sc[8 * t.cc + k][t.rb >> 1] = (uint8_t)sb;
+        });
+        __syncthreads();
+        const int64_t tr0 = (int64_t)blockIdx.y * TILE_R;
+        const int64_t tc0 = (int64_t)blockIdx.x * TILE_C;
+#pragma unroll
+        for (int p = 0; p < (TILE_C * TILE_R / 16) / NTHREADS; ++p) {
+            const int idx = threadIdx.x + NTHREADS * p;
+            const int col = idx >> 4, rbk = idx & 15;
+            const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
+            if (c < C && r < R) {
+                *(uint4*)(a.col_codes + c * R + r) = lds_codes[col][rbk];
+                if ((rbk & 1) == 0) a.col_scales[c * (R / 32) + r / 32] = lds_sc[col][rbk >> 1];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ NVFP4 dequantize
+
+// One thread per 16-element block: out = bf16((E2M1 * fp32(s_b)) / S).
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ s_enc, int64_t nblocks,
+                                                            uint16_t* __restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    const float S = s_enc[0];
+    const float sc = e4m3_decode_nonneg(scales[b] & 0x7Fu);
+    const uint2 cw = *(const uint2*)(codes + 8 * b);
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t c = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 0xFu;
+        const float mag = (c & 7u) <= 4u ? 0.5f * (float)(c & 7u) : ((c & 7u) == 5u ? 3.0f : ((c & 7u) == 6u ? 4.0f : 6.0f));
+        const float e = (c & 8u) ? -mag : mag;
+        const float p = e * sc;
+        const float d = p / S;
+        const uint32_t h = f32_to_bf16_rne(d);
+        if (j & 1) o[j >> 1] |= h << 16; else o[j >> 1] = h;
+    }
+    uint4* dst = (uint4*)(out + 16 * b);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// ------------------------------------------------------------------ standalone RHT
+
+template <int AXIS>
+__global__ __launch_bounds__(NTHREADS) void rht_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                       const int8_t* __restrict__ signs, float* __restrict__ out) {
+    const TileCoord t = tile_coord();
+    SubTile q;
+    load_subtile(x, R, C, t, q);
+    const uint32_t neg = sign_mask16(signs);
+    const bool colok = t.c0 < C;
+    if (AXIS == 1) {
+        const bool upper = (t.cc & 1) != 0;
+        static_for<0, 16>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            float v[8];
+            row_of(q, j, v);
+            rht16_pair(v, neg, upper);
+            const int64_t r = t.r0 + j;
+            if (colok && r < R) {
+                float4* d = (float4*)(out + r * C + t.c0);
+                d[0] = make_float4(v[0], v[1], v[2], v[3]);
+                d[1] = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        });
+    } else {
+        float y[16][8];
+        static_for<0, 8>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            float v[16];
+            col_of(q, k, v);
+            rht16(v, neg);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) y[j][k] = v[j];
+        });
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t r = t.r0 + j;
+            if (colok && r < R) {
+                float4* d = (float4*)(out + r * C + t.c0);
+                d[0] = make_float4(y[j][0], y[j][1], y[j][2], y[j][3]);
+                d[1] = make_float4(y[j][4], y[j][5], y[j][6], y[j][7]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static inline dim3 tile_grid(int64_t R, int64_t C) {
+    return dim3((unsigned)((C + TILE_C - 1) / TILE_C), (unsigned)((R + TILE_R - 1) / TILE_R), 1);
+}
+
+template <int DIRS, bool RHT, bool SR>
+static void launch_nv(const NvEncodeArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((nvfp4_amax_kernel<DIRS, RHT>), g, dim3(NTHREADS), 0, s, a.x, a.R, a.C, a.signs,
+                       (float*)a.amax);
+    hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR>), g, dim3(NTHREADS), 0, s, a);
+}
+
+template <int DIRS>
+static void launch_nv_dirs(const NvEncodeArgs& a, bool rht, bool sr, dim3 g, hipStream_t s) {
+    if (rht) {
+        if (sr) launch_nv<DIRS, true, true>(a, g, s); else launch_nv<DIRS, true, false>(a, g, s);
+    } else {
+        if (sr) launch_nv<DIRS, false, true>(a, g, s); else launch_nv<DIRS, false, false>(a, g, s);
+    }
+}
+
+__global__ void empty_tensor_scales_kernel(float* amax, float* s_enc) {
+    if (threadIdx.x < 2) {
+        amax[threadIdx.x] = 0.0f;
+        s_enc[threadIdx.x] = 1.0f;
+    }
+}
+
+int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
+                          uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
+                          uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, void* hip_stream) {
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (R == 0 || C == 0) {
+        hipLaunchKernelGGL(empty_tensor_scales_kernel, dim3(1), dim3(64), 0, s, amax, s_enc);
+        return (int)hipGetLastError();
+    }
+    hipLaunchKernelGGL(reset_amax_kernel, dim3(1), dim3(64), 0, s, amax);
+    NvEncodeArgs a{(const uint16_t*)x, R, C, signs, row_codes, row_scales, col_codes, col_scales,
+                   amax, s_enc, seed, stream};
+    const dim3 g = tile_grid(R, C);
+    const bool rht = signs != nullptr, sr = rounding == 1;
+    if (direction == 1) launch_nv_dirs<1>(a, rht, sr, g, s);
+    else if (direction == 2) launch_nv_dirs<2>(a, rht, sr, g, s);
+    else launch_nv_dirs<3>(a, rht, sr, g, s);
+    return (int)hipGetLastError();
+}
+
+int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, uint8_t* row_codes,
+                          uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
+    if (R == 0 || C == 0) return 0;
+    hipStream_t s = (hipStream_t)hip_stream;
+    MxArgs a{(const uint16_t*)x, R, C, row_codes, row_scales, col_codes, col_scales};
+    const dim3 g = tile_grid(R, C);
+    if (direction == 1) hipLaunchKernelGGL(mxfp8_kernel<1>, g, dim3(NTHREADS), 0, s, a);
+    else if (direction == 2) hipLaunchKernelGGL(mxfp8_kernel<2>, g, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL(mxfp8_kernel<3>, g, dim3(NTHREADS), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+int launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows,
+                            int64_t cols, void* out, void* hip_stream) {
+    const int64_t nb = rows * (cols / 16);
+    if (nb == 0) return 0;
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)hip_stream, codes, scales, s_enc, nb, (uint16_t*)out);
+    return (int)hipGetLastError();
+}
+
+int launch_rht_apply(const void* x, int64_t R, int64_t C, int axis, const int8_t* signs, float* out,
+                     void* hip_stream) {
+    if (R == 0 || C == 0) return 0;
+    const dim3 g = tile_grid(R, C);
+    if (axis == 1)
+        hipLaunchKernelGGL(rht_kernel<1>, g, dim3(NTHREADS), 0, (hipStream_t)hip_stream, (const uint16_t*)x, R, C,
+                           signs, out);
+    else
+        hipLaunchKernelGGL(rht_kernel<0>, g, dim3(NTHREADS), 0, (hipStream_t)hip_stream, (const uint16_t*)x, R, C,
+                           signs, out);
+    return (int)hipGetLastError();
+}
+
+const char* hip_error_string(int e) { return hipGetErrorString((hipError_t)e); }
+
+}  // namespace bsq

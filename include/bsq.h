@@ -1,0 +1,179 @@
+/*
+ * bsq.h -- C ABI of libbsq, the block-scaled quantized linear-layer hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations: NVFP4 quantization (rowwise / columnwise, round-to-nearest-even or
+ * Philox-keyed stochastic rounding, optional 16-point random Hadamard transform),
+ * NVFP4 dequantization, the MXFP8 cast, the standalone Hadamard transform, and the
+ * block-scaled GEMM C = A * B^T that consumes the quantized operands with fp32
+ * accumulation.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are row-major and contiguous.  A bf16 tensor x has shape [rows][cols].
+ *   - "Rowwise" blocks run along cols; "columnwise" blocks run along rows and are
+ *     stored as the rowwise quantization of x^T, i.e. with shape [cols][...].  A GEMM
+ *     operand is always the direction whose blocks run along the contraction dim,
+ *     so every GEMM here is C[M][N] = A[M][K] * B[N][K]^T with both operands stored
+ *     along K (fprop: X and W rowwise; dgrad: dY rowwise, W columnwise; wgrad: dY
+ *     and X columnwise).  This is the per-direction operand choice of the GEMM
+ *     dispatch on the page "[Pytorch][Common] Hybrid quantization"
+ *     (TransformerEngine PR #2817, Description and dispatch flowchart).
+ *   - Every pointer argument that names tensor data is a DEVICE pointer; every
+ *     device pointer must be 16-byte aligned.  The caller allocates and owns all
+ *     buffers; the library never allocates, frees or keeps device memory.
+ *   - Work is enqueued asynchronously on hip_stream (a hipStream_t; NULL is the
+ *     null stream).  Return values report argument validation and launch errors
+ *     only; faults during kernel execution surface at the next synchronisation.
+ *   - Status codes: 0 (BSQ_OK) or one of the BSQ_ERR_* values; validation happens
+ *     on the host before any HIP call, so a rejected call touches no device state.
+ *     bsq_last_error() returns a message for the last failing call of the thread.
+ */
+#ifndef BSQ_H
+#define BSQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bsq_status {
+    BSQ_OK = 0,
+    BSQ_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    BSQ_ERR_SHAPE = 2,       /* a dimension is negative or not a required multiple  */
+    BSQ_ERR_ARG = 3,         /* an enum/flag value is out of range                  */
+    BSQ_ERR_UNSUPPORTED = 4, /* a valid combination this library does not implement */
+    BSQ_ERR_HIP = 5,         /* a HIP runtime call (launch) failed                  */
+    BSQ_ERR_ALIGN = 6        /* a device pointer is not 16-byte aligned            */
+};
+
+/* direction bitmask: which quantizations to produce (the usage flags of a quantizer). */
+#define BSQ_ROW 1
+#define BSQ_COL 2
+/* element rounding */
+#define BSQ_RNE 0
+#define BSQ_SR 1
+/* GEMM operand formats */
+#define BSQ_FMT_NVFP4 0
+#define BSQ_FMT_MXFP8 1
+/* GEMM output types */
+#define BSQ_OUT_BF16 0
+#define BSQ_OUT_F32 1
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of a bf16 tensor.
+ *
+ * Defines: the recipe of the page "Add an NVFP4 quantization converter"
+ * (torchtitan PR #3914): 16-element blocks with one inner scale each and one outer
+ * per-tensor scale (review thread on the recipe's inner 1x16 scale), stochastic
+ * rounding keyed by a Philox seed and an RHT whose +-1 sign vector both GEMM
+ * operands share (Summary, "What changed").  Numerics, per block of 16 values v:
+ *   A     = max |v| over the tensor (over the transformed values when RHT is on,
+ *           separately per direction),
+ *   S     = 2688 / A in fp32 (6 * 448: the largest E2M1 code times the largest E4M3
+ *           value); A = 0 gives S = 1; an infinite S is clamped to FLT_MAX,
+ *   s_b   = E4M3_RNE_saturating((blockmax * S) / 6)  -- the block scale byte,
+ *   codes = E2M1(v * (S / fp32(s_b))), RNE or SR; all zero when s_b == 0.
+ * With SR, element i (linear index in the OUTPUT layout of its direction) is
+ * rounded up with probability equal to its position between the two neighbouring
+ * E2M1 values, using word i%4 of Philox4x32-10(counter = (lo32(i/4), hi32(i/4),
+ * sr_stream, d), key = (lo32(sr_seed), hi32(sr_seed))), d = 0 rowwise, 1
+ * columnwise; it is compared as (word >> 8) * 2^-24 < p.  Block scales are always RNE.
+ *
+ * Arguments:
+ *   x          [rows][cols] bf16 (device).
+ *   direction  BSQ_ROW, BSQ_COL or both.  BSQ_ROW needs cols % 16 == 0; BSQ_COL
+ *              needs rows % 16 == 0; in every case cols % 8 == 0.
+ *   rounding   BSQ_RNE or BSQ_SR (sr_seed/sr_stream are ignored under BSQ_RNE).
+ *   rht_signs  NULL, or 16 int8 values each +1 or -1 (device): apply the 16-point
+ *              random Hadamard transform y = x diag(d) H16 / 4 (Sylvester order,
+ *              fp32 butterfly with strides 1, 2, 4, 8) to each 16-block along the
+ *              blocked dimension before quantizing; the transformed values are
+ *              not rounded to bf16.
+ *   row_codes  [rows][cols/2] uint8: element 2j in bits 3:0 of byte j, 2j+1 in
+ *              bits 7:4 (sign in bit 3 of a nibble); row_scales [rows][cols/16]
+ *              E4M3 bytes.  Required iff BSQ_ROW.
+ *   col_codes  [cols][rows/2], col_scales [cols][rows/16]; required iff BSQ_COL.
+ *   amax_out   float[2] (device): [0] the rowwise amax A, [1] the columnwise one.
+ *              Also used as the accumulator of the amax pass.  Required.
+ *   s_enc_out  float[2] (device): the matching tensor scales S.  Required.
+ *              Slots of an unrequested direction are left unspecified.
+ */
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding,
+                   uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
+                   uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                   uint8_t* col_scales, float* amax_out, float* s_enc_out, void* hip_stream);
+
+/*
+ * nvfp4_dequantize -- bf16 value of an NVFP4 tensor: out = bf16_RNE((E2M1(code) *
+ * fp32(s_b)) / S) (the product is exact).  This is the "rowwise_dequantized"
+ * columnwise source of the hybrid quantizer on the page "[Pytorch][Common] Hybrid
+ * quantization" (TransformerEngine PR #2817, "Enable columnwise_source and hybrid
+ * recipes"): the backward operand is re-quantized from dequantize(rowwise(x)).
+ *   codes [rows][cols/2], scales [rows][cols/16], s_enc float[1] (all device);
+ *   out [rows][cols] bf16 (device).  cols % 16 == 0.
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc,
+                     int64_t rows, int64_t cols, void* out, void* hip_stream);
+
+/*
+ * mxfp8_quantize -- MXFP8 cast of a bf16 tensor: 32-element blocks, one E8M0 scale
+ * per block, E4M3 codes (block size and per-block scale count: page "[Pytorch]
+ * [Common] Hybrid quantization", review thread on MXFP8_BLOCK_SCALING_SIZE and the
+ * columnwise scale count; scale rule: the OCP MX shared exponent, from the MX
+ * paper cited in the TorchAO review page's references).  Per block:
+ *   X = floor(log2 blockmax) - 8 clamped to [-127, 127], scale byte X + 127,
+ *   codes = E4M3_RNE_saturating(v * 2^-X) (values above 448 clip);
+ *   an all-zero block gives scale byte 0 and codes 0.
+ * Arguments: x [rows][cols] bf16; BSQ_ROW needs cols % 32 == 0, BSQ_COL needs
+ * rows % 32 == 0, always cols % 8 == 0.  row_codes [rows][cols], row_scales
+ * [rows][cols/32]; col_codes [cols][rows], col_scales [cols][rows/32] (required
+ * iff the direction is requested).
+ */
+int mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int direction,
+                   uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                   uint8_t* col_scales, void* hip_stream);
+
+/*
+ * rht_apply -- the 16-point random Hadamard transform on its own: out = fp32 of
+ * each 16-block of x times diag(d) H16 / 4 (same definition and evaluation order as
+ * in nvfp4_quantize; page "Add an NVFP4 quantization converter", Summary: the
+ * transform cancels in a GEMM only when both operands share the sign vector).
+ *   x [rows][cols] bf16; axis 1: blocks of 16 consecutive elements of a row
+ *   (cols % 16 == 0); axis 0: blocks of 16 consecutive elements of a column
+ *   (rows % 16 == 0).  cols % 8 == 0.  signs: 16 int8 +-1 (device).
+ *   out [rows][cols] fp32 (device).
+ */
+int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t* signs,
+              float* out, void* hip_stream);
+
+/*
+ * blockscaled_gemm -- C[M][N] = alpha * sum_k A[m][k] B[n][k] on block-scaled
+ * operands with fp32 accumulation (the fprop / dgrad / wgrad GEMM of a quantized
+ * linear layer; page "Add an NVFP4 quantization converter", Design notes: the
+ * GEMM on low-precision operands is what the recipe buys).
+ *   fmt BSQ_FMT_NVFP4: a_codes [M][K/2], a_scales [M][K/16] (E4M3), a_s_enc float[1]
+ *       (device, the operand's tensor scale S), likewise for B; alpha =
+ *       1/(S_a * S_b).  K % 32 == 0.
+ *   fmt BSQ_FMT_MXFP8: a_codes [M][K] (E4M3), a_scales [M][K/32] (E8M0); s_enc
+ *       pointers are ignored (may be NULL); alpha = 1.  K % 32 == 0.
+ *   c [M][N], c_dtype BSQ_OUT_BF16 (RNE) or BSQ_OUT_F32.
+ *   M, N >= 0 arbitrary; M, N or K == 0 are valid (K == 0 writes zeros).
+ */
+int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
+                     const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
+                     const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
+                     void* c, int c_dtype, void* hip_stream);
+
+/* Message of the last failing call on this thread ("" if none).  Host memory owned
+ * by the library; valid until the thread's next call. */
+const char* bsq_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int bsq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSQ_H */

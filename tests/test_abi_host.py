@@ -1,0 +1,130 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every
+entry point include/bsq.h declares, and rejects every invalid argument with the
+documented status before any HIP call is made."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import block_scaled_precision_nvfp4_amd as bsq
+    if not os.path.exists(bsq.LIB_PATH):
+        from block_scaled_precision_nvfp4_amd import build
+        build.build()
+    return bsq.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ["nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "rht_apply", "blockscaled_gemm",
+              "bsq_last_error", "bsq_version"]:
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for f in declared_functions():
+        assert hasattr(L, f), f
+
+
+def test_version(L):
+    assert L.bsq_version() == 100
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails before any HIP call
+
+
+def q(L, x=FAKE, rows=256, cols=256, direction=1, rounding=0, signs=None, rc=FAKE, rs=FAKE, cc=FAKE, cs=FAKE,
+      amax=FAKE, senc=FAKE):
+    return L.nvfp4_quantize(x, rows, cols, direction, rounding, 0, 0, signs, rc, rs, cc, cs, amax, senc, None)
+
+
+def last(L):
+    return L.bsq_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(direction=0), 3, "direction"),
+    (dict(direction=4), 3, "direction"),
+    (dict(rounding=2), 3, "rounding"),
+    (dict(rows=-1), 2, "negative"),
+    (dict(cols=12), 2, "multiple of 8"),
+    (dict(cols=24, direction=1), 2, "cols % 16"),
+    (dict(rows=24, direction=2), 2, "rows % 16"),
+    (dict(amax=None), 1, "amax_out"),
+    (dict(senc=None), 1, "amax_out"),
+    (dict(x=None), 1, "x is NULL"),
+    (dict(rc=None, direction=1), 1, "rowwise outputs"),
+    (dict(cs=None, direction=3), 1, "columnwise outputs"),
+    (dict(x=FAKE + 8), 6, "aligned"),
+    (dict(signs=FAKE + 2), 6, "aligned"),
+])
+def test_nvfp4_quantize_validation(L, kw, status, needle):
+    assert q(L, **kw) == status
+    assert needle in last(L)
+
+
+def test_mxfp8_quantize_validation(L):
+    f = L.mxfp8_quantize
+    assert f(FAKE, 64, 48, 1, FAKE, FAKE, None, None, None) == 2 and "cols % 32" in last(L)
+    assert f(FAKE, 48, 64, 2, None, None, FAKE, FAKE, None) == 2 and "rows % 32" in last(L)
+    assert f(FAKE, 64, 64, 5, FAKE, FAKE, None, None, None) == 3
+    assert f(None, 64, 64, 1, FAKE, FAKE, None, None, None) == 1
+    assert f(FAKE, 64, 64, 2, FAKE, FAKE, None, FAKE, None) == 1
+    assert f(FAKE + 4, 64, 64, 1, FAKE, FAKE, None, None, None) == 6
+
+
+def test_rht_apply_validation(L):
+    f = L.rht_apply
+    assert f(FAKE, 64, 64, 2, FAKE, FAKE, None) == 3
+    assert f(FAKE, 64, 24, 1, FAKE, FAKE, None) == 2
+    assert f(FAKE, 24, 64, 0, FAKE, FAKE, None) == 2
+    assert f(FAKE, 64, 64, 1, None, FAKE, None) == 1
+
+
+def test_gemm_validation(L):
+    f = L.blockscaled_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert f(2, 128, 128, 128, *args, 0, None) == 3 and "fmt" in last(L)
+    assert f(0, 128, 128, 128, *args, 2, None) == 3 and "c_dtype" in last(L)
+    assert f(0, 128, 128, 48, *args, 0, None) == 2 and "multiple of 32" in last(L)
+    assert f(0, -1, 128, 64, *args, 0, None) == 2
+    assert f(0, 128, 128, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 1 and "tensor scales" in last(L)
+    assert f(0, 128, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert f(0, 128, 128, 64, FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 6
+    # empty products are valid no-ops that never reach the device
+    assert f(0, 0, 128, 64, *args, 0, None) == 0
+    assert f(1, 128, 0, 64, *args, 0, None) == 0
+
+
+def test_dequantize_validation(L):
+    f = L.nvfp4_dequantize
+    assert f(FAKE, FAKE, FAKE, 4, 24, FAKE, None) == 2
+    assert f(None, FAKE, FAKE, 4, 32, FAKE, None) == 1
+    assert f(FAKE, FAKE, FAKE, 0, 32, FAKE, None) == 0
+
+
+def test_error_cleared_on_success(L):
+    assert q(L, direction=0) == 3
+    assert last(L) != ""
+    assert L.blockscaled_gemm(0, 0, 8, 64, *([FAKE] * 7), 0, None) == 0
+    assert last(L) == ""
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import block_scaled_precision_nvfp4_amd as bsq
+    monkeypatch.setattr(bsq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(bsq, "_lib", None)
+    with pytest.raises(RuntimeError, match="libbsq.so not found"):
+        bsq.lib()

@@ -1,0 +1,166 @@
+"""GPU parity of the block-scaled GEMM against the CPU oracle (binary64 over the same
+quantized operands).  The bar: relative Frobenius error <= 2e-3 against the oracle
+output rounded as the GPU stores it (bf16 RNE for Y and dX, none for the fp32 dW).
+Small shapes are compared in full (several tiles, ragged M/N, a K tail shorter than
+the K slice); the workload shapes are compared on sampled rows x columns of C, with
+the GEMM launched exactly as the bench launches it."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsq
+from synthetic import (SEED_DY, SEED_SIGNS, SEED_SR_KEY, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16,
+                       outlier_bf16, rht_signs)
+from tests.gpu_common import GEMM_TOL, bf16_round, note, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def nv_gemm_check(a_cpu, b_cpu, out_dtype=torch.bfloat16, rows=None, cols=None, label="",
+                  a_dir=1, b_dir=1, rounding=0, signs=None):
+    """Quantize both operands on the GPU, run the GEMM, and compare against the oracle GEMM
+    of the GPU's own quantized operands (whose bit-exactness the quantize tests cover)."""
+    import oracle
+    note("nvfp4 gemm %s A%s B%s out=%s" % (label, tuple(a_cpu.shape), tuple(b_cpu.shape), out_dtype))
+    qa = bsq.nvfp4_quantize(a_cpu.to(DEV), direction=a_dir, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=0,
+                            rht_signs=signs)
+    qb = bsq.nvfp4_quantize(b_cpu.to(DEV), direction=b_dir, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=1,
+                            rht_signs=signs)
+    ka, kb = ("row" if a_dir == 1 else "col"), ("row" if b_dir == 1 else "col")
+    ia, ib = (0 if a_dir == 1 else 1), (0 if b_dir == 1 else 1)
+    y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qa[ka + "_codes"], qa[ka + "_scales"], qa["s_enc"][ia:ia + 1],
+                             qb[kb + "_codes"], qb[kb + "_scales"], qb["s_enc"][ib:ib + 1], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, qa[ka + "_codes"].cpu().numpy(), qa[ka + "_scales"].cpu().numpy(),
+                                  float(qa["s_enc"][ia].item()), qb[kb + "_codes"].cpu().numpy(),
+                                  qb[kb + "_scales"].cpu().numpy(), float(qb["s_enc"][ib].item()), rows=rows, cols=cols)
+    yc = y.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
+    err = rel_fro(yc, want)
+    note("  rel_fro vs rounded oracle = %.3e, vs exact oracle = %.3e" % (err, rel_fro(yc, ref)))
+    assert err <= GEMM_TOL, err
+    return err
+
+
+def mx_gemm_check(a_cpu, b_cpu, a_dir, b_dir, out_dtype=torch.bfloat16, rows=None, cols=None, label=""):
+    import oracle
+    note("mxfp8 gemm %s A%s B%s" % (label, tuple(a_cpu.shape), tuple(b_cpu.shape)))
+    qa = bsq.mxfp8_quantize(a_cpu.to(DEV), direction=a_dir)
+    qb = bsq.mxfp8_quantize(b_cpu.to(DEV), direction=b_dir)
+    ka, kb = ("row" if a_dir == 1 else "col"), ("row" if b_dir == 1 else "col")
+    y = bsq.blockscaled_gemm(bsq.FMT_MXFP8, qa[ka + "_codes"], qa[ka + "_scales"], None,
+                             qb[kb + "_codes"], qb[kb + "_scales"], None, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.blockscaled_gemm(oracle.FMT_MXFP8, qa[ka + "_codes"].cpu().numpy(), qa[ka + "_scales"].cpu().numpy(),
+                                  1.0, qb[kb + "_codes"].cpu().numpy(), qb[kb + "_scales"].cpu().numpy(), 1.0,
+                                  rows=rows, cols=cols)
+    yc = y.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
+    err = rel_fro(yc, want)
+    note("  rel_fro vs rounded oracle = %.3e" % err)
+    assert err <= GEMM_TOL, err
+    return err
+
+
+def test_tiny_config_full():
+    """X[128,256], W[256,256] ~ N(0,1); both NVFP4 rowwise RNE; Y = X W^T bf16."""
+    nv_gemm_check(gaussian_bf16((128, 256), 1.0, SEED_X), gaussian_bf16((256, 256), 1.0, SEED_W), label="tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (128, 128, 32), (1, 1, 64), (384, 260, 320), (64, 512, 1056)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_nvfp4_ragged_full(M, N, K, out_dtype):
+    nv_gemm_check(outlier_bf16((M, K), seed=M, mask_seed=K), gaussian_bf16((N, K), 0.02, N + 7), out_dtype=out_dtype,
+                  label="ragged")
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (256, 256, 256), (96, 160, 1056)])
+def test_mxfp8_ragged_full(M, N, K):
+    mx_gemm_check(outlier_bf16((M, K), seed=M + 1, mask_seed=K + 1), gaussian_bf16((N, K), 0.02, N + 9), 1, 1,
+                  label="ragged")
+
+
+def test_constant_operands_closed_form():
+    """All elements 1.0 in A and 0.5 in B: every output is K * 1.0 * 0.5 exactly."""
+    M, N, K = 160, 96, 512
+    a = torch.ones((M, K), dtype=torch.bfloat16)
+    b = torch.full((N, K), 0.5, dtype=torch.bfloat16)
+    qa = bsq.nvfp4_quantize(a.to(DEV))
+    qb = bsq.nvfp4_quantize(b.to(DEV))
+    y = bsq.blockscaled_gemm(0, qa["row_codes"], qa["row_scales"], qa["s_enc"][0:1], qb["row_codes"],
+                             qb["row_scales"], qb["s_enc"][0:1], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(y.cpu() == K * 0.5)
+
+
+def test_k_zero_writes_zeros():
+    a = torch.empty((64, 0), dtype=torch.uint8, device=DEV)
+    s = torch.empty((64, 0), dtype=torch.uint8, device=DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    y = torch.full((64, 64), 7.0, dtype=torch.float32, device=DEV)
+    bsq.blockscaled_gemm(0, a, s, one, a, s, one, out_dtype=torch.float32, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y.cpu() == 0)
+
+
+def test_wgrad_small_rht_sr_full():
+    """wgrad pairing at a small shape: dW = dY^T X, both columnwise with RHT + SR, fp32 out."""
+    nv_gemm_check(gaussian_bf16((512, 192), STD_DY, SEED_DY), gaussian_bf16((512, 160), 1.0, SEED_X),
+                  out_dtype=torch.float32, a_dir=2, b_dir=2, rounding=1, signs=rht_signs(SEED_SIGNS), label="wgrad-small")
+
+
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(n, size=min(k, n), replace=False))
+    idx[0], idx[-1] = 0, n - 1
+    return np.unique(idx)
+
+
+def test_fwd_llama3_8b_sampled():
+    """Y[16384, 14336] = X W^T at the Llama-3-8B FFN up-proj shape; 96 x 96 sampled outputs."""
+    nv_gemm_check(gaussian_bf16((16384, 4096), 1.0, SEED_X), gaussian_bf16((14336, 4096), STD_W, SEED_W),
+                  rows=_sample(16384, 96, 1), cols=_sample(14336, 96, 2), label="fwd")
+
+
+def test_wgrad_llama3_8b_sampled():
+    """dW[14336, 4096] = dY^T X with RHT + SR columnwise operands (K = 16384 tokens), fp32."""
+    nv_gemm_check(gaussian_bf16((16384, 14336), STD_DY, SEED_DY), gaussian_bf16((16384, 4096), 1.0, SEED_X),
+                  out_dtype=torch.float32, rows=_sample(14336, 64, 3), cols=_sample(4096, 64, 4),
+                  a_dir=2, b_dir=2, rounding=1, signs=rht_signs(SEED_SIGNS), label="wgrad")
+
+
+def test_hybrid_qwen3_8b_sampled():
+    """Per-direction recipe at the Qwen3-8B FFN shape: NVFP4 rowwise forward GEMM; MXFP8
+    dgrad dX = dY W (dY rowwise, W columnwise) and wgrad dW = dY^T X (both columnwise);
+    plus the columnwise operand built from the rowwise-dequantized NVFP4 forward value."""
+    X = gaussian_bf16((65536, 4096), 1.0, SEED_X)
+    W = gaussian_bf16((12288, 4096), STD_W, SEED_W)
+    nv_gemm_check(X, W, rows=_sample(65536, 64, 5), cols=_sample(12288, 64, 6), label="hybrid fwd")
+    dY = gaussian_bf16((65536, 12288), STD_DY, SEED_DY)
+    mx_gemm_check(dY, W, 1, 2, rows=_sample(65536, 64, 7), cols=_sample(4096, 64, 8), label="hybrid dgrad")
+    mx_gemm_check(dY, X, 2, 2, out_dtype=torch.float32, rows=_sample(12288, 48, 9), cols=_sample(4096, 48, 10),
+                  label="hybrid wgrad")
+
+
+def test_hybrid_rowwise_dequantized_source():
+    """columnwise_source = rowwise_dequantized: MXFP8 columnwise of bf16(dequant(NVFP4 rowwise X));
+    compared bit for bit with the oracle's chain on a [4096, 1024] slice of the workload."""
+    import oracle
+    from tests.gpu_common import assert_bytes_equal
+    X = gaussian_bf16((4096, 1024), 1.0, SEED_X)
+    note("hybrid rowwise_dequantized chain [4096,1024]")
+    q = bsq.nvfp4_quantize(X.to(DEV), direction=1)
+    d = bsq.nvfp4_dequantize(q["row_codes"], q["row_scales"], q["s_enc"][0:1])
+    m = bsq.mxfp8_quantize(d, direction=2)
+    torch.cuda.synchronize()
+    rq = oracle.nvfp4_quantize(X, direction=1)
+    rd = oracle.nvfp4_dequantize(rq["row_codes"], rq["row_scales"], float(rq["s_enc"][0]))
+    rm = oracle.mxfp8_quantize(rd, direction=2)
+    assert_bytes_equal(m["col_codes"], rm["col_codes"], "col codes")
+    assert_bytes_equal(m["col_scales"], rm["col_scales"], "col scales")

@@ -1,0 +1,164 @@
+"""GPU parity of the quantization kernels against the CPU oracle: bit-exact codes, scales,
+amax and tensor scales, on the same seeded inputs, through the C ABI.
+
+Shapes: the workloads' own shapes (quantize-only [8192, 4096] with 1 % outliers; the
+Llama-3-8B FFN activations and weights; the wgrad output gradient with RHT + SR), small
+shapes that span several tiles with ragged tails, and the degenerate cases (empty
+tensors, all-zero tensors)."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsq
+from synthetic import (SEED_DY, SEED_SIGNS, SEED_SR_KEY, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16,
+                       outlier_bf16, rht_signs)
+from tests.gpu_common import assert_bytes_equal, assert_f32_equal, note
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def check_nvfp4(x_cpu, direction, rounding=0, seed=0, stream=0, signs=None, label=""):
+    import oracle
+    note("nvfp4 %s shape=%s dir=%d rnd=%d rht=%s" % (label, tuple(x_cpu.shape), direction, rounding,
+                                                     signs is not None))
+    x = x_cpu.to(DEV)
+    got = bsq.nvfp4_quantize(x, direction=direction, rounding=rounding, sr_seed=seed, sr_stream=stream,
+                             rht_signs=signs)
+    torch.cuda.synchronize()
+    ref = oracle.nvfp4_quantize(x_cpu, direction=direction, rounding=rounding, sr_seed=seed, sr_stream=stream,
+                                signs=None if signs is None else signs.numpy())
+    for d, key in ((1, "row"), (2, "col")):
+        if direction & d:
+            i = 0 if key == "row" else 1
+            assert_f32_equal(got["amax"][i:i + 1], ref["amax"][i:i + 1], label + " amax " + key)
+            assert_f32_equal(got["s_enc"][i:i + 1], ref["s_enc"][i:i + 1], label + " s_enc " + key)
+            assert_bytes_equal(got[key + "_scales"], ref[key + "_scales"], label + " " + key + "_scales")
+            assert_bytes_equal(got[key + "_codes"], ref[key + "_codes"], label + " " + key + "_codes")
+    return got, ref
+
+
+def check_mxfp8(x_cpu, direction, label=""):
+    import oracle
+    note("mxfp8 %s shape=%s dir=%d" % (label, tuple(x_cpu.shape), direction))
+    got = bsq.mxfp8_quantize(x_cpu.to(DEV), direction=direction)
+    torch.cuda.synchronize()
+    ref = oracle.mxfp8_quantize(x_cpu, direction=direction)
+    for d, key in ((1, "row"), (2, "col")):
+        if direction & d:
+            assert_bytes_equal(got[key + "_scales"], ref[key + "_scales"], label + " " + key + "_scales")
+            assert_bytes_equal(got[key + "_codes"], ref[key + "_codes"], label + " " + key + "_codes")
+
+
+# ----------------------------------------------------------------- small and ragged
+
+@pytest.mark.parametrize("shape", [(128, 256), (256, 128), (272, 144), (16, 16), (48, 400), (528, 16)])
+@pytest.mark.parametrize("direction", [1, 2, 3])
+def test_nvfp4_rne_small(shape, direction):
+    check_nvfp4(outlier_bf16(shape, seed=11, mask_seed=12), direction, label="small")
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (272, 144), (32, 16)])
+@pytest.mark.parametrize("direction", [1, 2, 3])
+def test_nvfp4_rht_sr_small(shape, direction):
+    x = gaussian_bf16(shape, 1e-3, 21)
+    check_nvfp4(x, direction, rounding=1, seed=-1234567890123, stream=3, signs=rht_signs(SEED_SIGNS),
+                label="rht+sr")
+
+
+@pytest.mark.parametrize("rounding,use_rht", [(0, True), (1, False)])
+def test_nvfp4_rht_or_sr_alone(rounding, use_rht):
+    x = gaussian_bf16((512, 384), 1.0, 22)
+    check_nvfp4(x, 3, rounding=rounding, seed=SEED_SR_KEY, stream=0,
+                signs=rht_signs(SEED_SIGNS) if use_rht else None, label="rht-or-sr")
+
+
+def test_nvfp4_col_only_cols_multiple_of_8():
+    """Columnwise-only quantization allows cols % 16 == 8 (a ragged last 8-column chunk)."""
+    check_nvfp4(gaussian_bf16((64, 136), 1.0, 23), 2, label="col-only")
+
+
+def test_nvfp4_row_only_ragged_rows():
+    """Rowwise-only quantization allows any row count (rows beyond a 16-row group)."""
+    check_nvfp4(gaussian_bf16((37, 64), 1.0, 24), 1, label="row-ragged")
+
+
+def test_nvfp4_zero_and_empty():
+    check_nvfp4(torch.zeros((64, 64), dtype=torch.bfloat16), 3, label="zeros")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    got = bsq.nvfp4_quantize(x, direction=3)
+    torch.cuda.synchronize()
+    assert got["amax"].cpu().tolist() == [0.0, 0.0] and got["s_enc"].cpu().tolist() == [1.0, 1.0]
+
+
+def test_nvfp4_extreme_values():
+    """Subnormal bf16, huge values and signed zeros in one tensor."""
+    v = torch.tensor([0.0, -0.0, 1e-40, -1e-39, 3.0e38, -2.5e38, 1.0, -6.0] * 64, dtype=torch.float32)
+    x = v.reshape(32, 16).to(torch.bfloat16)
+    check_nvfp4(x, 3, label="extreme")
+    # with RHT the 16-point sums must stay finite (non-finite values are unsupported)
+    v2 = torch.tensor([0.0, -0.0, 1e-40, -1e-39, 1.0e37, -2.5e36, 1.0, -6.0] * 64, dtype=torch.float32)
+    check_nvfp4(v2.reshape(32, 16).to(torch.bfloat16), 3, rounding=1, seed=5, signs=rht_signs(3),
+                label="extreme-sr")
+
+
+@pytest.mark.parametrize("shape", [(128, 256), (256, 128), (288, 160), (32, 32)])
+@pytest.mark.parametrize("direction", [1, 2, 3])
+def test_mxfp8_small(shape, direction):
+    check_mxfp8(outlier_bf16(shape, seed=31, mask_seed=32), direction, label="small")
+
+
+def test_mxfp8_extreme_and_zero_blocks():
+    v = torch.zeros((64, 64), dtype=torch.float32)
+    v[0, :32] = torch.tensor([1e-40, -3e38] + [0.0] * 30)
+    v[1, 32:] = -0.0
+    v[2:] = torch.randn((62, 64), generator=torch.Generator().manual_seed(1)) * 1e30
+    check_mxfp8(v.to(torch.bfloat16), 3, label="extreme")
+
+
+def test_rht_apply_matches_oracle():
+    import oracle
+    for axis in (0, 1):
+        for shape in [(256, 128), (272, 144), (32, 16)]:
+            x = gaussian_bf16(shape, 1.0, 41)
+            note("rht_apply axis=%d shape=%s" % (axis, shape))
+            got = bsq.rht_apply(x.to(DEV), axis, rht_signs(SEED_SIGNS))
+            torch.cuda.synchronize()
+            assert_f32_equal(got, oracle.rht_apply(x, axis, rht_signs(SEED_SIGNS).numpy()), "rht axis %d" % axis)
+
+
+def test_dequantize_matches_oracle():
+    import oracle
+    x = outlier_bf16((256, 512), seed=51, mask_seed=52)
+    q = bsq.nvfp4_quantize(x.to(DEV), direction=1)
+    note("nvfp4_dequantize [256,512]")
+    d = bsq.nvfp4_dequantize(q["row_codes"], q["row_scales"], q["s_enc"][0:1])
+    torch.cuda.synchronize()
+    ref = oracle.nvfp4_dequantize(q["row_codes"].cpu().numpy(), q["row_scales"].cpu().numpy(),
+                                  float(q["s_enc"][0].item()))
+    assert np.array_equal(d.cpu().view(torch.int16).numpy().view(np.uint16), ref)
+
+
+# ----------------------------------------------------------------- workload shapes
+
+def test_quant_only_workload():
+    """[8192, 4096] N(0,1) with 1 % of entries x100: NVFP4 row + col (RNE) and MXFP8 row + col."""
+    x = outlier_bf16((8192, 4096))
+    check_nvfp4(x, 3, label="quant-only")
+    check_mxfp8(x, 3, label="quant-only")
+
+
+def test_fwd_operands_llama3_8b():
+    """Forward operands of the Llama-3-8B FFN up-projection, NVFP4 rowwise RNE."""
+    check_nvfp4(gaussian_bf16((16384, 4096), 1.0, SEED_X), 1, label="fwd X")
+    check_nvfp4(gaussian_bf16((14336, 4096), STD_W, SEED_W), 1, label="fwd W")
+
+
+def test_wgrad_operands_llama3_8b():
+    """wgrad operands: 16-point RHT along tokens, columnwise NVFP4, Philox SR (streams 0/1)."""
+    signs = rht_signs(SEED_SIGNS)
+    check_nvfp4(gaussian_bf16((16384, 14336), STD_DY, SEED_DY), 2, rounding=1, seed=SEED_SR_KEY, stream=0,
+                signs=signs, label="wgrad dY")
+    check_nvfp4(gaussian_bf16((16384, 4096), 1.0, SEED_X), 2, rounding=1, seed=SEED_SR_KEY, stream=1,
+                signs=signs, label="wgrad X")
