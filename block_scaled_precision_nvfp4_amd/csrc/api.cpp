@@ -125,7 +125,8 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
     if (!c) return fail(BSQ_ERR_NULL, "%s: c is NULL", fn);
     if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return fail(BSQ_ERR_NULL, "%s: operand pointer is NULL", fn);
     if (fmt == BSQ_FMT_NVFP4 && (!a_s_enc || !b_s_enc)) return fail(BSQ_ERR_NULL, "%s: NVFP4 needs both tensor scales", fn);
-    if (misaligned(a_codes) || misaligned(b_codes) || misaligned(c)) return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (misaligned(a_codes) || misaligned(b_codes) || misaligned(c) || misaligned(a_scales) || misaligned(b_scales))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     return launched(bsq::launch_blockscaled_gemm(fmt, M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales,
                                                  b_s_enc, c, c_dtype, hip_stream), fn);
 }
