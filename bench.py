@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     return p.parse_args()
 
 
