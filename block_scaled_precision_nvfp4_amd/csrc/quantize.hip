@@ -201,11 +201,15 @@ __device__ __forceinline__ uint32_t encode_block(const float* v, float bmax, flo
                 }
             }
         } else {
-#pragma unroll
-            for (int j = 0; j < N; ++j) {
-                const uint32_t c = e2m1_encode_rne(v[j] * enc);
-                w[j >> 3] |= c << (4 * (j & 7));
-            }
+            static_for<0, N / 8>([&](auto g_c) {
+                constexpr int g = decltype(g_c)::value;
+                uint32_t x = 0;
+                x = e2m1_pack2_rne<0>(x, v[8 * g + 0] * enc, v[8 * g + 1] * enc);
+                x = e2m1_pack2_rne<1>(x, v[8 * g + 2] * enc, v[8 * g + 3] * enc);
+                x = e2m1_pack2_rne<2>(x, v[8 * g + 4] * enc, v[8 * g + 5] * enc);
+                x = e2m1_pack2_rne<3>(x, v[8 * g + 6] * enc, v[8 * g + 7] * enc);
+                w[g] = x;
+            });
         }
     }
     return sb;
@@ -451,6 +455,189 @@ __global__ __launch_bounds__(NTHREADS) void rht_kernel(const uint16_t* __restric
     }
 }
 
+// ------------------------------------------------------------------ linear (rowwise) kernels
+//
+// Rowwise quantization never crosses a row (cols is a multiple of the block size), so the
+// tensor is a flat array of blocks: block b covers elements [16b, 16b + 16) (NVFP4) or
+// [32b, 32b + 32) (MXFP8), its codes and scale sit at linear offsets in the row-major
+// outputs, and the SR index of an element is its linear index.  These kernels stream the
+// tensor with grid-stride loops: lane u of a sweep owns the 16-byte unit u (8 values),
+// every wave-wide load is 1 KB contiguous, and UNITS independent loads per lane are in
+// flight.  They reach the HBM streaming rate where the 256 x 128 tile kernels (needed for
+// columnwise blocks) do not.
+
+constexpr int LIN_UNITS = 8;                 // 16-byte units per lane per sweep
+constexpr int LIN_THREADS = 256;
+constexpr int LIN_MAX_BLOCKS = 256 * 8;      // a few workgroups per CU
+
+__device__ __forceinline__ void lin_range(int64_t n16, int64_t& first, int64_t& stride) {
+    first = (int64_t)blockIdx.x * LIN_THREADS * LIN_UNITS + threadIdx.x;
+    stride = (int64_t)gridDim.x * LIN_THREADS * LIN_UNITS;
+    (void)n16;
+}
+
+// Plain tensor amax (both slots): max |x| over n16 16-byte units.
+template <int DIRS>
+__global__ __launch_bounds__(LIN_THREADS) void amax_linear_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                  float* __restrict__ amax) {
+    int64_t first, stride;
+    lin_range(n16, first, stride);
+    float m = 0.0f;
+    for (int64_t base = first; base < n16; base += stride) {
+        uint4 q[LIN_UNITS];
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            float v[8];
+            unpack_bf16x8(q[k], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        }
+    }
+    __shared__ float red[LIN_THREADS / 64];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0];
+#pragma unroll
+        for (int w = 1; w < LIN_THREADS / 64; ++w) a = __builtin_fmaxf(a, red[w]);
+        if (DIRS & 1) atomic_max_nonneg(amax + 0, a);
+        if (DIRS & 2) atomic_max_nonneg(amax + 1, a);
+    }
+}
+
+// Row-RHT amax: the 16-point transform of each block, the block held by a lane pair.
+__global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                          const int8_t* __restrict__ signs,
+                                                                          float* __restrict__ amax) {
+    int64_t first, stride;
+    lin_range(n16, first, stride);
+    const uint32_t neg = sign_mask16(signs);
+    const bool upper = (threadIdx.x & 1) != 0;
+    float m = 0.0f;
+    for (int64_t base = first; base < n16; base += stride) {
+        uint4 q[LIN_UNITS];
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            float v[8];
+            unpack_bf16x8(q[k], v);
+            rht16_pair(v, neg, upper);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        }
+    }
+    __shared__ float red[LIN_THREADS / 64];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0];
+#pragma unroll
+        for (int w = 1; w < LIN_THREADS / 64; ++w) a = __builtin_fmaxf(a, red[w]);
+        atomic_max_nonneg(amax + 0, a);
+    }
+}
+
+// Rowwise NVFP4 encode: unit u = half u%2 of block u/2.
+template <bool RHT, bool SR>
+__global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                       const int8_t* __restrict__ signs,
+                                                                       uint32_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales,
+                                                                       const float* __restrict__ amax,
+                                                                       float* __restrict__ s_enc_out, uint64_t seed,
+                                                                       uint32_t stream) {
+    int64_t first, stride;
+    lin_range(n16, first, stride);
+    const float S = nvfp4_tensor_scale(amax[0]);
+    if (blockIdx.x == 0 && threadIdx.x == 0) s_enc_out[0] = S;
+    const uint32_t neg = RHT ? sign_mask16(signs) : 0u;
+    const bool upper = (threadIdx.x & 1) != 0;
+    for (int64_t base = first; base < n16; base += stride) {
+        uint4 q[LIN_UNITS];
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            float v[8];
+            unpack_bf16x8(q[k], v);
+            if (RHT) rht16_pair(v, neg, upper);
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            uint32_t w;
+            const uint32_t sb = encode_block<8, SR>(v, m, S, (uint64_t)u * 8u, seed, stream, 0u, &w);
+            if (u < n16) {
+                codes[u] = w;
+                if (!upper) scales[u >> 1] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+// Rowwise MXFP8 cast: unit u = quarter u%4 of block u/4.
+__global__ __launch_bounds__(LIN_THREADS) void mxfp8_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                       uint2* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales) {
+    int64_t first, stride;
+    lin_range(n16, first, stride);
+    for (int64_t base = first; base < n16; base += stride) {
+        uint4 q[LIN_UNITS];
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            float v[8];
+            unpack_bf16x8(q[k], v);
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 2));
+            uint32_t lo = 0, hi = 0, sb = 0;
+            if (m != 0.0f) {
+                sb = mx_scale_byte(m);
+                const float inv = mx_inv_scale(sb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lo |= e4m3_encode(v[e] * inv) << (8 * e);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hi |= e4m3_encode(v[4 + e] * inv) << (8 * e);
+            }
+            if (u < n16) {
+                codes[u] = make_uint2(lo, hi);
+                if ((u & 3) == 0) scales[u >> 2] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+static inline unsigned lin_grid(int64_t n16) {
+    const int64_t per = (int64_t)LIN_THREADS * LIN_UNITS;
+    int64_t g = (n16 + per - 1) / per;
+    if (g > LIN_MAX_BLOCKS) g = LIN_MAX_BLOCKS;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline dim3 tile_grid(int64_t R, int64_t C) {
@@ -493,8 +680,35 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
                    amax, s_enc, seed, stream};
     const dim3 g = tile_grid(R, C);
     const bool rht = signs != nullptr, sr = rounding == 1;
-    if (direction == 1) launch_nv_dirs<1>(a, rht, sr, g, s);
-    else if (direction == 2) launch_nv_dirs<2>(a, rht, sr, g, s);
+    const int64_t n16 = R * C / 8;
+    const uint4* xv = (const uint4*)x;
+    const unsigned lg = lin_grid(n16);
+    if (direction == 1) {
+        // rowwise only: two streaming passes
+        if (rht) hipLaunchKernelGGL(amax_rht_row_linear_kernel, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, amax);
+        else hipLaunchKernelGGL(amax_linear_kernel<1>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, amax);
+        uint32_t* rc = (uint32_t*)row_codes;
+        if (rht && sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
+        else if (rht) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
+        else if (sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
+        else hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
+        return (int)hipGetLastError();
+    }
+    // columnwise (alone or with rowwise): the 256 x 128 tile kernels; without RHT the
+    // amax pass is the streaming one
+    if (!rht) {
+        if (direction == 2) hipLaunchKernelGGL(amax_linear_kernel<2>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, amax);
+        else hipLaunchKernelGGL(amax_linear_kernel<3>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, amax);
+        if (direction == 2) {
+            if (sr) hipLaunchKernelGGL((nvfp4_encode_kernel<2, false, true>), g, dim3(NTHREADS), 0, s, a);
+            else hipLaunchKernelGGL((nvfp4_encode_kernel<2, false, false>), g, dim3(NTHREADS), 0, s, a);
+        } else {
+            if (sr) hipLaunchKernelGGL((nvfp4_encode_kernel<3, false, true>), g, dim3(NTHREADS), 0, s, a);
+            else hipLaunchKernelGGL((nvfp4_encode_kernel<3, false, false>), g, dim3(NTHREADS), 0, s, a);
+        }
+        return (int)hipGetLastError();
+    }
+    if (direction == 2) launch_nv_dirs<2>(a, rht, sr, g, s);
     else launch_nv_dirs<3>(a, rht, sr, g, s);
     return (int)hipGetLastError();
 }
@@ -505,8 +719,11 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
     hipStream_t s = (hipStream_t)hip_stream;
     MxArgs a{(const uint16_t*)x, R, C, row_codes, row_scales, col_codes, col_scales};
     const dim3 g = tile_grid(R, C);
-    if (direction == 1) hipLaunchKernelGGL(mxfp8_kernel<1>, g, dim3(NTHREADS), 0, s, a);
-    else if (direction == 2) hipLaunchKernelGGL(mxfp8_kernel<2>, g, dim3(NTHREADS), 0, s, a);
+    if (direction == 1) {
+        const int64_t n16 = R * C / 8;
+        hipLaunchKernelGGL(mxfp8_row_linear_kernel, dim3(lin_grid(n16)), dim3(LIN_THREADS), 0, s, (const uint4*)x, n16,
+                           (uint2*)row_codes, row_scales);
+    } else if (direction == 2) hipLaunchKernelGGL(mxfp8_kernel<2>, g, dim3(NTHREADS), 0, s, a);
     else hipLaunchKernelGGL(mxfp8_kernel<3>, g, dim3(NTHREADS), 0, s, a);
     return (int)hipGetLastError();
 }
