@@ -67,10 +67,13 @@ struct Fmt {
     // waves per workgroup and MFMA tiles per wave: NVFP4 runs 8 waves (two per SIMD) of
     // 128 x 64 so that one wave's dequantization overlaps the other's MFMAs; MXFP8 (no
     // dequantization) runs 4 waves of 128 x 128.
-    static constexpr int NW = FMT == 0 ? 8 : 4;
+#ifndef BSQ_MX_WAVES
+#define BSQ_MX_WAVES 4
+#endif
+    static constexpr int NW = FMT == 0 ? 8 : BSQ_MX_WAVES;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int TM = 4;                 // 32-row A fragments per wave
-    static constexpr int TN = FMT == 0 ? 2 : 4;  // 32-row B fragments per wave
+    static constexpr int TM = 4;                             // 32-row A fragments per wave
+    static constexpr int TN = FMT == 0 ? 2 : (NW == 8 ? 2 : 4);   // 32-row B fragments per wave
     static constexpr int WAVES_N = GBN / (32 * TN);
 };
 
@@ -78,6 +81,12 @@ struct Fmt {
 // row was the fastest placement measured for the fragment reads (32 consecutive rows, one
 // chunk per lane half): about 110 B/clk/CU against 90 for bits 1..2 and 55 unswizzled.
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 3) & 3)) << 4); }
+
+// MXFP8 LDS scale byte of row r (0..255), K-block kb (0..1) of the slice:
+// [half r/128][block][row mod 32][fragment (r/32) mod 4].
+__device__ __forceinline__ int mx_sidx(int r, int kb) {
+    return (((r >> 7) * 2 + kb) << 7) + ((r & 31) << 2) + ((r >> 5) & 3);
+}
 
 // Byte offset of scale dword w (0..1) of LDS scale row r (NVFP4: 8 raw E4M3 bytes per row,
 // the two dwords swapped on rows with bit 4 set so that 32 consecutive rows reading the
@@ -199,7 +208,10 @@ __device__ __forceinline__ void stage_store(uint8_t* buf, const Stage& st) {
             const bool sw = ((r >> 4) & 1) != 0;
             *(uint2*)(ss + r * 8) = sw ? make_uint2(w1, w0) : make_uint2(w0, w1);
         } else {
-            *(uint32_t*)(ss + r * F::SCB) = w0;
+            // MXFP8: the 4 scale bytes a lane needs for its 4 fragments (rows r, r+32, r+64,
+            // r+96 of a 128-row half, one K-block) are adjacent, so one dword read fetches them
+            ss[mx_sidx(r, 0)] = (uint8_t)(w0 & 0xFF);
+            ss[mx_sidx(r, 1)] = (uint8_t)((w0 >> 8) & 0xFF);
         }
     }
 }
@@ -293,9 +305,11 @@ __device__ __forceinline__ void nv_interleave() {
 
 // ---------------------------------------------------------------- MXFP8 slice
 
+constexpr int MXTN = Fmt<1>::TN;   // B fragments per MXFP8 wave
+
 struct MxFrag {
-    intx8 a[4], b[4];
-    int as[4], bs[4];
+    intx8 a[4], b[MXTN];
+    uint32_t as, bs;   // byte i: scale of fragment i (K-block of the lane half)
 };
 
 // Lane (row, g) of fragment i: K elements 16g..16g+15 (chunk g) and 32+16g.. (chunk 2+g) of the
@@ -313,25 +327,39 @@ __device__ __forceinline__ void mx_read(const uint8_t* buf, int wm, int wn, int 
         const uint4 lo = *(const uint4*)(sA + swz(r, kh));
         const uint4 hi = *(const uint4*)(sA + swz(r, 2 + kh));
         f.a[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        f.as[i] = sAs[r * F::SCB + kh];
     }
+    f.as = *(const uint32_t*)(sAs + mx_sidx(wm + frow, kh));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < MXTN; ++j) {
         const int r = wn + 32 * j + frow;
         const uint4 lo = *(const uint4*)(sB + swz(r, kh));
         const uint4 hi = *(const uint4*)(sB + swz(r, 2 + kh));
         f.b[j] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        f.bs[j] = sBs[r * F::SCB + kh];
     }
+    f.bs = *(const uint32_t*)(sBs + mx_sidx(wn + frow, kh));
 }
 
-__device__ __forceinline__ void mx_mfma16(const MxFrag& f, floatx16 (&acc)[4][4]) {
+__device__ __forceinline__ void mx_mfma16(const MxFrag& f, floatx16 (&acc)[4][MXTN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.as[i], 0,
-                                                                         f.bs[j]);
+        for (int j = 0; j < MXTN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
+                                                                         (int)((f.as >> (8 * i)) & 0xFF), 0,
+                                                                         (int)((f.bs >> (8 * j)) & 0xFF));
+}
+
+// Scheduling hint for one MXFP8 slice: 2 MFMAs on the current operands first (so the wait for
+// them does not also wait for the new reads), then the next slice's 18 LDS reads spread
+// between the remaining MFMAs.
+__device__ __forceinline__ void mx_interleave() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
 }
 
 // Output tile of this workgroup.  Workgroup ids are dealt to the 8 XCDs round-robin; the
@@ -443,8 +471,11 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
             if (kt > 0) __syncthreads();
             if (kt + 2 < nk) stage_store<FMT>(lds + (int)((kt + 2) % F::NSTAGE) * F::STAGE, st);
             if (kt + 3 < nk) stage_load<FMT>(g, ops, (kt + 3) * F::BK, st);
-            if (kt + 1 < nk) mx_read(lds + (int)((kt + 1) % F::NSTAGE) * F::STAGE, wm, wn, lane, fn);
+            // unconditional so the reads share a scheduling region with the MFMAs; after the
+            // last slice they read a stale (but in-bounds) buffer whose values go unused
             mx_mfma16(fc, acc);
+            mx_read(lds + (int)((kt + 1) % F::NSTAGE) * F::STAGE, wm, wn, lane, fn);
+            mx_interleave();
         };
         for (int64_t kt = 0; kt < nk; kt += 2) {
             iter(kt, f0, f1);
