@@ -14,11 +14,18 @@ the NVFP4 quantize GB/s and the NVFP4 GEMM TFLOP/s of the forward pass, the roof
 the dominant kernel (the NVFP4 GEMM) timed with HIP events on its own stream, and the CPU
 oracle timed on a token-sample of the same step.
 
+The roofline's `traffic` (HBM bytes per launch of the forward NVFP4 GEMM) comes from a
+hardware-counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by the
+ratio the same counter shows for a plain copy of known size, which `--copy-calibration`
+runs); it is reported only while the GEMM sources still hash to the values recorded there.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration      (a 1 GiB device-to-device copy, for the counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,7 +52,56 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    p.add_argument("--copy-calibration", action="store_true")
     return p.parse_args()
+
+
+GEMM_SOURCES = ("block_scaled_precision_nvfp4_amd/csrc/gemm.hip",
+                "block_scaled_precision_nvfp4_amd/csrc/device_common.hpp")
+TRAFFIC_SUMMARY = "profiles/gemm_nvfp4_fwd_llama3_8b_hbm_traffic.md"
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward NVFP4 GEMM from the committed counter summary,
+    or None when the summary is absent or was taken on different GEMM sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+    if rec is None or rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec
+
+
+def copy_calibration(iters: int = 5):
+    """A plain device-to-device copy of 1 GiB, the known-size kernel the HBM counters are
+    scaled by (the copy reads 1 GiB and writes 1 GiB per launch)."""
+    import torch
+    n = 1 << 29   # bf16 elements = 1 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    print(json.dumps({"copy_bytes_each_way": 2 * n, "launches": iters, "ms": round(ms, 4),
+                      "GBps_read_plus_write": round(4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 class Step:
@@ -143,6 +199,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import block_scaled_precision_nvfp4_amd as bsq
     bsq.lib()
     dev = torch.device("cuda:0")
@@ -167,8 +226,13 @@ def main():
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
+    tr = measured_traffic()
+    # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
+    algo_bytes = (M_TOK + N_OUT) * K_IN * (0.5 + 1.0 / 16) + 2.0 * M_TOK * N_OUT
     roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fwd_tflops / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(fwd_tflops / F16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": None if tr is None else tr["traffic_bytes"],
+                "algorithmic_bytes": int(algo_bytes),
                 "kernel": "gemm_nvfp4 (fwd, f16 MFMA with in-register dequant)"}
     line = {
         "metric": "NVFP4 quant GB/s + block-scaled GEMM TFLOP/s at Llama-3-8B FFN shape",
