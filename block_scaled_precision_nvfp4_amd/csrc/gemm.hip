@@ -60,20 +60,18 @@ struct Fmt {
     static constexpr int EPB = FMT == 0 ? 2 : 1;      // elements per code byte
     static constexpr int BLK = FMT == 0 ? 16 : 32;    // elements per scale
     static constexpr int SPR = BK / BLK;              // scale bytes per row per slice (8 or 2)
-    static constexpr int SCB = FMT == 0 ? 8 : 4;      // LDS bytes per row for scales (raw bytes)
+    static constexpr int SCB = 8;                     // LDS bytes per row for scales
+    // NVFP4: 8 raw scale bytes per row; MXFP8: one dword slot per (row, K-block), 2 per row
     static constexpr int STAGE = (GBM + GBN) * (ROWB + SCB);
-    static constexpr int NSTAGE = 3;
+    static constexpr int NSTAGE = FMT == 0 ? 3 : 4;
     static constexpr int LDS = NSTAGE * STAGE;
     // waves per workgroup and MFMA tiles per wave: NVFP4 runs 8 waves (two per SIMD) of
     // 128 x 64 so that one wave's dequantization overlaps the other's MFMAs; MXFP8 (no
     // dequantization) runs 4 waves of 128 x 128.
-#ifndef BSQ_MX_WAVES
-#define BSQ_MX_WAVES 4
-#endif
-    static constexpr int NW = FMT == 0 ? 8 : BSQ_MX_WAVES;
+    static constexpr int NW = FMT == 0 ? 8 : 4;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int TM = 4;                             // 32-row A fragments per wave
-    static constexpr int TN = FMT == 0 ? 2 : (NW == 8 ? 2 : 4);   // 32-row B fragments per wave
+    static constexpr int TM = 4;                  // 32-row A fragments per wave
+    static constexpr int TN = FMT == 0 ? 2 : 4;   // 32-row B fragments per wave
     static constexpr int WAVES_N = GBN / (32 * TN);
 };
 
@@ -81,12 +79,6 @@ struct Fmt {
 // row was the fastest placement measured for the fragment reads (32 consecutive rows, one
 // chunk per lane half): about 110 B/clk/CU against 90 for bits 1..2 and 55 unswizzled.
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 3) & 3)) << 4); }
-
-// MXFP8 LDS scale byte of row r (0..255), K-block kb (0..1) of the slice:
-// [half r/128][block][row mod 32][fragment (r/32) mod 4].
-__device__ __forceinline__ int mx_sidx(int r, int kb) {
-    return (((r >> 7) * 2 + kb) << 7) + ((r & 31) << 2) + ((r >> 5) & 3);
-}
 
 // Byte offset of scale dword w (0..1) of LDS scale row r (NVFP4: 8 raw E4M3 bytes per row,
 // the two dwords swapped on rows with bit 4 set so that 32 consecutive rows reading the
@@ -204,15 +196,8 @@ __device__ __forceinline__ void stage_store(uint8_t* buf, const Stage& st) {
     for (int h = 0; h < RPT; ++h) {
         const int r = rr + HT * h;
         const uint32_t w0 = st.s[h][0], w1 = st.s[h][1];
-        if (FMT == 0) {
-            const bool sw = ((r >> 4) & 1) != 0;
-            *(uint2*)(ss + r * 8) = sw ? make_uint2(w1, w0) : make_uint2(w0, w1);
-        } else {
-            // MXFP8: the 4 scale bytes a lane needs for its 4 fragments (rows r, r+32, r+64,
-            // r+96 of a 128-row half, one K-block) are adjacent, so one dword read fetches them
-            ss[mx_sidx(r, 0)] = (uint8_t)(w0 & 0xFF);
-            ss[mx_sidx(r, 1)] = (uint8_t)((w0 >> 8) & 0xFF);
-        }
+        const bool sw = ((r >> 4) & 1) != 0;
+        *(uint2*)(ss + r * 8) = sw ? make_uint2(w1, w0) : make_uint2(w0, w1);
     }
 }
 
@@ -309,17 +294,23 @@ constexpr int MXTN = Fmt<1>::TN;   // B fragments per MXFP8 wave
 
 struct MxFrag {
     intx8 a[4], b[MXTN];
-    uint32_t as, bs;   // byte i: scale of fragment i (K-block of the lane half)
+    uint32_t as[4], bs[MXTN];   // byte 0: E8M0 scale of the fragment row's K-block (lane half)
 };
 
+// MXFP8 LDS stage: A codes [256][64 B] and B codes [256][64 B], 16-byte chunks swizzled by
+// swz(); then the scale slots of A and of B, one dword per (row, K-block) at 2*row + block,
+// whose byte 0 holds the E8M0 byte (the LDS DMA of a byte fills one dword slot per lane).
+constexpr int MX_SCALES = 2 * GBM * ROWB;
+constexpr int MX_STAGE = MX_SCALES + 2 * GBM * 2 * 4;
+static_assert(MX_STAGE == Fmt<1>::STAGE, "MXFP8 stage layout");
+
 // Lane (row, g) of fragment i: K elements 16g..16g+15 (chunk g) and 32+16g.. (chunk 2+g) of the
-// slice, and the E8M0 byte of K-block g.
+// slice, and the scale slot of K-block g.
 __device__ __forceinline__ void mx_read(const uint8_t* buf, int wm, int wn, int lane, MxFrag& f) {
-    using F = Fmt<1>;
     const uint8_t* sA = buf;
     const uint8_t* sB = buf + GBM * ROWB;
-    const uint8_t* sAs = buf + (GBM + GBN) * ROWB;
-    const uint8_t* sBs = sAs + GBM * F::SCB;
+    const uint32_t* sAs = (const uint32_t*)(buf + MX_SCALES);
+    const uint32_t* sBs = sAs + 2 * GBM;
     const int frow = lane & 31, kh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -327,16 +318,16 @@ __device__ __forceinline__ void mx_read(const uint8_t* buf, int wm, int wn, int 
         const uint4 lo = *(const uint4*)(sA + swz(r, kh));
         const uint4 hi = *(const uint4*)(sA + swz(r, 2 + kh));
         f.a[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        f.as[i] = sAs[2 * r + kh];
     }
-    f.as = *(const uint32_t*)(sAs + mx_sidx(wm + frow, kh));
 #pragma unroll
     for (int j = 0; j < MXTN; ++j) {
         const int r = wn + 32 * j + frow;
         const uint4 lo = *(const uint4*)(sB + swz(r, kh));
         const uint4 hi = *(const uint4*)(sB + swz(r, 2 + kh));
         f.b[j] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        f.bs[j] = sBs[2 * r + kh];
     }
-    f.bs = *(const uint32_t*)(sBs + mx_sidx(wn + frow, kh));
 }
 
 __device__ __forceinline__ void mx_mfma16(const MxFrag& f, floatx16 (&acc)[4][MXTN]) {
@@ -344,22 +335,130 @@ __device__ __forceinline__ void mx_mfma16(const MxFrag& f, floatx16 (&acc)[4][MX
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < MXTN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
-                                                                         (int)((f.as >> (8 * i)) & 0xFF), 0,
-                                                                         (int)((f.bs >> (8 * j)) & 0xFF));
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, (int)f.as[i],
+                                                                         0, (int)f.bs[j]);
 }
 
-// Scheduling hint for one MXFP8 slice: 2 MFMAs on the current operands first (so the wait for
-// them does not also wait for the new reads), then the next slice's 18 LDS reads spread
-// between the remaining MFMAs.
+// LDS DMA: a buffer load whose data goes straight to LDS.  A wave-wide DMA writes 64
+// consecutive LDS slots starting at the wave-uniform address in M0 -- 16 bytes per lane for
+// dwordx4, one dword slot per lane for a byte (the byte in its low 8 bits).  The loads are
+// issued as inline assembly so that the compiler does not track them: the loop waits for them
+// itself with s_waitcnt vmcnt (which only ever makes the compiler's own waits stricter), and
+// the compiler does not serialise every LDS read behind every DMA in flight.
+typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+
+struct RsrcWords {
+    u32x4s a, b, as, bs;
+};
+
+__device__ __forceinline__ u32x4s rsrc_words(const uint8_t* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+    const uint64_t a = (uint64_t)base;
+    return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)n, (uint32_t)RSRC_FLAGS};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void dma_b128(const u32x4s& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
+__device__ __forceinline__ void dma_u8(const u32x4s& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
+// Waits until at most N of this wave's vector-memory operations are in flight, then joins the
+// workgroup barrier.  The memory clobber keeps the compiler from moving LDS accesses across.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// DMA of one MXFP8 K slice starting at element k0 into stage buffer buf.  The chunk swizzle
+// is applied on the global side: the lane that fills LDS chunk slot cs of row r fetches
+// global chunk cs ^ ((r >> 3) & 3).  Scale slot (row r, K-block kb) is dword 2r + kb of the
+// operand's slot array.  Per lane: 8 code DMAs and 4 scale DMAs.
+constexpr int MX_DMA_PER_SLICE = 12;
+
+__device__ __forceinline__ void mx_dma(const GemmArgs& g, const RsrcWords& o, int64_t k0, uint8_t* buf) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t rowbytes = (uint32_t)g.K;
+    const bool tail = k0 + 64 > g.K;   // uniform
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r0 = 64 * p + 16 * wave;   // first row of this wave's 1 KiB piece
+        const int r = r0 + (lane >> 2), c = (lane & 3) ^ ((r >> 3) & 3);
+        uint32_t off = (uint32_t)r * rowbytes + 16u * c;
+        if (tail && k0 + 16 * c >= g.K) off = OOB;
+        dma_b128(o.a, lds_addr(buf + r0 * ROWB), off, (uint32_t)k0);
+        dma_b128(o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off, (uint32_t)k0);
+    }
+    const uint32_t sstride = (uint32_t)(g.K / 32);
+    const int64_t kb0 = k0 / 32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int s0 = 256 * p + 64 * wave;  // first slot of this wave's piece
+        const int sl = s0 + lane, r = sl >> 1, kb = sl & 1;
+        const uint32_t off = (kb0 + kb < (int64_t)sstride) ? (uint32_t)r * sstride + kb : OOB;
+        dma_u8(o.as, lds_addr(buf + MX_SCALES + 4 * s0), off, (uint32_t)kb0);
+        dma_u8(o.bs, lds_addr(buf + MX_SCALES + 8 * GBM + 4 * s0), off, (uint32_t)kb0);
+    }
+}
+
+// Scheduling hint for one MXFP8 slice: 2 MFMAs on the current operands first, then the next
+// slice's 24 LDS reads (16 code, 8 scale) spread between the remaining MFMAs.
 __device__ __forceinline__ void mx_interleave() {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
+    for (int i = 0; i < 12; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
+// MXFP8 main loop over K slices with 4 LDS stage buffers.  At the top of slice kt each wave
+// waits for its own DMAs of slice kt+1 (issued two slices earlier; only those of slice kt+2
+// may still be in flight), then a barrier publishes slice kt+1 to the workgroup and confirms
+// that every wave has consumed slice kt-1, whose buffer then receives the DMA of slice kt+3.
+// The fragments of slice kt+1 are read while slice kt's 16 MFMAs issue; the loop is unrolled
+// by two so that the two fragment register sets alternate without copies.
+__device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
+                                             int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
+    constexpr int D = MX_DMA_PER_SLICE;
+    if (nk <= 0) return;
+    RsrcWords o;
+    o.a = rsrc_words(g.a_codes + m0 * g.K, (g.M - m0) * g.K);
+    o.b = rsrc_words(g.b_codes + n0 * g.K, (g.N - n0) * g.K);
+    o.as = rsrc_words(g.a_scales + m0 * (g.K / 32), (g.M - m0) * (g.K / 32));
+    o.bs = rsrc_words(g.b_scales + n0 * (g.K / 32), (g.N - n0) * (g.K / 32));
+    auto buf = [&](int64_t k) { return lds + (int)(k & 3) * MX_STAGE; };
+    mx_dma(g, o, 0, buf(0));
+    if (nk > 1) mx_dma(g, o, 64, buf(1));
+    if (nk > 2) mx_dma(g, o, 128, buf(2));
+    if (nk > 2) wait_vm_barrier<2 * D>();
+    else if (nk > 1) wait_vm_barrier<D>();
+    else wait_vm_barrier<0>();
+    MxFrag f0, f1;
+    mx_read(buf(0), wm, wn, lane, f0);
+    auto iter = [&](int64_t kt, const MxFrag& fc, MxFrag& fn) {
+        if (kt + 2 < nk) wait_vm_barrier<D>();
+        else wait_vm_barrier<0>();
+        if (kt + 3 < nk) mx_dma(g, o, (kt + 3) * 64, buf(kt + 3));
+        // the reads after the last slice touch a stale (in-bounds) buffer and go unused
+        mx_mfma16(fc, acc);
+        mx_read(buf(kt + 1), wm, wn, lane, fn);
+        mx_interleave();
+    };
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+        iter(kt, f0, f1);
+        if (kt + 1 < nk) iter(kt + 1, f1, f0);
+    }
 }
 
 // Output tile of this workgroup.  Workgroup ids are dealt to the 8 XCDs round-robin; the
@@ -400,24 +499,24 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
 
     const int64_t nk = (g.K + F::BK - 1) / F::BK;
     const int frow = lane & 31, kh = lane >> 5;
-    // Pipeline over K slices with NSTAGE = 3 LDS buffers.  At the top of iteration kt a
-    // barrier makes slice kt+1 (stored during iteration kt-1) visible and guarantees that
-    // every wave is done with slice kt-1; the staged registers of slice kt+2 then go to
-    // slice kt-1's buffer and the global loads of slice kt+3 are issued, two iterations
-    // ahead of their use.
     const Operands ops = make_operands<FMT>(g, m0, n0);
-    Stage st;
-    if (nk > 0) {
-        stage_load<FMT>(g, ops, 0, st);
-        stage_store<FMT>(lds, st);
-        if (nk > 1) {
-            stage_load<FMT>(g, ops, F::BK, st);
-            stage_store<FMT>(lds + F::STAGE, st);
-        }
-        if (nk > 2) stage_load<FMT>(g, ops, 2 * F::BK, st);
-        __syncthreads();
-    }
     if constexpr (FMT == 0) {
+        // NVFP4 pipeline over K slices with NSTAGE = 3 LDS buffers.  At the top of iteration kt
+        // a barrier makes slice kt+1 (stored during iteration kt-1) visible and guarantees that
+        // every wave is done with slice kt-1; the staged registers of slice kt+2 then go to
+        // slice kt-1's buffer and the global loads of slice kt+3 are issued, two iterations
+        // ahead of their use.
+        Stage st;
+        if (nk > 0) {
+            stage_load<FMT>(g, ops, 0, st);
+            stage_store<FMT>(lds, st);
+            if (nk > 1) {
+                stage_load<FMT>(g, ops, F::BK, st);
+                stage_store<FMT>(lds + F::STAGE, st);
+            }
+            if (nk > 2) stage_load<FMT>(g, ops, 2 * F::BK, st);
+            __syncthreads();
+        }
         // NVFP4 software pipeline, one MFMA step (16 MFMAs of K = 16) at a time: while step s
         // issues its MFMAs, the code words of step s+1 are read from LDS and dequantized into
         // the next operand set.  The last step of a slice reads and dequantizes step 0 of the
@@ -462,25 +561,7 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
             for (int j = 0; j < NVTN; ++j) sb[j] = sbn[j];
         }
     } else {
-        // MXFP8: the fragments of slice kt+1 (visible since the barrier at the top of slice kt)
-        // are read into the second register set while slice kt's 16 MFMAs issue; the loop is
-        // unrolled by two so that the sets alternate without copies.
-        MxFrag f0, f1;
-        if (nk > 0) mx_read(lds, wm, wn, lane, f0);
-        auto iter = [&](int64_t kt, const MxFrag& fc, MxFrag& fn) {
-            if (kt > 0) __syncthreads();
-            if (kt + 2 < nk) stage_store<FMT>(lds + (int)((kt + 2) % F::NSTAGE) * F::STAGE, st);
-            if (kt + 3 < nk) stage_load<FMT>(g, ops, (kt + 3) * F::BK, st);
-            // unconditional so the reads share a scheduling region with the MFMAs; after the
-            // last slice they read a stale (but in-bounds) buffer whose values go unused
-            mx_mfma16(fc, acc);
-            mx_read(lds + (int)((kt + 1) % F::NSTAGE) * F::STAGE, wm, wn, lane, fn);
-            mx_interleave();
-        };
-        for (int64_t kt = 0; kt < nk; kt += 2) {
-            iter(kt, f0, f1);
-            if (kt + 1 < nk) iter(kt + 1, f1, f0);
-        }
+        mx_main_loop(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
 
     float alpha = 1.0f;
