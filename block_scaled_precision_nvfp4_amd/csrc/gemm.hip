@@ -291,53 +291,27 @@ __device__ __forceinline__ void nv_interleave() {
 // ---------------------------------------------------------------- MXFP8 slice
 
 constexpr int MXTN = Fmt<1>::TN;   // B fragments per MXFP8 wave
+static_assert(MXTN == 4 && Fmt<1>::NW == 4, "the MXFP8 slice is written for 4 waves of 4 x 4 tiles");
 
 struct MxFrag {
     intx8 a[4], b[MXTN];
-    uint32_t as[4], bs[MXTN];   // byte 0: E8M0 scale of the fragment row's K-block (lane half)
+    uint32_t as[4], bs[MXTN];   // low byte: E8M0 scale of the fragment row's K-block (lane half)
 };
 
-// MXFP8 LDS stage: A codes [256][64 B] and B codes [256][64 B], 16-byte chunks swizzled by
-// swz(); then the scale slots of A and of B, one dword per (row, K-block) at 2*row + block,
-// whose byte 0 holds the E8M0 byte (the LDS DMA of a byte fills one dword slot per lane).
-constexpr int MX_SCALES = 2 * GBM * ROWB;
-constexpr int MX_STAGE = MX_SCALES + 2 * GBM * 2 * 4;
-static_assert(MX_STAGE == Fmt<1>::STAGE, "MXFP8 stage layout");
-
-// Lane (row, g) of fragment i: K elements 16g..16g+15 (chunk g) and 32+16g.. (chunk 2+g) of the
-// slice, and the scale slot of K-block g.
-__device__ __forceinline__ void mx_read(const uint8_t* buf, int wm, int wn, int lane, MxFrag& f) {
-    const uint8_t* sA = buf;
-    const uint8_t* sB = buf + GBM * ROWB;
-    const uint32_t* sAs = (const uint32_t*)(buf + MX_SCALES);
-    const uint32_t* sBs = sAs + 2 * GBM;
-    const int frow = lane & 31, kh = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wm + 32 * i + frow;
-        const uint4 lo = *(const uint4*)(sA + swz(r, kh));
-        const uint4 hi = *(const uint4*)(sA + swz(r, 2 + kh));
-        f.a[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        f.as[i] = sAs[2 * r + kh];
-    }
-#pragma unroll
-    for (int j = 0; j < MXTN; ++j) {
-        const int r = wn + 32 * j + frow;
-        const uint4 lo = *(const uint4*)(sB + swz(r, kh));
-        const uint4 hi = *(const uint4*)(sB + swz(r, 2 + kh));
-        f.b[j] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        f.bs[j] = sBs[2 * r + kh];
-    }
-}
-
-__device__ __forceinline__ void mx_mfma16(const MxFrag& f, floatx16 (&acc)[4][MXTN]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < MXTN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, (int)f.as[i],
-                                                                         0, (int)f.bs[j]);
-}
+// MXFP8 LDS layout.  A code stage (one K slice) is A codes [256][64 B] then B codes
+// [256][64 B], the 16-byte chunks swizzled by swz().  Scales use one of two layouts:
+//  - grouped (K a multiple of 512): the scale bytes of 8 consecutive slices (16 K-blocks) of
+//    a row form one aligned 16-byte global record, fetched with one DMA lane per row every 8
+//    slices into a double-buffered region [group parity][operand][256 rows][16 B] after the
+//    4 code stages;
+//  - per slice (any other K): one dword slot per (row, K-block) after the codes of each
+//    stage, [operand][256 rows][2 slots], holding the byte in its low 8 bits (a byte DMA
+//    fills one dword slot per lane).
+constexpr int MX_CODES = 2 * GBM * ROWB;                  // 32 KiB
+constexpr int MX_STAGE_SLOTS = MX_CODES + 2 * GBM * 2 * 4;  // 36 KiB
+constexpr int MX_GROUP = 8;                                // slices per grouped scale record
+constexpr int MX_SREC = 2 * GBM * 16;                      // 8 KiB per scale group
+static_assert(4 * MX_STAGE_SLOTS == Fmt<1>::LDS && 4 * MX_CODES + 2 * MX_SREC <= Fmt<1>::LDS, "MXFP8 LDS");
 
 // LDS DMA: a buffer load whose data goes straight to LDS.  A wave-wide DMA writes 64
 // consecutive LDS slots starting at the wave-uniform address in M0 -- 16 bytes per lane for
@@ -378,87 +352,202 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// DMA of one MXFP8 K slice starting at element k0 into stage buffer buf.  The chunk swizzle
-// is applied on the global side: the lane that fills LDS chunk slot cs of row r fetches
-// global chunk cs ^ ((r >> 3) & 3).  Scale slot (row r, K-block kb) is dword 2r + kb of the
-// operand's slot array.  Per lane: 8 code DMAs and 4 scale DMAs.
-constexpr int MX_DMA_PER_SLICE = 12;
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
-__device__ __forceinline__ void mx_dma(const GemmArgs& g, const RsrcWords& o, int64_t k0, uint8_t* buf) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t rowbytes = (uint32_t)g.K;
-    const bool tail = k0 + 64 > g.K;   // uniform
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int r0 = 64 * p + 16 * wave;   // first row of this wave's 1 KiB piece
-        const int r = r0 + (lane >> 2), c = (lane & 3) ^ ((r >> 3) & 3);
-        uint32_t off = (uint32_t)r * rowbytes + 16u * c;
-        if (tail && k0 + 16 * c >= g.K) off = OOB;
-        dma_b128(o.a, lds_addr(buf + r0 * ROWB), off, (uint32_t)k0);
-        dma_b128(o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off, (uint32_t)k0);
-    }
-    const uint32_t sstride = (uint32_t)(g.K / 32);
+// Per-wave DMA plan of one MXFP8 K slice, in four parts that the main loop spreads between its
+// MFMAs.  Part P (0..3) moves rows 64P + 16w .. +16 (w = wave) of both operands' codes; the
+// chunk swizzle is applied on the global side (the lane that fills LDS chunk slot cs of row r
+// fetches global chunk cs ^ ((r >> 3) & 3)).  In the per-slice scale layout parts 0 and 1
+// also move scale slots 256P + 64w .. +64 of both operands.  A slice past the end of K is
+// issued with out-of-range offsets (no memory traffic, zeros into a free buffer) so that
+// every slice issues the same number of DMAs.
+struct MxDma {
+    RsrcWords o;
+    uint32_t rowbytes, sstride;
+    int wave, lane;
+    int64_t K;
+};
+
+template <int P>
+__device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t k0, bool live, uint8_t* buf) {
+    const int r0 = 64 * P + 16 * d.wave;
+    const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
+    uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
+    if (!live || k0 + 16 * c >= d.K) off = OOB;
+    const uint32_t soff = live ? (uint32_t)k0 : 0u;
+    dma_b128(d.o.a, lds_addr(buf + r0 * ROWB), off, soff);
+    dma_b128(d.o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off, soff);
+}
+
+template <int P>
+__device__ __forceinline__ void mx_dma_slots(const MxDma& d, int64_t k0, bool live, uint8_t* buf) {
+    const int s0 = 256 * P + 64 * d.wave;
+    const int sl = s0 + d.lane, r = sl >> 1, kb = sl & 1;
     const int64_t kb0 = k0 / 32;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int s0 = 256 * p + 64 * wave;  // first slot of this wave's piece
-        const int sl = s0 + lane, r = sl >> 1, kb = sl & 1;
-        const uint32_t off = (kb0 + kb < (int64_t)sstride) ? (uint32_t)r * sstride + kb : OOB;
-        dma_u8(o.as, lds_addr(buf + MX_SCALES + 4 * s0), off, (uint32_t)kb0);
-        dma_u8(o.bs, lds_addr(buf + MX_SCALES + 8 * GBM + 4 * s0), off, (uint32_t)kb0);
+    const uint32_t off = (live && kb0 + kb < (int64_t)d.sstride) ? (uint32_t)r * d.sstride + kb : OOB;
+    const uint32_t soff = live ? (uint32_t)kb0 : 0u;
+    dma_u8(d.o.as, lds_addr(buf + MX_CODES + 4 * s0), off, soff);
+    dma_u8(d.o.bs, lds_addr(buf + MX_CODES + 8 * GBM + 4 * s0), off, soff);
+}
+
+// Grouped scales: lane l of wave w fetches the 16-byte record of row 64w + l for group grp.
+__device__ __forceinline__ void mx_dma_group(const MxDma& d, int64_t grp, bool live, uint8_t* sbuf) {
+    const int r = 64 * d.wave + d.lane;
+    const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
+    const uint32_t soff = live ? (uint32_t)(16 * grp) : 0u;
+    dma_b128(d.o.as, lds_addr(sbuf + 64 * d.wave * 16), off, soff);
+    dma_b128(d.o.bs, lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
+}
+
+// Fragment reads of part P of a slice: A fragment P and B fragment P (lane (row, g): K elements
+// 16g..16g+15 (chunk g) and 32+16g.. (chunk 2+g) of the slice) and their scales (K-block g).
+// Grouped scales: byte 2q + g of the row's record, q = slice index within its group.
+template <int P, bool GROUPED>
+__device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* sbuf, int q, int wm, int wn,
+                                             int lane, MxFrag& f) {
+    const int frow = lane & 31, kh = lane >> 5;
+    const int ra = wm + 32 * P + frow, rb = wn + 32 * P + frow;
+    const uint8_t* sA = buf;
+    const uint8_t* sB = buf + GBM * ROWB;
+    uint4 lo = *(const uint4*)(sA + swz(ra, kh));
+    uint4 hi = *(const uint4*)(sA + swz(ra, 2 + kh));
+    f.a[P] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    lo = *(const uint4*)(sB + swz(rb, kh));
+    hi = *(const uint4*)(sB + swz(rb, 2 + kh));
+    f.b[P] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    if constexpr (GROUPED) {
+        f.as[P] = sbuf[ra * 16 + 2 * q + kh];
+        f.bs[P] = sbuf[GBM * 16 + rb * 16 + 2 * q + kh];
+    } else {
+        const uint32_t* slots = (const uint32_t*)(buf + MX_CODES);
+        f.as[P] = slots[2 * ra + kh];
+        f.bs[P] = slots[2 * GBM + 2 * rb + kh];
     }
 }
 
-// Scheduling hint for one MXFP8 slice: 2 MFMAs on the current operands first, then the next
-// slice's 24 LDS reads (16 code, 8 scale) spread between the remaining MFMAs.
-__device__ __forceinline__ void mx_interleave() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+template <bool GROUPED>
+__device__ __forceinline__ void mx_read(const uint8_t* buf, const uint8_t* sbuf, int q, int wm, int wn, int lane,
+                                        MxFrag& f) {
+    mx_read_part<0, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
+    mx_read_part<1, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
+    mx_read_part<2, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
+    mx_read_part<3, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
 }
 
-// MXFP8 main loop over K slices with 4 LDS stage buffers.  At the top of slice kt each wave
-// waits for its own DMAs of slice kt+1 (issued two slices earlier; only those of slice kt+2
-// may still be in flight), then a barrier publishes slice kt+1 to the workgroup and confirms
-// that every wave has consumed slice kt-1, whose buffer then receives the DMA of slice kt+3.
-// The fragments of slice kt+1 are read while slice kt's 16 MFMAs issue; the loop is unrolled
-// by two so that the two fragment register sets alternate without copies.
+// The 4 MFMAs of A fragment P against the 4 B fragments.
+template <int P>
+__device__ __forceinline__ void mx_mfma_row(const MxFrag& f, floatx16 (&acc)[4][MXTN]) {
+#pragma unroll
+    for (int j = 0; j < MXTN; ++j)
+        acc[P][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[P], f.b[j], acc[P][j], 0, 0, 0, (int)f.as[P], 0,
+                                                                     (int)f.bs[j]);
+}
+
+// MXFP8 main loop over K slices with 4 LDS code stages.  At the top of slice kt each wave
+// waits for its own DMAs of slice kt+1 (issued two slices earlier; only those issued during
+// slice kt-1 may still be in flight), then a barrier publishes slice kt+1 to the workgroup
+// and confirms that every wave has consumed slice kt-1, whose buffer then receives the DMA of
+// slice kt+3.  The slice's 16 MFMAs run in four parts; each part also issues a quarter of the
+// DMAs of slice kt+3 (so that the vector-memory queue never stalls the wave) and reads one A
+// and one B fragment of slice kt+1 into the other register set.  In the grouped layout the
+// scale record of group G+1 is fetched during slice 8G+1 (its buffer held group G-1, whose
+// last slice was consumed by then) and is complete, being older than the codes waited for,
+// when slice 8G+7 reads the fragments of slice 8G+8.
+template <bool GROUPED>
 __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
                                              int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
-    constexpr int D = MX_DMA_PER_SLICE;
+    constexpr int DC = 8;                    // code DMAs per slice per lane
+    constexpr int DS = GROUPED ? 0 : 4;      // per-slice scale DMAs
+    constexpr int DG = 2;                    // grouped scale DMAs (every MX_GROUP slices)
+    constexpr int STRIDE = GROUPED ? MX_CODES : MX_STAGE_SLOTS;
     if (nk <= 0) return;
-    RsrcWords o;
-    o.a = rsrc_words(g.a_codes + m0 * g.K, (g.M - m0) * g.K);
-    o.b = rsrc_words(g.b_codes + n0 * g.K, (g.N - n0) * g.K);
-    o.as = rsrc_words(g.a_scales + m0 * (g.K / 32), (g.M - m0) * (g.K / 32));
-    o.bs = rsrc_words(g.b_scales + n0 * (g.K / 32), (g.N - n0) * (g.K / 32));
-    auto buf = [&](int64_t k) { return lds + (int)(k & 3) * MX_STAGE; };
-    mx_dma(g, o, 0, buf(0));
-    if (nk > 1) mx_dma(g, o, 64, buf(1));
-    if (nk > 2) mx_dma(g, o, 128, buf(2));
-    if (nk > 2) wait_vm_barrier<2 * D>();
-    else if (nk > 1) wait_vm_barrier<D>();
-    else wait_vm_barrier<0>();
-    MxFrag f0, f1;
-    mx_read(buf(0), wm, wn, lane, f0);
-    auto iter = [&](int64_t kt, const MxFrag& fc, MxFrag& fn) {
-        if (kt + 2 < nk) wait_vm_barrier<D>();
-        else wait_vm_barrier<0>();
-        if (kt + 3 < nk) mx_dma(g, o, (kt + 3) * 64, buf(kt + 3));
-        // the reads after the last slice touch a stale (in-bounds) buffer and go unused
-        mx_mfma16(fc, acc);
-        mx_read(buf(kt + 1), wm, wn, lane, fn);
-        mx_interleave();
+    MxDma d;
+    d.o.a = rsrc_words(g.a_codes + m0 * g.K, (g.M - m0) * g.K);
+    d.o.b = rsrc_words(g.b_codes + n0 * g.K, (g.N - n0) * g.K);
+    d.o.as = rsrc_words(g.a_scales + m0 * (g.K / 32), (g.M - m0) * (g.K / 32));
+    d.o.bs = rsrc_words(g.b_scales + n0 * (g.K / 32), (g.N - n0) * (g.K / 32));
+    d.rowbytes = (uint32_t)g.K;
+    d.sstride = (uint32_t)(g.K / 32);
+    d.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    d.lane = lane;
+    d.K = g.K;
+    auto buf = [&](int64_t k) { return lds + (int)(k & 3) * STRIDE; };
+    auto sbuf = [&](int64_t grp) { return lds + 4 * MX_CODES + (int)(grp & 1) * MX_SREC; };
+    auto dma_slice = [&](int64_t k) {
+        const bool live = k < nk;
+        uint8_t* b = buf(k);
+        mx_dma_codes<0>(d, k * 64, live, b);
+        mx_dma_codes<1>(d, k * 64, live, b);
+        mx_dma_codes<2>(d, k * 64, live, b);
+        mx_dma_codes<3>(d, k * 64, live, b);
+        if constexpr (!GROUPED) {
+            mx_dma_slots<0>(d, k * 64, live, b);
+            mx_dma_slots<1>(d, k * 64, live, b);
+        }
     };
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-        iter(kt, f0, f1);
-        if (kt + 1 < nk) iter(kt + 1, f1, f0);
+    if constexpr (GROUPED) mx_dma_group(d, 0, true, sbuf(0));
+    dma_slice(0);
+    dma_slice(1);
+    dma_slice(2);
+    wait_vm_barrier<2 * (DC + DS)>();
+    MxFrag f0, f1;
+    mx_read<GROUPED>(buf(0), sbuf(0), 0, wm, wn, lane, f0);
+
+    // one slice; Q = kt mod MX_GROUP when grouped (the loop is then unrolled by MX_GROUP)
+    auto slice = [&](int64_t kt, auto q_c, const MxFrag& fc, MxFrag& fn) {
+        constexpr int Q = decltype(q_c)::value;
+        if constexpr (GROUPED && Q == 2) wait_vm_barrier<DC + DG>();   // slice kt-1 also issued a group
+        else wait_vm_barrier<DC + DS>();
+        const int64_t kd = kt + 3;
+        const bool live = kd < nk;
+        uint8_t* db = buf(kd);
+        const int64_t kn = kt + 1;                   // fragments read for the next slice
+        const uint8_t* nb = buf(kn);
+        const uint8_t* ns = sbuf(kn / MX_GROUP);
+        const int qn = GROUPED ? (Q + 1) % MX_GROUP : 0;
+        static_for<0, 4>([&](auto p_c) {
+            constexpr int P = decltype(p_c)::value;
+            mx_dma_codes<P>(d, kd * 64, live, db);
+            if constexpr (!GROUPED && P < 2) mx_dma_slots<P>(d, kd * 64, live, db);
+            if constexpr (GROUPED && Q == 1 && P == 0) {
+                const int64_t grp = kt / MX_GROUP + 1;
+                mx_dma_group(d, grp, grp * MX_GROUP < nk, sbuf(grp));
+            }
+            mx_mfma_row<P>(fc, acc);
+            // the reads after the last slice touch a stale (in-bounds) buffer and go unused
+            mx_read_part<P, GROUPED>(nb, ns, qn, wm, wn, lane, fn);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    if constexpr (GROUPED) {
+        // nk is a multiple of MX_GROUP
+        for (int64_t kt = 0; kt < nk; kt += MX_GROUP) {
+            slice(kt + 0, std::integral_constant<int, 0>{}, f0, f1);
+            slice(kt + 1, std::integral_constant<int, 1>{}, f1, f0);
+            slice(kt + 2, std::integral_constant<int, 2>{}, f0, f1);
+            slice(kt + 3, std::integral_constant<int, 3>{}, f1, f0);
+            slice(kt + 4, std::integral_constant<int, 4>{}, f0, f1);
+            slice(kt + 5, std::integral_constant<int, 5>{}, f1, f0);
+            slice(kt + 6, std::integral_constant<int, 6>{}, f0, f1);
+            slice(kt + 7, std::integral_constant<int, 7>{}, f1, f0);
+        }
+    } else {
+        for (int64_t kt = 0; kt < nk; kt += 2) {
+            slice(kt, std::integral_constant<int, 0>{}, f0, f1);
+            if (kt + 1 < nk) slice(kt + 1, std::integral_constant<int, 0>{}, f1, f0);
+        }
     }
+    wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
 }
 
 // Output tile of this workgroup.  Workgroup ids are dealt to the 8 XCDs round-robin; the
@@ -561,7 +650,8 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
             for (int j = 0; j < NVTN; ++j) sb[j] = sbn[j];
         }
     } else {
-        mx_main_loop(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        if (g.K % (MX_GROUP * 64) == 0) mx_main_loop<true>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        else mx_main_loop<false>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
 
     float alpha = 1.0f;

@@ -11,7 +11,7 @@ import torch
 import block_scaled_precision_nvfp4_amd as bsq
 from synthetic import (SEED_DY, SEED_SIGNS, SEED_SR_KEY, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16,
                        outlier_bf16, rht_signs)
-from tests.gpu_common import GEMM_TOL, bf16_round, note, rel_fro
+from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, note, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -20,8 +20,9 @@ DEV = "cuda:0"
 
 def nv_gemm_check(a_cpu, b_cpu, out_dtype=torch.bfloat16, rows=None, cols=None, label="",
                   a_dir=1, b_dir=1, rounding=0, signs=None):
-    """Quantize both operands on the GPU, run the GEMM, and compare against the oracle GEMM
-    of the GPU's own quantized operands (whose bit-exactness the quantize tests cover)."""
+    """Quantize both operands on the GPU and run the GEMM; quantize the same bf16 inputs with
+    the oracle (codes, scales and tensor scales must agree bit for bit) and compare the GEMM
+    against the oracle GEMM of the oracle's own operands."""
     import oracle
     note("nvfp4 gemm %s A%s B%s out=%s" % (label, tuple(a_cpu.shape), tuple(b_cpu.shape), out_dtype))
     qa = bsq.nvfp4_quantize(a_cpu.to(DEV), direction=a_dir, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=0,
@@ -33,9 +34,17 @@ def nv_gemm_check(a_cpu, b_cpu, out_dtype=torch.bfloat16, rows=None, cols=None, 
     y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qa[ka + "_codes"], qa[ka + "_scales"], qa["s_enc"][ia:ia + 1],
                              qb[kb + "_codes"], qb[kb + "_scales"], qb["s_enc"][ib:ib + 1], out_dtype=out_dtype)
     torch.cuda.synchronize()
-    ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, qa[ka + "_codes"].cpu().numpy(), qa[ka + "_scales"].cpu().numpy(),
-                                  float(qa["s_enc"][ia].item()), qb[kb + "_codes"].cpu().numpy(),
-                                  qb[kb + "_scales"].cpu().numpy(), float(qb["s_enc"][ib].item()), rows=rows, cols=cols)
+    sg = None if signs is None else signs.numpy()
+    ra = oracle.nvfp4_quantize(a_cpu, direction=a_dir, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=0, signs=sg)
+    rb = oracle.nvfp4_quantize(b_cpu, direction=b_dir, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=1, signs=sg)
+    for q, r, nm in ((qa, ra, "A"), (qb, rb, "B")):
+        k = ka if nm == "A" else kb
+        i = ia if nm == "A" else ib
+        assert_bytes_equal(q[k + "_codes"], r[k + "_codes"], nm + " codes")
+        assert_bytes_equal(q[k + "_scales"], r[k + "_scales"], nm + " scales")
+        assert_f32_equal(q["s_enc"][i:i + 1], np.asarray(r["s_enc"][i:i + 1], dtype=np.float32), nm + " s_enc")
+    ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, ra[ka + "_codes"], ra[ka + "_scales"], float(ra["s_enc"][ia]),
+                                  rb[kb + "_codes"], rb[kb + "_scales"], float(rb["s_enc"][ib]), rows=rows, cols=cols)
     yc = y.float().cpu().numpy().astype(np.float64)
     if rows is not None:
         yc = yc[np.asarray(rows)][:, np.asarray(cols)]
@@ -47,17 +56,22 @@ def nv_gemm_check(a_cpu, b_cpu, out_dtype=torch.bfloat16, rows=None, cols=None, 
 
 
 def mx_gemm_check(a_cpu, b_cpu, a_dir, b_dir, out_dtype=torch.bfloat16, rows=None, cols=None, label=""):
+    """As nv_gemm_check for MXFP8 operands (no tensor scale)."""
     import oracle
-    note("mxfp8 gemm %s A%s B%s" % (label, tuple(a_cpu.shape), tuple(b_cpu.shape)))
+    note("mxfp8 gemm %s A%s B%s out=%s" % (label, tuple(a_cpu.shape), tuple(b_cpu.shape), out_dtype))
     qa = bsq.mxfp8_quantize(a_cpu.to(DEV), direction=a_dir)
     qb = bsq.mxfp8_quantize(b_cpu.to(DEV), direction=b_dir)
     ka, kb = ("row" if a_dir == 1 else "col"), ("row" if b_dir == 1 else "col")
     y = bsq.blockscaled_gemm(bsq.FMT_MXFP8, qa[ka + "_codes"], qa[ka + "_scales"], None,
                              qb[kb + "_codes"], qb[kb + "_scales"], None, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    ref = oracle.blockscaled_gemm(oracle.FMT_MXFP8, qa[ka + "_codes"].cpu().numpy(), qa[ka + "_scales"].cpu().numpy(),
-                                  1.0, qb[kb + "_codes"].cpu().numpy(), qb[kb + "_scales"].cpu().numpy(), 1.0,
-                                  rows=rows, cols=cols)
+    ra = oracle.mxfp8_quantize(a_cpu, direction=a_dir)
+    rb = oracle.mxfp8_quantize(b_cpu, direction=b_dir)
+    for q, r, k, nm in ((qa, ra, ka, "A"), (qb, rb, kb, "B")):
+        assert_bytes_equal(q[k + "_codes"], r[k + "_codes"], nm + " codes")
+        assert_bytes_equal(q[k + "_scales"], r[k + "_scales"], nm + " scales")
+    ref = oracle.blockscaled_gemm(oracle.FMT_MXFP8, ra[ka + "_codes"], ra[ka + "_scales"], 1.0,
+                                  rb[kb + "_codes"], rb[kb + "_scales"], 1.0, rows=rows, cols=cols)
     yc = y.float().cpu().numpy().astype(np.float64)
     if rows is not None:
         yc = yc[np.asarray(rows)][:, np.asarray(cols)]
@@ -80,10 +94,12 @@ def test_nvfp4_ragged_full(M, N, K, out_dtype):
                   label="ragged")
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (256, 256, 256), (96, 160, 1056)])
-def test_mxfp8_ragged_full(M, N, K):
+# K = 96, 256, 1056: scales fetched per K slice; K = 512, 1536: grouped 16-block scale records
+@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (256, 256, 256), (96, 160, 1056), (200, 72, 512), (300, 260, 1536)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mxfp8_ragged_full(M, N, K, out_dtype):
     mx_gemm_check(outlier_bf16((M, K), seed=M + 1, mask_seed=K + 1), gaussian_bf16((N, K), 0.02, N + 9), 1, 1,
-                  label="ragged")
+                  out_dtype=out_dtype, label="ragged")
 
 
 def test_constant_operands_closed_form():

@@ -135,8 +135,10 @@ def test_dequantize_matches_oracle():
     note("nvfp4_dequantize [256,512]")
     d = bsq.nvfp4_dequantize(q["row_codes"], q["row_scales"], q["s_enc"][0:1])
     torch.cuda.synchronize()
-    ref = oracle.nvfp4_dequantize(q["row_codes"].cpu().numpy(), q["row_scales"].cpu().numpy(),
-                                  float(q["s_enc"][0].item()))
+    r = oracle.nvfp4_quantize(x, direction=1)
+    assert_bytes_equal(q["row_codes"], r["row_codes"], "codes")
+    assert_bytes_equal(q["row_scales"], r["row_scales"], "scales")
+    ref = oracle.nvfp4_dequantize(r["row_codes"], r["row_scales"], float(r["s_enc"][0]))
     assert np.array_equal(d.cpu().view(torch.int16).numpy().view(np.uint16), ref)
 
 
