@@ -54,20 +54,22 @@ struct GemmArgs {
     void* c;
 };
 
+// FMT 0: NVFP4, 8 waves (any K); FMT 1: MXFP8; FMT 2: NVFP4, 4 waves (K a multiple of 256).
 template <int FMT>
 struct Fmt {
-    static constexpr int BK = FMT == 0 ? 128 : 64;    // K elements per slice
-    static constexpr int EPB = FMT == 0 ? 2 : 1;      // elements per code byte
-    static constexpr int BLK = FMT == 0 ? 16 : 32;    // elements per scale
+    static constexpr bool NV = FMT != 1;
+    static constexpr int BK = NV ? 128 : 64;          // K elements per slice
+    static constexpr int EPB = NV ? 2 : 1;            // elements per code byte
+    static constexpr int BLK = NV ? 16 : 32;          // elements per scale
     static constexpr int SPR = BK / BLK;              // scale bytes per row per slice (8 or 2)
     static constexpr int SCB = 8;                     // LDS bytes per row for scales
     // NVFP4: 8 raw scale bytes per row; MXFP8: one dword slot per (row, K-block), 2 per row
     static constexpr int STAGE = (GBM + GBN) * (ROWB + SCB);
     static constexpr int NSTAGE = FMT == 0 ? 3 : 4;
     static constexpr int LDS = NSTAGE * STAGE;
-    // waves per workgroup and MFMA tiles per wave: NVFP4 runs 8 waves (two per SIMD) of
-    // 128 x 64 so that one wave's dequantization overlaps the other's MFMAs; MXFP8 (no
-    // dequantization) runs 4 waves of 128 x 128.
+    // waves per workgroup and MFMA tiles per wave: FMT 0 runs 8 waves (two per SIMD) of
+    // 128 x 64 so that one wave's dequantization overlaps the other's MFMAs; FMT 1 and 2 run
+    // 4 waves of 128 x 128.
     static constexpr int NW = FMT == 0 ? 8 : 4;
     static constexpr int THREADS = 64 * NW;
     static constexpr int TM = 4;                  // 32-row A fragments per wave
@@ -362,26 +364,27 @@ __device__ __forceinline__ void wait_vm() {
 // chunk swizzle is applied on the global side (the lane that fills LDS chunk slot cs of row r
 // fetches global chunk cs ^ ((r >> 3) & 3)).  In the per-slice scale layout parts 0 and 1
 // also move scale slots 256P + 64w .. +64 of both operands.  A slice past the end of K is
-// issued with out-of-range offsets (no memory traffic, zeros into a free buffer) so that
-// every slice issues the same number of DMAs.
+// issued with out-of-range offsets (no memory traffic; the zeros they write land in a free
+// buffer) so that every slice issues the same number of DMAs.
 struct MxDma {
     RsrcWords o;
-    uint32_t rowbytes, sstride;
+    uint32_t rowbytes, sstride;   // code bytes per row (K / elements per byte); scale bytes per row
     int wave, lane;
-    int64_t K;
 };
 
+// Codes of the slice whose first code byte in each row is b0 (64 bytes per row).
 template <int P>
-__device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t k0, bool live, uint8_t* buf) {
+__device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t b0, bool live, uint8_t* buf) {
     const int r0 = 64 * P + 16 * d.wave;
     const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
     uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
-    if (!live || k0 + 16 * c >= d.K) off = OOB;
-    const uint32_t soff = live ? (uint32_t)k0 : 0u;
+    if (!live || b0 + 16 * c >= (int64_t)d.rowbytes) off = OOB;
+    const uint32_t soff = live ? (uint32_t)b0 : 0u;
     dma_b128(d.o.a, lds_addr(buf + r0 * ROWB), off, soff);
     dma_b128(d.o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off, soff);
 }
 
+// MXFP8 per-slice scale slots of the slice starting at element k0.
 template <int P>
 __device__ __forceinline__ void mx_dma_slots(const MxDma& d, int64_t k0, bool live, uint8_t* buf) {
     const int s0 = 256 * P + 64 * d.wave;
@@ -393,13 +396,29 @@ __device__ __forceinline__ void mx_dma_slots(const MxDma& d, int64_t k0, bool li
     dma_u8(d.o.bs, lds_addr(buf + MX_CODES + 8 * GBM + 4 * s0), off, soff);
 }
 
-// Grouped scales: lane l of wave w fetches the 16-byte record of row 64w + l for group grp.
+// Grouped scales: lane l of wave w fetches the 16-byte record grp (scale bytes 16grp..16grp+15)
+// of row 64w + l, for both operands.
 __device__ __forceinline__ void mx_dma_group(const MxDma& d, int64_t grp, bool live, uint8_t* sbuf) {
     const int r = 64 * d.wave + d.lane;
     const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
     const uint32_t soff = live ? (uint32_t)(16 * grp) : 0u;
     dma_b128(d.o.as, lds_addr(sbuf + 64 * d.wave * 16), off, soff);
     dma_b128(d.o.bs, lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
+}
+
+template <int EPB, int BLK>
+__device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
+    MxDma d;
+    const int64_t rb = g.K / EPB, sb = g.K / BLK;
+    d.o.a = rsrc_words(g.a_codes + m0 * rb, (g.M - m0) * rb);
+    d.o.b = rsrc_words(g.b_codes + n0 * rb, (g.N - n0) * rb);
+    d.o.as = rsrc_words(g.a_scales + m0 * sb, (g.M - m0) * sb);
+    d.o.bs = rsrc_words(g.b_scales + n0 * sb, (g.N - n0) * sb);
+    d.rowbytes = (uint32_t)rb;
+    d.sstride = (uint32_t)sb;
+    d.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    d.lane = lane;
+    return d;
 }
 
 // Fragment reads of part P of a slice: A fragment P and B fragment P (lane (row, g): K elements
@@ -464,16 +483,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     constexpr int DG = 2;                    // grouped scale DMAs (every MX_GROUP slices)
     constexpr int STRIDE = GROUPED ? MX_CODES : MX_STAGE_SLOTS;
     if (nk <= 0) return;
-    MxDma d;
-    d.o.a = rsrc_words(g.a_codes + m0 * g.K, (g.M - m0) * g.K);
-    d.o.b = rsrc_words(g.b_codes + n0 * g.K, (g.N - n0) * g.K);
-    d.o.as = rsrc_words(g.a_scales + m0 * (g.K / 32), (g.M - m0) * (g.K / 32));
-    d.o.bs = rsrc_words(g.b_scales + n0 * (g.K / 32), (g.N - n0) * (g.K / 32));
-    d.rowbytes = (uint32_t)g.K;
-    d.sstride = (uint32_t)(g.K / 32);
-    d.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    d.lane = lane;
-    d.K = g.K;
+    const MxDma d = make_dma<1, 32>(g, m0, n0, lane);
     auto buf = [&](int64_t k) { return lds + (int)(k & 3) * STRIDE; };
     auto sbuf = [&](int64_t grp) { return lds + 4 * MX_CODES + (int)(grp & 1) * MX_SREC; };
     auto dma_slice = [&](int64_t k) {
@@ -546,6 +556,157 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
             slice(kt, std::integral_constant<int, 0>{}, f0, f1);
             if (kt + 1 < nk) slice(kt + 1, std::integral_constant<int, 0>{}, f1, f0);
         }
+    }
+    wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
+}
+
+// ---------------------------------------------------------------- NVFP4, 4 waves of 128 x 128
+
+// K a multiple of 256.  Same LDS organisation as the grouped MXFP8 path: 4 code stages of 64
+// bytes per row (128 elements), filled by DMA three slices ahead, and double-buffered 16-byte
+// scale records, each holding the 16 E4M3 scales of two slices of a row.  Each wave computes
+// 128 x 128 (4 x 4 MFMA tiles), so every dequantized A or B word feeds 4 MFMAs: half the
+// dequantization per MFMA of the 8-wave 128 x 64 arrangement.  With one wave per SIMD the
+// dequantization of step s+1 is interleaved between the MFMAs of step s.
+constexpr int NV4_CODES = 2 * GBM * ROWB;   // 32 KiB per stage
+constexpr int NV4_SREC = 2 * GBM * 16;      // 8 KiB per scale group (2 slices)
+static_assert(4 * NV4_CODES + 2 * NV4_SREC <= Fmt<2>::LDS, "NVFP4 4-wave LDS");
+
+struct Nv4Words {
+    uint32_t a[4], b[4];
+};
+struct Nv4Ops {
+    half8_t a[4], b[4];
+};
+
+// Step S (0..7) of a slice: lane (row, kh) holds the 8 codes of K elements 64kh + 8S .. +8,
+// dword S % 4 of chunk 2kh + S / 4 of its row (block 4kh + S / 2 of the slice).
+template <int S>
+__device__ __forceinline__ void nv4_read_words(const uint8_t* buf, int wm, int wn, int frow, int kh, Nv4Words& w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w.a[i] = *(const uint32_t*)(buf + swz(wm + 32 * i + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        w.b[j] = *(const uint32_t*)(buf + GBM * ROWB + swz(wn + 32 * j + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
+}
+
+// The lane's 4 scale bytes (blocks 4kh .. 4kh+3) of slice q (0/1) of a group record.
+__device__ __forceinline__ void nv4_read_scales(const uint8_t* sbuf, int q, int wm, int wn, int frow, int kh,
+                                                uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = *(const uint32_t*)(sbuf + (wm + 32 * i + frow) * 16 + 4 * (2 * q + kh));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sb[j] = *(const uint32_t*)(sbuf + GBM * 16 + (wn + 32 * j + frow) * 16 + 4 * (2 * q + kh));
+}
+
+template <int S>
+__device__ __forceinline__ void nv4_ops(const Nv4Words& w, const uint32_t (&sa)[4], const uint32_t (&sb)[4], Nv4Ops& o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.a[i] = nv_dequant(w.a[i], nv_scale(sa[i], S >> 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.b[j] = nv_dequant(w.b[j], nv_scale(sb[j], S >> 1));
+}
+
+__device__ __forceinline__ void nv4_mfma16(const Nv4Ops& o, floatx16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+}
+
+// One pipelined step: the next step's 8 word reads first, 2 MFMAs while they land, then the
+// remaining 14 MFMAs each followed by an equal share of the next step's dequantization.
+__device__ __forceinline__ void nv4_interleave() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+}
+
+// Main loop.  Slice kt: wait for this wave's DMAs of slice kt+1 (everything issued before the
+// DMAs of slice kt-1), barrier, then 8 MFMA steps; the code DMAs of slice kt+3 are spread over
+// steps 0, 2, 4, 6 and, in odd slices, the scale group (kt+3)/2 (slices kt+3, kt+4) is fetched
+// at step 1 -- its buffer held group (kt-1)/2, whose last scales were read during slice kt-1.
+// The scales of slice kt+1 are read at step 6 and the words of its step 0 at step 7.  An odd
+// slice issues 10 DMAs and an even one 8, so the wait at the top of an even slice allows 10
+// in flight; the prologue ends with an out-of-range group DMA so that slice 0 fits the rule.
+// An out-of-range DMA lane still writes (zeros) to LDS: every such DMA here targets a buffer
+// whose contents are no longer, or not yet, needed.
+__device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
+                                              int wm, int wn, int lane, floatx16 (&acc)[4][4]) {
+    if (nk <= 0) return;
+    const MxDma d = make_dma<2, 16>(g, m0, n0, lane);
+    const int frow = lane & 31, kh = lane >> 5;
+    auto buf = [&](int64_t k) { return lds + (int)(k & 3) * NV4_CODES; };
+    auto sbuf = [&](int64_t grp) { return lds + 4 * NV4_CODES + (int)(grp & 1) * NV4_SREC; };
+    auto dma_slice = [&](int64_t k) {
+        const bool live = k < nk;
+        mx_dma_codes<0>(d, k * 64, live, buf(k));
+        mx_dma_codes<1>(d, k * 64, live, buf(k));
+        mx_dma_codes<2>(d, k * 64, live, buf(k));
+        mx_dma_codes<3>(d, k * 64, live, buf(k));
+    };
+    mx_dma_group(d, 0, true, sbuf(0));
+    mx_dma_group(d, 1, 2 < nk, sbuf(1));
+    dma_slice(0);
+    dma_slice(1);
+    dma_slice(2);
+    // out of range: no memory traffic, but the DMA still writes its zeros -- into code stage 3,
+    // which is free until slice 3's DMA (issued after it) refills it
+    mx_dma_group(d, 0, false, buf(3));
+    wait_vm_barrier<18>();
+
+    Nv4Words w;
+    Nv4Ops cur, nxt;
+    uint32_t sa[4], sb[4], san[4], sbn[4];
+    nv4_read_scales(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
+    nv4_read_words<0>(buf(0), wm, wn, frow, kh, w);
+    nv4_ops<0>(w, sa, sb, cur);
+
+    auto slice = [&](int64_t kt, auto odd_c) {
+        constexpr bool ODD = decltype(odd_c)::value;
+        if constexpr (ODD) wait_vm_barrier<8>();
+        else wait_vm_barrier<10>();
+        const int64_t kd = kt + 3;
+        const bool live = kd < nk;
+        uint8_t* db = buf(kd);
+        const uint8_t* cb = buf(kt);
+        const uint8_t* nb = buf(kt + 1);
+        static_for<0, 8>([&](auto s_c) {
+            constexpr int S = decltype(s_c)::value;
+            if constexpr ((S & 1) == 0) mx_dma_codes<S / 2>(d, kd * 64, live, db);
+            if constexpr (ODD && S == 1) {
+                const int64_t grp = (kt + 3) / 2;
+                mx_dma_group(d, grp, 2 * grp < nk, sbuf(grp));
+            }
+            if constexpr (S < 7) {
+                nv4_read_words<S + 1>(cb, wm, wn, frow, kh, w);
+                if constexpr (S == 6) nv4_read_scales(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
+                nv4_ops<S + 1>(w, sa, sb, nxt);
+            } else {
+                // the reads after the last slice touch a stale (in-bounds) buffer and go unused
+                nv4_read_words<0>(nb, wm, wn, frow, kh, w);
+                nv4_ops<0>(w, san, sbn, nxt);
+            }
+            nv4_mfma16(cur, acc);
+            nv4_interleave();
+            cur = nxt;
+        });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = san[i];
+            sb[i] = sbn[i];
+        }
+    };
+    // nk is even
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+        slice(kt, std::false_type{});
+        slice(kt + 1, std::true_type{});
     }
     wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
 }
@@ -649,13 +810,15 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
             for (int j = 0; j < NVTN; ++j) sb[j] = sbn[j];
         }
-    } else {
+    } else if constexpr (FMT == 1) {
         if (g.K % (MX_GROUP * 64) == 0) mx_main_loop<true>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else mx_main_loop<false>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+    } else {
+        nv4_main_loop(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
 
     float alpha = 1.0f;
-    if (FMT == 0) alpha = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
+    if (F::NV) alpha = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
     static_for<0, 4 * TN>([&](auto t_c) {
         constexpr int i = decltype(t_c)::value / TN, j = decltype(t_c)::value % TN;
         const int64_t col = n0 + wn + 32 * j + frow;
@@ -693,6 +856,7 @@ int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint
     if (M == 0 || N == 0) return 0;
     hipStream_t s = (hipStream_t)hip_stream;
     GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c};
+    if (fmt == 0 && K % 256 == 0) return c_dtype == 1 ? launch_one<2, 1>(g, s) : launch_one<2, 0>(g, s);
     if (fmt == 0) return c_dtype == 1 ? launch_one<0, 1>(g, s) : launch_one<0, 0>(g, s);
     return c_dtype == 1 ? launch_one<1, 1>(g, s) : launch_one<1, 0>(g, s);
 }

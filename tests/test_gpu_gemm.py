@@ -87,7 +87,9 @@ def test_tiny_config_full():
     nv_gemm_check(gaussian_bf16((128, 256), 1.0, SEED_X), gaussian_bf16((256, 256), 1.0, SEED_W), label="tiny")
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (128, 128, 32), (1, 1, 64), (384, 260, 320), (64, 512, 1056)])
+# K a multiple of 256 runs the 4-wave kernel with grouped scale records, any other K the 8-wave one
+@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (128, 128, 32), (1, 1, 64), (384, 260, 320), (64, 512, 1056),
+                                   (200, 72, 256), (1, 1, 256), (384, 260, 768), (300, 520, 2048)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_nvfp4_ragged_full(M, N, K, out_dtype):
     nv_gemm_check(outlier_bf16((M, K), seed=M, mask_seed=K), gaussian_bf16((N, K), 0.02, N + 7), out_dtype=out_dtype,
