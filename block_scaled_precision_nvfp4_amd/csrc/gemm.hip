@@ -616,27 +616,28 @@ __device__ __forceinline__ void nv4_mfma16(const Nv4Ops& o, floatx16 (&acc)[4][4
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
 }
 
-// One pipelined step: the next step's 8 word reads first, 2 MFMAs while they land, then the
-// remaining 14 MFMAs each followed by an equal share of the next step's dequantization.
+// One step (after its LDS reads, which a scheduling barrier keeps at the top of the step):
+// each of the 16 MFMAs followed by an equal share of the dequantization of the next step,
+// whose words were read a step earlier.
 __device__ __forceinline__ void nv4_interleave() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < 15; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 // Main loop.  Slice kt: wait for this wave's DMAs of slice kt+1 (everything issued before the
 // DMAs of slice kt-1), barrier, then 8 MFMA steps; the code DMAs of slice kt+3 are spread over
 // steps 0, 2, 4, 6 and, in odd slices, the scale group (kt+3)/2 (slices kt+3, kt+4) is fetched
 // at step 1 -- its buffer held group (kt-1)/2, whose last scales were read during slice kt-1.
-// The scales of slice kt+1 are read at step 6 and the words of its step 0 at step 7.  An odd
-// slice issues 10 DMAs and an even one 8, so the wait at the top of an even slice allows 10
-// in flight; the prologue ends with an out-of-range group DMA so that slice 0 fits the rule.
-// An out-of-range DMA lane still writes (zeros) to LDS: every such DMA here targets a buffer
-// whose contents are no longer, or not yet, needed.
+// Operand pipeline: during step s the words of step s+2 are read and those of step s+1 (read
+// during step s-1) are dequantized; steps 6 and 7 read the first two steps of slice kt+1, whose
+// scales are read at step 5.  An odd slice issues 10 DMAs and an even one 8, so the wait at the
+// top of an even slice allows 10 in flight; the prologue ends with an out-of-range group DMA
+// so that slice 0 fits the rule.  An out-of-range DMA lane still writes (zeros) to LDS: every
+// such DMA here targets a buffer whose contents are no longer, or not yet, needed.
 __device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
                                               int wm, int wn, int lane, floatx16 (&acc)[4][4]) {
     if (nk <= 0) return;
@@ -661,12 +662,13 @@ __device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int
     mx_dma_group(d, 0, false, buf(3));
     wait_vm_barrier<18>();
 
-    Nv4Words w;
+    Nv4Words w1, w2;   // words of the next step and of the step after it
     Nv4Ops cur, nxt;
     uint32_t sa[4], sb[4], san[4], sbn[4];
     nv4_read_scales(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
-    nv4_read_words<0>(buf(0), wm, wn, frow, kh, w);
-    nv4_ops<0>(w, sa, sb, cur);
+    nv4_read_words<0>(buf(0), wm, wn, frow, kh, w1);
+    nv4_ops<0>(w1, sa, sb, cur);
+    nv4_read_words<1>(buf(0), wm, wn, frow, kh, w1);
 
     auto slice = [&](int64_t kt, auto odd_c) {
         constexpr bool ODD = decltype(odd_c)::value;
@@ -684,18 +686,19 @@ __device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int
                 const int64_t grp = (kt + 3) / 2;
                 mx_dma_group(d, grp, 2 * grp < nk, sbuf(grp));
             }
-            if constexpr (S < 7) {
-                nv4_read_words<S + 1>(cb, wm, wn, frow, kh, w);
-                if constexpr (S == 6) nv4_read_scales(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
-                nv4_ops<S + 1>(w, sa, sb, nxt);
-            } else {
-                // the reads after the last slice touch a stale (in-bounds) buffer and go unused
-                nv4_read_words<0>(nb, wm, wn, frow, kh, w);
-                nv4_ops<0>(w, san, sbn, nxt);
-            }
+            // words of step S+2 (the reads after the last slice touch a stale, in-bounds buffer)
+            if constexpr (S + 2 < 8) nv4_read_words<S + 2>(cb, wm, wn, frow, kh, w2);
+            else nv4_read_words<S + 2 - 8>(nb, wm, wn, frow, kh, w2);
+            if constexpr (S == 5) nv4_read_scales(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
+            __builtin_amdgcn_sched_barrier(0);
+            // dequantize step S+1
+            if constexpr (S + 1 < 8) nv4_ops<S + 1>(w1, sa, sb, nxt);
+            else nv4_ops<0>(w1, san, sbn, nxt);
             nv4_mfma16(cur, acc);
             nv4_interleave();
+            __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
+            w1 = w2;
         });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
