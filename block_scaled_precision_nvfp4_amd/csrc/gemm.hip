@@ -54,7 +54,9 @@ struct GemmArgs {
     void* c;
 };
 
-// FMT 0: NVFP4, 8 waves (any K); FMT 1: MXFP8; FMT 2: NVFP4, 4 waves (K a multiple of 256).
+// FMT 0: NVFP4, 8 waves of 128 x 64, register-staged (any K); FMT 1: MXFP8, 4 waves of 128 x
+// 128; FMT 2: NVFP4 with LDS DMA and grouped scale records (K a multiple of 256), 4 waves of
+// 128 x 128.
 template <int FMT>
 struct Fmt {
     static constexpr bool NV = FMT != 1;
@@ -67,13 +69,12 @@ struct Fmt {
     static constexpr int STAGE = (GBM + GBN) * (ROWB + SCB);
     static constexpr int NSTAGE = FMT == 0 ? 3 : 4;
     static constexpr int LDS = NSTAGE * STAGE;
-    // waves per workgroup and MFMA tiles per wave: FMT 0 runs 8 waves (two per SIMD) of
-    // 128 x 64 so that one wave's dequantization overlaps the other's MFMAs; FMT 1 and 2 run
-    // 4 waves of 128 x 128.
+    // waves per workgroup and MFMA tiles per wave: 8 waves (two per SIMD) of 128 x 64 or 4
+    // waves of 128 x 128.
     static constexpr int NW = FMT == 0 ? 8 : 4;
     static constexpr int THREADS = 64 * NW;
     static constexpr int TM = 4;                  // 32-row A fragments per wave
-    static constexpr int TN = FMT == 0 ? 2 : 4;   // 32-row B fragments per wave
+    static constexpr int TN = NW == 8 ? 2 : 4;    // 32-row B fragments per wave
     static constexpr int WAVES_N = GBN / (32 * TN);
 };
 
@@ -373,9 +374,9 @@ struct MxDma {
 };
 
 // Codes of the slice whose first code byte in each row is b0 (64 bytes per row).
-template <int P>
+template <int P, int NW = 4>
 __device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t b0, bool live, uint8_t* buf) {
-    const int r0 = 64 * P + 16 * d.wave;
+    const int r0 = 16 * NW * P + 16 * d.wave;
     const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
     uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
     if (!live || b0 + 16 * c >= (int64_t)d.rowbytes) off = OOB;
@@ -396,14 +397,23 @@ __device__ __forceinline__ void mx_dma_slots(const MxDma& d, int64_t k0, bool li
     dma_u8(d.o.bs, lds_addr(buf + MX_CODES + 8 * GBM + 4 * s0), off, soff);
 }
 
-// Grouped scales: lane l of wave w fetches the 16-byte record grp (scale bytes 16grp..16grp+15)
-// of row 64w + l, for both operands.
+// Grouped scales: the 16-byte record grp (scale bytes 16grp..16grp+15) of every row of both
+// operands, one lane per row: with 4 waves lane l of wave w takes row 64w + l of A and of B,
+// with 8 waves waves 0-3 take the A rows and waves 4-7 the B rows.
+template <int NW = 4>
 __device__ __forceinline__ void mx_dma_group(const MxDma& d, int64_t grp, bool live, uint8_t* sbuf) {
-    const int r = 64 * d.wave + d.lane;
-    const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
     const uint32_t soff = live ? (uint32_t)(16 * grp) : 0u;
-    dma_b128(d.o.as, lds_addr(sbuf + 64 * d.wave * 16), off, soff);
-    dma_b128(d.o.bs, lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
+    if constexpr (NW == 4) {
+        const int r = 64 * d.wave + d.lane;
+        const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
+        dma_b128(d.o.as, lds_addr(sbuf + 64 * d.wave * 16), off, soff);
+        dma_b128(d.o.bs, lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
+    } else {
+        const int op = d.wave >> 2, w4 = d.wave & 3;
+        const int r = 64 * w4 + d.lane;
+        const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
+        dma_b128(op ? d.o.bs : d.o.as, lds_addr(sbuf + op * GBM * 16 + 64 * w4 * 16), off, soff);
+    }
 }
 
 template <int EPB, int BLK>
@@ -560,86 +570,104 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
 }
 
-// ---------------------------------------------------------------- NVFP4, 4 waves of 128 x 128
+// ---------------------------------------------------------------- NVFP4 with LDS DMA
 
 // K a multiple of 256.  Same LDS organisation as the grouped MXFP8 path: 4 code stages of 64
 // bytes per row (128 elements), filled by DMA three slices ahead, and double-buffered 16-byte
-// scale records, each holding the 16 E4M3 scales of two slices of a row.  Each wave computes
-// 128 x 128 (4 x 4 MFMA tiles), so every dequantized A or B word feeds 4 MFMAs: half the
-// dequantization per MFMA of the 8-wave 128 x 64 arrangement.  With one wave per SIMD the
-// dequantization of step s+1 is interleaved between the MFMAs of step s.
+// scale records, each holding the 16 E4M3 scales of two slices of a row.  4 waves of 128 x 128
+// (TN = 4: 4 x 4 MFMA tiles, so each dequantized word feeds 4 MFMAs).  Each wave dequantizes,
+// between the MFMAs of step s, the operands of step s+1.  The loop is bound by VALU issue: a
+// lone wave issues at most one VALU instruction per 8 clocks (measured), and dequantization
+// costs 4 per 32-clock MFMA (2 conversions, 2 scale multiplies) plus addressing and scales.
+// The code is written for TN = 2 as well (8 waves of 128 x 64, two per SIMD, whose VALU issue
+// rate adds up), which measured slower.
 constexpr int NV4_CODES = 2 * GBM * ROWB;   // 32 KiB per stage
 constexpr int NV4_SREC = 2 * GBM * 16;      // 8 KiB per scale group (2 slices)
-static_assert(4 * NV4_CODES + 2 * NV4_SREC <= Fmt<2>::LDS, "NVFP4 4-wave LDS");
+static_assert(4 * NV4_CODES + 2 * NV4_SREC <= Fmt<2>::LDS, "NVFP4 DMA LDS");
 
-struct Nv4Words {
-    uint32_t a[4], b[4];
+template <int TN>
+struct NvWordsT {
+    uint32_t a[4], b[TN];
 };
-struct Nv4Ops {
-    half8_t a[4], b[4];
+template <int TN>
+struct NvOpsT {
+    half8_t a[4], b[TN];
 };
 
 // Step S (0..7) of a slice: lane (row, kh) holds the 8 codes of K elements 64kh + 8S .. +8,
 // dword S % 4 of chunk 2kh + S / 4 of its row (block 4kh + S / 2 of the slice).
-template <int S>
-__device__ __forceinline__ void nv4_read_words(const uint8_t* buf, int wm, int wn, int frow, int kh, Nv4Words& w) {
+template <int S, int TN>
+__device__ __forceinline__ void nvw_read_words(const uint8_t* buf, int wm, int wn, int frow, int kh, NvWordsT<TN>& w) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         w.a[i] = *(const uint32_t*)(buf + swz(wm + 32 * i + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
         w.b[j] = *(const uint32_t*)(buf + GBM * ROWB + swz(wn + 32 * j + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
 }
 
 // The lane's 4 scale bytes (blocks 4kh .. 4kh+3) of slice q (0/1) of a group record.
-__device__ __forceinline__ void nv4_read_scales(const uint8_t* sbuf, int q, int wm, int wn, int frow, int kh,
-                                                uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+template <int TN>
+__device__ __forceinline__ void nvw_read_scales(const uint8_t* sbuf, int q, int wm, int wn, int frow, int kh,
+                                                uint32_t (&sa)[4], uint32_t (&sb)[TN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sa[i] = *(const uint32_t*)(sbuf + (wm + 32 * i + frow) * 16 + 4 * (2 * q + kh));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = *(const uint32_t*)(sbuf + GBM * 16 + (wn + 32 * j + frow) * 16 + 4 * (2 * q + kh));
+    for (int j = 0; j < TN; ++j)
+        sb[j] = *(const uint32_t*)(sbuf + GBM * 16 + (wn + 32 * j + frow) * 16 + 4 * (2 * q + kh));
 }
 
-template <int S>
-__device__ __forceinline__ void nv4_ops(const Nv4Words& w, const uint32_t (&sa)[4], const uint32_t (&sb)[4], Nv4Ops& o) {
+template <int S, int TN>
+__device__ __forceinline__ void nvw_ops(const NvWordsT<TN>& w, const uint32_t (&sa)[4], const uint32_t (&sb)[TN],
+                                        NvOpsT<TN>& o) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.a[i] = nv_dequant(w.a[i], nv_scale(sa[i], S >> 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.b[j] = nv_dequant(w.b[j], nv_scale(sb[j], S >> 1));
+    for (int j = 0; j < TN; ++j) o.b[j] = nv_dequant(w.b[j], nv_scale(sb[j], S >> 1));
 }
 
-__device__ __forceinline__ void nv4_mfma16(const Nv4Ops& o, floatx16 (&acc)[4][4]) {
+template <int TN>
+__device__ __forceinline__ void nvw_mfma(const NvOpsT<TN>& o, floatx16 (&acc)[4][TN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
 }
 
 // One step (after its LDS reads, which a scheduling barrier keeps at the top of the step):
-// each of the 16 MFMAs followed by an equal share of the dequantization of the next step,
-// whose words were read a step earlier.
-__device__ __forceinline__ void nv4_interleave() {
+// each MFMA followed by an equal share of the dequantization of the next step, whose words
+// were read a step earlier.
+template <int TN>
+__device__ __forceinline__ void nvw_interleave() {
+    constexpr int NM = 4 * TN;                                  // MFMAs per step
+    constexpr int NV = ((4 + TN) * 8 + 2 * (4 + TN) + NM - 2) / (NM - 1);   // VALU per MFMA gap
 #pragma unroll
-    for (int i = 0; i < 15; ++i) {
+    for (int i = 0; i < NM - 1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 // Main loop.  Slice kt: wait for this wave's DMAs of slice kt+1 (everything issued before the
 // DMAs of slice kt-1), barrier, then 8 MFMA steps; the code DMAs of slice kt+3 are spread over
-// steps 0, 2, 4, 6 and, in odd slices, the scale group (kt+3)/2 (slices kt+3, kt+4) is fetched
-// at step 1 -- its buffer held group (kt-1)/2, whose last scales were read during slice kt-1.
+// the steps and, in odd slices, the scale group (kt+3)/2 (slices kt+3, kt+4) is fetched at
+// step 1 -- its buffer held group (kt-1)/2, whose last scales were read during slice kt-1.
 // Operand pipeline: during step s the words of step s+2 are read and those of step s+1 (read
 // during step s-1) are dequantized; steps 6 and 7 read the first two steps of slice kt+1, whose
-// scales are read at step 5.  An odd slice issues 10 DMAs and an even one 8, so the wait at the
-// top of an even slice allows 10 in flight; the prologue ends with an out-of-range group DMA
-// so that slice 0 fits the rule.  An out-of-range DMA lane still writes (zeros) to LDS: every
-// such DMA here targets a buffer whose contents are no longer, or not yet, needed.
-__device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
-                                              int wm, int wn, int lane, floatx16 (&acc)[4][4]) {
+// scales are read at step 5.  An odd slice issues DG more DMAs than an even one, so the wait
+// at the top of an even slice allows DC + DG in flight; the prologue ends with an out-of-range
+// group DMA so that slice 0 fits the rule.  An out-of-range DMA lane still writes (zeros) to
+// LDS: every such DMA here targets a buffer whose contents are no longer, or not yet, needed.
+template <int TN>
+__device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
+                                              int wm, int wn, int lane, floatx16 (&acc)[4][TN]) {
+    constexpr int NW = 16 / TN;           // waves
+    constexpr int PARTS = 16 / NW;        // code DMA parts per slice (4 or 2)
+    constexpr int DC = 2 * PARTS;         // code DMAs per lane per slice
+    constexpr int DG = NW == 4 ? 2 : 1;   // group DMAs per lane
+    constexpr int PSTEP = 8 / PARTS;      // steps between code DMA parts
     if (nk <= 0) return;
     const MxDma d = make_dma<2, 16>(g, m0, n0, lane);
     const int frow = lane & 31, kh = lane >> 5;
@@ -647,33 +675,30 @@ __device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int
     auto sbuf = [&](int64_t grp) { return lds + 4 * NV4_CODES + (int)(grp & 1) * NV4_SREC; };
     auto dma_slice = [&](int64_t k) {
         const bool live = k < nk;
-        mx_dma_codes<0>(d, k * 64, live, buf(k));
-        mx_dma_codes<1>(d, k * 64, live, buf(k));
-        mx_dma_codes<2>(d, k * 64, live, buf(k));
-        mx_dma_codes<3>(d, k * 64, live, buf(k));
+        static_for<0, PARTS>([&](auto p_c) { mx_dma_codes<decltype(p_c)::value, NW>(d, k * 64, live, buf(k)); });
     };
-    mx_dma_group(d, 0, true, sbuf(0));
-    mx_dma_group(d, 1, 2 < nk, sbuf(1));
+    mx_dma_group<NW>(d, 0, true, sbuf(0));
+    mx_dma_group<NW>(d, 1, 2 < nk, sbuf(1));
     dma_slice(0);
     dma_slice(1);
     dma_slice(2);
     // out of range: no memory traffic, but the DMA still writes its zeros -- into code stage 3,
     // which is free until slice 3's DMA (issued after it) refills it
-    mx_dma_group(d, 0, false, buf(3));
-    wait_vm_barrier<18>();
+    mx_dma_group<NW>(d, 0, false, buf(3));
+    wait_vm_barrier<2 * DC + DG>();
 
-    Nv4Words w1, w2;   // words of the next step and of the step after it
-    Nv4Ops cur, nxt;
-    uint32_t sa[4], sb[4], san[4], sbn[4];
-    nv4_read_scales(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
-    nv4_read_words<0>(buf(0), wm, wn, frow, kh, w1);
-    nv4_ops<0>(w1, sa, sb, cur);
-    nv4_read_words<1>(buf(0), wm, wn, frow, kh, w1);
+    NvWordsT<TN> w1, w2;   // words of the next step and of the step after it
+    NvOpsT<TN> cur, nxt;
+    uint32_t sa[4], sb[TN], san[4], sbn[TN];
+    nvw_read_scales<TN>(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
+    nvw_read_words<0, TN>(buf(0), wm, wn, frow, kh, w1);
+    nvw_ops<0, TN>(w1, sa, sb, cur);
+    nvw_read_words<1, TN>(buf(0), wm, wn, frow, kh, w1);
 
     auto slice = [&](int64_t kt, auto odd_c) {
         constexpr bool ODD = decltype(odd_c)::value;
-        if constexpr (ODD) wait_vm_barrier<8>();
-        else wait_vm_barrier<10>();
+        if constexpr (ODD) wait_vm_barrier<DC>();
+        else wait_vm_barrier<DC + DG>();
         const int64_t kd = kt + 3;
         const bool live = kd < nk;
         uint8_t* db = buf(kd);
@@ -681,30 +706,29 @@ __device__ __forceinline__ void nv4_main_loop(const GemmArgs& g, int64_t m0, int
         const uint8_t* nb = buf(kt + 1);
         static_for<0, 8>([&](auto s_c) {
             constexpr int S = decltype(s_c)::value;
-            if constexpr ((S & 1) == 0) mx_dma_codes<S / 2>(d, kd * 64, live, db);
+            if constexpr (S % PSTEP == 0) mx_dma_codes<S / PSTEP, NW>(d, kd * 64, live, db);
             if constexpr (ODD && S == 1) {
                 const int64_t grp = (kt + 3) / 2;
-                mx_dma_group(d, grp, 2 * grp < nk, sbuf(grp));
+                mx_dma_group<NW>(d, grp, 2 * grp < nk, sbuf(grp));
             }
             // words of step S+2 (the reads after the last slice touch a stale, in-bounds buffer)
-            if constexpr (S + 2 < 8) nv4_read_words<S + 2>(cb, wm, wn, frow, kh, w2);
-            else nv4_read_words<S + 2 - 8>(nb, wm, wn, frow, kh, w2);
-            if constexpr (S == 5) nv4_read_scales(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
+            if constexpr (S + 2 < 8) nvw_read_words<S + 2, TN>(cb, wm, wn, frow, kh, w2);
+            else nvw_read_words<S + 2 - 8, TN>(nb, wm, wn, frow, kh, w2);
+            if constexpr (S == 5) nvw_read_scales<TN>(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
             __builtin_amdgcn_sched_barrier(0);
             // dequantize step S+1
-            if constexpr (S + 1 < 8) nv4_ops<S + 1>(w1, sa, sb, nxt);
-            else nv4_ops<0>(w1, san, sbn, nxt);
-            nv4_mfma16(cur, acc);
-            nv4_interleave();
+            if constexpr (S + 1 < 8) nvw_ops<S + 1, TN>(w1, sa, sb, nxt);
+            else nvw_ops<0, TN>(w1, san, sbn, nxt);
+            nvw_mfma<TN>(cur, acc);
+            nvw_interleave<TN>();
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
             w1 = w2;
         });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = san[i];
-            sb[i] = sbn[i];
-        }
+        for (int i = 0; i < 4; ++i) sa[i] = san[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb[j] = sbn[j];
     };
     // nk is even
     for (int64_t kt = 0; kt < nk; kt += 2) {
@@ -817,7 +841,7 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
         if (g.K % (MX_GROUP * 64) == 0) mx_main_loop<true>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else mx_main_loop<false>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     } else {
-        nv4_main_loop(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        nvw_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
 
     float alpha = 1.0f;
