@@ -14,7 +14,15 @@
 //     (NVFP4) or 256-byte (MXFP8) segment from one wave.
 // The NVFP4 path runs an amax pass (atomic max of the binary32 bit pattern, which orders
 // like the value for non-negative floats) before the encode pass, because every block
-// scale depends on the per-tensor scale.
+// scale depends on the per-tensor scale.  The amax pass accumulates into a library-owned
+// pair of slots per (device, stream) that alternate between consecutive calls on that
+// stream: the encode pass of a call reads its slot, publishes amax and S to the caller's
+// amax_out / s_enc_out, and clears the other slot for the next call -- so no separate
+// reset launch precedes the amax pass.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -85,14 +93,36 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Atomic max of a non-negative float (its bit pattern orders as an unsigned integer).  The
+// atomic is skipped when the running maximum already covers v, which is safe: the value read
+// never exceeds the final maximum.
 __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
-    atomicMax((unsigned int*)p, __float_as_uint(v));
+    const unsigned cur = __hip_atomic_load((unsigned int*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(v) > cur) atomicMax((unsigned int*)p, __float_as_uint(v));
 }
 
-// ------------------------------------------------------------------ amax pass
+// Per-call amax accumulator: for each direction AMAX_SUB sub-slots, one per 128-byte line,
+// which workgroups update by workgroup index modulo AMAX_SUB; the consumer takes the max of
+// the sub-slots.  Spreading the atomics over lines keeps thousands of workgroups from
+// serialising on one address when the pass starts and every slot still reads zero.
+constexpr int AMAX_SUB = 64;
+constexpr int AMAX_STRIDE = 32;                             // floats per sub-slot line
+constexpr int AMAX_DIR = AMAX_SUB * AMAX_STRIDE;            // floats per direction
+constexpr int AMAX_SLOT = 2 * AMAX_DIR;                     // floats per call slot
 
-__global__ void reset_amax_kernel(float* amax) {
-    if (threadIdx.x < 2) amax[threadIdx.x] = 0.0f;
+__device__ __forceinline__ void amax_report(float* acc, int dir, unsigned wg, float v) {
+    atomic_max_nonneg(acc + dir * AMAX_DIR + (int)(wg % AMAX_SUB) * AMAX_STRIDE, v);
+}
+
+// The accumulated amax of direction dir, computed by every wave (lane l reads sub-slot l).
+__device__ __forceinline__ float amax_collect(const float* acc, int dir) {
+    const int l = threadIdx.x & 63;
+    return wave_max(acc[dir * AMAX_DIR + l * AMAX_STRIDE]);
+}
+
+// Clears both call slots of a stream (2 * AMAX_SLOT floats) on their first use.
+__global__ void reset_amax_kernel(float* slots) {
+    for (int i = threadIdx.x; i < 2 * AMAX_SLOT; i += blockDim.x) slots[i] = 0.0f;
 }
 
 // DIRS: which slots to fill (bit 0 rowwise, bit 1 columnwise).  Without RHT both
@@ -155,8 +185,9 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_kernel(const uint16_t* __
             a = __builtin_fmaxf(a, red[0][w]);
             b = __builtin_fmaxf(b, red[1][w]);
         }
-        if (DIRS & 1) atomic_max_nonneg(amax + 0, a);
-        if (DIRS & 2) atomic_max_nonneg(amax + 1, b);
+        const unsigned wg = blockIdx.y * gridDim.x + blockIdx.x;
+        if (DIRS & 1) amax_report(amax, 0, wg, a);
+        if (DIRS & 2) amax_report(amax, 1, wg, b);
     }
 }
 
@@ -170,11 +201,28 @@ struct NvEncodeArgs {
     uint8_t* row_scales;
     uint8_t* col_codes;
     uint8_t* col_scales;
-    const float* amax;
+    const float* acc;    // amax accumulated by this call's amax pass
+    float* acc_next;     // the other slot, cleared here for the next call on the stream
+    float* amax_out;
     float* s_enc_out;
     uint64_t seed;
     uint32_t stream;
 };
+
+// First wave of workgroup 0 of an encode pass: publish amax and S of both directions (a0, a1
+// collected by the wave) and clear the next call's slot.
+__device__ __forceinline__ void publish_scales(float a0, float a1, float* acc_next, float* amax_out,
+                                               float* s_enc_out) {
+    const int l = threadIdx.x;
+    if (l == 0) {
+        amax_out[0] = a0;
+        amax_out[1] = a1;
+        s_enc_out[0] = nvfp4_tensor_scale(a0);
+        s_enc_out[1] = nvfp4_tensor_scale(a1);
+    }
+    acc_next[l * AMAX_STRIDE] = 0.0f;
+    acc_next[AMAX_DIR + l * AMAX_STRIDE] = 0.0f;
+}
 
 // Encode one 16-block's worth of values held by this thread (n = 8 or 16 values) with the
 // block amax already known.  Writes the packed codes (n/2 bytes as n/8 words) into w[].
@@ -222,12 +270,10 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     SubTile q;
     load_subtile(a.x, R, C, t, q);
     const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
-    const float Srow = nvfp4_tensor_scale(a.amax[0]);
-    const float Scol = nvfp4_tensor_scale(a.amax[1]);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-        if (DIRS & 1) a.s_enc_out[0] = Srow;
-        if (DIRS & 2) a.s_enc_out[1] = Scol;
-    }
+    const float arow = amax_collect(a.acc, 0), acol = amax_collect(a.acc, 1);
+    const float Srow = nvfp4_tensor_scale(arow);
+    const float Scol = nvfp4_tensor_scale(acol);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) publish_scales(arow, acol, a.acc_next, a.amax_out, a.s_enc_out);
     const bool colok = t.c0 < C;
 
     if (DIRS & 1) {
@@ -506,8 +552,8 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_linear_kernel(const uint4* _
         float a = red[0];
 #pragma unroll
         for (int w = 1; w < LIN_THREADS / 64; ++w) a = __builtin_fmaxf(a, red[w]);
-        if (DIRS & 1) atomic_max_nonneg(amax + 0, a);
-        if (DIRS & 2) atomic_max_nonneg(amax + 1, a);
+        if (DIRS & 1) amax_report(amax, 0, blockIdx.x, a);
+        if (DIRS & 2) amax_report(amax, 1, blockIdx.x, a);
     }
 }
 
@@ -544,7 +590,7 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const 
         float a = red[0];
 #pragma unroll
         for (int w = 1; w < LIN_THREADS / 64; ++w) a = __builtin_fmaxf(a, red[w]);
-        atomic_max_nonneg(amax + 0, a);
+        amax_report(amax, 0, blockIdx.x, a);
     }
 }
 
@@ -554,13 +600,16 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
                                                                        const int8_t* __restrict__ signs,
                                                                        uint32_t* __restrict__ codes,
                                                                        uint8_t* __restrict__ scales,
-                                                                       const float* __restrict__ amax,
+                                                                       const float* __restrict__ acc,
+                                                                       float* __restrict__ acc_next,
+                                                                       float* __restrict__ amax_out,
                                                                        float* __restrict__ s_enc_out, uint64_t seed,
                                                                        uint32_t stream) {
     int64_t first, stride;
     lin_range(n16, first, stride);
-    const float S = nvfp4_tensor_scale(amax[0]);
-    if (blockIdx.x == 0 && threadIdx.x == 0) s_enc_out[0] = S;
+    const float arow = amax_collect(acc, 0);
+    const float S = nvfp4_tensor_scale(arow);
+    if (blockIdx.x == 0 && threadIdx.x < 64) publish_scales(arow, amax_collect(acc, 1), acc_next, amax_out, s_enc_out);
     const uint32_t neg = RHT ? sign_mask16(signs) : 0u;
     const bool upper = (threadIdx.x & 1) != 0;
     for (int64_t base = first; base < n16; base += stride) {
@@ -647,7 +696,7 @@ static inline dim3 tile_grid(int64_t R, int64_t C) {
 template <int DIRS, bool RHT, bool SR>
 static void launch_nv(const NvEncodeArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((nvfp4_amax_kernel<DIRS, RHT>), g, dim3(NTHREADS), 0, s, a.x, a.R, a.C, a.signs,
-                       (float*)a.amax);
+                       (float*)a.acc);
     hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR>), g, dim3(NTHREADS), 0, s, a);
 }
 
@@ -667,6 +716,35 @@ __global__ void empty_tensor_scales_kernel(float* amax, float* s_enc) {
     }
 }
 
+// The two amax slots of (device, stream); on first use they are cleared by a kernel on
+// that stream.  Returns the slot of this call and the one to clear for the next.
+struct AmaxSlots {
+    float* buf = nullptr;
+    unsigned parity = 0;
+};
+
+static int amax_slots(hipStream_t s, float** cur, float** nxt) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, AmaxSlots> slots;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    std::lock_guard<std::mutex> lock(mu);
+    AmaxSlots& sl = slots[{dev, s}];
+    if (sl.buf == nullptr) {
+        e = hipMalloc(&sl.buf, 2 * AMAX_SLOT * sizeof(float));
+        if (e != hipSuccess) {
+            sl.buf = nullptr;
+            return (int)e;
+        }
+        hipLaunchKernelGGL(reset_amax_kernel, dim3(1), dim3(256), 0, s, sl.buf);
+    }
+    *cur = sl.buf + AMAX_SLOT * sl.parity;
+    *nxt = sl.buf + AMAX_SLOT * (sl.parity ^ 1u);
+    sl.parity ^= 1u;
+    return 0;
+}
+
 int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
                           uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
                           uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, void* hip_stream) {
@@ -675,9 +753,11 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
         hipLaunchKernelGGL(empty_tensor_scales_kernel, dim3(1), dim3(64), 0, s, amax, s_enc);
         return (int)hipGetLastError();
     }
-    hipLaunchKernelGGL(reset_amax_kernel, dim3(1), dim3(64), 0, s, amax);
+    float *acc = nullptr, *acc_next = nullptr;
+    const int st = amax_slots(s, &acc, &acc_next);
+    if (st != 0) return st;
     NvEncodeArgs a{(const uint16_t*)x, R, C, signs, row_codes, row_scales, col_codes, col_scales,
-                   amax, s_enc, seed, stream};
+                   acc, acc_next, amax, s_enc, seed, stream};
     const dim3 g = tile_grid(R, C);
     const bool rht = signs != nullptr, sr = rounding == 1;
     const int64_t n16 = R * C / 8;
@@ -685,20 +765,21 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
     const unsigned lg = lin_grid(n16);
     if (direction == 1) {
         // rowwise only: two streaming passes
-        if (rht) hipLaunchKernelGGL(amax_rht_row_linear_kernel, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, amax);
-        else hipLaunchKernelGGL(amax_linear_kernel<1>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, amax);
+        if (rht) hipLaunchKernelGGL(amax_rht_row_linear_kernel, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, acc);
+        else hipLaunchKernelGGL(amax_linear_kernel<1>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, acc);
         uint32_t* rc = (uint32_t*)row_codes;
-        if (rht && sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
-        else if (rht) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
-        else if (sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
-        else hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, (const float*)amax, s_enc, seed, stream);
+        const float* ca = acc;
+        if (rht && sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
+        else if (rht) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
+        else if (sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
+        else hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
         return (int)hipGetLastError();
     }
     // columnwise (alone or with rowwise): the 256 x 128 tile kernels; without RHT the
     // amax pass is the streaming one
     if (!rht) {
-        if (direction == 2) hipLaunchKernelGGL(amax_linear_kernel<2>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, amax);
-        else hipLaunchKernelGGL(amax_linear_kernel<3>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, amax);
+        if (direction == 2) hipLaunchKernelGGL(amax_linear_kernel<2>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, acc);
+        else hipLaunchKernelGGL(amax_linear_kernel<3>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, acc);
         if (direction == 2) {
             if (sr) hipLaunchKernelGGL((nvfp4_encode_kernel<2, false, true>), g, dim3(NTHREADS), 0, s, a);
             else hipLaunchKernelGGL((nvfp4_encode_kernel<2, false, false>), g, dim3(NTHREADS), 0, s, a);

@@ -95,9 +95,13 @@ enum bsq_status {
  *              E4M3 bytes.  Required iff BSQ_ROW.
  *   col_codes  [cols][rows/2], col_scales [cols][rows/16]; required iff BSQ_COL.
  *   amax_out   float[2] (device): [0] the rowwise amax A, [1] the columnwise one.
- *              Also used as the accumulator of the amax pass.  Required.
+ *              Required.
  *   s_enc_out  float[2] (device): the matching tensor scales S.  Required.
  *              Slots of an unrequested direction are left unspecified.
+ * The amax pass accumulates into two library-owned device slots per (device, stream),
+ * allocated on the first call on that stream and used alternately by consecutive calls;
+ * calls on one stream are therefore ordered as usual, and calls on different streams do
+ * not share slots.  The first call on a stream allocates (hipMalloc) those 16 bytes.
  */
 int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding,
                    uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,

@@ -92,6 +92,37 @@ def test_nvfp4_zero_and_empty():
     assert got["amax"].cpu().tolist() == [0.0, 0.0] and got["s_enc"].cpu().tolist() == [1.0, 1.0]
 
 
+def test_amax_slots_alternate_per_stream():
+    """The amax accumulator is per (device, stream) and alternates between consecutive calls:
+    a call must never see the amax of an earlier call, on the same stream or on another."""
+    import oracle
+    big = outlier_bf16((256, 512), seed=81, mask_seed=82)        # amax in the hundreds
+    small = gaussian_bf16((256, 512), 1e-4, 83)                  # amax ~ 5e-4
+    refs = {id(t): oracle.nvfp4_quantize(t, direction=3) for t in (big, small)}
+    note("amax slots: alternating big/small tensors on one stream")
+    for t in (big, small, small, big, small):
+        got = bsq.nvfp4_quantize(t.to(DEV), direction=3)
+        torch.cuda.synchronize()
+        assert_f32_equal(got["amax"], refs[id(t)]["amax"], "amax")
+        assert_bytes_equal(got["row_codes"], refs[id(t)]["row_codes"], "row codes")
+    note("amax slots: two streams")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    xb, xs = big.to(DEV), small.to(DEV)
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            g1 = bsq.nvfp4_quantize(xb, direction=1)
+        with torch.cuda.stream(s2):
+            g2 = bsq.nvfp4_quantize(xs, direction=1)
+        outs.append((g1, g2))
+    torch.cuda.synchronize()
+    for g1, g2 in outs:
+        assert_f32_equal(g1["amax"][0:1], refs[id(big)]["amax"][0:1], "stream 1 amax")
+        assert_f32_equal(g2["amax"][0:1], refs[id(small)]["amax"][0:1], "stream 2 amax")
+        assert_bytes_equal(g2["row_codes"], refs[id(small)]["row_codes"], "stream 2 codes")
+
+
 def test_nvfp4_extreme_values():
     """Subnormal bf16, huge values and signed zeros in one tensor."""
     v = torch.tensor([0.0, -0.0, 1e-40, -1e-39, 3.0e38, -2.5e38, 1.0, -6.0] * 64, dtype=torch.float32)
