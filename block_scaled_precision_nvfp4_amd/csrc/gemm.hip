@@ -738,6 +738,53 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
     wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
 }
 
+// ---------------------------------------------------------------- epilogue
+
+// Epilogue of a tile that lies entirely inside C (4 waves of 128 x 128).  Each wave stages its
+// block in its own LDS region, row-major with rows padded by 16 bytes (the two lane halves of a
+// fragment write rows 4 apart, which the padding puts on different banks), and reads it back
+// as 16-byte row chunks for fully coalesced 16-byte global stores -- instead of one 2- or
+// 4-byte store per accumulator.  bf16 output takes all 128 rows in one pass (34 KiB per
+// wave); fp32 output two passes of 64 rows.  A wave reads back only what it wrote, and the LDS
+// executes one wave's instructions in order, so no barrier is needed between the two.
+template <bool OUT_F32>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, int64_t m0, int64_t n0, int wm,
+                                               int wn, int wave, int lane, float alpha, floatx16 (&acc)[4][4]) {
+    constexpr int ES = OUT_F32 ? 4 : 2;          // bytes per element
+    constexpr int ROWS = OUT_F32 ? 64 : 128;     // rows per pass
+    constexpr int RS = 128 * ES + 16;            // LDS row stride
+    constexpr int CPR = 128 * ES / 16;           // 16-byte chunks per row
+    static_assert(4 * ROWS * RS <= Fmt<2>::LDS && Fmt<2>::LDS == Fmt<1>::LDS, "epilogue staging");
+    uint8_t* reg = lds + wave * ROWS * RS;
+    const int frow = lane & 31, kh = lane >> 5;
+    uint8_t* cbase = (uint8_t*)g.c + ((m0 + wm) * g.N + n0 + wn) * ES;
+    static_for<0, 128 / ROWS>([&](auto h_c) {
+        constexpr int H = decltype(h_c)::value;
+        constexpr int I0 = H * ROWS / 32;
+        static_for<0, ROWS / 32>([&](auto i_c) {
+            constexpr int IL = decltype(i_c)::value;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * IL + 8 * (r >> 2) + 4 * kh + (r & 3);
+                    const float v = acc[I0 + IL][j][r] * alpha;
+                    if constexpr (OUT_F32) *(float*)(reg + row * RS + (32 * j + frow) * 4) = v;
+                    else *(__bf16*)(reg + row * RS + (32 * j + frow) * 2) = (__bf16)v;
+                }
+            }
+        });
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int p = 0; p < ROWS * CPR / 64; ++p) {
+            const int q = 64 * p + lane, row = q / CPR, c16 = q % CPR;
+            const uint4 v = *(const uint4*)(reg + row * RS + c16 * 16);
+            *(uint4*)(cbase + (int64_t)(H * ROWS + row) * g.N * ES + c16 * 16) = v;
+        }
+        asm volatile("" ::: "memory");
+    });
+}
+
 // Output tile of this workgroup.  Workgroup ids are dealt to the 8 XCDs round-robin; the
 // id is remapped so that XCD x receives the contiguous tile range [x*T/8, (x+1)*T/8),
 // walked in bands of GROUP tile-rows (column-major inside a band) for L2 reuse.
@@ -846,6 +893,15 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
 
     float alpha = 1.0f;
     if (F::NV) alpha = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
+    if constexpr (FMT != 0) {
+        constexpr int ES = OUT_F32 ? 4 : 2;
+        const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
+        if (full) {
+            __syncthreads();   // every wave is done with the operand buffers (and its DMAs)
+            store_tile_lds<OUT_F32>(g, lds, m0, n0, wm, wn, wave, lane, alpha, acc);
+            return;
+        }
+    }
     static_for<0, 4 * TN>([&](auto t_c) {
         constexpr int i = decltype(t_c)::value / TN, j = decltype(t_c)::value % TN;
         const int64_t col = n0 + wn + 32 * j + frow;
