@@ -8,7 +8,7 @@ resident in HBM:
   wgrad  16-point RHT + Philox SR, NVFP4 columnwise of dY[16384,14336] and X;
          dW = dY^T X (fp32)
   dgrad  per-direction (hybrid) recipe: MXFP8 rowwise of dY, MXFP8 columnwise of
-         bf16(dequant(NVFP4 rowwise W)); dX = dY W (bf16)
+         bf16(dequant(NVFP4 rowwise W)) (one fused call from W's NVFP4 codes); dX = dY W (bf16)
 value = the step's GEMM FLOPs (3 x 2MNK) / step time, in TFLOP/s.  The line also carries
 the NVFP4 quantize GB/s and the NVFP4 GEMM TFLOP/s of the forward pass, the roofline of
 the dominant kernel (the NVFP4 GEMM) timed with HIP events on its own stream, and the CPU
@@ -152,8 +152,7 @@ class Step:
         mark("g_wgrad1")
         # dgrad (MXFP8 backward operands; W from its rowwise-dequantized NVFP4 value)
         mdy = bsq.mxfp8_quantize(self.dY, direction=bsq.ROW)
-        wdq = bsq.nvfp4_dequantize(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1])
-        mw = bsq.mxfp8_quantize(wdq, direction=bsq.COL)
+        mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL)
         mark("g_dgrad0")
         dx = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["row_codes"], mdy["row_scales"], None,
                                   mw["col_codes"], mw["col_scales"], None, out_dtype=torch.bfloat16)

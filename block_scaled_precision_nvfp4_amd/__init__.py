@@ -47,10 +47,11 @@ def lib():
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
+        L.mxfp8_requantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
         L.rht_apply.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.blockscaled_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
-        for f in ("nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "rht_apply", "blockscaled_gemm",
-                  "bsq_version"):
+        for f in ("nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
+                  "blockscaled_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int
         L.bsq_last_error.argtypes = []
         L.bsq_last_error.restype = C.c_char_p
@@ -148,6 +149,32 @@ def mxfp8_quantize(x: torch.Tensor, direction: int = ROW) -> Dict[str, torch.Ten
     _check("mxfp8_quantize", lib().mxfp8_quantize(
         x.data_ptr(), R, Cc, direction, _ptr(out.get("row_codes")), _ptr(out.get("row_scales")),
         _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _stream(dev)))
+    return out
+
+
+def mxfp8_requantize_nvfp4(codes: torch.Tensor, scales: torch.Tensor, s_enc: torch.Tensor,
+                           direction: int = COL) -> Dict[str, torch.Tensor]:
+    """MXFP8 cast of the rowwise-dequantized value of an NVFP4 rowwise tensor (``codes``
+    [rows, cols/2], ``scales`` [rows, cols/16], 1-element float32 ``s_enc``), without the
+    bf16 intermediate; bit-identical to ``mxfp8_quantize(nvfp4_dequantize(...))``."""
+    _dev_tensor(codes, torch.uint8, "codes")
+    _dev_tensor(scales, torch.uint8, "scales")
+    _dev_tensor(s_enc, torch.float32, "s_enc")
+    R, Cc = codes.shape[0], codes.shape[1] * 2
+    if tuple(scales.shape) != (R, Cc // 16):
+        raise ValueError("scales must be [rows, cols/16]")
+    dev = codes.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out: Dict[str, torch.Tensor] = {}
+    if direction & ROW:
+        out["row_codes"] = torch.empty((R, Cc), **u8)
+        out["row_scales"] = torch.empty((R, Cc // 32), **u8)
+    if direction & COL:
+        out["col_codes"] = torch.empty((Cc, R), **u8)
+        out["col_scales"] = torch.empty((Cc, R // 32), **u8)
+    _check("mxfp8_requantize_nvfp4", lib().mxfp8_requantize_nvfp4(
+        codes.data_ptr(), scales.data_ptr(), s_enc.data_ptr(), R, Cc, direction, _ptr(out.get("row_codes")),
+        _ptr(out.get("row_scales")), _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _stream(dev)))
     return out
 
 

@@ -98,6 +98,25 @@ int mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int direction, uin
                                                col_scales, hip_stream), fn);
 }
 
+int mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows,
+                           int64_t cols, int direction, uint8_t* row_codes, uint8_t* row_scales,
+                           uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
+    static const char* fn = "mxfp8_requantize_nvfp4";
+    if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (cols % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 16", fn, (long long)cols);
+    if ((direction & BSQ_ROW) && cols % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: rowwise needs cols %% 32 == 0, got %lld", fn, (long long)cols);
+    if ((direction & BSQ_COL) && rows % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: columnwise needs rows %% 32 == 0, got %lld", fn, (long long)rows);
+    if (rows == 0 || cols == 0) return ok();
+    if (!codes || !scales || !s_enc) return fail(BSQ_ERR_NULL, "%s: NVFP4 input is NULL", fn);
+    if ((direction & BSQ_ROW) && (!row_codes || !row_scales)) return fail(BSQ_ERR_NULL, "%s: rowwise outputs are NULL", fn);
+    if ((direction & BSQ_COL) && (!col_codes || !col_scales)) return fail(BSQ_ERR_NULL, "%s: columnwise outputs are NULL", fn);
+    if (misaligned(codes) || misaligned(row_codes) || misaligned(col_codes))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_mxfp8_requantize_nvfp4(codes, scales, s_enc, rows, cols, direction, row_codes,
+                                                       row_scales, col_codes, col_scales, hip_stream), fn);
+}
+
 int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t* signs, float* out,
               void* hip_stream) {
     static const char* fn = "rht_apply";

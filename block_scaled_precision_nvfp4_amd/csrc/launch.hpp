@@ -15,6 +15,9 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream);
 int launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows,
                             int64_t cols, void* out, void* hip_stream);
+int launch_mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t R,
+                                  int64_t C, int direction, uint8_t* row_codes, uint8_t* row_scales,
+                                  uint8_t* col_codes, uint8_t* col_scales, void* hip_stream);
 int launch_rht_apply(const void* x, int64_t R, int64_t C, int axis, const int8_t* signs, float* out,
                      void* hip_stream);
 int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,

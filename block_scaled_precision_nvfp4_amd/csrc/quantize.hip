@@ -345,8 +345,45 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float m) {
 // 2^-X for scale byte b (X = b - 127): binary32 with exponent field 254 - b (b <= 246).
 __device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
 
+// bf16 bits of the dequantized NVFP4 element with code c (4 bits) in a block with scale value
+// sc: bf16_RNE((E2M1(c) * sc) / S).  The product is exact; one rounded division, then RNE.
+__device__ __forceinline__ uint32_t nvfp4_dequant_bf16(uint32_t c, float sc, float S) {
+    const uint32_t m = c & 7u;
+    const float mag = m <= 4u ? 0.5f * (float)m : (m == 5u ? 3.0f : (m == 6u ? 4.0f : 6.0f));
+    const float e = (c & 8u) ? -mag : mag;
+    return f32_to_bf16_rne((e * sc) / S);
+}
+
+// Sub-tile of the bf16 tensor bf16(dequant(NVFP4 rowwise)) -- the same values the dequantize
+// kernel writes -- computed from the codes and scales: row j of the thread's 16 x 8 sub-tile
+// is code word c0/8 of the row and scale byte c0/16.
+__device__ __forceinline__ void load_subtile_nvfp4(const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ scales, float S, int64_t R,
+                                                   int64_t C, const TileCoord& t, SubTile q) {
+    const bool colok = t.c0 < C;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int64_t r = t.r0 + j;
+        uint32_t cw = 0u, sbyte = 0u;
+        if (colok && r < R) {
+            cw = *(const uint32_t*)(codes + r * (C / 2) + t.c0 / 2);
+            sbyte = scales[r * (C / 16) + t.c0 / 16];
+        }
+        const float sc = e4m3_decode_nonneg(sbyte & 0x7Fu);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = nvfp4_dequant_bf16((cw >> (8 * w)) & 0xFu, sc, S);
+            const uint32_t hi = nvfp4_dequant_bf16((cw >> (8 * w + 4)) & 0xFu, sc, S);
+            q[j][w] = lo | (hi << 16);
+        }
+    }
+}
+
 struct MxArgs {
-    const uint16_t* x;
+    const uint16_t* x;         // bf16 source, or
+    const uint8_t* nv_codes;   // NVFP4 rowwise source (codes, scales, tensor scale)
+    const uint8_t* nv_scales;
+    const float* nv_s_enc;
     int64_t R, C;
     uint8_t* row_codes;
     uint8_t* row_scales;
@@ -354,12 +391,14 @@ struct MxArgs {
     uint8_t* col_scales;
 };
 
-template <int DIRS>
+// SRC 0: bf16 input; SRC 1: the rowwise-dequantized value of an NVFP4 tensor.
+template <int DIRS, int SRC = 0>
 __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
     SubTile q;
-    load_subtile(a.x, R, C, t, q);
+    if constexpr (SRC == 0) load_subtile(a.x, R, C, t, q);
+    else load_subtile_nvfp4(a.nv_codes, a.nv_scales, a.nv_s_enc[0], R, C, t, q);
     const bool colok = t.c0 < C;
 
     if (DIRS & 1) {
@@ -443,11 +482,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const uint32_t c = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 0xFu;
-        const float mag = (c & 7u) <= 4u ? 0.5f * (float)(c & 7u) : ((c & 7u) == 5u ? 3.0f : ((c & 7u) == 6u ? 4.0f : 6.0f));
-        const float e = (c & 8u) ? -mag : mag;
-        const float p = e * sc;
-        const float d = p / S;
-        const uint32_t h = f32_to_bf16_rne(d);
+        const uint32_t h = nvfp4_dequant_bf16(c, sc, S);
         if (j & 1) o[j >> 1] |= h << 16; else o[j >> 1] = h;
     }
     uint4* dst = (uint4*)(out + 16 * b);
@@ -798,7 +833,7 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
     if (R == 0 || C == 0) return 0;
     hipStream_t s = (hipStream_t)hip_stream;
-    MxArgs a{(const uint16_t*)x, R, C, row_codes, row_scales, col_codes, col_scales};
+    MxArgs a{(const uint16_t*)x, nullptr, nullptr, nullptr, R, C, row_codes, row_scales, col_codes, col_scales};
     const dim3 g = tile_grid(R, C);
     if (direction == 1) {
         const int64_t n16 = R * C / 8;
@@ -806,6 +841,19 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
                            (uint2*)row_codes, row_scales);
     } else if (direction == 2) hipLaunchKernelGGL(mxfp8_kernel<2>, g, dim3(NTHREADS), 0, s, a);
     else hipLaunchKernelGGL(mxfp8_kernel<3>, g, dim3(NTHREADS), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+int launch_mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t R,
+                                  int64_t C, int direction, uint8_t* row_codes, uint8_t* row_scales,
+                                  uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
+    if (R == 0 || C == 0) return 0;
+    hipStream_t s = (hipStream_t)hip_stream;
+    MxArgs a{nullptr, codes, scales, s_enc, R, C, row_codes, row_scales, col_codes, col_scales};
+    const dim3 g = tile_grid(R, C);
+    if (direction == 1) hipLaunchKernelGGL((mxfp8_kernel<1, 1>), g, dim3(NTHREADS), 0, s, a);
+    else if (direction == 2) hipLaunchKernelGGL((mxfp8_kernel<2, 1>), g, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((mxfp8_kernel<3, 1>), g, dim3(NTHREADS), 0, s, a);
     return (int)hipGetLastError();
 }
 

@@ -139,6 +139,23 @@ int mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int direction,
                    uint8_t* col_scales, void* hip_stream);
 
 /*
+ * mxfp8_requantize_nvfp4 -- MXFP8 cast (as mxfp8_quantize) of the bf16 tensor
+ * nvfp4_dequantize(codes, scales, s_enc), computed from the NVFP4 rowwise codes and scales
+ * without materialising the bf16 tensor: the "rowwise_dequantized" columnwise source of the
+ * hybrid quantizer (page "[Pytorch][Common] Hybrid quantization", TransformerEngine PR
+ * #2817, commit note "Enable columnwise_source and hybrid recipes": the backward operand is
+ * built from dequantize(rowwise(x))), fused.  Bit-identical to nvfp4_dequantize followed by
+ * mxfp8_quantize.
+ *   codes [rows][cols/2], scales [rows][cols/16], s_enc float[1]: an NVFP4 rowwise tensor
+ *              (device).  cols % 16 == 0.
+ *   direction, outputs and their preconditions as for mxfp8_quantize.
+ */
+int mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* s_enc,
+                           int64_t rows, int64_t cols, int direction, uint8_t* row_codes,
+                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                           void* hip_stream);
+
+/*
  * rht_apply -- the 16-point random Hadamard transform on its own: out = fp32 of
  * each 16-block of x times diag(d) H16 / 4 (same definition and evaluation order as
  * in nvfp4_quantize; page "Add an NVFP4 quantization converter", Summary: the

@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for f in ["nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "rht_apply", "blockscaled_gemm",
-              "bsq_last_error", "bsq_version"]:
+    for f in ["nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
+              "blockscaled_gemm", "bsq_last_error", "bsq_version"]:
         assert f in names
 
 
@@ -83,6 +83,19 @@ def test_mxfp8_quantize_validation(L):
     assert f(None, 64, 64, 1, FAKE, FAKE, None, None, None) == 1
     assert f(FAKE, 64, 64, 2, FAKE, FAKE, None, FAKE, None) == 1
     assert f(FAKE + 4, 64, 64, 1, FAKE, FAKE, None, None, None) == 6
+
+
+def test_mxfp8_requantize_validation(L):
+    f = L.mxfp8_requantize_nvfp4
+    assert f(FAKE, FAKE, FAKE, 64, 64, 0, FAKE, FAKE, None, None, None) == 3 and "direction" in last(L)
+    assert f(FAKE, FAKE, FAKE, 64, 24, 2, None, None, FAKE, FAKE, None) == 2 and "multiple of 16" in last(L)
+    assert f(FAKE, FAKE, FAKE, 64, 48, 1, FAKE, FAKE, None, None, None) == 2 and "cols % 32" in last(L)
+    assert f(FAKE, FAKE, FAKE, 48, 64, 2, None, None, FAKE, FAKE, None) == 2 and "rows % 32" in last(L)
+    assert f(FAKE, None, FAKE, 64, 64, 2, None, None, FAKE, FAKE, None) == 1 and "NVFP4 input" in last(L)
+    assert f(FAKE, FAKE, None, 64, 64, 2, None, None, FAKE, FAKE, None) == 1
+    assert f(FAKE, FAKE, FAKE, 64, 64, 2, None, None, None, FAKE, None) == 1 and "columnwise outputs" in last(L)
+    assert f(FAKE + 4, FAKE, FAKE, 64, 64, 2, None, None, FAKE, FAKE, None) == 6
+    assert f(FAKE, FAKE, FAKE, 0, 64, 2, None, None, FAKE, FAKE, None) == 0
 
 
 def test_rht_apply_validation(L):

@@ -166,6 +166,27 @@ def test_hybrid_qwen3_8b_sampled():
                   label="hybrid wgrad")
 
 
+@pytest.mark.parametrize("shape,direction", [((4096, 1024), 2), ((256, 512), 3), ((96, 160), 1), ((200, 64), 1)])
+def test_fused_requantize_matches_chain(shape, direction):
+    """mxfp8_requantize_nvfp4 = mxfp8_quantize(nvfp4_dequantize(.)) bit for bit, against the
+    oracle's chain and the library's own two-call chain (ragged row counts for rowwise)."""
+    import oracle
+    X = outlier_bf16(shape, seed=shape[0] + 3, mask_seed=shape[1] + 5)
+    note("fused requantize %s dir=%d" % (shape, direction))
+    q = bsq.nvfp4_quantize(X.to(DEV), direction=1)
+    f = bsq.mxfp8_requantize_nvfp4(q["row_codes"], q["row_scales"], q["s_enc"][0:1], direction=direction)
+    d = bsq.nvfp4_dequantize(q["row_codes"], q["row_scales"], q["s_enc"][0:1])
+    m = bsq.mxfp8_quantize(d, direction=direction)
+    torch.cuda.synchronize()
+    rq = oracle.nvfp4_quantize(X, direction=1)
+    rd = oracle.nvfp4_dequantize(rq["row_codes"], rq["row_scales"], float(rq["s_enc"][0]))
+    rm = oracle.mxfp8_quantize(rd, direction=direction)
+    for key in (("row",) if direction & 1 else ()) + (("col",) if direction & 2 else ()):
+        for part in ("_codes", "_scales"):
+            assert_bytes_equal(f[key + part], rm[key + part], "fused vs oracle " + key + part)
+            assert torch.equal(f[key + part], m[key + part]), "fused vs two-call chain " + key + part
+
+
 def test_hybrid_rowwise_dequantized_source():
     """columnwise_source = rowwise_dequantized: MXFP8 columnwise of bf16(dequant(NVFP4 rowwise X));
     compared bit for bit with the oracle's chain on a [4096, 1024] slice of the workload."""
