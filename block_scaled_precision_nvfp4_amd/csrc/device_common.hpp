@@ -135,9 +135,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
         // one 32 x 32 -> 64-bit multiply per product (v_mad_u64_u32) instead of mul_lo + mul_hi
         const uint64_t p0 = (uint64_t)M0 * c.x, p1 = (uint64_t)M1 * c.z;
         u32x4 n;
-        n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+        // three-input XOR in one v_bitop3_b32 (truth table 0x96)
+        n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);
         n.y = (uint32_t)p1;
-        n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
         n.w = (uint32_t)p0;
         c = n;
         k0 += W0;
