@@ -80,6 +80,13 @@ def lib():
                                           u8p, u8p, C.c_float, u8p, u8p, C.c_float,
                                           i64p, C.c_int64, i64p, C.c_int64, f64p]
         L.or_blockscaled_gemm.restype = C.c_int
+        L.or_nvfp4_quantize_rowscaled.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int, C.c_uint64, C.c_uint32,
+                                                  i8p, u8p, u8p, f32p, f32p]
+        L.or_nvfp4_quantize_rowscaled.restype = C.c_int
+        L.or_blockscaled_gemm_rows.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64,
+                                               u8p, u8p, f32p, C.c_int, u8p, u8p, f32p, C.c_int,
+                                               i64p, C.c_int64, i64p, C.c_int64, f64p]
+        L.or_blockscaled_gemm_rows.restype = C.c_int
         L.or_num_threads.argtypes = []; L.or_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -208,6 +215,26 @@ def nvfp4_quantize(x, direction: int = ROW, rounding: int = RNE, sr_seed: int = 
     return out
 
 
+def nvfp4_quantize_rowscaled(x, rounding: int = RNE, sr_seed: int = 0, sr_stream: int = 0, signs=None) -> dict:
+    """Row-scaled NVFP4 (rowwise, one amax and tensor scale per row) of bf16 x[R][C].
+    Returns codes [R][C/2], scales [R][C/16], amax[R], s_enc[R]."""
+    xb = _bits(x)
+    R, Cc = xb.shape
+    codes = np.zeros((R, Cc // 2), np.uint8)
+    scales = np.zeros((R, Cc // 16), np.uint8)
+    amax = np.zeros(R, np.float32)
+    s_enc = np.zeros(R, np.float32)
+    sg = _signs(signs)
+    u8 = C.c_uint8
+    st = lib().or_nvfp4_quantize_rowscaled(
+        _p(xb, C.c_uint16), R, Cc, rounding, sr_seed & (2**64 - 1), sr_stream,
+        _p(sg, C.c_int8) if sg is not None else C.POINTER(C.c_int8)(),
+        _p(codes, u8), _p(scales, u8), _p(amax, C.c_float), _p(s_enc, C.c_float))
+    if st != 0:
+        raise ValueError("oracle nvfp4_quantize_rowscaled failed with status %d" % st)
+    return {"codes": codes, "scales": scales, "amax": amax, "s_enc": s_enc}
+
+
 def nvfp4_dequantize(codes: np.ndarray, scales: np.ndarray, s_enc: float) -> np.ndarray:
     """bf16 bits [rows][cols] of the dequantized NVFP4 tensor."""
     rows, half = codes.shape
@@ -256,7 +283,9 @@ def rht_apply(x, axis: int, signs) -> np.ndarray:
 
 def blockscaled_gemm(fmt: int, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc,
                      rows=None, cols=None) -> np.ndarray:
-    """binary64 C = A B^T of the dequantized operands (optionally only rows x cols of C)."""
+    """binary64 C = A B^T of the dequantized operands (optionally only rows x cols of C).
+    An NVFP4 tensor scale is a number (per-tensor) or an array with one scale per row of
+    that operand (row-scaled)."""
     M = a_codes.shape[0]
     N = b_codes.shape[0]
     K = a_codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
@@ -264,10 +293,15 @@ def blockscaled_gemm(fmt: int, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_
     ni = np.ascontiguousarray(np.arange(N, dtype=np.int64) if cols is None else np.asarray(cols, np.int64))
     out = np.zeros((mi.size, ni.size), np.float64)
     u8 = C.c_uint8
-    st = lib().or_blockscaled_gemm(
+    sa = np.ascontiguousarray(np.atleast_1d(np.asarray(a_s_enc, np.float32)))
+    sb = np.ascontiguousarray(np.atleast_1d(np.asarray(b_s_enc, np.float32)))
+    a_rows, b_rows = int(sa.size > 1 or (sa.size == M and M > 1)), int(sb.size > 1 or (sb.size == N and N > 1))
+    if a_rows and sa.size != M or b_rows and sb.size != N:
+        raise ValueError("per-row tensor scales must have one entry per operand row")
+    st = lib().or_blockscaled_gemm_rows(
         fmt, M, N, K,
-        _p(np.ascontiguousarray(a_codes), u8), _p(np.ascontiguousarray(a_scales), u8), float(a_s_enc),
-        _p(np.ascontiguousarray(b_codes), u8), _p(np.ascontiguousarray(b_scales), u8), float(b_s_enc),
+        _p(np.ascontiguousarray(a_codes), u8), _p(np.ascontiguousarray(a_scales), u8), _p(sa, C.c_float), a_rows,
+        _p(np.ascontiguousarray(b_codes), u8), _p(np.ascontiguousarray(b_scales), u8), _p(sb, C.c_float), b_rows,
         _p(mi, C.c_int64), mi.size, _p(ni, C.c_int64), ni.size, _p(out, C.c_double))
     if st != 0:
         raise ValueError("oracle blockscaled_gemm failed with status %d" % st)

@@ -305,19 +305,20 @@ uint8_t or_nvfp4_block_scale(float block_amax, float s_enc)
 }
 
 /* NVFP4 quantization of every row of v[rows][cols] (cols % 16 == 0) with tensor
- * scale s_enc.  Writes codes [rows][cols/2] (element 2j in the low nibble of
+ * scale s_tensor, or with row r's own scale s_rows[r] when s_rows is given.  Writes codes [rows][cols/2] (element 2j in the low nibble of
  * byte j, element 2j+1 in the high nibble) and scales [rows][cols/16].  For a
  * nonzero block scale s_b the elements are multiplied by S / fp32(s_b) (one
  * division, then one multiplication per element) and rounded onto E2M1; a zero
  * block scale gives all-zero codes.  Under SR, element i (linear index in this
  * [rows][cols] output) draws its word from or_sr_word(seed, stream, dir, i). */
-static void quantize_rows_nvfp4(const float* v, int64_t rows, int64_t cols, float s_enc,
-                                int rounding, uint64_t seed, uint32_t stream, uint32_t dir,
-                                uint8_t* codes, uint8_t* scales)
+static void quantize_rows_nvfp4(const float* v, int64_t rows, int64_t cols, float s_tensor,
+                                const float* s_rows, int rounding, uint64_t seed, uint32_t stream,
+                                uint32_t dir, uint8_t* codes, uint8_t* scales)
 {
     const int64_t nb = cols / 16;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
+        const float s_enc = s_rows ? s_rows[r] : s_tensor;
         for (int64_t b = 0; b < nb; ++b) {
             const float* blk = v + r * cols + 16 * b;
             float bmax = 0.0f;
@@ -372,13 +373,40 @@ int or_nvfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int direction, in
         if (signs) rht_rows(v, rows, cols, signs);
         float a = amax_of(v, rows * cols);
         float s = or_nvfp4_tensor_scale(a);
-        quantize_rows_nvfp4(v, rows, cols, s, rounding, seed, stream, (uint32_t)dir,
+        quantize_rows_nvfp4(v, rows, cols, s, NULL, rounding, seed, stream, (uint32_t)dir,
                             dir == 0 ? row_codes : col_codes,
                             dir == 0 ? row_scales : col_scales);
         amax_out[dir] = a;
         s_enc_out[dir] = s;
         free(v);
     }
+    return 0;
+}
+
+/* Row-scaled NVFP4 (the "row_scaled_nvfp4" rowwise quantizer of the Composer-style recipe
+ * on the page "[Pytorch][Common] Hybrid quantization"; outer scale per row, inner scale
+ * 1x16, as asked in the review of "Add an NVFP4 quantization converter"): the rowwise
+ * quantization above with each row's own amax A_r and tensor scale S_r = f(A_r) (same
+ * rule as the per-tensor scale) in place of the tensor's.  With a sign vector the RHT is
+ * applied along the rows first and A_r is taken over the transformed row.  Writes codes
+ * [R][C/2], scales [R][C/16], amax_rows[R], s_enc_rows[R].  SR words are drawn exactly
+ * as for the rowwise per-tensor quantization (direction 0, linear output index). */
+int or_nvfp4_quantize_rowscaled(const uint16_t* x, int64_t R, int64_t C, int rounding,
+                                uint64_t seed, uint32_t stream, const int8_t* signs,
+                                uint8_t* codes, uint8_t* scales, float* amax_rows,
+                                float* s_enc_rows)
+{
+    if (C % 16 != 0) return -1;
+    float* v = widen(x, R, C, 0);
+    if (!v) return -2;
+    if (signs) rht_rows(v, R, C, signs);
+    for (int64_t r = 0; r < R; ++r) {
+        float a = amax_of(v + r * C, C);
+        amax_rows[r] = a;
+        s_enc_rows[r] = or_nvfp4_tensor_scale(a);
+    }
+    quantize_rows_nvfp4(v, R, C, 0.0f, s_enc_rows, rounding, seed, stream, 0u, codes, scales);
+    free(v);
     return 0;
 }
 
@@ -519,13 +547,15 @@ static double deq_elem(int fmt, const uint8_t* codes, const uint8_t* scales, dou
 /* Block-scaled GEMM C = A * B^T on the dequantized operands, A [M][K], B [N][K]
  * (both stored along K), in binary64: C[m][n] = sum_k A[m][k] * B[n][k].  Only
  * the rows mi[0..nm) and columns ni[0..nn) of C are computed, into
- * out[nm][nn]; pass every index for the full product.  s_enc values are the
- * per-tensor scales (ignored for MXFP8). */
-int or_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
-                        const uint8_t* a_codes, const uint8_t* a_scales, float a_s_enc,
-                        const uint8_t* b_codes, const uint8_t* b_scales, float b_s_enc,
-                        const int64_t* mi, int64_t nm, const int64_t* ni, int64_t nn,
-                        double* out)
+ * out[nm][nn]; pass every index for the full product.  NVFP4 tensor scales:
+ * a_s[0] for every row of A, or a_s[m] for row m when a_per_row (row-scaled
+ * operand); likewise b_s for the rows of B.  Ignored for MXFP8. */
+int or_blockscaled_gemm_rows(int fmt, int64_t M, int64_t N, int64_t K,
+                             const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s,
+                             int a_per_row, const uint8_t* b_codes, const uint8_t* b_scales,
+                             const float* b_s, int b_per_row,
+                             const int64_t* mi, int64_t nm, const int64_t* ni, int64_t nn,
+                             double* out)
 {
     if (fmt == 0 && K % 16 != 0) return -1;
     if (fmt == 1 && K % 32 != 0) return -1;
@@ -543,11 +573,11 @@ int or_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < nm; ++i)
         for (int64_t k = 0; k < K; ++k)
-            a[i * K + k] = deq_elem(fmt, a_codes, a_scales, (double)a_s_enc, K, mi[i], k);
+            a[i * K + k] = deq_elem(fmt, a_codes, a_scales, (double)a_s[a_per_row ? mi[i] : 0], K, mi[i], k);
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < nn; ++j)
         for (int64_t k = 0; k < K; ++k)
-            b[j * K + k] = deq_elem(fmt, b_codes, b_scales, (double)b_s_enc, K, ni[j], k);
+            b[j * K + k] = deq_elem(fmt, b_codes, b_scales, (double)b_s[b_per_row ? ni[j] : 0], K, ni[j], k);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < nm; ++i)
         for (int64_t j = 0; j < nn; ++j) {
@@ -558,6 +588,17 @@ int or_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
     free(a);
     free(b);
     return 0;
+}
+
+/* The same with one tensor scale per operand. */
+int or_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* a_codes, const uint8_t* a_scales, float a_s_enc,
+                        const uint8_t* b_codes, const uint8_t* b_scales, float b_s_enc,
+                        const int64_t* mi, int64_t nm, const int64_t* ni, int64_t nn,
+                        double* out)
+{
+    return or_blockscaled_gemm_rows(fmt, M, N, K, a_codes, a_scales, &a_s_enc, 0, b_codes, b_scales,
+                                    &b_s_enc, 0, mi, nm, ni, nn, out);
 }
 
 /* Number of OpenMP threads the oracle uses. */
