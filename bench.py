@@ -164,6 +164,34 @@ class Step:
         return sum(x.elapsed_time(y) for x, y in zip(a, b)) / len(a)
 
 
+def rowscaled_figures(step, iters: int):
+    """Side figures outside the step: row-scaled NVFP4 (one outer scale per row) of X and the
+    forward GEMM with row-scaled X, each timed over ``iters`` back-to-back launches."""
+    bsq, torch = step.bsq, step.torch
+    qw = bsq.nvfp4_quantize(step.W, direction=bsq.ROW)
+    qx = bsq.nvfp4_quantize_rowscaled(step.X)
+    fmt = bsq.FMT_NVFP4 | bsq.FMT_A_ROWSCALED
+    y = bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"], qw["row_scales"],
+                             qw["s_enc"][0:1])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(iters):
+        bsq.nvfp4_quantize_rowscaled(step.X)
+    ev[1].record()
+    for _ in range(iters):
+        bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"], qw["row_scales"],
+                             qw["s_enc"][0:1], out=y)
+    ev[2].record()
+    torch.cuda.synchronize()
+    q_ms = ev[0].elapsed_time(ev[1]) / iters
+    g_ms = ev[1].elapsed_time(ev[2]) / iters
+    q_bytes = M_TOK * K_IN * NVFP4_BYTES_PER_ELT + 8.0 * M_TOK   # + amax and S per row
+    return {"nvfp4_rowscaled_quant_X_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "nvfp4_rowscaled_quant_X_ms": round(q_ms, 4),
+            "gemm_fwd_rowscaled_X_TFLOPs": round(2.0 * M_TOK * N_OUT * K_IN / (g_ms * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(tokens: int):
     """The oracle on a token-sample of the step: the same operations with M = tokens."""
     import numpy as np
@@ -231,6 +259,7 @@ def main():
     g_dgrad = step.avg_ms("g_dgrad")
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
+    side = rowscaled_figures(step, max(3, args.steps // 2))
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
     tr = measured_traffic()
     # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
@@ -253,6 +282,7 @@ def main():
         "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "gemm_fwd_nvfp4": round(g_fwd, 4),
                       "gemm_wgrad_nvfp4": round(g_wgrad, 4), "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
         "mxfp8_gemm_TFLOPs": round(gemm_flops / (g_dgrad * 1e-3) / 1e12, 2),
+        "row_scaled": side,
         "roofline": roofline,
         "cpu_baseline": None,
     }

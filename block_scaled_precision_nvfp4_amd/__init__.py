@@ -18,6 +18,7 @@ import torch
 ROW, COL = 1, 2
 RNE, SR = 0, 1
 FMT_NVFP4, FMT_MXFP8 = 0, 1
+FMT_A_ROWSCALED, FMT_B_ROWSCALED = 0x10, 0x20
 OUT_BF16, OUT_F32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,12 +46,13 @@ def lib():
         L = C.CDLL(LIB_PATH)
         vp, i64, i32, u32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize_rowscaled.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp]
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
         L.mxfp8_requantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
         L.rht_apply.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.blockscaled_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
-        for f in ("nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
+        for f in ("nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
                   "blockscaled_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int
         L.bsq_last_error.argtypes = []
@@ -117,6 +119,24 @@ def nvfp4_quantize(x: torch.Tensor, direction: int = ROW, rounding: int = RNE, s
         x.data_ptr(), R, Cc, direction, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg),
         _ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
         _ptr(out.get("col_scales")), out["amax"].data_ptr(), out["s_enc"].data_ptr(), _stream(dev)))
+    return out
+
+
+def nvfp4_quantize_rowscaled(x: torch.Tensor, rounding: int = RNE, sr_seed: int = 0, sr_stream: int = 0,
+                             rht_signs=None) -> Dict[str, torch.Tensor]:
+    """Rowwise NVFP4 with one outer scale per row.  Returns ``codes`` [rows, cols/2],
+    ``scales`` [rows, cols/16] (uint8), ``amax`` and ``s_enc`` (float32[rows])."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    R, Cc = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {"codes": torch.empty((R, Cc // 2), **u8), "scales": torch.empty((R, Cc // 16), **u8),
+           "amax": torch.empty(R, dtype=torch.float32, device=dev),
+           "s_enc": torch.empty(R, dtype=torch.float32, device=dev)}
+    sg = _signs(rht_signs, dev)
+    _check("nvfp4_quantize_rowscaled", lib().nvfp4_quantize_rowscaled(
+        x.data_ptr(), R, Cc, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg), out["codes"].data_ptr(),
+        out["scales"].data_ptr(), out["amax"].data_ptr(), out["s_enc"].data_ptr(), _stream(dev)))
     return out
 
 
@@ -192,13 +212,22 @@ def rht_apply(x: torch.Tensor, axis: int, rht_signs) -> torch.Tensor:
 def blockscaled_gemm(fmt: int, a_codes: torch.Tensor, a_scales: torch.Tensor, a_s_enc: Optional[torch.Tensor],
                      b_codes: torch.Tensor, b_scales: torch.Tensor, b_s_enc: Optional[torch.Tensor],
                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """C[M, N] = A[M, K] B[N, K]^T on NVFP4 (fmt 0) or MXFP8 (fmt 1) operands, fp32 accumulate."""
+    """C[M, N] = A[M, K] B[N, K]^T on NVFP4 (fmt 0) or MXFP8 (fmt 1) operands, fp32 accumulate.
+    ``fmt`` may carry FMT_A_ROWSCALED / FMT_B_ROWSCALED (NVFP4): that operand's ``s_enc`` then
+    holds one float per row."""
     _dev_tensor(a_codes, torch.uint8, "a_codes")
     _dev_tensor(b_codes, torch.uint8, "b_codes")
     _dev_tensor(a_scales, torch.uint8, "a_scales")
     _dev_tensor(b_scales, torch.uint8, "b_scales")
     M, N = a_codes.shape[0], b_codes.shape[0]
-    K = a_codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
+    base = fmt & ~(FMT_A_ROWSCALED | FMT_B_ROWSCALED)
+    K = a_codes.shape[1] * (2 if base == FMT_NVFP4 else 1)
+    for flag, t, n, name in ((FMT_A_ROWSCALED, a_s_enc, M, "a_s_enc"), (FMT_B_ROWSCALED, b_s_enc, N, "b_s_enc")):
+        if base == FMT_NVFP4 and t is not None:
+            _dev_tensor(t, torch.float32, name)
+            want = n if fmt & flag else 1
+            if t.numel() < want:
+                raise ValueError("%s has %d entries, needs %d" % (name, t.numel(), want))
     if b_codes.shape[1] != a_codes.shape[1]:
         raise ValueError("operands disagree on K")
     c_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[out_dtype]

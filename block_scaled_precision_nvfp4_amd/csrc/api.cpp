@@ -132,11 +132,31 @@ int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t*
     return launched(bsq::launch_rht_apply(x, rows, cols, axis, signs, out, hip_stream), fn);
 }
 
+int nvfp4_quantize_rowscaled(const void* x, int64_t rows, int64_t cols, int rounding, uint64_t sr_seed,
+                             uint32_t sr_stream, const int8_t* rht_signs, uint8_t* codes, uint8_t* scales,
+                             float* amax_rows, float* s_enc_rows, void* hip_stream) {
+    static const char* fn = "nvfp4_quantize_rowscaled";
+    if (rounding != BSQ_RNE && rounding != BSQ_SR) return fail(BSQ_ERR_ARG, "%s: rounding must be 0 (RNE) or 1 (SR), got %d", fn, rounding);
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape [%lld, %lld]", fn, (long long)rows, (long long)cols);
+    if (cols % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 16", fn, (long long)cols);
+    if (rows == 0) return ok();
+    if (!amax_rows || !s_enc_rows) return fail(BSQ_ERR_NULL, "%s: amax_rows and s_enc_rows are required", fn);
+    if (cols > 0 && (!x || !codes || !scales)) return fail(BSQ_ERR_NULL, "%s: x, codes or scales is NULL", fn);
+    if (misaligned(x) || misaligned(codes) || misaligned(rht_signs))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_nvfp4_quantize_rowscaled(x, rows, cols, rounding, sr_seed, sr_stream, rht_signs,
+                                                         codes, scales, amax_rows, s_enc_rows, hip_stream), fn);
+}
+
 int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                      const float* a_s_enc, const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
                      void* c, int c_dtype, void* hip_stream) {
     static const char* fn = "blockscaled_gemm";
-    if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), got %d", fn, fmt);
+    const int a_rows = (fmt & BSQ_FMT_A_ROWSCALED) != 0, b_rows = (fmt & BSQ_FMT_B_ROWSCALED) != 0;
+    const int flags = fmt & (BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
+    fmt &= ~(BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
+    if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), optionally with the row-scaled flags, got %d", fn, fmt | flags);
+    if (flags && fmt != BSQ_FMT_NVFP4) return fail(BSQ_ERR_ARG, "%s: the row-scaled flags apply to NVFP4 operands only", fn);
     if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
     if (M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
     if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
@@ -147,7 +167,7 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
     if (misaligned(a_codes) || misaligned(b_codes) || misaligned(c) || misaligned(a_scales) || misaligned(b_scales))
         return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     return launched(bsq::launch_blockscaled_gemm(fmt, M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales,
-                                                 b_s_enc, c, c_dtype, hip_stream), fn);
+                                                 b_s_enc, a_rows, b_rows, c, c_dtype, hip_stream), fn);
 }
 
 }  // extern "C"

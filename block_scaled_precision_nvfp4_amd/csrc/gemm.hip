@@ -10,7 +10,9 @@
 // exponent, here 2^8) and one packed f16 multiply by the block scale, held as the f16
 // whose bit pattern is (E4M3 byte << 7): for every E4M3 code, normal or subnormal, that
 // f16 equals the E4M3 value times 2^-8, so the product is exactly code * scale.  The
-// tensor scales enter once, in the epilogue: alpha = 1 / (S_a * S_b).
+// tensor scales enter once, in the epilogue: alpha = 1 / (S_a * S_b).  An operand may
+// instead carry one outer scale per row (row-scaled NVFP4); the epilogue then takes
+// alpha(m, n) from a per-tile table of row and column factors (see tile_factors).
 //
 // MXFP8 operands (E4M3 codes, one E8M0 scale per 32 K-elements) map one-to-one onto the
 // scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4.  Its K layout: in lane (row, g), bytes
@@ -52,6 +54,7 @@ struct GemmArgs {
     const uint8_t* b_scales;
     const float* b_s_enc;
     void* c;
+    int a_rows, b_rows;   // the operand's tensor scale is per row (float[M] / float[N])
 };
 
 // FMT 0: NVFP4, 8 waves of 128 x 64, register-staged (any K); FMT 1: MXFP8, 4 waves of 128 x
@@ -747,9 +750,10 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
 // 4-byte store per accumulator.  bf16 output takes all 128 rows in one pass (34 KiB per
 // wave); fp32 output two passes of 64 rows.  A wave reads back only what it wrote, and the LDS
 // executes one wave's instructions in order, so no barrier is needed between the two.
-template <bool OUT_F32>
+template <bool OUT_F32, bool SCALED>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, int64_t m0, int64_t n0, int wm,
-                                               int wn, int wave, int lane, float alpha, floatx16 (&acc)[4][4]) {
+                                               int wn, int wave, int lane, const float* fa, const float* fb,
+                                               floatx16 (&acc)[4][4]) {
     constexpr int ES = OUT_F32 ? 4 : 2;          // bytes per element
     constexpr int ROWS = OUT_F32 ? 64 : 128;     // rows per pass
     constexpr int RS = 128 * ES + 16;            // LDS row stride
@@ -758,17 +762,29 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
     uint8_t* reg = lds + wave * ROWS * RS;
     const int frow = lane & 31, kh = lane >> 5;
     uint8_t* cbase = (uint8_t*)g.c + ((m0 + wm) * g.N + n0 + wn) * ES;
+    float fbv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fbv[j] = fb[wn + 32 * j + frow];
+    }
     static_for<0, 128 / ROWS>([&](auto h_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr int I0 = H * ROWS / 32;
         static_for<0, ROWS / 32>([&](auto i_c) {
             constexpr int IL = decltype(i_c)::value;
+            float fav[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 f4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                if constexpr (SCALED) f4 = *(const float4*)(fa + wm + 32 * (I0 + IL) + 8 * q + 4 * kh);
+                fav[4 * q] = f4.x; fav[4 * q + 1] = f4.y; fav[4 * q + 2] = f4.z; fav[4 * q + 3] = f4.w;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * IL + 8 * (r >> 2) + 4 * kh + (r & 3);
-                    const float v = acc[I0 + IL][j][r] * alpha;
+                    const float v = SCALED ? acc[I0 + IL][j][r] * (fav[r] * fbv[j]) : acc[I0 + IL][j][r];
                     if constexpr (OUT_F32) *(float*)(reg + row * RS + (32 * j + frow) * 4) = v;
                     else *(__bf16*)(reg + row * RS + (32 * j + frow) * 2) = (__bf16)v;
                 }
@@ -783,6 +799,44 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
         }
         asm volatile("" ::: "memory");
     });
+}
+
+// Per-tile output factors, alpha(m, n) = fa[m - m0] * fb[n - n0], written to LDS (two
+// float[256] tables after the epilogue's staging regions) by the whole workgroup.
+//   per-tensor scales:         fa = 1 / (S_a S_b), fb = 1
+//   A per row, B per tensor:   fa[m] = 1 / (S_a[m] S_b), fb = 1
+//   A per tensor, B per row:   fa = 1, fb[n] = 1 / (S_a S_b[n])
+//   both per row:              fa[m] = 1 / S_a[m], fb[n] = 1 / S_b[n]
+// Each factor is the binary64 quotient rounded once to fp32, so with at most one row-scaled
+// operand alpha is exactly what the per-tensor formula gives; with two it is the fp32 product
+// of two such reciprocals.  MXFP8: fa = fb = 1.  Rows and columns past M and N are not
+// read (their factors are never used).
+constexpr int FACT_BYTES = 2 * 256 * 4;
+
+template <int FMT>
+__device__ __forceinline__ void tile_factors(const GemmArgs& g, int64_t m0, int64_t n0, float* fa, float* fb) {
+    using F = Fmt<FMT>;
+    for (int i = threadIdx.x; i < 512; i += F::THREADS) {
+        float f = 1.0f;
+        if constexpr (F::NV) {
+            const int t = i & 255;
+            if (i < 256) {
+                const int64_t m = m0 + t;
+                if (m < g.M) {
+                    const double sa = g.a_rows ? (double)g.a_s_enc[m] : (double)g.a_s_enc[0];
+                    if (g.a_rows) f = (float)(1.0 / (g.b_rows ? sa : sa * (double)g.b_s_enc[0]));
+                    else if (!g.b_rows) f = (float)(1.0 / (sa * (double)g.b_s_enc[0]));
+                }
+            } else {
+                const int64_t n = n0 + t;
+                if (n < g.N && g.b_rows) {
+                    const double sb = (double)g.b_s_enc[n];
+                    f = (float)(1.0 / (g.a_rows ? sb : sb * (double)g.a_s_enc[0]));
+                }
+            }
+        }
+        (i < 256 ? fa : fb)[i & 255] = f;
+    }
 }
 
 // Output tile of this workgroup.  Workgroup ids are dealt to the 8 XCDs round-robin; the
@@ -891,25 +945,35 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
         nvw_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
 
-    float alpha = 1.0f;
-    if (F::NV) alpha = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
+    static_assert(FMT == 0 || (F::LDS - FACT_BYTES >= 4 * 128 * (128 * 2 + 16) &&
+                               F::LDS - FACT_BYTES >= 4 * 64 * (128 * 4 + 16)),
+                  "factor tables overlap the epilogue staging");
+    // NVFP4 output factors (MXFP8 needs none: its scales are inside the MFMA)
+    float* fa = (float*)(lds + F::LDS - FACT_BYTES);
+    float* fb = fa + 256;
+    __syncthreads();   // every wave is done with the operand buffers (and its DMAs)
+    if constexpr (F::NV) {
+        tile_factors<FMT>(g, m0, n0, fa, fb);
+        __syncthreads();
+    }
     if constexpr (FMT != 0) {
         constexpr int ES = OUT_F32 ? 4 : 2;
         const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
         if (full) {
-            __syncthreads();   // every wave is done with the operand buffers (and its DMAs)
-            store_tile_lds<OUT_F32>(g, lds, m0, n0, wm, wn, wave, lane, alpha, acc);
+            store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, acc);
             return;
         }
     }
     static_for<0, 4 * TN>([&](auto t_c) {
         constexpr int i = decltype(t_c)::value / TN, j = decltype(t_c)::value % TN;
         const int64_t col = n0 + wn + 32 * j + frow;
+        const float fbj = F::NV ? fb[wn + 32 * j + frow] : 1.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int lrow = wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int64_t row = m0 + lrow;
             if (row < g.M && col < g.N) {
-                const float v = acc[i][j][r] * alpha;
+                const float v = F::NV ? acc[i][j][r] * (fa[lrow] * fbj) : acc[i][j][r];
                 if (OUT_F32) ((float*)g.c)[row * g.N + col] = v;
                 else ((uint16_t*)g.c)[row * g.N + col] = (uint16_t)f32_to_bf16_rne(v);
             }
@@ -935,10 +999,11 @@ static int launch_one(const GemmArgs& g, hipStream_t s) {
 
 int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                             const uint8_t* a_scales, const float* a_s_enc, const uint8_t* b_codes,
-                            const uint8_t* b_scales, const float* b_s_enc, void* c, int c_dtype, void* hip_stream) {
+                            const uint8_t* b_scales, const float* b_s_enc, int a_rows, int b_rows, void* c,
+                            int c_dtype, void* hip_stream) {
     if (M == 0 || N == 0) return 0;
     hipStream_t s = (hipStream_t)hip_stream;
-    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c};
+    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows};
     if (fmt == 0 && K % 256 == 0) return c_dtype == 1 ? launch_one<2, 1>(g, s) : launch_one<2, 0>(g, s);
     if (fmt == 0) return c_dtype == 1 ? launch_one<0, 1>(g, s) : launch_one<0, 0>(g, s);
     return c_dtype == 1 ? launch_one<1, 1>(g, s) : launch_one<1, 0>(g, s);

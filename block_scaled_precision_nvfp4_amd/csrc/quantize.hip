@@ -21,6 +21,7 @@
 // reset launch precedes the amax pass.
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "device_common.hpp"
@@ -674,6 +675,119 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
     }
 }
 
+// ------------------------------------------------------------------ row-scaled NVFP4
+//
+// Per-row outer scale: row r is quantized with S_r = 2688 / amax(row r) (the rowwise
+// quantizer of the Composer-style recipe on the page "[Pytorch][Common] Hybrid
+// quantization"; the "outer scale rowwise, inner scale 1x16" recipe of the review on "Add an
+// NVFP4 quantization converter").  A group of T = 2^lgt threads (2 <= T <= 256) owns a row:
+// thread `sub` of the group holds the 16-byte units sub + T*k (k < RS_UNITS) of each chunk
+// of T * RS_UNITS units, so adjacent lanes read adjacent units and the two halves of a
+// 16-block sit on a lane pair.  A row of at most one chunk (cols <= 16384 at T = 256) is
+// read once and kept in registers (as bf16; the transform is recomputed) between its amax
+// reduction and its encode; a longer row is
+// walked twice, the second walk re-reading it (normal loads, so the first walk leaves it
+// in L2).  The SR index of an element is its linear index, as in the per-tensor rowwise
+// quantization.
+constexpr int RS_UNITS = 8;
+constexpr int RS_THREADS = 256;
+constexpr int RS_MAX_BLOCKS = 256 * 8;
+
+template <bool RHT, bool SR>
+__global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4* __restrict__ x, int64_t R,
+                                                                     int64_t upr, int lgt,
+                                                                     const int8_t* __restrict__ signs,
+                                                                     uint32_t* __restrict__ codes,
+                                                                     uint8_t* __restrict__ scales,
+                                                                     float* __restrict__ amax_rows,
+                                                                     float* __restrict__ s_enc_rows, uint64_t seed,
+                                                                     uint32_t stream) {
+    const int T = 1 << lgt;
+    const int sub = threadIdx.x & (T - 1);
+    const int grp = threadIdx.x >> lgt;
+    const int rpw = RS_THREADS >> lgt;                 // rows per workgroup pass
+    const int64_t chunk = (int64_t)T * RS_UNITS;
+    const bool one = upr <= chunk;                     // uniform
+    const uint32_t neg = RHT ? sign_mask16(signs) : 0u;
+    const bool upper = (threadIdx.x & 1) != 0;
+    __shared__ float red[RS_THREADS / 64];
+
+    // The loop bounds are the same for every thread of the workgroup (the barrier below
+    // needs that); rows past R are computed on zeros and not stored.
+    for (int64_t rb = (int64_t)blockIdx.x * rpw; rb < R; rb += (int64_t)gridDim.x * rpw) {
+        const int64_t r = rb + grp;
+        const bool live = r < R;
+        const int64_t base = (live ? r : 0) * upr;
+        uint4 q[RS_UNITS];   // the raw bf16 units of the current chunk
+        auto load_chunk = [&](int64_t c0, auto streaming) {
+#pragma unroll
+            for (int k = 0; k < RS_UNITS; ++k) {
+                const int64_t u = c0 + sub + (int64_t)T * k;
+                if (live && u < upr) q[k] = decltype(streaming)::value ? load16_stream(x + base + u) : x[base + u];
+                else q[k] = make_uint4(0, 0, 0, 0);
+            }
+        };
+        // values of unit k (transformed when RHT is on) and their largest magnitude
+        auto values = [&](int k, float v[8]) {
+            unpack_bf16x8(q[k], v);
+            if (RHT) rht16_pair(v, neg, upper);
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+            return m;
+        };
+        float m = 0.0f;
+        if (one) {
+            load_chunk(0, std::true_type{});
+#pragma unroll
+            for (int k = 0; k < RS_UNITS; ++k) {
+                float v[8];
+                m = __builtin_fmaxf(m, values(k, v));
+            }
+        } else {
+            for (int64_t c0 = 0; c0 < upr; c0 += chunk) {
+                load_chunk(c0, std::false_type{});
+#pragma unroll
+                for (int k = 0; k < RS_UNITS; ++k) {
+                    float v[8];
+                    m = __builtin_fmaxf(m, values(k, v));
+                }
+            }
+        }
+        // row amax: across the group's lanes, then across its waves
+        for (int o = 1; o < T && o < 64; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+        if (T > 64) {
+            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+            __syncthreads();
+            const int w0 = (grp * T) >> 6;
+            m = red[w0];
+            for (int w = 1; w < (T >> 6); ++w) m = __builtin_fmaxf(m, red[w0 + w]);
+            __syncthreads();
+        }
+        const float S = nvfp4_tensor_scale(m);
+        if (live && sub == 0) {
+            amax_rows[r] = m;
+            s_enc_rows[r] = S;
+        }
+        for (int64_t c0 = 0; c0 < upr; c0 += chunk) {
+            if (!one) load_chunk(c0, std::false_type{});
+#pragma unroll
+            for (int k = 0; k < RS_UNITS; ++k) {
+                const int64_t u = c0 + sub + (int64_t)T * k;
+                float v[8];
+                float bm = values(k, v);
+                bm = __builtin_fmaxf(bm, __shfl_xor(bm, 1));
+                uint32_t w;
+                const uint32_t sb = encode_block<8, SR>(v, bm, S, (uint64_t)(base + u) * 8u, seed, stream, 0u, &w);
+                if (live && u < upr) {
+                    codes[base + u] = w;
+                    if (!upper) scales[(base + u) >> 1] = (uint8_t)sb;
+                }
+            }
+        }
+    }
+}
+
 // Rowwise MXFP8 cast: unit u = quarter u%4 of block u/4.
 __global__ __launch_bounds__(LIN_THREADS) void mxfp8_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
                                                                        uint2* __restrict__ codes,
@@ -826,6 +940,29 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
     }
     if (direction == 2) launch_nv_dirs<2>(a, rht, sr, g, s);
     else launch_nv_dirs<3>(a, rht, sr, g, s);
+    return (int)hipGetLastError();
+}
+
+int launch_nvfp4_quantize_rowscaled(const void* x, int64_t R, int64_t C, int rounding, uint64_t seed,
+                                    uint32_t stream, const int8_t* signs, uint8_t* codes, uint8_t* scales,
+                                    float* amax_rows, float* s_enc_rows, void* hip_stream) {
+    if (R == 0) return 0;
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int64_t upr = C / 8;
+    // threads per row: the power of two that holds the row in at most RS_UNITS units per lane
+    int lgt = 1;
+    while (lgt < 8 && ((int64_t)RS_UNITS << lgt) < upr) ++lgt;
+    const int64_t rpw = RS_THREADS >> lgt;
+    int64_t g = (R + rpw - 1) / rpw;
+    if (g > RS_MAX_BLOCKS) g = RS_MAX_BLOCKS;
+    const uint4* xv = (const uint4*)x;
+    uint32_t* cw = (uint32_t*)codes;
+    const bool rht = signs != nullptr, sr = rounding == 1;
+    const dim3 grid((unsigned)g), block(RS_THREADS);
+    if (rht && sr) hipLaunchKernelGGL((nvfp4_rowscaled_kernel<true, true>), grid, block, 0, s, xv, R, upr, lgt, signs, cw, scales, amax_rows, s_enc_rows, seed, stream);
+    else if (rht) hipLaunchKernelGGL((nvfp4_rowscaled_kernel<true, false>), grid, block, 0, s, xv, R, upr, lgt, signs, cw, scales, amax_rows, s_enc_rows, seed, stream);
+    else if (sr) hipLaunchKernelGGL((nvfp4_rowscaled_kernel<false, true>), grid, block, 0, s, xv, R, upr, lgt, signs, cw, scales, amax_rows, s_enc_rows, seed, stream);
+    else hipLaunchKernelGGL((nvfp4_rowscaled_kernel<false, false>), grid, block, 0, s, xv, R, upr, lgt, signs, cw, scales, amax_rows, s_enc_rows, seed, stream);
     return (int)hipGetLastError();
 }
 

@@ -20,7 +20,8 @@
  *     (TransformerEngine PR #2817, Description and dispatch flowchart).
  *   - Every pointer argument that names tensor data is a DEVICE pointer; every
  *     device pointer must be 16-byte aligned.  The caller allocates and owns all
- *     buffers; the library never allocates, frees or keeps device memory.
+ *     buffers.  The only device memory the library allocates itself is the amax
+ *     accumulator of nvfp4_quantize (described there).
  *   - Work is enqueued asynchronously on hip_stream (a hipStream_t; NULL is the
  *     null stream).  Return values report argument validation and launch errors
  *     only; faults during kernel execution surface at the next synchronisation.
@@ -56,6 +57,9 @@ enum bsq_status {
 /* GEMM operand formats */
 #define BSQ_FMT_NVFP4 0
 #define BSQ_FMT_MXFP8 1
+/* flags OR'ed into BSQ_FMT_NVFP4: that operand's tensor scale is one float per row */
+#define BSQ_FMT_A_ROWSCALED 0x10
+#define BSQ_FMT_B_ROWSCALED 0x20
 /* GEMM output types */
 #define BSQ_OUT_BF16 0
 #define BSQ_OUT_F32 1
@@ -101,12 +105,40 @@ enum bsq_status {
  * The amax pass accumulates into two library-owned device slots per (device, stream),
  * allocated on the first call on that stream and used alternately by consecutive calls;
  * calls on one stream are therefore ordered as usual, and calls on different streams do
- * not share slots.  The first call on a stream allocates (hipMalloc) those 16 bytes.
+ * not share slots.  The first call on a stream allocates (hipMalloc) those slots, 32 KiB,
+ * which stay allocated until the process ends.
  */
 int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding,
                    uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
                    uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
                    uint8_t* col_scales, float* amax_out, float* s_enc_out, void* hip_stream);
+
+/*
+ * nvfp4_quantize_rowscaled -- rowwise NVFP4 quantization with one outer fp32 scale per
+ * row instead of one per tensor.
+ *
+ * Defines: the "row_scaled_nvfp4" rowwise quantizer of the Composer-style recipe on the
+ * page "[Pytorch][Common] Hybrid quantization" (TransformerEngine PR #2817, Description),
+ * and the recipe with "outer scale rowwise, inner scale 1x16" raised in the review of "Add
+ * an NVFP4 quantization converter" (torchtitan PR #3914).  Row r is quantized exactly as
+ * nvfp4_quantize(direction = BSQ_ROW) quantizes a tensor, with A replaced by the row's amax
+ * A_r (over the transformed values when RHT is on) and S by S_r = 2688 / A_r (A_r = 0 gives
+ * S_r = 1; infinite S_r is clamped to FLT_MAX).  SR draws use the element's linear index
+ * r * cols + c and d = 0, as in the per-tensor rowwise quantization.
+ *
+ * Arguments:
+ *   x          [rows][cols] bf16 (device); cols % 16 == 0.
+ *   rounding, sr_seed, sr_stream, rht_signs: as for nvfp4_quantize.
+ *   codes      [rows][cols/2] uint8, scales [rows][cols/16] E4M3 (device), laid out as the
+ *              rowwise outputs of nvfp4_quantize.
+ *   amax_rows  float[rows] (device): A_r.  s_enc_rows float[rows] (device): S_r.
+ * A row is read from memory once when cols <= 16384 and twice otherwise.  The call uses no
+ * memory beyond its arguments.
+ */
+int nvfp4_quantize_rowscaled(const void* x, int64_t rows, int64_t cols, int rounding,
+                             uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
+                             uint8_t* codes, uint8_t* scales, float* amax_rows,
+                             float* s_enc_rows, void* hip_stream);
 
 /*
  * nvfp4_dequantize -- bf16 value of an NVFP4 tensor: out = bf16_RNE((E2M1(code) *
@@ -176,6 +208,11 @@ int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t*
  *   fmt BSQ_FMT_NVFP4: a_codes [M][K/2], a_scales [M][K/16] (E4M3), a_s_enc float[1]
  *       (device, the operand's tensor scale S), likewise for B; alpha =
  *       1/(S_a * S_b).  K % 32 == 0.
+ *   fmt BSQ_FMT_NVFP4 | BSQ_FMT_A_ROWSCALED and/or BSQ_FMT_B_ROWSCALED: that operand is
+ *       row-scaled (nvfp4_quantize_rowscaled) and its s_enc pointer is float[M] (A) or
+ *       float[N] (B); alpha(m, n) = 1/(S_a[m] * S_b[n]).  With one row-scaled operand the
+ *       factor is the binary64 quotient rounded once to fp32, as in the per-tensor case;
+ *       with two it is the fp32 product of 1/S_a[m] and 1/S_b[n], each so rounded.
  *   fmt BSQ_FMT_MXFP8: a_codes [M][K] (E4M3), a_scales [M][K/32] (E8M0); s_enc
  *       pointers are ignored (may be NULL); alpha = 1.  K % 32 == 0.
  *   c [M][N], c_dtype BSQ_OUT_BF16 (RNE) or BSQ_OUT_F32.

@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for f in ["nvfp4_quantize", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
-              "blockscaled_gemm", "bsq_last_error", "bsq_version"]:
+    for f in ["nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize",
+              "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "bsq_last_error", "bsq_version"]:
         assert f in names
 
 
@@ -119,6 +119,43 @@ def test_gemm_validation(L):
     # empty products are valid no-ops that never reach the device
     assert f(0, 0, 128, 64, *args, 0, None) == 0
     assert f(1, 128, 0, 64, *args, 0, None) == 0
+
+
+def test_gemm_rowscaled_flag_validation(L):
+    f = L.blockscaled_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    # the row-scaled flags are NVFP4-only and must not hide an invalid base format
+    assert f(1 | 0x10, 128, 128, 64, *args, 0, None) == 3 and "NVFP4 operands only" in last(L)
+    assert f(2 | 0x20, 128, 128, 64, *args, 0, None) == 3 and "fmt" in last(L)
+    assert f(0x40, 128, 128, 64, *args, 0, None) == 3
+    assert f(0x10 | 0x20, 128, 128, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
+    assert f(0x30, 0, 128, 64, *args, 0, None) == 0
+
+
+def rq(L, x=FAKE, rows=64, cols=256, rounding=0, signs=None, codes=FAKE, scales=FAKE, amax=FAKE, senc=FAKE):
+    return L.nvfp4_quantize_rowscaled(x, rows, cols, rounding, 0, 0, signs, codes, scales, amax, senc, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(rounding=3), 3, "rounding"),
+    (dict(rows=-2), 2, "negative"),
+    (dict(cols=40), 2, "multiple of 16"),
+    (dict(amax=None), 1, "amax_rows"),
+    (dict(senc=None), 1, "amax_rows"),
+    (dict(x=None), 1, "NULL"),
+    (dict(codes=None), 1, "NULL"),
+    (dict(scales=None), 1, "NULL"),
+    (dict(x=FAKE + 4), 6, "aligned"),
+    (dict(codes=FAKE + 8), 6, "aligned"),
+    (dict(signs=FAKE + 1), 6, "aligned"),
+])
+def test_nvfp4_quantize_rowscaled_validation(L, kw, status, needle):
+    assert rq(L, **kw) == status
+    assert needle in last(L)
+
+
+def test_nvfp4_quantize_rowscaled_empty_is_a_no_op(L):
+    assert rq(L, rows=0, x=None, codes=None, scales=None, amax=None, senc=None) == 0
 
 
 def test_dequantize_validation(L):
