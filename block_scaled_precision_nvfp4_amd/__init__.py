@@ -19,6 +19,7 @@ ROW, COL = 1, 2
 RNE, SR = 0, 1
 FMT_NVFP4, FMT_MXFP8 = 0, 1
 FMT_A_ROWSCALED, FMT_B_ROWSCALED = 0x10, 0x20
+GROUP_M, GROUP_K = 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,8 +53,9 @@ def lib():
         L.mxfp8_requantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
         L.rht_apply.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.blockscaled_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+        L.blockscaled_grouped_gemm.argtypes = [i32, i32, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         for f in ("nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
-                  "blockscaled_gemm", "bsq_version"):
+                  "blockscaled_gemm", "blockscaled_grouped_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int
         L.bsq_last_error.argtypes = []
         L.bsq_last_error.restype = C.c_char_p
@@ -240,4 +242,46 @@ def blockscaled_gemm(fmt: int, a_codes: torch.Tensor, a_scales: torch.Tensor, a_
     _check("blockscaled_gemm", lib().blockscaled_gemm(
         fmt, M, N, K, a_codes.data_ptr(), a_scales.data_ptr(), _ptr(a_s_enc), b_codes.data_ptr(),
         b_scales.data_ptr(), _ptr(b_s_enc), out.data_ptr(), c_dtype, _stream(a_codes.device)))
+    return out
+
+
+def blockscaled_grouped_gemm(fmt: int, mode: int, offsets: torch.Tensor, a_codes: torch.Tensor,
+                             a_scales: torch.Tensor, a_s_enc: Optional[torch.Tensor], b_codes: torch.Tensor,
+                             b_scales: torch.Tensor, b_s_enc: Optional[torch.Tensor],
+                             out_dtype: torch.dtype = torch.bfloat16,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One block-scaled GEMM per group; ``offsets`` is an int64 device tensor of groups + 1
+    boundaries.  GROUP_M: A [M, K] (rows grouped), B [groups, N, K] (codes as [groups, N,
+    K/2] or [groups * N, K/2] for NVFP4), C [M, N] (rows outside every group untouched).
+    GROUP_K: A [M, K] and B [N, K] grouped along K, C [groups, M, N]."""
+    _dev_tensor(offsets, torch.int64, "offsets")
+    for t, nm in ((a_codes, "a_codes"), (b_codes, "b_codes"), (a_scales, "a_scales"), (b_scales, "b_scales")):
+        _dev_tensor(t, torch.uint8, nm)
+    for t, nm in ((a_s_enc, "a_s_enc"), (b_s_enc, "b_s_enc")):
+        if t is not None:
+            _dev_tensor(t, torch.float32, nm)
+    G = offsets.numel() - 1
+    if G < 0:
+        raise ValueError("offsets needs groups + 1 entries")
+    base = fmt & ~(FMT_A_ROWSCALED | FMT_B_ROWSCALED)
+    epb = 2 if base == FMT_NVFP4 else 1
+    M, K = a_codes.shape[0], a_codes.shape[-1] * epb
+    if mode == GROUP_M:
+        N = b_codes.shape[-2] if b_codes.dim() == 3 else (b_codes.shape[0] // G if G else 0)
+        shape = (M, N)
+    else:
+        N = b_codes.shape[0]
+        shape = (G, M, N)
+    if b_codes.shape[-1] * epb != K:
+        raise ValueError("operands disagree on K")
+    c_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=a_codes.device)
+    else:
+        _dev_tensor(out, out_dtype, "out")
+        if tuple(out.shape) != shape:
+            raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), shape))
+    _check("blockscaled_grouped_gemm", lib().blockscaled_grouped_gemm(
+        fmt, mode, G, offsets.data_ptr(), M, N, K, a_codes.data_ptr(), a_scales.data_ptr(), _ptr(a_s_enc),
+        b_codes.data_ptr(), b_scales.data_ptr(), _ptr(b_s_enc), out.data_ptr(), c_dtype, _stream(a_codes.device)))
     return out

@@ -170,4 +170,34 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
                                                  b_s_enc, a_rows, b_rows, c, c_dtype, hip_stream), fn);
 }
 
+int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* offsets, int64_t M, int64_t N,
+                             int64_t K, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
+                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc, void* c,
+                             int c_dtype, void* hip_stream) {
+    static const char* fn = "blockscaled_grouped_gemm";
+    const int a_rows = (fmt & BSQ_FMT_A_ROWSCALED) != 0, b_rows = (fmt & BSQ_FMT_B_ROWSCALED) != 0;
+    const int flags = fmt & (BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
+    fmt &= ~(BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
+    if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), optionally with the row-scaled flags, got %d", fn, fmt | flags);
+    if (flags && fmt != BSQ_FMT_NVFP4) return fail(BSQ_ERR_ARG, "%s: the row-scaled flags apply to NVFP4 operands only", fn);
+    if (mode != BSQ_GROUP_M && mode != BSQ_GROUP_K) return fail(BSQ_ERR_ARG, "%s: mode must be 1 (BSQ_GROUP_M) or 2 (BSQ_GROUP_K), got %d", fn, mode);
+    if (flags && mode != BSQ_GROUP_M) return fail(BSQ_ERR_ARG, "%s: row-scaled operands are supported with BSQ_GROUP_M only", fn);
+    if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
+    if (groups < 0 || M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative size", fn);
+    if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (groups == 0 || M == 0 || N == 0) return ok();
+    if (groups > (int64_t)1 << 24) return fail(BSQ_ERR_SHAPE, "%s: too many groups (%lld)", fn, (long long)groups);
+    if (bsq::grouped_gemm_workgroups(mode, groups, M, N) > 0x7FFFFFFF) return fail(BSQ_ERR_SHAPE, "%s: problem too large for one launch", fn);
+    if (!offsets) return fail(BSQ_ERR_NULL, "%s: offsets is NULL", fn);
+    if (!c) return fail(BSQ_ERR_NULL, "%s: c is NULL", fn);
+    if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return fail(BSQ_ERR_NULL, "%s: operand pointer is NULL", fn);
+    if (fmt == BSQ_FMT_NVFP4 && (!a_s_enc || !b_s_enc)) return fail(BSQ_ERR_NULL, "%s: NVFP4 needs both tensor-scale arrays", fn);
+    if ((reinterpret_cast<uintptr_t>(offsets) & 7u) != 0) return fail(BSQ_ERR_ALIGN, "%s: offsets must be 8-byte aligned", fn);
+    if (misaligned(a_codes) || misaligned(b_codes) || misaligned(c) || misaligned(a_scales) || misaligned(b_scales))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_blockscaled_grouped_gemm(fmt, mode, groups, offsets, M, N, K, a_codes, a_scales,
+                                                         a_s_enc, b_codes, b_scales, b_s_enc, a_rows, b_rows, c,
+                                                         c_dtype, hip_stream), fn);
+}
+
 }  // extern "C"

@@ -55,6 +55,7 @@ struct GemmArgs {
     const float* b_s_enc;
     void* c;
     int a_rows, b_rows;   // the operand's tensor scale is per row (float[M] / float[N])
+    int64_t ld;           // elements between consecutive rows of A and of B (K unless grouped along K)
 };
 
 // FMT 0: NVFP4, 8 waves of 128 x 64, register-staged (any K); FMT 1: MXFP8, 4 waves of 128 x
@@ -121,7 +122,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
 template <int FMT>
 __device__ __forceinline__ Operands make_operands(const GemmArgs& g, int64_t m0, int64_t n0) {
     using F = Fmt<FMT>;
-    const int64_t rowbytes = g.K / F::EPB, sstride = g.K / F::BLK;
+    const int64_t rowbytes = g.ld / F::EPB, sstride = g.ld / F::BLK;
     Operands o;
     o.a = make_rsrc(g.a_codes + m0 * rowbytes, (g.M - m0) * rowbytes);
     o.b = make_rsrc(g.b_codes + n0 * rowbytes, (g.N - n0) * rowbytes);
@@ -134,7 +135,7 @@ template <int FMT>
 __device__ __forceinline__ void stage_load(const GemmArgs& g, const Operands& o, int64_t k0, Stage& st) {
     using F = Fmt<FMT>;
     const int tid = threadIdx.x;
-    const uint32_t rowbytes = (uint32_t)(g.K / F::EPB);
+    const uint32_t rowbytes = (uint32_t)(g.ld / F::EPB);
     const int soff = (int)(k0 / F::EPB);
     const bool tail = k0 + F::BK > g.K;   // uniform
 #pragma unroll
@@ -151,9 +152,10 @@ __device__ __forceinline__ void stage_load(const GemmArgs& g, const Operands& o,
     // reading it through readfirstlane lets the resource stay in scalar registers.
     constexpr int HT = F::THREADS / 2, RPT = GBM / HT;
     const int op = __builtin_amdgcn_readfirstlane(tid / HT), rr = tid % HT;
-    const uint32_t sstride = (uint32_t)(g.K / F::BLK);
+    const uint32_t sstride = (uint32_t)(g.ld / F::BLK);
     const int ssoff = (int)(k0 / F::BLK);
-    const bool aligned = (sstride % F::SPR) == 0 && !tail;   // uniform
+    const bool aligned = (sstride % F::SPR) == 0 && !tail &&
+                         (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % F::SPR) == 0;   // uniform
 #pragma unroll
     for (int h = 0; h < RPT; ++h) {
         const uint32_t off = (uint32_t)(rr + HT * h) * sstride;
@@ -372,7 +374,8 @@ __device__ __forceinline__ void wait_vm() {
 // buffer) so that every slice issues the same number of DMAs.
 struct MxDma {
     RsrcWords o;
-    uint32_t rowbytes, sstride;   // code bytes per row (K / elements per byte); scale bytes per row
+    uint32_t rowbytes, sstride;   // code and scale bytes between consecutive rows
+    uint32_t kbytes, kblocks;     // code and scale bytes of a row's K elements
     int wave, lane;
 };
 
@@ -382,7 +385,7 @@ __device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t b0, bool li
     const int r0 = 16 * NW * P + 16 * d.wave;
     const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
     uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
-    if (!live || b0 + 16 * c >= (int64_t)d.rowbytes) off = OOB;
+    if (!live || b0 + 16 * c >= (int64_t)d.kbytes) off = OOB;
     const uint32_t soff = live ? (uint32_t)b0 : 0u;
     dma_b128(d.o.a, lds_addr(buf + r0 * ROWB), off, soff);
     dma_b128(d.o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off, soff);
@@ -394,7 +397,7 @@ __device__ __forceinline__ void mx_dma_slots(const MxDma& d, int64_t k0, bool li
     const int s0 = 256 * P + 64 * d.wave;
     const int sl = s0 + d.lane, r = sl >> 1, kb = sl & 1;
     const int64_t kb0 = k0 / 32;
-    const uint32_t off = (live && kb0 + kb < (int64_t)d.sstride) ? (uint32_t)r * d.sstride + kb : OOB;
+    const uint32_t off = (live && kb0 + kb < (int64_t)d.kblocks) ? (uint32_t)r * d.sstride + kb : OOB;
     const uint32_t soff = live ? (uint32_t)kb0 : 0u;
     dma_u8(d.o.as, lds_addr(buf + MX_CODES + 4 * s0), off, soff);
     dma_u8(d.o.bs, lds_addr(buf + MX_CODES + 8 * GBM + 4 * s0), off, soff);
@@ -422,13 +425,15 @@ __device__ __forceinline__ void mx_dma_group(const MxDma& d, int64_t grp, bool l
 template <int EPB, int BLK>
 __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
     MxDma d;
-    const int64_t rb = g.K / EPB, sb = g.K / BLK;
+    const int64_t rb = g.ld / EPB, sb = g.ld / BLK;
     d.o.a = rsrc_words(g.a_codes + m0 * rb, (g.M - m0) * rb);
     d.o.b = rsrc_words(g.b_codes + n0 * rb, (g.N - n0) * rb);
     d.o.as = rsrc_words(g.a_scales + m0 * sb, (g.M - m0) * sb);
     d.o.bs = rsrc_words(g.b_scales + n0 * sb, (g.N - n0) * sb);
     d.rowbytes = (uint32_t)rb;
     d.sstride = (uint32_t)sb;
+    d.kbytes = (uint32_t)(g.K / EPB);
+    d.kblocks = (uint32_t)(g.K / BLK);
     d.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     d.lane = lane;
     return d;
@@ -842,9 +847,8 @@ __device__ __forceinline__ void tile_factors(const GemmArgs& g, int64_t m0, int6
 // Output tile of this workgroup.  Workgroup ids are dealt to the 8 XCDs round-robin; the
 // id is remapped so that XCD x receives the contiguous tile range [x*T/8, (x+1)*T/8),
 // walked in bands of GROUP tile-rows (column-major inside a band) for L2 reuse.
-__device__ __forceinline__ void tile_of(int64_t nbm, int64_t nbn, int64_t& tm, int64_t& tn) {
+__device__ __forceinline__ void tile_of(int64_t nbm, int64_t nbn, int64_t id, int64_t& tm, int64_t& tn) {
     const int64_t T = nbm * nbn;
-    int64_t id = blockIdx.x;
     const int64_t T8 = (T / 8) * 8;
     if (id < T8) id = (id % 8) * (T8 / 8) + id / 8;
     constexpr int64_t GROUP = 8;
@@ -856,13 +860,140 @@ __device__ __forceinline__ void tile_of(int64_t nbm, int64_t nbn, int64_t& tm, i
     tn = in / rows;
 }
 
-template <int FMT, int OUT_F32>
-__global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) {
+// ---------------------------------------------------------------- grouped launches
+//
+// A grouped launch runs one GEMM per group g, the groups given by boundaries offs[g] ..
+// offs[g+1] on the device (clamped to [0, extent]):
+//   M-grouped (the per-expert GEMMs of a mixture-of-experts layer, fprop and dgrad): the
+//     group's rows of A [extent][K] and of C [extent][N], against B_g [N][K], the g-th of
+//     the stacked B [groups][N][K];
+//   K-grouped (wgrad): C_g [M][N], the g-th of the stacked C [groups][M][N], contracts
+//     columns offs[g] .. offs[g+1] of A [M][extent] and B [N][extent] (rows of length
+//     extent); the boundaries must be multiples of 32 (a group whose are not is computed as
+//     empty, C_g = 0).
+// Workgroups are dealt to the groups in order, each group taking a multiple of 8 of them so
+// that its tiles see the same XCD phase as a plain launch; a workgroup past its group's tiles
+// exits at once.  Everything a group needs -- its operand and output bases, its tensor scales
+// and its extent -- is folded into the GemmArgs, and the tile code runs unchanged.
+struct GroupArgs {
+    const int64_t* offs;   // groups + 1 boundaries (device)
+    int64_t groups;
+    int64_t extent;        // rows of A and C (M-grouped) or K (K-grouped)
+};
+
+__device__ __forceinline__ void group_bounds(const GroupArgs& q, int64_t grp, int64_t& o0, int64_t& o1) {
+    int64_t a = q.offs[grp], b = q.offs[grp + 1];
+    a = a < 0 ? 0 : (a > q.extent ? q.extent : a);
+    b = b < a ? a : (b > q.extent ? q.extent : b);
+    o0 = a;
+    o1 = b;
+}
+
+__device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
+    const int lo = __shfl((int)(uint32_t)v, src), hi = __shfl((int)(uint32_t)((uint64_t)v >> 32), src);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// A wave-uniform 64-bit value moved to scalar registers (buffer resources built from it must
+// be scalar).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// M-grouped: the group of workgroup bid and its index within the group's share (each wave
+// scans the boundaries itself, 64 groups at a time, with a wave prefix sum of the shares).
+// The loop runs to the end with a uniform trip count and the results pass through
+// readfirstlane, so that they stay in scalar registers.
+__device__ __forceinline__ bool group_of_m(const GroupArgs& q, int64_t nbn, int64_t bid, int64_t& grp,
+                                           int64_t& local) {
+    const int lane = threadIdx.x & 63;
+    int64_t before = 0, found = -1, loc = 0;
+    for (int64_t c0 = 0; c0 < q.groups; c0 += 64) {
+        const int64_t gi = c0 + lane;
+        int64_t t = 0;
+        if (gi < q.groups) {
+            int64_t o0, o1;
+            group_bounds(q, gi, o0, o1);
+            t = (((o1 - o0 + GBM - 1) / GBM) * nbn + 7) & ~(int64_t)7;
+        }
+        int64_t incl = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t v = shfl64(incl, lane >= o ? lane - o : lane);
+            if (lane >= o) incl += v;
+        }
+        const int64_t start = before + incl - t;
+        const uint64_t hit = __ballot(t > 0 && bid >= start && bid < start + t);
+        if (found < 0 && hit != 0) {
+            const int l = __builtin_ctzll(hit);
+            found = uniform64(c0 + l);
+            loc = uniform64(bid - shfl64(start, l));
+        }
+        before = uniform64(before + shfl64(incl, 63));
+    }
+    grp = found;
+    local = loc;
+    return found >= 0;
+}
+
+// Fold group bookkeeping into g; bid becomes the workgroup's index within its group's tiles.
+// Returns false for a workgroup with no tile.
+template <int FMT, int OUT_F32, int GM>
+__device__ __forceinline__ bool enter_group(GemmArgs& g, const GroupArgs& q, int64_t& bid) {
+    using F = Fmt<FMT>;
+    constexpr int ES = OUT_F32 ? 4 : 2;
+    const int64_t rb = g.ld / F::EPB, sb = g.ld / F::BLK;
+    const int64_t nbn = (g.N + GBN - 1) / GBN;
+    int64_t grp, local, o0, o1;
+    if constexpr (GM == 1) {
+        if (!group_of_m(q, nbn, bid, grp, local)) return false;
+        group_bounds(q, grp, o0, o1);
+        g.M = o1 - o0;
+        g.a_codes += o0 * rb;
+        g.a_scales += o0 * sb;
+        g.b_codes += grp * g.N * rb;
+        g.b_scales += grp * g.N * sb;
+        g.c = (uint8_t*)g.c + o0 * g.N * ES;
+        if constexpr (F::NV) {
+            g.a_s_enc += g.a_rows ? o0 : grp;
+            g.b_s_enc += g.b_rows ? grp * g.N : grp;
+        }
+    } else {
+        const int64_t nbm = (g.M + GBM - 1) / GBM;
+        const int64_t share = (nbm * nbn + 7) & ~(int64_t)7;
+        grp = bid / share;
+        local = bid - grp * share;
+        if (grp >= q.groups) return false;
+        group_bounds(q, grp, o0, o1);
+        if (o0 % 32 != 0 || (o1 - o0) % 32 != 0) o1 = o0 = 0;
+        g.K = o1 - o0;
+        g.a_codes += o0 / F::EPB;
+        g.a_scales += o0 / F::BLK;
+        g.b_codes += o0 / F::EPB;
+        g.b_scales += o0 / F::BLK;
+        g.c = (uint8_t*)g.c + grp * g.M * g.N * ES;
+        if constexpr (F::NV) {
+            g.a_s_enc += grp;
+            g.b_s_enc += grp;
+        }
+    }
+    bid = local;
+    return bid < ((g.M + GBM - 1) / GBM) * nbn;
+}
+
+template <int FMT, int OUT_F32, int GM>
+__global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, GroupArgs q) {
     using F = Fmt<FMT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int64_t bid = blockIdx.x;
+    if constexpr (GM != 0) {
+        if (!enter_group<FMT, OUT_F32, GM>(g, q, bid)) return;   // uniform
+    }
     int64_t tm, tn;
-    tile_of((g.M + GBM - 1) / GBM, (g.N + GBN - 1) / GBN, tm, tn);
+    tile_of((g.M + GBM - 1) / GBM, (g.N + GBN - 1) / GBN, bid, tm, tn);
     const int64_t m0 = tm * GBM, n0 = tn * GBN;
     constexpr int TN = F::TN;
     const int wm = (wave / F::WAVES_N) * 128, wn = (wave % F::WAVES_N) * 32 * TN;
@@ -939,7 +1070,10 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
             for (int j = 0; j < NVTN; ++j) sb[j] = sbn[j];
         }
     } else if constexpr (FMT == 1) {
-        if (g.K % (MX_GROUP * 64) == 0) mx_main_loop<true>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        // 16-byte scale records need K a multiple of 512 and 16-byte aligned scale rows
+        const bool recs = g.K % (MX_GROUP * 64) == 0 && (g.ld / 32) % 16 == 0 &&
+                          (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) == 0;
+        if (recs) mx_main_loop<true>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else mx_main_loop<false>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     } else {
         nvw_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
@@ -982,19 +1116,31 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g) 
     });
 }
 
-template <int FMT, int OUT>
-static int launch_one(const GemmArgs& g, hipStream_t s) {
+template <int FMT, int OUT, int GM>
+static int launch_one(const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipStream_t s) {
     using F = Fmt<FMT>;
     static bool configured = false;   // raising the dynamic-LDS limit is a per-process, per-kernel setting
     if (!configured) {
-        const hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<FMT, OUT>,
+        const hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<FMT, OUT, GM>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS);
         if (e != hipSuccess) return (int)e;
         configured = true;
     }
-    const int64_t tiles = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
-    hipLaunchKernelGGL((gemm_kernel<FMT, OUT>), dim3((unsigned)tiles), dim3(F::THREADS), F::LDS, s, g);
+    if (tiles <= 0) return 0;
+    hipLaunchKernelGGL((gemm_kernel<FMT, OUT, GM>), dim3((unsigned)tiles), dim3(F::THREADS), F::LDS, s, g, q);
     return (int)hipGetLastError();
+}
+
+template <int GM>
+static int launch_fmt(int fmt, int c_dtype, const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipStream_t s) {
+    // NVFP4: the LDS DMA kernel when every K handled is a multiple of 256 (known on the host
+    // unless K varies per group), the register-staged kernel otherwise
+    if constexpr (GM != 2) {
+        if (fmt == 0 && g.K % 256 == 0)
+            return c_dtype == 1 ? launch_one<2, 1, GM>(g, q, tiles, s) : launch_one<2, 0, GM>(g, q, tiles, s);
+    }
+    if (fmt == 0) return c_dtype == 1 ? launch_one<0, 1, GM>(g, q, tiles, s) : launch_one<0, 0, GM>(g, q, tiles, s);
+    return c_dtype == 1 ? launch_one<1, 1, GM>(g, q, tiles, s) : launch_one<1, 0, GM>(g, q, tiles, s);
 }
 
 int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
@@ -1002,11 +1148,28 @@ int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint
                             const uint8_t* b_scales, const float* b_s_enc, int a_rows, int b_rows, void* c,
                             int c_dtype, void* hip_stream) {
     if (M == 0 || N == 0) return 0;
+    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K};
+    const int64_t tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+    return launch_fmt<0>(fmt, c_dtype, g, GroupArgs{nullptr, 0, 0}, tiles, (hipStream_t)hip_stream);
+}
+
+int64_t grouped_gemm_workgroups(int mode, int64_t groups, int64_t M, int64_t N) {
+    const int64_t nbm = (M + GBM - 1) / GBM, nbn = (N + GBN - 1) / GBN;
+    if (mode == 1) return nbn * (nbm + groups) + 7 * groups;   // >= the sum of the groups' shares
+    return groups * ((nbm * nbn + 7) & ~(int64_t)7);
+}
+
+int launch_blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* offsets, int64_t M, int64_t N,
+                                    int64_t K, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
+                                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
+                                    int a_rows, int b_rows, void* c, int c_dtype, void* hip_stream) {
+    if (groups == 0 || M == 0 || N == 0) return 0;
+    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K};
+    const GroupArgs q{offsets, groups, mode == 1 ? M : K};
+    const int64_t tiles = grouped_gemm_workgroups(mode, groups, M, N);
     hipStream_t s = (hipStream_t)hip_stream;
-    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows};
-    if (fmt == 0 && K % 256 == 0) return c_dtype == 1 ? launch_one<2, 1>(g, s) : launch_one<2, 0>(g, s);
-    if (fmt == 0) return c_dtype == 1 ? launch_one<0, 1>(g, s) : launch_one<0, 0>(g, s);
-    return c_dtype == 1 ? launch_one<1, 1>(g, s) : launch_one<1, 0>(g, s);
+    if (mode == 1) return launch_fmt<1>(fmt, c_dtype, g, q, tiles, s);
+    return launch_fmt<2>(fmt, c_dtype, g, q, tiles, s);
 }
 
 }  // namespace bsq

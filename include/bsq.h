@@ -60,6 +60,9 @@ enum bsq_status {
 /* flags OR'ed into BSQ_FMT_NVFP4: that operand's tensor scale is one float per row */
 #define BSQ_FMT_A_ROWSCALED 0x10
 #define BSQ_FMT_B_ROWSCALED 0x20
+/* grouped GEMM modes */
+#define BSQ_GROUP_M 1   /* groups split the rows of A and C (per-expert fprop / dgrad) */
+#define BSQ_GROUP_K 2   /* groups split the contraction (per-expert wgrad)             */
 /* GEMM output types */
 #define BSQ_OUT_BF16 0
 #define BSQ_OUT_F32 1
@@ -222,6 +225,44 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
                      const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
                      const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
                      void* c, int c_dtype, void* hip_stream);
+
+/*
+ * blockscaled_grouped_gemm -- one block-scaled GEMM per group in a single launch: the
+ * grouped GEMM of a mixture-of-experts linear layer ("general_grouped_gemm" of the
+ * GroupedLinear path in the dispatch flowchart of the page "[Pytorch][Common] Hybrid
+ * quantization", TransformerEngine PR #2817, whose Composer-style grouped recipe quantizes
+ * the expert inputs as row-scaled NVFP4 for fprop and uses MXFP8 for the backward GEMMs).
+ * Each group's GEMM computes exactly what blockscaled_gemm computes on that group's operands.
+ *
+ *   offsets  int64[groups + 1] (device, 8-byte aligned): group g covers indices
+ *            offsets[g] .. offsets[g+1] of the grouped dimension.  Read on the device, so the
+ *            routing that produces them needs no host synchronisation.  A group's start is
+ *            clamped to [0, extent] and its end to [start, extent], so no group ever touches
+ *            memory outside the tensors.  Groups must not overlap: with overlapping
+ *            BSQ_GROUP_M groups the output is unspecified (still within C).
+ *   mode BSQ_GROUP_M (fprop, dgrad): extent = M.  A [M][K] holds the groups' rows one after
+ *            another (tokens sorted by expert); B [groups][N][K] stacks one operand per
+ *            group; C [M][N]: rows offsets[g] .. offsets[g+1] = A_g B_g^T.  Rows outside
+ *            every group are not written.  Any group sizes (zero included).
+ *   mode BSQ_GROUP_K (wgrad): extent = K.  A [M][K] and B [N][K] are whole-tensor operands
+ *            stored along the grouped dimension (e.g. the columnwise quantization of dY and X
+ *            over all tokens); C [groups][M][N]: C_g = A[:, offsets[g]..offsets[g+1]) *
+ *            B[:, same]^T.  Boundaries must be multiples of 32 (where per-group and
+ *            whole-tensor MXFP8 blocks coincide); a group whose boundaries are not is
+ *            computed as empty (C_g = 0), as is an empty group.
+ *   fmt, codes, scales, c, c_dtype: as for blockscaled_gemm, with K % 32 == 0.
+ *   NVFP4 tensor scales: a_s_enc float[groups] and b_s_enc float[groups] (one per group's
+ *            operand); with BSQ_FMT_A_ROWSCALED (BSQ_GROUP_M only) a_s_enc is float[M], one
+ *            per row of A, and with BSQ_FMT_B_ROWSCALED b_s_enc is float[groups * N].
+ *            alpha follows blockscaled_gemm.  MXFP8 ignores them.
+ * The launch covers an upper bound of the groups' tiles computed on the host from M, N and
+ * groups; workgroups past the tiles that the device-side offsets produce exit at once.
+ */
+int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* offsets,
+                             int64_t M, int64_t N, int64_t K,
+                             const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
+                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
+                             void* c, int c_dtype, void* hip_stream);
 
 /* Message of the last failing call on this thread ("" if none).  Host memory owned
  * by the library; valid until the thread's next call. */

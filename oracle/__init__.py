@@ -308,5 +308,61 @@ def blockscaled_gemm(fmt: int, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_
     return out
 
 
+GROUP_M, GROUP_K = 1, 2
+
+
+def _group_bounds(offsets, g: int, extent: int):
+    """Boundaries of group g clamped to [0, extent], the upper one raised to the lower."""
+    a = min(max(int(offsets[g]), 0), extent)
+    b = min(max(int(offsets[g + 1]), a), extent)
+    return a, b
+
+
+def blockscaled_grouped_gemm(fmt: int, mode: int, offsets, a_codes, a_scales, a_s_enc, b_codes, b_scales,
+                             b_s_enc, a_rows: bool = False, b_rows: bool = False) -> np.ndarray:
+    """One block-scaled GEMM per group, group g covering offsets[g] .. offsets[g+1] of the
+    grouped dimension (the grouped GEMM of a mixture-of-experts linear layer: the
+    general_grouped_gemm step of the GroupedLinear path in the dispatch flowchart of the page
+    "[Pytorch][Common] Hybrid quantization").  Each group is the plain GEMM of its slices.
+      GROUP_M: rows of A [M][K] and C [M][N]; B is stacked per group, b_codes [G][N][K/epb];
+               returns C [M][N] in float64, NaN in rows outside every group.
+      GROUP_K: columns of A [M][K] and B [N][K]; returns C [G][M][N].  A group whose
+               boundaries are not multiples of 32 is empty (its C_g is 0), as the library
+               documents.
+    NVFP4 tensor scales: one per group, or (GROUP_M, a_rows / b_rows) one per row of A / of
+    the stacked B.  MXFP8 ignores them."""
+    G = len(offsets) - 1
+    epb = 2 if fmt == FMT_NVFP4 else 1
+    blk = 16 if fmt == FMT_NVFP4 else 32
+    M = a_codes.shape[0]
+    nv = fmt == FMT_NVFP4
+    sa = np.atleast_1d(np.asarray(a_s_enc, np.float32)) if nv else None
+    sb = np.atleast_1d(np.asarray(b_s_enc, np.float32)) if nv else None
+    if mode == GROUP_M:
+        N = b_codes.shape[1]
+        out = np.full((M, N), np.nan)
+        for g in range(G):
+            o0, o1 = _group_bounds(offsets, g, M)
+            if o1 == o0:
+                continue
+            s_a = (sa[o0:o1] if a_rows else float(sa[g])) if nv else 1.0
+            s_b = (sb[g * N:(g + 1) * N] if b_rows else float(sb[g])) if nv else 1.0
+            out[o0:o1] = blockscaled_gemm(fmt, a_codes[o0:o1], a_scales[o0:o1], s_a,
+                                          b_codes[g], b_scales[g], s_b)
+        return out
+    K = a_codes.shape[1] * epb
+    N = b_codes.shape[0]
+    out = np.zeros((G, M, N))
+    for g in range(G):
+        o0, o1 = _group_bounds(offsets, g, K)
+        if o1 == o0 or o0 % 32 or (o1 - o0) % 32:
+            continue
+        cs, ss = slice(o0 // epb, o1 // epb), slice(o0 // blk, o1 // blk)
+        out[g] = blockscaled_gemm(fmt, np.ascontiguousarray(a_codes[:, cs]), np.ascontiguousarray(a_scales[:, ss]),
+                                  float(sa[g]) if nv else 1.0, np.ascontiguousarray(b_codes[:, cs]),
+                                  np.ascontiguousarray(b_scales[:, ss]), float(sb[g]) if nv else 1.0)
+    return out
+
+
 if __name__ == "__main__":
     print(build(force=True), file=sys.stderr)

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ["nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize",
-              "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "bsq_last_error", "bsq_version"]:
+              "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "blockscaled_grouped_gemm",
+              "bsq_last_error", "bsq_version"]:
         assert f in names
 
 
@@ -130,6 +131,39 @@ def test_gemm_rowscaled_flag_validation(L):
     assert f(0x40, 128, 128, 64, *args, 0, None) == 3
     assert f(0x10 | 0x20, 128, 128, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
     assert f(0x30, 0, 128, 64, *args, 0, None) == 0
+
+
+def gg(L, fmt=0, mode=1, groups=4, offs=FAKE, M=256, N=256, K=256, ac=FAKE, as_=FAKE, sa=FAKE, bc=FAKE, bs=FAKE,
+       sb=FAKE, c=FAKE, c_dtype=0):
+    return L.blockscaled_grouped_gemm(fmt, mode, groups, offs, M, N, K, ac, as_, sa, bc, bs, sb, c, c_dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(fmt=2), 3, "fmt"),
+    (dict(fmt=1 | 0x10), 3, "NVFP4 operands only"),
+    (dict(mode=0), 3, "mode"),
+    (dict(mode=3), 3, "mode"),
+    (dict(mode=2, fmt=0x10), 3, "BSQ_GROUP_M only"),
+    (dict(c_dtype=5), 3, "c_dtype"),
+    (dict(groups=-1), 2, "negative"),
+    (dict(K=48), 2, "multiple of 32"),
+    (dict(groups=(1 << 24) + 1), 2, "too many groups"),
+    (dict(offs=None), 1, "offsets"),
+    (dict(c=None), 1, "c is NULL"),
+    (dict(bc=None), 1, "operand"),
+    (dict(sa=None), 1, "tensor-scale"),
+    (dict(offs=FAKE + 4), 6, "8-byte"),
+    (dict(ac=FAKE + 8), 6, "aligned"),
+])
+def test_grouped_gemm_validation(L, kw, status, needle):
+    assert gg(L, **kw) == status
+    assert needle in last(L)
+
+
+def test_grouped_gemm_empty_is_a_no_op(L):
+    assert gg(L, groups=0, offs=None, c=None) == 0
+    assert gg(L, M=0, offs=None) == 0
+    assert gg(L, fmt=1, sa=None, sb=None, N=0) == 0
 
 
 def rq(L, x=FAKE, rows=64, cols=256, rounding=0, signs=None, codes=FAKE, scales=FAKE, amax=FAKE, senc=FAKE):

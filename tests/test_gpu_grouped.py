@@ -1,0 +1,258 @@
+"""GPU parity of the grouped block-scaled GEMM (one GEMM per group in one launch, group
+boundaries read on the device) against the CPU oracle, through the C ABI.
+
+M-grouped (per-expert fprop / dgrad): ragged group sizes including empty groups, rows before
+the first and after the last group (which must stay untouched), K a multiple of 256 (LDS-DMA
+NVFP4 kernel) and not (register-staged kernel), per-group and per-row (row-scaled) NVFP4
+tensor scales, MXFP8, and more than 64 groups (the device-side scan takes several chunks).
+K-grouped (per-expert wgrad): MXFP8 operands quantized columnwise over all tokens, NVFP4
+operands quantized per group, empty and misaligned groups (computed as empty).  Operands
+are quantized on the GPU and by the oracle from the same bf16 inputs and must agree bit for
+bit before the GEMMs are compared (relative Frobenius error <= 2e-3 against the oracle
+output rounded as the GPU stores it)."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_nvfp4_amd as bsq
+from synthetic import STD_W, gaussian_bf16, outlier_bf16
+from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, note, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def splits_to_offsets(first, sizes):
+    return [first] + list(first + np.cumsum(sizes))
+
+
+def check_close(got64, ref64, out_dtype, what):
+    want = bf16_round(ref64) if out_dtype == torch.bfloat16 else ref64
+    err = rel_fro(got64, want)
+    note("  %s rel_fro = %.3e" % (what, err))
+    assert err <= GEMM_TOL, (what, err)
+
+
+def nv_experts(G, N, K, seed):
+    """Per-expert NVFP4 weights, each quantized on its own (GPU and oracle)."""
+    import oracle
+    ws = [gaussian_bf16((N, K), STD_W * (1 + g), seed + g) for g in range(G)]
+    q = [bsq.nvfp4_quantize(w.to(DEV), direction=bsq.ROW) for w in ws]
+    r = [oracle.nvfp4_quantize(w, direction=oracle.ROW) for w in ws]
+    for qq, rr in zip(q, r):
+        assert_bytes_equal(qq["row_codes"], rr["row_codes"], "expert codes")
+    gpu = (torch.stack([x["row_codes"] for x in q]).contiguous(), torch.stack([x["row_scales"] for x in q]).contiguous(),
+           torch.cat([x["s_enc"][0:1] for x in q]).contiguous())
+    ref = (np.stack([x["row_codes"] for x in r]), np.stack([x["row_scales"] for x in r]),
+           np.array([x["s_enc"][0] for x in r], np.float32))
+    return gpu, ref
+
+
+def nv_tokens_per_group(x, offs):
+    """Expert inputs quantized per group (each group its own tensor scale), in one buffer."""
+    import oracle
+    M, K = x.shape
+    G = len(offs) - 1
+    gc = torch.zeros((M, K // 2), dtype=torch.uint8, device=DEV)
+    gs = torch.zeros((M, K // 16), dtype=torch.uint8, device=DEV)
+    gS = torch.ones(G, dtype=torch.float32, device=DEV)
+    rc = np.zeros((M, K // 2), np.uint8)
+    rs = np.zeros((M, K // 16), np.uint8)
+    rS = np.ones(G, np.float32)
+    for g in range(G):
+        o0, o1 = offs[g], offs[g + 1]
+        if o1 == o0:
+            continue
+        q = bsq.nvfp4_quantize(x[o0:o1].contiguous().to(DEV), direction=bsq.ROW)
+        r = oracle.nvfp4_quantize(x[o0:o1].contiguous(), direction=oracle.ROW)
+        gc[o0:o1], gs[o0:o1], gS[g:g + 1] = q["row_codes"], q["row_scales"], q["s_enc"][0:1]
+        rc[o0:o1], rs[o0:o1], rS[g] = r["row_codes"], r["row_scales"], r["s_enc"][0]
+    torch.cuda.synchronize()
+    assert_bytes_equal(gc, rc, "per-group A codes")
+    assert_f32_equal(gS, rS, "per-group A s_enc")
+    return (gc, gs, gS), (rc, rs, rS)
+
+
+def run_m_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, out_dtype, a_rows=False, label=""):
+    import oracle
+    note("grouped M %s fmt=%d M=%d N=%d groups=%d out=%s" % (label, fmt, M, N, len(offs) - 1, out_dtype))
+    o = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    out = torch.full((M, N), 1.0, dtype=out_dtype, device=DEV)
+    f = fmt | (bsq.FMT_A_ROWSCALED if a_rows else 0)
+    bsq.blockscaled_grouped_gemm(f, bsq.GROUP_M, o, *a_gpu, *b_gpu, out_dtype=out_dtype, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_M, offs, *a_ref, *b_ref, a_rows=a_rows)
+    got = out.float().cpu().numpy().astype(np.float64)
+    inside = ~np.isnan(ref[:, 0])
+    assert np.all(got[~inside] == 1.0), "rows outside every group were written"
+    if inside.any():
+        check_close(got[inside], ref[inside], out_dtype, label)
+
+
+@pytest.mark.parametrize("K", [512, 160])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_m_grouped_nvfp4_per_group_scales(K, out_dtype):
+    sizes = [300, 0, 517, 211]
+    offs = splits_to_offsets(16, sizes)
+    M, N = offs[-1] + 9, 384
+    x = outlier_bf16((M, K), seed=K, mask_seed=K + 1)
+    a_gpu, a_ref = nv_tokens_per_group(x, offs)
+    b_gpu, b_ref = nv_experts(len(sizes), N, K, 100)
+    run_m_grouped(bsq.FMT_NVFP4, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, out_dtype, label="nvfp4 per-group")
+
+
+def test_m_grouped_nvfp4_rowscaled_inputs():
+    """The Composer-style grouped fprop: row-scaled NVFP4 expert inputs (one call over all
+    tokens: rows are independent), per-tensor NVFP4 experts."""
+    import oracle
+    sizes = [640, 37, 0, 1100, 256]
+    offs = splits_to_offsets(0, sizes)
+    M, N, K = offs[-1], 512, 1024
+    x = (gaussian_bf16((M, K), 1.0, 7).float() * torch.logspace(-2, 2, M).reshape(M, 1)).to(torch.bfloat16)
+    q = bsq.nvfp4_quantize_rowscaled(x.to(DEV))
+    r = oracle.nvfp4_quantize_rowscaled(x)
+    torch.cuda.synchronize()
+    assert_bytes_equal(q["codes"], r["codes"], "row-scaled codes")
+    assert_f32_equal(q["s_enc"], r["s_enc"], "row-scaled s_enc")
+    b_gpu, b_ref = nv_experts(len(sizes), N, K, 200)
+    run_m_grouped(bsq.FMT_NVFP4, (q["codes"], q["scales"], q["s_enc"]), (r["codes"], r["scales"], r["s_enc"]),
+                  b_gpu, b_ref, offs, M, N, torch.bfloat16, a_rows=True, label="row-scaled fprop")
+
+
+def test_m_grouped_mxfp8_dgrad():
+    import oracle
+    sizes = [96, 500, 0, 333]
+    offs = splits_to_offsets(5, sizes)
+    M, N, K = offs[-1] + 3, 320, 512
+    dy = gaussian_bf16((M, K), 1e-3, 11)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.ROW)
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.ROW)
+    ws = [gaussian_bf16((N, K), STD_W, 300 + g) for g in range(len(sizes))]
+    qb = [bsq.mxfp8_quantize(w.to(DEV), direction=bsq.ROW) for w in ws]
+    rb = [oracle.mxfp8_quantize(w, direction=oracle.ROW) for w in ws]
+    torch.cuda.synchronize()
+    assert_bytes_equal(qa["row_codes"], ra["row_codes"], "dY codes")
+    b_gpu = (torch.stack([x["row_codes"] for x in qb]).contiguous(), torch.stack([x["row_scales"] for x in qb]).contiguous(), None)
+    b_ref = (np.stack([x["row_codes"] for x in rb]), np.stack([x["row_scales"] for x in rb]), None)
+    run_m_grouped(bsq.FMT_MXFP8, (qa["row_codes"], qa["row_scales"], None), (ra["row_codes"], ra["row_scales"], None),
+                  b_gpu, b_ref, offs, M, N, torch.bfloat16, label="mxfp8 dgrad")
+
+
+def test_m_grouped_many_groups():
+    """100 groups of 0..40 rows: the device-side scan walks two 64-group chunks."""
+    rng = np.random.default_rng(12)
+    sizes = rng.integers(0, 41, 100)
+    sizes[[3, 64, 65, 99]] = 0
+    offs = splits_to_offsets(0, sizes)
+    M, N, K = offs[-1], 128, 256
+    x = gaussian_bf16((M, K), 1.0, 13)
+    a_gpu, a_ref = nv_tokens_per_group(x, offs)
+    b_gpu, b_ref = nv_experts(100, N, K, 400)
+    run_m_grouped(bsq.FMT_NVFP4, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, torch.bfloat16, label="100 groups")
+
+
+def run_k_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, label=""):
+    import oracle
+    note("grouped K %s fmt=%d M=%d N=%d groups=%d" % (label, fmt, M, N, len(offs) - 1))
+    o = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    out = bsq.blockscaled_grouped_gemm(fmt, bsq.GROUP_K, o, *a_gpu, *b_gpu, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_K, offs, *a_ref, *b_ref)
+    got = out.cpu().numpy().astype(np.float64)
+    for g in range(len(offs) - 1):
+        if not ref[g].any():
+            assert not got[g].any(), "group %d should be zero" % g
+        else:
+            check_close(got[g], ref[g], torch.float32, "%s group %d" % (label, g))
+
+
+def test_k_grouped_mxfp8_wgrad():
+    """dW_g = dY_g^T X_g over token groups, both operands MXFP8 columnwise over all tokens: an
+    empty group, groups of 32 and 64 tokens, two misaligned groups (empty by definition), and
+    groups whose length is a multiple of 512 (scale-record path, at offset 0 and inside the
+    rows) next to ones that are not."""
+    import oracle
+    offs = [0, 512, 512, 544, 1000, 1024, 1536, 1984, 2048]
+    T, M, N = 2048, 320, 192
+    dy = gaussian_bf16((T, M), 1e-3, 21)
+    x = outlier_bf16((T, N), seed=22, mask_seed=23)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.COL)
+    qb = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.COL)
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.COL)
+    rb = oracle.mxfp8_quantize(x, direction=oracle.COL)
+    torch.cuda.synchronize()
+    assert_bytes_equal(qa["col_codes"], ra["col_codes"], "dY col codes")
+    assert_bytes_equal(qb["col_codes"], rb["col_codes"], "X col codes")
+    run_k_grouped(bsq.FMT_MXFP8, (qa["col_codes"], qa["col_scales"], None), (ra["col_codes"], ra["col_scales"], None),
+                  (qb["col_codes"], qb["col_scales"], None), (rb["col_codes"], rb["col_scales"], None),
+                  offs, M, N, label="mxfp8 wgrad")
+
+
+def test_k_grouped_nvfp4_per_group_scales():
+    """NVFP4 wgrad operands quantized columnwise per group (each group its own tensor scale)
+    and laid out along the token dimension."""
+    import oracle
+    offs = [0, 256, 288, 288, 800]
+    T, M, N = 800, 288, 160
+    dy = gaussian_bf16((T, M), 1e-3, 31)
+    x = gaussian_bf16((T, N), 1.0, 32)
+    G = len(offs) - 1
+    parts_q, parts_r = [], []
+    for g in range(G):
+        o0, o1 = offs[g], offs[g + 1]
+        if o1 == o0:
+            parts_q.append(None)
+            parts_r.append(None)
+            continue
+        parts_q.append([bsq.nvfp4_quantize(t[o0:o1].contiguous().to(DEV), direction=bsq.COL) for t in (dy, x)])
+        parts_r.append([oracle.nvfp4_quantize(t[o0:o1].contiguous(), direction=oracle.COL) for t in (dy, x)])
+    torch.cuda.synchronize()
+
+    def cat_gpu(i, key):
+        return torch.cat([p[i][key] for p in parts_q if p is not None], dim=1).contiguous()
+
+    def cat_ref(i, key):
+        return np.ascontiguousarray(np.concatenate([p[i][key] for p in parts_r if p is not None], axis=1))
+
+    def s_gpu(i):
+        return torch.cat([p[i]["s_enc"][1:2] if p is not None else torch.ones(1, device=DEV) for p in parts_q]).contiguous()
+
+    def s_ref(i):
+        return np.array([p[i]["s_enc"][1] if p is not None else 1.0 for p in parts_r], np.float32)
+
+    for i in (0, 1):
+        assert_bytes_equal(cat_gpu(i, "col_codes"), cat_ref(i, "col_codes"), "col codes %d" % i)
+        assert_f32_equal(s_gpu(i), s_ref(i), "per-group s_enc %d" % i)
+    run_k_grouped(bsq.FMT_NVFP4, (cat_gpu(0, "col_codes"), cat_gpu(0, "col_scales"), s_gpu(0)),
+                  (cat_ref(0, "col_codes"), cat_ref(0, "col_scales"), s_ref(0)),
+                  (cat_gpu(1, "col_codes"), cat_gpu(1, "col_scales"), s_gpu(1)),
+                  (cat_ref(1, "col_codes"), cat_ref(1, "col_scales"), s_ref(1)), offs, M, N, label="nvfp4 wgrad")
+
+
+def test_grouped_moe_fprop_sampled():
+    """A mixture-of-experts fprop at a realistic size: 8 experts, 16384 routed tokens,
+    K = 4096, N = 2048, row-scaled NVFP4 inputs; compared on sampled rows x columns."""
+    import oracle
+    G, T, N, K = 8, 16384, 2048, 4096
+    rng = np.random.default_rng(41)
+    cuts = np.sort(rng.choice(np.arange(1, T), G - 1, replace=False))
+    offs = [0] + [int(c) for c in cuts] + [T]
+    note("grouped M moe fprop sampled offs=%s" % offs)
+    x = gaussian_bf16((T, K), 1.0, 42)
+    q = bsq.nvfp4_quantize_rowscaled(x.to(DEV))
+    b_gpu, b_ref = nv_experts(G, N, K, 500)
+    o = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    y = bsq.blockscaled_grouped_gemm(bsq.FMT_NVFP4 | bsq.FMT_A_ROWSCALED, bsq.GROUP_M, o, q["codes"], q["scales"],
+                                     q["s_enc"], *b_gpu)
+    torch.cuda.synchronize()
+    r = oracle.nvfp4_quantize_rowscaled(x)
+    assert_bytes_equal(q["codes"], r["codes"], "row-scaled codes")
+    cols = np.sort(rng.choice(N, 64, replace=False))
+    yc = y.float().cpu().numpy().astype(np.float64)
+    for g in range(G):
+        o0, o1 = offs[g], offs[g + 1]
+        rows = np.sort(rng.choice(np.arange(o0, o1), min(12, o1 - o0), replace=False))
+        ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, r["codes"][o0:o1], r["scales"][o0:o1], r["s_enc"][o0:o1],
+                                      b_ref[0][g], b_ref[1][g], float(b_ref[2][g]), rows=rows - o0, cols=cols)
+        check_close(yc[rows][:, cols], ref, torch.bfloat16, "expert %d" % g)
