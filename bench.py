@@ -192,6 +192,64 @@ def rowscaled_figures(step, iters: int):
             "gemm_fwd_rowscaled_X_TFLOPs": round(2.0 * M_TOK * N_OUT * K_IN / (g_ms * 1e-3) / 1e12, 2)}
 
 
+MOE_EXPERTS = 8
+
+
+def grouped_figures(step, iters: int):
+    """Side figures outside the step: the same layer's tokens routed to MOE_EXPERTS experts
+    of the same shape (seeded random split), run as grouped GEMMs in the Composer-style
+    grouped recipe -- fprop on row-scaled NVFP4 inputs and per-expert NVFP4 weights, dgrad and
+    wgrad on MXFP8 -- each timed over ``iters`` launches.  Total flops equal the dense GEMM's."""
+    import numpy as np
+    bsq, torch = step.bsq, step.torch
+    G = MOE_EXPERTS
+    rng = np.random.default_rng(2024)
+    cuts = np.sort(rng.choice(np.arange(1, M_TOK // 32), G - 1, replace=False)) * 32   # wgrad needs 32-multiples
+    offs_l = [0] + [int(c) for c in cuts] + [M_TOK]
+    offs = torch.tensor(offs_l, dtype=torch.int64, device=step.dev)
+    qx = bsq.nvfp4_quantize_rowscaled(step.X)
+    w_codes = torch.empty((G, N_OUT, K_IN // 2), dtype=torch.uint8, device=step.dev)
+    w_scales = torch.empty((G, N_OUT, K_IN // 16), dtype=torch.uint8, device=step.dev)
+    w_s = torch.empty(G, dtype=torch.float32, device=step.dev)
+    mw_codes = torch.empty((G, K_IN, N_OUT), dtype=torch.uint8, device=step.dev)
+    mw_scales = torch.empty((G, K_IN, N_OUT // 32), dtype=torch.uint8, device=step.dev)
+    for g in range(G):   # experts: W scaled per expert so that every expert has its own tensor scale
+        wg = (step.W.float() * (1.0 + 0.1 * g)).to(torch.bfloat16)
+        q = bsq.nvfp4_quantize(wg, direction=bsq.ROW)
+        w_codes[g], w_scales[g], w_s[g:g + 1] = q["row_codes"], q["row_scales"], q["s_enc"][0:1]
+        m = bsq.mxfp8_requantize_nvfp4(q["row_codes"], q["row_scales"], q["s_enc"][0:1], direction=bsq.COL)
+        mw_codes[g], mw_scales[g] = m["col_codes"], m["col_scales"]
+    mdy = bsq.mxfp8_quantize(step.dY, direction=bsq.ROW | bsq.COL)
+    mx = bsq.mxfp8_quantize(step.X, direction=bsq.COL)
+    fwd_fmt = bsq.FMT_NVFP4 | bsq.FMT_A_ROWSCALED
+    y = torch.empty((M_TOK, N_OUT), dtype=torch.bfloat16, device=step.dev)
+    dx = torch.empty((M_TOK, K_IN), dtype=torch.bfloat16, device=step.dev)
+    dw = torch.empty((G, N_OUT, K_IN), dtype=torch.float32, device=step.dev)
+    launches = {
+        "fprop": lambda: bsq.blockscaled_grouped_gemm(fwd_fmt, bsq.GROUP_M, offs, qx["codes"], qx["scales"],
+                                                      qx["s_enc"], w_codes, w_scales, w_s, out=y),
+        "dgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8, bsq.GROUP_M, offs, mdy["row_codes"],
+                                                      mdy["row_scales"], None, mw_codes, mw_scales, None, out=dx),
+        "wgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8, bsq.GROUP_K, offs, mdy["col_codes"],
+                                                      mdy["col_scales"], None, mx["col_codes"], mx["col_scales"],
+                                                      None, out_dtype=torch.float32, out=dw),
+    }
+    out = {"experts": G, "tokens_per_expert": [offs_l[i + 1] - offs_l[i] for i in range(G)]}
+    flops = 2.0 * M_TOK * N_OUT * K_IN
+    for name, fn in launches.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out["grouped_%s_TFLOPs" % name] = round(flops / (ms * 1e-3) / 1e12, 2)
+    return out
+
+
 def cpu_baseline(tokens: int):
     """The oracle on a token-sample of the step: the same operations with M = tokens."""
     import numpy as np
@@ -260,6 +318,7 @@ def main():
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
     side = rowscaled_figures(step, max(3, args.steps // 2))
+    moe = grouped_figures(step, max(3, args.steps // 2))
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
     tr = measured_traffic()
     # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
@@ -283,6 +342,7 @@ def main():
                       "gemm_wgrad_nvfp4": round(g_wgrad, 4), "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
         "mxfp8_gemm_TFLOPs": round(gemm_flops / (g_dgrad * 1e-3) / 1e12, 2),
         "row_scaled": side,
+        "moe_grouped": moe,
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -175,3 +175,27 @@ def test_edge_rules(orc):
     assert not got[3].any()                           # 16..128 (500 clamped): 16 not aligned
     got2 = orc.blockscaled_grouped_gemm(orc.FMT_MXFP8, orc.GROUP_K, [0, 64, 500], ac, as_, None, bc, bs, None)
     assert np.array_equal(got2[1], whole(64, 128))   # 500 clamped to T
+
+
+def test_split_quantize_of_the_grouped_recipe_is_the_whole_tensor_call(orc):
+    """Row-scaled NVFP4 (RNE) and MXFP8 of each token split equal the whole-tensor
+    quantization restricted to the split when the splits are multiples of 32 (rows are
+    independent, MXFP8 has no tensor scale) -- so the grouped recipe's split-quantize needs
+    no per-split launch."""
+    T, K = 224, 96
+    offs = [0, 64, 64, 160, 224]
+    x = outlier_bf16((T, K), seed=70, mask_seed=71)
+    rs = orc.nvfp4_quantize_rowscaled(x)
+    mx = orc.mxfp8_quantize(x, direction=orc.ROW | orc.COL)
+    for g in range(4):
+        o0, o1 = offs[g], offs[g + 1]
+        if o1 == o0:
+            continue
+        part = x[o0:o1].contiguous()
+        p_rs = orc.nvfp4_quantize_rowscaled(part)
+        assert np.array_equal(p_rs["codes"], rs["codes"][o0:o1]) and np.array_equal(p_rs["s_enc"], rs["s_enc"][o0:o1])
+        assert np.array_equal(p_rs["scales"], rs["scales"][o0:o1])
+        p_mx = orc.mxfp8_quantize(part, direction=orc.ROW | orc.COL)
+        assert np.array_equal(p_mx["row_codes"], mx["row_codes"][o0:o1])
+        assert np.array_equal(p_mx["col_codes"], mx["col_codes"][:, o0:o1])
+        assert np.array_equal(p_mx["col_scales"], mx["col_scales"][:, o0 // 32:o1 // 32])
