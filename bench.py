@@ -192,6 +192,28 @@ def rowscaled_figures(step, iters: int):
             "gemm_fwd_rowscaled_X_TFLOPs": round(2.0 * M_TOK * N_OUT * K_IN / (g_ms * 1e-3) / 1e12, 2)}
 
 
+def linear_layer_figures(step, iters: int):
+    """Side figure outside the step: the NVFP4 linear layer entry points (forward saving the
+    quantized activation, backward with RHT + SR on every backward operand and NVFP4 dgrad),
+    forward + backward timed over ``iters`` iterations with a preallocated workspace."""
+    bsq, torch = step.bsq, step.torch
+    L = bsq.lib()
+    ws = torch.empty(L.nvfp4_linear_workspace_bytes(M_TOK, K_IN, N_OUT), dtype=torch.uint8, device=step.dev)
+    y, saved = bsq.nvfp4_linear_forward(step.X, step.W, step.seed, step.signs, workspace=ws)
+    bsq.nvfp4_linear_backward(step.dY, step.W, saved, step.seed, step.signs, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        y, saved = bsq.nvfp4_linear_forward(step.X, step.W, step.seed, step.signs, workspace=ws)
+        bsq.nvfp4_linear_backward(step.dY, step.W, saved, step.seed, step.signs, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    return {"ms": round(ms, 4), "TFLOPs": round(3 * 2.0 * M_TOK * N_OUT * K_IN / (ms * 1e-3) / 1e12, 2),
+            "saved_activation_bytes": int(saved.numel()), "bf16_activation_bytes": 2 * M_TOK * K_IN}
+
+
 MOE_EXPERTS = 8
 
 
@@ -319,6 +341,7 @@ def main():
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
     side = rowscaled_figures(step, max(3, args.steps // 2))
     moe = grouped_figures(step, max(3, args.steps // 2))
+    layer = linear_layer_figures(step, max(3, args.steps // 2))
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
     tr = measured_traffic()
     # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
@@ -343,6 +366,7 @@ def main():
         "mxfp8_gemm_TFLOPs": round(gemm_flops / (g_dgrad * 1e-3) / 1e12, 2),
         "row_scaled": side,
         "moe_grouped": moe,
+        "nvfp4_linear_layer": layer,
         "roofline": roofline,
         "cpu_baseline": None,
     }

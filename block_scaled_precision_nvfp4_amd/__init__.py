@@ -54,7 +54,14 @@ def lib():
         L.rht_apply.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.blockscaled_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         L.blockscaled_grouped_gemm.argtypes = [i32, i32, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]
-        for f in ("nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
+        L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nvfp4_linear_workspace_bytes.restype = C.c_int64
+        L.nvfp4_linear_saved_bytes.argtypes = [i64, i64]
+        L.nvfp4_linear_saved_bytes.restype = C.c_int64
+        L.nvfp4_linear_forward.argtypes = [vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
+        L.nvfp4_linear_backward.argtypes = [vp, vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
+        for f in ("nvfp4_linear_forward", "nvfp4_linear_backward", "nvfp4_quantize", "nvfp4_quantize_rowscaled",
+                  "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
                   "blockscaled_gemm", "blockscaled_grouped_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int
         L.bsq_last_error.argtypes = []
@@ -285,3 +292,47 @@ def blockscaled_grouped_gemm(fmt: int, mode: int, offsets: torch.Tensor, a_codes
         fmt, mode, G, offsets.data_ptr(), M, N, K, a_codes.data_ptr(), a_scales.data_ptr(), _ptr(a_s_enc),
         b_codes.data_ptr(), b_scales.data_ptr(), _ptr(b_s_enc), out.data_ptr(), c_dtype, _stream(a_codes.device)))
     return out
+
+
+def nvfp4_linear_forward(x: torch.Tensor, w: torch.Tensor, sr_seed: int, rht_signs,
+                         workspace: Optional[torch.Tensor] = None):
+    """NVFP4 linear forward: returns (y [T, N] bf16, saved) where ``saved`` (a uint8 device
+    tensor) holds the quantized activation that nvfp4_linear_backward needs."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(w, torch.bfloat16, "w")
+    T, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    L = lib()
+    saved = torch.empty(L.nvfp4_linear_saved_bytes(T, K), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(L.nvfp4_linear_workspace_bytes(T, K, N), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    sg = _signs(rht_signs, dev)
+    _check("nvfp4_linear_forward", L.nvfp4_linear_forward(
+        x.data_ptr(), w.data_ptr(), T, K, N, sr_seed & (2 ** 64 - 1), sg.data_ptr(), saved.data_ptr(),
+        workspace.data_ptr(), y.data_ptr(), _stream(dev)))
+    return y, saved
+
+
+def nvfp4_linear_backward(dy: torch.Tensor, w: torch.Tensor, saved: torch.Tensor, sr_seed: int, rht_signs,
+                          workspace: Optional[torch.Tensor] = None):
+    """NVFP4 linear backward: returns (dx [T, K] bf16, dw [N, K] fp32)."""
+    _dev_tensor(dy, torch.bfloat16, "dy")
+    _dev_tensor(w, torch.bfloat16, "w")
+    _dev_tensor(saved, torch.uint8, "saved")
+    T, N = dy.shape
+    K = w.shape[1]
+    dev = dy.device
+    L = lib()
+    if saved.numel() < L.nvfp4_linear_saved_bytes(T, K):
+        raise ValueError("saved buffer is too small for this layer")
+    if workspace is None:
+        workspace = torch.empty(L.nvfp4_linear_workspace_bytes(T, K, N), dtype=torch.uint8, device=dev)
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    sg = _signs(rht_signs, dev)
+    _check("nvfp4_linear_backward", L.nvfp4_linear_backward(
+        dy.data_ptr(), w.data_ptr(), saved.data_ptr(), T, K, N, sr_seed & (2 ** 64 - 1), sg.data_ptr(),
+        workspace.data_ptr(), dx.data_ptr(), dw.data_ptr(), _stream(dev)))
+    return dx, dw

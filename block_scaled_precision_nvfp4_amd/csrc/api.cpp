@@ -201,3 +201,154 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- the linear layer
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// One NVFP4 operand inside a caller buffer: codes, scales, then amax[2] and s_enc[2].
+struct Nv {
+    int64_t codes, scales, amax, s_enc, end;
+};
+
+Nv nv_at(int64_t base, int64_t elems) {
+    Nv o;
+    o.codes = base;
+    o.scales = up(o.codes + elems / 2);
+    o.amax = up(o.scales + elems / 16);
+    o.s_enc = o.amax + 8;
+    o.end = up(o.s_enc + 8);
+    return o;
+}
+
+struct LinearLayout {
+    Nv x_row, w_row;            // forward workspace
+    Nv dy, w_col;               // backward workspace (dy holds both directions' codes)
+    int64_t dy_col_codes, dy_col_scales;
+    int64_t fwd_bytes, bwd_bytes;
+    Nv x_col;                   // the saved activation
+    int64_t saved_bytes;
+};
+
+LinearLayout linear_layout(int64_t T, int64_t K, int64_t N) {
+    LinearLayout L;
+    L.x_row = nv_at(0, T * K);
+    L.w_row = nv_at(L.x_row.end, N * K);
+    L.fwd_bytes = L.w_row.end;
+    L.dy = nv_at(0, T * N);
+    L.dy_col_codes = L.dy.end;
+    L.dy_col_scales = up(L.dy_col_codes + T * N / 2);
+    L.w_col = nv_at(up(L.dy_col_scales + T * N / 16), K * N);
+    L.bwd_bytes = L.w_col.end;
+    L.x_col = nv_at(0, K * T);
+    L.saved_bytes = L.x_col.end;
+    return L;
+}
+
+template <typename T>
+T* at(void* base, int64_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off); }
+
+int linear_shape_check(const char* fn, int64_t T, int64_t K, int64_t N) {
+    if (T < 0 || K < 0 || N < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (T % 32 != 0 || K % 32 != 0 || N % 32 != 0)
+        return fail(BSQ_ERR_SHAPE, "%s: tokens, in_features and out_features must be multiples of 32, got %lld, %lld, %lld",
+                    fn, (long long)T, (long long)K, (long long)N);
+    return BSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4_linear_workspace_bytes(int64_t tokens, int64_t in_features, int64_t out_features) {
+    if (tokens < 0 || in_features < 0 || out_features < 0) return -1;
+    const LinearLayout L = linear_layout(tokens, in_features, out_features);
+    return L.fwd_bytes > L.bwd_bytes ? L.fwd_bytes : L.bwd_bytes;
+}
+
+int64_t nvfp4_linear_saved_bytes(int64_t tokens, int64_t in_features) {
+    if (tokens < 0 || in_features < 0) return -1;
+    return linear_layout(tokens, in_features, 0).saved_bytes;
+}
+
+int nvfp4_linear_forward(const void* x, const void* w, int64_t tokens, int64_t in_features, int64_t out_features,
+                         uint64_t sr_seed, const int8_t* rht_signs, void* saved, void* workspace, void* y,
+                         void* hip_stream) {
+    static const char* fn = "nvfp4_linear_forward";
+    const int64_t T = tokens, K = in_features, N = out_features;
+    int st = linear_shape_check(fn, T, K, N);
+    if (st) return st;
+    if (T == 0 || K == 0 || N == 0) return fail(BSQ_ERR_SHAPE, "%s: empty layer", fn);
+    if (!x || !w || !rht_signs || !saved || !workspace || !y) return fail(BSQ_ERR_NULL, "%s: NULL argument", fn);
+    if (misaligned(x) || misaligned(w) || misaligned(rht_signs) || misaligned(saved) || misaligned(workspace) ||
+        misaligned(y))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    const LinearLayout L = linear_layout(T, K, N);
+    void* ws = workspace;
+    // fprop operands: rowwise NVFP4, RNE
+    st = bsq::launch_nvfp4_quantize(x, T, K, BSQ_ROW, BSQ_RNE, 0, 0, nullptr, at<uint8_t>(ws, L.x_row.codes),
+                                    at<uint8_t>(ws, L.x_row.scales), nullptr, nullptr, at<float>(ws, L.x_row.amax),
+                                    at<float>(ws, L.x_row.s_enc), hip_stream);
+    if (st) return launched(st, fn);
+    st = bsq::launch_nvfp4_quantize(w, N, K, BSQ_ROW, BSQ_RNE, 0, 0, nullptr, at<uint8_t>(ws, L.w_row.codes),
+                                    at<uint8_t>(ws, L.w_row.scales), nullptr, nullptr, at<float>(ws, L.w_row.amax),
+                                    at<float>(ws, L.w_row.s_enc), hip_stream);
+    if (st) return launched(st, fn);
+    st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, T, N, K, at<uint8_t>(ws, L.x_row.codes),
+                                      at<uint8_t>(ws, L.x_row.scales), at<float>(ws, L.x_row.s_enc),
+                                      at<uint8_t>(ws, L.w_row.codes), at<uint8_t>(ws, L.w_row.scales),
+                                      at<float>(ws, L.w_row.s_enc), 0, 0, y, BSQ_OUT_BF16, hip_stream);
+    if (st) return launched(st, fn);
+    // the saved activation: X columnwise along tokens (the wgrad contraction), RHT + SR
+    st = bsq::launch_nvfp4_quantize(x, T, K, BSQ_COL, BSQ_SR, sr_seed, 1, rht_signs, nullptr, nullptr,
+                                    at<uint8_t>(saved, L.x_col.codes), at<uint8_t>(saved, L.x_col.scales),
+                                    at<float>(saved, L.x_col.amax), at<float>(saved, L.x_col.s_enc), hip_stream);
+    return launched(st, fn);
+}
+
+int nvfp4_linear_backward(const void* dy, const void* w, const void* saved, int64_t tokens, int64_t in_features,
+                          int64_t out_features, uint64_t sr_seed, const int8_t* rht_signs, void* workspace, void* dx,
+                          float* dw, void* hip_stream) {
+    static const char* fn = "nvfp4_linear_backward";
+    const int64_t T = tokens, K = in_features, N = out_features;
+    int st = linear_shape_check(fn, T, K, N);
+    if (st) return st;
+    if (T == 0 || K == 0 || N == 0) return fail(BSQ_ERR_SHAPE, "%s: empty layer", fn);
+    if (!dy || !w || !saved || !rht_signs || !workspace || !dx || !dw) return fail(BSQ_ERR_NULL, "%s: NULL argument", fn);
+    if (misaligned(dy) || misaligned(w) || misaligned(saved) || misaligned(rht_signs) || misaligned(workspace) ||
+        misaligned(dx) || misaligned(dw))
+        return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    const LinearLayout L = linear_layout(T, K, N);
+    void* ws = workspace;
+    void* sv = const_cast<void*>(saved);
+    // dY in both directions in one pass (RHT + SR; rowwise along out_features for dgrad,
+    // columnwise along tokens for wgrad)
+    st = bsq::launch_nvfp4_quantize(dy, T, N, BSQ_ROW | BSQ_COL, BSQ_SR, sr_seed, 0, rht_signs,
+                                    at<uint8_t>(ws, L.dy.codes), at<uint8_t>(ws, L.dy.scales),
+                                    at<uint8_t>(ws, L.dy_col_codes), at<uint8_t>(ws, L.dy_col_scales),
+                                    at<float>(ws, L.dy.amax), at<float>(ws, L.dy.s_enc), hip_stream);
+    if (st) return launched(st, fn);
+    // wgrad: dW[N][K] = dY^T X over tokens
+    st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, N, K, T, at<uint8_t>(ws, L.dy_col_codes),
+                                      at<uint8_t>(ws, L.dy_col_scales), at<float>(ws, L.dy.s_enc) + 1,
+                                      at<uint8_t>(sv, L.x_col.codes), at<uint8_t>(sv, L.x_col.scales),
+                                      at<float>(sv, L.x_col.s_enc) + 1, 0, 0, dw, BSQ_OUT_F32, hip_stream);
+    if (st) return launched(st, fn);
+    // dgrad operand W columnwise along out_features, RHT + SR
+    st = bsq::launch_nvfp4_quantize(w, N, K, BSQ_COL, BSQ_SR, sr_seed, 2, rht_signs, nullptr, nullptr,
+                                    at<uint8_t>(ws, L.w_col.codes), at<uint8_t>(ws, L.w_col.scales),
+                                    at<float>(ws, L.w_col.amax), at<float>(ws, L.w_col.s_enc), hip_stream);
+    if (st) return launched(st, fn);
+    // dgrad: dX[T][K] = dY W over out_features
+    st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, T, K, N, at<uint8_t>(ws, L.dy.codes),
+                                      at<uint8_t>(ws, L.dy.scales), at<float>(ws, L.dy.s_enc),
+                                      at<uint8_t>(ws, L.w_col.codes), at<uint8_t>(ws, L.w_col.scales),
+                                      at<float>(ws, L.w_col.s_enc) + 1, 0, 0, dx, BSQ_OUT_BF16, hip_stream);
+    return launched(st, fn);
+}
+
+}  // extern "C"

@@ -264,6 +264,48 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
                              const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
                              void* c, int c_dtype, void* hip_stream);
 
+/*
+ * The NVFP4 linear layer, forward and backward, as two calls over the kernels above: the
+ * quantized linear of the page "Add an NVFP4 quantization converter" (torchtitan PR #3914:
+ * Summary / "What changed" -- forward operands in NVFP4, the backward GEMMs' operands with
+ * the 16-point RHT under a shared sign vector along their contraction dimension and
+ * stochastic rounding keyed by a seed; "Numerical and performance validation", Table 1 and
+ * its takeaway -- the layer keeps quantized activations and their scales for the backward
+ * pass instead of bf16, which is where its memory saving comes from).
+ *
+ *   forward:  Y[T][N] (bf16) = NVFP4_row_RNE(X) * NVFP4_row_RNE(W)^T, and `saved` receives
+ *             X's columnwise NVFP4 along tokens with RHT + SR (SR stream 1) -- the wgrad
+ *             operand, 0.5625 bytes per element instead of the 2 of bf16 X.
+ *   backward: dY is quantized once in both directions with RHT + SR (SR stream 0; rowwise
+ *             along N for dgrad, columnwise along tokens for wgrad); W columnwise along N with
+ *             RHT + SR (SR stream 2);
+ *             dW[N][K] (fp32) = dY_col * X_col^T  (contraction over tokens, X from `saved`),
+ *             dX[T][K] (bf16) = dY_row * W_col^T  (contraction over N).
+ * Each step is exactly the corresponding nvfp4_quantize / blockscaled_gemm call; the
+ * intermediate quantized operands live in `workspace`.
+ *
+ *   x [T][K], w [N][K], dy [T][N] bf16 (device); T = tokens, K = in_features,
+ *   N = out_features, all multiples of 32 and non-zero.
+ *   sr_seed, rht_signs: as for nvfp4_quantize (rht_signs required); the same values must be
+ *   passed to forward and backward (the saved operand was drawn with them).
+ *   saved      device buffer of nvfp4_linear_saved_bytes(T, K) bytes, written by forward and
+ *              read by backward (layout private to the library).
+ *   workspace  device buffer of nvfp4_linear_workspace_bytes(T, K, N) bytes, scratch for
+ *              either call (contents not preserved).
+ *   y [T][N] bf16; dx [T][K] bf16; dw [N][K] fp32 (device).
+ * Work is enqueued on hip_stream; a failed launch returns BSQ_ERR_HIP with the steps before
+ * it already enqueued.  The size queries return -1 for negative sizes.
+ */
+int64_t nvfp4_linear_workspace_bytes(int64_t tokens, int64_t in_features, int64_t out_features);
+int64_t nvfp4_linear_saved_bytes(int64_t tokens, int64_t in_features);
+int nvfp4_linear_forward(const void* x, const void* w, int64_t tokens, int64_t in_features,
+                         int64_t out_features, uint64_t sr_seed, const int8_t* rht_signs,
+                         void* saved, void* workspace, void* y, void* hip_stream);
+int nvfp4_linear_backward(const void* dy, const void* w, const void* saved, int64_t tokens,
+                          int64_t in_features, int64_t out_features, uint64_t sr_seed,
+                          const int8_t* rht_signs, void* workspace, void* dx, float* dw,
+                          void* hip_stream);
+
 /* Message of the last failing call on this thread ("" if none).  Host memory owned
  * by the library; valid until the thread's next call. */
 const char* bsq_last_error(void);

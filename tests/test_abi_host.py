@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ["nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize",
               "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "blockscaled_grouped_gemm",
-              "bsq_last_error", "bsq_version"]:
+              "nvfp4_linear_workspace_bytes", "nvfp4_linear_saved_bytes", "nvfp4_linear_forward",
+              "nvfp4_linear_backward", "bsq_last_error", "bsq_version"]:
         assert f in names
 
 
@@ -164,6 +165,27 @@ def test_grouped_gemm_empty_is_a_no_op(L):
     assert gg(L, groups=0, offs=None, c=None) == 0
     assert gg(L, M=0, offs=None) == 0
     assert gg(L, fmt=1, sa=None, sb=None, N=0) == 0
+
+
+def test_linear_sizes(L):
+    T, K, N = 256, 512, 384
+    saved = L.nvfp4_linear_saved_bytes(T, K)
+    ws = L.nvfp4_linear_workspace_bytes(T, K, N)
+    assert saved >= T * K * 9 // 16 + 16 and saved < T * K * 2
+    # workspace holds the forward operands of X and W, or dY (both directions) and W's columnwise
+    assert ws >= max((T + N) * K * 9 // 16, 2 * T * N * 9 // 16 + N * K * 9 // 16)
+    assert L.nvfp4_linear_saved_bytes(-1, 4) == -1 and L.nvfp4_linear_workspace_bytes(1, -1, 1) == -1
+
+
+def test_linear_validation(L):
+    fwd, bwd = L.nvfp4_linear_forward, L.nvfp4_linear_backward
+    assert fwd(FAKE, FAKE, 48, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, None) == 2 and "multiples of 32" in last(L)
+    assert fwd(FAKE, FAKE, 0, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, None) == 2 and "empty" in last(L)
+    assert fwd(FAKE, FAKE, 64, 64, 64, 0, None, FAKE, FAKE, FAKE, None) == 1
+    assert fwd(FAKE, FAKE, 64, 64, 64, 0, FAKE, FAKE, FAKE + 8, FAKE, None) == 6
+    assert bwd(FAKE, FAKE, FAKE, 64, 64, 40, 0, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert bwd(FAKE, FAKE, None, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert bwd(FAKE, FAKE, FAKE, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE + 4, None) == 6
 
 
 def rq(L, x=FAKE, rows=64, cols=256, rounding=0, signs=None, codes=FAKE, scales=FAKE, amax=FAKE, senc=FAKE):
