@@ -19,7 +19,7 @@ hardware-counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
 ratio the same counter shows for a plain copy of known size, which `--copy-calibration`
 runs); it is reported only while the GEMM sources still hash to the values recorded there.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-side-figures]
        python bench.py --copy-calibration      (a 1 GiB device-to-device copy, for the counters)
 """
 from __future__ import annotations
@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--no-side-figures", action="store_true",
+                   help="skip the row-scaled, grouped and linear-layer figures (for counter runs)")
     return p.parse_args()
 
 
@@ -339,9 +341,11 @@ def main():
     g_dgrad = step.avg_ms("g_dgrad")
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
-    side = rowscaled_figures(step, max(3, args.steps // 2))
-    moe = grouped_figures(step, max(3, args.steps // 2))
-    layer = linear_layer_figures(step, max(3, args.steps // 2))
+    side = moe = layer = None
+    if not args.no_side_figures:
+        side = rowscaled_figures(step, max(3, args.steps // 2))
+        moe = grouped_figures(step, max(3, args.steps // 2))
+        layer = linear_layer_figures(step, max(3, args.steps // 2))
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
     tr = measured_traffic()
     # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
