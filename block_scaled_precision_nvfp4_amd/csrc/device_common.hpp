@@ -68,6 +68,20 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     return e4m3_encode_nonneg(__builtin_fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
 }
 
+// Four values -> four E4M3 codes (nearest-even, saturating at 448, sign kept), value i in
+// byte i.  The hardware conversion v_cvt_pk_fp8_f32 rounds to nearest-even but returns NaN
+// above 464 instead of saturating, so each value is first clamped to [-448, 448] (one
+// v_med3).  Checked on MI355X against e4m3_encode on 1.6 million values (every code, every
+// midpoint and its neighbours, the subnormal range, +-0, values up to 3e38): identical codes.
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3) {
+    const float lo = -448.0f, hi = 448.0f;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v0, lo, hi), __builtin_amdgcn_fmed3f(v1, lo, hi),
+                                            0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v2, lo, hi), __builtin_amdgcn_fmed3f(v3, lo, hi), w,
+                                        true);
+    return (uint32_t)w;
+}
+
 // Non-negative E4M3 code (<= 0x7E) -> float.
 __device__ __forceinline__ float e4m3_decode_nonneg(uint32_t c) {
     if (c < 8u) return (float)c * 0x1p-9f;

@@ -358,6 +358,13 @@ __device__ __forceinline__ uint32_t nvfp4_dequant_bf16(uint32_t c, float sc, flo
 // Sub-tile of the bf16 tensor bf16(dequant(NVFP4 rowwise)) -- the same values the dequantize
 // kernel writes -- computed from the codes and scales: row j of the thread's 16 x 8 sub-tile
 // is code word c0/8 of the row and scale byte c0/16.
+//
+// The seven nonzero E2M1 magnitudes are 0.5 * 2^k (k = 0..3) and 1.5 * 2^k (k = 0..2), so per
+// row two quotients suffice: with qa = fl32(0.5 sc / S) and qb = fl32(1.5 sc / S) both normal
+// and far enough from overflow (exponent field 1..250), fl32(2^k x) = 2^k fl32(x) and
+// bf16(2^k q) = 2^k bf16(q), so the bf16 result of magnitude m is bf16(qa or qb) with k added
+// to its exponent field -- bit-identical to rounding each product separately.  Rows outside
+// that range (zero or tiny scales, extreme tensor scales) take the per-element path.
 __device__ __forceinline__ void load_subtile_nvfp4(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scales, float S, int64_t R,
                                                    int64_t C, const TileCoord& t, SubTile q) {
@@ -371,11 +378,26 @@ __device__ __forceinline__ void load_subtile_nvfp4(const uint8_t* __restrict__ c
             sbyte = scales[r * (C / 16) + t.c0 / 16];
         }
         const float sc = e4m3_decode_nonneg(sbyte & 0x7Fu);
+        const float qa = (0.5f * sc) / S, qb = (1.5f * sc) / S;
+        const uint32_t ea = __float_as_uint(qa) >> 23, eb = __float_as_uint(qb) >> 23;
+        if (ea - 1u < 250u && eb - 1u < 250u) {
+            const uint32_t ba = f32_to_bf16_rne(qa), bb = f32_to_bf16_rne(qb);
+            auto deq = [&](uint32_t c) {
+                const uint32_t m = c & 7u;
+                const uint32_t k = (0x23120100u >> (4u * m)) & 0xFu;       // exponent step of magnitude m
+                const uint32_t base = ((0xA8u >> m) & 1u) ? bb : ba;       // m = 3, 5, 7: the 1.5 family
+                const uint32_t mag = m ? base + (k << 7) : 0u;
+                return mag | ((c & 8u) << 12);
+            };
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = nvfp4_dequant_bf16((cw >> (8 * w)) & 0xFu, sc, S);
-            const uint32_t hi = nvfp4_dequant_bf16((cw >> (8 * w + 4)) & 0xFu, sc, S);
-            q[j][w] = lo | (hi << 16);
+            for (int w = 0; w < 4; ++w) q[j][w] = deq((cw >> (8 * w)) & 0xFu) | (deq((cw >> (8 * w + 4)) & 0xFu) << 16);
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t lo = nvfp4_dequant_bf16((cw >> (8 * w)) & 0xFu, sc, S);
+                const uint32_t hi = nvfp4_dequant_bf16((cw >> (8 * w + 4)) & 0xFu, sc, S);
+                q[j][w] = lo | (hi << 16);
+            }
         }
     }
 }
@@ -417,10 +439,8 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
             if (m != 0.0f) {
                 sb = mx_scale_byte(m);
                 const float inv = mx_inv_scale(sb);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) lo |= e4m3_encode(v[k] * inv) << (8 * k);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) hi |= e4m3_encode(v[4 + k] * inv) << (8 * k);
+                lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+                hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
             }
             if (colok && r < R) {
                 *(uint2*)(a.row_codes + r * C + t.c0) = make_uint2(lo, hi);
@@ -446,7 +466,8 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
                 sb = mx_scale_byte(m);
                 const float inv = mx_inv_scale(sb);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) w[j >> 2] |= e4m3_encode(v[j] * inv) << (8 * (j & 3));
+                for (int q = 0; q < 4; ++q)
+                    w[q] = e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
             }
             lds_codes[8 * t.cc + k][t.rb] = make_uint4(w[0], w[1], w[2], w[3]);
             if (!upper) lds_sc[8 * t.cc + k][t.rb >> 1] = (uint8_t)sb;
@@ -815,10 +836,8 @@ __global__ __launch_bounds__(LIN_THREADS) void mxfp8_row_linear_kernel(const uin
             if (m != 0.0f) {
                 sb = mx_scale_byte(m);
                 const float inv = mx_inv_scale(sb);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) lo |= e4m3_encode(v[e] * inv) << (8 * e);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hi |= e4m3_encode(v[4 + e] * inv) << (8 * e);
+                lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+                hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
             }
             if (u < n16) {
                 codes[u] = make_uint2(lo, hi);

@@ -187,6 +187,26 @@ def test_fused_requantize_matches_chain(shape, direction):
             assert torch.equal(f[key + part], m[key + part]), "fused vs two-call chain " + key + part
 
 
+@pytest.mark.parametrize("factor", [1e-34, 1e-25, 1e30, 5e35])
+def test_fused_requantize_extreme_tensor_scales(factor):
+    """Inputs scaled so that the per-block quotients leave the normal range (tiny tensor amax
+    with small block scales) or approach overflow (huge amax): the fused kernel's two-quotient
+    shortcut must hand those rows to its per-element path and stay bit-identical."""
+    import oracle
+    X = (outlier_bf16((256, 512), seed=91, mask_seed=92).float() * factor).to(torch.bfloat16)
+    assert torch.isfinite(X.float()).all()
+    note("fused requantize extreme factor=%g" % factor)
+    q = bsq.nvfp4_quantize(X.to(DEV), direction=1)
+    f = bsq.mxfp8_requantize_nvfp4(q["row_codes"], q["row_scales"], q["s_enc"][0:1], direction=3)
+    torch.cuda.synchronize()
+    rq = oracle.nvfp4_quantize(X, direction=1)
+    rd = oracle.nvfp4_dequantize(rq["row_codes"], rq["row_scales"], float(rq["s_enc"][0]))
+    rm = oracle.mxfp8_quantize(rd, direction=3)
+    for key in ("row", "col"):
+        for part in ("_codes", "_scales"):
+            assert_bytes_equal(f[key + part], rm[key + part], "fused vs oracle " + key + part)
+
+
 def test_hybrid_rowwise_dequantized_source():
     """columnwise_source = rowwise_dequantized: MXFP8 columnwise of bf16(dequant(NVFP4 rowwise X));
     compared bit for bit with the oracle's chain on a [4096, 1024] slice of the workload."""
