@@ -166,6 +166,50 @@ class Step:
         return sum(x.elapsed_time(y) for x, y in zip(a, b)) / len(a)
 
 
+def measured_peaks(dev):
+    """The rates this GPU sustains, beside the published peaks: a 512 MiB device-to-device copy
+    (read + write bytes over time) and register-only MFMA loops (libbsq_peak.so) for the f16
+    32x32x16 and the FP8 scaled 32x32x64 instructions, at one and two waves per SIMD."""
+    import ctypes
+    import torch
+    import block_scaled_precision_nvfp4_amd as bsq
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    path = os.path.join(os.path.dirname(bsq.LIB_PATH), "libbsq_peak.so")
+    L = ctypes.CDLL(path)
+    L.bsq_peak_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.bsq_peak_mfma_loop.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    out = {"copy_GBps": round(copy_gbps, 1)}
+    for kind, name, flop in ((0, "mfma_f16_32x32x16_TFLOPs", 2.0 * 32 * 32 * 16),
+                             (1, "mfma_fp8_32x32x64_TFLOPs", 2.0 * 32 * 32 * 64)):
+        best = 0.0
+        for wgs in (256 * 4, 256 * 8):          # one and two waves per SIMD
+            iters = 4096 if kind == 0 else 2048
+            sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+            assert L.bsq_peak_mfma_loop(kind, wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)) == 0
+            torch.cuda.synchronize()
+            e0.record()
+            assert L.bsq_peak_mfma_loop(kind, wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            flops = wgs * 4 * iters * 8 * flop
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[name] = round(best, 1)
+    return out
+
+
 def rowscaled_figures(step, iters: int):
     """Side figures outside the step: row-scaled NVFP4 (one outer scale per row) of X and the
     forward GEMM with row-scaled X, each timed over ``iters`` back-to-back launches."""
@@ -341,6 +385,7 @@ def main():
     g_dgrad = step.avg_ms("g_dgrad")
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
+    peaks = measured_peaks(dev)
     side = moe = layer = None
     if not args.no_side_figures:
         side = rowscaled_figures(step, max(3, args.steps // 2))
@@ -352,6 +397,8 @@ def main():
     algo_bytes = (M_TOK + N_OUT) * K_IN * (0.5 + 1.0 / 16) + 2.0 * M_TOK * N_OUT
     roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(fwd_tflops / F16_MFMA_PEAK_TFLOPS, 4),
+                "measured_peak": peaks["mfma_f16_32x32x16_TFLOPs"],
+                "frac_of_measured": round(fwd_tflops / peaks["mfma_f16_32x32x16_TFLOPs"], 4),
                 "traffic": None if tr is None else tr["traffic_bytes"],
                 "algorithmic_bytes": int(algo_bytes),
                 "kernel": "gemm_nvfp4 (fwd, f16 MFMA with in-register dequant)"}
@@ -364,10 +411,15 @@ def main():
                    "tokens": M_TOK, "in_features": K_IN, "out_features": N_OUT,
                    "fwd": "NVFP4 row RNE", "wgrad": "NVFP4 col RHT16+SR", "dgrad": "MXFP8 (W from rowwise-dequantized)"},
         "nvfp4_quant_GBps": round(q_bytes / (q_fwd * 1e-3) / 1e9, 1),
+        "nvfp4_quant_frac": {"of_peak_8TBps": round(q_bytes / (q_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "of_measured_copy": round(q_bytes / (q_fwd * 1e-3) / 1e9 / peaks["copy_GBps"], 4)},
         "nvfp4_gemm_TFLOPs": round(fwd_tflops, 2),
         "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "gemm_fwd_nvfp4": round(g_fwd, 4),
                       "gemm_wgrad_nvfp4": round(g_wgrad, 4), "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
         "mxfp8_gemm_TFLOPs": round(gemm_flops / (g_dgrad * 1e-3) / 1e12, 2),
+        "mxfp8_gemm_frac": {"of_peak": round(gemm_flops / (g_dgrad * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                            "of_measured": round(gemm_flops / (g_dgrad * 1e-3) / 1e12 / peaks["mfma_fp8_32x32x64_TFLOPs"], 4)},
+        "measured_peaks": peaks,
         "row_scaled": side,
         "moe_grouped": moe,
         "nvfp4_linear_layer": layer,

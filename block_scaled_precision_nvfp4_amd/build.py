@@ -40,10 +40,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+PEAK_SOURCE = "peak.hip"
+PEAK_LIB = os.path.join(HERE, "libbsq_peak.so")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PEAK_SOURCE]))
+    peak_obj = objs.pop()
+    # the MFMA-rate measurement aid goes into its own library, apart from the product
+    tmp = PEAK_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, peak_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed: %s\n%s" % (r.stdout, r.stderr))
+    os.replace(tmp, PEAK_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
