@@ -300,7 +300,9 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     }
 
     if (DIRS & 2) {
-        // codes of column (8cc + k), row block rb -> lds_codes[8cc + k][rb]
+        // codes of column (8cc + k), row block rb -> lds_codes[8cc + k][rb ^ cc]: the XOR spreads
+        // the 16 column groups of a wave's writes over all banks (a column's 16 blocks stay in
+        // its own 128-byte row, so the read-back of a column is still one contiguous row)
         __shared__ uint2 lds_codes[TILE_C][TILE_R / 16];
         __shared__ uint8_t lds_sc[TILE_C][TILE_R / 16];
         static_for<0, 8>([&](auto k_c) {
@@ -315,8 +317,8 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             const uint64_t c = (uint64_t)(t.c0 + k);
             const uint32_t sb = encode_block<16, SR>(v, m, Scol, c * (uint64_t)R + (uint64_t)t.r0,
                                                      a.seed, a.stream, 1u, w);
-            lds_codes[8 * t.cc + k][t.rb] = make_uint2(w[0], w[1]);
-            lds_sc[8 * t.cc + k][t.rb] = (uint8_t)sb;
+            lds_codes[8 * t.cc + k][t.rb ^ t.cc] = make_uint2(w[0], w[1]);
+            lds_sc[8 * t.cc + k][t.rb ^ t.cc] = (uint8_t)sb;
         });
         __syncthreads();
         const int64_t tr0 = (int64_t)blockIdx.y * TILE_R;
@@ -327,8 +329,8 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             const int col = idx >> 4, rbk = idx & 15;
             const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
             if (c < C && r < R) {
-                *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk];
-                a.col_scales[c * (R / 16) + r / 16] = lds_sc[col][rbk];
+                *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk ^ (col >> 3)];
+                a.col_scales[c * (R / 16) + r / 16] = lds_sc[col][rbk ^ (col >> 3)];
             }
         }
     }
@@ -450,6 +452,8 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
     }
 
     if (DIRS & 2) {
+        // same placement as the NVFP4 columnwise transpose: block rb of column 8cc + k at
+        // [8cc + k][rb ^ cc] (scales at [8cc + k][(rb >> 1) ^ (cc & 7)])
         __shared__ uint4 lds_codes[TILE_C][TILE_R / 16];
         __shared__ uint8_t lds_sc[TILE_C][TILE_R / 32];
         const bool upper = (t.rb & 1) != 0;
@@ -469,8 +473,8 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
                 for (int q = 0; q < 4; ++q)
                     w[q] = e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
             }
-            lds_codes[8 * t.cc + k][t.rb] = make_uint4(w[0], w[1], w[2], w[3]);
-            if (!upper) lds_sc[8 * t.cc + k][t.rb >> 1] = (uint8_t)sb;
+            lds_codes[8 * t.cc + k][t.rb ^ t.cc] = make_uint4(w[0], w[1], w[2], w[3]);
+            if (!upper) lds_sc[8 * t.cc + k][(t.rb >> 1) ^ (t.cc & 7)] = (uint8_t)sb;
         });
         __syncthreads();
         const int64_t tr0 = (int64_t)blockIdx.y * TILE_R;
@@ -481,8 +485,8 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
             const int col = idx >> 4, rbk = idx & 15;
             const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
             if (c < C && r < R) {
-                *(uint4*)(a.col_codes + c * R + r) = lds_codes[col][rbk];
-                if ((rbk & 1) == 0) a.col_scales[c * (R / 32) + r / 32] = lds_sc[col][rbk >> 1];
+                *(uint4*)(a.col_codes + c * R + r) = lds_codes[col][rbk ^ (col >> 3)];
+                if ((rbk & 1) == 0) a.col_scales[c * (R / 32) + r / 32] = lds_sc[col][(rbk >> 1) ^ ((col >> 3) & 7)];
             }
         }
     }
