@@ -790,7 +790,15 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * IL + 8 * (r >> 2) + 4 * kh + (r & 3);
                     const float v = SCALED ? acc[I0 + IL][j][r] * (fav[r] * fbv[j]) : acc[I0 + IL][j][r];
-                    if constexpr (OUT_F32) *(float*)(reg + row * RS + (32 * j + frow) * 4) = v;
+                    if constexpr (OUT_F32) {
+                        // two 16-bit halves: written as one 32-bit store straight from the
+                        // accumulator registers, the fp32 path made the MXFP8 kernel's register
+                        // allocation spill hundreds of bytes per lane in its main loop
+                        const uint32_t b = __float_as_uint(v);
+                        uint8_t* p = reg + row * RS + (32 * j + frow) * 4;
+                        *(uint16_t*)p = (uint16_t)(b & 0xFFFFu);
+                        *(uint16_t*)(p + 2) = (uint16_t)(b >> 16);
+                    }
                     else *(__bf16*)(reg + row * RS + (32 * j + frow) * 2) = (__bf16)v;
                 }
             }
@@ -1108,7 +1116,12 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
             const int64_t row = m0 + lrow;
             if (row < g.M && col < g.N) {
                 const float v = F::NV ? acc[i][j][r] * (fa[lrow] * fbj) : acc[i][j][r];
-                if (OUT_F32) ((float*)g.c)[row * g.N + col] = v;
+                if (OUT_F32) {   // as two halves, for the reason given in store_tile_lds
+                    const uint32_t b = __float_as_uint(v);
+                    uint16_t* p = (uint16_t*)((float*)g.c + row * g.N + col);
+                    p[0] = (uint16_t)(b & 0xFFFFu);
+                    p[1] = (uint16_t)(b >> 16);
+                }
                 else ((uint16_t*)g.c)[row * g.N + col] = (uint16_t)f32_to_bf16_rne(v);
             }
         }
