@@ -260,6 +260,51 @@ def linear_layer_figures(step, iters: int):
             "saved_activation_bytes": int(saved.numel()), "bf16_activation_bytes": 2 * M_TOK * K_IN}
 
 
+QWEN_TOK, QWEN_N, QWEN_K = 65536, 12288, 4096
+
+
+def qwen3_8b_hybrid_figures(dev, iters: int):
+    """Side figure outside the step: the per-direction (hybrid) recipe at the Qwen3-8B FFN shape,
+    X [65536, 4096], W [12288, 4096], dY [65536, 12288] -- forward NVFP4 rowwise GEMM; MXFP8
+    rowwise dY, MXFP8 columnwise dY and X from the bf16 originals and W from its rowwise-
+    dequantized NVFP4 value; dgrad dX = dY W (bf16) and wgrad dW = dY^T X (fp32) on MXFP8.
+    Inputs are drawn on the device (seeded generator, same distributions as the step's)."""
+    import torch
+    import block_scaled_precision_nvfp4_amd as bsq
+    gen = torch.Generator(device=dev)
+    def randn(shape, std, seed):
+        gen.manual_seed(seed)
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+    X = randn((QWEN_TOK, QWEN_K), 1.0, 2234)
+    W = randn((QWEN_N, QWEN_K), 0.02, 2235)
+    dY = randn((QWEN_TOK, QWEN_N), 1e-4, 2236)
+    def run():
+        qx = bsq.nvfp4_quantize(X, direction=bsq.ROW)
+        qw = bsq.nvfp4_quantize(W, direction=bsq.ROW)
+        y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qx["row_codes"], qx["row_scales"], qx["s_enc"][0:1],
+                                 qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1])
+        mdy = bsq.mxfp8_quantize(dY, direction=bsq.ROW | bsq.COL)
+        mx = bsq.mxfp8_quantize(X, direction=bsq.COL)
+        mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL)
+        dx = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["row_codes"], mdy["row_scales"], None, mw["col_codes"],
+                                  mw["col_scales"], None)
+        dw = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["col_codes"], mdy["col_scales"], None, mx["col_codes"],
+                                  mx["col_scales"], None, out_dtype=torch.float32)
+        return y, dx, dw
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = 3 * 2.0 * QWEN_TOK * QWEN_N * QWEN_K
+    return {"shape": "X[%d,%d] W[%d,%d]" % (QWEN_TOK, QWEN_K, QWEN_N, QWEN_K), "ms_per_step": round(ms, 3),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+
 MOE_EXPERTS = 8
 
 
@@ -386,11 +431,12 @@ def main():
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
     peaks = measured_peaks(dev)
-    side = moe = layer = None
+    side = moe = layer = qwen = None
     if not args.no_side_figures:
         side = rowscaled_figures(step, max(3, args.steps // 2))
         moe = grouped_figures(step, max(3, args.steps // 2))
         layer = linear_layer_figures(step, max(3, args.steps // 2))
+        qwen = qwen3_8b_hybrid_figures(dev, 3)
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
     tr = measured_traffic()
     # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
@@ -423,6 +469,7 @@ def main():
         "row_scaled": side,
         "moe_grouped": moe,
         "nvfp4_linear_layer": layer,
+        "qwen3_8b_hybrid": qwen,
         "roofline": roofline,
         "cpu_baseline": None,
     }
