@@ -32,6 +32,10 @@ int ok() {
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Largest K of a GEMM: a 256-row operand tile (codes) must stay below 2^31 bytes, the range of
+// one buffer resource: 8 Mi elements for MXFP8 (1 byte each), 16 Mi for NVFP4.
+int64_t gemm_max_k(int fmt) { return fmt == BSQ_FMT_MXFP8 ? (int64_t)1 << 23 : (int64_t)1 << 24; }
+
 int launched(int hip_code, const char* what) {
     if (hip_code != 0)
         return fail(BSQ_ERR_HIP, "%s: kernel launch failed: %s", what, bsq::hip_error_string(hip_code));
@@ -160,6 +164,7 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
     if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
     if (M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
     if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (K > gemm_max_k(fmt)) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) exceeds %lld", fn, (long long)K, (long long)gemm_max_k(fmt));
     if (M == 0 || N == 0) return ok();
     if (!c) return fail(BSQ_ERR_NULL, "%s: c is NULL", fn);
     if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return fail(BSQ_ERR_NULL, "%s: operand pointer is NULL", fn);
@@ -185,6 +190,7 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
     if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
     if (groups < 0 || M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative size", fn);
     if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (K > gemm_max_k(fmt)) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) exceeds %lld", fn, (long long)K, (long long)gemm_max_k(fmt));
     if (groups == 0 || M == 0 || N == 0) return ok();
     if (groups > (int64_t)1 << 24) return fail(BSQ_ERR_SHAPE, "%s: too many groups (%lld)", fn, (long long)groups);
     if (bsq::grouped_gemm_workgroups(mode, groups, M, N) > 0x7FFFFFFF) return fail(BSQ_ERR_SHAPE, "%s: problem too large for one launch", fn);

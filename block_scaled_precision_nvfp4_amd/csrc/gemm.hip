@@ -114,6 +114,11 @@ struct Operands {
 constexpr int RSRC_FLAGS = 0x00020000;   // raw 32-bit data, no format conversion
 constexpr uint32_t OOB = 0x80000000u;    // an offset beyond every resource's range
 
+// Rows of an operand that a tile's resource covers: the tile's own rows that exist.  (Covering
+// only the tile keeps the byte range far below the resource's 2^31 limit for any K the C ABI
+// accepts, and rows past M or N still read as zero.)
+__device__ __forceinline__ int64_t tile_rows(int64_t left, int64_t tile) { return left < tile ? left : tile; }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, RSRC_FLAGS);
@@ -124,10 +129,11 @@ __device__ __forceinline__ Operands make_operands(const GemmArgs& g, int64_t m0,
     using F = Fmt<FMT>;
     const int64_t rowbytes = g.ld / F::EPB, sstride = g.ld / F::BLK;
     Operands o;
-    o.a = make_rsrc(g.a_codes + m0 * rowbytes, (g.M - m0) * rowbytes);
-    o.b = make_rsrc(g.b_codes + n0 * rowbytes, (g.N - n0) * rowbytes);
-    o.as = make_rsrc(g.a_scales + m0 * sstride, (g.M - m0) * sstride);
-    o.bs = make_rsrc(g.b_scales + n0 * sstride, (g.N - n0) * sstride);
+    const int64_t ra = tile_rows(g.M - m0, GBM), rb = tile_rows(g.N - n0, GBN);
+    o.a = make_rsrc(g.a_codes + m0 * rowbytes, ra * rowbytes);
+    o.b = make_rsrc(g.b_codes + n0 * rowbytes, rb * rowbytes);
+    o.as = make_rsrc(g.a_scales + m0 * sstride, ra * sstride);
+    o.bs = make_rsrc(g.b_scales + n0 * sstride, rb * sstride);
     return o;
 }
 
@@ -426,10 +432,11 @@ template <int EPB, int BLK>
 __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
     MxDma d;
     const int64_t rb = g.ld / EPB, sb = g.ld / BLK;
-    d.o.a = rsrc_words(g.a_codes + m0 * rb, (g.M - m0) * rb);
-    d.o.b = rsrc_words(g.b_codes + n0 * rb, (g.N - n0) * rb);
-    d.o.as = rsrc_words(g.a_scales + m0 * sb, (g.M - m0) * sb);
-    d.o.bs = rsrc_words(g.b_scales + n0 * sb, (g.N - n0) * sb);
+    const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, GBN);
+    d.o.a = rsrc_words(g.a_codes + m0 * rb, ra * rb);
+    d.o.b = rsrc_words(g.b_codes + n0 * rb, rbn * rb);
+    d.o.as = rsrc_words(g.a_scales + m0 * sb, ra * sb);
+    d.o.bs = rsrc_words(g.b_scales + n0 * sb, rbn * sb);
     d.rowbytes = (uint32_t)rb;
     d.sstride = (uint32_t)sb;
     d.kbytes = (uint32_t)(g.K / EPB);

@@ -115,6 +115,8 @@ def test_gemm_validation(L):
     assert f(0, 128, 128, 128, *args, 2, None) == 3 and "c_dtype" in last(L)
     assert f(0, 128, 128, 48, *args, 0, None) == 2 and "multiple of 32" in last(L)
     assert f(0, -1, 128, 64, *args, 0, None) == 2
+    assert f(1, 128, 128, (1 << 23) + 32, *args, 0, None) == 2 and "exceeds" in last(L)
+    assert f(0, 128, 128, (1 << 24) + 32, *args, 0, None) == 2 and "exceeds" in last(L)
     assert f(0, 128, 128, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 1 and "tensor scales" in last(L)
     assert f(0, 128, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
     assert f(0, 128, 128, 64, FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 6
