@@ -32,6 +32,9 @@
 // NVFP4, dequantized) while the current step's MFMAs issue.  Workgroups are renumbered so
 // that each of the 8 XCDs (which take workgroups round-robin) works on a contiguous band of
 // output tiles and reuses operand rows from its own L2.
+#include <mutex>
+#include <set>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -1139,12 +1142,20 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
 template <int FMT, int OUT, int GM>
 static int launch_one(const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipStream_t s) {
     using F = Fmt<FMT>;
-    static bool configured = false;   // raising the dynamic-LDS limit is a per-process, per-kernel setting
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<FMT, OUT, GM>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS);
-        if (e != hipSuccess) return (int)e;
-        configured = true;
+    // raising the dynamic-LDS limit is a per-kernel setting; made once per device, under a lock
+    static std::mutex mu;
+    static std::set<int> configured;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!configured.count(dev)) {
+            e = hipFuncSetAttribute((const void*)gemm_kernel<FMT, OUT, GM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    F::LDS);
+            if (e != hipSuccess) return (int)e;
+            configured.insert(dev);
+        }
     }
     if (tiles <= 0) return 0;
     hipLaunchKernelGGL((gemm_kernel<FMT, OUT, GM>), dim3((unsigned)tiles), dim3(F::THREADS), F::LDS, s, g, q);
