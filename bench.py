@@ -210,6 +210,42 @@ def measured_peaks(dev):
     return out
 
 
+def quant_only_figures(dev, peaks, iters: int = 10):
+    """Side figure outside the step: the quantize-only workload, [8192, 4096] N(0,1) bf16 with 1 %
+    of entries x100, each cast timed alone over ``iters`` launches that rotate over 4 copies of
+    the input (so no launch reads what the previous one just read).  GB/s are algorithmic: the
+    input read once plus the outputs written."""
+    import torch
+    import block_scaled_precision_nvfp4_amd as bsq
+    from synthetic import outlier_bf16
+    R, C = 8192, 4096
+    base = outlier_bf16((R, C)).to(dev)
+    xs = [base.clone() for _ in range(4)]
+    n = R * C
+    cases = {
+        "nvfp4_row_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.ROW), 2.0 + 0.5625),
+        "nvfp4_col_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.COL), 2.0 + 0.5625),
+        "nvfp4_row_col_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.ROW | bsq.COL), 2.0 + 2 * 0.5625),
+        "mxfp8_row": (lambda x: bsq.mxfp8_quantize(x, direction=bsq.ROW), 2.0 + 1.03125),
+        "mxfp8_col": (lambda x: bsq.mxfp8_quantize(x, direction=bsq.COL), 2.0 + 1.03125),
+    }
+    out = {"shape": [R, C]}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, (fn, bpe) in cases.items():
+        fn(xs[0])
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(iters):
+            fn(xs[i % 4])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        gbps = bpe * n / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "GBps": round(gbps, 1), "of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+                     "of_measured_copy": round(gbps / peaks["copy_GBps"], 4)}
+    return out
+
+
 def rowscaled_figures(step, iters: int):
     """Side figures outside the step: row-scaled NVFP4 (one outer scale per row) of X and the
     forward GEMM with row-scaled X, each timed over ``iters`` back-to-back launches."""
@@ -431,8 +467,9 @@ def main():
     q_fwd = step.avg_ms("q_fwd")
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
     peaks = measured_peaks(dev)
-    side = moe = layer = qwen = None
+    side = moe = layer = qwen = quant_only = None
     if not args.no_side_figures:
+        quant_only = quant_only_figures(dev, peaks)
         side = rowscaled_figures(step, max(3, args.steps // 2))
         moe = grouped_figures(step, max(3, args.steps // 2))
         layer = linear_layer_figures(step, max(3, args.steps // 2))
@@ -466,6 +503,7 @@ def main():
         "mxfp8_gemm_frac": {"of_peak": round(gemm_flops / (g_dgrad * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
                             "of_measured": round(gemm_flops / (g_dgrad * 1e-3) / 1e12 / peaks["mfma_fp8_32x32x64_TFLOPs"], 4)},
         "measured_peaks": peaks,
+        "quant_only": quant_only,
         "row_scaled": side,
         "moe_grouped": moe,
         "nvfp4_linear_layer": layer,
