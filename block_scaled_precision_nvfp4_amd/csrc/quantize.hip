@@ -708,15 +708,15 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
 // NVFP4 quantization converter").  A group of T = 2^lgt threads (2 <= T <= 256) owns a row:
 // thread `sub` of the group holds the 16-byte units sub + T*k (k < RS_UNITS) of each chunk
 // of T * RS_UNITS units, so adjacent lanes read adjacent units and the two halves of a
-// 16-block sit on a lane pair.  A row of at most one chunk (cols <= 16384 at T = 256) is
+// 16-block sit on a lane pair.  A row of at most one chunk (cols <= 8192 at T = 256) is
 // read once and kept in registers (as bf16; the transform is recomputed) between its amax
 // reduction and its encode; a longer row is
 // walked twice, the second walk re-reading it (normal loads, so the first walk leaves it
 // in L2).  The SR index of an element is its linear index, as in the per-tensor rowwise
 // quantization.
-constexpr int RS_UNITS = 8;
+constexpr int RS_UNITS = 4;
 constexpr int RS_THREADS = 256;
-constexpr int RS_MAX_BLOCKS = 256 * 8;
+constexpr int RS_MAX_BLOCKS = 256 * 32;
 
 template <bool RHT, bool SR>
 __global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4* __restrict__ x, int64_t R,
@@ -794,6 +794,10 @@ __global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4
             amax_rows[r] = m;
             s_enc_rows[r] = S;
         }
+        // the empty asm makes the units opaque, so the encode recomputes each unit's values from
+        // its 4 registers instead of the compiler keeping the amax pass's 8 floats per unit alive
+#pragma unroll
+        for (int k = 0; k < RS_UNITS; ++k) asm volatile("" : "+v"(q[k].x), "+v"(q[k].y), "+v"(q[k].z), "+v"(q[k].w));
         for (int64_t c0 = 0; c0 < upr; c0 += chunk) {
             if (!one) load_chunk(c0, std::false_type{});
 #pragma unroll

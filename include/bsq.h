@@ -135,7 +135,7 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
  *   codes      [rows][cols/2] uint8, scales [rows][cols/16] E4M3 (device), laid out as the
  *              rowwise outputs of nvfp4_quantize.
  *   amax_rows  float[rows] (device): A_r.  s_enc_rows float[rows] (device): S_r.
- * A row is read from memory once when cols <= 16384 and twice otherwise.  The call uses no
+ * A row is read from memory once when cols <= 8192 and twice otherwise.  The call uses no
  * memory beyond its arguments.
  */
 int nvfp4_quantize_rowscaled(const void* x, int64_t rows, int64_t cols, int rounding,

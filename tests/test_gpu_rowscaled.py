@@ -3,11 +3,11 @@ the C ABI: bit-exact codes, scales, per-row amax and per-row tensor scales; and 
 with per-row tensor scales on either or both operands, to the GEMM bar (relative Frobenius
 error <= 2e-3 against the oracle output rounded as the GPU stores it).
 
-The quantizer splits a row over 2..256 threads depending on its length, so the shapes
-cover every split: cols 16 and 64 (2 threads), 400 (8), 4096 (64, one wave), 8192 (128,
-two waves), 14336 (256, 7 units per thread) and rows longer than one register-resident
-chunk (cols > 16384, read twice); row counts that leave a partial workgroup, and enough
-rows that the grid-stride loop runs more than once.  The GEMM cases cover full 256 x 256
+The quantizer splits a row over 2..256 threads depending on its length (at most four
+16-byte units per thread and chunk), so the shapes cover every split: cols 16 and 64 (2
+threads), 400 (16), 4096 (128, two waves), 8192 (256, one register-resident chunk) and
+rows longer than one chunk (cols 14336, 16400, 40000: read twice); row counts that leave
+a partial workgroup, and enough rows that the grid-stride loop runs more than once.  The GEMM cases cover full 256 x 256
 tiles (staged epilogue), ragged edge tiles and K not a multiple of 256 (the register-staged
 NVFP4 kernel)."""
 import numpy as np
@@ -57,10 +57,25 @@ def test_rowscaled_rht_or_sr_alone(rounding, use_rht):
 
 
 def test_rowscaled_grid_stride():
-    """More row groups than the grid holds: 2 threads per row (300000 rows) and 256 threads
-    per row (2100 rows), so every workgroup walks several row groups."""
-    check_rowscaled(gaussian_bf16((300000, 16), 1.0, 63), label="stride-T2")
-    check_rowscaled(gaussian_bf16((2100, 14336), 1.0, 64), label="stride-T256")
+    """More row groups than the grid holds (8192 workgroups): 2 threads per row
+    (1100000 rows of 16) and 256 threads per row (8300 rows of 14336), so workgroups walk
+    several row groups.  Rows are quantized independently under RNE, so the oracle runs on
+    sampled rows -- the last ones (reached only on a second pass of the stride loop) and a
+    random spread."""
+    import oracle
+    for rows, cols, seed in ((1100000, 16, 63), (8300, 14336, 64)):
+        x = gaussian_bf16((rows, cols), 1.0, seed)
+        note("nvfp4 rowscaled stride shape=%s" % ((rows, cols),))
+        got = bsq.nvfp4_quantize_rowscaled(x.to(DEV))
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(seed)
+        pick = np.unique(np.concatenate([np.arange(rows - 40, rows), rng.choice(rows, 200, replace=False)]))
+        ref = oracle.nvfp4_quantize_rowscaled(x[torch.from_numpy(pick)].contiguous())
+        idx = torch.from_numpy(pick).to(DEV)
+        assert_f32_equal(got["amax"][idx], ref["amax"], "stride amax")
+        assert_f32_equal(got["s_enc"][idx], ref["s_enc"], "stride s_enc")
+        assert_bytes_equal(got["scales"][idx], ref["scales"], "stride scales")
+        assert_bytes_equal(got["codes"][idx], ref["codes"], "stride codes")
 
 
 def test_rowscaled_rows_of_very_different_magnitude():
