@@ -50,6 +50,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Two binary32 values -> packed bf16 (lo = a, hi = b), round to nearest even: the hardware
+// conversion v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    const bf16x2_t p = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
 // ---------------------------------------------------------------- E4M3 (OCP "fn")
 // Non-negative t -> E4M3 code, nearest-even, saturating at 448 (code 0x7E).
 // Subnormal range [0, 2^-6): code = rint(t * 2^9) (0..8; 8 is the first normal).

@@ -644,13 +644,18 @@ __device__ __forceinline__ void nvw_ops(const NvWordsT<TN>& w, const uint32_t (&
     for (int j = 0; j < TN; ++j) o.b[j] = nv_dequant(w.b[j], nv_scale(sb[j], S >> 1));
 }
 
+// The B fragment is the MFMA's first operand and the A fragment its second, so each 32 x 32
+// accumulator tile holds C^T: lane (frow, kh) has, in acc[i][j][r], row 32i + frow and column
+// 32j + 8(r >> 2) + 4kh + (r & 3) of the wave's block -- four consecutive columns of one row
+// per group of 4 registers, which the epilogue packs into one 8-byte (bf16) or 16-byte (fp32)
+// LDS store instead of transposing single elements.
 template <int TN>
 __device__ __forceinline__ void nvw_mfma(const NvOpsT<TN>& o, floatx16 (&acc)[4][TN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.b[j], o.a[i], acc[i][j], 0, 0, 0);
 }
 
 // One step (after its LDS reads, which a scheduling barrier keeps at the top of the step):
@@ -765,7 +770,10 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
 // 4-byte store per accumulator.  bf16 output takes all 128 rows in one pass (34 KiB per
 // wave); fp32 output two passes of 64 rows.  A wave reads back only what it wrote, and the LDS
 // executes one wave's instructions in order, so no barrier is needed between the two.
-template <bool OUT_F32, bool SCALED>
+// TR: the accumulators hold C^T tiles (see nvw_mfma), so each group of 4 registers is 4
+// consecutive columns of one row and goes to LDS as one 8- or 16-byte store; otherwise each
+// accumulator is one 2- or 4-byte store.
+template <bool OUT_F32, bool SCALED, bool TR>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, int64_t m0, int64_t n0, int wm,
                                                int wn, int wave, int lane, const float* fa, const float* fb,
                                                floatx16 (&acc)[4][4]) {
@@ -778,14 +786,35 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
     const int frow = lane & 31, kh = lane >> 5;
     uint8_t* cbase = (uint8_t*)g.c + ((m0 + wm) * g.N + n0 + wn) * ES;
     float fbv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (SCALED) {
+    if constexpr (SCALED && !TR) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) fbv[j] = fb[wn + 32 * j + frow];
     }
     static_for<0, 128 / ROWS>([&](auto h_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr int I0 = H * ROWS / 32;
-        static_for<0, ROWS / 32>([&](auto i_c) {
+        if constexpr (TR) static_for<0, ROWS / 32>([&](auto i_c) {
+            constexpr int IL = decltype(i_c)::value;
+            const int row = 32 * IL + frow;
+            const float fr = SCALED ? fa[wm + 32 * (I0 + IL) + frow] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = 32 * j + 8 * q + 4 * kh;
+                    float4 fc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                    if constexpr (SCALED) fc = *(const float4*)(fb + wn + col);
+                    float4 v = make_float4(acc[I0 + IL][j][4 * q], acc[I0 + IL][j][4 * q + 1],
+                                           acc[I0 + IL][j][4 * q + 2], acc[I0 + IL][j][4 * q + 3]);
+                    if constexpr (SCALED) {
+                        v.x *= fr * fc.x; v.y *= fr * fc.y; v.z *= fr * fc.z; v.w *= fr * fc.w;
+                    }
+                    if constexpr (OUT_F32) *(float4*)(reg + row * RS + col * 4) = v;
+                    else *(uint2*)(reg + row * RS + col * 2) = make_uint2(bf16x2_rne(v.x, v.y), bf16x2_rne(v.z, v.w));
+                }
+            }
+        });
+        else static_for<0, ROWS / 32>([&](auto i_c) {
             constexpr int IL = decltype(i_c)::value;
             float fav[16];
 #pragma unroll
@@ -1112,20 +1141,22 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         constexpr int ES = OUT_F32 ? 4 : 2;
         const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
         if (full) {
-            store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, acc);
+            store_tile_lds<OUT_F32, F::NV, FMT == 2>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, acc);
             return;
         }
     }
+    // FMT 2 accumulators hold C^T tiles (see nvw_mfma): swap the roles of frow and r
+    constexpr bool TR = FMT == 2;
     static_for<0, 4 * TN>([&](auto t_c) {
         constexpr int i = decltype(t_c)::value / TN, j = decltype(t_c)::value % TN;
-        const int64_t col = n0 + wn + 32 * j + frow;
-        const float fbj = F::NV ? fb[wn + 32 * j + frow] : 1.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int lrow = wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-            const int64_t row = m0 + lrow;
+            const int within = 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int lrow = wm + 32 * i + (TR ? frow : within);
+            const int lcol = wn + 32 * j + (TR ? within : frow);
+            const int64_t row = m0 + lrow, col = n0 + lcol;
             if (row < g.M && col < g.N) {
-                const float v = F::NV ? acc[i][j][r] * (fa[lrow] * fbj) : acc[i][j][r];
+                const float v = F::NV ? acc[i][j][r] * (fa[lrow] * fb[lcol]) : acc[i][j][r];
                 if (OUT_F32) {   // as two halves, for the reason given in store_tile_lds
                     const uint32_t b = __float_as_uint(v);
                     uint16_t* p = (uint16_t*)((float*)g.c + row * g.N + col);
