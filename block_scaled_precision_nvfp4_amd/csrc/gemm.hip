@@ -614,14 +614,35 @@ struct NvOpsT {
 
 // Step S (0..7) of a slice: lane (row, kh) holds the 8 codes of K elements 64kh + 8S .. +8,
 // dword S % 4 of chunk 2kh + S / 4 of its row (block 4kh + S / 2 of the slice).
+// Half H (0/1) of a slice: lane (row, kh) reads chunk 2kh + H of its row with one 16-byte LDS
+// read -- the code words of steps 4H .. 4H+3 (dword S % 4 for step S).
+template <int TN>
+struct NvQuadT {
+    uint4 a[4], b[TN];
+};
+
+template <int H, int TN>
+__device__ __forceinline__ void nvw_read_quad(const uint8_t* buf, int wm, int wn, int frow, int kh, NvQuadT<TN>& q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q.a[i] = *(const uint4*)(buf + swz(wm + 32 * i + frow, 2 * kh + H));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) q.b[j] = *(const uint4*)(buf + GBM * ROWB + swz(wn + 32 * j + frow, 2 * kh + H));
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t dword_of(const uint4& v) {
+    if constexpr (D == 0) return v.x;
+    else if constexpr (D == 1) return v.y;
+    else if constexpr (D == 2) return v.z;
+    else return v.w;
+}
+
 template <int S, int TN>
-__device__ __forceinline__ void nvw_read_words(const uint8_t* buf, int wm, int wn, int frow, int kh, NvWordsT<TN>& w) {
+__device__ __forceinline__ void nvw_words_of(const NvQuadT<TN>& q, NvWordsT<TN>& w) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        w.a[i] = *(const uint32_t*)(buf + swz(wm + 32 * i + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
+    for (int i = 0; i < 4; ++i) w.a[i] = dword_of<S & 3>(q.a[i]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-        w.b[j] = *(const uint32_t*)(buf + GBM * ROWB + swz(wn + 32 * j + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
+    for (int j = 0; j < TN; ++j) w.b[j] = dword_of<S & 3>(q.b[j]);
 }
 
 // The lane's 4 scale bytes (blocks 4kh .. 4kh+3) of slice q (0/1) of a group record.
@@ -710,13 +731,16 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
     mx_dma_group<NW>(d, 0, false, buf(3));
     wait_vm_barrier<2 * DC + DG>();
 
-    NvWordsT<TN> w1, w2;   // words of the next step and of the step after it
+    // q0: code words of steps 0-3 of the current slice (from step 6 on: of the next slice);
+    // q1: steps 4-7 of the current slice, read at step 2
+    NvQuadT<TN> q0, q1;
+    NvWordsT<TN> w;
     NvOpsT<TN> cur, nxt;
     uint32_t sa[4], sb[TN], san[4], sbn[TN];
     nvw_read_scales<TN>(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
-    nvw_read_words<0, TN>(buf(0), wm, wn, frow, kh, w1);
-    nvw_ops<0, TN>(w1, sa, sb, cur);
-    nvw_read_words<1, TN>(buf(0), wm, wn, frow, kh, w1);
+    nvw_read_quad<0, TN>(buf(0), wm, wn, frow, kh, q0);
+    nvw_words_of<0, TN>(q0, w);
+    nvw_ops<0, TN>(w, sa, sb, cur);
 
     auto slice = [&](int64_t kt, auto odd_c) {
         constexpr bool ODD = decltype(odd_c)::value;
@@ -734,19 +758,23 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
                 const int64_t grp = (kt + 3) / 2;
                 mx_dma_group<NW>(d, grp, 2 * grp < nk, sbuf(grp));
             }
-            // words of step S+2 (the reads after the last slice touch a stale, in-bounds buffer)
-            if constexpr (S + 2 < 8) nvw_read_words<S + 2, TN>(cb, wm, wn, frow, kh, w2);
-            else nvw_read_words<S + 2 - 8, TN>(nb, wm, wn, frow, kh, w2);
+            // second half of this slice at step 2 (q1 was last read at step 6 of the previous
+            // slice), first half of the next slice at step 6 (q0 was last read at step 2; the
+            // read after the last slice touches a stale, in-bounds buffer)
+            if constexpr (S == 2) nvw_read_quad<1, TN>(cb, wm, wn, frow, kh, q1);
+            if constexpr (S == 6) nvw_read_quad<0, TN>(nb, wm, wn, frow, kh, q0);
             if constexpr (S == 5) nvw_read_scales<TN>(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
             __builtin_amdgcn_sched_barrier(0);
             // dequantize step S+1
-            if constexpr (S + 1 < 8) nvw_ops<S + 1, TN>(w1, sa, sb, nxt);
-            else nvw_ops<0, TN>(w1, san, sbn, nxt);
+            if constexpr (S + 1 < 4) nvw_words_of<S + 1, TN>(q0, w);
+            else if constexpr (S + 1 < 8) nvw_words_of<S + 1, TN>(q1, w);
+            else nvw_words_of<0, TN>(q0, w);
+            if constexpr (S + 1 < 8) nvw_ops<S + 1, TN>(w, sa, sb, nxt);
+            else nvw_ops<0, TN>(w, san, sbn, nxt);
             nvw_mfma<TN>(cur, acc);
             nvw_interleave<TN>();
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
-            w1 = w2;
         });
 #pragma unroll
         for (int i = 0; i < 4; ++i) sa[i] = san[i];
