@@ -431,6 +431,35 @@ __device__ __forceinline__ void mx_dma_group(const MxDma& d, int64_t grp, bool l
     }
 }
 
+// The same DMAs for the NVFP4 kernel, whose K is a multiple of 256: a slice inside K never
+// reaches past K in any lane, so the one decision per slice is uniform -- a slice (or scale
+// group) past the end of K is issued with resources of zero size, which put every lane out of
+// range (no memory traffic; the zeros land in a free buffer).  The lane offsets are fixed for
+// the tile, and the whole per-slice selection is scalar work.
+__device__ __forceinline__ u32x4s sized(u32x4s rsrc, bool live) {
+    rsrc[2] = live ? rsrc[2] : 0u;
+    return rsrc;
+}
+
+template <int P, int NW>
+__device__ __forceinline__ void nv4_dma_codes(const MxDma& d, uint32_t b0, bool live, uint8_t* buf) {
+    const int r0 = 16 * NW * P + 16 * d.wave;
+    const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
+    const uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
+    const uint32_t soff = live ? b0 : 0u;
+    dma_b128(sized(d.o.a, live), lds_addr(buf + r0 * ROWB), off, soff);
+    dma_b128(sized(d.o.b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off, soff);
+}
+
+template <int NW>
+__device__ __forceinline__ void nv4_dma_group(const MxDma& d, uint32_t grp, bool live, uint8_t* sbuf) {
+    static_assert(NW == 4, "one lane per row of each operand");
+    const uint32_t soff = live ? 16u * grp : 0u;
+    const uint32_t off = (uint32_t)(64 * d.wave + d.lane) * d.sstride;
+    dma_b128(sized(d.o.as, live), lds_addr(sbuf + 64 * d.wave * 16), off, soff);
+    dma_b128(sized(d.o.bs, live), lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
+}
+
 template <int EPB, int BLK>
 __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
     MxDma d;
@@ -717,18 +746,19 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
     const int frow = lane & 31, kh = lane >> 5;
     auto buf = [&](int64_t k) { return lds + (int)(k & 3) * NV4_CODES; };
     auto sbuf = [&](int64_t grp) { return lds + 4 * NV4_CODES + (int)(grp & 1) * NV4_SREC; };
-    auto dma_slice = [&](int64_t k) {
-        const bool live = k < nk;
-        static_for<0, PARTS>([&](auto p_c) { mx_dma_codes<decltype(p_c)::value, NW>(d, k * 64, live, buf(k)); });
+    const int nk32 = (int)nk;   // nk <= 2^17 (K <= 2^24)
+    auto dma_slice = [&](int k) {
+        const bool live = k < nk32;
+        static_for<0, PARTS>([&](auto p_c) { nv4_dma_codes<decltype(p_c)::value, NW>(d, 64u * k, live, buf(k)); });
     };
-    mx_dma_group<NW>(d, 0, true, sbuf(0));
-    mx_dma_group<NW>(d, 1, 2 < nk, sbuf(1));
+    nv4_dma_group<NW>(d, 0, true, sbuf(0));
+    nv4_dma_group<NW>(d, 1, 2 < nk32, sbuf(1));
     dma_slice(0);
     dma_slice(1);
     dma_slice(2);
     // out of range: no memory traffic, but the DMA still writes its zeros -- into code stage 3,
     // which is free until slice 3's DMA (issued after it) refills it
-    mx_dma_group<NW>(d, 0, false, buf(3));
+    nv4_dma_group<NW>(d, 0, false, buf(3));
     wait_vm_barrier<2 * DC + DG>();
 
     // q0: code words of steps 0-3 of the current slice (from step 6 on: of the next slice);
@@ -742,21 +772,21 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
     nvw_words_of<0, TN>(q0, w);
     nvw_ops<0, TN>(w, sa, sb, cur);
 
-    auto slice = [&](int64_t kt, auto odd_c) {
+    auto slice = [&](int kt, auto odd_c) {
         constexpr bool ODD = decltype(odd_c)::value;
         if constexpr (ODD) wait_vm_barrier<DC>();
         else wait_vm_barrier<DC + DG>();
-        const int64_t kd = kt + 3;
-        const bool live = kd < nk;
+        const int kd = kt + 3;
+        const bool live = kd < nk32;
         uint8_t* db = buf(kd);
         const uint8_t* cb = buf(kt);
         const uint8_t* nb = buf(kt + 1);
         static_for<0, 8>([&](auto s_c) {
             constexpr int S = decltype(s_c)::value;
-            if constexpr (S % PSTEP == 0) mx_dma_codes<S / PSTEP, NW>(d, kd * 64, live, db);
+            if constexpr (S % PSTEP == 0) nv4_dma_codes<S / PSTEP, NW>(d, 64u * kd, live, db);
             if constexpr (ODD && S == 1) {
-                const int64_t grp = (kt + 3) / 2;
-                mx_dma_group<NW>(d, grp, 2 * grp < nk, sbuf(grp));
+                const int grp = (kt + 3) / 2;
+                nv4_dma_group<NW>(d, grp, 2 * grp < nk32, sbuf(grp));
             }
             // second half of this slice at step 2 (q1 was last read at step 6 of the previous
             // slice), first half of the next slice at step 6 (q0 was last read at step 2; the
@@ -782,7 +812,7 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
         for (int j = 0; j < TN; ++j) sb[j] = sbn[j];
     };
     // nk is even
-    for (int64_t kt = 0; kt < nk; kt += 2) {
+    for (int kt = 0; kt < nk32; kt += 2) {
         slice(kt, std::false_type{});
         slice(kt + 1, std::true_type{});
     }
