@@ -830,11 +830,13 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
 // executes one wave's instructions in order, so no barrier is needed between the two.
 // TR: the accumulators hold C^T tiles (see nvw_mfma), so each group of 4 registers is 4
 // consecutive columns of one row and goes to LDS as one 8- or 16-byte store; otherwise each
-// accumulator is one 2- or 4-byte store.
+// accumulator is one 2- or 4-byte store.  TR with fa == nullptr: every output is scaled by the
+// uniform alpha (per-tensor scales on both operands); otherwise the lane reads its row and
+// column factors from the tables once, before staging.
 template <bool OUT_F32, bool SCALED, bool TR>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, int64_t m0, int64_t n0, int wm,
                                                int wn, int wave, int lane, const float* fa, const float* fb,
-                                               floatx16 (&acc)[4][4]) {
+                                               float alpha, floatx16 (&acc)[4][4]) {
     constexpr int ES = OUT_F32 ? 4 : 2;          // bytes per element
     constexpr int ROWS = OUT_F32 ? 64 : 128;     // rows per pass
     constexpr int RS = 128 * ES + 16;            // LDS row stride
@@ -848,27 +850,46 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
 #pragma unroll
         for (int j = 0; j < 4; ++j) fbv[j] = fb[wn + 32 * j + frow];
     }
+    const bool tables = SCALED && fa != nullptr;   // uniform
+    float frv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    float4 fcv[4][4];
+    if constexpr (TR && SCALED) {
+        if (tables) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) frv[i] = fa[wm + 32 * i + frow];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) fcv[j][q] = *(const float4*)(fb + wn + 32 * j + 8 * q + 4 * kh);
+        }
+    }
     static_for<0, 128 / ROWS>([&](auto h_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr int I0 = H * ROWS / 32;
+        // one 4-column group of row `row` (within the pass), columns col..col+3 of the block
+        auto put = [&](int row, int col, float4 v) {
+            if constexpr (OUT_F32) *(float4*)(reg + row * RS + col * 4) = v;
+            else *(uint2*)(reg + row * RS + col * 2) = make_uint2(bf16x2_rne(v.x, v.y), bf16x2_rne(v.z, v.w));
+        };
         if constexpr (TR) static_for<0, ROWS / 32>([&](auto i_c) {
             constexpr int IL = decltype(i_c)::value;
-            const int row = 32 * IL + frow;
-            const float fr = SCALED ? fa[wm + 32 * (I0 + IL) + frow] : 1.0f;
+            constexpr int I = I0 + IL;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int col = 32 * j + 8 * q + 4 * kh;
-                    float4 fc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                    if constexpr (SCALED) fc = *(const float4*)(fb + wn + col);
-                    float4 v = make_float4(acc[I0 + IL][j][4 * q], acc[I0 + IL][j][4 * q + 1],
-                                           acc[I0 + IL][j][4 * q + 2], acc[I0 + IL][j][4 * q + 3]);
+                    float4 v = make_float4(acc[I][j][4 * q], acc[I][j][4 * q + 1], acc[I][j][4 * q + 2],
+                                           acc[I][j][4 * q + 3]);
                     if constexpr (SCALED) {
-                        v.x *= fr * fc.x; v.y *= fr * fc.y; v.z *= fr * fc.z; v.w *= fr * fc.w;
+                        if (tables) {
+                            const float fr = frv[I];
+                            const float4 fc = fcv[j][q];
+                            v.x *= fr * fc.x; v.y *= fr * fc.y; v.z *= fr * fc.z; v.w *= fr * fc.w;
+                        } else {
+                            v.x *= alpha; v.y *= alpha; v.z *= alpha; v.w *= alpha;
+                        }
                     }
-                    if constexpr (OUT_F32) *(float4*)(reg + row * RS + col * 4) = v;
-                    else *(uint2*)(reg + row * RS + col * 2) = make_uint2(bf16x2_rne(v.x, v.y), bf16x2_rne(v.z, v.w));
+                    put(32 * IL + frow, 32 * j + 8 * q + 4 * kh, v);
                 }
             }
         });
@@ -1112,6 +1133,17 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int64_t nk = (g.K + F::BK - 1) / F::BK;
+    // Uniform output factor of the LDS-DMA NVFP4 kernel with per-tensor scales on both
+    // operands, alpha = fp32(1 / (S_a S_b)) with the product and quotient in binary64 (as in
+    // tile_factors); computed before the main loop so that the epilogue does not wait for the
+    // scale loads.
+    float alpha_pt = 1.0f;
+    if constexpr (FMT == 2) {
+        if (!g.a_rows && !g.b_rows) alpha_pt = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
+#if __HIP_DEVICE_COMPILE__
+        asm volatile("" : "+v"(alpha_pt));
+#endif
+    }
     const int frow = lane & 31, kh = lane >> 5;
     const Operands ops = make_operands<FMT>(g, m0, n0);
     if constexpr (FMT == 0) {
@@ -1183,6 +1215,7 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     } else {
         nvw_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
+    (void)alpha_pt;
 
     static_assert(FMT == 0 || (F::LDS - FACT_BYTES >= 4 * 128 * (128 * 2 + 16) &&
                                F::LDS - FACT_BYTES >= 4 * 64 * (128 * 4 + 16)),
@@ -1191,15 +1224,22 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     float* fa = (float*)(lds + F::LDS - FACT_BYTES);
     float* fb = fa + 256;
     __syncthreads();   // every wave is done with the operand buffers (and its DMAs)
+    constexpr int ES = OUT_F32 ? 4 : 2;
+    const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
+    if constexpr (FMT == 2) {
+        // per-tensor scales on both operands: one uniform factor, no tables
+        if (full && !g.a_rows && !g.b_rows) {
+            store_tile_lds<OUT_F32, true, true>(g, lds, m0, n0, wm, wn, wave, lane, nullptr, nullptr, alpha_pt, acc);
+            return;
+        }
+    }
     if constexpr (F::NV) {
         tile_factors<FMT>(g, m0, n0, fa, fb);
         __syncthreads();
     }
     if constexpr (FMT != 0) {
-        constexpr int ES = OUT_F32 ? 4 : 2;
-        const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
         if (full) {
-            store_tile_lds<OUT_F32, F::NV, FMT == 2>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, acc);
+            store_tile_lds<OUT_F32, F::NV, FMT == 2>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, acc);
             return;
         }
     }
