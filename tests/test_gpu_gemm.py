@@ -96,6 +96,19 @@ def test_nvfp4_ragged_full(M, N, K, out_dtype):
                   label="ragged")
 
 
+@pytest.mark.parametrize("fa,fb", [(2.0 ** -60, 2.0 ** 40), (2.0 ** 50, 2.0 ** -50), (3.0e-20, 7.0e15)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_nvfp4_full_tiles_extreme_tensor_scales(fa, fb, out_dtype):
+    """Full 256 x 256 tiles with K a multiple of 256 (the LDS-DMA kernel, whose per-tensor
+    epilogue multiplies by one alpha = 1 / (S_a S_b) computed per lane before the main loop)
+    with operands scaled far apart, so that S_a and S_b sit near the ends of the fp32 range
+    while their product does not."""
+    a = (gaussian_bf16((512, 512), 1.0, 93).float() * fa).to(torch.bfloat16)
+    b = (outlier_bf16((256, 512), seed=94, mask_seed=95).float() * fb).to(torch.bfloat16)
+    assert torch.isfinite(a.float()).all() and torch.isfinite(b.float()).all()
+    nv_gemm_check(a, b, out_dtype=out_dtype, label="extreme scales %g %g" % (fa, fb))
+
+
 # K = 96, 256, 1056: scales fetched per K slice; K = 512, 1536: grouped 16-block scale records
 @pytest.mark.parametrize("M,N,K", [(200, 72, 96), (256, 256, 256), (96, 160, 1056), (200, 72, 512), (300, 260, 1536)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
