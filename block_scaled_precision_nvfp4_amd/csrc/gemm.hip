@@ -412,30 +412,12 @@ __device__ __forceinline__ void mx_dma_slots(const MxDma& d, int64_t k0, bool li
     dma_u8(d.o.bs, lds_addr(buf + MX_CODES + 8 * GBM + 4 * s0), off, soff);
 }
 
-// Grouped scales: the 16-byte record grp (scale bytes 16grp..16grp+15) of every row of both
-// operands, one lane per row: with 4 waves lane l of wave w takes row 64w + l of A and of B,
-// with 8 waves waves 0-3 take the A rows and waves 4-7 the B rows.
-template <int NW = 4>
-__device__ __forceinline__ void mx_dma_group(const MxDma& d, int64_t grp, bool live, uint8_t* sbuf) {
-    const uint32_t soff = live ? (uint32_t)(16 * grp) : 0u;
-    if constexpr (NW == 4) {
-        const int r = 64 * d.wave + d.lane;
-        const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
-        dma_b128(d.o.as, lds_addr(sbuf + 64 * d.wave * 16), off, soff);
-        dma_b128(d.o.bs, lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
-    } else {
-        const int op = d.wave >> 2, w4 = d.wave & 3;
-        const int r = 64 * w4 + d.lane;
-        const uint32_t off = live ? (uint32_t)r * d.sstride : OOB;
-        dma_b128(op ? d.o.bs : d.o.as, lds_addr(sbuf + op * GBM * 16 + 64 * w4 * 16), off, soff);
-    }
-}
-
-// The same DMAs for the NVFP4 kernel, whose K is a multiple of 256: a slice inside K never
-// reaches past K in any lane, so the one decision per slice is uniform -- a slice (or scale
-// group) past the end of K is issued with resources of zero size, which put every lane out of
-// range (no memory traffic; the zeros land in a free buffer).  The lane offsets are fixed for
-// the tile, and the whole per-slice selection is scalar work.
+// The same DMAs where K is a multiple of the slice group (the NVFP4 kernel: K % 256 == 0; the
+// MXFP8 kernel with grouped scale records: K % 512 == 0): a slice inside K never reaches past
+// K in any lane, so the one decision per slice is uniform -- a slice (or scale group) past the
+// end of K is issued with resources of zero size, which put every lane out of range (no memory
+// traffic; the zeros land in a free buffer).  The lane offsets are fixed for the tile, and the
+// whole per-slice selection is scalar work.
 __device__ __forceinline__ u32x4s sized(u32x4s rsrc, bool live) {
     rsrc[2] = live ? rsrc[2] : 0u;
     return rsrc;
@@ -451,6 +433,8 @@ __device__ __forceinline__ void nv4_dma_codes(const MxDma& d, uint32_t b0, bool 
     dma_b128(sized(d.o.b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off, soff);
 }
 
+// Grouped scales: the 16-byte record grp (scale bytes 16grp..16grp+15) of every row of both
+// operands, one lane per row: lane l of wave w takes row 64w + l of A and of B.
 template <int NW>
 __device__ __forceinline__ void nv4_dma_group(const MxDma& d, uint32_t grp, bool live, uint8_t* sbuf) {
     static_assert(NW == 4, "one lane per row of each operand");
@@ -543,19 +527,23 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     const MxDma d = make_dma<1, 32>(g, m0, n0, lane);
     auto buf = [&](int64_t k) { return lds + (int)(k & 3) * STRIDE; };
     auto sbuf = [&](int64_t grp) { return lds + 4 * MX_CODES + (int)(grp & 1) * MX_SREC; };
+    const int nk32 = (int)nk;   // nk <= 2^17 (K <= 2^23)
+    // slice k's code DMAs, part P (K a multiple of 512 with grouped records: the scalar form)
+    auto dma_part = [&](auto p_c, int64_t k, bool live, uint8_t* b) {
+        constexpr int P = decltype(p_c)::value;
+        if constexpr (GROUPED) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
+        else mx_dma_codes<P>(d, k * 64, live, b);
+    };
     auto dma_slice = [&](int64_t k) {
-        const bool live = k < nk;
+        const bool live = (int)k < nk32;
         uint8_t* b = buf(k);
-        mx_dma_codes<0>(d, k * 64, live, b);
-        mx_dma_codes<1>(d, k * 64, live, b);
-        mx_dma_codes<2>(d, k * 64, live, b);
-        mx_dma_codes<3>(d, k * 64, live, b);
+        static_for<0, 4>([&](auto p_c) { dma_part(p_c, k, live, b); });
         if constexpr (!GROUPED) {
             mx_dma_slots<0>(d, k * 64, live, b);
             mx_dma_slots<1>(d, k * 64, live, b);
         }
     };
-    if constexpr (GROUPED) mx_dma_group(d, 0, true, sbuf(0));
+    if constexpr (GROUPED) nv4_dma_group<4>(d, 0, true, sbuf(0));
     dma_slice(0);
     dma_slice(1);
     dma_slice(2);
@@ -569,7 +557,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
         if constexpr (GROUPED && Q == 2) wait_vm_barrier<DC + DG>();   // slice kt-1 also issued a group
         else wait_vm_barrier<DC + DS>();
         const int64_t kd = kt + 3;
-        const bool live = kd < nk;
+        const bool live = (int)kd < nk32;
         uint8_t* db = buf(kd);
         const int64_t kn = kt + 1;                   // fragments read for the next slice
         const uint8_t* nb = buf(kn);
@@ -577,11 +565,11 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
         const int qn = GROUPED ? (Q + 1) % MX_GROUP : 0;
         static_for<0, 4>([&](auto p_c) {
             constexpr int P = decltype(p_c)::value;
-            mx_dma_codes<P>(d, kd * 64, live, db);
+            dma_part(p_c, kd, live, db);
             if constexpr (!GROUPED && P < 2) mx_dma_slots<P>(d, kd * 64, live, db);
             if constexpr (GROUPED && Q == 1 && P == 0) {
-                const int64_t grp = kt / MX_GROUP + 1;
-                mx_dma_group(d, grp, grp * MX_GROUP < nk, sbuf(grp));
+                const int grp = (int)(kt / MX_GROUP) + 1;
+                nv4_dma_group<4>(d, (uint32_t)grp, grp * MX_GROUP < nk32, sbuf(grp));
             }
             mx_mfma_row<P>(fc, acc);
             // the reads after the last slice touch a stale (in-bounds) buffer and go unused
