@@ -85,10 +85,13 @@ struct Fmt {
     static constexpr int WAVES_N = GBN / (32 * TN);
 };
 
-// Byte offset of 16-byte chunk c (0..3) of LDS code row r.  The XOR with bits 3..4 of the
-// row was the fastest placement measured for the fragment reads (32 consecutive rows, one
-// chunk per lane half): about 110 B/clk/CU against 90 for bits 1..2 and 55 unswizzled.
-__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 3) & 3)) << 4); }
+// Byte offset of 16-byte chunk c (0..3) of LDS code row r: the chunk index is XORed with bits
+// 3..4 of the row (the DMAs apply the same permutation on the global side, swz_chunk).  For
+// the register-staged kernel's reads this placement measured about 110 B/clk/CU against 90 for
+// bits 1..2 and 55 unswizzled; for the 16-byte fragment reads of the LDS-DMA kernels bits 2..3
+// and 1..2 measured the same as 3..4 (within 1 %).
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 3) & 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_chunk(r, c) << 4); }
 
 // Byte offset of scale dword w (0..1) of LDS scale row r (NVFP4: 8 raw E4M3 bytes per row,
 // the two dwords swapped on rows with bit 4 set so that 32 consecutive rows reading the
@@ -377,7 +380,7 @@ __device__ __forceinline__ void wait_vm() {
 // Per-wave DMA plan of one MXFP8 K slice, in four parts that the main loop spreads between its
 // MFMAs.  Part P (0..3) moves rows 64P + 16w .. +16 (w = wave) of both operands' codes; the
 // chunk swizzle is applied on the global side (the lane that fills LDS chunk slot cs of row r
-// fetches global chunk cs ^ ((r >> 3) & 3)).  In the per-slice scale layout parts 0 and 1
+// fetches global chunk swz_chunk(r, cs)).  In the per-slice scale layout parts 0 and 1
 // also move scale slots 256P + 64w .. +64 of both operands.  A slice past the end of K is
 // issued with out-of-range offsets (no memory traffic; the zeros they write land in a free
 // buffer) so that every slice issues the same number of DMAs.
@@ -392,7 +395,7 @@ struct MxDma {
 template <int P, int NW = 4>
 __device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t b0, bool live, uint8_t* buf) {
     const int r0 = 16 * NW * P + 16 * d.wave;
-    const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
+    const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
     uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
     if (!live || b0 + 16 * c >= (int64_t)d.kbytes) off = OOB;
     const uint32_t soff = live ? (uint32_t)b0 : 0u;
@@ -426,7 +429,7 @@ __device__ __forceinline__ u32x4s sized(u32x4s rsrc, bool live) {
 template <int P, int NW>
 __device__ __forceinline__ void nv4_dma_codes(const MxDma& d, uint32_t b0, bool live, uint8_t* buf) {
     const int r0 = 16 * NW * P + 16 * d.wave;
-    const int r = r0 + (d.lane >> 2), c = (d.lane & 3) ^ ((r >> 3) & 3);
+    const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
     const uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
     const uint32_t soff = live ? b0 : 0u;
     dma_b128(sized(d.o.a, live), lds_addr(buf + r0 * ROWB), off, soff);
