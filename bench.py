@@ -246,6 +246,22 @@ def quant_only_figures(dev, peaks, iters: int = 10):
     return out
 
 
+def timed_ms(torch, fn, iters: int) -> float:
+    """Mean ms of ``fn`` over ``iters`` back-to-back calls, after ``iters`` untimed calls that
+    bring the shader clock up (after a pause it takes ~10 ms of dense work to ramp: the first
+    calls of a GEMM run up to 15 % slower)."""
+    for _ in range(iters):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
 def rowscaled_figures(step, iters: int):
     """Side figures outside the step: row-scaled NVFP4 (one outer scale per row) of X and the
     forward GEMM with row-scaled X, each timed over ``iters`` back-to-back launches."""
@@ -255,19 +271,9 @@ def rowscaled_figures(step, iters: int):
     fmt = bsq.FMT_NVFP4 | bsq.FMT_A_ROWSCALED
     y = bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"], qw["row_scales"],
                              qw["s_enc"][0:1])
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ev[0].record()
-    for _ in range(iters):
-        bsq.nvfp4_quantize_rowscaled(step.X)
-    ev[1].record()
-    for _ in range(iters):
-        bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"], qw["row_scales"],
-                             qw["s_enc"][0:1], out=y)
-    ev[2].record()
-    torch.cuda.synchronize()
-    q_ms = ev[0].elapsed_time(ev[1]) / iters
-    g_ms = ev[1].elapsed_time(ev[2]) / iters
+    q_ms = timed_ms(torch, lambda: bsq.nvfp4_quantize_rowscaled(step.X), iters)
+    g_ms = timed_ms(torch, lambda: bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"],
+                                                        qw["row_scales"], qw["s_enc"][0:1], out=y), iters)
     q_bytes = M_TOK * K_IN * NVFP4_BYTES_PER_ELT + 8.0 * M_TOK   # + amax and S per row
     return {"nvfp4_rowscaled_quant_X_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
             "nvfp4_rowscaled_quant_X_ms": round(q_ms, 4),
@@ -282,16 +288,11 @@ def linear_layer_figures(step, iters: int):
     L = bsq.lib()
     ws = torch.empty(L.nvfp4_linear_workspace_bytes(M_TOK, K_IN, N_OUT), dtype=torch.uint8, device=step.dev)
     y, saved = bsq.nvfp4_linear_forward(step.X, step.W, step.seed, step.signs, workspace=ws)
-    bsq.nvfp4_linear_backward(step.dY, step.W, saved, step.seed, step.signs, workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        y, saved = bsq.nvfp4_linear_forward(step.X, step.W, step.seed, step.signs, workspace=ws)
-        bsq.nvfp4_linear_backward(step.dY, step.W, saved, step.seed, step.signs, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+
+    def fwd_bwd():
+        _, sv = bsq.nvfp4_linear_forward(step.X, step.W, step.seed, step.signs, workspace=ws)
+        bsq.nvfp4_linear_backward(step.dY, step.W, sv, step.seed, step.signs, workspace=ws)
+    ms = timed_ms(torch, fwd_bwd, iters)
     return {"ms": round(ms, 4), "TFLOPs": round(3 * 2.0 * M_TOK * N_OUT * K_IN / (ms * 1e-3) / 1e12, 2),
             "saved_activation_bytes": int(saved.numel()), "bf16_activation_bytes": 2 * M_TOK * K_IN}
 
@@ -327,15 +328,7 @@ def qwen3_8b_hybrid_figures(dev, iters: int):
         dw = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["col_codes"], mdy["col_scales"], None, mx["col_codes"],
                                   mx["col_scales"], None, out_dtype=torch.float32)
         return y, dx, dw
-    run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    ms = timed_ms(torch, run, iters)
     flops = 3 * 2.0 * QWEN_TOK * QWEN_N * QWEN_K
     return {"shape": "X[%d,%d] W[%d,%d]" % (QWEN_TOK, QWEN_K, QWEN_N, QWEN_K), "ms_per_step": round(ms, 3),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1)}
@@ -386,15 +379,7 @@ def grouped_figures(step, iters: int):
     out = {"experts": G, "tokens_per_expert": [offs_l[i + 1] - offs_l[i] for i in range(G)]}
     flops = 2.0 * M_TOK * N_OUT * K_IN
     for name, fn in launches.items():
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
+        ms = timed_ms(torch, fn, iters)
         out["grouped_%s_TFLOPs" % name] = round(flops / (ms * 1e-3) / 1e12, 2)
     return out
 
