@@ -614,11 +614,11 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
 // bytes per row (128 elements), filled by DMA three slices ahead, and double-buffered 16-byte
 // scale records, each holding the 16 E4M3 scales of two slices of a row.  4 waves of 128 x 128
 // (TN = 4: 4 x 4 MFMA tiles, so each dequantized word feeds 4 MFMAs).  Each wave dequantizes,
-// between the MFMAs of step s, the operands of step s+1.  The loop is bound by VALU issue: a
-// lone wave issues at most one VALU instruction per 8 clocks (measured), and dequantization
-// costs 4 per 32-clock MFMA (2 conversions, 2 scale multiplies) plus addressing and scales.
-// The code is written for TN = 2 as well (8 waves of 128 x 64, two per SIMD, whose VALU issue
-// rate adds up), which measured slower.
+// between the MFMAs of step s, the operands of step s+1.  The loop is bound by VALU issue:
+// each VALU instruction between two 32-clock MFMAs of a wave adds about one clock (measured),
+// and dequantization costs 4 per MFMA (2 conversions, 2 scale multiplies) plus scales.  An
+// 8-wave layout of 128 x 64 per wave (TN = 2, two waves per SIMD) needs 6 per MFMA and
+// measured slower; the DMA helpers here serve the 4-wave layout only.
 constexpr int NV4_CODES = 2 * GBM * ROWB;   // 32 KiB per stage
 constexpr int NV4_SREC = 2 * GBM * 16;      // 8 KiB per scale group (2 slices)
 static_assert(4 * NV4_CODES + 2 * NV4_SREC <= Fmt<2>::LDS, "NVFP4 DMA LDS");
@@ -718,9 +718,10 @@ __device__ __forceinline__ void nvw_interleave() {
 // DMAs of slice kt-1), barrier, then 8 MFMA steps; the code DMAs of slice kt+3 are spread over
 // the steps and, in odd slices, the scale group (kt+3)/2 (slices kt+3, kt+4) is fetched at
 // step 1 -- its buffer held group (kt-1)/2, whose last scales were read during slice kt-1.
-// Operand pipeline: during step s the words of step s+2 are read and those of step s+1 (read
-// during step s-1) are dequantized; steps 6 and 7 read the first two steps of slice kt+1, whose
-// scales are read at step 5.  An odd slice issues DG more DMAs than an even one, so the wait
+// Operand pipeline: each fragment's code words come in two 16-byte halves per slice (steps
+// 0-3 and 4-7): the second half of slice kt is read at step 2, the first half of slice kt+1 at
+// step 6 (slice kt+1 is complete since the barrier at the top of slice kt), and its scales at
+// step 5; during step s the operands of step s+1 are dequantized.  An odd slice issues DG more DMAs than an even one, so the wait
 // at the top of an even slice allows DC + DG in flight; the prologue ends with an out-of-range
 // group DMA so that slice 0 fits the rule.  An out-of-range DMA lane still writes (zeros) to
 // LDS: every such DMA here targets a buffer whose contents are no longer, or not yet, needed.
