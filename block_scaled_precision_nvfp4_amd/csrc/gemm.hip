@@ -500,13 +500,15 @@ __device__ __forceinline__ void mx_read(const uint8_t* buf, const uint8_t* sbuf,
     mx_read_part<3, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
 }
 
-// The 4 MFMAs of A fragment P against the 4 B fragments.
+// The 4 MFMAs of A fragment P against the 4 B fragments.  As in the NVFP4 LDS-DMA kernel the B
+// fragment (with its scales) is the first operand, so the accumulators hold C^T tiles (see
+// nvw_mfma).
 template <int P>
 __device__ __forceinline__ void mx_mfma_row(const MxFrag& f, floatx16 (&acc)[4][MXTN]) {
 #pragma unroll
     for (int j = 0; j < MXTN; ++j)
-        acc[P][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[P], f.b[j], acc[P][j], 0, 0, 0, (int)f.as[P], 0,
-                                                                     (int)f.bs[j]);
+        acc[P][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[P], acc[P][j], 0, 0, 0, (int)f.bs[j], 0,
+                                                                     (int)f.as[P]);
 }
 
 // MXFP8 main loop over K slices with 4 LDS code stages.  At the top of slice kt each wave
@@ -813,19 +815,17 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
 
 // ---------------------------------------------------------------- epilogue
 
-// Epilogue of a tile that lies entirely inside C (4 waves of 128 x 128).  Each wave stages its
-// block in its own LDS region, row-major with rows padded by 16 bytes (the two lane halves of a
-// fragment write rows 4 apart, which the padding puts on different banks), and reads it back
-// as 16-byte row chunks for fully coalesced 16-byte global stores -- instead of one 2- or
-// 4-byte store per accumulator.  bf16 output takes all 128 rows in one pass (34 KiB per
-// wave); fp32 output two passes of 64 rows.  A wave reads back only what it wrote, and the LDS
-// executes one wave's instructions in order, so no barrier is needed between the two.
-// TR: the accumulators hold C^T tiles (see nvw_mfma), so each group of 4 registers is 4
-// consecutive columns of one row and goes to LDS as one 8- or 16-byte store; otherwise each
-// accumulator is one 2- or 4-byte store.  TR with fa == nullptr: every output is scaled by the
-// uniform alpha (per-tensor scales on both operands); otherwise the lane reads its row and
-// column factors from the tables once, before staging.
-template <bool OUT_F32, bool SCALED, bool TR>
+// Epilogue of a tile that lies entirely inside C (4 waves of 128 x 128).  The accumulators
+// hold C^T tiles (see nvw_mfma and mx_mfma_row), so each group of 4 registers is 4 consecutive
+// columns of one row.  Each wave stages its block in its own LDS region, row-major with rows
+// padded by 16 bytes, one 8-byte (bf16, two packed conversions) or 16-byte (fp32) store per
+// group, and reads it back as 16-byte row chunks for fully coalesced 16-byte global stores.
+// bf16 output takes all 128 rows in one pass (34 KiB per wave); fp32 output two passes of 64
+// rows.  A wave reads back only what it wrote, and the LDS executes one wave's instructions in
+// order, so no barrier is needed between the two.  SCALED (NVFP4) with fa == nullptr: every
+// output is scaled by the uniform alpha (per-tensor scales on both operands); otherwise the
+// lane reads its row and column factors from the tables once, before staging.
+template <bool OUT_F32, bool SCALED>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, int64_t m0, int64_t n0, int wm,
                                                int wn, int wave, int lane, const float* fa, const float* fb,
                                                float alpha, floatx16 (&acc)[4][4]) {
@@ -837,15 +837,10 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
     uint8_t* reg = lds + wave * ROWS * RS;
     const int frow = lane & 31, kh = lane >> 5;
     uint8_t* cbase = (uint8_t*)g.c + ((m0 + wm) * g.N + n0 + wn) * ES;
-    float fbv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (SCALED && !TR) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fbv[j] = fb[wn + 32 * j + frow];
-    }
     const bool tables = SCALED && fa != nullptr;   // uniform
     float frv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
     float4 fcv[4][4];
-    if constexpr (TR && SCALED) {
+    if constexpr (SCALED) {
         if (tables) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) frv[i] = fa[wm + 32 * i + frow];
@@ -858,12 +853,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
     static_for<0, 128 / ROWS>([&](auto h_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr int I0 = H * ROWS / 32;
-        // one 4-column group of row `row` (within the pass), columns col..col+3 of the block
-        auto put = [&](int row, int col, float4 v) {
-            if constexpr (OUT_F32) *(float4*)(reg + row * RS + col * 4) = v;
-            else *(uint2*)(reg + row * RS + col * 2) = make_uint2(bf16x2_rne(v.x, v.y), bf16x2_rne(v.z, v.w));
-        };
-        if constexpr (TR) static_for<0, ROWS / 32>([&](auto i_c) {
+        static_for<0, ROWS / 32>([&](auto i_c) {
             constexpr int IL = decltype(i_c)::value;
             constexpr int I = I0 + IL;
 #pragma unroll
@@ -881,35 +871,10 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
                             v.x *= alpha; v.y *= alpha; v.z *= alpha; v.w *= alpha;
                         }
                     }
-                    put(32 * IL + frow, 32 * j + 8 * q + 4 * kh, v);
-                }
-            }
-        });
-        else static_for<0, ROWS / 32>([&](auto i_c) {
-            constexpr int IL = decltype(i_c)::value;
-            float fav[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float4 f4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                if constexpr (SCALED) f4 = *(const float4*)(fa + wm + 32 * (I0 + IL) + 8 * q + 4 * kh);
-                fav[4 * q] = f4.x; fav[4 * q + 1] = f4.y; fav[4 * q + 2] = f4.z; fav[4 * q + 3] = f4.w;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * IL + 8 * (r >> 2) + 4 * kh + (r & 3);
-                    const float v = SCALED ? acc[I0 + IL][j][r] * (fav[r] * fbv[j]) : acc[I0 + IL][j][r];
-                    if constexpr (OUT_F32) {
-                        // two 16-bit halves: written as one 32-bit store straight from the
-                        // accumulator registers, the fp32 path made the MXFP8 kernel's register
-                        // allocation spill hundreds of bytes per lane in its main loop
-                        const uint32_t b = __float_as_uint(v);
-                        uint8_t* p = reg + row * RS + (32 * j + frow) * 4;
-                        *(uint16_t*)p = (uint16_t)(b & 0xFFFFu);
-                        *(uint16_t*)(p + 2) = (uint16_t)(b >> 16);
-                    }
-                    else *(__bf16*)(reg + row * RS + (32 * j + frow) * 2) = (__bf16)v;
+                    // row 32 IL + frow of this pass, columns col .. col + 3 of the block
+                    const int row = 32 * IL + frow, col = 32 * j + 8 * q + 4 * kh;
+                    if constexpr (OUT_F32) *(float4*)(reg + row * RS + col * 4) = v;
+                    else *(uint2*)(reg + row * RS + col * 2) = make_uint2(bf16x2_rne(v.x, v.y), bf16x2_rne(v.z, v.w));
                 }
             }
         });
@@ -1221,7 +1186,7 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     if constexpr (FMT == 2) {
         // per-tensor scales on both operands: one uniform factor, no tables
         if (full && !g.a_rows && !g.b_rows) {
-            store_tile_lds<OUT_F32, true, true>(g, lds, m0, n0, wm, wn, wave, lane, nullptr, nullptr, alpha_pt, acc);
+            store_tile_lds<OUT_F32, true>(g, lds, m0, n0, wm, wn, wave, lane, nullptr, nullptr, alpha_pt, acc);
             return;
         }
     }
@@ -1231,12 +1196,12 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     }
     if constexpr (FMT != 0) {
         if (full) {
-            store_tile_lds<OUT_F32, F::NV, FMT == 2>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, acc);
+            store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, acc);
             return;
         }
     }
-    // FMT 2 accumulators hold C^T tiles (see nvw_mfma): swap the roles of frow and r
-    constexpr bool TR = FMT == 2;
+    // FMT 1 and 2 accumulators hold C^T tiles (see nvw_mfma): swap the roles of frow and r
+    constexpr bool TR = FMT != 0;
     static_for<0, 4 * TN>([&](auto t_c) {
         constexpr int i = decltype(t_c)::value / TN, j = decltype(t_c)::value % TN;
 #pragma unroll
@@ -1247,7 +1212,10 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
             const int64_t row = m0 + lrow, col = n0 + lcol;
             if (row < g.M && col < g.N) {
                 const float v = F::NV ? acc[i][j][r] * (fa[lrow] * fb[lcol]) : acc[i][j][r];
-                if (OUT_F32) {   // as two halves, for the reason given in store_tile_lds
+                if (OUT_F32) {
+                    // two 16-bit halves: one 32-bit store per accumulator here changes the
+                    // MXFP8 kernel's register allocation so that its main loop spills ~220
+                    // registers per lane
                     const uint32_t b = __float_as_uint(v);
                     uint16_t* p = (uint16_t*)((float*)g.c + row * g.N + col);
                     p[0] = (uint16_t)(b & 0xFFFFu);
