@@ -34,7 +34,9 @@ bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 1
 
 // Largest K of a GEMM: a 256-row operand tile (codes) must stay below 2^31 bytes, the range of
 // one buffer resource: 8 Mi elements for MXFP8 (1 byte each), 16 Mi for NVFP4.
-int64_t gemm_max_k(int fmt) { return fmt == BSQ_FMT_MXFP8 ? (int64_t)1 << 23 : (int64_t)1 << 24; }
+// Exclusive bound on K: a 256-row operand tile of K-element rows (K/2 bytes NVFP4, K bytes
+// MXFP8) must span fewer than 2^31 bytes, the largest range a buffer resource covers.
+int64_t gemm_k_limit(int fmt) { return fmt == BSQ_FMT_MXFP8 ? (int64_t)1 << 23 : (int64_t)1 << 24; }
 
 int launched(int hip_code, const char* what) {
     if (hip_code != 0)
@@ -164,7 +166,8 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
     if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
     if (M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
     if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
-    if (K > gemm_max_k(fmt)) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) exceeds %lld", fn, (long long)K, (long long)gemm_max_k(fmt));
+    if (K >= gemm_k_limit(fmt))
+        return fail(BSQ_ERR_SHAPE, "%s: K (%lld) exceeds %lld", fn, (long long)K, (long long)gemm_k_limit(fmt) - 1);
     if (M == 0 || N == 0) return ok();
     if (!c) return fail(BSQ_ERR_NULL, "%s: c is NULL", fn);
     if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return fail(BSQ_ERR_NULL, "%s: operand pointer is NULL", fn);
@@ -190,7 +193,8 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
     if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
     if (groups < 0 || M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative size", fn);
     if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
-    if (K > gemm_max_k(fmt)) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) exceeds %lld", fn, (long long)K, (long long)gemm_max_k(fmt));
+    if (K >= gemm_k_limit(fmt))
+        return fail(BSQ_ERR_SHAPE, "%s: K (%lld) exceeds %lld", fn, (long long)K, (long long)gemm_k_limit(fmt) - 1);
     if (groups == 0 || M == 0 || N == 0) return ok();
     if (groups > (int64_t)1 << 24) return fail(BSQ_ERR_SHAPE, "%s: too many groups (%lld)", fn, (long long)groups);
     if (bsq::grouped_gemm_workgroups(mode, groups, M, N) > 0x7FFFFFFF) return fail(BSQ_ERR_SHAPE, "%s: problem too large for one launch", fn);
@@ -263,6 +267,10 @@ int linear_shape_check(const char* fn, int64_t T, int64_t K, int64_t N) {
     if (T % 32 != 0 || K % 32 != 0 || N % 32 != 0)
         return fail(BSQ_ERR_SHAPE, "%s: tokens, in_features and out_features must be multiples of 32, got %lld, %lld, %lld",
                     fn, (long long)T, (long long)K, (long long)N);
+    // each is the contraction length of one of the three NVFP4 GEMMs (wgrad contracts over tokens)
+    const int64_t lim = gemm_k_limit(BSQ_FMT_NVFP4);
+    if (T >= lim || K >= lim || N >= lim)
+        return fail(BSQ_ERR_SHAPE, "%s: tokens, in_features and out_features must be below %lld", fn, (long long)lim);
     return BSQ_OK;
 }
 

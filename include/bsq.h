@@ -219,8 +219,8 @@ int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t*
  *   fmt BSQ_FMT_MXFP8: a_codes [M][K] (E4M3), a_scales [M][K/32] (E8M0); s_enc
  *       pointers are ignored (may be NULL); alpha = 1.  K % 32 == 0.
  *   c [M][N], c_dtype BSQ_OUT_BF16 (RNE) or BSQ_OUT_F32.
- *   M, N >= 0 arbitrary; M, N or K == 0 are valid (K == 0 writes zeros).  K is at most
- *   2^24 (NVFP4) or 2^23 (MXFP8), so that a 256-row operand tile stays below 2 GiB.
+ *   M, N >= 0 arbitrary; M, N or K == 0 are valid (K == 0 writes zeros).  K is below 2^24
+ *   (NVFP4) or 2^23 (MXFP8), so that a 256-row operand tile stays below 2 GiB.
  */
 int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
                      const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
@@ -286,7 +286,8 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
  * intermediate quantized operands live in `workspace`.
  *
  *   x [T][K], w [N][K], dy [T][N] bf16 (device); T = tokens, K = in_features,
- *   N = out_features, all multiples of 32 and non-zero.
+ *   N = out_features, all multiples of 32, non-zero and below 2^24 (each is the contraction
+ *   length of one of the three GEMMs).
  *   sr_seed, rht_signs: as for nvfp4_quantize (rht_signs required); the same values must be
  *   passed to forward and backward (the saved operand was drawn with them).
  *   saved      device buffer of nvfp4_linear_saved_bytes(T, K) bytes, written by forward and

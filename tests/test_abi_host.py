@@ -117,6 +117,10 @@ def test_gemm_validation(L):
     assert f(0, -1, 128, 64, *args, 0, None) == 2
     assert f(1, 128, 128, (1 << 23) + 32, *args, 0, None) == 2 and "exceeds" in last(L)
     assert f(0, 128, 128, (1 << 24) + 32, *args, 0, None) == 2 and "exceeds" in last(L)
+    # the bound is exclusive: a 256-row tile of 2^24 NVFP4 (2^23 MXFP8) elements per row would
+    # span exactly 2^31 bytes, one more than a buffer resource covers
+    assert f(0, 128, 128, 1 << 24, *args, 0, None) == 2 and "exceeds" in last(L)
+    assert f(1, 128, 128, 1 << 23, *args, 0, None) == 2 and "exceeds" in last(L)
     assert f(0, 128, 128, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 1 and "tensor scales" in last(L)
     assert f(0, 128, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
     assert f(0, 128, 128, 64, FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 6
@@ -186,6 +190,9 @@ def test_linear_validation(L):
     assert fwd(FAKE, FAKE, 64, 64, 64, 0, None, FAKE, FAKE, FAKE, None) == 1
     assert fwd(FAKE, FAKE, 64, 64, 64, 0, FAKE, FAKE, FAKE + 8, FAKE, None) == 6
     assert bwd(FAKE, FAKE, FAKE, 64, 64, 40, 0, FAKE, FAKE, FAKE, FAKE, None) == 2
+    # tokens are the wgrad GEMM's contraction length: bounded like any NVFP4 K
+    assert fwd(FAKE, FAKE, 1 << 24, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, None) == 2 and "below" in last(L)
+    assert bwd(FAKE, FAKE, FAKE, 64, 64, 1 << 24, 0, FAKE, FAKE, FAKE, FAKE, None) == 2 and "below" in last(L)
     assert bwd(FAKE, FAKE, None, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert bwd(FAKE, FAKE, FAKE, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE + 4, None) == 6
 
