@@ -815,7 +815,8 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
 
 // ---------------------------------------------------------------- epilogue
 
-// Epilogue of a tile that lies entirely inside C (4 waves of 128 x 128).  The accumulators
+// Epilogue of a tile whose columns lie inside C (4 waves of 128 x 128); rows from m_end on
+// (the tile's last rows past M, e.g. the end of an M-group) are not stored.  The accumulators
 // hold C^T tiles (see nvw_mfma and mx_mfma_row), so each group of 4 registers is 4 consecutive
 // columns of one row.  Each wave stages its block in its own LDS region, row-major with rows
 // padded by 16 bytes, one 8-byte (bf16, two packed conversions) or 16-byte (fp32) store per
@@ -828,7 +829,7 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
 template <bool OUT_F32, bool SCALED>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, int64_t m0, int64_t n0, int wm,
                                                int wn, int wave, int lane, const float* fa, const float* fb,
-                                               float alpha, floatx16 (&acc)[4][4]) {
+                                               float alpha, int64_t m_end, floatx16 (&acc)[4][4]) {
     constexpr int ES = OUT_F32 ? 4 : 2;          // bytes per element
     constexpr int ROWS = OUT_F32 ? 64 : 128;     // rows per pass
     constexpr int RS = 128 * ES + 16;            // LDS row stride
@@ -883,7 +884,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
         for (int p = 0; p < ROWS * CPR / 64; ++p) {
             const int q = 64 * p + lane, row = q / CPR, c16 = q % CPR;
             const uint4 v = *(const uint4*)(reg + row * RS + c16 * 16);
-            *(uint4*)(cbase + (int64_t)(H * ROWS + row) * g.N * ES + c16 * 16) = v;
+            if (wm + H * ROWS + row < m_end) *(uint4*)(cbase + (int64_t)(H * ROWS + row) * g.N * ES + c16 * 16) = v;
         }
         asm volatile("" ::: "memory");
     });
@@ -1182,11 +1183,13 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     float* fb = fa + 256;
     __syncthreads();   // every wave is done with the operand buffers (and its DMAs)
     constexpr int ES = OUT_F32 ? 4 : 2;
-    const bool full = m0 + GBM <= g.M && n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
+    // staged epilogue: every column of the tile inside C (rows past M are skipped there)
+    const bool staged = n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
+    const int64_t m_end = g.M - m0;
     if constexpr (FMT == 2) {
         // per-tensor scales on both operands: one uniform factor, no tables
-        if (full && !g.a_rows && !g.b_rows) {
-            store_tile_lds<OUT_F32, true>(g, lds, m0, n0, wm, wn, wave, lane, nullptr, nullptr, alpha_pt, acc);
+        if (staged && !g.a_rows && !g.b_rows) {
+            store_tile_lds<OUT_F32, true>(g, lds, m0, n0, wm, wn, wave, lane, nullptr, nullptr, alpha_pt, m_end, acc);
             return;
         }
     }
@@ -1195,8 +1198,8 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         __syncthreads();
     }
     if constexpr (FMT != 0) {
-        if (full) {
-            store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, acc);
+        if (staged) {
+            store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, m_end, acc);
             return;
         }
     }

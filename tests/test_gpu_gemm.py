@@ -87,9 +87,11 @@ def test_tiny_config_full():
     nv_gemm_check(gaussian_bf16((128, 256), 1.0, SEED_X), gaussian_bf16((256, 256), 1.0, SEED_W), label="tiny")
 
 
-# K a multiple of 256 runs the 4-wave kernel with grouped scale records, any other K the 8-wave one
+# K a multiple of 256 runs the 4-wave kernel with grouped scale records, any other K the 8-wave one;
+# (300, 520, 2048) and (40, 512, 512) have tiles with every column inside C but rows past M
+# (staged through LDS with those rows skipped)
 @pytest.mark.parametrize("M,N,K", [(200, 72, 96), (128, 128, 32), (1, 1, 64), (384, 260, 320), (64, 512, 1056),
-                                   (200, 72, 256), (1, 1, 256), (384, 260, 768), (300, 520, 2048)])
+                                   (200, 72, 256), (1, 1, 256), (384, 260, 768), (300, 520, 2048), (40, 512, 512)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_nvfp4_ragged_full(M, N, K, out_dtype):
     nv_gemm_check(outlier_bf16((M, K), seed=M, mask_seed=K), gaussian_bf16((N, K), 0.02, N + 7), out_dtype=out_dtype,
@@ -109,8 +111,11 @@ def test_nvfp4_full_tiles_extreme_tensor_scales(fa, fb, out_dtype):
     nv_gemm_check(a, b, out_dtype=out_dtype, label="extreme scales %g %g" % (fa, fb))
 
 
-# K = 96, 256, 1056: scales fetched per K slice; K = 512, 1536: grouped 16-block scale records
-@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (256, 256, 256), (96, 160, 1056), (200, 72, 512), (300, 260, 1536)])
+# K = 96, 256, 1056: scales fetched per K slice; K = 512, 1536: grouped 16-block scale records.
+# (300, 512, *): tiles whose columns all lie inside C but whose last rows do not -- staged
+# through LDS with the rows past M skipped.
+@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (256, 256, 256), (96, 160, 1056), (200, 72, 512), (300, 260, 1536),
+                                   (300, 512, 512), (300, 512, 1056)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_mxfp8_ragged_full(M, N, K, out_dtype):
     mx_gemm_check(outlier_bf16((M, K), seed=M + 1, mask_seed=K + 1), gaussian_bf16((N, K), 0.02, N + 9), 1, 1,
