@@ -416,7 +416,7 @@ def cpu_baseline(tokens: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU: the path here has no multi-GPU implementation (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
