@@ -122,6 +122,40 @@ def test_mxfp8_ragged_full(M, N, K, out_dtype):
                   out_dtype=out_dtype, label="ragged")
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_largest_k(fmt):
+    """The largest K the C ABI accepts (2^24 - 256 NVFP4, 2^23 - 512 MXFP8, both on the
+    LDS-DMA kernels): a 256-row operand tile then spans just under 2^31 bytes, the largest
+    range of a buffer resource, and the lane offsets reach their top bits.  Seeded random codes
+    and scales (no quantization at this size); sampled rows x columns against the oracle."""
+    import oracle
+    K = (1 << 24) - 256 if fmt == 0 else (1 << 23) - 512
+    M = N = 256
+    rng = np.random.default_rng(97 + fmt)
+    if fmt == 0:
+        ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+        bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        asc = rng.integers(0x30, 0x48, (M, K // 16), dtype=np.uint8)
+        bsc = rng.integers(0x30, 0x48, (N, K // 16), dtype=np.uint8)
+    else:
+        ac = rng.integers(0, 256, (M, K), dtype=np.uint8) & 0x77   # finite E4M3 codes
+        bc = rng.integers(0, 256, (N, K), dtype=np.uint8) & 0x77
+        asc = rng.integers(120, 134, (M, K // 32), dtype=np.uint8)
+        bsc = rng.integers(120, 134, (N, K // 32), dtype=np.uint8)
+    note("largest K: fmt=%d K=%d" % (fmt, K))
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    sa, sb = (one, one) if fmt == 0 else (None, None)
+    y = bsq.blockscaled_gemm(fmt, t(ac), t(asc), sa, t(bc), t(bsc), sb)
+    torch.cuda.synchronize()
+    rows, cols = np.array([0, 77, 128, 255]), np.array([0, 31, 200, 255])
+    ref = oracle.blockscaled_gemm(fmt, ac, asc, 1.0, bc, bsc, 1.0, rows=rows, cols=cols)
+    yc = y.float().cpu().numpy().astype(np.float64)[rows][:, cols]
+    err = rel_fro(yc, bf16_round(ref))
+    note("  rel_fro vs rounded oracle = %.3e" % err)
+    assert err <= GEMM_TOL, err
+
+
 def test_constant_operands_closed_form():
     """All elements 1.0 in A and 0.5 in B: every output is K * 1.0 * 0.5 exactly."""
     M, N, K = 160, 96, 512
