@@ -182,6 +182,42 @@ def test_quant_only_workload():
     check_mxfp8(x, 3, label="quant-only")
 
 
+def test_rowwise_beyond_2g_elements():
+    """A [131088, 16384] tensor (2^31 + 2^18 elements, input byte offsets past 2^32), NVFP4
+    rowwise RNE and MXFP8 rowwise.  The tensor maximum (100, above every N(0,1) draw) is
+    planted in row 0, so any set of rows that contains row 0 has the tensor's scale; rowwise
+    codes depend only on their row and that scale, so the oracle quantizes sampled rows
+    (row 0 among them, the first and last rows, the middle, a random spread) on their own."""
+    import oracle
+    R, C = 131072 + 16, 16384
+    note("rowwise beyond 2^31 elements: generating %s on the host (~1 min)" % ((R, C),))
+    x = gaussian_bf16((R, C), 1.0, 99)
+    x[0, 5] = 100.0
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, 1, R // 2, R - 2, R - 1], rng.choice(R, 12, replace=False)]))
+    sub = x[torch.from_numpy(rows)].contiguous()
+    note("rowwise beyond 2^31 elements: quantizing on the GPU")
+    xd = x.to(DEV)
+    del x
+    got = bsq.nvfp4_quantize(xd, direction=1)
+    idx = torch.from_numpy(rows).to(DEV)
+    g_codes, g_scales = got["row_codes"][idx].contiguous(), got["row_scales"][idx].contiguous()
+    g_amax, g_senc = got["amax"][0:1].clone(), got["s_enc"][0:1].clone()
+    del got
+    mx = bsq.mxfp8_quantize(xd, direction=1)
+    m_codes, m_scales = mx["row_codes"][idx].contiguous(), mx["row_scales"][idx].contiguous()
+    del mx, xd
+    torch.cuda.synchronize()
+    ref = oracle.nvfp4_quantize(sub, direction=1)
+    assert_f32_equal(g_amax, ref["amax"][0:1], "amax")
+    assert_f32_equal(g_senc, ref["s_enc"][0:1], "s_enc")
+    assert_bytes_equal(g_scales, ref["row_scales"], "row_scales")
+    assert_bytes_equal(g_codes, ref["row_codes"], "row_codes")
+    mref = oracle.mxfp8_quantize(sub, direction=1)
+    assert_bytes_equal(m_scales, mref["row_scales"], "mxfp8 row_scales")
+    assert_bytes_equal(m_codes, mref["row_codes"], "mxfp8 row_codes")
+
+
 def test_fwd_operands_llama3_8b():
     """Forward operands of the Llama-3-8B FFN up-projection, NVFP4 rowwise RNE."""
     check_nvfp4(gaussian_bf16((16384, 4096), 1.0, SEED_X), 1, label="fwd X")
