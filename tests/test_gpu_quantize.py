@@ -182,12 +182,14 @@ def test_quant_only_workload():
     check_mxfp8(x, 3, label="quant-only")
 
 
-def test_rowwise_beyond_2g_elements():
-    """A [131088, 16384] tensor (2^31 + 2^18 elements, input byte offsets past 2^32), NVFP4
-    rowwise RNE and MXFP8 rowwise.  The tensor maximum (100, above every N(0,1) draw) is
-    planted in row 0, so any set of rows that contains row 0 has the tensor's scale; rowwise
-    codes depend only on their row and that scale, so the oracle quantizes sampled rows
-    (row 0 among them, the first and last rows, the middle, a random spread) on their own."""
+def test_beyond_2g_elements():
+    """A [131088, 16384] tensor (2^31 + 2^18 elements, input byte offsets past 2^32): NVFP4
+    rowwise RNE, MXFP8 rowwise and NVFP4 columnwise RNE with RHT.  The tensor maximum (100,
+    above every N(0,1) draw) is planted at row 0, column 5, so any set of rows containing row 0
+    (or of columns containing column 5) has the tensor's scale; rowwise codes depend only on
+    their row and that scale, columnwise codes only on their column, so the oracle quantizes
+    sampled rows (the first and last, the middle, a random spread) or sampled columns on
+    their own."""
     import oracle
     R, C = 131072 + 16, 16384
     note("rowwise beyond 2^31 elements: generating %s on the host (~1 min)" % ((R, C),))
@@ -206,7 +208,17 @@ def test_rowwise_beyond_2g_elements():
     del got
     mx = bsq.mxfp8_quantize(xd, direction=1)
     m_codes, m_scales = mx["row_codes"][idx].contiguous(), mx["row_scales"][idx].contiguous()
-    del mx, xd
+    del mx
+    # columnwise with RHT (blocks and transform run along rows, so columns are independent
+    # given the tensor scale; column 5 holds the maximum, about 25 after the transform)
+    signs = rht_signs(SEED_SIGNS)
+    cols = np.unique(np.concatenate([[0, 5, C // 2, C - 1], rng.choice(C, 8, replace=False)]))
+    col = bsq.nvfp4_quantize(xd, direction=2, rht_signs=signs)
+    cidx = torch.from_numpy(cols).to(DEV)
+    c_codes, c_scales = col["col_codes"][cidx].contiguous(), col["col_scales"][cidx].contiguous()
+    c_amax, c_senc = col["amax"][1:2].clone(), col["s_enc"][1:2].clone()
+    sub_c = xd[:, cidx].cpu().contiguous()
+    del col, xd
     torch.cuda.synchronize()
     ref = oracle.nvfp4_quantize(sub, direction=1)
     assert_f32_equal(g_amax, ref["amax"][0:1], "amax")
@@ -216,6 +228,11 @@ def test_rowwise_beyond_2g_elements():
     mref = oracle.mxfp8_quantize(sub, direction=1)
     assert_bytes_equal(m_scales, mref["row_scales"], "mxfp8 row_scales")
     assert_bytes_equal(m_codes, mref["row_codes"], "mxfp8 row_codes")
+    cref = oracle.nvfp4_quantize(sub_c, direction=2, signs=signs.numpy())
+    assert_f32_equal(c_amax, cref["amax"][1:2], "col amax")
+    assert_f32_equal(c_senc, cref["s_enc"][1:2], "col s_enc")
+    assert_bytes_equal(c_scales, cref["col_scales"], "col_scales")
+    assert_bytes_equal(c_codes, cref["col_codes"], "col_codes")
 
 
 def test_fwd_operands_llama3_8b():
