@@ -156,6 +156,43 @@ def test_largest_k(fmt):
     assert err <= GEMM_TOL, err
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_output_beyond_2g_elements(fmt):
+    """C of [65792, 32768] (2^31 + 2^24 elements, bf16 output offsets past 2^32 bytes) with a
+    short K: both operands quantized on the GPU and by the oracle (bit for bit), C compared on
+    sampled rows x columns, the last rows and columns among them."""
+    import oracle
+    M, N, K = 65536 + 256, 32768, 512
+    note("gemm output beyond 2^31 elements: fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
+    a = gaussian_bf16((M, K), 1.0, 201)
+    b = gaussian_bf16((N, K), 0.05, 202)
+    if fmt == 0:
+        qa, qb = bsq.nvfp4_quantize(a.to(DEV), direction=1), bsq.nvfp4_quantize(b.to(DEV), direction=1)
+        ra, rb = oracle.nvfp4_quantize(a, direction=1), oracle.nvfp4_quantize(b, direction=1)
+        y = bsq.blockscaled_gemm(fmt, qa["row_codes"], qa["row_scales"], qa["s_enc"][0:1], qb["row_codes"],
+                                 qb["row_scales"], qb["s_enc"][0:1])
+        sa, sb = float(ra["s_enc"][0]), float(rb["s_enc"][0])
+    else:
+        qa, qb = bsq.mxfp8_quantize(a.to(DEV), direction=1), bsq.mxfp8_quantize(b.to(DEV), direction=1)
+        ra, rb = oracle.mxfp8_quantize(a, direction=1), oracle.mxfp8_quantize(b, direction=1)
+        y = bsq.blockscaled_gemm(fmt, qa["row_codes"], qa["row_scales"], None, qb["row_codes"], qb["row_scales"], None)
+        sa = sb = 1.0
+    torch.cuda.synchronize()
+    for q, r, nm in ((qa, ra, "A"), (qb, rb, "B")):
+        assert_bytes_equal(q["row_codes"], r["row_codes"], nm + " codes")
+        assert_bytes_equal(q["row_scales"], r["row_scales"], nm + " scales")
+    rng = np.random.default_rng(203 + fmt)
+    rows = np.unique(np.concatenate([[0, M // 2, M - 1], rng.choice(M, 13, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N // 2, N - 1], rng.choice(N, 13, replace=False)]))
+    yc = y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
+    del y
+    ref = oracle.blockscaled_gemm(fmt, ra["row_codes"], ra["row_scales"], sa, rb["row_codes"], rb["row_scales"], sb,
+                                  rows=rows, cols=cols)
+    err = rel_fro(yc, bf16_round(ref))
+    note("  rel_fro vs rounded oracle = %.3e" % err)
+    assert err <= GEMM_TOL, err
+
+
 def test_constant_operands_closed_form():
     """All elements 1.0 in A and 0.5 in B: every output is K * 1.0 * 0.5 exactly."""
     M, N, K = 160, 96, 512

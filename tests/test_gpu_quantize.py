@@ -184,7 +184,7 @@ def test_quant_only_workload():
 
 def test_beyond_2g_elements():
     """A [131088, 16384] tensor (2^31 + 2^18 elements, input byte offsets past 2^32): NVFP4
-    rowwise RNE, MXFP8 rowwise and NVFP4 columnwise RNE with RHT.  The tensor maximum (100,
+    rowwise RNE, MXFP8 rowwise, row-scaled NVFP4 and NVFP4 columnwise RNE with RHT.  The tensor maximum (100,
     above every N(0,1) draw) is planted at row 0, column 5, so any set of rows containing row 0
     (or of columns containing column 5) has the tensor's scale; rowwise codes depend only on
     their row and that scale, columnwise codes only on their column, so the oracle quantizes
@@ -209,6 +209,10 @@ def test_beyond_2g_elements():
     mx = bsq.mxfp8_quantize(xd, direction=1)
     m_codes, m_scales = mx["row_codes"][idx].contiguous(), mx["row_scales"][idx].contiguous()
     del mx
+    rs = bsq.nvfp4_quantize_rowscaled(xd)   # one outer scale per row: rows fully independent
+    r_codes, r_scales = rs["codes"][idx].contiguous(), rs["scales"][idx].contiguous()
+    r_amax, r_senc = rs["amax"][idx].contiguous(), rs["s_enc"][idx].contiguous()
+    del rs
     # columnwise with RHT (blocks and transform run along rows, so columns are independent
     # given the tensor scale; column 5 holds the maximum, about 25 after the transform)
     signs = rht_signs(SEED_SIGNS)
@@ -228,6 +232,11 @@ def test_beyond_2g_elements():
     mref = oracle.mxfp8_quantize(sub, direction=1)
     assert_bytes_equal(m_scales, mref["row_scales"], "mxfp8 row_scales")
     assert_bytes_equal(m_codes, mref["row_codes"], "mxfp8 row_codes")
+    rref = oracle.nvfp4_quantize_rowscaled(sub)
+    assert_f32_equal(r_amax, rref["amax"], "row-scaled amax")
+    assert_f32_equal(r_senc, rref["s_enc"], "row-scaled s_enc")
+    assert_bytes_equal(r_scales, rref["scales"], "row-scaled scales")
+    assert_bytes_equal(r_codes, rref["codes"], "row-scaled codes")
     cref = oracle.nvfp4_quantize(sub_c, direction=2, signs=signs.numpy())
     assert_f32_equal(c_amax, cref["amax"][1:2], "col amax")
     assert_f32_equal(c_senc, cref["s_enc"][1:2], "col s_enc")
