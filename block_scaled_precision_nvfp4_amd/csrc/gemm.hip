@@ -75,7 +75,8 @@ struct Fmt {
     // NVFP4: 8 raw scale bytes per row; MXFP8: one dword slot per (row, K-block), 2 per row
     static constexpr int STAGE = (GBM + GBN) * (ROWB + SCB);
     static constexpr int NSTAGE = FMT == 0 ? 3 : 4;
-    static constexpr int LDS = NSTAGE * STAGE;
+    // MXFP8 also keeps room for three 8 KiB scale-record buffers after its 4 code stages
+    static constexpr int LDS = NSTAGE * STAGE + (FMT == 1 ? 8192 : 0);
     // waves per workgroup and MFMA tiles per wave: 8 waves (two per SIMD) of 128 x 64 or 4
     // waves of 128 x 128.
     static constexpr int NW = FMT == 0 ? 8 : 4;
@@ -319,19 +320,25 @@ struct MxFrag {
 };
 
 // MXFP8 LDS layout.  A code stage (one K slice) is A codes [256][64 B] then B codes
-// [256][64 B], the 16-byte chunks swizzled by swz().  Scales use one of two layouts:
-//  - grouped (K a multiple of 512): the scale bytes of 8 consecutive slices (16 K-blocks) of
-//    a row form one aligned 16-byte global record, fetched with one DMA lane per row every 8
-//    slices into a double-buffered region [group parity][operand][256 rows][16 B] after the
-//    4 code stages;
-//  - per slice (any other K): one dword slot per (row, K-block) after the codes of each
-//    stage, [operand][256 rows][2 slots], holding the byte in its low 8 bits (a byte DMA
-//    fills one dword slot per lane).
+// [256][64 B], the 16-byte chunks swizzled by swz().  Scales use one of three layouts:
+//  - grouped (MX_RECS; K a multiple of 512, 16-byte aligned rows): the scale bytes of 8
+//    consecutive slices (16 K-blocks) of a row form one aligned 16-byte global record,
+//    fetched with one DMA lane per row every 8 slices into a double-buffered region
+//    [group parity][operand][256 rows][16 B] after the 4 code stages;
+//  - offset records (MX_OFFRECS; rows a multiple of 16 scale bytes apart, any K and base):
+//    the aligned 16-byte records that hold a row's scale bytes, which start delta bytes into
+//    the first one (the same delta for every row of an operand).  Slice group G reads bytes
+//    of records G and G+1, so the records rotate through three buffers of the grouped
+//    region's shape, record j in buffer j mod 3;
+//  - per slice (MX_SLOTS; any other row pitch): one dword slot per (row, K-block) after the
+//    codes of each stage, [operand][256 rows][2 slots], holding the byte in its low 8 bits
+//    (a byte DMA fills one dword slot per lane).
+constexpr int MX_SLOTS = 0, MX_RECS = 1, MX_OFFRECS = 2;
 constexpr int MX_CODES = 2 * GBM * ROWB;                  // 32 KiB
 constexpr int MX_STAGE_SLOTS = MX_CODES + 2 * GBM * 2 * 4;  // 36 KiB
 constexpr int MX_GROUP = 8;                                // slices per grouped scale record
 constexpr int MX_SREC = 2 * GBM * 16;                      // 8 KiB per scale group
-static_assert(4 * MX_STAGE_SLOTS == Fmt<1>::LDS && 4 * MX_CODES + 2 * MX_SREC <= Fmt<1>::LDS, "MXFP8 LDS");
+static_assert(4 * MX_STAGE_SLOTS <= Fmt<1>::LDS && 4 * MX_CODES + 3 * MX_SREC <= Fmt<1>::LDS, "MXFP8 LDS");
 
 // LDS DMA: a buffer load whose data goes straight to LDS.  A wave-wide DMA writes 64
 // consecutive LDS slots starting at the wave-uniform address in M0 -- 16 bytes per lane for
@@ -447,6 +454,16 @@ __device__ __forceinline__ void nv4_dma_group(const MxDma& d, uint32_t grp, bool
     dma_b128(sized(d.o.bs, live), lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), off, soff);
 }
 
+// Offset records: record j (16 aligned bytes) of every row of both operands, one lane per row
+// as in nv4_dma_group; offa / offb hold the lane's row offset from the resource base (an
+// out-of-range offset for a row past the tile).  The record offset goes into the vector offset
+// so that the resource's range check covers the whole address.
+__device__ __forceinline__ void mx_dma_offrec(const MxDma& d, uint32_t offa, uint32_t offb, uint32_t j, bool live,
+                                              uint8_t* sbuf) {
+    dma_b128(sized(d.o.as, live), lds_addr(sbuf + 64 * d.wave * 16), offa + 16u * j, 0u);
+    dma_b128(sized(d.o.bs, live), lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), offb + 16u * j, 0u);
+}
+
 template <int EPB, int BLK>
 __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
     MxDma d;
@@ -465,12 +482,19 @@ __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t
     return d;
 }
 
+// The lane's scale bytes of a slice in the offset-record layout: a at A fragment row 0's byte,
+// b at B fragment row 0's (fragment P's rows are 512P bytes further).
+struct MxSPtr {
+    const uint8_t* a;
+    const uint8_t* b;
+};
+
 // Fragment reads of part P of a slice: A fragment P and B fragment P (lane (row, g): K elements
 // 16g..16g+15 (chunk g) and 32+16g.. (chunk 2+g) of the slice) and their scales (K-block g).
 // Grouped scales: byte 2q + g of the row's record, q = slice index within its group.
-template <int P, bool GROUPED>
-__device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* sbuf, int q, int wm, int wn,
-                                             int lane, MxFrag& f) {
+template <int P, int MODE>
+__device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* sbuf, int q, MxSPtr sp, int wm,
+                                             int wn, int lane, MxFrag& f) {
     const int frow = lane & 31, kh = lane >> 5;
     const int ra = wm + 32 * P + frow, rb = wn + 32 * P + frow;
     const uint8_t* sA = buf;
@@ -481,9 +505,12 @@ __device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* 
     lo = *(const uint4*)(sB + swz(rb, kh));
     hi = *(const uint4*)(sB + swz(rb, 2 + kh));
     f.b[P] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    if constexpr (GROUPED) {
+    if constexpr (MODE == MX_RECS) {
         f.as[P] = sbuf[ra * 16 + 2 * q + kh];
         f.bs[P] = sbuf[GBM * 16 + rb * 16 + 2 * q + kh];
+    } else if constexpr (MODE == MX_OFFRECS) {
+        f.as[P] = sp.a[512 * P];
+        f.bs[P] = sp.b[512 * P];
     } else {
         const uint32_t* slots = (const uint32_t*)(buf + MX_CODES);
         f.as[P] = slots[2 * ra + kh];
@@ -491,13 +518,13 @@ __device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* 
     }
 }
 
-template <bool GROUPED>
-__device__ __forceinline__ void mx_read(const uint8_t* buf, const uint8_t* sbuf, int q, int wm, int wn, int lane,
-                                        MxFrag& f) {
-    mx_read_part<0, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
-    mx_read_part<1, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
-    mx_read_part<2, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
-    mx_read_part<3, GROUPED>(buf, sbuf, q, wm, wn, lane, f);
+template <int MODE>
+__device__ __forceinline__ void mx_read(const uint8_t* buf, const uint8_t* sbuf, int q, MxSPtr sp, int wm, int wn,
+                                        int lane, MxFrag& f) {
+    mx_read_part<0, MODE>(buf, sbuf, q, sp, wm, wn, lane, f);
+    mx_read_part<1, MODE>(buf, sbuf, q, sp, wm, wn, lane, f);
+    mx_read_part<2, MODE>(buf, sbuf, q, sp, wm, wn, lane, f);
+    mx_read_part<3, MODE>(buf, sbuf, q, sp, wm, wn, lane, f);
 }
 
 // The 4 MFMAs of A fragment P against the 4 B fragments.  As in the NVFP4 LDS-DMA kernel the B
@@ -520,65 +547,137 @@ __device__ __forceinline__ void mx_mfma_row(const MxFrag& f, floatx16 (&acc)[4][
 // and one B fragment of slice kt+1 into the other register set.  In the grouped layout the
 // scale record of group G+1 is fetched during slice 8G+1 (its buffer held group G-1, whose
 // last slice was consumed by then) and is complete, being older than the codes waited for,
-// when slice 8G+7 reads the fragments of slice 8G+8.
-template <bool GROUPED>
+// when slice 8G+7 reads the fragments of slice 8G+8.  Offset records follow the same
+// schedule one record later: records 0 and 1 come with the first slices, record G+2 is
+// fetched during slice 8G+1 into the buffer of record G-1 (last read for slice 8G-1) and is
+// first read for slice 8G+8.
+template <int MODE>
 __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
                                              int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
+    constexpr bool REC = MODE != MX_SLOTS;
     constexpr int DC = 8;                    // code DMAs per slice per lane
-    constexpr int DS = GROUPED ? 0 : 4;      // per-slice scale DMAs
-    constexpr int DG = 2;                    // grouped scale DMAs (every MX_GROUP slices)
-    constexpr int STRIDE = GROUPED ? MX_CODES : MX_STAGE_SLOTS;
+    constexpr int DS = REC ? 0 : 4;          // per-slice scale DMAs
+    constexpr int DG = 2;                    // scale-record DMAs (every MX_GROUP slices)
+    constexpr int STRIDE = REC ? MX_CODES : MX_STAGE_SLOTS;
     if (nk <= 0) return;
-    const MxDma d = make_dma<1, 32>(g, m0, n0, lane);
+    MxDma d = make_dma<1, 32>(g, m0, n0, lane);
     auto buf = [&](int64_t k) { return lds + (int)(k & 3) * STRIDE; };
     auto sbuf = [&](int64_t grp) { return lds + 4 * MX_CODES + (int)(grp & 1) * MX_SREC; };
+    auto rbuf = [&](int j3) { return lds + 4 * MX_CODES + j3 * MX_SREC; };   // offset record j, j3 = j mod 3
     const int nk32 = (int)nk;   // nk <= 2^17 (K <= 2^23)
+    const int kbl = (int)d.kblocks;
+
+    // Offset records: the resources span the aligned records that hold the tile's scale bytes,
+    // from the one holding its first byte through the one holding its last (whole records:
+    // the range check drops a dword that reaches past the range; the bytes past the tensor's
+    // end share the last byte's 16 aligned bytes, so its page).  Every row of an operand
+    // starts dl bytes into its first record.
+    int dla = 0, dlb = 0;
+    uint32_t offa = OOB, offb = OOB;
+    if constexpr (MODE == MX_OFFRECS) {
+        const int64_t sb = g.ld / 32;
+        const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, GBN);
+        const uint8_t* pa = g.a_scales + m0 * sb;
+        const uint8_t* pb = g.b_scales + n0 * sb;
+        dla = (int)((uintptr_t)pa & 15);
+        dlb = (int)((uintptr_t)pb & 15);
+        d.o.as = rsrc_words(pa - dla, (dla + (ra - 1) * sb + kbl + 15) & ~(int64_t)15);
+        d.o.bs = rsrc_words(pb - dlb, (dlb + (rbn - 1) * sb + kbl + 15) & ~(int64_t)15);
+        const int row = 64 * d.wave + lane;
+        offa = row < ra ? (uint32_t)(row * sb) : OOB;
+        offb = row < rbn ? (uint32_t)(row * sb) : OOB;
+    }
+    // The lane's scale bytes of slice q of a group whose first record is in buffer c3: byte
+    // dl + 2q + kh of the group's two records (below 32).  Where K ends inside a slice (an odd
+    // number of K-blocks) the last slice's second K-block has zero codes but its scale bytes
+    // belong to other data, where a NaN would leak into the sums: that K-block takes the
+    // first one's scale (1 = 0 there), so its products stay zero unless the row's own last
+    // scale is NaN.
+    const bool hi = lane >= 32;
+    const int lrow_a = (wm + (lane & 31)) * 16, lrow_b = GBM * 16 + (wn + (lane & 31)) * 16;
+    const int last_odd = (MODE == MX_OFFRECS && (kbl & 1)) ? nk32 - 1 : -1;
+    auto rec_ptrs = [&](int c3, int q, int64_t k) {
+        const uint8_t* cur = rbuf(c3);
+        const uint8_t* nxt = rbuf(c3 == 2 ? 0 : c3 + 1);
+        auto at = [&](int t) { return t < 16 ? cur + t : nxt + (t - 16); };
+        const int ta = dla + 2 * q, tb = dlb + 2 * q, up = (int)k == last_odd ? 0 : 1;
+        MxSPtr sp;
+        sp.a = (hi ? at(ta + up) : at(ta)) + lrow_a;
+        sp.b = (hi ? at(tb + up) : at(tb)) + lrow_b;
+        return sp;
+    };
+    int g3 = 0;   // offset records: the current group's index mod 3
+
     // slice k's code DMAs, part P (K a multiple of 512 with grouped records: the scalar form)
     auto dma_part = [&](auto p_c, int64_t k, bool live, uint8_t* b) {
         constexpr int P = decltype(p_c)::value;
-        if constexpr (GROUPED) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
+        if constexpr (MODE == MX_RECS) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
         else mx_dma_codes<P>(d, k * 64, live, b);
     };
     auto dma_slice = [&](int64_t k) {
         const bool live = (int)k < nk32;
         uint8_t* b = buf(k);
         static_for<0, 4>([&](auto p_c) { dma_part(p_c, k, live, b); });
-        if constexpr (!GROUPED) {
+        if constexpr (!REC) {
             mx_dma_slots<0>(d, k * 64, live, b);
             mx_dma_slots<1>(d, k * 64, live, b);
         }
     };
-    if constexpr (GROUPED) nv4_dma_group<4>(d, 0, true, sbuf(0));
+    if constexpr (MODE == MX_RECS) nv4_dma_group<4>(d, 0, true, sbuf(0));
+    if constexpr (MODE == MX_OFFRECS) {
+        mx_dma_offrec(d, offa, offb, 0, true, rbuf(0));
+        mx_dma_offrec(d, offa, offb, 1, 16 < 15 + kbl, rbuf(1));
+    }
     dma_slice(0);
     dma_slice(1);
     dma_slice(2);
     wait_vm_barrier<2 * (DC + DS)>();
     MxFrag f0, f1;
-    mx_read<GROUPED>(buf(0), sbuf(0), 0, wm, wn, lane, f0);
+    MxSPtr sp0{nullptr, nullptr};
+    if constexpr (MODE == MX_OFFRECS) sp0 = rec_ptrs(0, 0, 0);
+    mx_read<MODE>(buf(0), sbuf(0), 0, sp0, wm, wn, lane, f0);
 
-    // one slice; Q = kt mod MX_GROUP when grouped (the loop is then unrolled by MX_GROUP)
+    // One slice.  Grouped records: Q = kt mod MX_GROUP (the loop is unrolled by MX_GROUP).
+    // Offset records: the slice's place in its group is a run-time value, so that one loop
+    // takes any number of slices; only scalar work depends on it.
     auto slice = [&](int64_t kt, auto q_c, const MxFrag& fc, MxFrag& fn) {
         constexpr int Q = decltype(q_c)::value;
-        if constexpr (GROUPED && Q == 2) wait_vm_barrier<DC + DG>();   // slice kt-1 also issued a group
-        else wait_vm_barrier<DC + DS>();
+        [[maybe_unused]] const int qr = (int)(kt & (MX_GROUP - 1));   // offset records
+        [[maybe_unused]] const int g3n = g3 == 2 ? 0 : g3 + 1;
+        if constexpr (MODE == MX_OFFRECS) {
+            if (qr == 2) wait_vm_barrier<DC + DG>();   // slice kt-1 also issued a record
+            else wait_vm_barrier<DC>();
+        } else if constexpr (REC && Q == 2) {
+            wait_vm_barrier<DC + DG>();
+        } else {
+            wait_vm_barrier<DC + DS>();
+        }
         const int64_t kd = kt + 3;
         const bool live = (int)kd < nk32;
         uint8_t* db = buf(kd);
         const int64_t kn = kt + 1;                   // fragments read for the next slice
         const uint8_t* nb = buf(kn);
         const uint8_t* ns = sbuf(kn / MX_GROUP);
-        const int qn = GROUPED ? (Q + 1) % MX_GROUP : 0;
+        const int qn = REC ? (Q + 1) % MX_GROUP : 0;
+        MxSPtr spn{nullptr, nullptr};
+        if constexpr (MODE == MX_OFFRECS) spn = rec_ptrs(qr == MX_GROUP - 1 ? g3n : g3, (qr + 1) & (MX_GROUP - 1), kn);
         static_for<0, 4>([&](auto p_c) {
             constexpr int P = decltype(p_c)::value;
             dma_part(p_c, kd, live, db);
-            if constexpr (!GROUPED && P < 2) mx_dma_slots<P>(d, kd * 64, live, db);
-            if constexpr (GROUPED && Q == 1 && P == 0) {
+            if constexpr (!REC && P < 2) mx_dma_slots<P>(d, kd * 64, live, db);
+            if constexpr (MODE == MX_RECS && Q == 1 && P == 0) {
                 const int grp = (int)(kt / MX_GROUP) + 1;
                 nv4_dma_group<4>(d, (uint32_t)grp, grp * MX_GROUP < nk32, sbuf(grp));
             }
+            if constexpr (MODE == MX_OFFRECS && P == 0) {
+                if (qr == 1) {
+                    const int j = (int)(kt / MX_GROUP) + 2;
+                    mx_dma_offrec(d, offa, offb, (uint32_t)j, 16 * j < 15 + kbl, rbuf(g3 == 0 ? 2 : g3 - 1));
+                }
+            }
             mx_mfma_row<P>(fc, acc);
             // the reads after the last slice touch a stale (in-bounds) buffer and go unused
-            mx_read_part<P, GROUPED>(nb, ns, qn, wm, wn, lane, fn);
+            mx_read_part<P, MODE>(nb, ns, qn, spn, wm, wn, lane, fn);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -588,23 +687,32 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (MODE == MX_OFFRECS) g3 = qr == MX_GROUP - 1 ? g3n : g3;
     };
-    if constexpr (GROUPED) {
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    using Q3 = std::integral_constant<int, 3>;
+    using Q4 = std::integral_constant<int, 4>;
+    using Q5 = std::integral_constant<int, 5>;
+    using Q6 = std::integral_constant<int, 6>;
+    using Q7 = std::integral_constant<int, 7>;
+    if constexpr (MODE == MX_RECS) {
         // nk is a multiple of MX_GROUP
         for (int64_t kt = 0; kt < nk; kt += MX_GROUP) {
-            slice(kt + 0, std::integral_constant<int, 0>{}, f0, f1);
-            slice(kt + 1, std::integral_constant<int, 1>{}, f1, f0);
-            slice(kt + 2, std::integral_constant<int, 2>{}, f0, f1);
-            slice(kt + 3, std::integral_constant<int, 3>{}, f1, f0);
-            slice(kt + 4, std::integral_constant<int, 4>{}, f0, f1);
-            slice(kt + 5, std::integral_constant<int, 5>{}, f1, f0);
-            slice(kt + 6, std::integral_constant<int, 6>{}, f0, f1);
-            slice(kt + 7, std::integral_constant<int, 7>{}, f1, f0);
+            slice(kt + 0, Q0{}, f0, f1);
+            slice(kt + 1, Q1{}, f1, f0);
+            slice(kt + 2, Q2{}, f0, f1);
+            slice(kt + 3, Q3{}, f1, f0);
+            slice(kt + 4, Q4{}, f0, f1);
+            slice(kt + 5, Q5{}, f1, f0);
+            slice(kt + 6, Q6{}, f0, f1);
+            slice(kt + 7, Q7{}, f1, f0);
         }
     } else {
         for (int64_t kt = 0; kt < nk; kt += 2) {
-            slice(kt, std::integral_constant<int, 0>{}, f0, f1);
-            if (kt + 1 < nk) slice(kt + 1, std::integral_constant<int, 0>{}, f1, f0);
+            slice(kt, Q0{}, f0, f1);
+            if (kt + 1 < nk) slice(kt + 1, Q0{}, f1, f0);
         }
     }
     wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
@@ -834,7 +942,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, uint8_t* lds, 
     constexpr int ROWS = OUT_F32 ? 64 : 128;     // rows per pass
     constexpr int RS = 128 * ES + 16;            // LDS row stride
     constexpr int CPR = 128 * ES / 16;           // 16-byte chunks per row
-    static_assert(4 * ROWS * RS <= Fmt<2>::LDS && Fmt<2>::LDS == Fmt<1>::LDS, "epilogue staging");
+    static_assert(4 * ROWS * RS <= Fmt<2>::LDS && Fmt<2>::LDS <= Fmt<1>::LDS, "epilogue staging");
     uint8_t* reg = lds + wave * ROWS * RS;
     const int frow = lane & 31, kh = lane >> 5;
     uint8_t* cbase = (uint8_t*)g.c + ((m0 + wm) * g.N + n0 + wn) * ES;
@@ -1165,11 +1273,14 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
             for (int j = 0; j < NVTN; ++j) sb[j] = sbn[j];
         }
     } else if constexpr (FMT == 1) {
-        // 16-byte scale records need K a multiple of 512 and 16-byte aligned scale rows
-        const bool recs = g.K % (MX_GROUP * 64) == 0 && (g.ld / 32) % 16 == 0 &&
+        // scale records need rows 16 bytes apart; aligned ones also K a multiple of 512 and
+        // 16-byte aligned scale tensors
+        const bool rows16 = (g.ld / 32) % 16 == 0;
+        const bool recs = rows16 && g.K % (MX_GROUP * 64) == 0 &&
                           (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) == 0;
-        if (recs) mx_main_loop<true>(g, m0, n0, nk, lds, wm, wn, lane, acc);
-        else mx_main_loop<false>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        if (recs) mx_main_loop<MX_RECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        else if (rows16) mx_main_loop<MX_OFFRECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        else mx_main_loop<MX_SLOTS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     } else {
         nvw_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }

@@ -189,6 +189,41 @@ def test_k_grouped_mxfp8_wgrad():
                   offs, M, N, label="mxfp8 wgrad")
 
 
+def test_k_grouped_mxfp8_offset_records():
+    """K-grouped MXFP8 wgrad whose groups start at many byte offsets inside a 16-byte scale
+    record (starts at multiples of 32 tokens), with odd numbers of K-blocks (the last K slice
+    half outside the group), one group spanning several 8-slice record groups, and NaN scale
+    bytes in the two columns after the last group (a misaligned group, computed as empty),
+    which must not reach the last group's sums."""
+    import oracle
+    kblocks = [3, 17, 1, 37, 5, 2, 41]
+    offs = [0]
+    for n in kblocks:
+        offs.append(offs[-1] + 32 * n)
+    end = offs[-1]
+    offs += [end + 8, 4096]
+    T, M, N = 4096, 320, 192
+    dy = gaussian_bf16((T, M), 1e-3, 81)
+    x = outlier_bf16((T, N), seed=82, mask_seed=83)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.COL)
+    qb = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.COL)
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.COL)
+    rb = oracle.mxfp8_quantize(x, direction=oracle.COL)
+    torch.cuda.synchronize()
+    for q, r, nm in ((qa, ra, "dY"), (qb, rb, "X")):
+        assert_bytes_equal(q["col_codes"], r["col_codes"], nm + " col codes")
+        assert_bytes_equal(q["col_scales"], r["col_scales"], nm + " col scales")
+    nan_cols = slice(end // 32, end // 32 + 2)
+    for t in (qa["col_scales"], qb["col_scales"]):
+        t[:, nan_cols] = 255
+    for r in (ra, rb):
+        r["col_scales"] = np.array(r["col_scales"], copy=True)
+        r["col_scales"][:, nan_cols] = 255
+    run_k_grouped(bsq.FMT_MXFP8, (qa["col_codes"], qa["col_scales"], None), (ra["col_codes"], ra["col_scales"], None),
+                  (qb["col_codes"], qb["col_scales"], None), (rb["col_codes"], rb["col_scales"], None),
+                  offs, M, N, label="mxfp8 offset records")
+
+
 def test_k_grouped_nvfp4_per_group_scales():
     """NVFP4 wgrad operands quantized columnwise per group (each group its own tensor scale)
     and laid out along the token dimension."""
