@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--no-side-figures", action="store_true",
                    help="skip the row-scaled, grouped and linear-layer figures (for counter runs)")
+    p.add_argument("--mx-row-major", action="store_true",
+                   help="MXFP8 GEMM operands in row-major instead of slab layout (for comparison)")
     return p.parse_args()
 
 
@@ -109,7 +111,7 @@ def copy_calibration(iters: int = 5):
 class Step:
     """Buffers and launches of one step; every kernel runs on torch's current stream."""
 
-    def __init__(self, dev):
+    def __init__(self, dev, mx_rows: bool = False):
         import torch
         import block_scaled_precision_nvfp4_amd as bsq
         from synthetic import (SEED_DY, SEED_SIGNS, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16, rht_signs)
@@ -120,6 +122,7 @@ class Step:
         self.signs = rht_signs(SEED_SIGNS).to(dev)
         self.seed = 42
         self.dev = dev
+        self.mx_rows = mx_rows
         self.ev = {}
 
     def _ev(self, name):
@@ -152,11 +155,13 @@ class Step:
         dw = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qdy["col_codes"], qdy["col_scales"], qdy["s_enc"][1:2],
                                   qxc["col_codes"], qxc["col_scales"], qxc["s_enc"][1:2], out_dtype=torch.float32)
         mark("g_wgrad1")
-        # dgrad (MXFP8 backward operands; W from its rowwise-dequantized NVFP4 value)
-        mdy = bsq.mxfp8_quantize(self.dY, direction=bsq.ROW)
-        mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL)
+        # dgrad (MXFP8 backward operands; W from its rowwise-dequantized NVFP4 value), codes in
+        # the GEMM's slab layout unless the row-major layout is asked for
+        lay, fmx = (0, bsq.FMT_MXFP8) if self.mx_rows else (bsq.MX_SLAB, bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB)
+        mdy = bsq.mxfp8_quantize(self.dY, direction=bsq.ROW | lay)
+        mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL | lay)
         mark("g_dgrad0")
-        dx = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["row_codes"], mdy["row_scales"], None,
+        dx = bsq.blockscaled_gemm(fmx, mdy["row_codes"], mdy["row_scales"], None,
                                   mw["col_codes"], mw["col_scales"], None, out_dtype=torch.bfloat16)
         mark("g_dgrad1")
         return y, dw, dx
@@ -300,7 +305,7 @@ def linear_layer_figures(step, iters: int):
 QWEN_TOK, QWEN_N, QWEN_K = 65536, 12288, 4096
 
 
-def qwen3_8b_hybrid_figures(dev, iters: int):
+def qwen3_8b_hybrid_figures(dev, iters: int, mx_rows: bool = False):
     """Side figure outside the step: the per-direction (hybrid) recipe at the Qwen3-8B FFN shape,
     X [65536, 4096], W [12288, 4096], dY [65536, 12288] -- forward NVFP4 rowwise GEMM; MXFP8
     rowwise dY, MXFP8 columnwise dY and X from the bf16 originals and W from its rowwise-
@@ -315,17 +320,18 @@ def qwen3_8b_hybrid_figures(dev, iters: int):
     X = randn((QWEN_TOK, QWEN_K), 1.0, 2234)
     W = randn((QWEN_N, QWEN_K), 0.02, 2235)
     dY = randn((QWEN_TOK, QWEN_N), 1e-4, 2236)
+    lay, fmx = (0, bsq.FMT_MXFP8) if mx_rows else (bsq.MX_SLAB, bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB)
     def run():
         qx = bsq.nvfp4_quantize(X, direction=bsq.ROW)
         qw = bsq.nvfp4_quantize(W, direction=bsq.ROW)
         y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qx["row_codes"], qx["row_scales"], qx["s_enc"][0:1],
                                  qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1])
-        mdy = bsq.mxfp8_quantize(dY, direction=bsq.ROW | bsq.COL)
-        mx = bsq.mxfp8_quantize(X, direction=bsq.COL)
-        mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL)
-        dx = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["row_codes"], mdy["row_scales"], None, mw["col_codes"],
+        mdy = bsq.mxfp8_quantize(dY, direction=bsq.ROW | bsq.COL | lay)
+        mx = bsq.mxfp8_quantize(X, direction=bsq.COL | lay)
+        mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL | lay)
+        dx = bsq.blockscaled_gemm(fmx, mdy["row_codes"], mdy["row_scales"], None, mw["col_codes"],
                                   mw["col_scales"], None)
-        dw = bsq.blockscaled_gemm(bsq.FMT_MXFP8, mdy["col_codes"], mdy["col_scales"], None, mx["col_codes"],
+        dw = bsq.blockscaled_gemm(fmx, mdy["col_codes"], mdy["col_scales"], None, mx["col_codes"],
                                   mx["col_scales"], None, out_dtype=torch.float32)
         return y, dx, dw
     ms = timed_ms(torch, run, iters)
@@ -427,7 +433,7 @@ def main():
     import block_scaled_precision_nvfp4_amd as bsq
     bsq.lib()
     dev = torch.device("cuda:0")
-    step = Step(dev)
+    step = Step(dev, args.mx_row_major)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -458,7 +464,7 @@ def main():
         side = rowscaled_figures(step, max(3, args.steps // 2))
         moe = grouped_figures(step, max(3, args.steps // 2))
         layer = linear_layer_figures(step, max(3, args.steps // 2))
-        qwen = qwen3_8b_hybrid_figures(dev, 3)
+        qwen = qwen3_8b_hybrid_figures(dev, 3, args.mx_row_major)
     fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
     tr = measured_traffic()
     # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
@@ -477,7 +483,8 @@ def main():
         "dtype": "nvfp4/mxfp8 operands, f16/fp8 MFMA, fp32 accumulate", "data": "synthetic",
         "config": {"workload": "quantized linear fwd+wgrad+dgrad step, Llama-3-8B FFN up-proj",
                    "tokens": M_TOK, "in_features": K_IN, "out_features": N_OUT,
-                   "fwd": "NVFP4 row RNE", "wgrad": "NVFP4 col RHT16+SR", "dgrad": "MXFP8 (W from rowwise-dequantized)"},
+                   "fwd": "NVFP4 row RNE", "wgrad": "NVFP4 col RHT16+SR", "dgrad": "MXFP8 (W from rowwise-dequantized)",
+                   "mxfp8_code_layout": "row-major" if args.mx_row_major else "slab"},
         "nvfp4_quant_GBps": round(q_bytes / (q_fwd * 1e-3) / 1e9, 1),
         "nvfp4_quant_frac": {"of_peak_8TBps": round(q_bytes / (q_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                              "of_measured_copy": round(q_bytes / (q_fwd * 1e-3) / 1e9 / peaks["copy_GBps"], 4)},

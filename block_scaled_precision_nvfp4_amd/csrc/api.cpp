@@ -86,11 +86,26 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s
     return launched(bsq::launch_nvfp4_dequantize(codes, scales, s_enc, rows, cols, out, hip_stream), fn);
 }
 
+// MXFP8 cast directions, optionally with BSQ_MX_SLAB (the codes' contraction length, cols for
+// rowwise and rows for columnwise codes, must then be a multiple of 64)
+static int mx_direction_check(const char* fn, int direction, int64_t rows, int64_t cols) {
+    const int dirs = direction & ~BSQ_MX_SLAB;
+    if (dirs < 1 || dirs > 3)
+        return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, optionally with BSQ_MX_SLAB, got %d", fn, direction);
+    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (direction & BSQ_MX_SLAB) {
+        if ((dirs & BSQ_ROW) && cols % 64 != 0)
+            return fail(BSQ_ERR_SHAPE, "%s: rowwise slab codes need cols %% 64 == 0, got %lld", fn, (long long)cols);
+        if ((dirs & BSQ_COL) && rows % 64 != 0)
+            return fail(BSQ_ERR_SHAPE, "%s: columnwise slab codes need rows %% 64 == 0, got %lld", fn, (long long)rows);
+    }
+    return BSQ_OK;
+}
+
 int mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int direction, uint8_t* row_codes,
                    uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
     static const char* fn = "mxfp8_quantize";
-    if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
-    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (const int st = mx_direction_check(fn, direction, rows, cols)) return st;
     if (cols % 8 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
     if ((direction & BSQ_ROW) && cols % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: rowwise needs cols %% 32 == 0, got %lld", fn, (long long)cols);
     if ((direction & BSQ_COL) && rows % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: columnwise needs rows %% 32 == 0, got %lld", fn, (long long)rows);
@@ -108,8 +123,7 @@ int mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, const fl
                            int64_t cols, int direction, uint8_t* row_codes, uint8_t* row_scales,
                            uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
     static const char* fn = "mxfp8_requantize_nvfp4";
-    if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
-    if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
+    if (const int st = mx_direction_check(fn, direction, rows, cols)) return st;
     if (cols % 16 != 0) return fail(BSQ_ERR_SHAPE, "%s: cols (%lld) must be a multiple of 16", fn, (long long)cols);
     if ((direction & BSQ_ROW) && cols % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: rowwise needs cols %% 32 == 0, got %lld", fn, (long long)cols);
     if ((direction & BSQ_COL) && rows % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: columnwise needs rows %% 32 == 0, got %lld", fn, (long long)rows);
@@ -159,10 +173,13 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
                      void* c, int c_dtype, void* hip_stream) {
     static const char* fn = "blockscaled_gemm";
     const int a_rows = (fmt & BSQ_FMT_A_ROWSCALED) != 0, b_rows = (fmt & BSQ_FMT_B_ROWSCALED) != 0;
-    const int flags = fmt & (BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
-    fmt &= ~(BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
-    if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), optionally with the row-scaled flags, got %d", fn, fmt | flags);
-    if (flags && fmt != BSQ_FMT_NVFP4) return fail(BSQ_ERR_ARG, "%s: the row-scaled flags apply to NVFP4 operands only", fn);
+    const int slab = (fmt & BSQ_FMT_MX_SLAB) != 0;
+    const int flags = fmt & (BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED | BSQ_FMT_MX_SLAB);
+    fmt &= ~(BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED | BSQ_FMT_MX_SLAB);
+    if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), optionally with the row-scaled or slab flags, got %d", fn, fmt | flags);
+    if ((a_rows || b_rows) && fmt != BSQ_FMT_NVFP4) return fail(BSQ_ERR_ARG, "%s: the row-scaled flags apply to NVFP4 operands only", fn);
+    if (slab && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: BSQ_FMT_MX_SLAB applies to MXFP8 operands only", fn);
+    if (slab && K % 512 != 0) return fail(BSQ_ERR_SHAPE, "%s: slab operands need K %% 512 == 0, got %lld", fn, (long long)K);
     if (c_dtype != BSQ_OUT_BF16 && c_dtype != BSQ_OUT_F32) return fail(BSQ_ERR_ARG, "%s: c_dtype must be 0 (bf16) or 1 (f32), got %d", fn, c_dtype);
     if (M < 0 || N < 0 || K < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape", fn);
     if (K % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
@@ -175,7 +192,7 @@ int blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_
     if (misaligned(a_codes) || misaligned(b_codes) || misaligned(c) || misaligned(a_scales) || misaligned(b_scales))
         return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     return launched(bsq::launch_blockscaled_gemm(fmt, M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales,
-                                                 b_s_enc, a_rows, b_rows, c, c_dtype, hip_stream), fn);
+                                                 b_s_enc, a_rows, b_rows, c, c_dtype, hip_stream, slab), fn);
 }
 
 int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* offsets, int64_t M, int64_t N,

@@ -59,6 +59,7 @@ struct GemmArgs {
     void* c;
     int a_rows, b_rows;   // the operand's tensor scale is per row (float[M] / float[N])
     int64_t ld;           // elements between consecutive rows of A and of B (K unless grouped along K)
+    int slab;             // MXFP8 codes of both operands in the slab layout (K a multiple of 512)
 };
 
 // FMT 0: NVFP4, 8 waves of 128 x 64, register-staged (any K); FMT 1: MXFP8, 4 waves of 128 x
@@ -333,7 +334,11 @@ struct MxFrag {
 //  - per slice (MX_SLOTS; any other row pitch): one dword slot per (row, K-block) after the
 //    codes of each stage, [operand][256 rows][2 slots], holding the byte in its low 8 bits
 //    (a byte DMA fills one dword slot per lane).
-constexpr int MX_SLOTS = 0, MX_RECS = 1, MX_OFFRECS = 2;
+// MX_SLAB is MX_RECS on codes in the slab layout: a 256-row band of an operand (one tile's
+// rows) stored slice by slice, [K/64][n rows][64 B], so that each slice of the band is one
+// contiguous block that the DMAs read whole (row-major codes come as 64-byte pieces of rows
+// 2 KiB and more apart, which fill LDS at about 60 % of the rate).
+constexpr int MX_SLOTS = 0, MX_RECS = 1, MX_OFFRECS = 2, MX_SLAB = 3;
 constexpr int MX_CODES = 2 * GBM * ROWB;                  // 32 KiB
 constexpr int MX_STAGE_SLOTS = MX_CODES + 2 * GBM * 2 * 4;  // 36 KiB
 constexpr int MX_GROUP = 8;                                // slices per grouped scale record
@@ -395,6 +400,7 @@ struct MxDma {
     RsrcWords o;
     uint32_t rowbytes, sstride;   // code and scale bytes between consecutive rows
     uint32_t kbytes, kblocks;     // code and scale bytes of a row's K elements
+    uint32_t slab_a, slab_b;      // slab layout: bytes of one slice of the tile's A / B rows
     int wave, lane;
 };
 
@@ -464,6 +470,25 @@ __device__ __forceinline__ void mx_dma_offrec(const MxDma& d, uint32_t offa, uin
     dma_b128(sized(d.o.bs, live), lds_addr(sbuf + GBM * 16 + 64 * d.wave * 16), offb + 16u * j, 0u);
 }
 
+// Slab layout: the resource of slice k's block (`bytes` long, none when not live), whose rows
+// sit 64 bytes apart; rows past the tile's fall outside it.
+__device__ __forceinline__ u32x4s slab_rsrc(u32x4s r, uint32_t k, uint32_t bytes, bool live) {
+    const uint64_t base = (((uint64_t)(r[1] & 0xFFFFu) << 32) | r[0]) + (uint64_t)k * bytes;
+    r[0] = (uint32_t)base;
+    r[1] = (r[1] & 0xFFFF0000u) | ((uint32_t)(base >> 32) & 0xFFFFu);
+    r[2] = live ? bytes : 0u;
+    return r;
+}
+
+template <int P>
+__device__ __forceinline__ void mx_slab_codes(const MxDma& d, uint32_t k, bool live, uint8_t* buf) {
+    const int r0 = 64 * P + 16 * d.wave;
+    const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
+    const uint32_t off = (uint32_t)r * 64u + 16u * c;
+    dma_b128(slab_rsrc(d.o.a, k, d.slab_a, live), lds_addr(buf + r0 * ROWB), off, 0u);
+    dma_b128(slab_rsrc(d.o.b, k, d.slab_b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off, 0u);
+}
+
 template <int EPB, int BLK>
 __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
     MxDma d;
@@ -477,6 +502,8 @@ __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t
     d.sstride = (uint32_t)sb;
     d.kbytes = (uint32_t)(g.K / EPB);
     d.kblocks = (uint32_t)(g.K / BLK);
+    d.slab_a = (uint32_t)ra * 64u;
+    d.slab_b = (uint32_t)rbn * 64u;
     d.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     d.lane = lane;
     return d;
@@ -505,7 +532,7 @@ __device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* 
     lo = *(const uint4*)(sB + swz(rb, kh));
     hi = *(const uint4*)(sB + swz(rb, 2 + kh));
     f.b[P] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    if constexpr (MODE == MX_RECS) {
+    if constexpr (MODE == MX_RECS || MODE == MX_SLAB) {
         f.as[P] = sbuf[ra * 16 + 2 * q + kh];
         f.bs[P] = sbuf[GBM * 16 + rb * 16 + 2 * q + kh];
     } else if constexpr (MODE == MX_OFFRECS) {
@@ -555,6 +582,7 @@ template <int MODE>
 __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
                                              int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
     constexpr bool REC = MODE != MX_SLOTS;
+    constexpr bool ALIGNED = MODE == MX_RECS || MODE == MX_SLAB;   // aligned records, nk % MX_GROUP == 0
     constexpr int DC = 8;                    // code DMAs per slice per lane
     constexpr int DS = REC ? 0 : 4;          // per-slice scale DMAs
     constexpr int DG = 2;                    // scale-record DMAs (every MX_GROUP slices)
@@ -612,6 +640,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     auto dma_part = [&](auto p_c, int64_t k, bool live, uint8_t* b) {
         constexpr int P = decltype(p_c)::value;
         if constexpr (MODE == MX_RECS) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
+        else if constexpr (MODE == MX_SLAB) mx_slab_codes<P>(d, (uint32_t)k, live, b);
         else mx_dma_codes<P>(d, k * 64, live, b);
     };
     auto dma_slice = [&](int64_t k) {
@@ -623,7 +652,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
             mx_dma_slots<1>(d, k * 64, live, b);
         }
     };
-    if constexpr (MODE == MX_RECS) nv4_dma_group<4>(d, 0, true, sbuf(0));
+    if constexpr (ALIGNED) nv4_dma_group<4>(d, 0, true, sbuf(0));
     if constexpr (MODE == MX_OFFRECS) {
         mx_dma_offrec(d, offa, offb, 0, true, rbuf(0));
         mx_dma_offrec(d, offa, offb, 1, 16 < 15 + kbl, rbuf(1));
@@ -665,7 +694,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
             constexpr int P = decltype(p_c)::value;
             dma_part(p_c, kd, live, db);
             if constexpr (!REC && P < 2) mx_dma_slots<P>(d, kd * 64, live, db);
-            if constexpr (MODE == MX_RECS && Q == 1 && P == 0) {
+            if constexpr (ALIGNED && Q == 1 && P == 0) {
                 const int grp = (int)(kt / MX_GROUP) + 1;
                 nv4_dma_group<4>(d, (uint32_t)grp, grp * MX_GROUP < nk32, sbuf(grp));
             }
@@ -697,7 +726,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     using Q5 = std::integral_constant<int, 5>;
     using Q6 = std::integral_constant<int, 6>;
     using Q7 = std::integral_constant<int, 7>;
-    if constexpr (MODE == MX_RECS) {
+    if constexpr (ALIGNED) {
         // nk is a multiple of MX_GROUP
         for (int64_t kt = 0; kt < nk; kt += MX_GROUP) {
             slice(kt + 0, Q0{}, f0, f1);
@@ -1278,7 +1307,8 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         const bool rows16 = (g.ld / 32) % 16 == 0;
         const bool recs = rows16 && g.K % (MX_GROUP * 64) == 0 &&
                           (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) == 0;
-        if (recs) mx_main_loop<MX_RECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        if (recs && g.slab) mx_main_loop<MX_SLAB>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        else if (recs) mx_main_loop<MX_RECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (rows16) mx_main_loop<MX_OFFRECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else mx_main_loop<MX_SLOTS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     } else {
@@ -1380,9 +1410,9 @@ static int launch_fmt(int fmt, int c_dtype, const GemmArgs& g, const GroupArgs& 
 int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                             const uint8_t* a_scales, const float* a_s_enc, const uint8_t* b_codes,
                             const uint8_t* b_scales, const float* b_s_enc, int a_rows, int b_rows, void* c,
-                            int c_dtype, void* hip_stream) {
+                            int c_dtype, void* hip_stream, int slab) {
     if (M == 0 || N == 0) return 0;
-    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K};
+    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K, slab};
     const int64_t tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
     return launch_fmt<0>(fmt, c_dtype, g, GroupArgs{nullptr, 0, 0}, tiles, (hipStream_t)hip_stream);
 }

@@ -414,7 +414,17 @@ struct MxArgs {
     uint8_t* row_scales;
     uint8_t* col_codes;
     uint8_t* col_scales;
+    int slab;   // codes in the slab layout (see slab_offset)
 };
+
+// Byte offset of code (r, k) of a [rows][K] code matrix in the slab layout: rows in bands of
+// 256 (the last band holds the rest), band b at byte 256 b K, holding its n rows as K/64
+// consecutive slabs of n x 64 bytes (K a multiple of 64).  A GEMM tile's rows are one band,
+// and each 64-element K slice of them one contiguous block.
+__device__ __forceinline__ int64_t slab_offset(int64_t r, int64_t k, int64_t rows, int64_t K) {
+    const int64_t b = r >> 8, left = rows - (b << 8), n = left < 256 ? left : 256;
+    return (b << 8) * K + (k >> 6) * n * 64 + (r & 255) * 64 + (k & 63);
+}
 
 // SRC 0: bf16 input; SRC 1: the rowwise-dequantized value of an NVFP4 tensor.
 template <int DIRS, int SRC = 0>
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
                 hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
             }
             if (colok && r < R) {
-                *(uint2*)(a.row_codes + r * C + t.c0) = make_uint2(lo, hi);
+                *(uint2*)(a.row_codes + (a.slab ? slab_offset(r, t.c0, R, C) : r * C + t.c0)) = make_uint2(lo, hi);
                 if ((t.cc & 3) == 0) a.row_scales[r * (C / 32) + t.c0 / 32] = (uint8_t)sb;
             }
         });
@@ -485,7 +495,7 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
             const int col = idx >> 4, rbk = idx & 15;
             const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
             if (c < C && r < R) {
-                *(uint4*)(a.col_codes + c * R + r) = lds_codes[col][rbk ^ (col >> 3)];
+                *(uint4*)(a.col_codes + (a.slab ? slab_offset(c, r, C, R) : c * R + r)) = lds_codes[col][rbk ^ (col >> 3)];
                 if ((rbk & 1) == 0) a.col_scales[c * (R / 32) + r / 32] = lds_sc[col][(rbk >> 1) ^ ((col >> 3) & 7)];
             }
         }
@@ -997,9 +1007,13 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
     if (R == 0 || C == 0) return 0;
     hipStream_t s = (hipStream_t)hip_stream;
-    MxArgs a{(const uint16_t*)x, nullptr, nullptr, nullptr, R, C, row_codes, row_scales, col_codes, col_scales};
+    const int slab = (direction & 4) != 0;
+    direction &= 3;
+    MxArgs a{(const uint16_t*)x, nullptr, nullptr, nullptr, R, C, row_codes, row_scales, col_codes, col_scales, slab};
     const dim3 g = tile_grid(R, C);
-    if (direction == 1) {
+    if (direction == 1 && slab) {
+        hipLaunchKernelGGL(mxfp8_kernel<1>, g, dim3(NTHREADS), 0, s, a);
+    } else if (direction == 1) {
         const int64_t n16 = R * C / 8;
         hipLaunchKernelGGL(mxfp8_row_linear_kernel, dim3(lin_grid(n16)), dim3(LIN_THREADS), 0, s, (const uint4*)x, n16,
                            (uint2*)row_codes, row_scales);
@@ -1013,7 +1027,9 @@ int launch_mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, c
                                   uint8_t* col_codes, uint8_t* col_scales, void* hip_stream) {
     if (R == 0 || C == 0) return 0;
     hipStream_t s = (hipStream_t)hip_stream;
-    MxArgs a{nullptr, codes, scales, s_enc, R, C, row_codes, row_scales, col_codes, col_scales};
+    const int slab = (direction & 4) != 0;
+    direction &= 3;
+    MxArgs a{nullptr, codes, scales, s_enc, R, C, row_codes, row_scales, col_codes, col_scales, slab};
     const dim3 g = tile_grid(R, C);
     if (direction == 1) hipLaunchKernelGGL((mxfp8_kernel<1, 1>), g, dim3(NTHREADS), 0, s, a);
     else if (direction == 2) hipLaunchKernelGGL((mxfp8_kernel<2, 1>), g, dim3(NTHREADS), 0, s, a);

@@ -51,6 +51,8 @@ enum bsq_status {
 /* direction bitmask: which quantizations to produce (the usage flags of a quantizer). */
 #define BSQ_ROW 1
 #define BSQ_COL 2
+/* OR'ed into an MXFP8 cast's direction: the codes it writes are in the slab layout */
+#define BSQ_MX_SLAB 4
 /* element rounding */
 #define BSQ_RNE 0
 #define BSQ_SR 1
@@ -60,6 +62,19 @@ enum bsq_status {
 /* flags OR'ed into BSQ_FMT_NVFP4: that operand's tensor scale is one float per row */
 #define BSQ_FMT_A_ROWSCALED 0x10
 #define BSQ_FMT_B_ROWSCALED 0x20
+/* flag OR'ed into BSQ_FMT_MXFP8: both operands' codes are in the slab layout */
+#define BSQ_FMT_MX_SLAB 0x40
+
+/*
+ * The slab layout of an MXFP8 code matrix [rows][K] (K % 64 == 0): a layout of the same
+ * rows * K bytes for the GEMM, not part of the format.  Rows are taken in bands of 256 (the
+ * last band holds the remaining n = rows - 256 b); band b starts at byte 256 b K and holds
+ * its n rows as K/64 consecutive slabs of n x 64 bytes, so byte k of row r is at
+ *   256 b K + (k / 64) n 64 + (r - 256 b) 64 + k % 64,   b = r / 256.
+ * A GEMM tile's rows are one band and each 64-element K slice of them one contiguous
+ * block, which the GEMM's loads fill LDS from at about 1.6 times the rate of 64-byte pieces
+ * of row-major rows.  Scales keep their row-major layout.
+ */
 /* grouped GEMM modes */
 #define BSQ_GROUP_M 1   /* groups split the rows of A and C (per-expert fprop / dgrad) */
 #define BSQ_GROUP_K 2   /* groups split the contraction (per-expert wgrad)             */
@@ -167,7 +182,9 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s
  * Arguments: x [rows][cols] bf16; BSQ_ROW needs cols % 32 == 0, BSQ_COL needs
  * rows % 32 == 0, always cols % 8 == 0.  row_codes [rows][cols], row_scales
  * [rows][cols/32]; col_codes [cols][rows], col_scales [cols][rows/32] (required
- * iff the direction is requested).
+ * iff the direction is requested).  direction | BSQ_MX_SLAB writes the requested codes in
+ * the slab layout (rowwise: cols % 64 == 0; columnwise: rows % 64 == 0), the scales as
+ * before.
  */
 int mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int direction,
                    uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
@@ -218,6 +235,9 @@ int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t*
  *       with two it is the fp32 product of 1/S_a[m] and 1/S_b[n], each so rounded.
  *   fmt BSQ_FMT_MXFP8: a_codes [M][K] (E4M3), a_scales [M][K/32] (E8M0); s_enc
  *       pointers are ignored (may be NULL); alpha = 1.  K % 32 == 0.
+ *   fmt BSQ_FMT_MXFP8 | BSQ_FMT_MX_SLAB: a_codes and b_codes in the slab layout (as an
+ *       MXFP8 cast with BSQ_MX_SLAB writes them), scales as for BSQ_FMT_MXFP8; K % 512 == 0,
+ *       else BSQ_ERR_SHAPE.  Not accepted by blockscaled_grouped_gemm.
  *   c [M][N], c_dtype BSQ_OUT_BF16 (RNE) or BSQ_OUT_F32.
  *   M, N >= 0 arbitrary; M, N or K == 0 are valid (K == 0 writes zeros).  K is below 2^24
  *   (NVFP4) or 2^23 (MXFP8), so that a 256-row operand tile stays below 2 GiB.

@@ -81,7 +81,14 @@ def test_mxfp8_quantize_validation(L):
     f = L.mxfp8_quantize
     assert f(FAKE, 64, 48, 1, FAKE, FAKE, None, None, None) == 2 and "cols % 32" in last(L)
     assert f(FAKE, 48, 64, 2, None, None, FAKE, FAKE, None) == 2 and "rows % 32" in last(L)
-    assert f(FAKE, 64, 64, 5, FAKE, FAKE, None, None, None) == 3
+    assert f(FAKE, 64, 64, 8, FAKE, FAKE, None, None, None) == 3 and "direction" in last(L)
+    assert f(FAKE, 64, 64, 4, FAKE, FAKE, None, None, None) == 3 and "direction" in last(L)
+    # the slab layout needs whole 64-byte slices along the codes' contraction dimension
+    assert f(FAKE, 64, 96, 1 | 4, FAKE, FAKE, None, None, None) == 2 and "cols % 64" in last(L)
+    assert f(FAKE, 96, 64, 2 | 4, None, None, FAKE, FAKE, None) == 2 and "rows % 64" in last(L)
+    # rowwise slab codes leave rows free (this call gets as far as the NULL input)
+    assert f(None, 96, 64, 1 | 4, FAKE, FAKE, None, None, None) == 1 and "x is NULL" in last(L)
+    assert f(FAKE, 0, 64, 2 | 4, None, None, FAKE, FAKE, None) == 0
     assert f(None, 64, 64, 1, FAKE, FAKE, None, None, None) == 1
     assert f(FAKE, 64, 64, 2, FAKE, FAKE, None, FAKE, None) == 1
     assert f(FAKE + 4, 64, 64, 1, FAKE, FAKE, None, None, None) == 6
@@ -98,6 +105,8 @@ def test_mxfp8_requantize_validation(L):
     assert f(FAKE, FAKE, FAKE, 64, 64, 2, None, None, None, FAKE, None) == 1 and "columnwise outputs" in last(L)
     assert f(FAKE + 4, FAKE, FAKE, 64, 64, 2, None, None, FAKE, FAKE, None) == 6
     assert f(FAKE, FAKE, FAKE, 0, 64, 2, None, None, FAKE, FAKE, None) == 0
+    assert f(FAKE, FAKE, FAKE, 64, 96, 1 | 4, FAKE, FAKE, None, None, None) == 2 and "cols % 64" in last(L)
+    assert f(FAKE, FAKE, FAKE, 96, 64, 2 | 4, None, None, FAKE, FAKE, None) == 2 and "rows % 64" in last(L)
 
 
 def test_rht_apply_validation(L):
@@ -138,6 +147,18 @@ def test_gemm_rowscaled_flag_validation(L):
     assert f(0x40, 128, 128, 64, *args, 0, None) == 3
     assert f(0x10 | 0x20, 128, 128, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
     assert f(0x30, 0, 128, 64, *args, 0, None) == 0
+
+
+def test_gemm_slab_flag_validation(L):
+    f = L.blockscaled_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert f(0 | 0x40, 128, 128, 512, *args, 0, None) == 3 and "MXFP8 operands only" in last(L)
+    assert f(1 | 0x40, 128, 128, 1056, *args, 0, None) == 2 and "K % 512" in last(L)
+    assert f(1 | 0x40 | 0x10, 128, 128, 512, *args, 0, None) == 3 and "NVFP4 operands only" in last(L)
+    assert f(1 | 0x40, 128, 128, 512, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 6
+    assert f(1 | 0x40, 0, 128, 512, *args, 0, None) == 0
+    # not a grouped-GEMM flag
+    assert L.blockscaled_grouped_gemm(1 | 0x40, 1, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3
 
 
 def gg(L, fmt=0, mode=1, groups=4, offs=FAKE, M=256, N=256, K=256, ac=FAKE, as_=FAKE, sa=FAKE, bc=FAKE, bs=FAKE,

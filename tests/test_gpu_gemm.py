@@ -276,6 +276,84 @@ def test_fused_requantize_matches_chain(shape, direction):
             assert torch.equal(f[key + part], m[key + part]), "fused vs two-call chain " + key + part
 
 
+def from_slab(t: torch.Tensor, rows: int, K: int) -> np.ndarray:
+    """The row-major [rows][K] codes held by a buffer in the slab layout: rows in bands of 256,
+    band b from byte 256 b K holding its n rows as K/64 slabs of n x 64 bytes."""
+    flat = t.cpu().numpy().reshape(-1)
+    assert flat.size == rows * K
+    out = np.empty((rows, K), np.uint8)
+    for b0 in range(0, rows, 256):
+        n = min(256, rows - b0)
+        out[b0:b0 + n] = flat[b0 * K:(b0 + n) * K].reshape(K // 64, n, 64).transpose(1, 0, 2).reshape(n, K)
+    return out
+
+
+def slab_dgrad_check(T, N_out, N_in, out_dtype, rows=None, cols=None, label=""):
+    """dX[T, N_in] = dY W as the MXFP8 dgrad with slab-layout codes: dY rowwise (MX_SLAB) and
+    W columnwise from its NVFP4 rowwise codes (fused requantize, MX_SLAB).  The slab buffers
+    must hold exactly the oracle's codes, and the GEMM must match the oracle's GEMM."""
+    import oracle
+    note("mxfp8 slab dgrad %s T=%d out=%d in=%d %s" % (label, T, N_out, N_in, out_dtype))
+    dy = gaussian_bf16((T, N_out), STD_DY, SEED_DY)
+    W = gaussian_bf16((N_out, N_in), STD_W, SEED_W)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.ROW | bsq.MX_SLAB)
+    qw = bsq.nvfp4_quantize(W.to(DEV), direction=bsq.ROW)
+    qb = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1],
+                                    direction=bsq.COL | bsq.MX_SLAB)
+    y = bsq.blockscaled_gemm(bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB, qa["row_codes"], qa["row_scales"], None,
+                             qb["col_codes"], qb["col_scales"], None, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.ROW)
+    rw = oracle.nvfp4_quantize(W, direction=oracle.ROW)
+    rb = oracle.mxfp8_quantize(oracle.nvfp4_dequantize(rw["row_codes"], rw["row_scales"], float(rw["s_enc"][0])),
+                               direction=oracle.COL)
+    ga, gb = from_slab(qa["row_codes"], T, N_out), from_slab(qb["col_codes"], N_in, N_out)
+    assert np.array_equal(ga, ra["row_codes"]), "dY slab codes"
+    assert np.array_equal(gb, rb["col_codes"]), "W slab codes"
+    assert_bytes_equal(qa["row_scales"], ra["row_scales"], "dY scales")
+    assert_bytes_equal(qb["col_scales"], rb["col_scales"], "W scales")
+    ref = oracle.blockscaled_gemm(oracle.FMT_MXFP8, ra["row_codes"], ra["row_scales"], 1.0,
+                                  rb["col_codes"], rb["col_scales"], 1.0, rows=rows, cols=cols)
+    yc = y.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
+    err = rel_fro(yc, want)
+    note("  rel_fro = %.3e" % err)
+    assert err <= GEMM_TOL, err
+
+
+@pytest.mark.parametrize("shape", [(320, 448), (64, 64), (1088, 128)])
+def test_mxfp8_cast_slab_layout(shape):
+    """mxfp8_quantize with MX_SLAB in both directions: the slab buffers hold exactly the
+    oracle's row-major codes (ragged last bands, a single short band), scales unchanged."""
+    import oracle
+    R, C = shape
+    note("mxfp8 slab cast shape=%s" % (shape,))
+    x = outlier_bf16(shape, seed=R + 7, mask_seed=C + 9)
+    q = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.ROW | bsq.COL | bsq.MX_SLAB)
+    torch.cuda.synchronize()
+    r = oracle.mxfp8_quantize(x, direction=oracle.ROW | oracle.COL)
+    assert np.array_equal(from_slab(q["row_codes"], R, C), r["row_codes"]), "row codes"
+    assert np.array_equal(from_slab(q["col_codes"], C, R), r["col_codes"]), "col codes"
+    assert_bytes_equal(q["row_scales"], r["row_scales"], "row scales")
+    assert_bytes_equal(q["col_scales"], r["col_scales"], "col scales")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mxfp8_slab_operands_ragged(out_dtype):
+    """Slab-layout MXFP8 dgrad with a ragged last band in both operands (300 tokens, 320
+    input features) and K = 1536 (three 8-slice scale groups)."""
+    slab_dgrad_check(300, 1536, 320, out_dtype, label="ragged")
+
+
+def test_mxfp8_slab_dgrad_llama3_8b_sampled():
+    """The slab-layout MXFP8 dgrad at the Llama-3-8B FFN shape, dX[16384, 4096] = dY W with
+    K = 14336, as the bench launches it; 96 x 64 sampled outputs."""
+    slab_dgrad_check(16384, 14336, 4096, torch.bfloat16, rows=_sample(16384, 96, 11), cols=_sample(4096, 64, 12),
+                     label="llama3-8b")
+
+
 @pytest.mark.parametrize("factor", [1e-34, 1e-25, 1e30, 5e35])
 def test_fused_requantize_extreme_tensor_scales(factor):
     """Inputs scaled so that the per-block quotients leave the normal range (tiny tensor amax
