@@ -827,10 +827,14 @@ __global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4
     }
 }
 
-// Rowwise MXFP8 cast: unit u = quarter u%4 of block u/4.
+// Rowwise MXFP8 cast: unit u = quarter u%4 of block u/4 (elements 8u..8u+7 in row-major
+// order).  SLAB writes the codes in the slab layout of a [R][C] matrix: the unit's row is
+// u / (C/8), from a binary64 estimate (exact to within one for u < 2^52) corrected exactly.
+template <bool SLAB>
 __global__ __launch_bounds__(LIN_THREADS) void mxfp8_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
                                                                        uint2* __restrict__ codes,
-                                                                       uint8_t* __restrict__ scales) {
+                                                                       uint8_t* __restrict__ scales, int64_t R,
+                                                                       int64_t C, double inv_c8) {
     int64_t first, stride;
     lin_range(n16, first, stride);
     for (int64_t base = first; base < n16; base += stride) {
@@ -858,7 +862,15 @@ __global__ __launch_bounds__(LIN_THREADS) void mxfp8_row_linear_kernel(const uin
                 hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
             }
             if (u < n16) {
-                codes[u] = make_uint2(lo, hi);
+                int64_t at = u;
+                if constexpr (SLAB) {
+                    const int64_t c8 = C >> 3;
+                    int64_t r = (int64_t)((double)u * inv_c8);
+                    if (r * c8 > u) --r;
+                    else if ((r + 1) * c8 <= u) ++r;
+                    at = slab_offset(r, (u - r * c8) << 3, R, C) >> 3;
+                }
+                codes[at] = make_uint2(lo, hi);
                 if ((u & 3) == 0) scales[u >> 2] = (uint8_t)sb;
             }
         }
@@ -1011,12 +1023,15 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
     direction &= 3;
     MxArgs a{(const uint16_t*)x, nullptr, nullptr, nullptr, R, C, row_codes, row_scales, col_codes, col_scales, slab};
     const dim3 g = tile_grid(R, C);
-    if (direction == 1 && slab) {
-        hipLaunchKernelGGL(mxfp8_kernel<1>, g, dim3(NTHREADS), 0, s, a);
-    } else if (direction == 1) {
+    if (direction == 1) {
         const int64_t n16 = R * C / 8;
-        hipLaunchKernelGGL(mxfp8_row_linear_kernel, dim3(lin_grid(n16)), dim3(LIN_THREADS), 0, s, (const uint4*)x, n16,
-                           (uint2*)row_codes, row_scales);
+        const double inv_c8 = 8.0 / (double)C;
+        if (slab)
+            hipLaunchKernelGGL(mxfp8_row_linear_kernel<true>, dim3(lin_grid(n16)), dim3(LIN_THREADS), 0, s,
+                               (const uint4*)x, n16, (uint2*)row_codes, row_scales, R, C, inv_c8);
+        else
+            hipLaunchKernelGGL(mxfp8_row_linear_kernel<false>, dim3(lin_grid(n16)), dim3(LIN_THREADS), 0, s,
+                               (const uint4*)x, n16, (uint2*)row_codes, row_scales, R, C, inv_c8);
     } else if (direction == 2) hipLaunchKernelGGL(mxfp8_kernel<2>, g, dim3(NTHREADS), 0, s, a);
     else hipLaunchKernelGGL(mxfp8_kernel<3>, g, dim3(NTHREADS), 0, s, a);
     return (int)hipGetLastError();

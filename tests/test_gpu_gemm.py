@@ -325,8 +325,9 @@ def slab_dgrad_check(T, N_out, N_in, out_dtype, rows=None, cols=None, label=""):
 
 @pytest.mark.parametrize("shape", [(320, 448), (64, 64), (1088, 128)])
 def test_mxfp8_cast_slab_layout(shape):
-    """mxfp8_quantize with MX_SLAB in both directions: the slab buffers hold exactly the
-    oracle's row-major codes (ragged last bands, a single short band), scales unchanged."""
+    """mxfp8_quantize with MX_SLAB in both directions and rowwise alone: the slab buffers hold
+    exactly the oracle's row-major codes (ragged last bands, a single short band), scales
+    unchanged."""
     import oracle
     R, C = shape
     note("mxfp8 slab cast shape=%s" % (shape,))
@@ -338,6 +339,11 @@ def test_mxfp8_cast_slab_layout(shape):
     assert np.array_equal(from_slab(q["col_codes"], C, R), r["col_codes"]), "col codes"
     assert_bytes_equal(q["row_scales"], r["row_scales"], "row scales")
     assert_bytes_equal(q["col_scales"], r["col_scales"], "col scales")
+    # rowwise alone takes the streaming kernel
+    q1 = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.ROW | bsq.MX_SLAB)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_slab(q1["row_codes"], R, C), r["row_codes"]), "row codes (rowwise only)"
+    assert_bytes_equal(q1["row_scales"], r["row_scales"], "row scales (rowwise only)")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
