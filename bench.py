@@ -65,11 +65,16 @@ GEMM_SOURCES = ("block_scaled_precision_nvfp4_amd/csrc/gemm.hip",
 TRAFFIC_SUMMARY = "profiles/gemm_nvfp4_fwd_llama3_8b_hbm_traffic.md"
 
 
-def gemm_source_hash() -> str:
+def gemm_source_hash(root: str = ROOT) -> str:
+    """SHA-256 of the GEMM kernel sources with comments and blank lines dropped: counters taken
+    on the same code stay valid across comment edits."""
     h = hashlib.sha256()
     for rel in GEMM_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -20,18 +20,22 @@
 // K-elements 32+16g..32+16g+15; the scale of K-block 0 (elements 0-31) comes from lanes
 // 0-31, that of K-block 1 from lanes 32-63.
 //
-// Tiling: a workgroup computes a 256 x 256 tile of C.  NVFP4 runs 8 waves (two per SIMD),
-// each a 128 x 64 block of 4 x 2 MFMA tiles of 32 x 32 (128 fp32 accumulators per lane), so
-// that one wave's dequantization overlaps the other's MFMAs; MXFP8 runs 4 waves of 128 x
-// 128 (4 x 4 tiles, 256 accumulators).  Each K slice (128 elements for NVFP4, 64 for MXFP8)
-// of both operands is 64 bytes of codes per row, loaded with buffer loads (the hardware
-// range check zero-fills rows beyond M or N, an out-of-range offset the K tail) into
-// registers and stored to a ring of 3 LDS buffers, two slices ahead of its use, with one
-// barrier per slice.  16-byte chunks are XOR-swizzled by row for conflict-free fragment
-// reads.  Inside a slice the operands of the next MFMA step are read from LDS (and, for
-// NVFP4, dequantized) while the current step's MFMAs issue.  Workgroups are renumbered so
-// that each of the 8 XCDs (which take workgroups round-robin) works on a contiguous band of
-// output tiles and reuses operand rows from its own L2.
+// Tiling: a workgroup computes a 256 x 256 tile of C.  Each K slice (128 elements for NVFP4,
+// 64 for MXFP8) of both operands is 64 bytes of codes per row.  The NVFP4 kernel for K a
+// multiple of 256 and the MXFP8 kernel run 4 waves of 128 x 128 (4 x 4 MFMA tiles of 32 x 32,
+// 256 fp32 accumulators per lane) and move each slice from memory straight into a ring of 4
+// LDS stages by LDS DMA, three slices ahead of its use, with one barrier per slice; their
+// scales come as 16-byte records of a row's scale bytes (MXFP8 also per-slice bytes where
+// rows are not 16 bytes apart), and MXFP8 codes may come in the slab layout, where each slice
+// of a tile's rows is one contiguous block.  The register-staged NVFP4 kernel (other K, and
+// K-grouped NVFP4) runs 8 waves (two per SIMD) of 128 x 64, so that one wave's dequantization
+// overlaps the other's MFMAs, and stages slices through registers into 3 LDS buffers.  The
+// buffer loads' range check zero-fills rows beyond M or N, and an out-of-range offset the K
+// tail.  16-byte chunks are XOR-swizzled by row for conflict-free fragment reads.  Inside a
+// slice the operands of the next MFMA step are read from LDS (and, for NVFP4, dequantized)
+// while the current step's MFMAs issue.  Workgroups are renumbered so that each of the 8 XCDs
+// (which take workgroups round-robin) works on a contiguous band of output tiles and reuses
+// operand rows from its own L2.
 #include <mutex>
 #include <set>
 
