@@ -156,6 +156,45 @@ def test_largest_k(fmt):
     assert err <= GEMM_TOL, err
 
 
+def test_largest_k_slab():
+    """Slab-layout MXFP8 operands at the largest K the C ABI accepts (2^23 - 512): slice k's
+    block starts k * n * 64 bytes into a band, just under 2^31 for the last slice of a full
+    band, and A has a ragged second band (300 rows).  Codes +1, -1 or 0 with A's scales 2^0
+    and B's 2^0 or 2^-1 keep every partial sum a multiple of 1/2 below 2^23, exact in fp32
+    whatever the summation order, so the fp32 output must equal the oracle exactly: a code
+    or scale read from the wrong place would show.  Sampled outputs."""
+    import oracle
+    K, M, N = (1 << 23) - 512, 300, 256
+    rng = np.random.default_rng(131)
+    lut = np.array([0x38, 0xB8, 0x00], np.uint8)   # E4M3 +1, -1, 0
+    ac = lut[rng.integers(0, 3, (M, K), dtype=np.uint8)]
+    bc = lut[rng.integers(0, 3, (N, K), dtype=np.uint8)]
+    asc = np.full((M, K // 32), 127, np.uint8)
+    bsc = rng.integers(126, 128, (N, K // 32), dtype=np.uint8)
+    note("largest K slab: K=%d M=%d N=%d" % (K, M, N))
+
+    def to_slab(c):
+        rows = c.shape[0]
+        out = np.empty(rows * K, np.uint8)
+        for b0 in range(0, rows, 256):
+            n = min(256, rows - b0)
+            out[b0 * K:(b0 + n) * K] = c[b0:b0 + n].reshape(n, K // 64, 64).transpose(1, 0, 2).reshape(-1)
+        return out.reshape(rows, K)
+
+    sa, sb = to_slab(ac), to_slab(bc)
+    assert np.array_equal(from_slab(torch.from_numpy(sa), M, K), ac)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    y = bsq.blockscaled_gemm(bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB, t(sa), t(asc), None, t(sb), t(bsc), None,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del sa, sb
+    rows, cols = np.array([0, 77, 255, 256, 299]), np.array([0, 31, 200, 255])
+    ref = oracle.blockscaled_gemm(1, ac, asc, 1.0, bc, bsc, 1.0, rows=rows, cols=cols)
+    yc = y.cpu().numpy().astype(np.float64)[rows][:, cols]
+    note("  max |diff| = %g over %d outputs (|C| up to %g)" % (np.abs(yc - ref).max(), yc.size, np.abs(ref).max()))
+    assert np.array_equal(yc, ref)
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_output_beyond_2g_elements(fmt):
     """C of [65792, 32768] (2^31 + 2^24 elements, bf16 output offsets past 2^32 bytes) with a
