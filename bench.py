@@ -370,7 +370,8 @@ def grouped_figures(step, iters: int):
         wg = (step.W.float() * (1.0 + 0.1 * g)).to(torch.bfloat16)
         q = bsq.nvfp4_quantize(wg, direction=bsq.ROW)
         w_codes[g], w_scales[g], w_s[g:g + 1] = q["row_codes"], q["row_scales"], q["s_enc"][0:1]
-        m = bsq.mxfp8_requantize_nvfp4(q["row_codes"], q["row_scales"], q["s_enc"][0:1], direction=bsq.COL)
+        m = bsq.mxfp8_requantize_nvfp4(q["row_codes"], q["row_scales"], q["s_enc"][0:1],
+                                       direction=bsq.COL | (0 if step.mx_rows else bsq.MX_SLAB))
         mw_codes[g], mw_scales[g] = m["col_codes"], m["col_scales"]
     mdy = bsq.mxfp8_quantize(step.dY, direction=bsq.ROW | bsq.COL)
     mx = bsq.mxfp8_quantize(step.X, direction=bsq.COL)
@@ -381,7 +382,8 @@ def grouped_figures(step, iters: int):
     launches = {
         "fprop": lambda: bsq.blockscaled_grouped_gemm(fwd_fmt, bsq.GROUP_M, offs, qx["codes"], qx["scales"],
                                                       qx["s_enc"], w_codes, w_scales, w_s, out=y),
-        "dgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8, bsq.GROUP_M, offs, mdy["row_codes"],
+        "dgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8 | (0 if step.mx_rows else bsq.FMT_MX_SLAB_B),
+                                                      bsq.GROUP_M, offs, mdy["row_codes"],
                                                       mdy["row_scales"], None, mw_codes, mw_scales, None, out=dx),
         "wgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8, bsq.GROUP_K, offs, mdy["col_codes"],
                                                       mdy["col_scales"], None, mx["col_codes"], mx["col_scales"],

@@ -20,7 +20,8 @@ MX_SLAB = 4   # OR'ed into an MXFP8 cast's direction: codes in the slab layout
 RNE, SR = 0, 1
 FMT_NVFP4, FMT_MXFP8 = 0, 1
 FMT_A_ROWSCALED, FMT_B_ROWSCALED = 0x10, 0x20
-FMT_MX_SLAB = 0x40   # OR'ed into FMT_MXFP8: both operands' codes in the slab layout
+FMT_MX_SLAB_A, FMT_MX_SLAB_B = 0x40, 0x80   # OR'ed into FMT_MXFP8: that operand's codes in the slab layout
+FMT_MX_SLAB = FMT_MX_SLAB_A | FMT_MX_SLAB_B
 GROUP_M, GROUP_K = 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 

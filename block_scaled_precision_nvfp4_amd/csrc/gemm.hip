@@ -63,7 +63,7 @@ struct GemmArgs {
     void* c;
     int a_rows, b_rows;   // the operand's tensor scale is per row (float[M] / float[N])
     int64_t ld;           // elements between consecutive rows of A and of B (K unless grouped along K)
-    int slab;             // MXFP8 codes of both operands in the slab layout (K a multiple of 512)
+    int slab;             // MXFP8 codes in the slab layout (K a multiple of 512): bit 0 A, bit 1 B
 };
 
 // FMT 0: NVFP4, 8 waves of 128 x 64, register-staged (any K); FMT 1: MXFP8, 4 waves of 128 x
@@ -484,13 +484,21 @@ __device__ __forceinline__ u32x4s slab_rsrc(u32x4s r, uint32_t k, uint32_t bytes
     return r;
 }
 
-template <int P>
+// Slice k's codes where at least one operand is in the slab layout (SL bit 0: A is, bit 1: B
+// is); the other operand is read row-major as in nv4_dma_codes.  The layouts are template
+// parameters: chosen at run time, the two resources of an operand cost the main loop its
+// scalar DMA setup.
+template <int P, int SL>
 __device__ __forceinline__ void mx_slab_codes(const MxDma& d, uint32_t k, bool live, uint8_t* buf) {
     const int r0 = 64 * P + 16 * d.wave;
     const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
-    const uint32_t off = (uint32_t)r * 64u + 16u * c;
-    dma_b128(slab_rsrc(d.o.a, k, d.slab_a, live), lds_addr(buf + r0 * ROWB), off, 0u);
-    dma_b128(slab_rsrc(d.o.b, k, d.slab_b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off, 0u);
+    const uint32_t off_s = (uint32_t)r * 64u + 16u * c;
+    const uint32_t off_r = (uint32_t)r * d.rowbytes + 16u * c;
+    const uint32_t soff = live ? 64u * k : 0u;
+    if constexpr (SL & 1) dma_b128(slab_rsrc(d.o.a, k, d.slab_a, live), lds_addr(buf + r0 * ROWB), off_s, 0u);
+    else dma_b128(sized(d.o.a, live), lds_addr(buf + r0 * ROWB), off_r, soff);
+    if constexpr (SL & 2) dma_b128(slab_rsrc(d.o.b, k, d.slab_b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off_s, 0u);
+    else dma_b128(sized(d.o.b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off_r, soff);
 }
 
 template <int EPB, int BLK>
@@ -582,7 +590,7 @@ __device__ __forceinline__ void mx_mfma_row(const MxFrag& f, floatx16 (&acc)[4][
 // schedule one record later: records 0 and 1 come with the first slices, record G+2 is
 // fetched during slice 8G+1 into the buffer of record G-1 (last read for slice 8G-1) and is
 // first read for slice 8G+8.
-template <int MODE>
+template <int MODE, int SL = 0>
 __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
                                              int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
     constexpr bool REC = MODE != MX_SLOTS;
@@ -644,7 +652,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     auto dma_part = [&](auto p_c, int64_t k, bool live, uint8_t* b) {
         constexpr int P = decltype(p_c)::value;
         if constexpr (MODE == MX_RECS) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
-        else if constexpr (MODE == MX_SLAB) mx_slab_codes<P>(d, (uint32_t)k, live, b);
+        else if constexpr (MODE == MX_SLAB) mx_slab_codes<P, SL>(d, (uint32_t)k, live, b);
         else mx_dma_codes<P>(d, k * 64, live, b);
     };
     auto dma_slice = [&](int64_t k) {
@@ -1311,7 +1319,9 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         const bool rows16 = (g.ld / 32) % 16 == 0;
         const bool recs = rows16 && g.K % (MX_GROUP * 64) == 0 &&
                           (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) == 0;
-        if (recs && g.slab) mx_main_loop<MX_SLAB>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        if (recs && g.slab == 3) mx_main_loop<MX_SLAB, 3>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        else if (recs && g.slab == 2) mx_main_loop<MX_SLAB, 2>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        else if (recs && g.slab == 1) mx_main_loop<MX_SLAB, 1>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (recs) mx_main_loop<MX_RECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (rows16) mx_main_loop<MX_OFFRECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else mx_main_loop<MX_SLOTS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
@@ -1430,9 +1440,9 @@ int64_t grouped_gemm_workgroups(int mode, int64_t groups, int64_t M, int64_t N) 
 int launch_blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* offsets, int64_t M, int64_t N,
                                     int64_t K, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
                                     const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
-                                    int a_rows, int b_rows, void* c, int c_dtype, void* hip_stream) {
+                                    int a_rows, int b_rows, void* c, int c_dtype, void* hip_stream, int slab) {
     if (groups == 0 || M == 0 || N == 0) return 0;
-    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K};
+    GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K, slab};
     const GroupArgs q{offsets, groups, mode == 1 ? M : K};
     const int64_t tiles = grouped_gemm_workgroups(mode, groups, M, N);
     hipStream_t s = (hipStream_t)hip_stream;

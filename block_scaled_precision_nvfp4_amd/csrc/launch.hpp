@@ -28,7 +28,7 @@ int64_t grouped_gemm_workgroups(int mode, int64_t groups, int64_t M, int64_t N);
 int launch_blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* offsets, int64_t M, int64_t N,
                                     int64_t K, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s_enc,
                                     const uint8_t* b_codes, const uint8_t* b_scales, const float* b_s_enc,
-                                    int a_rows, int b_rows, void* c, int c_dtype, void* hip_stream);
+                                    int a_rows, int b_rows, void* c, int c_dtype, void* hip_stream, int slab = 0);
 int launch_nvfp4_quantize_rowscaled(const void* x, int64_t R, int64_t C, int rounding, uint64_t seed,
                                     uint32_t stream, const int8_t* signs, uint8_t* codes, uint8_t* scales,
                                     float* amax_rows, float* s_enc_rows, void* hip_stream);

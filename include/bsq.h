@@ -62,8 +62,10 @@ enum bsq_status {
 /* flags OR'ed into BSQ_FMT_NVFP4: that operand's tensor scale is one float per row */
 #define BSQ_FMT_A_ROWSCALED 0x10
 #define BSQ_FMT_B_ROWSCALED 0x20
-/* flag OR'ed into BSQ_FMT_MXFP8: both operands' codes are in the slab layout */
-#define BSQ_FMT_MX_SLAB 0x40
+/* flags OR'ed into BSQ_FMT_MXFP8: that operand's codes are in the slab layout */
+#define BSQ_FMT_MX_SLAB_A 0x40
+#define BSQ_FMT_MX_SLAB_B 0x80
+#define BSQ_FMT_MX_SLAB (BSQ_FMT_MX_SLAB_A | BSQ_FMT_MX_SLAB_B)
 
 /*
  * The slab layout of an MXFP8 code matrix [rows][K] (K % 64 == 0): a layout of the same
@@ -235,9 +237,11 @@ int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t*
  *       with two it is the fp32 product of 1/S_a[m] and 1/S_b[n], each so rounded.
  *   fmt BSQ_FMT_MXFP8: a_codes [M][K] (E4M3), a_scales [M][K/32] (E8M0); s_enc
  *       pointers are ignored (may be NULL); alpha = 1.  K % 32 == 0.
- *   fmt BSQ_FMT_MXFP8 | BSQ_FMT_MX_SLAB: a_codes and b_codes in the slab layout (as an
- *       MXFP8 cast with BSQ_MX_SLAB writes them), scales as for BSQ_FMT_MXFP8; K % 512 == 0,
- *       else BSQ_ERR_SHAPE.  Not accepted by blockscaled_grouped_gemm.
+ *   fmt BSQ_FMT_MXFP8 | BSQ_FMT_MX_SLAB_A and/or BSQ_FMT_MX_SLAB_B (BSQ_FMT_MX_SLAB: both):
+ *       that operand's codes are in the slab layout (as an MXFP8 cast with BSQ_MX_SLAB
+ *       writes them), scales as for BSQ_FMT_MXFP8; K % 512 == 0, else BSQ_ERR_SHAPE.
+ *       blockscaled_grouped_gemm accepts BSQ_FMT_MX_SLAB_B with BSQ_GROUP_M only, B being
+ *       G slab-layout matrices [N][K] one after the other.
  *   c [M][N], c_dtype BSQ_OUT_BF16 (RNE) or BSQ_OUT_F32.
  *   M, N >= 0 arbitrary; M, N or K == 0 are valid (K == 0 writes zeros).  K is below 2^24
  *   (NVFP4) or 2^23 (MXFP8), so that a 256-row operand tile stays below 2 GiB.

@@ -46,3 +46,15 @@ def rel_fro(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 GEMM_TOL = 2e-3
+
+
+def from_slab(t: torch.Tensor, rows: int, K: int) -> np.ndarray:
+    """The row-major [rows][K] codes held by a buffer in the slab layout: rows in bands of 256,
+    band b from byte 256 b K holding its n rows as K/64 slabs of n x 64 bytes."""
+    flat = t.cpu().numpy().reshape(-1)
+    assert flat.size == rows * K
+    out = np.empty((rows, K), np.uint8)
+    for b0 in range(0, rows, 256):
+        n = min(256, rows - b0)
+        out[b0:b0 + n] = flat[b0 * K:(b0 + n) * K].reshape(K // 64, n, 64).transpose(1, 0, 2).reshape(n, K)
+    return out

@@ -11,7 +11,7 @@ import torch
 import block_scaled_precision_nvfp4_amd as bsq
 from synthetic import (SEED_DY, SEED_SIGNS, SEED_SR_KEY, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16,
                        outlier_bf16, rht_signs)
-from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, note, rel_fro
+from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, from_slab, note, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -315,38 +315,29 @@ def test_fused_requantize_matches_chain(shape, direction):
             assert torch.equal(f[key + part], m[key + part]), "fused vs two-call chain " + key + part
 
 
-def from_slab(t: torch.Tensor, rows: int, K: int) -> np.ndarray:
-    """The row-major [rows][K] codes held by a buffer in the slab layout: rows in bands of 256,
-    band b from byte 256 b K holding its n rows as K/64 slabs of n x 64 bytes."""
-    flat = t.cpu().numpy().reshape(-1)
-    assert flat.size == rows * K
-    out = np.empty((rows, K), np.uint8)
-    for b0 in range(0, rows, 256):
-        n = min(256, rows - b0)
-        out[b0:b0 + n] = flat[b0 * K:(b0 + n) * K].reshape(K // 64, n, 64).transpose(1, 0, 2).reshape(n, K)
-    return out
-
-
-def slab_dgrad_check(T, N_out, N_in, out_dtype, rows=None, cols=None, label=""):
+def slab_dgrad_check(T, N_out, N_in, out_dtype, rows=None, cols=None, label="", which=3):
     """dX[T, N_in] = dY W as the MXFP8 dgrad with slab-layout codes: dY rowwise (MX_SLAB) and
     W columnwise from its NVFP4 rowwise codes (fused requantize, MX_SLAB).  The slab buffers
-    must hold exactly the oracle's codes, and the GEMM must match the oracle's GEMM."""
+    must hold exactly the oracle's codes, and the GEMM must match the oracle's GEMM.  which:
+    1 only dY, 2 only W in the slab layout (the other row-major), 3 both."""
     import oracle
     note("mxfp8 slab dgrad %s T=%d out=%d in=%d %s" % (label, T, N_out, N_in, out_dtype))
     dy = gaussian_bf16((T, N_out), STD_DY, SEED_DY)
     W = gaussian_bf16((N_out, N_in), STD_W, SEED_W)
-    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.ROW | bsq.MX_SLAB)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.ROW | (bsq.MX_SLAB if which & 1 else 0))
     qw = bsq.nvfp4_quantize(W.to(DEV), direction=bsq.ROW)
     qb = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1],
-                                    direction=bsq.COL | bsq.MX_SLAB)
-    y = bsq.blockscaled_gemm(bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB, qa["row_codes"], qa["row_scales"], None,
+                                    direction=bsq.COL | (bsq.MX_SLAB if which & 2 else 0))
+    flags = (bsq.FMT_MX_SLAB_A if which & 1 else 0) | (bsq.FMT_MX_SLAB_B if which & 2 else 0)
+    y = bsq.blockscaled_gemm(bsq.FMT_MXFP8 | flags, qa["row_codes"], qa["row_scales"], None,
                              qb["col_codes"], qb["col_scales"], None, out_dtype=out_dtype)
     torch.cuda.synchronize()
     ra = oracle.mxfp8_quantize(dy, direction=oracle.ROW)
     rw = oracle.nvfp4_quantize(W, direction=oracle.ROW)
     rb = oracle.mxfp8_quantize(oracle.nvfp4_dequantize(rw["row_codes"], rw["row_scales"], float(rw["s_enc"][0])),
                                direction=oracle.COL)
-    ga, gb = from_slab(qa["row_codes"], T, N_out), from_slab(qb["col_codes"], N_in, N_out)
+    ga = from_slab(qa["row_codes"], T, N_out) if which & 1 else qa["row_codes"].cpu().numpy()
+    gb = from_slab(qb["col_codes"], N_in, N_out) if which & 2 else qb["col_codes"].cpu().numpy()
     assert np.array_equal(ga, ra["row_codes"]), "dY slab codes"
     assert np.array_equal(gb, rb["col_codes"]), "W slab codes"
     assert_bytes_equal(qa["row_scales"], ra["row_scales"], "dY scales")
@@ -385,11 +376,13 @@ def test_mxfp8_cast_slab_layout(shape):
     assert_bytes_equal(q1["row_scales"], r["row_scales"], "row scales (rowwise only)")
 
 
+@pytest.mark.parametrize("which", [3, 1, 2])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_mxfp8_slab_operands_ragged(out_dtype):
+def test_mxfp8_slab_operands_ragged(out_dtype, which):
     """Slab-layout MXFP8 dgrad with a ragged last band in both operands (300 tokens, 320
-    input features) and K = 1536 (three 8-slice scale groups)."""
-    slab_dgrad_check(300, 1536, 320, out_dtype, label="ragged")
+    input features) and K = 1536 (three 8-slice scale groups): both operands in the slab
+    layout, or one of them with the other row-major."""
+    slab_dgrad_check(300, 1536, 320, out_dtype, label="ragged which=%d" % which, which=which)
 
 
 def test_mxfp8_slab_dgrad_llama3_8b_sampled():

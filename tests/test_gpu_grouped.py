@@ -16,7 +16,7 @@ import torch
 
 import block_scaled_precision_nvfp4_amd as bsq
 from synthetic import STD_W, gaussian_bf16, outlier_bf16
-from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, note, rel_fro
+from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, from_slab, note, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -74,12 +74,12 @@ def nv_tokens_per_group(x, offs):
     return (gc, gs, gS), (rc, rs, rS)
 
 
-def run_m_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, out_dtype, a_rows=False, label=""):
+def run_m_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, out_dtype, a_rows=False, label="", layout=0):
     import oracle
     note("grouped M %s fmt=%d M=%d N=%d groups=%d out=%s" % (label, fmt, M, N, len(offs) - 1, out_dtype))
     o = torch.tensor(offs, dtype=torch.int64, device=DEV)
     out = torch.full((M, N), 1.0, dtype=out_dtype, device=DEV)
-    f = fmt | (bsq.FMT_A_ROWSCALED if a_rows else 0)
+    f = fmt | (bsq.FMT_A_ROWSCALED if a_rows else 0) | layout
     bsq.blockscaled_grouped_gemm(f, bsq.GROUP_M, o, *a_gpu, *b_gpu, out_dtype=out_dtype, out=out)
     torch.cuda.synchronize()
     ref = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_M, offs, *a_ref, *b_ref, a_rows=a_rows)
@@ -137,6 +137,30 @@ def test_m_grouped_mxfp8_dgrad():
     b_ref = (np.stack([x["row_codes"] for x in rb]), np.stack([x["row_scales"] for x in rb]), None)
     run_m_grouped(bsq.FMT_MXFP8, (qa["row_codes"], qa["row_scales"], None), (ra["row_codes"], ra["row_scales"], None),
                   b_gpu, b_ref, offs, M, N, torch.bfloat16, label="mxfp8 dgrad")
+
+
+def test_m_grouped_mxfp8_dgrad_slab_b():
+    """M-grouped MXFP8 dgrad with each expert's codes in the slab layout (a ragged last band:
+    N = 320), the token operand row-major, K = 1536: the slab bytes hold exactly the oracle's
+    codes and the GEMM matches the oracle's."""
+    import oracle
+    sizes = [96, 500, 0, 333]
+    offs = splits_to_offsets(5, sizes)
+    M, N, K = offs[-1] + 3, 320, 1536
+    dy = gaussian_bf16((M, K), 1e-3, 12)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.ROW)
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.ROW)
+    ws = [gaussian_bf16((N, K), STD_W, 310 + g) for g in range(len(sizes))]
+    qb = [bsq.mxfp8_quantize(w.to(DEV), direction=bsq.ROW | bsq.MX_SLAB) for w in ws]
+    rb = [oracle.mxfp8_quantize(w, direction=oracle.ROW) for w in ws]
+    torch.cuda.synchronize()
+    assert_bytes_equal(qa["row_codes"], ra["row_codes"], "dY codes")
+    for g, (x, r) in enumerate(zip(qb, rb)):
+        assert np.array_equal(from_slab(x["row_codes"], N, K), r["row_codes"]), "expert %d slab codes" % g
+    b_gpu = (torch.stack([x["row_codes"] for x in qb]).contiguous(), torch.stack([x["row_scales"] for x in qb]).contiguous(), None)
+    b_ref = (np.stack([x["row_codes"] for x in rb]), np.stack([x["row_scales"] for x in rb]), None)
+    run_m_grouped(bsq.FMT_MXFP8, (qa["row_codes"], qa["row_scales"], None), (ra["row_codes"], ra["row_scales"], None),
+                  b_gpu, b_ref, offs, M, N, torch.bfloat16, label="mxfp8 dgrad slab B", layout=bsq.FMT_MX_SLAB_B)
 
 
 def test_m_grouped_many_groups():
