@@ -338,10 +338,12 @@ struct MxFrag {
 //  - per slice (MX_SLOTS; any other row pitch): one dword slot per (row, K-block) after the
 //    codes of each stage, [operand][256 rows][2 slots], holding the byte in its low 8 bits
 //    (a byte DMA fills one dword slot per lane).
-// MX_SLAB is MX_RECS on codes in the slab layout: a 256-row band of an operand (one tile's
-// rows) stored slice by slice, [K/64][n rows][64 B], so that each slice of the band is one
-// contiguous block that the DMAs read whole (row-major codes come as 64-byte pieces of rows
-// 2 KiB and more apart, which fill LDS at about 60 % of the rate).
+// MX_SLAB is MX_RECS with the codes of one or both operands in the slab layout: a 256-row
+// band of an operand (one tile's rows) stored slice by slice, [K/64][n rows][64 B], so that
+// each slice of the band is one contiguous block that the DMAs read whole (row-major codes
+// come as 64-byte pieces of rows 2 KiB and more apart, which fill LDS at about 60 % of the
+// rate).  The API admits slab operands only where K % 512 == 0, so they always meet the
+// aligned-record conditions.
 constexpr int MX_SLOTS = 0, MX_RECS = 1, MX_OFFRECS = 2, MX_SLAB = 3;
 constexpr int MX_CODES = 2 * GBM * ROWB;                  // 32 KiB
 constexpr int MX_STAGE_SLOTS = MX_CODES + 2 * GBM * 2 * 4;  // 36 KiB
