@@ -139,7 +139,8 @@ def test_m_grouped_mxfp8_dgrad():
                   b_gpu, b_ref, offs, M, N, torch.bfloat16, label="mxfp8 dgrad")
 
 
-def test_m_grouped_mxfp8_dgrad_slab_b():
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_m_grouped_mxfp8_dgrad_slab_b(out_dtype):
     """M-grouped MXFP8 dgrad with each expert's codes in the slab layout (a ragged last band:
     N = 320), the token operand row-major, K = 1536: the slab bytes hold exactly the oracle's
     codes and the GEMM matches the oracle's."""
@@ -160,7 +161,7 @@ def test_m_grouped_mxfp8_dgrad_slab_b():
     b_gpu = (torch.stack([x["row_codes"] for x in qb]).contiguous(), torch.stack([x["row_scales"] for x in qb]).contiguous(), None)
     b_ref = (np.stack([x["row_codes"] for x in rb]), np.stack([x["row_scales"] for x in rb]), None)
     run_m_grouped(bsq.FMT_MXFP8, (qa["row_codes"], qa["row_scales"], None), (ra["row_codes"], ra["row_scales"], None),
-                  b_gpu, b_ref, offs, M, N, torch.bfloat16, label="mxfp8 dgrad slab B", layout=bsq.FMT_MX_SLAB_B)
+                  b_gpu, b_ref, offs, M, N, out_dtype, label="mxfp8 dgrad slab B", layout=bsq.FMT_MX_SLAB_B)
 
 
 def test_m_grouped_many_groups():
