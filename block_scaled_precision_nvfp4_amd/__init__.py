@@ -24,6 +24,7 @@ FMT_MX_SLAB_A, FMT_MX_SLAB_B = 0x40, 0x80   # OR'ed into FMT_MXFP8: that operand
 FMT_MX_SLAB = FMT_MX_SLAB_A | FMT_MX_SLAB_B
 GROUP_M, GROUP_K = 1, 2
 OUT_BF16, OUT_F32 = 0, 1
+NVFP4_QUANTIZE_WORKSPACE_BYTES = 8192   # BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsq.so")
@@ -49,7 +50,7 @@ def lib():
                                "`python -m block_scaled_precision_nvfp4_amd.build`" % LIB_PATH)
         L = C.CDLL(LIB_PATH)
         vp, i64, i32, u32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64
-        L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_rowscaled.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp]
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
@@ -96,6 +97,17 @@ def _dev_tensor(t: torch.Tensor, dtype, name: str):
     return t
 
 
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    """The caller's scratch tensor (checked for size and device), or a new one."""
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != torch.device(device):
+        raise TypeError("workspace must be a device tensor on %s" % (device,))
+    if not ws.is_contiguous() or ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace must be contiguous and hold at least %d bytes" % nbytes)
+    return ws
+
+
 def _signs(rht_signs, device):
     if rht_signs is None:
         return None
@@ -109,10 +121,12 @@ def _signs(rht_signs, device):
 
 
 def nvfp4_quantize(x: torch.Tensor, direction: int = ROW, rounding: int = RNE, sr_seed: int = 0,
-                   sr_stream: int = 0, rht_signs=None) -> Dict[str, torch.Tensor]:
+                   sr_stream: int = 0, rht_signs=None, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """NVFP4-quantize a bf16 [rows, cols] device tensor.  Returns the requested directions'
     ``{row,col}_codes`` / ``{row,col}_scales`` (uint8) and ``amax`` / ``s_enc`` (float32[2],
-    index 0 rowwise, 1 columnwise), all on x's device."""
+    index 0 rowwise, 1 columnwise), all on x's device.  ``workspace`` (a device tensor of at
+    least NVFP4_QUANTIZE_WORKSPACE_BYTES bytes) is the call's scratch; one is allocated when
+    none is given."""
     _dev_tensor(x, torch.bfloat16, "x")
     R, Cc = x.shape
     dev = x.device
@@ -126,11 +140,12 @@ def nvfp4_quantize(x: torch.Tensor, direction: int = ROW, rounding: int = RNE, s
         out["col_scales"] = torch.empty((Cc, R // 16), **u8)
     out["amax"] = torch.empty(2, dtype=torch.float32, device=dev)
     out["s_enc"] = torch.empty(2, dtype=torch.float32, device=dev)
+    ws = _workspace(workspace, NVFP4_QUANTIZE_WORKSPACE_BYTES, dev)
     sg = _signs(rht_signs, dev)
     _check("nvfp4_quantize", lib().nvfp4_quantize(
         x.data_ptr(), R, Cc, direction, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg),
         _ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
-        _ptr(out.get("col_scales")), out["amax"].data_ptr(), out["s_enc"].data_ptr(), _stream(dev)))
+        _ptr(out.get("col_scales")), out["amax"].data_ptr(), out["s_enc"].data_ptr(), ws.data_ptr(), _stream(dev)))
     return out
 
 

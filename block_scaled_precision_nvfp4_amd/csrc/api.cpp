@@ -54,7 +54,7 @@ const char* bsq_last_error(void) { return g_last_error.c_str(); }
 
 int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding, uint64_t sr_seed,
                    uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
-                   uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out,
+                   uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out, void* workspace,
                    void* hip_stream) {
     static const char* fn = "nvfp4_quantize";
     if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
@@ -68,11 +68,12 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
     if (!empty && !x) return fail(BSQ_ERR_NULL, "%s: x is NULL", fn);
     if ((direction & BSQ_ROW) && !empty && (!row_codes || !row_scales)) return fail(BSQ_ERR_NULL, "%s: rowwise outputs are NULL", fn);
     if ((direction & BSQ_COL) && !empty && (!col_codes || !col_scales)) return fail(BSQ_ERR_NULL, "%s: columnwise outputs are NULL", fn);
-    if (misaligned(x) || misaligned(row_codes) || misaligned(col_codes) || misaligned(rht_signs))
+    if (!empty && !workspace) return fail(BSQ_ERR_NULL, "%s: workspace is NULL", fn);
+    if (misaligned(x) || misaligned(row_codes) || misaligned(col_codes) || misaligned(rht_signs) || misaligned(workspace))
         return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     return launched(bsq::launch_nvfp4_quantize(x, rows, cols, direction, rounding, sr_seed, sr_stream, rht_signs,
                                                row_codes, row_scales, col_codes, col_scales, amax_out, s_enc_out,
-                                               hip_stream), fn);
+                                               static_cast<float*>(workspace), hip_stream), fn);
 }
 
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows, int64_t cols,
@@ -257,6 +258,7 @@ Nv nv_at(int64_t base, int64_t elems) {
 }
 
 struct LinearLayout {
+    int64_t qws;                // the quantize calls' scratch (partial maxima), both phases
     Nv x_row, w_row;            // forward workspace
     Nv dy, w_col;               // backward workspace (dy holds both directions' codes)
     int64_t dy_col_codes, dy_col_scales;
@@ -267,10 +269,12 @@ struct LinearLayout {
 
 LinearLayout linear_layout(int64_t T, int64_t K, int64_t N) {
     LinearLayout L;
-    L.x_row = nv_at(0, T * K);
+    L.qws = 0;
+    const int64_t q0 = up(BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES);
+    L.x_row = nv_at(q0, T * K);
     L.w_row = nv_at(L.x_row.end, N * K);
     L.fwd_bytes = L.w_row.end;
-    L.dy = nv_at(0, T * N);
+    L.dy = nv_at(q0, T * N);
     L.dy_col_codes = L.dy.end;
     L.dy_col_scales = up(L.dy_col_codes + T * N / 2);
     L.w_col = nv_at(up(L.dy_col_scales + T * N / 16), K * N);
@@ -327,11 +331,11 @@ int nvfp4_linear_forward(const void* x, const void* w, int64_t tokens, int64_t i
     // fprop operands: rowwise NVFP4, RNE
     st = bsq::launch_nvfp4_quantize(x, T, K, BSQ_ROW, BSQ_RNE, 0, 0, nullptr, at<uint8_t>(ws, L.x_row.codes),
                                     at<uint8_t>(ws, L.x_row.scales), nullptr, nullptr, at<float>(ws, L.x_row.amax),
-                                    at<float>(ws, L.x_row.s_enc), hip_stream);
+                                    at<float>(ws, L.x_row.s_enc), at<float>(ws, L.qws), hip_stream);
     if (st) return launched(st, fn);
     st = bsq::launch_nvfp4_quantize(w, N, K, BSQ_ROW, BSQ_RNE, 0, 0, nullptr, at<uint8_t>(ws, L.w_row.codes),
                                     at<uint8_t>(ws, L.w_row.scales), nullptr, nullptr, at<float>(ws, L.w_row.amax),
-                                    at<float>(ws, L.w_row.s_enc), hip_stream);
+                                    at<float>(ws, L.w_row.s_enc), at<float>(ws, L.qws), hip_stream);
     if (st) return launched(st, fn);
     st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, T, N, K, at<uint8_t>(ws, L.x_row.codes),
                                       at<uint8_t>(ws, L.x_row.scales), at<float>(ws, L.x_row.s_enc),
@@ -341,7 +345,8 @@ int nvfp4_linear_forward(const void* x, const void* w, int64_t tokens, int64_t i
     // the saved activation: X columnwise along tokens (the wgrad contraction), RHT + SR
     st = bsq::launch_nvfp4_quantize(x, T, K, BSQ_COL, BSQ_SR, sr_seed, 1, rht_signs, nullptr, nullptr,
                                     at<uint8_t>(saved, L.x_col.codes), at<uint8_t>(saved, L.x_col.scales),
-                                    at<float>(saved, L.x_col.amax), at<float>(saved, L.x_col.s_enc), hip_stream);
+                                    at<float>(saved, L.x_col.amax), at<float>(saved, L.x_col.s_enc), at<float>(ws, L.qws),
+                                    hip_stream);
     return launched(st, fn);
 }
 
@@ -365,7 +370,7 @@ int nvfp4_linear_backward(const void* dy, const void* w, const void* saved, int6
     st = bsq::launch_nvfp4_quantize(dy, T, N, BSQ_ROW | BSQ_COL, BSQ_SR, sr_seed, 0, rht_signs,
                                     at<uint8_t>(ws, L.dy.codes), at<uint8_t>(ws, L.dy.scales),
                                     at<uint8_t>(ws, L.dy_col_codes), at<uint8_t>(ws, L.dy_col_scales),
-                                    at<float>(ws, L.dy.amax), at<float>(ws, L.dy.s_enc), hip_stream);
+                                    at<float>(ws, L.dy.amax), at<float>(ws, L.dy.s_enc), at<float>(ws, L.qws), hip_stream);
     if (st) return launched(st, fn);
     // wgrad: dW[N][K] = dY^T X over tokens
     st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, N, K, T, at<uint8_t>(ws, L.dy_col_codes),
@@ -376,7 +381,8 @@ int nvfp4_linear_backward(const void* dy, const void* w, const void* saved, int6
     // dgrad operand W columnwise along out_features, RHT + SR
     st = bsq::launch_nvfp4_quantize(w, N, K, BSQ_COL, BSQ_SR, sr_seed, 2, rht_signs, nullptr, nullptr,
                                     at<uint8_t>(ws, L.w_col.codes), at<uint8_t>(ws, L.w_col.scales),
-                                    at<float>(ws, L.w_col.amax), at<float>(ws, L.w_col.s_enc), hip_stream);
+                                    at<float>(ws, L.w_col.amax), at<float>(ws, L.w_col.s_enc), at<float>(ws, L.qws),
+                                    hip_stream);
     if (st) return launched(st, fn);
     // dgrad: dX[T][K] = dY W over out_features
     st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, T, K, N, at<uint8_t>(ws, L.dy.codes),

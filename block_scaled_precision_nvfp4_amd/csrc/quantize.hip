@@ -12,18 +12,18 @@
 //     columnwise 32-blocks span the lanes t and t^16.  Columnwise codes are transposed
 //     through LDS so that every output row (= input column) receives a full 128-byte
 //     (NVFP4) or 256-byte (MXFP8) segment from one wave.
-// The NVFP4 path runs an amax pass (atomic max of the binary32 bit pattern, which orders
-// like the value for non-negative floats) before the encode pass, because every block
-// scale depends on the per-tensor scale.  The amax pass accumulates into a library-owned
-// pair of slots per (device, stream) that alternate between consecutive calls on that
-// stream: the encode pass of a call reads its slot, publishes amax and S to the caller's
-// amax_out / s_enc_out, and clears the other slot for the next call -- so no separate
-// reset launch precedes the amax pass.
-#include <map>
-#include <mutex>
+// The NVFP4 path runs an amax pass before the encode pass, because every block scale
+// depends on the per-tensor scale.  The amax pass runs at most AMAX_PARTS workgroups, each
+// walking its share of the tensor; workgroup w stores its maximum to slot w of the caller's
+// workspace (a plain store, one per direction it serves).  Every encode workgroup reduces the
+// stored maxima itself, and workgroup 0 publishes amax and S.  Nothing accumulates from one
+// call to the next: the workspace needs no initial contents, each call writes every slot it
+// reads before reading it, and a replayed graph or a failed launch leaves nothing that a later
+// call could read.
 #include <type_traits>
 #include <utility>
 
+#include "../../include/bsq.h"
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -38,14 +38,18 @@ struct TileCoord {
     int rb, cc;       // sub-tile coordinates inside the workgroup tile
 };
 
-__device__ __forceinline__ TileCoord tile_coord() {
+// The thread's sub-tile in tile (ty, tx) of the 256 x 128 tile grid.
+__device__ __forceinline__ TileCoord tile_coord_at(int64_t ty, int64_t tx) {
     TileCoord t;
     t.rb = threadIdx.x >> 4;
     t.cc = threadIdx.x & 15;
-    t.r0 = (int64_t)blockIdx.y * TILE_R + 16 * t.rb;
-    t.c0 = (int64_t)blockIdx.x * TILE_C + 8 * t.cc;
+    t.r0 = ty * TILE_R + 16 * t.rb;
+    t.c0 = tx * TILE_C + 8 * t.cc;
     return t;
 }
+
+// The thread's sub-tile in the workgroup's own tile (one workgroup per tile).
+__device__ __forceinline__ TileCoord tile_coord() { return tile_coord_at(blockIdx.y, blockIdx.x); }
 
 // Load the thread's 16 x 8 bf16 sub-tile; rows >= R or a column chunk >= C read as zero
 // (C % 8 == 0, so a chunk is either entirely inside or entirely outside).
@@ -94,64 +98,112 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Atomic max of a non-negative float (its bit pattern orders as an unsigned integer).  The
-// atomic is skipped when the running maximum already covers v, which is safe: the value read
-// never exceeds the final maximum.
-__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
-    const unsigned cur = __hip_atomic_load((unsigned int*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__float_as_uint(v) > cur) atomicMax((unsigned int*)p, __float_as_uint(v));
-}
+// ------------------------------------------------------------------ per-tensor amax
 
-// Per-call amax accumulator: for each direction AMAX_SUB sub-slots, one per 128-byte line,
-// which workgroups update by workgroup index modulo AMAX_SUB; the consumer takes the max of
-// the sub-slots.  Spreading the atomics over lines keeps thousands of workgroups from
-// serialising on one address when the pass starts and every slot still reads zero.
-constexpr int AMAX_SUB = 64;
-constexpr int AMAX_STRIDE = 32;                             // floats per sub-slot line
-constexpr int AMAX_DIR = AMAX_SUB * AMAX_STRIDE;            // floats per direction
-constexpr int AMAX_SLOT = 2 * AMAX_DIR;                     // floats per call slot
+// Largest number of amax-pass workgroups; the workspace holds AMAX_PARTS partial maxima per
+// direction (rowwise at [0, AMAX_PARTS), columnwise at [AMAX_PARTS, 2 AMAX_PARTS)).
+constexpr int AMAX_PARTS = 1024;
+static_assert(2 * AMAX_PARTS * sizeof(float) == BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES, "workspace size");
 
-__device__ __forceinline__ void amax_report(float* acc, int dir, unsigned wg, float v) {
-    atomic_max_nonneg(acc + dir * AMAX_DIR + (int)(wg % AMAX_SUB) * AMAX_STRIDE, v);
-}
-
-// The accumulated amax of direction dir, computed by every wave (lane l reads sub-slot l).
-__device__ __forceinline__ float amax_collect(const float* acc, int dir) {
-    const int l = threadIdx.x & 63;
-    return wave_max(acc[dir * AMAX_DIR + l * AMAX_STRIDE]);
-}
-
-// Clears both call slots of a stream (2 * AMAX_SLOT floats) on their first use.
-__global__ void reset_amax_kernel(float* slots) {
-    for (int i = threadIdx.x; i < 2 * AMAX_SLOT; i += blockDim.x) slots[i] = 0.0f;
-}
-
-// DIRS: which slots to fill (bit 0 rowwise, bit 1 columnwise).  Without RHT both
-// directions share the plain amax; with RHT each direction takes the amax of its own
-// transformed values.
-template <int DIRS, bool RHT>
-__global__ __launch_bounds__(NTHREADS) void nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t R,
-                                                              int64_t C, const int8_t* __restrict__ signs,
-                                                              float* __restrict__ amax) {
-    const TileCoord t = tile_coord();
-    SubTile q;
-    load_subtile(x, R, C, t, q);
-    float mrow = 0.0f, mcol = 0.0f;
-    if (!RHT) {
-        static_for<0, 16>([&](auto j_c) {
-            constexpr int j = decltype(j_c)::value;
-            float v[8];
-            row_of(q, j, v);
+// Maximum of a workgroup (NT threads) of per-thread values a and b, returned to thread 0.
+template <int NT>
+__device__ __forceinline__ void block_max2(float& a, float& b) {
+    __shared__ float red[2][NT / 64];
+    a = wave_max(a);
+    b = wave_max(b);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        red[0][wave] = a;
+        red[1][wave] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) mrow = __builtin_fmaxf(mrow, __builtin_fabsf(v[k]));
-        });
-        mcol = mrow;
-    } else {
-        const uint32_t neg = sign_mask16(signs);
+        for (int w = 1; w < NT / 64; ++w) {
+            a = __builtin_fmaxf(a, red[0][w]);
+            b = __builtin_fmaxf(b, red[1][w]);
+        }
+    }
+}
+
+// Amax pass epilogue: the workgroup's maxima of the rowwise (a) and columnwise (b) values go to
+// its slots of the directions in DIRS.
+template <int NT, int DIRS>
+__device__ __forceinline__ void store_parts(float a, float b, float* __restrict__ parts) {
+    block_max2<NT>(a, b);
+    if (threadIdx.x == 0) {
+        if (DIRS & 1) parts[blockIdx.x] = a;
+        if (DIRS & 2) parts[AMAX_PARTS + blockIdx.x] = b;
+    }
+}
+
+// Encode pass prologue: the tensor amax of the directions in DIRS, reduced by the whole
+// workgroup (NT threads, 4 NT >= AMAX_PARTS) from the nparts partial maxima the amax pass
+// stored, returned to every thread.  Contains barriers: every thread must call it.
+template <int NT, int DIRS>
+__device__ __forceinline__ float2 parts_max(const float* __restrict__ parts, int nparts) {
+    static_assert(4 * NT >= AMAX_PARTS, "four partial maxima per thread at most");
+    __shared__ float red[2][NT / 64];
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = threadIdx.x + NT * k;
+        if (i < nparts) {
+            if (DIRS & 1) a = __builtin_fmaxf(a, parts[i]);
+            if (DIRS & 2) b = __builtin_fmaxf(b, parts[AMAX_PARTS + i]);
+        }
+    }
+    a = wave_max(a);
+    b = wave_max(b);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        red[0][wave] = a;
+        red[1][wave] = b;
+    }
+    __syncthreads();
+    a = red[0][0];
+    b = red[1][0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        a = __builtin_fmaxf(a, red[0][w]);
+        b = __builtin_fmaxf(b, red[1][w]);
+    }
+    return make_float2(a, b);
+}
+
+// Workgroup 0 of an encode pass publishes amax and S of the directions in DIRS.
+template <int DIRS>
+__device__ __forceinline__ void publish_scales(float2 am, float* amax_out, float* s_enc_out) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        if (DIRS & 1) {
+            amax_out[0] = am.x;
+            s_enc_out[0] = nvfp4_tensor_scale(am.x);
+        }
+        if (DIRS & 2) {
+            amax_out[1] = am.y;
+            s_enc_out[1] = nvfp4_tensor_scale(am.y);
+        }
+    }
+}
+
+// Amax of the transformed values per direction (DIRS: bit 0 rowwise, bit 1 columnwise; with
+// RHT each direction takes the amax of its own transformed values), over 256 x 128 tiles: a
+// grid of at most AMAX_PARTS workgroups, workgroup w taking tiles w, w + grid, ...
+template <int DIRS>
+__global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                                  int64_t C, const int8_t* __restrict__ signs,
+                                                                  float* __restrict__ parts) {
+    const int64_t ntc = (C + TILE_C - 1) / TILE_C, nt = ntc * ((R + TILE_R - 1) / TILE_R);
+    const uint32_t neg = sign_mask16(signs);
+    float mrow = 0.0f, mcol = 0.0f;
+    for (int64_t tix = blockIdx.x; tix < nt; tix += gridDim.x) {
+        const TileCoord t = tile_coord_at(tix / ntc, tix % ntc);
+        SubTile q;
+        load_subtile(x, R, C, t, q);
         if (DIRS & 1) {
             const bool upper = (t.cc & 1) != 0;
-        static_for<0, 16>([&](auto j_c) {
-            constexpr int j = decltype(j_c)::value;
+            static_for<0, 16>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
                 float v[8];
                 row_of(q, j, v);
                 rht16_pair(v, neg, upper);
@@ -160,36 +212,17 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_kernel(const uint16_t* __
             });
         }
         if (DIRS & 2) {
-        static_for<0, 8>([&](auto k_c) {
-            constexpr int k = decltype(k_c)::value;
+            static_for<0, 8>([&](auto k_c) {
+                constexpr int k = decltype(k_c)::value;
                 float v[16];
-            col_of(q, k, v);
+                col_of(q, k, v);
                 rht16(v, neg);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mcol = __builtin_fmaxf(mcol, __builtin_fabsf(v[j]));
             });
         }
     }
-    __shared__ float red[2][NTHREADS / 64];
-    mrow = wave_max(mrow);
-    mcol = wave_max(mcol);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red[0][wave] = mrow;
-        red[1][wave] = mcol;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float a = red[0][0], b = red[1][0];
-#pragma unroll
-        for (int w = 1; w < NTHREADS / 64; ++w) {
-            a = __builtin_fmaxf(a, red[0][w]);
-            b = __builtin_fmaxf(b, red[1][w]);
-        }
-        const unsigned wg = blockIdx.y * gridDim.x + blockIdx.x;
-        if (DIRS & 1) amax_report(amax, 0, wg, a);
-        if (DIRS & 2) amax_report(amax, 1, wg, b);
-    }
+    store_parts<NTHREADS, DIRS>(mrow, mcol, parts);
 }
 
 // ------------------------------------------------------------------ NVFP4 encode
@@ -202,28 +235,13 @@ struct NvEncodeArgs {
     uint8_t* row_scales;
     uint8_t* col_codes;
     uint8_t* col_scales;
-    const float* acc;    // amax accumulated by this call's amax pass
-    float* acc_next;     // the other slot, cleared here for the next call on the stream
+    const float* parts;  // the amax pass's partial maxima (AMAX_PARTS per direction)
+    int nparts;          // how many the amax pass stored per direction
     float* amax_out;
     float* s_enc_out;
     uint64_t seed;
     uint32_t stream;
 };
-
-// First wave of workgroup 0 of an encode pass: publish amax and S of both directions (a0, a1
-// collected by the wave) and clear the next call's slot.
-__device__ __forceinline__ void publish_scales(float a0, float a1, float* acc_next, float* amax_out,
-                                               float* s_enc_out) {
-    const int l = threadIdx.x;
-    if (l == 0) {
-        amax_out[0] = a0;
-        amax_out[1] = a1;
-        s_enc_out[0] = nvfp4_tensor_scale(a0);
-        s_enc_out[1] = nvfp4_tensor_scale(a1);
-    }
-    acc_next[l * AMAX_STRIDE] = 0.0f;
-    acc_next[AMAX_DIR + l * AMAX_STRIDE] = 0.0f;
-}
 
 // Encode one 16-block's worth of values held by this thread (n = 8 or 16 values) with the
 // block amax already known.  Writes the packed codes (n/2 bytes as n/8 words) into w[].
@@ -271,10 +289,10 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     SubTile q;
     load_subtile(a.x, R, C, t, q);
     const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
-    const float arow = amax_collect(a.acc, 0), acol = amax_collect(a.acc, 1);
-    const float Srow = nvfp4_tensor_scale(arow);
-    const float Scol = nvfp4_tensor_scale(acol);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) publish_scales(arow, acol, a.acc_next, a.amax_out, a.s_enc_out);
+    const float2 am = parts_max<NTHREADS, DIRS>(a.parts, a.nparts);
+    const float Srow = nvfp4_tensor_scale(am.x);
+    const float Scol = nvfp4_tensor_scale(am.y);
+    publish_scales<DIRS>(am, a.amax_out, a.s_enc_out);
     const bool colok = t.c0 < C;
 
     if (DIRS & 1) {
@@ -593,10 +611,11 @@ __device__ __forceinline__ void lin_range(int64_t n16, int64_t& first, int64_t& 
     (void)n16;
 }
 
-// Plain tensor amax (both slots): max |x| over n16 16-byte units.
+// Plain tensor amax: max |x| over n16 16-byte units, stored to the slots of the directions in
+// DIRS (without RHT both directions share it).
 template <int DIRS>
 __global__ __launch_bounds__(LIN_THREADS) void amax_linear_kernel(const uint4* __restrict__ x, int64_t n16,
-                                                                  float* __restrict__ amax) {
+                                                                  float* __restrict__ parts) {
     int64_t first, stride;
     lin_range(n16, first, stride);
     float m = 0.0f;
@@ -615,23 +634,13 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_linear_kernel(const uint4* _
             for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
         }
     }
-    __shared__ float red[LIN_THREADS / 64];
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float a = red[0];
-#pragma unroll
-        for (int w = 1; w < LIN_THREADS / 64; ++w) a = __builtin_fmaxf(a, red[w]);
-        if (DIRS & 1) amax_report(amax, 0, blockIdx.x, a);
-        if (DIRS & 2) amax_report(amax, 1, blockIdx.x, a);
-    }
+    store_parts<LIN_THREADS, DIRS>(m, m, parts);
 }
 
 // Row-RHT amax: the 16-point transform of each block, the block held by a lane pair.
 __global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
                                                                           const int8_t* __restrict__ signs,
-                                                                          float* __restrict__ amax) {
+                                                                          float* __restrict__ parts) {
     int64_t first, stride;
     lin_range(n16, first, stride);
     const uint32_t neg = sign_mask16(signs);
@@ -653,16 +662,7 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const 
             for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
         }
     }
-    __shared__ float red[LIN_THREADS / 64];
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float a = red[0];
-#pragma unroll
-        for (int w = 1; w < LIN_THREADS / 64; ++w) a = __builtin_fmaxf(a, red[w]);
-        amax_report(amax, 0, blockIdx.x, a);
-    }
+    store_parts<LIN_THREADS, 1>(m, m, parts);
 }
 
 // Rowwise NVFP4 encode: unit u = half u%2 of block u/2.
@@ -671,16 +671,15 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
                                                                        const int8_t* __restrict__ signs,
                                                                        uint32_t* __restrict__ codes,
                                                                        uint8_t* __restrict__ scales,
-                                                                       const float* __restrict__ acc,
-                                                                       float* __restrict__ acc_next,
+                                                                       const float* __restrict__ parts, int nparts,
                                                                        float* __restrict__ amax_out,
                                                                        float* __restrict__ s_enc_out, uint64_t seed,
                                                                        uint32_t stream) {
     int64_t first, stride;
     lin_range(n16, first, stride);
-    const float arow = amax_collect(acc, 0);
-    const float S = nvfp4_tensor_scale(arow);
-    if (blockIdx.x == 0 && threadIdx.x < 64) publish_scales(arow, amax_collect(acc, 1), acc_next, amax_out, s_enc_out);
+    const float2 am = parts_max<LIN_THREADS, 1>(parts, nparts);
+    const float S = nvfp4_tensor_scale(am.x);
+    publish_scales<1>(am, amax_out, s_enc_out);
     const uint32_t neg = RHT ? sign_mask16(signs) : 0u;
     const bool upper = (threadIdx.x & 1) != 0;
     for (int64_t base = first; base < n16; base += stride) {
@@ -891,22 +890,6 @@ static inline dim3 tile_grid(int64_t R, int64_t C) {
     return dim3((unsigned)((C + TILE_C - 1) / TILE_C), (unsigned)((R + TILE_R - 1) / TILE_R), 1);
 }
 
-template <int DIRS, bool RHT, bool SR>
-static void launch_nv(const NvEncodeArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((nvfp4_amax_kernel<DIRS, RHT>), g, dim3(NTHREADS), 0, s, a.x, a.R, a.C, a.signs,
-                       (float*)a.acc);
-    hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR>), g, dim3(NTHREADS), 0, s, a);
-}
-
-template <int DIRS>
-static void launch_nv_dirs(const NvEncodeArgs& a, bool rht, bool sr, dim3 g, hipStream_t s) {
-    if (rht) {
-        if (sr) launch_nv<DIRS, true, true>(a, g, s); else launch_nv<DIRS, true, false>(a, g, s);
-    } else {
-        if (sr) launch_nv<DIRS, false, true>(a, g, s); else launch_nv<DIRS, false, false>(a, g, s);
-    }
-}
-
 __global__ void empty_tensor_scales_kernel(float* amax, float* s_enc) {
     if (threadIdx.x < 2) {
         amax[threadIdx.x] = 0.0f;
@@ -914,82 +897,71 @@ __global__ void empty_tensor_scales_kernel(float* amax, float* s_enc) {
     }
 }
 
-// The two amax slots of (device, stream); on first use they are cleared by a kernel on
-// that stream.  Returns the slot of this call and the one to clear for the next.
-struct AmaxSlots {
-    float* buf = nullptr;
-    unsigned parity = 0;
-};
+static inline unsigned amax_grid(int64_t units, int64_t per) {
+    int64_t g = (units + per - 1) / per;
+    if (g > AMAX_PARTS) g = AMAX_PARTS;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
 
-static int amax_slots(hipStream_t s, float** cur, float** nxt) {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, AmaxSlots> slots;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return (int)e;
-    std::lock_guard<std::mutex> lock(mu);
-    AmaxSlots& sl = slots[{dev, s}];
-    if (sl.buf == nullptr) {
-        e = hipMalloc(&sl.buf, 2 * AMAX_SLOT * sizeof(float));
-        if (e != hipSuccess) {
-            sl.buf = nullptr;
-            return (int)e;
-        }
-        hipLaunchKernelGGL(reset_amax_kernel, dim3(1), dim3(256), 0, s, sl.buf);
-    }
-    *cur = sl.buf + AMAX_SLOT * sl.parity;
-    *nxt = sl.buf + AMAX_SLOT * (sl.parity ^ 1u);
-    sl.parity ^= 1u;
-    return 0;
+// The error of the launch just made (0 if it was accepted).
+static inline int launch_status() { return (int)hipGetLastError(); }
+
+template <int DIRS, bool RHT, bool SR>
+static int launch_encode_tiles(const NvEncodeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR>), tile_grid(a.R, a.C), dim3(NTHREADS), 0, s, a);
+    return launch_status();
+}
+
+template <int DIRS, bool RHT>
+static int launch_encode_tiles(const NvEncodeArgs& a, bool sr, hipStream_t s) {
+    return sr ? launch_encode_tiles<DIRS, RHT, true>(a, s) : launch_encode_tiles<DIRS, RHT, false>(a, s);
 }
 
 int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
                           uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
-                          uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, void* hip_stream) {
+                          uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, float* parts,
+                          void* hip_stream) {
     hipStream_t s = (hipStream_t)hip_stream;
     if (R == 0 || C == 0) {
         hipLaunchKernelGGL(empty_tensor_scales_kernel, dim3(1), dim3(64), 0, s, amax, s_enc);
-        return (int)hipGetLastError();
+        return launch_status();
     }
-    float *acc = nullptr, *acc_next = nullptr;
-    const int st = amax_slots(s, &acc, &acc_next);
-    if (st != 0) return st;
-    NvEncodeArgs a{(const uint16_t*)x, R, C, signs, row_codes, row_scales, col_codes, col_scales,
-                   acc, acc_next, amax, s_enc, seed, stream};
-    const dim3 g = tile_grid(R, C);
     const bool rht = signs != nullptr, sr = rounding == 1;
     const int64_t n16 = R * C / 8;
     const uint4* xv = (const uint4*)x;
-    const unsigned lg = lin_grid(n16);
+    // amax pass: the streaming kernels, except for a columnwise transform (along rows)
+    unsigned np;
+    if (rht && (direction & 2)) {
+        np = amax_grid(((R + TILE_R - 1) / TILE_R) * ((C + TILE_C - 1) / TILE_C), 1);
+        if (direction == 2)
+            hipLaunchKernelGGL(nvfp4_amax_rht_kernel<2>, dim3(np), dim3(NTHREADS), 0, s, (const uint16_t*)x, R, C, signs, parts);
+        else
+            hipLaunchKernelGGL(nvfp4_amax_rht_kernel<3>, dim3(np), dim3(NTHREADS), 0, s, (const uint16_t*)x, R, C, signs, parts);
+    } else {
+        np = amax_grid(n16, (int64_t)LIN_THREADS * LIN_UNITS);
+        if (rht) hipLaunchKernelGGL(amax_rht_row_linear_kernel, dim3(np), dim3(LIN_THREADS), 0, s, xv, n16, signs, parts);
+        else if (direction == 1) hipLaunchKernelGGL(amax_linear_kernel<1>, dim3(np), dim3(LIN_THREADS), 0, s, xv, n16, parts);
+        else if (direction == 2) hipLaunchKernelGGL(amax_linear_kernel<2>, dim3(np), dim3(LIN_THREADS), 0, s, xv, n16, parts);
+        else hipLaunchKernelGGL(amax_linear_kernel<3>, dim3(np), dim3(LIN_THREADS), 0, s, xv, n16, parts);
+    }
+    if (const int e = launch_status()) return e;
+    const int nparts = (int)np;
     if (direction == 1) {
-        // rowwise only: two streaming passes
-        if (rht) hipLaunchKernelGGL(amax_rht_row_linear_kernel, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, acc);
-        else hipLaunchKernelGGL(amax_linear_kernel<1>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, acc);
+        // rowwise only: the streaming encode
+        const dim3 lg(lin_grid(n16));
         uint32_t* rc = (uint32_t*)row_codes;
-        const float* ca = acc;
-        if (rht && sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
-        else if (rht) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
-        else if (sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, true>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
-        else hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, false>), dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, ca, acc_next, amax, s_enc, seed, stream);
-        return (int)hipGetLastError();
+        if (rht && sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, true>), lg, dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, parts, nparts, amax, s_enc, seed, stream);
+        else if (rht) hipLaunchKernelGGL((nvfp4_row_linear_kernel<true, false>), lg, dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, parts, nparts, amax, s_enc, seed, stream);
+        else if (sr) hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, true>), lg, dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, parts, nparts, amax, s_enc, seed, stream);
+        else hipLaunchKernelGGL((nvfp4_row_linear_kernel<false, false>), lg, dim3(LIN_THREADS), 0, s, xv, n16, signs, rc, row_scales, parts, nparts, amax, s_enc, seed, stream);
+        return launch_status();
     }
-    // columnwise (alone or with rowwise): the 256 x 128 tile kernels; without RHT the
-    // amax pass is the streaming one
-    if (!rht) {
-        if (direction == 2) hipLaunchKernelGGL(amax_linear_kernel<2>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, acc);
-        else hipLaunchKernelGGL(amax_linear_kernel<3>, dim3(lg), dim3(LIN_THREADS), 0, s, xv, n16, acc);
-        if (direction == 2) {
-            if (sr) hipLaunchKernelGGL((nvfp4_encode_kernel<2, false, true>), g, dim3(NTHREADS), 0, s, a);
-            else hipLaunchKernelGGL((nvfp4_encode_kernel<2, false, false>), g, dim3(NTHREADS), 0, s, a);
-        } else {
-            if (sr) hipLaunchKernelGGL((nvfp4_encode_kernel<3, false, true>), g, dim3(NTHREADS), 0, s, a);
-            else hipLaunchKernelGGL((nvfp4_encode_kernel<3, false, false>), g, dim3(NTHREADS), 0, s, a);
-        }
-        return (int)hipGetLastError();
-    }
-    if (direction == 2) launch_nv_dirs<2>(a, rht, sr, g, s);
-    else launch_nv_dirs<3>(a, rht, sr, g, s);
-    return (int)hipGetLastError();
+    // columnwise, alone or with rowwise: the 256 x 128 tile kernels
+    const NvEncodeArgs a{(const uint16_t*)x, R, C, signs, row_codes, row_scales, col_codes, col_scales,
+                         parts, nparts, amax, s_enc, seed, stream};
+    if (direction == 2) return rht ? launch_encode_tiles<2, true>(a, sr, s) : launch_encode_tiles<2, false>(a, sr, s);
+    return rht ? launch_encode_tiles<3, true>(a, sr, s) : launch_encode_tiles<3, false>(a, sr, s);
 }
 
 int launch_nvfp4_quantize_rowscaled(const void* x, int64_t R, int64_t C, int rounding, uint64_t seed,

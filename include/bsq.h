@@ -20,8 +20,9 @@
  *     (TransformerEngine PR #2817, Description and dispatch flowchart).
  *   - Every pointer argument that names tensor data is a DEVICE pointer; every
  *     device pointer must be 16-byte aligned.  The caller allocates and owns all
- *     buffers.  The only device memory the library allocates itself is the amax
- *     accumulator of nvfp4_quantize (described there).
+ *     buffers, scratch space included (the `workspace` arguments); the library allocates
+ *     no device memory and keeps no state between calls besides the thread-local error
+ *     message.
  *   - Work is enqueued asynchronously on hip_stream (a hipStream_t; NULL is the
  *     null stream).  Return values report argument validation and launch errors
  *     only; faults during kernel execution surface at the next synchronisation.
@@ -122,16 +123,21 @@ enum bsq_status {
  *              Required.
  *   s_enc_out  float[2] (device): the matching tensor scales S.  Required.
  *              Slots of an unrequested direction are left unspecified.
- * The amax pass accumulates into two library-owned device slots per (device, stream),
- * allocated on the first call on that stream and used alternately by consecutive calls;
- * calls on one stream are therefore ordered as usual, and calls on different streams do
- * not share slots.  The first call on a stream allocates (hipMalloc) those slots, 32 KiB,
- * which stay allocated until the process ends.
+ *   workspace  BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES of device scratch (16-byte aligned),
+ *              owned by the caller: the amax pass stores per-workgroup partial maxima there
+ *              and the encode pass reads them.  No initial contents are needed and the
+ *              contents afterwards are unspecified; each call writes every slot it reads, so
+ *              a call never depends on an earlier one (graph replays included).  The
+ *              workspace must not overlap another argument, and two calls that may run at
+ *              the same time (on different streams) need different workspaces.  Required
+ *              unless the tensor is empty.
  */
+#define BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES 8192
 int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding,
                    uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
                    uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
-                   uint8_t* col_scales, float* amax_out, float* s_enc_out, void* hip_stream);
+                   uint8_t* col_scales, float* amax_out, float* s_enc_out, void* workspace,
+                   void* hip_stream);
 
 /*
  * nvfp4_quantize_rowscaled -- rowwise NVFP4 quantization with one outer fp32 scale per

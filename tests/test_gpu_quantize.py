@@ -67,11 +67,28 @@ def test_nvfp4_rht_sr_small(shape, direction):
                 label="rht+sr")
 
 
+# RHT without SR and SR without RHT, in each direction: rowwise-only runs the streaming
+# kernels (amax_rht_row_linear + the rowwise encode), columnwise-only and both directions the
+# tile kernels.  Ragged small shapes (rows not a multiple of 16 where rowwise-only allows it,
+# cols % 16 == 8 for columnwise-only) and the forward activation shape.
+_ALONE_SHAPES = {1: (37, 400), 2: (272, 136), 3: (272, 144)}
+
+
+@pytest.mark.parametrize("direction", [1, 2, 3])
 @pytest.mark.parametrize("rounding,use_rht", [(0, True), (1, False)])
-def test_nvfp4_rht_or_sr_alone(rounding, use_rht):
-    x = gaussian_bf16((512, 384), 1.0, 22)
-    check_nvfp4(x, 3, rounding=rounding, seed=SEED_SR_KEY, stream=0,
-                signs=rht_signs(SEED_SIGNS) if use_rht else None, label="rht-or-sr")
+def test_nvfp4_rht_or_sr_alone(rounding, use_rht, direction):
+    x = gaussian_bf16(_ALONE_SHAPES[direction], 1.0, 22 + direction)
+    check_nvfp4(x, direction, rounding=rounding, seed=SEED_SR_KEY, stream=direction,
+                signs=rht_signs(SEED_SIGNS) if use_rht else None, label="rht-or-sr small")
+
+
+@pytest.mark.parametrize("direction", [1, 2, 3])
+@pytest.mark.parametrize("rounding,use_rht", [(0, True), (1, False)])
+def test_nvfp4_rht_or_sr_alone_workload(rounding, use_rht, direction):
+    """The same variants on the forward activation shape [16384, 4096]."""
+    x = gaussian_bf16((16384, 4096), 1.0, SEED_X)
+    check_nvfp4(x, direction, rounding=rounding, seed=SEED_SR_KEY, stream=1,
+                signs=rht_signs(SEED_SIGNS) if use_rht else None, label="rht-or-sr [16384,4096]")
 
 
 def test_nvfp4_col_only_cols_multiple_of_8():
@@ -92,35 +109,84 @@ def test_nvfp4_zero_and_empty():
     assert got["amax"].cpu().tolist() == [0.0, 0.0] and got["s_enc"].cpu().tolist() == [1.0, 1.0]
 
 
-def test_amax_slots_alternate_per_stream():
-    """The amax accumulator is per (device, stream) and alternates between consecutive calls:
-    a call must never see the amax of an earlier call, on the same stream or on another."""
+def test_calls_share_no_state():
+    """Each call reduces only the partial maxima its own amax pass stored: consecutive calls
+    with one workspace (a large-amax tensor, then a small one, and back), and calls on two
+    streams with a workspace each, never see another call's amax."""
     import oracle
     big = outlier_bf16((256, 512), seed=81, mask_seed=82)        # amax in the hundreds
     small = gaussian_bf16((256, 512), 1e-4, 83)                  # amax ~ 5e-4
     refs = {id(t): oracle.nvfp4_quantize(t, direction=3) for t in (big, small)}
-    note("amax slots: alternating big/small tensors on one stream")
+    ws = torch.empty(bsq.NVFP4_QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=DEV)
+    note("one workspace: alternating big/small tensors on one stream")
     for t in (big, small, small, big, small):
-        got = bsq.nvfp4_quantize(t.to(DEV), direction=3)
+        got = bsq.nvfp4_quantize(t.to(DEV), direction=3, workspace=ws)
         torch.cuda.synchronize()
         assert_f32_equal(got["amax"], refs[id(t)]["amax"], "amax")
         assert_bytes_equal(got["row_codes"], refs[id(t)]["row_codes"], "row codes")
-    note("amax slots: two streams")
+        assert_bytes_equal(got["col_codes"], refs[id(t)]["col_codes"], "col codes")
+    note("two streams, a workspace each")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     xb, xs = big.to(DEV), small.to(DEV)
+    w1 = torch.empty(bsq.NVFP4_QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=DEV)
+    w2 = torch.empty(bsq.NVFP4_QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=DEV)
     torch.cuda.synchronize()
     outs = []
     for _ in range(3):
         with torch.cuda.stream(s1):
-            g1 = bsq.nvfp4_quantize(xb, direction=1)
+            g1 = bsq.nvfp4_quantize(xb, direction=1, workspace=w1)
         with torch.cuda.stream(s2):
-            g2 = bsq.nvfp4_quantize(xs, direction=1)
+            g2 = bsq.nvfp4_quantize(xs, direction=1, workspace=w2)
         outs.append((g1, g2))
     torch.cuda.synchronize()
     for g1, g2 in outs:
         assert_f32_equal(g1["amax"][0:1], refs[id(big)]["amax"][0:1], "stream 1 amax")
         assert_f32_equal(g2["amax"][0:1], refs[id(small)]["amax"][0:1], "stream 2 amax")
         assert_bytes_equal(g2["row_codes"], refs[id(small)]["row_codes"], "stream 2 codes")
+
+
+@pytest.mark.parametrize("direction,rounding,use_rht", [(1, 0, False), (3, 0, False), (2, 1, True)])
+def test_graph_replay(direction, rounding, use_rht):
+    """nvfp4_quantize captured in a HIP graph (torch.cuda.graph) and replayed on new inputs
+    copied into the captured input buffer: a large-amax tensor, then a small-amax one, then
+    the large one again, with eager work and synchronisation between replays.  Every replay
+    must match the oracle bit for bit (nothing carries over from one replay to the next)."""
+    import oracle
+    shape = (512, 384)
+    inputs = [outlier_bf16(shape, seed=91, mask_seed=92), gaussian_bf16(shape, 1e-4, 93),
+              outlier_bf16(shape, seed=91, mask_seed=92), gaussian_bf16(shape, 3.0, 94)]
+    signs = rht_signs(SEED_SIGNS) if use_rht else None
+    refs = [oracle.nvfp4_quantize(t, direction=direction, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=4,
+                                  signs=None if signs is None else signs.numpy()) for t in inputs]
+    xin = inputs[3].to(DEV)
+    sg = None if signs is None else signs.to(DEV)
+    note("graph capture dir=%d rnd=%d rht=%s" % (direction, rounding, use_rht))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture, as torch requires
+        bsq.nvfp4_quantize(xin, direction=direction, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=4, rht_signs=sg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = bsq.nvfp4_quantize(xin, direction=direction, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=4,
+                                 rht_signs=sg)
+    for i, (t, ref) in enumerate(zip(inputs, refs)):
+        note("graph replay %d" % i)
+        xin.copy_(t.to(DEV))
+        eager = bsq.nvfp4_quantize(xin, direction=direction, rounding=rounding, sr_seed=SEED_SR_KEY, sr_stream=4,
+                                   rht_signs=sg)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for d, key in ((1, "row"), (2, "col")):
+            if direction & d:
+                k = 0 if d == 1 else 1
+                assert_f32_equal(out["amax"][k:k + 1], ref["amax"][k:k + 1], "replay %d amax %s" % (i, key))
+                assert_f32_equal(out["s_enc"][k:k + 1], ref["s_enc"][k:k + 1], "replay %d s_enc %s" % (i, key))
+                assert_bytes_equal(out[key + "_scales"], ref[key + "_scales"], "replay %d %s scales" % (i, key))
+                assert_bytes_equal(out[key + "_codes"], ref[key + "_codes"], "replay %d %s codes" % (i, key))
+                assert torch.equal(out[key + "_codes"], eager[key + "_codes"]), "replay %d vs eager" % i
 
 
 def test_nvfp4_extreme_values():
