@@ -36,9 +36,6 @@
 // while the current step's MFMAs issue.  Workgroups are renumbered so that each of the 8 XCDs
 // (which take workgroups round-robin) works on a contiguous band of output tiles and reuses
 // operand rows from its own L2.
-#include <mutex>
-#include <set>
-
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -1221,7 +1218,8 @@ __device__ __forceinline__ bool enter_group(GemmArgs& g, const GroupArgs& q, int
 template <int FMT, int OUT_F32, int GM>
 __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, GroupArgs q) {
     using F = Fmt<FMT>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    // static LDS (up to 152 KiB of gfx950's 160 KiB): no per-kernel attribute to raise at run time
+    __shared__ __attribute__((aligned(16))) uint8_t lds[F::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int64_t bid = blockIdx.x;
     if constexpr (GM != 0) {
@@ -1390,25 +1388,21 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
 
 template <int FMT, int OUT, int GM>
 static int launch_one(const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipStream_t s) {
-    using F = Fmt<FMT>;
-    // raising the dynamic-LDS limit is a per-kernel setting; made once per device, under a lock
-    static std::mutex mu;
-    static std::set<int> configured;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return (int)e;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        if (!configured.count(dev)) {
-            e = hipFuncSetAttribute((const void*)gemm_kernel<FMT, OUT, GM>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    F::LDS);
-            if (e != hipSuccess) return (int)e;
-            configured.insert(dev);
-        }
-    }
     if (tiles <= 0) return 0;
-    hipLaunchKernelGGL((gemm_kernel<FMT, OUT, GM>), dim3((unsigned)tiles), dim3(F::THREADS), F::LDS, s, g, q);
+    hipLaunchKernelGGL((gemm_kernel<FMT, OUT, GM>), dim3((unsigned)tiles), dim3(Fmt<FMT>::THREADS), 0, s, g, q);
     return (int)hipGetLastError();
+}
+
+// Slab-layout MXFP8 codes are read only by the aligned-record main loop; any other scale path
+// would address them as row-major.  The C ABI admits slab operands only where that loop
+// applies; this check keeps every launch path to the same rule.
+static bool slab_ok(const GemmArgs& g, int fmt, int mode) {
+    if (g.slab == 0) return true;
+    if (fmt != 1 || g.K % (MX_GROUP * 64) != 0) return false;
+    if ((((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) != 0) return false;
+    if (mode == 2) return false;                    // K-grouped: group starts are not aligned records
+    if (mode == 1 && (g.slab & 1)) return false;    // M-grouped: group bands cut the token operand
+    return true;
 }
 
 template <int GM>
@@ -1429,6 +1423,7 @@ int launch_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint
                             int c_dtype, void* hip_stream, int slab) {
     if (M == 0 || N == 0) return 0;
     GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K, slab};
+    if (!slab_ok(g, fmt, 0)) return (int)hipErrorInvalidValue;
     const int64_t tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
     return launch_fmt<0>(fmt, c_dtype, g, GroupArgs{nullptr, 0, 0}, tiles, (hipStream_t)hip_stream);
 }
@@ -1446,6 +1441,7 @@ int launch_blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int
     if (groups == 0 || M == 0 || N == 0) return 0;
     GemmArgs g{M, N, K, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, c, a_rows, b_rows, K, slab};
     const GroupArgs q{offsets, groups, mode == 1 ? M : K};
+    if (!slab_ok(g, fmt, mode)) return (int)hipErrorInvalidValue;
     const int64_t tiles = grouped_gemm_workgroups(mode, groups, M, N);
     hipStream_t s = (hipStream_t)hip_stream;
     if (mode == 1) return launch_fmt<1>(fmt, c_dtype, g, q, tiles, s);
