@@ -85,9 +85,10 @@ def lib():
         L.or_nvfp4_quantize_rowscaled.restype = C.c_int
         L.or_blockscaled_gemm_rows.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64,
                                                u8p, u8p, f32p, C.c_int, u8p, u8p, f32p, C.c_int,
-                                               i64p, C.c_int64, i64p, C.c_int64, f64p]
+                                               i64p, C.c_int64, i64p, C.c_int64, f64p, f64p]
         L.or_blockscaled_gemm_rows.restype = C.c_int
         L.or_num_threads.argtypes = []; L.or_num_threads.restype = C.c_int
+        L.or_set_num_threads.argtypes = [C.c_int]; L.or_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -117,6 +118,11 @@ def _signs(signs):
 
 def num_threads() -> int:
     return lib().or_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (OpenMP); the results do not depend on it."""
+    lib().or_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- scalar codecs
@@ -282,16 +288,18 @@ def rht_apply(x, axis: int, signs) -> np.ndarray:
 
 
 def blockscaled_gemm(fmt: int, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc,
-                     rows=None, cols=None) -> np.ndarray:
+                     rows=None, cols=None, with_abs: bool = False):
     """binary64 C = A B^T of the dequantized operands (optionally only rows x cols of C).
     An NVFP4 tensor scale is a number (per-tensor) or an array with one scale per row of
-    that operand (row-scaled)."""
+    that operand (row-scaled).  With ``with_abs`` the result is (C, S), S[m][n] =
+    sum_k |A[m][k] B[n][k]| (what bounds the rounding error of a finite-precision C)."""
     M = a_codes.shape[0]
     N = b_codes.shape[0]
     K = a_codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
     mi = np.ascontiguousarray(np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, np.int64))
     ni = np.ascontiguousarray(np.arange(N, dtype=np.int64) if cols is None else np.asarray(cols, np.int64))
     out = np.zeros((mi.size, ni.size), np.float64)
+    out_abs = np.zeros((mi.size, ni.size), np.float64) if with_abs else None
     u8 = C.c_uint8
     sa = np.ascontiguousarray(np.atleast_1d(np.asarray(a_s_enc, np.float32)))
     sb = np.ascontiguousarray(np.atleast_1d(np.asarray(b_s_enc, np.float32)))
@@ -302,10 +310,11 @@ def blockscaled_gemm(fmt: int, a_codes, a_scales, a_s_enc, b_codes, b_scales, b_
         fmt, M, N, K,
         _p(np.ascontiguousarray(a_codes), u8), _p(np.ascontiguousarray(a_scales), u8), _p(sa, C.c_float), a_rows,
         _p(np.ascontiguousarray(b_codes), u8), _p(np.ascontiguousarray(b_scales), u8), _p(sb, C.c_float), b_rows,
-        _p(mi, C.c_int64), mi.size, _p(ni, C.c_int64), ni.size, _p(out, C.c_double))
+        _p(mi, C.c_int64), mi.size, _p(ni, C.c_int64), ni.size, _p(out, C.c_double),
+        None if out_abs is None else _p(out_abs, C.c_double))
     if st != 0:
         raise ValueError("oracle blockscaled_gemm failed with status %d" % st)
-    return out
+    return (out, out_abs) if with_abs else out
 
 
 GROUP_M, GROUP_K = 1, 2
@@ -319,7 +328,7 @@ def _group_bounds(offsets, g: int, extent: int):
 
 
 def blockscaled_grouped_gemm(fmt: int, mode: int, offsets, a_codes, a_scales, a_s_enc, b_codes, b_scales,
-                             b_s_enc, a_rows: bool = False, b_rows: bool = False) -> np.ndarray:
+                             b_s_enc, a_rows: bool = False, b_rows: bool = False, with_abs: bool = False):
     """One block-scaled GEMM per group, group g covering offsets[g] .. offsets[g+1] of the
     grouped dimension (the grouped GEMM of a mixture-of-experts linear layer: the
     general_grouped_gemm step of the GroupedLinear path in the dispatch flowchart of the page
@@ -330,7 +339,8 @@ def blockscaled_grouped_gemm(fmt: int, mode: int, offsets, a_codes, a_scales, a_
                boundaries are not multiples of 32 is empty (its C_g is 0), as the library
                documents.
     NVFP4 tensor scales: one per group, or (GROUP_M, a_rows / b_rows) one per row of A / of
-    the stacked B.  MXFP8 ignores them."""
+    the stacked B.  MXFP8 ignores them.  With ``with_abs`` the result is (C, S) with S the
+    sums of absolute products, as blockscaled_gemm gives them."""
     G = len(offsets) - 1
     epb = 2 if fmt == FMT_NVFP4 else 1
     blk = 16 if fmt == FMT_NVFP4 else 32
@@ -341,27 +351,30 @@ def blockscaled_grouped_gemm(fmt: int, mode: int, offsets, a_codes, a_scales, a_
     if mode == GROUP_M:
         N = b_codes.shape[1]
         out = np.full((M, N), np.nan)
+        out_abs = np.full((M, N), np.nan)
         for g in range(G):
             o0, o1 = _group_bounds(offsets, g, M)
             if o1 == o0:
                 continue
             s_a = (sa[o0:o1] if a_rows else float(sa[g])) if nv else 1.0
             s_b = (sb[g * N:(g + 1) * N] if b_rows else float(sb[g])) if nv else 1.0
-            out[o0:o1] = blockscaled_gemm(fmt, a_codes[o0:o1], a_scales[o0:o1], s_a,
-                                          b_codes[g], b_scales[g], s_b)
-        return out
+            out[o0:o1], out_abs[o0:o1] = blockscaled_gemm(fmt, a_codes[o0:o1], a_scales[o0:o1], s_a,
+                                                          b_codes[g], b_scales[g], s_b, with_abs=True)
+        return (out, out_abs) if with_abs else out
     K = a_codes.shape[1] * epb
     N = b_codes.shape[0]
     out = np.zeros((G, M, N))
+    out_abs = np.zeros((G, M, N))
     for g in range(G):
         o0, o1 = _group_bounds(offsets, g, K)
         if o1 == o0 or o0 % 32 or (o1 - o0) % 32:
             continue
         cs, ss = slice(o0 // epb, o1 // epb), slice(o0 // blk, o1 // blk)
-        out[g] = blockscaled_gemm(fmt, np.ascontiguousarray(a_codes[:, cs]), np.ascontiguousarray(a_scales[:, ss]),
-                                  float(sa[g]) if nv else 1.0, np.ascontiguousarray(b_codes[:, cs]),
-                                  np.ascontiguousarray(b_scales[:, ss]), float(sb[g]) if nv else 1.0)
-    return out
+        out[g], out_abs[g] = blockscaled_gemm(
+            fmt, np.ascontiguousarray(a_codes[:, cs]), np.ascontiguousarray(a_scales[:, ss]),
+            float(sa[g]) if nv else 1.0, np.ascontiguousarray(b_codes[:, cs]),
+            np.ascontiguousarray(b_scales[:, ss]), float(sb[g]) if nv else 1.0, with_abs=True)
+    return (out, out_abs) if with_abs else out
 
 
 if __name__ == "__main__":

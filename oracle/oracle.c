@@ -549,13 +549,15 @@ static double deq_elem(int fmt, const uint8_t* codes, const uint8_t* scales, dou
  * the rows mi[0..nm) and columns ni[0..nn) of C are computed, into
  * out[nm][nn]; pass every index for the full product.  NVFP4 tensor scales:
  * a_s[0] for every row of A, or a_s[m] for row m when a_per_row (row-scaled
- * operand); likewise b_s for the rows of B.  Ignored for MXFP8. */
+ * operand); likewise b_s for the rows of B.  Ignored for MXFP8.  When out_abs is
+ * not NULL it receives sum_k |A[m][k] * B[n][k]| for the same outputs (the scale
+ * of the rounding-error bound of any finite-precision evaluation of C). */
 int or_blockscaled_gemm_rows(int fmt, int64_t M, int64_t N, int64_t K,
                              const uint8_t* a_codes, const uint8_t* a_scales, const float* a_s,
                              int a_per_row, const uint8_t* b_codes, const uint8_t* b_scales,
                              const float* b_s, int b_per_row,
                              const int64_t* mi, int64_t nm, const int64_t* ni, int64_t nn,
-                             double* out)
+                             double* out, double* out_abs)
 {
     if (fmt == 0 && K % 16 != 0) return -1;
     if (fmt == 1 && K % 32 != 0) return -1;
@@ -581,9 +583,14 @@ int or_blockscaled_gemm_rows(int fmt, int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < nm; ++i)
         for (int64_t j = 0; j < nn; ++j) {
-            double s = 0.0;
-            for (int64_t k = 0; k < K; ++k) s += a[i * K + k] * b[j * K + k];
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = a[i * K + k] * b[j * K + k];
+                s += p;
+                t += fabs(p);
+            }
             out[i * nn + j] = s;
+            if (out_abs) out_abs[i * nn + j] = t;
         }
     free(a);
     free(b);
@@ -598,7 +605,7 @@ int or_blockscaled_gemm(int fmt, int64_t M, int64_t N, int64_t K,
                         double* out)
 {
     return or_blockscaled_gemm_rows(fmt, M, N, K, a_codes, a_scales, &a_s_enc, 0, b_codes, b_scales,
-                                    &b_s_enc, 0, mi, nm, ni, nn, out);
+                                    &b_s_enc, 0, mi, nm, ni, nn, out, NULL);
 }
 
 /* Number of OpenMP threads the oracle uses. */
@@ -608,5 +615,15 @@ int or_num_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Sets the number of OpenMP threads of later oracle calls (n >= 1). */
+void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

@@ -1,9 +1,12 @@
 """GPU parity of the block-scaled GEMM against the CPU oracle (binary64 over the same
 quantized operands).  The bar: relative Frobenius error <= 2e-3 against the oracle
 output rounded as the GPU stores it (bf16 RNE for Y and dX, none for the fp32 dW).
-Small shapes are compared in full (several tiles, ragged M/N, a K tail shorter than
-the K slice); the workload shapes are compared on sampled rows x columns of C, with
-the GEMM launched exactly as the bench launches it."""
+Every compared element must also lie within the rounding-error bound of fp32
+accumulation (assert_gemm_elements).  Small shapes are compared in full (several tiles,
+ragged M/N, a K tail shorter than the K slice); the workload shapes are compared on rows
+x columns of C that include the first and last row and column of every 256-wide band
+(so every output tile is checked), with the GEMM launched exactly as the bench
+launches it."""
 import numpy as np
 import pytest
 import torch
@@ -11,11 +14,20 @@ import torch
 import block_scaled_precision_nvfp4_amd as bsq
 from synthetic import (SEED_DY, SEED_SIGNS, SEED_SR_KEY, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16,
                        outlier_bf16, rht_signs)
-from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, from_slab, note, rel_fro
+from tests.gpu_common import (GEMM_TOL, assert_bytes_equal, assert_f32_equal, assert_gemm_elements, bf16_round,
+                              from_slab, note, rel_fro, stratified)
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+
+
+def sampled_output(y: torch.Tensor, rows=None, cols=None) -> np.ndarray:
+    """C (or rows x cols of it) as float64 on the host, indexed on the device first."""
+    if rows is not None:
+        y = y[torch.from_numpy(np.asarray(rows, np.int64)).to(y.device)][:, torch.from_numpy(
+            np.asarray(cols, np.int64)).to(y.device)]
+    return y.float().cpu().numpy().astype(np.float64)
 
 
 def nv_gemm_check(a_cpu, b_cpu, out_dtype=torch.bfloat16, rows=None, cols=None, label="",
@@ -43,15 +55,16 @@ def nv_gemm_check(a_cpu, b_cpu, out_dtype=torch.bfloat16, rows=None, cols=None, 
         assert_bytes_equal(q[k + "_codes"], r[k + "_codes"], nm + " codes")
         assert_bytes_equal(q[k + "_scales"], r[k + "_scales"], nm + " scales")
         assert_f32_equal(q["s_enc"][i:i + 1], np.asarray(r["s_enc"][i:i + 1], dtype=np.float32), nm + " s_enc")
-    ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, ra[ka + "_codes"], ra[ka + "_scales"], float(ra["s_enc"][ia]),
-                                  rb[kb + "_codes"], rb[kb + "_scales"], float(rb["s_enc"][ib]), rows=rows, cols=cols)
-    yc = y.float().cpu().numpy().astype(np.float64)
-    if rows is not None:
-        yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    ref, sabs = oracle.blockscaled_gemm(oracle.FMT_NVFP4, ra[ka + "_codes"], ra[ka + "_scales"],
+                                        float(ra["s_enc"][ia]), rb[kb + "_codes"], rb[kb + "_scales"],
+                                        float(rb["s_enc"][ib]), rows=rows, cols=cols, with_abs=True)
+    yc = sampled_output(y, rows, cols)
     want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
     err = rel_fro(yc, want)
     note("  rel_fro vs rounded oracle = %.3e, vs exact oracle = %.3e" % (err, rel_fro(yc, ref)))
     assert err <= GEMM_TOL, err
+    K = a_cpu.shape[1] if a_dir == 1 else a_cpu.shape[0]
+    assert_gemm_elements(yc, ref, sabs, K, out_dtype == torch.bfloat16, "nvfp4 " + label)
     return err
 
 
@@ -70,15 +83,17 @@ def mx_gemm_check(a_cpu, b_cpu, a_dir, b_dir, out_dtype=torch.bfloat16, rows=Non
     for q, r, k, nm in ((qa, ra, ka, "A"), (qb, rb, kb, "B")):
         assert_bytes_equal(q[k + "_codes"], r[k + "_codes"], nm + " codes")
         assert_bytes_equal(q[k + "_scales"], r[k + "_scales"], nm + " scales")
-    ref = oracle.blockscaled_gemm(oracle.FMT_MXFP8, ra[ka + "_codes"], ra[ka + "_scales"], 1.0,
-                                  rb[kb + "_codes"], rb[kb + "_scales"], 1.0, rows=rows, cols=cols)
-    yc = y.float().cpu().numpy().astype(np.float64)
-    if rows is not None:
-        yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    ref, sabs = oracle.blockscaled_gemm(oracle.FMT_MXFP8, ra[ka + "_codes"], ra[ka + "_scales"], 1.0,
+                                        rb[kb + "_codes"], rb[kb + "_scales"], 1.0, rows=rows, cols=cols,
+                                        with_abs=True)
+    yc = sampled_output(y, rows, cols)
     want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
     err = rel_fro(yc, want)
     note("  rel_fro vs rounded oracle = %.3e" % err)
     assert err <= GEMM_TOL, err
+    K = a_cpu.shape[1] if a_dir == 1 else a_cpu.shape[0]
+    assert_gemm_elements(yc, ref, sabs, K, out_dtype == torch.bfloat16, "mxfp8 " + label,
+                         mx=(ra[ka + "_codes"], ra[ka + "_scales"], rb[kb + "_codes"], rb[kb + "_scales"], rows, cols))
     return err
 
 
@@ -149,11 +164,13 @@ def test_largest_k(fmt):
     y = bsq.blockscaled_gemm(fmt, t(ac), t(asc), sa, t(bc), t(bsc), sb)
     torch.cuda.synchronize()
     rows, cols = np.array([0, 77, 128, 255]), np.array([0, 31, 200, 255])
-    ref = oracle.blockscaled_gemm(fmt, ac, asc, 1.0, bc, bsc, 1.0, rows=rows, cols=cols)
+    ref, sabs = oracle.blockscaled_gemm(fmt, ac, asc, 1.0, bc, bsc, 1.0, rows=rows, cols=cols, with_abs=True)
     yc = y.float().cpu().numpy().astype(np.float64)[rows][:, cols]
     err = rel_fro(yc, bf16_round(ref))
     note("  rel_fro vs rounded oracle = %.3e" % err)
     assert err <= GEMM_TOL, err
+    assert_gemm_elements(yc, ref, sabs, K, True, "largest K fmt %d" % fmt,
+                         mx=None if fmt == 0 else (ac, asc, bc, bsc, rows, cols))
 
 
 def test_largest_k_slab():
@@ -225,11 +242,14 @@ def test_output_beyond_2g_elements(fmt):
     cols = np.unique(np.concatenate([[0, N // 2, N - 1], rng.choice(N, 13, replace=False)]))
     yc = y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
     del y
-    ref = oracle.blockscaled_gemm(fmt, ra["row_codes"], ra["row_scales"], sa, rb["row_codes"], rb["row_scales"], sb,
-                                  rows=rows, cols=cols)
+    ref, sabs = oracle.blockscaled_gemm(fmt, ra["row_codes"], ra["row_scales"], sa, rb["row_codes"], rb["row_scales"],
+                                        sb, rows=rows, cols=cols, with_abs=True)
     err = rel_fro(yc, bf16_round(ref))
     note("  rel_fro vs rounded oracle = %.3e" % err)
     assert err <= GEMM_TOL, err
+    assert_gemm_elements(yc, ref, sabs, K, True, "output beyond 2^31 fmt %d" % fmt,
+                         mx=None if fmt == 0 else (ra["row_codes"], ra["row_scales"], rb["row_codes"],
+                                                   rb["row_scales"], rows, cols))
 
 
 def test_constant_operands_closed_form():
@@ -261,23 +281,18 @@ def test_wgrad_small_rht_sr_full():
                   out_dtype=torch.float32, a_dir=2, b_dir=2, rounding=1, signs=rht_signs(SEED_SIGNS), label="wgrad-small")
 
 
-def _sample(n, k, seed):
-    rng = np.random.default_rng(seed)
-    idx = np.sort(rng.choice(n, size=min(k, n), replace=False))
-    idx[0], idx[-1] = 0, n - 1
-    return np.unique(idx)
-
-
 def test_fwd_llama3_8b_sampled():
-    """Y[16384, 14336] = X W^T at the Llama-3-8B FFN up-proj shape; 96 x 96 sampled outputs."""
+    """Y[16384, 14336] = X W^T at the Llama-3-8B FFN up-proj shape; every 256 x 256 output tile
+    sampled (192 x 168 outputs)."""
     nv_gemm_check(gaussian_bf16((16384, 4096), 1.0, SEED_X), gaussian_bf16((14336, 4096), STD_W, SEED_W),
-                  rows=_sample(16384, 96, 1), cols=_sample(14336, 96, 2), label="fwd")
+                  rows=stratified(16384, 1), cols=stratified(14336, 2), label="fwd")
 
 
 def test_wgrad_llama3_8b_sampled():
-    """dW[14336, 4096] = dY^T X with RHT + SR columnwise operands (K = 16384 tokens), fp32."""
+    """dW[14336, 4096] = dY^T X with RHT + SR columnwise operands (K = 16384 tokens), fp32;
+    every output tile sampled."""
     nv_gemm_check(gaussian_bf16((16384, 14336), STD_DY, SEED_DY), gaussian_bf16((16384, 4096), 1.0, SEED_X),
-                  out_dtype=torch.float32, rows=_sample(14336, 64, 3), cols=_sample(4096, 64, 4),
+                  out_dtype=torch.float32, rows=stratified(14336, 3), cols=stratified(4096, 4),
                   a_dir=2, b_dir=2, rounding=1, signs=rht_signs(SEED_SIGNS), label="wgrad")
 
 
@@ -287,17 +302,19 @@ def test_hybrid_qwen3_8b_sampled():
     plus the columnwise operand built from the rowwise-dequantized NVFP4 forward value."""
     X = gaussian_bf16((65536, 4096), 1.0, SEED_X)
     W = gaussian_bf16((12288, 4096), STD_W, SEED_W)
-    nv_gemm_check(X, W, rows=_sample(65536, 64, 5), cols=_sample(12288, 64, 6), label="hybrid fwd")
+    nv_gemm_check(X, W, rows=stratified(65536, 5, extra=0), cols=stratified(12288, 6), label="hybrid fwd")
     dY = gaussian_bf16((65536, 12288), STD_DY, SEED_DY)
-    mx_gemm_check(dY, W, 1, 2, rows=_sample(65536, 64, 7), cols=_sample(4096, 64, 8), label="hybrid dgrad")
-    mx_gemm_check(dY, X, 2, 2, out_dtype=torch.float32, rows=_sample(12288, 48, 9), cols=_sample(4096, 48, 10),
+    mx_gemm_check(dY, W, 1, 2, rows=stratified(65536, 7, extra=0), cols=stratified(4096, 8), label="hybrid dgrad")
+    mx_gemm_check(dY, X, 2, 2, out_dtype=torch.float32, rows=stratified(12288, 9), cols=stratified(4096, 10),
                   label="hybrid wgrad")
 
 
-@pytest.mark.parametrize("shape,direction", [((4096, 1024), 2), ((256, 512), 3), ((96, 160), 1), ((200, 64), 1)])
+@pytest.mark.parametrize("shape,direction", [((4096, 1024), 2), ((256, 512), 3), ((96, 160), 1), ((200, 64), 1),
+                                             ((320, 448), 1 | 4), ((320, 448), 3 | 4), ((1088, 128), 1 | 4)])
 def test_fused_requantize_matches_chain(shape, direction):
     """mxfp8_requantize_nvfp4 = mxfp8_quantize(nvfp4_dequantize(.)) bit for bit, against the
-    oracle's chain and the library's own two-call chain (ragged row counts for rowwise)."""
+    oracle's chain and the library's own two-call chain (ragged row counts for rowwise); with
+    MX_SLAB (direction | 4) the codes are compared in the slab layout (ragged last bands)."""
     import oracle
     X = outlier_bf16(shape, seed=shape[0] + 3, mask_seed=shape[1] + 5)
     note("fused requantize %s dir=%d" % (shape, direction))
@@ -308,10 +325,14 @@ def test_fused_requantize_matches_chain(shape, direction):
     torch.cuda.synchronize()
     rq = oracle.nvfp4_quantize(X, direction=1)
     rd = oracle.nvfp4_dequantize(rq["row_codes"], rq["row_scales"], float(rq["s_enc"][0]))
-    rm = oracle.mxfp8_quantize(rd, direction=direction)
+    rm = oracle.mxfp8_quantize(rd, direction=direction & 3)
+    R, C = shape
     for key in (("row",) if direction & 1 else ()) + (("col",) if direction & 2 else ()):
         for part in ("_codes", "_scales"):
-            assert_bytes_equal(f[key + part], rm[key + part], "fused vs oracle " + key + part)
+            got = f[key + part]
+            if direction & 4 and part == "_codes":
+                got = torch.from_numpy(from_slab(got, R, C) if key == "row" else from_slab(got, C, R))
+            assert_bytes_equal(got, rm[key + part], "fused vs oracle " + key + part)
             assert torch.equal(f[key + part], m[key + part]), "fused vs two-call chain " + key + part
 
 
@@ -342,15 +363,15 @@ def slab_dgrad_check(T, N_out, N_in, out_dtype, rows=None, cols=None, label="", 
     assert np.array_equal(gb, rb["col_codes"]), "W slab codes"
     assert_bytes_equal(qa["row_scales"], ra["row_scales"], "dY scales")
     assert_bytes_equal(qb["col_scales"], rb["col_scales"], "W scales")
-    ref = oracle.blockscaled_gemm(oracle.FMT_MXFP8, ra["row_codes"], ra["row_scales"], 1.0,
-                                  rb["col_codes"], rb["col_scales"], 1.0, rows=rows, cols=cols)
-    yc = y.float().cpu().numpy().astype(np.float64)
-    if rows is not None:
-        yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    ref, sabs = oracle.blockscaled_gemm(oracle.FMT_MXFP8, ra["row_codes"], ra["row_scales"], 1.0,
+                                        rb["col_codes"], rb["col_scales"], 1.0, rows=rows, cols=cols, with_abs=True)
+    yc = sampled_output(y, rows, cols)
     want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
     err = rel_fro(yc, want)
     note("  rel_fro = %.3e" % err)
     assert err <= GEMM_TOL, err
+    assert_gemm_elements(yc, ref, sabs, N_out, out_dtype == torch.bfloat16, "slab dgrad " + label,
+                         mx=(ra["row_codes"], ra["row_scales"], rb["col_codes"], rb["col_scales"], rows, cols))
 
 
 @pytest.mark.parametrize("shape", [(320, 448), (64, 64), (1088, 128)])
@@ -387,8 +408,8 @@ def test_mxfp8_slab_operands_ragged(out_dtype, which):
 
 def test_mxfp8_slab_dgrad_llama3_8b_sampled():
     """The slab-layout MXFP8 dgrad at the Llama-3-8B FFN shape, dX[16384, 4096] = dY W with
-    K = 14336, as the bench launches it; 96 x 64 sampled outputs."""
-    slab_dgrad_check(16384, 14336, 4096, torch.bfloat16, rows=_sample(16384, 96, 11), cols=_sample(4096, 64, 12),
+    K = 14336, as the bench launches it; every output tile sampled."""
+    slab_dgrad_check(16384, 14336, 4096, torch.bfloat16, rows=stratified(16384, 11), cols=stratified(4096, 12),
                      label="llama3-8b")
 
 

@@ -9,14 +9,16 @@ K-grouped (per-expert wgrad): MXFP8 operands quantized columnwise over all token
 operands quantized per group, empty and misaligned groups (computed as empty).  Operands
 are quantized on the GPU and by the oracle from the same bf16 inputs and must agree bit for
 bit before the GEMMs are compared (relative Frobenius error <= 2e-3 against the oracle
-output rounded as the GPU stores it)."""
+output rounded as the GPU stores it, and every element within the rounding-error bound of
+fp32 accumulation)."""
 import numpy as np
 import pytest
 import torch
 
 import block_scaled_precision_nvfp4_amd as bsq
 from synthetic import STD_W, gaussian_bf16, outlier_bf16
-from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, from_slab, note, rel_fro
+from tests.gpu_common import (GEMM_TOL, assert_bytes_equal, assert_f32_equal, assert_gemm_elements, bf16_round,
+                              from_slab, mxfp8_mfma_model, note, rel_fro, stratified)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,11 +29,12 @@ def splits_to_offsets(first, sizes):
     return [first] + list(first + np.cumsum(sizes))
 
 
-def check_close(got64, ref64, out_dtype, what):
+def check_close(got64, ref64, out_dtype, what, sabs, K, model=None):
     want = bf16_round(ref64) if out_dtype == torch.bfloat16 else ref64
     err = rel_fro(got64, want)
     note("  %s rel_fro = %.3e" % (what, err))
     assert err <= GEMM_TOL, (what, err)
+    assert_gemm_elements(got64, ref64, sabs, K, out_dtype == torch.bfloat16, what, model=model)
 
 
 def nv_experts(G, N, K, seed):
@@ -82,12 +85,23 @@ def run_m_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, out_dtype, a_rows
     f = fmt | (bsq.FMT_A_ROWSCALED if a_rows else 0) | layout
     bsq.blockscaled_grouped_gemm(f, bsq.GROUP_M, o, *a_gpu, *b_gpu, out_dtype=out_dtype, out=out)
     torch.cuda.synchronize()
-    ref = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_M, offs, *a_ref, *b_ref, a_rows=a_rows)
+    ref, sabs = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_M, offs, *a_ref, *b_ref, a_rows=a_rows,
+                                                with_abs=True)
     got = out.float().cpu().numpy().astype(np.float64)
     inside = ~np.isnan(ref[:, 0])
     assert np.all(got[~inside] == 1.0), "rows outside every group were written"
+    K = a_ref[0].shape[1] * (2 if fmt == bsq.FMT_NVFP4 else 1)
     if inside.any():
-        check_close(got[inside], ref[inside], out_dtype, label)
+        model = None
+        if fmt == bsq.FMT_MXFP8:
+            # the FP8 MFMA instruction model, group by group: that group's rows of A against its B
+            model = np.full(ref.shape, np.nan)
+            for g in range(len(offs) - 1):
+                o0, o1 = offs[g], offs[g + 1]
+                if o1 > o0:
+                    model[o0:o1] = mxfp8_mfma_model(a_ref[0][o0:o1], a_ref[1][o0:o1], b_ref[0][g], b_ref[1][g])
+            model = model[inside]
+        check_close(got[inside], ref[inside], out_dtype, label, sabs[inside], K, model=model)
 
 
 @pytest.mark.parametrize("K", [512, 160])
@@ -183,13 +197,18 @@ def run_k_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, label=""):
     o = torch.tensor(offs, dtype=torch.int64, device=DEV)
     out = bsq.blockscaled_grouped_gemm(fmt, bsq.GROUP_K, o, *a_gpu, *b_gpu, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    ref = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_K, offs, *a_ref, *b_ref)
+    ref, sabs = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_K, offs, *a_ref, *b_ref, with_abs=True)
     got = out.cpu().numpy().astype(np.float64)
     for g in range(len(offs) - 1):
+        o0, o1 = offs[g], offs[g + 1]
         if not ref[g].any():
             assert not got[g].any(), "group %d should be zero" % g
         else:
-            check_close(got[g], ref[g], torch.float32, "%s group %d" % (label, g))
+            model = None
+            if fmt == bsq.FMT_MXFP8:   # the group's K range of the whole-token operands
+                model = mxfp8_mfma_model(a_ref[0][:, o0:o1], a_ref[1][:, o0 // 32:o1 // 32],
+                                         b_ref[0][:, o0:o1], b_ref[1][:, o0 // 32:o1 // 32])
+            check_close(got[g], ref[g], torch.float32, "%s group %d" % (label, g), sabs[g], o1 - o0, model=model)
 
 
 def test_k_grouped_mxfp8_wgrad():
@@ -292,7 +311,9 @@ def test_k_grouped_nvfp4_per_group_scales():
 
 def test_grouped_moe_fprop_sampled():
     """A mixture-of-experts fprop at a realistic size: 8 experts, 16384 routed tokens,
-    K = 4096, N = 2048, row-scaled NVFP4 inputs; compared on sampled rows x columns."""
+    K = 4096, N = 2048, row-scaled NVFP4 inputs; compared on rows x columns that include the
+    first and last row and column of every 256-wide band of each group's output (every output
+    tile of every group)."""
     import oracle
     G, T, N, K = 8, 16384, 2048, 4096
     rng = np.random.default_rng(41)
@@ -308,11 +329,12 @@ def test_grouped_moe_fprop_sampled():
     torch.cuda.synchronize()
     r = oracle.nvfp4_quantize_rowscaled(x)
     assert_bytes_equal(q["codes"], r["codes"], "row-scaled codes")
-    cols = np.sort(rng.choice(N, 64, replace=False))
-    yc = y.float().cpu().numpy().astype(np.float64)
+    cols = stratified(N, 43)
     for g in range(G):
         o0, o1 = offs[g], offs[g + 1]
-        rows = np.sort(rng.choice(np.arange(o0, o1), min(12, o1 - o0), replace=False))
-        ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, r["codes"][o0:o1], r["scales"][o0:o1], r["s_enc"][o0:o1],
-                                      b_ref[0][g], b_ref[1][g], float(b_ref[2][g]), rows=rows - o0, cols=cols)
-        check_close(yc[rows][:, cols], ref, torch.bfloat16, "expert %d" % g)
+        rows = o0 + stratified(o1 - o0, 44 + g)
+        yc = y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy()
+        ref, sabs = oracle.blockscaled_gemm(oracle.FMT_NVFP4, r["codes"][o0:o1], r["scales"][o0:o1],
+                                            r["s_enc"][o0:o1], b_ref[0][g], b_ref[1][g], float(b_ref[2][g]),
+                                            rows=rows - o0, cols=cols, with_abs=True)
+        check_close(yc.astype(np.float64), ref, torch.bfloat16, "expert %d" % g, sabs, K)

@@ -16,7 +16,8 @@ import torch
 
 import block_scaled_precision_nvfp4_amd as bsq
 from synthetic import SEED_SIGNS, SEED_SR_KEY, SEED_X, STD_W, gaussian_bf16, outlier_bf16, rht_signs
-from tests.gpu_common import GEMM_TOL, assert_bytes_equal, assert_f32_equal, bf16_round, note, rel_fro
+from tests.gpu_common import (GEMM_TOL, assert_bytes_equal, assert_f32_equal, assert_gemm_elements, bf16_round, note,
+                              rel_fro, stratified)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,10 +138,11 @@ def rowscaled_gemm_check(M, N, K, a_rows, b_rows, out_dtype=torch.bfloat16, rows
         assert_bytes_equal(gc, rc, nm + " codes")
         assert_bytes_equal(gs, rs, nm + " scales")
         assert_f32_equal(gS, np.atleast_1d(np.asarray(rS, np.float32)), nm + " s_enc")
-    ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, *refs[0], *refs[1], rows=rows, cols=cols)
+    ref, sabs = oracle.blockscaled_gemm(oracle.FMT_NVFP4, *refs[0], *refs[1], rows=rows, cols=cols, with_abs=True)
     yc = y.float().cpu().numpy().astype(np.float64)
     if rows is not None:
         yc = yc[np.asarray(rows)][:, np.asarray(cols)]
+    assert_gemm_elements(yc, ref, sabs, K, out_dtype == torch.bfloat16, "row-scaled " + label)
     want = bf16_round(ref) if out_dtype == torch.bfloat16 else ref
     # relative error per output row, so that rows of small magnitude count as much as large
     den = np.maximum(np.linalg.norm(want, axis=1), 1e-300)
@@ -180,7 +182,8 @@ def test_rowscaled_gemm_equal_scales_is_bitwise_per_tensor():
 
 def test_rowscaled_gemm_llama3_8b_fprop_sampled():
     """Forward GEMM of the Llama-3-8B FFN up-projection with row-scaled activations
-    [16384, 4096] and per-tensor weights [14336, 4096], compared on sampled rows x cols."""
+    [16384, 4096] and per-tensor weights [14336, 4096], compared on rows x cols that touch
+    every output tile."""
     import oracle
     M, N, K = 16384, 14336, 4096
     note("nvfp4 gemm rowscaled llama3-8b fprop")
@@ -195,12 +198,11 @@ def test_rowscaled_gemm_llama3_8b_fprop_sampled():
     rb = oracle.nvfp4_quantize(w, direction=oracle.ROW)
     assert_bytes_equal(qa["codes"], ra["codes"], "A codes")
     assert_f32_equal(qa["s_enc"], ra["s_enc"], "A s_enc")
-    rng = np.random.default_rng(76)
-    rows = np.sort(rng.choice(M, 96, replace=False))
-    cols = np.sort(rng.choice(N, 96, replace=False))
-    ref = oracle.blockscaled_gemm(oracle.FMT_NVFP4, ra["codes"], ra["scales"], ra["s_enc"], rb["row_codes"],
-                                  rb["row_scales"], float(rb["s_enc"][0]), rows=rows, cols=cols)
-    yc = y.float().cpu().numpy().astype(np.float64)[rows][:, cols]
+    rows, cols = stratified(M, 76), stratified(N, 77)
+    ref, sabs = oracle.blockscaled_gemm(oracle.FMT_NVFP4, ra["codes"], ra["scales"], ra["s_enc"], rb["row_codes"],
+                                        rb["row_scales"], float(rb["s_enc"][0]), rows=rows, cols=cols, with_abs=True)
+    yc = y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
     err = rel_fro(yc, bf16_round(ref))
     note("  rel_fro = %.3e" % err)
     assert err <= GEMM_TOL, err
+    assert_gemm_elements(yc, ref, sabs, K, True, "row-scaled llama3-8b fprop")

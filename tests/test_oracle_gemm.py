@@ -97,6 +97,14 @@ def test_matches_numpy_matmul_of_dequantized(orc):
                                qb["row_codes"], qb["row_scales"], qb["s_enc"][0],
                                rows=[39, 0, 7], cols=[3, 23])
     assert np.array_equal(sub, got[[39, 0, 7]][:, [3, 23]])
+    # the sum of absolute products (the error-bound scale the GPU parity gates use) is the
+    # product of the absolute dequantized operands, and at least |C|
+    c2, s2 = orc.blockscaled_gemm(orc.FMT_NVFP4, qa["row_codes"], qa["row_scales"], qa["s_enc"][0],
+                                  qb["row_codes"], qb["row_scales"], qb["s_enc"][0], rows=[39, 0, 7], cols=[3, 23],
+                                  with_abs=True)
+    assert np.array_equal(c2, sub)
+    np.testing.assert_allclose(s2, (np.abs(deq(qa)) @ np.abs(deq(qb)).T)[[39, 0, 7]][:, [3, 23]], rtol=1e-12)
+    assert np.all(s2 >= np.abs(c2))
 
 
 def test_quantized_gemm_close_to_exact_product(orc):
