@@ -62,14 +62,22 @@ def parse():
 
 GEMM_SOURCES = ("block_scaled_precision_nvfp4_amd/csrc/gemm.hip",
                 "block_scaled_precision_nvfp4_amd/csrc/device_common.hpp")
-TRAFFIC_SUMMARY = "profiles/gemm_nvfp4_fwd_llama3_8b_hbm_traffic.md"
+QUANT_SOURCES = ("block_scaled_precision_nvfp4_amd/csrc/quantize.hip",
+                 "block_scaled_precision_nvfp4_amd/csrc/device_common.hpp")
+# HBM traffic per launch (hardware counters) of the kernels the line reports a roofline for:
+# the summary under profiles/ and the sources it was taken on
+TRAFFIC = {
+    "gemm_fwd_nvfp4": ("profiles/gemm_nvfp4_fwd_llama3_8b_hbm_traffic.md", GEMM_SOURCES),
+    "gemm_wgrad_nvfp4": ("profiles/gemm_nvfp4_wgrad_llama3_8b_hbm_traffic.md", GEMM_SOURCES),
+    "quant_dy_col_rht_sr": ("profiles/nvfp4_col_rht_sr_dy_llama3_8b_hbm_traffic.md", QUANT_SOURCES),
+}
 
 
-def gemm_source_hash(root: str = ROOT) -> str:
-    """SHA-256 of the GEMM kernel sources with comments and blank lines dropped: counters taken
-    on the same code stay valid across comment edits."""
+def source_hash(files=GEMM_SOURCES, root: str = ROOT) -> str:
+    """SHA-256 of kernel sources with comments and blank lines dropped: counters taken on the
+    same code stay valid across comment edits."""
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES:
+    for rel in files:
         with open(os.path.join(root, rel)) as f:
             for line in f:
                 code = line.split("//", 1)[0].rstrip()
@@ -78,10 +86,11 @@ def gemm_source_hash(root: str = ROOT) -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the forward NVFP4 GEMM from the committed counter summary,
-    or None when the summary is absent or was taken on different GEMM sources."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+def measured_traffic(key: str):
+    """HBM bytes per launch of a kernel (group) from its committed counter summary, or None
+    when the summary is absent or was taken on other sources."""
+    rel, files = TRAFFIC[key]
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None
     rec = None
@@ -89,7 +98,7 @@ def measured_traffic():
         for line in f:
             if line.startswith("traffic-record: "):
                 rec = json.loads(line[len("traffic-record: "):])
-    if rec is None or rec.get("source_sha256") != gemm_source_hash():
+    if rec is None or rec.get("source_sha256") != source_hash(files):
         return None
     return rec
 
@@ -127,6 +136,9 @@ class Step:
         self.signs = rht_signs(SEED_SIGNS).to(dev)
         self.seed = 42
         self.dev = dev
+        # scratch of the NVFP4 quantize calls (their per-workgroup partial maxima); the step's
+        # calls run in stream order, so one workspace serves them all
+        self.qws = torch.empty(bsq.NVFP4_QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
         self.mx_rows = mx_rows
         self.ev = {}
 
@@ -138,24 +150,33 @@ class Step:
 
     def run(self, marks=()):
         """One step.  Event pairs are recorded around the kernel groups named in ``marks``
-        (each marker pair is a stream barrier, so the throughput loop records only the pair
-        around the forward GEMM)."""
+        (each pair is a stream barrier, so the throughput loop records only the pairs around
+        the two NVFP4 GEMMs):
+          q_fwd  NVFP4 rowwise RNE of X and W        g_fwd    forward NVFP4 GEMM
+          q_dy   NVFP4 columnwise RHT + SR of dY      q_xc     the same of X
+          g_wgrad  wgrad NVFP4 GEMM                   q_mx     MXFP8 rowwise dY + requantized W
+          g_dgrad  dgrad MXFP8 GEMM"""
         bsq, torch = self.bsq, self.torch
         mark = (lambda name: self._ev(name) if name[:-1] in marks else None)
         # fwd
         mark("q_fwd0")
-        qx = bsq.nvfp4_quantize(self.X, direction=bsq.ROW)
-        qw = bsq.nvfp4_quantize(self.W, direction=bsq.ROW)
+        ws = self.qws
+        qx = bsq.nvfp4_quantize(self.X, direction=bsq.ROW, workspace=ws)
+        qw = bsq.nvfp4_quantize(self.W, direction=bsq.ROW, workspace=ws)
         mark("q_fwd1")
         mark("g_fwd0")
         y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qx["row_codes"], qx["row_scales"], qx["s_enc"][0:1],
                                  qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], out_dtype=torch.bfloat16)
         mark("g_fwd1")
         # wgrad
+        mark("q_dy0")
         qdy = bsq.nvfp4_quantize(self.dY, direction=bsq.COL, rounding=bsq.SR, sr_seed=self.seed, sr_stream=0,
-                                 rht_signs=self.signs)
+                                 rht_signs=self.signs, workspace=ws)
+        mark("q_dy1")
+        mark("q_xc0")
         qxc = bsq.nvfp4_quantize(self.X, direction=bsq.COL, rounding=bsq.SR, sr_seed=self.seed, sr_stream=1,
-                                 rht_signs=self.signs)
+                                 rht_signs=self.signs, workspace=ws)
+        mark("q_xc1")
         mark("g_wgrad0")
         dw = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qdy["col_codes"], qdy["col_scales"], qdy["s_enc"][1:2],
                                   qxc["col_codes"], qxc["col_scales"], qxc["s_enc"][1:2], out_dtype=torch.float32)
@@ -163,8 +184,10 @@ class Step:
         # dgrad (MXFP8 backward operands; W from its rowwise-dequantized NVFP4 value), codes in
         # the GEMM's slab layout unless the row-major layout is asked for
         lay, fmx = (0, bsq.FMT_MXFP8) if self.mx_rows else (bsq.MX_SLAB, bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB)
+        mark("q_mx0")
         mdy = bsq.mxfp8_quantize(self.dY, direction=bsq.ROW | lay)
         mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL | lay)
+        mark("q_mx1")
         mark("g_dgrad0")
         dx = bsq.blockscaled_gemm(fmx, mdy["row_codes"], mdy["row_scales"], None,
                                   mw["col_codes"], mw["col_scales"], None, out_dtype=torch.bfloat16)
@@ -231,11 +254,13 @@ def quant_only_figures(dev, peaks, iters: int = 10):
     R, C = 8192, 4096
     base = outlier_bf16((R, C)).to(dev)
     xs = [base.clone() for _ in range(4)]
+    ws = torch.empty(bsq.NVFP4_QUANTIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     n = R * C
     cases = {
-        "nvfp4_row_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.ROW), 2.0 + 0.5625),
-        "nvfp4_col_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.COL), 2.0 + 0.5625),
-        "nvfp4_row_col_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.ROW | bsq.COL), 2.0 + 2 * 0.5625),
+        "nvfp4_row_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.ROW, workspace=ws), 2.0 + 0.5625),
+        "nvfp4_col_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.COL, workspace=ws), 2.0 + 0.5625),
+        "nvfp4_row_col_rne": (lambda x: bsq.nvfp4_quantize(x, direction=bsq.ROW | bsq.COL, workspace=ws),
+                              2.0 + 2 * 0.5625),
         "mxfp8_row": (lambda x: bsq.mxfp8_quantize(x, direction=bsq.ROW), 2.0 + 1.03125),
         "mxfp8_col": (lambda x: bsq.mxfp8_quantize(x, direction=bsq.COL), 2.0 + 1.03125),
     }
@@ -398,10 +423,14 @@ def grouped_figures(step, iters: int):
 
 
 def cpu_baseline(tokens: int):
-    """The oracle on a token-sample of the step: the same operations with M = tokens."""
-    import numpy as np
+    """The oracle on the host cores: (1) the step on a token sample (the same operations with
+    M = tokens; all threads), the headline value; (2) the full quantize-only workload
+    ([8192, 4096] with 1 % outliers: NVFP4 rowwise, NVFP4 columnwise, MXFP8 rowwise) with all
+    threads and with one.  GB/s are the algorithmic bytes of the GPU figures."""
     import oracle
-    from synthetic import (SEED_DY, SEED_SIGNS, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16, rht_signs)
+    from synthetic import (SEED_DY, SEED_SIGNS, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16, outlier_bf16,
+                           rht_signs)
+    threads = oracle.num_threads()
     X = gaussian_bf16((tokens, K_IN), 1.0, SEED_X)
     W = gaussian_bf16((N_OUT, K_IN), STD_W, SEED_W)
     dY = gaussian_bf16((tokens, N_OUT), STD_DY, SEED_DY)
@@ -422,8 +451,44 @@ def cpu_baseline(tokens: int):
                             mw["col_codes"], mw["col_scales"], 1.0)
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * tokens * N_OUT * K_IN
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "the full step with %d of %d tokens (M = %d); %.1f s on the host" % (tokens, M_TOK, tokens, dt)}
+
+    xq = outlier_bf16((8192, 4096))
+    n = xq.numel()
+    casts = (("nvfp4_row", lambda: oracle.nvfp4_quantize(xq, direction=oracle.ROW), 2.5625),
+             ("nvfp4_col", lambda: oracle.nvfp4_quantize(xq, direction=oracle.COL), 2.5625),
+             ("mxfp8_row", lambda: oracle.mxfp8_quantize(xq, direction=oracle.ROW), 2.0 + 1.03125))
+
+    def quant_only(nthreads):
+        oracle.set_num_threads(nthreads)
+        out = {"threads": oracle.num_threads()}
+        for name, fn, bpe in casts:
+            t = time.perf_counter()
+            fn()
+            sec = time.perf_counter() - t
+            out[name] = {"s": round(sec, 3), "GBps": round(bpe * n / sec / 1e9, 2)}
+        return out
+    q_all = quant_only(threads)
+    q_one = quant_only(1)
+    oracle.set_num_threads(threads)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "the full step with %d of %d tokens (M = %d), %d threads; %.1f s" % (tokens, M_TOK, tokens, threads, dt),
+            "host_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+            "quant_only_full": {"shape": [8192, 4096], "all_threads": q_all, "one_thread": q_one}}
+
+
+def roofline_entry(bound, achieved, peak, unit, kernel, algorithmic_bytes, traffic_key=None, **extra):
+    """One roofline object: achieved / peak for a kernel, with the counter-measured HBM traffic
+    per launch when a summary taken on the current sources exists."""
+    tr = measured_traffic(traffic_key) if traffic_key else None
+    e = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": None if tr is None else tr["traffic_bytes"],
+         "algorithmic_bytes": int(algorithmic_bytes), "kernel": kernel}
+    e.update(extra)
+    return e
 
 
 def main():
@@ -448,22 +513,24 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
     for _ in range(args.steps):
-        step.run(marks=("g_fwd",))
+        step.run(marks=("g_fwd", "g_wgrad"))
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
     gemm_flops = 2.0 * M_TOK * N_OUT * K_IN
     value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
-    g_fwd = step.avg_ms("g_fwd")   # the dominant kernel, timed inside the timed steps
+    # the two NVFP4 GEMMs (the longest kernels of the step), timed inside the timed steps
+    g_fwd = step.avg_ms("g_fwd")
+    g_wgrad = step.avg_ms("g_wgrad")
 
     # per-group breakdown in separate, untimed steps (the marker barriers would add gaps)
     for _ in range(max(2, args.steps // 2)):
-        step.run(marks=("q_fwd", "g_wgrad", "g_dgrad"))
+        step.run(marks=("q_fwd", "q_dy", "q_xc", "q_mx", "g_dgrad"))
     torch.cuda.synchronize()
-    g_wgrad = step.avg_ms("g_wgrad")
     g_dgrad = step.avg_ms("g_dgrad")
-    q_fwd = step.avg_ms("q_fwd")
+    q_fwd, q_dy, q_xc, q_mx = (step.avg_ms(k) for k in ("q_fwd", "q_dy", "q_xc", "q_mx"))
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
+    dy_bytes = NVFP4_BYTES_PER_ELT * M_TOK * N_OUT
     peaks = measured_peaks(dev)
     side = moe = layer = qwen = quant_only = None
     if not args.no_side_figures:
@@ -472,17 +539,59 @@ def main():
         moe = grouped_figures(step, max(3, args.steps // 2))
         layer = linear_layer_figures(step, max(3, args.steps // 2))
         qwen = qwen3_8b_hybrid_figures(dev, 3, args.mx_row_major)
-    fwd_tflops = gemm_flops / (g_fwd * 1e-3) / 1e12
-    tr = measured_traffic()
-    # algorithmic bytes of one forward GEMM launch: both operands' codes and scales once, Y once
-    algo_bytes = (M_TOK + N_OUT) * K_IN * (0.5 + 1.0 / 16) + 2.0 * M_TOK * N_OUT
-    roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fwd_tflops / F16_MFMA_PEAK_TFLOPS, 4),
-                "measured_peak": peaks["mfma_f16_32x32x16_TFLOPs"],
-                "frac_of_measured": round(fwd_tflops / peaks["mfma_f16_32x32x16_TFLOPs"], 4),
-                "traffic": None if tr is None else tr["traffic_bytes"],
-                "algorithmic_bytes": int(algo_bytes),
-                "kernel": "gemm_nvfp4 (fwd, f16 MFMA with in-register dequant)"}
+    tflops = lambda ms: gemm_flops / (ms * 1e-3) / 1e12
+    gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    # algorithmic bytes of one GEMM launch: both operands' codes and scales once, C once
+    nv_op = 0.5 + 1.0 / 16
+    algo = {"fwd": (M_TOK + N_OUT) * K_IN * nv_op + 2.0 * M_TOK * N_OUT,
+            "wgrad": (N_OUT + K_IN) * M_TOK * nv_op + 4.0 * N_OUT * K_IN,
+            "dgrad": (M_TOK + K_IN) * N_OUT * 1.03125 + 2.0 * M_TOK * K_IN}
+    gemms = {
+        "fwd_nvfp4": roofline_entry("mfma", tflops(g_fwd), F16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+                                    "gemm_kernel<2,0,0>: NVFP4 fwd Y = X W^T, f16 MFMA with in-register dequant",
+                                    algo["fwd"], "gemm_fwd_nvfp4", ms=round(g_fwd, 4),
+                                    frac_of_measured=round(tflops(g_fwd) / peaks["mfma_f16_32x32x16_TFLOPs"], 4)),
+        "wgrad_nvfp4": roofline_entry("mfma", tflops(g_wgrad), F16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+                                      "gemm_kernel<2,1,0>: NVFP4 wgrad dW = dY^T X (fp32 out), f16 MFMA",
+                                      algo["wgrad"], "gemm_wgrad_nvfp4", ms=round(g_wgrad, 4),
+                                      frac_of_measured=round(tflops(g_wgrad) / peaks["mfma_f16_32x32x16_TFLOPs"], 4)),
+        "dgrad_mxfp8": roofline_entry("mfma", tflops(g_dgrad), FP8_MFMA_PEAK_TFLOPS, "TFLOP/s",
+                                      "gemm_kernel<1,0,0>: MXFP8 dgrad dX = dY W, scaled fp8 MFMA", algo["dgrad"],
+                                      ms=round(g_dgrad, 4),
+                                      frac_of_measured=round(tflops(g_dgrad) / peaks["mfma_fp8_32x32x64_TFLOPs"], 4)),
+    }
+    # the roofline of the dominant kernel: the NVFP4 GEMM with the longer average launch
+    dominant = "wgrad_nvfp4" if g_wgrad >= g_fwd else "fwd_nvfp4"
+    roofline = dict(gemms[dominant])
+    roofline["measured_peak"] = peaks["mfma_f16_32x32x16_TFLOPs"]
+    # quantization rooflines: HBM-bound; an NVFP4 cast with a per-tensor amax reads its input
+    # twice (amax pass, encode pass), so besides the fraction of 8 TB/s the entry gives the
+    # fraction of what two reads + one write allow at 8 TB/s
+    two_pass = lambda bpe_write: (2.0 + bpe_write) / (4.0 + bpe_write)
+    quant = {
+        "dy_col_rht_sr": roofline_entry(
+            "hbm", gbps(dy_bytes, q_dy), HBM_PEAK_GBPS, "GB/s",
+            "nvfp4_amax_rht_kernel<2> + nvfp4_encode_kernel<2,true,true>: NVFP4 columnwise RHT16 + Philox SR of "
+            "dY[16384,14336]", dy_bytes, "quant_dy_col_rht_sr", us=round(q_dy * 1e3, 2),
+            two_pass_bound_frac=round(gbps(dy_bytes, q_dy) / (HBM_PEAK_GBPS * two_pass(0.5625)), 4)),
+        "x_col_rht_sr": roofline_entry(
+            "hbm", gbps(NVFP4_BYTES_PER_ELT * M_TOK * K_IN, q_xc), HBM_PEAK_GBPS, "GB/s",
+            "NVFP4 columnwise RHT16 + Philox SR of X[16384,4096]", NVFP4_BYTES_PER_ELT * M_TOK * K_IN,
+            us=round(q_xc * 1e3, 2)),
+        "fwd_row_rne_XW": roofline_entry(
+            "hbm", gbps(q_bytes, q_fwd), HBM_PEAK_GBPS, "GB/s", "NVFP4 rowwise RNE of X and W (two passes each)",
+            q_bytes, us=round(q_fwd * 1e3, 2),
+            two_pass_bound_frac=round(gbps(q_bytes, q_fwd) / (HBM_PEAK_GBPS * two_pass(0.5625)), 4)),
+        "mx_dgrad_operands": roofline_entry(
+            "hbm", gbps(M_TOK * N_OUT * 3.03125 + N_OUT * K_IN * (0.5625 + 1.03125), q_mx), HBM_PEAK_GBPS, "GB/s",
+            "MXFP8 rowwise of dY + MXFP8 columnwise of W from its NVFP4 codes (one pass each)",
+            M_TOK * N_OUT * 3.03125 + N_OUT * K_IN * (0.5625 + 1.03125), us=round(q_mx * 1e3, 2)),
+    }
+    if quant_only is not None:
+        for name, e in quant_only.items():
+            if name.startswith("nvfp4") and isinstance(e, dict):
+                w = 2 * 0.5625 if name == "nvfp4_row_col_rne" else 0.5625
+                e["two_pass_bound_frac"] = round(e["GBps"] / (HBM_PEAK_GBPS * two_pass(w)), 4)
     line = {
         "metric": "NVFP4 quant GB/s + block-scaled GEMM TFLOP/s at Llama-3-8B FFN shape",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -492,21 +601,25 @@ def main():
                    "tokens": M_TOK, "in_features": K_IN, "out_features": N_OUT,
                    "fwd": "NVFP4 row RNE", "wgrad": "NVFP4 col RHT16+SR", "dgrad": "MXFP8 (W from rowwise-dequantized)",
                    "mxfp8_code_layout": "row-major" if args.mx_row_major else "slab"},
-        "nvfp4_quant_GBps": round(q_bytes / (q_fwd * 1e-3) / 1e9, 1),
-        "nvfp4_quant_frac": {"of_peak_8TBps": round(q_bytes / (q_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                             "of_measured_copy": round(q_bytes / (q_fwd * 1e-3) / 1e9 / peaks["copy_GBps"], 4)},
-        "nvfp4_gemm_TFLOPs": round(fwd_tflops, 2),
-        "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "gemm_fwd_nvfp4": round(g_fwd, 4),
-                      "gemm_wgrad_nvfp4": round(g_wgrad, 4), "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
-        "mxfp8_gemm_TFLOPs": round(gemm_flops / (g_dgrad * 1e-3) / 1e12, 2),
-        "mxfp8_gemm_frac": {"of_peak": round(gemm_flops / (g_dgrad * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
-                            "of_measured": round(gemm_flops / (g_dgrad * 1e-3) / 1e12 / peaks["mfma_fp8_32x32x64_TFLOPs"], 4)},
+        "nvfp4_quant_GBps": round(gbps(q_bytes, q_fwd), 1),
+        "nvfp4_quant_frac": {"of_peak_8TBps": round(gbps(q_bytes, q_fwd) / HBM_PEAK_GBPS, 4),
+                             "of_measured_copy": round(gbps(q_bytes, q_fwd) / peaks["copy_GBps"], 4)},
+        "nvfp4_gemm_TFLOPs": round(tflops(g_fwd), 2),
+        "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "nvfp4_quant_dy_col": round(q_dy, 4),
+                      "nvfp4_quant_x_col": round(q_xc, 4), "mxfp8_casts_dgrad": round(q_mx, 4),
+                      "gemm_fwd_nvfp4": round(g_fwd, 4), "gemm_wgrad_nvfp4": round(g_wgrad, 4),
+                      "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
+        "mxfp8_gemm_TFLOPs": round(tflops(g_dgrad), 2),
+        "mxfp8_gemm_frac": {"of_peak": round(tflops(g_dgrad) / FP8_MFMA_PEAK_TFLOPS, 4),
+                            "of_measured": round(tflops(g_dgrad) / peaks["mfma_fp8_32x32x64_TFLOPs"], 4)},
         "measured_peaks": peaks,
         "quant_only": quant_only,
         "row_scaled": side,
         "moe_grouped": moe,
         "nvfp4_linear_layer": layer,
         "qwen3_8b_hybrid": qwen,
+        "gemm_rooflines": gemms,
+        "quant_rooflines": quant,
         "roofline": roofline,
         "cpu_baseline": None,
     }
