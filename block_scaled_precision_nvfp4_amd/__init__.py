@@ -51,6 +51,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         vp, i64, i32, u32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize_noalloc.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_rowscaled.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp]
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
@@ -64,7 +65,8 @@ def lib():
         L.nvfp4_linear_saved_bytes.restype = C.c_int64
         L.nvfp4_linear_forward.argtypes = [vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_backward.argtypes = [vp, vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
-        for f in ("nvfp4_linear_forward", "nvfp4_linear_backward", "nvfp4_quantize", "nvfp4_quantize_rowscaled",
+        for f in ("nvfp4_linear_forward", "nvfp4_linear_backward", "nvfp4_quantize", "nvfp4_quantize_noalloc",
+                  "nvfp4_quantize_rowscaled",
                   "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
                   "blockscaled_gemm", "blockscaled_grouped_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int

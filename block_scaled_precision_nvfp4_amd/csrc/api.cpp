@@ -52,11 +52,12 @@ int bsq_version(void) { return 100; }
 
 const char* bsq_last_error(void) { return g_last_error.c_str(); }
 
-int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding, uint64_t sr_seed,
-                   uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
-                   uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out, void* workspace,
-                   void* hip_stream) {
-    static const char* fn = "nvfp4_quantize";
+// Argument checks shared by nvfp4_quantize and nvfp4_quantize_noalloc (need_ws: the call takes
+// a workspace argument).
+static int nvfp4_quantize_check(const char* fn, const void* x, int64_t rows, int64_t cols, int direction,
+                                int rounding, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
+                                uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out,
+                                bool need_ws, void* workspace) {
     if (direction < 1 || direction > 3) return fail(BSQ_ERR_ARG, "%s: direction must be 1 (row), 2 (col) or 3, got %d", fn, direction);
     if (rounding != BSQ_RNE && rounding != BSQ_SR) return fail(BSQ_ERR_ARG, "%s: rounding must be 0 (RNE) or 1 (SR), got %d", fn, rounding);
     if (rows < 0 || cols < 0) return fail(BSQ_ERR_SHAPE, "%s: negative shape [%lld, %lld]", fn, (long long)rows, (long long)cols);
@@ -68,12 +69,36 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
     if (!empty && !x) return fail(BSQ_ERR_NULL, "%s: x is NULL", fn);
     if ((direction & BSQ_ROW) && !empty && (!row_codes || !row_scales)) return fail(BSQ_ERR_NULL, "%s: rowwise outputs are NULL", fn);
     if ((direction & BSQ_COL) && !empty && (!col_codes || !col_scales)) return fail(BSQ_ERR_NULL, "%s: columnwise outputs are NULL", fn);
-    if (!empty && !workspace) return fail(BSQ_ERR_NULL, "%s: workspace is NULL", fn);
+    if (need_ws && !empty && !workspace) return fail(BSQ_ERR_NULL, "%s: workspace is NULL", fn);
     if (misaligned(x) || misaligned(row_codes) || misaligned(col_codes) || misaligned(rht_signs) || misaligned(workspace))
         return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return BSQ_OK;
+}
+
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int rounding, uint64_t sr_seed,
+                   uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
+                   uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out, void* workspace,
+                   void* hip_stream) {
+    static const char* fn = "nvfp4_quantize";
+    if (const int st = nvfp4_quantize_check(fn, x, rows, cols, direction, rounding, rht_signs, row_codes, row_scales,
+                                            col_codes, col_scales, amax_out, s_enc_out, true, workspace))
+        return st;
     return launched(bsq::launch_nvfp4_quantize(x, rows, cols, direction, rounding, sr_seed, sr_stream, rht_signs,
                                                row_codes, row_scales, col_codes, col_scales, amax_out, s_enc_out,
                                                static_cast<float*>(workspace), hip_stream), fn);
+}
+
+int nvfp4_quantize_noalloc(const void* x, int64_t rows, int64_t cols, int direction, int rounding, uint64_t sr_seed,
+                           uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
+                           uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out,
+                           void* hip_stream) {
+    static const char* fn = "nvfp4_quantize_noalloc";
+    if (const int st = nvfp4_quantize_check(fn, x, rows, cols, direction, rounding, rht_signs, row_codes, row_scales,
+                                            col_codes, col_scales, amax_out, s_enc_out, false, nullptr))
+        return st;
+    return launched(bsq::launch_nvfp4_quantize_noalloc(x, rows, cols, direction, rounding, sr_seed, sr_stream,
+                                                       rht_signs, row_codes, row_scales, col_codes, col_scales,
+                                                       amax_out, s_enc_out, hip_stream), fn);
 }
 
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows, int64_t cols,

@@ -12,6 +12,10 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
                           uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
                           uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, float* workspace,
                           void* hip_stream);
+int launch_nvfp4_quantize_noalloc(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
+                                  uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
+                                  uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc,
+                                  void* hip_stream);
 int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, uint8_t* row_codes,
                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, void* hip_stream);
 int launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows,

@@ -20,6 +20,7 @@
 // call to the next: the workspace needs no initial contents, each call writes every slot it
 // reads before reading it, and a replayed graph or a failed launch leaves nothing that a later
 // call could read.
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -962,6 +963,48 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
                          parts, nparts, amax, s_enc, seed, stream};
     if (direction == 2) return rht ? launch_encode_tiles<2, true>(a, sr, s) : launch_encode_tiles<2, false>(a, sr, s);
     return rht ? launch_encode_tiles<3, true>(a, sr, s) : launch_encode_tiles<3, false>(a, sr, s);
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+//
+// nvfp4_quantize_noalloc keeps the amax pass's partial maxima in this file-scope device array
+// instead of a caller workspace: one copy per GPU, BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES, held
+// until the process ends.  Host code never passes the array's name to a kernel (on the host
+// it is a stand-in, not a device address): the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept in scratch_addr.  No initial
+// contents are needed (each call stores every slot it reads), so nothing is cleared; calls
+// that overlap on one GPU share the array and race.
+static __device__ __align__(256) float scratch[2 * AMAX_PARTS];
+
+constexpr int SCRATCH_DEVICES = 64;
+
+// Device address of this device's `scratch` (looked up on the first call on the device).
+static int scratch_addr(float** out) {
+    static std::mutex mu;
+    static float* addr[SCRATCH_DEVICES] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= SCRATCH_DEVICES) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        addr[dev] = static_cast<float*>(p);
+    }
+    *out = addr[dev];
+    return 0;
+}
+
+int launch_nvfp4_quantize_noalloc(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
+                                  uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
+                                  uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc,
+                                  void* hip_stream) {
+    float* parts = nullptr;
+    if (const int e = scratch_addr(&parts)) return e;
+    return launch_nvfp4_quantize(x, R, C, direction, rounding, seed, stream, signs, row_codes, row_scales, col_codes,
+                                 col_scales, amax, s_enc, parts, hip_stream);
 }
 
 int launch_nvfp4_quantize_rowscaled(const void* x, int64_t R, int64_t C, int rounding, uint64_t seed,

@@ -140,6 +140,25 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
                    void* hip_stream);
 
 /*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize without the workspace argument, for callers that
+ * cannot allocate device memory or pass scratch: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, numerics, outputs and errors are those
+ * of nvfp4_quantize; the partial maxima go to a fixed device array inside the library instead
+ * (BSQ_NVFP4_QUANTIZE_WORKSPACE_BYTES per GPU, set aside when the library is loaded and held
+ * until the process ends; its device address is looked up on the first call on each GPU).
+ * The array's size does not depend on the tensor, so every size nvfp4_quantize accepts is
+ * accepted.  Every call on a GPU shares that GPU's array: calls that may run at the same time
+ * on one GPU (on different streams, or from threads that do not order their calls) race and
+ * give unspecified results.  The array needs no initial contents (each call writes every
+ * slot it reads), so nothing carries over from one call to the next.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ */
+int nvfp4_quantize_noalloc(const void* x, int64_t rows, int64_t cols, int direction, int rounding,
+                           uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
+                           uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                           uint8_t* col_scales, float* amax_out, float* s_enc_out, void* hip_stream);
+
+/*
  * nvfp4_quantize_rowscaled -- rowwise NVFP4 quantization with one outer fp32 scale per
  * row instead of one per tensor.
  *
