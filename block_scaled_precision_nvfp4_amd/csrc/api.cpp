@@ -48,7 +48,7 @@ int launched(int hip_code, const char* what) {
 
 extern "C" {
 
-int bsq_version(void) { return 100; }
+int bsq_version(void) { return 200; }
 
 const char* bsq_last_error(void) { return g_last_error.c_str(); }
 

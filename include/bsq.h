@@ -361,7 +361,7 @@ int nvfp4_linear_backward(const void* dy, const void* w, const void* saved, int6
  * by the library; valid until the thread's next call. */
 const char* bsq_last_error(void);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 200 (nvfp4_quantize takes a caller workspace). */
 int bsq_version(void);
 
 #ifdef __cplusplus

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for f in ["nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize",
               "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "blockscaled_grouped_gemm",
               "nvfp4_linear_workspace_bytes", "nvfp4_linear_saved_bytes", "nvfp4_linear_forward",
-              "nvfp4_linear_backward", "bsq_last_error", "bsq_version"]:
+              "nvfp4_linear_backward", "bsq_last_error", "bsq_version", "nvfp4_quantize_noalloc"]:
         assert f in names
 
 
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version(L):
-    assert L.bsq_version() == 100
+    assert L.bsq_version() == 200
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails before any HIP call
