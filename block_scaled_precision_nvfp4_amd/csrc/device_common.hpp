@@ -118,31 +118,24 @@ __device__ __forceinline__ uint32_t e2m1_pack2_rne(uint32_t w, float a, float b)
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
 }
 
-// Stochastic rounding onto the E2M1 grid: lo = largest grid value <= |v| (|v| < 6),
-// p = (|v| - lo) / (hi - lo) exactly (the spacing is a power of two), round up iff
-// (u >> 8) * 2^-24 < p.  |v| >= 6 saturates.  For |v| >= 1 the grid point below is |v| with
-// its binary32 mantissa truncated to one bit (code 2 + 2e + m for exponent e, mantissa bit
-// m) and the spacing is 2^(e-1); below 1 the grid is {0, 0.5} with spacing 0.5.
+// Stochastic rounding onto the E2M1 grid: with lo the grid value at or below |v| and p =
+// (|v| - lo) / spacing (exact), round up iff (u >> 8) * 2^-24 < p; |v| >= 6 saturates.
+// Branch-free integer form of that comparison:
+//   |v| in [1, 6): p = (low 22 mantissa bits) / 2^22 and lo's code is 2 + 2e + (mantissa
+//     bit 22) = (|v| bits >> 22) - 252; (u >> 8) < 4 * low22 <=> u < low22 << 10, and
+//     (v bits << 10) is low22 << 10 (sign, exponent and bit 22 shifted out);
+//   |v| in [0.5, 1): grid {0.5, 1}, p = (23 mantissa bits) / 2^23, up iff u < (v bits << 9);
+//     the code below is 1, which max((|v| bits >> 22) - 252, 1) also gives;
+//   |v| < 0.5: grid {0, 0.5}, p = 2|v|, up iff (u >> 8) * 2^-25 < |v| (both sides exact);
+//   codes above 7 (|v| >= 6) are clamped to 7.  The sign bit is copied (-0 gives code 0x8).
 __device__ __forceinline__ uint32_t e2m1_encode_sr(float v, uint32_t u) {
-    const float a = __builtin_fabsf(v);
-    const uint32_t s = (__float_as_uint(v) >> 28) & 8u;
-    if (a >= 6.0f) return 7u | s;
-    uint32_t lo;
-    float lov, inv;
-    if (a >= 1.0f) {
-        const uint32_t bits = __float_as_uint(a);
-        const uint32_t e = (bits >> 23) - 127u;              // 0, 1 or 2
-        lo = 2u + 2u * e + ((bits >> 22) & 1u);
-        lov = __uint_as_float(bits & 0xFFC00000u);
-        inv = __uint_as_float((128u - e) << 23);             // 2^(1 - e)
-    } else {
-        lo = a >= 0.5f ? 1u : 0u;
-        lov = lo ? 0.5f : 0.0f;
-        inv = 2.0f;
-    }
-    const float p = (a - lov) * inv;
-    const float r = (float)(u >> 8) * 0x1p-24f;
-    return (lo + (uint32_t)(r < p)) | s;
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t ab = b & 0x7FFFFFFFu;
+    const uint32_t thr = b << (ab >= 0x3F800000u ? 10 : 9);
+    const int lo = max((int)(ab >> 22) - 252, 1);
+    const uint32_t big = min((uint32_t)lo + (u < thr ? 1u : 0u), 7u);
+    const uint32_t small = (float)(u >> 8) * 0x1p-25f < __uint_as_float(ab) ? 1u : 0u;
+    return (ab < 0x3F000000u ? small : big) | ((b >> 28) & 8u);
 }
 
 // ---------------------------------------------------------------- Philox4x32-10
@@ -180,12 +173,15 @@ __device__ __forceinline__ uint32_t word_of(const u32x4& w, int i) {
 }
 
 // ---------------------------------------------------------------- Hadamard
-// In-place y = v diag(d) H16 / 4 on 16 registers: sign flip, butterfly strides 1, 2, 4,
-// 8 with (a, b) -> (a + b, a - b), then the exact scaling by 1/4.  d is a bitmask:
-// bit i set means d_i = -1.
-__device__ __forceinline__ void rht16(float v[16], uint32_t negmask) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = ((negmask >> i) & 1u) ? -v[i] : v[i];
+// y = v diag(d) H16 / 4 per 16-block: sign flip, butterfly strides 1, 2, 4, 8 with (a, b) ->
+// (a + b, a - b), then the exact scaling by 1/4.  d is a bitmask: bit i set means d_i = -1.
+// The quantize kernels flip the signs on the packed bf16 words before unpacking and fold the
+// 1/4 into the encode multiplier, so they call the butterfly alone (rht16_core /
+// rht16_pair_core); every butterfly output is a multiple of 2^-133 (a sum of bf16 values,
+// rounded to fp32), which makes its quarter exact.
+
+// The butterfly on 16 registers (no sign, no scaling).
+__device__ __forceinline__ void rht16_core(float v[16]) {
 #pragma unroll
     for (int h = 1; h < 16; h *= 2) {
 #pragma unroll
@@ -198,18 +194,20 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t negmask) {
             }
         }
     }
+}
+
+__device__ __forceinline__ void rht16(float v[16], uint32_t negmask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = ((negmask >> i) & 1u) ? -v[i] : v[i];
+    rht16_core(v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
 }
 
-// Half of a 16-point transform held by a lane pair: this lane holds elements
-// 8*upper .. 8*upper+7 of the block and its partner (lane ^ 1) the other half.
-// Strides 1, 2, 4 are local; stride 8 pairs element j of the lower half with
-// element j of the upper half.
-__device__ __forceinline__ void rht16_pair(float v[8], uint32_t negmask, bool upper) {
-    const int off = upper ? 8 : 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ((negmask >> (i + off)) & 1u) ? -v[i] : v[i];
+// The butterfly of a 16-block held by a lane pair: this lane holds elements 8*upper ..
+// 8*upper+7 and its partner (lane ^ 1) the other half.  Strides 1, 2, 4 are local; stride 8
+// pairs element j of the lower half with element j of the upper half.
+__device__ __forceinline__ void rht16_pair_core(float v[8], bool upper) {
 #pragma unroll
     for (int h = 1; h < 8; h *= 2) {
 #pragma unroll
@@ -228,8 +226,35 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t negmask, bool up
         // lower lane: a + b with a = own; upper lane: a - b with a = partner's
         v[j] = upper ? (other - v[j]) : (v[j] + other);
     }
+}
+
+__device__ __forceinline__ void rht16_pair(float v[8], uint32_t negmask, bool upper) {
+    const int off = upper ? 8 : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ((negmask >> (i + off)) & 1u) ? -v[i] : v[i];
+    rht16_pair_core(v, upper);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] *= 0.25f;
+}
+
+// XOR masks that flip the signs of a lane's packed bf16 words (two values per word) for the
+// transform along a row: word w of the lane's 8 values holds block elements 8*upper + 2w and
+// 8*upper + 2w + 1.
+__device__ __forceinline__ uint32_t row_sign_word(uint32_t negmask, bool upper, int w) {
+    const uint32_t n = negmask >> ((upper ? 8 : 0) + 2 * w);
+    return ((n & 1u) << 15) | ((n & 2u) << 30);
+}
+
+// Block-scale code of a block with largest magnitude bmax under tensor scale S: the E4M3 code
+// of (bmax * S) / 6, the quotient formed with two fused multiply-adds from RN(1/6):
+// q0 = t RN(1/6), q = q0 + (t - 6 q0) RN(1/6).  For every binary32 t in [0, 2688 (1 + 2^-21)]
+// (t never exceeds 2688 (1 + 2^-23)) q equals the correctly rounded t / 6 except where t is
+// below 10^-30, where both encode to code 0 -- checked exhaustively over all 1.16 * 10^9 values.
+__device__ __forceinline__ uint32_t block_scale_code(float bmax, float S) {
+    const float t = bmax * S;
+    const float r6 = 0x1.555556p-3f;
+    const float q0 = t * r6;
+    return e4m3_encode_nonneg(__builtin_fmaf(__builtin_fmaf(-q0, 6.0f, t), r6, q0));
 }
 
 // NVFP4 per-tensor scale from the amax: 2688 / A, A = 0 -> 1, overflow -> FLT_MAX.

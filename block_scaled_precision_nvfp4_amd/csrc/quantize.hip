@@ -56,11 +56,30 @@ __device__ __forceinline__ TileCoord tile_coord() { return tile_coord_at(blockId
 // (C % 8 == 0, so a chunk is either entirely inside or entirely outside).
 // The sub-tile lives in registers as q[row][word], word w holding columns 2w and 2w+1;
 // every loop that indexes it is fully unrolled so that all indices are constants.
+// The loads go through a buffer resource over the tile's rows that exist (rows past R read
+// as zero through its range check, a column chunk past C through an offset beyond it), so a
+// row costs one 32-bit offset add instead of 64-bit address arithmetic and a branch; tensors
+// whose 256-row tile spans 2^31 bytes or more (C >= 2^22) take 64-bit addresses instead.
 typedef uint32_t SubTile[16][4];
 
 __device__ __forceinline__ void load_subtile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                              const TileCoord& t, SubTile q) {
     const bool colok = t.c0 < C;
+    if (C < ((int64_t)1 << 22)) {   // uniform
+        const int64_t row0 = t.r0 - 16 * t.rb;   // the tile's first row
+        const int64_t rows = (R - row0) < TILE_R ? (R - row0) : TILE_R;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + row0 * C), (short)0, (int)(rows * C * 2), 0x00020000);
+        const uint32_t stride = (uint32_t)C * 2u;
+        const uint32_t off0 = colok ? (uint32_t)(16 * t.rb) * stride + (uint32_t)t.c0 * 2u : 0x80000000u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            // aux 2: non-temporal (the data is read once)
+            const u32v4 v = __builtin_bit_cast(u32v4, __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + j * stride, 0, 2));
+            q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int64_t r = t.r0 + j;
@@ -68,6 +87,13 @@ __device__ __forceinline__ void load_subtile(const uint16_t* __restrict__ x, int
         if (colok && r < R) v = load16_stream(x + r * C + t.c0);
         q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
     }
+}
+
+// Sign flips of the 16-point transform applied to the packed sub-tile.  Columnwise blocks run
+// down the sub-tile's 16 rows, so row j takes sign d_j in both halves of each word; rowwise
+// blocks run along a lane pair's 16 columns, so word w takes the signs of its two columns.
+__device__ __forceinline__ uint32_t col_sign_word(uint32_t negmask, int j) {
+    return ((negmask >> j) & 1u) ? 0x80008000u : 0u;
 }
 
 // Row j of the sub-tile as 8 floats.
@@ -189,25 +215,32 @@ __device__ __forceinline__ void publish_scales(float2 am, float* amax_out, float
 
 // Amax of the transformed values per direction (DIRS: bit 0 rowwise, bit 1 columnwise; with
 // RHT each direction takes the amax of its own transformed values), over 256 x 128 tiles: a
-// grid of at most AMAX_PARTS workgroups, workgroup w taking tiles w, w + grid, ...
+// grid of at most AMAX_PARTS workgroups, workgroup w taking tiles w, w + grid, ...  The
+// butterfly's outputs h are four times the transform's values, exactly, so the maxima of |h|
+// are taken and quartered once at the end.
 template <int DIRS>
 __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t* __restrict__ x, int64_t R,
                                                                   int64_t C, const int8_t* __restrict__ signs,
                                                                   float* __restrict__ parts) {
     const int64_t ntc = (C + TILE_C - 1) / TILE_C, nt = ntc * ((R + TILE_R - 1) / TILE_R);
     const uint32_t neg = sign_mask16(signs);
+    const bool upper = (threadIdx.x & 1) != 0;   // the lane's half of its rowwise blocks (cc & 1)
     float mrow = 0.0f, mcol = 0.0f;
     for (int64_t tix = blockIdx.x; tix < nt; tix += gridDim.x) {
         const TileCoord t = tile_coord_at(tix / ntc, tix % ntc);
         SubTile q;
         load_subtile(x, R, C, t, q);
         if (DIRS & 1) {
-            const bool upper = (t.cc & 1) != 0;
             static_for<0, 16>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 float v[8];
-                row_of(q, j, v);
-                rht16_pair(v, neg, upper);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t word = q[j][w] ^ row_sign_word(neg, upper, w);
+                    v[2 * w] = bf16_lo(word);
+                    v[2 * w + 1] = bf16_hi(word);
+                }
+                rht16_pair_core(v, upper);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) mrow = __builtin_fmaxf(mrow, __builtin_fabsf(v[k]));
             });
@@ -216,14 +249,18 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t
             static_for<0, 8>([&](auto k_c) {
                 constexpr int k = decltype(k_c)::value;
                 float v[16];
-                col_of(q, k, v);
-                rht16(v, neg);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t word = q[j][k >> 1] ^ col_sign_word(neg, j);
+                    v[j] = (k & 1) ? bf16_hi(word) : bf16_lo(word);
+                }
+                rht16_core(v);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mcol = __builtin_fmaxf(mcol, __builtin_fabsf(v[j]));
             });
         }
     }
-    store_parts<NTHREADS, DIRS>(mrow, mcol, parts);
+    store_parts<NTHREADS, DIRS>(mrow * 0.25f, mcol * 0.25f, parts);
 }
 
 // ------------------------------------------------------------------ NVFP4 encode
@@ -244,19 +281,40 @@ struct NvEncodeArgs {
     uint32_t stream;
 };
 
-// Encode one 16-block's worth of values held by this thread (n = 8 or 16 values) with the
-// block amax already known.  Writes the packed codes (n/2 bytes as n/8 words) into w[].
-// first_index: output-layout index of v[0]; consecutive values are consecutive indices.
-template <int N, bool SR>
-__device__ __forceinline__ uint32_t encode_block(const float* v, float bmax, float S, uint64_t first_index,
-                                                 uint64_t seed, uint32_t stream, uint32_t dir, uint32_t* w) {
-    float tt = bmax * S;
-    tt = tt / 6.0f;
-    const uint32_t sb = e4m3_encode_nonneg(tt);
+// The encode multiplier S / fp32(s_b) of every nonzero scale code s_b (codes 1..126) for tensor
+// scale S, built by the workgroup in LDS (threads [base, base + 128) of it), so that a block
+// reads its multiplier instead of dividing.  The caller synchronises before use.
+__device__ __forceinline__ void build_enc_table(float S, float* tab, int base) {
+    const int c = (int)threadIdx.x - base;
+    if (c >= 0 && c < 128) tab[c] = (c >= 1 && c <= 126) ? S / e4m3_decode_nonneg((uint32_t)c) : 0.0f;
+}
+
+// Encode one 16-block's worth of values held by this thread (N = 8 or 16 values) whose
+// largest magnitude vmax (over the block) is known.  Writes the packed codes (N/2 bytes as
+// N/8 words) into w[] and returns the scale code.  first_index: output-layout index of v[0];
+// consecutive values are consecutive indices.  enc_tab: the workgroup's multiplier table for
+// S, or null (then the multiplier is divided out here).  QUARTER: v holds the butterfly's
+// outputs h, four times the transform's values (exactly); the block is then encoded from
+// h * fl(enc / 4), which equals fl((h / 4) * enc) whenever enc / 4 is exact (one rounding of
+// the same product), and otherwise from (h / 4) * enc.
+template <int N, bool SR, bool QUARTER>
+__device__ __forceinline__ uint32_t encode_block(float* v, float vmax, float S, const float* enc_tab,
+                                                 uint64_t first_index, uint64_t seed, uint32_t stream, uint32_t dir,
+                                                 uint32_t* w) {
+    const uint32_t sb = block_scale_code(QUARTER ? vmax * 0.25f : vmax, S);
 #pragma unroll
     for (int i = 0; i < N / 8; ++i) w[i] = 0u;
     if (sb != 0u) {
-        const float enc = S / e4m3_decode_nonneg(sb);
+        float enc = enc_tab ? enc_tab[sb] : S / e4m3_decode_nonneg(sb);
+        if (QUARTER) {
+            const float e4 = enc * 0.25f;
+            if (e4 * 4.0f == enc) {
+                enc = e4;
+            } else {
+#pragma unroll
+                for (int j = 0; j < N; ++j) v[j] *= 0.25f;
+            }
+        }
         if (SR) {
 #pragma unroll
             for (int g = 0; g < N / 4; ++g) {
@@ -294,6 +352,10 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     const float Srow = nvfp4_tensor_scale(am.x);
     const float Scol = nvfp4_tensor_scale(am.y);
     publish_scales<DIRS>(am, a.amax_out, a.s_enc_out);
+    __shared__ float enc_tab[2][128];
+    if (DIRS & 1) build_enc_table(Srow, enc_tab[0], 0);
+    if (DIRS & 2) build_enc_table(Scol, enc_tab[1], DIRS == 3 ? 128 : 0);
+    __syncthreads();
     const bool colok = t.c0 < C;
 
     if (DIRS & 1) {
@@ -302,15 +364,25 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             constexpr int j = decltype(j_c)::value;
             const int64_t r = t.r0 + j;
             float v[8];
-            row_of(q, j, v);
-            if (RHT) rht16_pair(v, neg, upper);
+            if (RHT) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t word = q[j][w] ^ row_sign_word(neg, upper, w);
+                    v[2 * w] = bf16_lo(word);
+                    v[2 * w + 1] = bf16_hi(word);
+                }
+                rht16_pair_core(v, upper);
+            } else {
+                row_of(q, j, v);
+            }
             float m = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
             m = __builtin_fmaxf(m, __shfl_xor(m, 1));
             uint32_t w;
-            const uint32_t sb = encode_block<8, SR>(v, m, Srow, (uint64_t)r * (uint64_t)C + (uint64_t)t.c0,
-                                                    a.seed, a.stream, 0u, &w);
+            const uint32_t sb = encode_block<8, SR, RHT>(v, m, Srow, enc_tab[0],
+                                                         (uint64_t)r * (uint64_t)C + (uint64_t)t.c0, a.seed, a.stream,
+                                                         0u, &w);
             if (colok && r < R) {
                 *(uint32_t*)(a.row_codes + r * (C / 2) + t.c0 / 2) = w;
                 if (!upper) a.row_scales[r * (C / 16) + t.c0 / 16] = (uint8_t)sb;
@@ -324,18 +396,25 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
         // its own 128-byte row, so the read-back of a column is still one contiguous row)
         __shared__ uint2 lds_codes[TILE_C][TILE_R / 16];
         __shared__ uint8_t lds_sc[TILE_C][TILE_R / 16];
+        if (RHT) {
+            // column blocks run down the rows: flip row j's sign once for both columns of a word
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) q[j][w] ^= col_sign_word(neg, j);
+        }
         static_for<0, 8>([&](auto k_c) {
             constexpr int k = decltype(k_c)::value;
             float v[16];
             col_of(q, k, v);
-            if (RHT) rht16(v, neg);
+            if (RHT) rht16_core(v);
             float m = 0.0f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
             uint32_t w[2];
             const uint64_t c = (uint64_t)(t.c0 + k);
-            const uint32_t sb = encode_block<16, SR>(v, m, Scol, c * (uint64_t)R + (uint64_t)t.r0,
-                                                     a.seed, a.stream, 1u, w);
+            const uint32_t sb = encode_block<16, SR, RHT>(v, m, Scol, enc_tab[1],
+                                                          c * (uint64_t)R + (uint64_t)t.r0, a.seed, a.stream, 1u, w);
             lds_codes[8 * t.cc + k][t.rb ^ t.cc] = make_uint2(w[0], w[1]);
             lds_sc[8 * t.cc + k][t.rb ^ t.cc] = (uint8_t)sb;
         });
@@ -638,7 +717,8 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_linear_kernel(const uint4* _
     store_parts<LIN_THREADS, DIRS>(m, m, parts);
 }
 
-// Row-RHT amax: the 16-point transform of each block, the block held by a lane pair.
+// Row-RHT amax: the 16-point transform of each block, the block held by a lane pair (the
+// maximum of the butterfly's |h|, quartered at the end: exact).
 __global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const uint4* __restrict__ x, int64_t n16,
                                                                           const int8_t* __restrict__ signs,
                                                                           float* __restrict__ parts) {
@@ -646,6 +726,9 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const 
     lin_range(n16, first, stride);
     const uint32_t neg = sign_mask16(signs);
     const bool upper = (threadIdx.x & 1) != 0;
+    uint32_t sw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sw[w] = row_sign_word(neg, upper, w);
     float m = 0.0f;
     for (int64_t base = first; base < n16; base += stride) {
         uint4 q[LIN_UNITS];
@@ -657,13 +740,13 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_rht_row_linear_kernel(const 
 #pragma unroll
         for (int k = 0; k < LIN_UNITS; ++k) {
             float v[8];
-            unpack_bf16x8(q[k], v);
-            rht16_pair(v, neg, upper);
+            unpack_bf16x8(make_uint4(q[k].x ^ sw[0], q[k].y ^ sw[1], q[k].z ^ sw[2], q[k].w ^ sw[3]), v);
+            rht16_pair_core(v, upper);
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
         }
     }
-    store_parts<LIN_THREADS, 1>(m, m, parts);
+    store_parts<LIN_THREADS, 1>(m * 0.25f, 0.0f, parts);
 }
 
 // Rowwise NVFP4 encode: unit u = half u%2 of block u/2.
@@ -681,8 +764,14 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
     const float2 am = parts_max<LIN_THREADS, 1>(parts, nparts);
     const float S = nvfp4_tensor_scale(am.x);
     publish_scales<1>(am, amax_out, s_enc_out);
+    __shared__ float enc_tab[128];
+    build_enc_table(S, enc_tab, 0);
+    __syncthreads();
     const uint32_t neg = RHT ? sign_mask16(signs) : 0u;
     const bool upper = (threadIdx.x & 1) != 0;
+    uint32_t sw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sw[w] = RHT ? row_sign_word(neg, upper, w) : 0u;
     for (int64_t base = first; base < n16; base += stride) {
         uint4 q[LIN_UNITS];
 #pragma unroll
@@ -694,14 +783,18 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
         for (int k = 0; k < LIN_UNITS; ++k) {
             const int64_t u = base + (int64_t)k * LIN_THREADS;
             float v[8];
-            unpack_bf16x8(q[k], v);
-            if (RHT) rht16_pair(v, neg, upper);
+            if (RHT) {
+                unpack_bf16x8(make_uint4(q[k].x ^ sw[0], q[k].y ^ sw[1], q[k].z ^ sw[2], q[k].w ^ sw[3]), v);
+                rht16_pair_core(v, upper);
+            } else {
+                unpack_bf16x8(q[k], v);
+            }
             float m = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
             m = __builtin_fmaxf(m, __shfl_xor(m, 1));
             uint32_t w;
-            const uint32_t sb = encode_block<8, SR>(v, m, S, (uint64_t)u * 8u, seed, stream, 0u, &w);
+            const uint32_t sb = encode_block<8, SR, RHT>(v, m, S, enc_tab, (uint64_t)u * 8u, seed, stream, 0u, &w);
             if (u < n16) {
                 codes[u] = w;
                 if (!upper) scales[u >> 1] = (uint8_t)sb;
@@ -817,7 +910,8 @@ __global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4
                 float bm = values(k, v);
                 bm = __builtin_fmaxf(bm, __shfl_xor(bm, 1));
                 uint32_t w;
-                const uint32_t sb = encode_block<8, SR>(v, bm, S, (uint64_t)(base + u) * 8u, seed, stream, 0u, &w);
+                const uint32_t sb = encode_block<8, SR, false>(v, bm, S, nullptr, (uint64_t)(base + u) * 8u, seed, stream,
+                                                               0u, &w);
                 if (live && u < upr) {
                     codes[base + u] = w;
                     if (!upper) scales[(base + u) >> 1] = (uint8_t)sb;
