@@ -500,11 +500,13 @@ __device__ __forceinline__ void mx_slab_codes(const MxDma& d, uint32_t k, bool l
     else dma_b128(sized(d.o.b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off_r, soff);
 }
 
+// DMA plan of the tile at (m0, n0); its B rows are the first `brows` (GBN, or 128 for the
+// persistent kernel's half tiles) -- the DMAs of B rows past them read nothing and write zeros.
 template <int EPB, int BLK>
-__device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane) {
+__device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t n0, int lane, int64_t brows = GBN) {
     MxDma d;
     const int64_t rb = g.ld / EPB, sb = g.ld / BLK;
-    const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, GBN);
+    const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, brows);
     d.o.a = rsrc_words(g.a_codes + m0 * rb, ra * rb);
     d.o.b = rsrc_words(g.b_codes + n0 * rb, rbn * rb);
     d.o.as = rsrc_words(g.a_scales + m0 * sb, ra * sb);
@@ -849,6 +851,17 @@ __device__ __forceinline__ void nvw_mfma(const NvOpsT<TN>& o, floatx16 (&acc)[4]
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.b[j], o.a[i], acc[i][j], 0, 0, 0);
 }
 
+// The first step of a tile: the accumulators start from zero (no separate clearing, so that a
+// tile's accumulators are not live across the previous tile's epilogue).
+template <int TN>
+__device__ __forceinline__ void nvw_mfma_first(const NvOpsT<TN>& o, floatx16 (&acc)[4][TN]) {
+    const floatx16 z = {};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.b[j], o.a[i], z, 0, 0, 0);
+}
+
 // One step (after its LDS reads, which a scheduling barrier keeps at the top of the step):
 // each MFMA followed by an equal share of the dequantization of the next step, whose words
 // were read a step earlier.
@@ -875,16 +888,17 @@ __device__ __forceinline__ void nvw_interleave() {
 // at the top of an even slice allows DC + DG in flight; the prologue ends with an out-of-range
 // group DMA so that slice 0 fits the rule.  An out-of-range DMA lane still writes (zeros) to
 // LDS: every such DMA here targets a buffer whose contents are no longer, or not yet, needed.
-template <int TN>
+// NW waves share the DMAs of a 256 x 256 tile (NW = 16 / TN: the waves cover it); with NW = 4
+// and TN = 2 the 4 waves cover 256 x 128 (a half tile, brows = 128).
+template <int TN, int NW = 16 / TN>
 __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
-                                              int wm, int wn, int lane, floatx16 (&acc)[4][TN]) {
-    constexpr int NW = 16 / TN;           // waves
+                                              int wm, int wn, int lane, floatx16 (&acc)[4][TN], int64_t brows = GBN) {
     constexpr int PARTS = 16 / NW;        // code DMA parts per slice (4 or 2)
     constexpr int DC = 2 * PARTS;         // code DMAs per lane per slice
     constexpr int DG = NW == 4 ? 2 : 1;   // group DMAs per lane
     constexpr int PSTEP = 8 / PARTS;      // steps between code DMA parts
     if (nk <= 0) return;
-    const MxDma d = make_dma<2, 16>(g, m0, n0, lane);
+    const MxDma d = make_dma<2, 16>(g, m0, n0, lane, brows);
     const int frow = lane & 31, kh = lane >> 5;
     auto buf = [&](int64_t k) { return lds + (int)(k & 3) * NV4_CODES; };
     auto sbuf = [&](int64_t grp) { return lds + 4 * NV4_CODES + (int)(grp & 1) * NV4_SREC; };
@@ -1386,6 +1400,264 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     });
 }
 
+// ---------------------------------------------------------------- persistent NVFP4 kernel
+//
+// Plain NVFP4 launches with per-tensor scales on both operands and K a multiple of 256 (at
+// least 512).  At most one workgroup per CU: workgroup b computes the output tiles b, b + P,
+// b + 2P, ... (P = gridDim.x, a multiple of 8 whenever it is below the tile count, so that all
+// tiles of a workgroup have the XCD phase tile_of assumes).  The LDS ring and the operand
+// pipeline of nvw_main_loop run on from one tile to the next: the next tile's slices 0-2 and
+// its first two scale groups are fetched during the current tile's last three slices, and its
+// first MFMA step is read and dequantized during the current tile's last step.  In between,
+// each lane stores its accumulators straight to C (the ring already holds the next tile, so
+// the epilogue cannot stage through LDS) and the next tile starts at once.  With one tile per
+// workgroup, every workgroup of the chip stores its tile at the same moment and then waits for
+// its successor's first slices: at M = 16384, N = 14336 that launch spends about 9 us per tile
+// outside the K loop (a K sweep), 5.7 us of them on the stores (the same kernel with the
+// stores dropped).
+//
+// Between two tiles the output goes out through the one LDS stage that is free at that point,
+// the stage of the tile's last slice (the next tile's slice 3 lands there only after the DMA
+// issued in its slice 0): each wave stages its 128 x 32 TN block in passes through its own
+// 8 KiB of that stage and stores whole 16-byte chunks of rows, so that a store instruction
+// covers whole 128-byte lines of C (storing 4 accumulators per lane straight from registers
+// touches 32 lines per instruction and measured slower).  The stores are buffer stores through
+// a resource over the tile's rows of C, issued by every lane (a chunk outside C gets an offset
+// past the range and is dropped), so a wave issues exactly nvp_stores<OUT_F32>() of them per
+// tile.  The vector-memory counter retires operations in issue order, and the DMAs that the
+// tops of the next tile's slices 0 and 1 wait for were issued before the stores: those two
+// waits allow the stores and the DMAs issued after them in flight, and the stores drain while
+// the two slices run.  Every other wait is the one of nvw_main_loop.
+template <bool OUT_F32>
+constexpr int nvp_stores() { return OUT_F32 ? 64 : 32; }   // 128 rows x 256 or 512 bytes / (64 x 16)
+
+__device__ __forceinline__ RsrcWords nvp_rsrc(const GemmArgs& g, int64_t m0, int64_t n0) {
+    const int64_t rb = g.ld / 2, sb = g.ld / 16;
+    const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, GBN);
+    return RsrcWords{rsrc_words(g.a_codes + m0 * rb, ra * rb), rsrc_words(g.b_codes + n0 * rb, rbn * rb),
+                     rsrc_words(g.a_scales + m0 * sb, ra * sb), rsrc_words(g.b_scales + n0 * sb, rbn * sb)};
+}
+
+// An accumulator read where it is used.  The "a" constraint keeps the value in its AGPR up to
+// this point; with plain reads the register allocator copies all 256 accumulators of a tile
+// to VGPRs right after their last MFMAs, and the persistent kernel then spills.
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One tile's accumulators (C^T layout, see nvw_mfma) times alpha, to C.  The tile at (m0, n0)
+// is 256 x 64 TN (2 x 2 waves of 128 x 32 TN); `stage` is 32 KiB of LDS no other wave touches
+// until the next barrier.  A pass stages 32 rows (one accumulator row group i) by JS x 32
+// columns of the wave's block in the wave's 8 KiB, row-major with the 16-byte chunk index
+// XORed with the row, then each lane stores CPL chunks.  Every lane takes part in every pass.
+template <bool OUT_F32, int TN>
+__device__ __forceinline__ void nvp_store(const GemmArgs& g, int64_t m0, int64_t n0, int wm, int wn, int wave,
+                                          int lane, float alpha, const floatx16 (&acc)[4][TN], uint8_t* stage) {
+    constexpr int ES = OUT_F32 ? 4 : 2;
+    constexpr int JS = 8 / ES < TN ? 8 / ES : TN;   // 32-column groups per pass (8 KiB / 32 rows / 32 / ES)
+    constexpr int RB = 32 * JS * ES;                // staged bytes per row
+    constexpr int CPR = RB / 16;                    // 16-byte chunks per row (a power of 2)
+    constexpr int CPL = 32 * CPR / 64;              // chunks per lane per pass
+    static_assert(32 * RB <= 8192 && (CPR & (CPR - 1)) == 0 && CPL * 64 == 32 * CPR, "pass shape");
+    uint8_t* reg = stage + wave * 8192;
+    const int frow = lane & 31, kh = lane >> 5;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc((const uint8_t*)g.c + m0 * g.N * ES, tile_rows(g.M - m0, GBM) * g.N * ES);
+    const uint32_t pitch = (uint32_t)(g.N * ES);
+    const int64_t cleft = g.N - n0 - wn;   // columns of C from the block's first one on
+    const uint32_t cbase = (uint32_t)(n0 + wn) * ES;
+    static_for<0, 4 * (TN / JS)>([&](auto p_c) {
+        constexpr int I = decltype(p_c)::value / (TN / JS), J0 = (decltype(p_c)::value % (TN / JS)) * JS;
+#pragma unroll
+        for (int jj = 0; jj < JS; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = J0 + jj;
+                const float x = acc_read(acc[I][j][4 * q]) * alpha, y = acc_read(acc[I][j][4 * q + 1]) * alpha;
+                const float z = acc_read(acc[I][j][4 * q + 2]) * alpha, w = acc_read(acc[I][j][4 * q + 3]) * alpha;
+                const int col = 32 * jj + 8 * q + 4 * kh;   // first of the 4 columns, within the pass
+                uint8_t* dst = reg + frow * RB + (((col * ES / 16) ^ (frow & (CPR - 1))) << 4) + (col * ES) % 16;
+                if constexpr (OUT_F32) *(float4*)dst = make_float4(x, y, z, w);
+                else *(uint2*)dst = make_uint2(bf16x2_rne(x, y), bf16x2_rne(z, w));
+            }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const int t = 64 * k + lane, r = t / CPR, c = t % CPR;
+            const uint4 v = *(const uint4*)(reg + r * RB + ((c ^ (r & (CPR - 1))) << 4));
+            const int col = 32 * J0 + c * (16 / ES);   // first column of the chunk in the block
+            const uint32_t off = col < cleft ? (uint32_t)(wm + 32 * I + r) * pitch + cbase + (uint32_t)(col * ES) : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4s{v.x, v.y, v.z, v.w}, rs, (int)off, 0, 0);
+        }
+    });
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_full, int64_t halves) {
+    constexpr int TN = 4, NW = 4, DC = 8, DG = 2, PSTEP = 2;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[Fmt<2>::LDS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int frow = lane & 31, kh = lane >> 5;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+    const int64_t nbm = (g.M + GBM - 1) / GBM, nbn = (g.N + GBN - 1) / GBN;
+    const int64_t P = gridDim.x;
+    const int items = (int)((t_full - 1 - (int64_t)blockIdx.x) / P) + 1;   // t_full >= P
+    const int nk = (int)(g.K / 128);   // even, >= 4
+    // alpha = fp32(1 / (S_a S_b)), product and quotient in binary64 (as in tile_factors)
+    float alpha = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
+#if __HIP_DEVICE_COMPILE__
+    asm volatile("" : "+v"(alpha));
+#endif
+    auto origin = [&](int it, int64_t& m0, int64_t& n0) {
+        int64_t tm, tn;
+        tile_of(nbm, nbn, (int64_t)blockIdx.x + (int64_t)it * P, tm, tn);
+        m0 = tm * GBM;
+        n0 = tn * GBN;
+    };
+    int64_t m0, n0, m1 = 0, n1 = 0;
+    origin(0, m0, n0);
+    MxDma d = make_dma<2, 16>(g, m0, n0, lane);
+    RsrcWords rc = d.o, rn = d.o;   // resources of the current and of the next tile
+    bool has_next = items > 1;
+    if (has_next) {
+        origin(1, m1, n1);
+        rn = nvp_rsrc(g, m1, n1);
+    }
+    // ring positions by global slice / scale-group index (a tile's slice 0 is slice it * nk)
+    auto buf = [&](int k) { return lds + (k & 3) * NV4_CODES; };
+    auto sbuf = [&](int grp) { return lds + 4 * NV4_CODES + (grp & 1) * NV4_SREC; };
+
+    floatx16 acc[4][TN];   // each tile's first step writes them (nvw_mfma_first)
+
+    // prologue of the first tile, as in nvw_main_loop (nk >= 4: groups 0 and 1 both exist)
+    nv4_dma_group<NW>(d, 0, true, sbuf(0));
+    nv4_dma_group<NW>(d, 1, true, sbuf(1));
+    static_for<0, 3>([&](auto k_c) {
+        constexpr int K0 = decltype(k_c)::value;
+        static_for<0, 4>([&](auto p_c) { nv4_dma_codes<decltype(p_c)::value, NW>(d, 64u * K0, true, buf(K0)); });
+    });
+    nv4_dma_group<NW>(d, 0, false, buf(3));   // no traffic; keeps the wait counts uniform
+    wait_vm_barrier<2 * DC + DG>();
+
+    NvQuadT<TN> q0, q1;
+    NvWordsT<TN> w;
+    NvOpsT<TN> cur, nxt;
+    uint32_t sa[4], sb[TN], san[4], sbn[TN];
+    nvw_read_scales<TN>(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
+    nvw_read_quad<0, TN>(buf(0), wm, wn, frow, kh, q0);
+    nvw_words_of<0, TN>(q0, w);
+    nvw_ops<0, TN>(w, sa, sb, cur);
+
+    for (int it = 0; it < items; ++it) {
+        const int gs0 = it * nk;
+        // slice kt of this tile; in the tile's last slice (LAST) the last step neither reads nor
+        // dequantizes the next tile's first step: that happens after the stores, so that those
+        // operands are not live across the epilogue
+        auto slice = [&](int kt, auto odd_c, auto last_c, auto first_c) {
+            constexpr bool ODD = decltype(odd_c)::value, LAST = decltype(last_c)::value;
+            constexpr bool FIRST = decltype(first_c)::value;
+            // the previous tile's stores may be in flight at the tops of slices 0 and 1
+            constexpr int NST = nvp_stores<OUT_F32>();
+            constexpr int W0 = DC + DG + NST < 63 ? DC + DG + NST : 63, W1 = DC + NST < 63 ? DC + NST : 63;
+            if (kt < 2 && it > 0) {
+                if constexpr (ODD) wait_vm_barrier<W1>();
+                else wait_vm_barrier<W0>();
+            } else if constexpr (ODD) wait_vm_barrier<DC>();
+            else wait_vm_barrier<DC + DG>();
+            const int kd = kt + 3;
+            const bool nx = kd >= nk;              // the slice fetched now belongs to the next tile
+            const bool live = !nx || has_next;
+            MxDma dd = d;
+            dd.o = nx ? rn : rc;
+            const uint32_t kloc = (uint32_t)(nx ? kd - nk : kd);
+            uint8_t* db = buf(gs0 + kd);
+            const uint8_t* cb = buf(gs0 + kt);
+            const uint8_t* nb = buf(gs0 + kt + 1);
+            static_for<0, 8>([&](auto s_c) {
+                constexpr int S = decltype(s_c)::value;
+                if constexpr (S % PSTEP == 0) nv4_dma_codes<S / PSTEP, NW>(dd, 64u * kloc, live, db);
+                if constexpr (ODD && S == 1) nv4_dma_group<NW>(dd, kloc / 2, live, sbuf((gs0 + kd) / 2));
+                if constexpr (S == 2) nvw_read_quad<1, TN>(cb, wm, wn, frow, kh, q1);
+                if constexpr (S == 6 && !LAST) nvw_read_quad<0, TN>(nb, wm, wn, frow, kh, q0);
+                if constexpr (S == 5)
+                    nvw_read_scales<TN>(sbuf((gs0 + kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (S + 1 < 8) {
+                    if constexpr (S + 1 < 4) nvw_words_of<S + 1, TN>(q0, w);
+                    else nvw_words_of<S + 1, TN>(q1, w);
+                    nvw_ops<S + 1, TN>(w, sa, sb, nxt);
+                } else if constexpr (!LAST) {
+                    nvw_words_of<0, TN>(q0, w);
+                    nvw_ops<0, TN>(w, san, sbn, nxt);
+                }
+                if constexpr (FIRST && S == 0) nvw_mfma_first<TN>(cur, acc);
+                else nvw_mfma<TN>(cur, acc);
+                if constexpr (S + 1 < 8 || !LAST) nvw_interleave<TN>();
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (S + 1 < 8 || !LAST) cur = nxt;
+            });
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[i] = san[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) sb[j] = sbn[j];
+        };
+        using F_ = std::false_type;
+        using T_ = std::true_type;
+        slice(0, F_{}, F_{}, T_{});
+        slice(1, T_{}, F_{}, F_{});
+        for (int kt = 2; kt < nk - 2; kt += 2) {
+            slice(kt, F_{}, F_{}, F_{});
+            slice(kt + 1, T_{}, F_{}, F_{});
+        }
+        slice(nk - 2, F_{}, F_{}, F_{});
+        slice(nk - 1, T_{}, T_{}, F_{});
+        lds_barrier();   // every wave is done with the stage of the last slice
+        nvp_store<OUT_F32, TN>(g, m0, n0, wm, wn, wave, lane, alpha, acc, buf(gs0 + nk - 1));
+        // the next tile's first step (its slice 0 landed before the top of this tile's last
+        // slice; sa / sb now hold its scales)
+        nvw_read_quad<0, TN>(buf(gs0 + nk), wm, wn, frow, kh, q0);
+        nvw_words_of<0, TN>(q0, w);
+        nvw_ops<0, TN>(w, sa, sb, cur);
+        m0 = m1;
+        n0 = n1;
+        rc = rn;
+        has_next = it + 2 < items;
+        if (has_next) {
+            origin(it + 2, m1, n1);
+            rn = nvp_rsrc(g, m1, n1);
+        }
+    }
+    wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
+
+    // The last, partial round of tiles (t_full .. t_full + halves / 2), each split into two
+    // 256 x 128 halves, one per workgroup: 4 waves of 128 x 64 (TN = 2) with the full tile's
+    // DMA plan (the B rows past 128 read nothing).  A half costs a little more than half a tile
+    // (6 dequantization VALU per MFMA against 4.4), against a whole tile for the workgroups of
+    // a partial round that is left whole.
+    if ((int64_t)blockIdx.x < halves) {
+        __syncthreads();   // every wave is done with the ring
+        int64_t tm, tn;
+        tile_of(nbm, nbn, t_full + (int64_t)blockIdx.x / 2, tm, tn);
+        const int64_t hm0 = tm * GBM, hn0 = tn * GBN + 128 * (blockIdx.x & 1);
+        if (hn0 < g.N) {   // uniform
+            const int hwm = (wave >> 1) * 128, hwn = (wave & 1) * 64;
+            floatx16 hacc[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) hacc[i][j][r] = 0.0f;
+            nvw_main_loop<2, 4>(g, hm0, hn0, nk, lds, hwm, hwn, lane, hacc, 128);
+            lds_barrier();   // every wave is done with the ring
+            nvp_store<OUT_F32, 2>(g, hm0, hn0, hwm, hwn, wave, lane, alpha, hacc, lds);
+        }
+    }
+}
+
 template <int FMT, int OUT, int GM>
 static int launch_one(const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipStream_t s) {
     if (tiles <= 0) return 0;
@@ -1405,8 +1677,43 @@ static bool slab_ok(const GemmArgs& g, int fmt, int mode) {
     return true;
 }
 
+// Workgroups of a persistent NVFP4 launch over `tiles` output tiles, or 0 where that kernel does
+// not apply: per-tensor scales on both operands, K a multiple of 256 and at least 512, N a
+// multiple of 8 (every 16-byte chunk of a row of C lies inside C or outside it), C 16-byte aligned, a
+// tile's rows of C within a 2^31-byte resource, and the global slice count of a workgroup
+// within int range.
+static int64_t persistent_workgroups(const GemmArgs& g, int c_dtype, int64_t tiles) {
+    if (tiles >= ((int64_t)1 << 31)) return 0;
+    const int64_t es = c_dtype == 1 ? 4 : 2;
+    if (g.a_rows || g.b_rows || g.K % 256 != 0 || g.K < 512 || g.N % 8 != 0) return 0;
+    if ((uintptr_t)g.c % 16 != 0 || (int64_t)GBM * g.N * es > 0x7FFFFFFF) return 0;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+        return 0;
+    const int64_t p = tiles <= cus ? tiles : (int64_t)(cus / 8) * 8;
+    if (((tiles + p - 1) / p) * (g.K / 128) >= ((int64_t)1 << 30)) return 0;
+    return p;
+}
+
 template <int GM>
 static int launch_fmt(int fmt, int c_dtype, const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipStream_t s) {
+    if constexpr (GM == 0) {
+        if (fmt == 0) {
+            const int64_t p = persistent_workgroups(g, c_dtype, tiles);
+            if (p > 0) {
+                // a last round that would leave at least half the workgroups idle is split into
+                // half tiles, one per workgroup
+                const int64_t r = tiles % p;
+                const int64_t t_full = (r != 0 && 2 * r <= p) ? tiles - r : tiles;
+                const int64_t halves = t_full < tiles ? 2 * r : 0;
+                if (c_dtype == 1)
+                    hipLaunchKernelGGL(gemm_nvp_kernel<true>, dim3((unsigned)p), dim3(256), 0, s, g, t_full, halves);
+                else hipLaunchKernelGGL(gemm_nvp_kernel<false>, dim3((unsigned)p), dim3(256), 0, s, g, t_full, halves);
+                return (int)hipGetLastError();
+            }
+        }
+    }
     // NVFP4: the LDS DMA kernel when every K handled is a multiple of 256 (known on the host
     // unless K varies per group), the register-staged kernel otherwise
     if constexpr (GM != 2) {

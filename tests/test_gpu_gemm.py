@@ -290,10 +290,28 @@ def test_fwd_llama3_8b_sampled():
 
 def test_wgrad_llama3_8b_sampled():
     """dW[14336, 4096] = dY^T X with RHT + SR columnwise operands (K = 16384 tokens), fp32;
-    every output tile sampled."""
+    every output tile sampled, and both 128-column halves of each (on a 256-CU device the 896
+    tiles leave a last round of 128, which the persistent kernel splits into halves)."""
     nv_gemm_check(gaussian_bf16((16384, 14336), STD_DY, SEED_DY), gaussian_bf16((16384, 4096), 1.0, SEED_X),
-                  out_dtype=torch.float32, rows=stratified(14336, 3), cols=stratified(4096, 4),
+                  out_dtype=torch.float32, rows=stratified(14336, 3), cols=stratified(4096, 4, band=128),
                   a_dir=2, b_dir=2, rounding=1, signs=rht_signs(SEED_SIGNS), label="wgrad")
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [
+    (4352, 4096, 768, torch.bfloat16),    # 272 tiles: last round split into halves; K / 128 = 6 slices
+    (4352, 4160, 512, torch.float32),     # 289 tiles, the last column band 64 wide
+    (6144, 4864, 1024, torch.bfloat16),   # 456 tiles: a last round too large to split
+    (8192, 8192, 512, torch.float32),     # 1024 tiles: 4 whole tiles per workgroup
+])
+def test_persistent_tiles(M, N, K, out_dtype):
+    """Launches that take the persistent NVFP4 kernel (per-tensor scales, K a multiple of 256,
+    more tiles than a 256-CU device has CUs): several tiles per workgroup with the LDS ring and
+    the operand pipeline carried from tile to tile (also when a tile's slice count is not a
+    multiple of the ring's 4 stages), and a last round either whole or split into 256 x 128
+    halves.  Every 256-row band and every 128-column band is sampled."""
+    nv_gemm_check(gaussian_bf16((M, K), 1.0, SEED_X + 10), gaussian_bf16((N, K), STD_W, SEED_W + 10),
+                  out_dtype=out_dtype, rows=stratified(M, 5), cols=stratified(N, 6, band=128),
+                  label="persistent %dx%dx%d" % (M, N, K))
 
 
 def test_hybrid_qwen3_8b_sampled():
