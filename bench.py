@@ -565,11 +565,11 @@ def main():
             "dgrad": (M_TOK + K_IN) * N_OUT * 1.03125 + 2.0 * M_TOK * K_IN}
     gemms = {
         "fwd_nvfp4": roofline_entry("mfma", tflops(g_fwd), F16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-                                    "gemm_kernel<2,0,0>: NVFP4 fwd Y = X W^T, f16 MFMA with in-register dequant",
+                                    "gemm_nvp_kernel<false>: NVFP4 fwd Y = X W^T, persistent, f16 MFMA with in-register dequant",
                                     algo["fwd"], "gemm_fwd_nvfp4", ms=round(g_fwd, 4),
                                     frac_of_measured=round(tflops(g_fwd) / peaks["mfma_f16_32x32x16_TFLOPs"], 4)),
         "wgrad_nvfp4": roofline_entry("mfma", tflops(g_wgrad), F16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-                                      "gemm_kernel<2,1,0>: NVFP4 wgrad dW = dY^T X (fp32 out), f16 MFMA",
+                                      "gemm_nvp_kernel<true>: NVFP4 wgrad dW = dY^T X (fp32 out), persistent, f16 MFMA",
                                       algo["wgrad"], "gemm_wgrad_nvfp4", ms=round(g_wgrad, 4),
                                       frac_of_measured=round(tflops(g_wgrad) / peaks["mfma_f16_32x32x16_TFLOPs"], 4)),
         "dgrad_mxfp8": roofline_entry("mfma", tflops(g_dgrad), FP8_MFMA_PEAK_TFLOPS, "TFLOP/s",

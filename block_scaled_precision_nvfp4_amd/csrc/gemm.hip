@@ -88,13 +88,17 @@ struct Fmt {
     static constexpr int WAVES_N = GBN / (32 * TN);
 };
 
-// Byte offset of 16-byte chunk c (0..3) of LDS code row r: the chunk index is XORed with bits
-// 3..4 of the row (the DMAs apply the same permutation on the global side, swz_chunk).  For
-// the register-staged kernel's reads this placement measured about 110 B/clk/CU against 90 for
-// bits 1..2 and 55 unswizzled; for the 16-byte fragment reads of the LDS-DMA kernels bits 2..3
-// and 1..2 measured the same as 3..4 (within 1 %).
+// Byte offset of 16-byte chunk c (0..3) of LDS code row r (64-byte rows, so 4 rows fill the 64
+// banks).  Register-staged kernel (swz): the chunk index is XORed with bits 3..4 of the row; for
+// its 4-byte reads this placement measured about 110 B/clk/CU against 90 for bits 1..2 and 55
+// unswizzled.  LDS-DMA kernels (swzd; the DMAs apply the same permutation on the global side,
+// swzd_chunk): XORed with bits 2..3, so that the 16 lanes of a 16-byte read that takes one
+// chunk of 16 consecutive rows cover all 64 banks once (bits 3..4 leave rows r and r + 4 on the
+// same banks: a 2-way conflict).
 __device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 3) & 3); }
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_chunk(r, c) << 4); }
+__device__ __forceinline__ int swzd_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int swzd(int r, int c) { return r * ROWB + (swzd_chunk(r, c) << 4); }
 
 // Byte offset of scale dword w (0..1) of LDS scale row r (NVFP4: 8 raw E4M3 bytes per row,
 // the two dwords swapped on rows with bit 4 set so that 32 consecutive rows reading the
@@ -322,7 +326,7 @@ struct MxFrag {
 };
 
 // MXFP8 LDS layout.  A code stage (one K slice) is A codes [256][64 B] then B codes
-// [256][64 B], the 16-byte chunks swizzled by swz().  Scales use one of three layouts:
+// [256][64 B], the 16-byte chunks swizzled by swzd().  Scales use one of three layouts:
 //  - grouped (MX_RECS; K a multiple of 512, 16-byte aligned rows): the scale bytes of 8
 //    consecutive slices (16 K-blocks) of a row form one aligned 16-byte global record,
 //    fetched with one DMA lane per row every 8 slices into a double-buffered region
@@ -395,7 +399,7 @@ __device__ __forceinline__ void wait_vm() {
 // Per-wave DMA plan of one MXFP8 K slice, in four parts that the main loop spreads between its
 // MFMAs.  Part P (0..3) moves rows 64P + 16w .. +16 (w = wave) of both operands' codes; the
 // chunk swizzle is applied on the global side (the lane that fills LDS chunk slot cs of row r
-// fetches global chunk swz_chunk(r, cs)).  In the per-slice scale layout parts 0 and 1
+// fetches global chunk swzd_chunk(r, cs)).  In the per-slice scale layout parts 0 and 1
 // also move scale slots 256P + 64w .. +64 of both operands.  A slice past the end of K is
 // issued with out-of-range offsets (no memory traffic; the zeros they write land in a free
 // buffer) so that every slice issues the same number of DMAs.
@@ -411,7 +415,7 @@ struct MxDma {
 template <int P, int NW = 4>
 __device__ __forceinline__ void mx_dma_codes(const MxDma& d, int64_t b0, bool live, uint8_t* buf) {
     const int r0 = 16 * NW * P + 16 * d.wave;
-    const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
+    const int r = r0 + (d.lane >> 2), c = swzd_chunk(r, d.lane & 3);
     uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
     if (!live || b0 + 16 * c >= (int64_t)d.kbytes) off = OOB;
     const uint32_t soff = live ? (uint32_t)b0 : 0u;
@@ -445,7 +449,7 @@ __device__ __forceinline__ u32x4s sized(u32x4s rsrc, bool live) {
 template <int P, int NW>
 __device__ __forceinline__ void nv4_dma_codes(const MxDma& d, uint32_t b0, bool live, uint8_t* buf) {
     const int r0 = 16 * NW * P + 16 * d.wave;
-    const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
+    const int r = r0 + (d.lane >> 2), c = swzd_chunk(r, d.lane & 3);
     const uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
     const uint32_t soff = live ? b0 : 0u;
     dma_b128(sized(d.o.a, live), lds_addr(buf + r0 * ROWB), off, soff);
@@ -490,7 +494,7 @@ __device__ __forceinline__ u32x4s slab_rsrc(u32x4s r, uint32_t k, uint32_t bytes
 template <int P, int SL>
 __device__ __forceinline__ void mx_slab_codes(const MxDma& d, uint32_t k, bool live, uint8_t* buf) {
     const int r0 = 64 * P + 16 * d.wave;
-    const int r = r0 + (d.lane >> 2), c = swz_chunk(r, d.lane & 3);
+    const int r = r0 + (d.lane >> 2), c = swzd_chunk(r, d.lane & 3);
     const uint32_t off_s = (uint32_t)r * 64u + 16u * c;
     const uint32_t off_r = (uint32_t)r * d.rowbytes + 16u * c;
     const uint32_t soff = live ? 64u * k : 0u;
@@ -539,11 +543,11 @@ __device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* 
     const int ra = wm + 32 * P + frow, rb = wn + 32 * P + frow;
     const uint8_t* sA = buf;
     const uint8_t* sB = buf + GBM * ROWB;
-    uint4 lo = *(const uint4*)(sA + swz(ra, kh));
-    uint4 hi = *(const uint4*)(sA + swz(ra, 2 + kh));
+    uint4 lo = *(const uint4*)(sA + swzd(ra, kh));
+    uint4 hi = *(const uint4*)(sA + swzd(ra, 2 + kh));
     f.a[P] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    lo = *(const uint4*)(sB + swz(rb, kh));
-    hi = *(const uint4*)(sB + swz(rb, 2 + kh));
+    lo = *(const uint4*)(sB + swzd(rb, kh));
+    hi = *(const uint4*)(sB + swzd(rb, 2 + kh));
     f.b[P] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     if constexpr (MODE == MX_RECS || MODE == MX_SLAB) {
         f.as[P] = sbuf[ra * 16 + 2 * q + kh];
@@ -796,9 +800,9 @@ struct NvQuadT {
 template <int H, int TN>
 __device__ __forceinline__ void nvw_read_quad(const uint8_t* buf, int wm, int wn, int frow, int kh, NvQuadT<TN>& q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q.a[i] = *(const uint4*)(buf + swz(wm + 32 * i + frow, 2 * kh + H));
+    for (int i = 0; i < 4; ++i) q.a[i] = *(const uint4*)(buf + swzd(wm + 32 * i + frow, 2 * kh + H));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) q.b[j] = *(const uint4*)(buf + GBM * ROWB + swz(wn + 32 * j + frow, 2 * kh + H));
+    for (int j = 0; j < TN; ++j) q.b[j] = *(const uint4*)(buf + GBM * ROWB + swzd(wn + 32 * j + frow, 2 * kh + H));
 }
 
 template <int D>
