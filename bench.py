@@ -354,16 +354,14 @@ def qwen3_8b_hybrid_figures(dev, iters: int, mx_rows: bool = False):
     X [65536, 4096], W [12288, 4096], dY [65536, 12288] -- forward NVFP4 rowwise GEMM; MXFP8
     rowwise dY, MXFP8 columnwise dY and X from the bf16 originals and W from its rowwise-
     dequantized NVFP4 value; dgrad dX = dY W (bf16) and wgrad dW = dY^T X (fp32) on MXFP8.
-    Inputs are drawn on the device (seeded generator, same distributions as the step's)."""
+    Inputs are drawn as the step's are (CPU generator, seeds X 1234, W 1235, dY 1236, the same
+    standard deviations), at these shapes."""
     import torch
     import block_scaled_precision_nvfp4_amd as bsq
-    gen = torch.Generator(device=dev)
-    def randn(shape, std, seed):
-        gen.manual_seed(seed)
-        return (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
-    X = randn((QWEN_TOK, QWEN_K), 1.0, 2234)
-    W = randn((QWEN_N, QWEN_K), 0.02, 2235)
-    dY = randn((QWEN_TOK, QWEN_N), 1e-4, 2236)
+    from synthetic import SEED_DY, SEED_W, SEED_X, STD_DY, STD_W, gaussian_bf16
+    X = gaussian_bf16((QWEN_TOK, QWEN_K), 1.0, SEED_X).to(dev)
+    W = gaussian_bf16((QWEN_N, QWEN_K), STD_W, SEED_W).to(dev)
+    dY = gaussian_bf16((QWEN_TOK, QWEN_N), STD_DY, SEED_DY).to(dev)
     lay, fmx = (0, bsq.FMT_MXFP8) if mx_rows else (bsq.MX_SLAB, bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB)
     def run():
         qx = bsq.nvfp4_quantize(X, direction=bsq.ROW)
