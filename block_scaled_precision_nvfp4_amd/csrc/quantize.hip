@@ -340,6 +340,38 @@ __device__ __forceinline__ uint32_t encode_block(float* v, float vmax, float S, 
     return sb;
 }
 
+// The columnwise scales of a tile: column col's BN = 256 / BLK scale bytes sit in LDS at
+// sc[col][b ^ x(col)] (the placement the encode writes them in: x = (col >> 3) mod BN) and
+// are contiguous in the output row of column tc0 + col.  One thread per column gathers them
+// and, where the tile's rows are all inside R and the output row's bytes are aligned for it,
+// writes them with one BN-byte store (16 for NVFP4, 8 for MXFP8) instead of BN byte stores
+// spread over the workgroup.
+template <int BLK>
+__device__ __forceinline__ void store_col_scales(const uint8_t* sc, uint8_t* out, int64_t R, int64_t C, int64_t tr0,
+                                                 int64_t tc0) {
+    constexpr int BN = TILE_R / BLK;
+    const int col = threadIdx.x;
+    if (col >= TILE_C) return;
+    const int64_t c = tc0 + col;
+    if (c >= C) return;
+    const int x = (col >> 3) & (BN - 1);
+    uint8_t* dst = out + c * (R / BLK) + tr0 / BLK;
+    if (tr0 + TILE_R <= R && ((uintptr_t)dst % BN) == 0) {
+        uint32_t w[BN / 4];
+#pragma unroll
+        for (int i = 0; i < BN / 4; ++i) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v |= (uint32_t)sc[col * BN + ((4 * i + k) ^ x)] << (8 * k);
+            w[i] = v;
+        }
+        if constexpr (BN == 16) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+        else *(uint2*)dst = make_uint2(w[0], w[1]);
+    } else {
+        for (int b = 0; b < BN && tr0 + (int64_t)b * BLK < R; ++b) dst[b] = sc[col * BN + (b ^ x)];
+    }
+}
+
 template <int DIRS, bool RHT, bool SR>
 __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) {
     const TileCoord t = tile_coord();
@@ -425,11 +457,9 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             const int idx = threadIdx.x + NTHREADS * p;
             const int col = idx >> 4, rbk = idx & 15;
             const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
-            if (c < C && r < R) {
-                *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk ^ (col >> 3)];
-                a.col_scales[c * (R / 16) + r / 16] = lds_sc[col][rbk ^ (col >> 3)];
-            }
+            if (c < C && r < R) *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk ^ (col >> 3)];
         }
+        store_col_scales<16>(&lds_sc[0][0], a.col_scales, R, C, tr0, tc0);
     }
 }
 
@@ -596,9 +626,9 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
                 const uint4 cv = lds_codes[col][rbk ^ (col >> 3)];
                 __builtin_nontemporal_store(u32v4{cv.x, cv.y, cv.z, cv.w},
                                             (u32v4*)(a.col_codes + (a.slab ? slab_offset(c, r, C, R) : c * R + r)));
-                if ((rbk & 1) == 0) a.col_scales[c * (R / 32) + r / 32] = lds_sc[col][(rbk >> 1) ^ ((col >> 3) & 7)];
             }
         }
+        store_col_scales<32>(&lds_sc[0][0], a.col_scales, R, C, tr0, tc0);
     }
 }
 
