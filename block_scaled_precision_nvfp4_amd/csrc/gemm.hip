@@ -20,22 +20,21 @@
 // K-elements 32+16g..32+16g+15; the scale of K-block 0 (elements 0-31) comes from lanes
 // 0-31, that of K-block 1 from lanes 32-63.
 //
-// Tiling: a workgroup computes a 256 x 256 tile of C.  Each K slice (128 elements for NVFP4,
-// 64 for MXFP8) of both operands is 64 bytes of codes per row.  The NVFP4 kernel for K a
-// multiple of 256 and the MXFP8 kernel run 4 waves of 128 x 128 (4 x 4 MFMA tiles of 32 x 32,
-// 256 fp32 accumulators per lane) and move each slice from memory straight into a ring of 4
-// LDS stages by LDS DMA, three slices ahead of its use, with one barrier per slice; their
-// scales come as 16-byte records of a row's scale bytes (MXFP8 also per-slice bytes where
-// rows are not 16 bytes apart), and MXFP8 codes may come in the slab layout, where each slice
-// of a tile's rows is one contiguous block.  The register-staged NVFP4 kernel (other K, and
-// K-grouped NVFP4) runs 8 waves (two per SIMD) of 128 x 64, so that one wave's dequantization
-// overlaps the other's MFMAs, and stages slices through registers into 3 LDS buffers.  The
-// buffer loads' range check zero-fills rows beyond M or N, and an out-of-range offset the K
-// tail.  16-byte chunks are XOR-swizzled by row for conflict-free fragment reads.  Inside a
-// slice the operands of the next MFMA step are read from LDS (and, for NVFP4, dequantized)
-// while the current step's MFMAs issue.  Workgroups are renumbered so that each of the 8 XCDs
-// (which take workgroups round-robin) works on a contiguous band of output tiles and reuses
-// operand rows from its own L2.
+// Tiling: a workgroup computes a 256 x 256 tile of C with 4 waves of 128 x 128 (4 x 4 MFMA
+// tiles of 32 x 32, 256 fp32 accumulators per lane).  Each K slice (128 elements for NVFP4, 64
+// for MXFP8) of both operands is 64 bytes of codes per row, moved from memory straight into a
+// ring of 4 LDS stages by LDS DMA, three slices ahead of its use, with one barrier per slice.
+// Scales: 16-byte records of a row's scale bytes where scale rows lie 16 bytes apart (NVFP4 K a
+// multiple of 256; MXFP8 also at an offset inside the record, or per-slice bytes otherwise),
+// and for NVFP4 with any other K (or K-grouped) per-slice records of 3 aligned dwords per row.
+// MXFP8 codes may come in the slab layout, where each slice of a tile's rows is one contiguous
+// block.  Plain NVFP4 launches with per-tensor scales run persistently (gemm_nvp_kernel),
+// carrying the LDS ring from one tile to the next.  The buffer loads' range check zero-fills
+// rows beyond M or N, and an out-of-range offset the K tail.  16-byte chunks are XOR-swizzled
+// by row.  Inside a slice the operands of the next MFMA step are read from LDS (and, for
+// NVFP4, dequantized) while the current step's MFMAs issue.  Workgroups are renumbered so that
+// each of the 8 XCDs (which take workgroups round-robin) works on a contiguous band of output
+// tiles and reuses operand rows from its own L2.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -63,66 +62,32 @@ struct GemmArgs {
     int slab;             // MXFP8 codes in the slab layout (K a multiple of 512): bit 0 A, bit 1 B
 };
 
-// FMT 0: NVFP4, 8 waves of 128 x 64, register-staged (any K); FMT 1: MXFP8, 4 waves of 128 x
-// 128; FMT 2: NVFP4 with LDS DMA and grouped scale records (K a multiple of 256), 4 waves of
-// 128 x 128.
+// FMT 1: MXFP8; FMT 2: NVFP4 with grouped scale records (K a multiple of 256); FMT 3: NVFP4
+// with per-slice scale records (K a multiple of 32).  All three: 4 waves of 128 x 128, 4 LDS
+// stages filled by LDS DMA.
 template <int FMT>
 struct Fmt {
     static constexpr bool NV = FMT != 1;
     static constexpr int BK = NV ? 128 : 64;          // K elements per slice
     static constexpr int EPB = NV ? 2 : 1;            // elements per code byte
     static constexpr int BLK = NV ? 16 : 32;          // elements per scale
-    static constexpr int SPR = BK / BLK;              // scale bytes per row per slice (8 or 2)
-    static constexpr int SCB = 8;                     // LDS bytes per row for scales
-    // NVFP4: 8 raw scale bytes per row; MXFP8: one dword slot per (row, K-block), 2 per row
-    static constexpr int STAGE = (GBM + GBN) * (ROWB + SCB);
-    static constexpr int NSTAGE = FMT == 0 ? 3 : 4;
-    // MXFP8 also keeps room for three 8 KiB scale-record buffers after its 4 code stages
-    static constexpr int LDS = NSTAGE * STAGE + (FMT == 1 ? 8192 : 0);
-    // waves per workgroup and MFMA tiles per wave: 8 waves (two per SIMD) of 128 x 64 or 4
-    // waves of 128 x 128.
-    static constexpr int NW = FMT == 0 ? 8 : 4;
-    static constexpr int THREADS = 64 * NW;
-    static constexpr int TM = 4;                  // 32-row A fragments per wave
-    static constexpr int TN = NW == 8 ? 2 : 4;    // 32-row B fragments per wave
+    // static LDS per workgroup: MXFP8 4 x 36 KiB stages + an 8 KiB scale-record buffer; NVFP4
+    // with records 4 x 32 KiB code stages + 2 x 8 KiB record groups; NVFP4 per slice 4 x 38 KiB
+    static constexpr int LDS = FMT == 3 ? 4 * (2 * GBM * ROWB + 2 * GBM * 12)
+                                        : 4 * (GBM + GBN) * (ROWB + 8) + (FMT == 1 ? 8192 : 0);
+    static constexpr int THREADS = 256;               // 4 waves
+    static constexpr int TN = 4;                      // 32-row B fragments per wave (128 x 128)
     static constexpr int WAVES_N = GBN / (32 * TN);
 };
 
 // Byte offset of 16-byte chunk c (0..3) of LDS code row r (64-byte rows, so 4 rows fill the 64
-// banks).  Register-staged kernel (swz): the chunk index is XORed with bits 3..4 of the row; for
-// its 4-byte reads this placement measured about 110 B/clk/CU against 90 for bits 1..2 and 55
-// unswizzled.  LDS-DMA kernels (swzd; the DMAs apply the same permutation on the global side,
-// swzd_chunk): XORed with bits 2..3, so that the 16 lanes of a 16-byte read that takes one
-// chunk of 16 consecutive rows cover all 64 banks once (bits 3..4 leave rows r and r + 4 on the
-// same banks: a 2-way conflict).
-__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 3) & 3); }
-__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_chunk(r, c) << 4); }
+// banks): the chunk index is XORed with bits 2..3 of the row (the DMAs apply the same
+// permutation on the global side, swzd_chunk), so that the 16 lanes of a 16-byte read that takes
+// one chunk of 16 consecutive rows cover all 64 banks once (bits 3..4 would leave rows r and
+// r + 4 on the same banks).
 __device__ __forceinline__ int swzd_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
 __device__ __forceinline__ int swzd(int r, int c) { return r * ROWB + (swzd_chunk(r, c) << 4); }
 
-// Byte offset of scale dword w (0..1) of LDS scale row r (NVFP4: 8 raw E4M3 bytes per row,
-// the two dwords swapped on rows with bit 4 set so that 32 consecutive rows reading the
-// same dword hit 32 distinct banks).
-__device__ __forceinline__ int sswz(int r, int w) { return r * 8 + ((w ^ ((r >> 4) & 1)) << 2); }
-
-// Staging registers of one K slice: chunks (tid + 256p) of the 256 x 4 chunk grid of A and
-// of B, and the scale bytes of two rows of one operand.
-struct Stage {
-    uint4 a[4], b[4];
-    uint32_t s[2][2];   // [row half][word]
-};
-
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
-
-// Buffer resources of this workgroup's operand rows.  Each resource starts at the tile's
-// first row and covers the rows that exist, so a load from a row beyond M or N returns zero
-// (hardware range check); a chunk beyond K gets an offset past the range.  Loads are issued
-// unconditionally (a branch around a load makes the compiler wait for it before the next
-// one), each with one 32-bit lane offset and the slice's byte offset as a scalar.
-struct Operands {
-    __amdgpu_buffer_rsrc_t a, b, as, bs;
-};
 
 constexpr int RSRC_FLAGS = 0x00020000;   // raw 32-bit data, no format conversion
 constexpr uint32_t OOB = 0x80000000u;    // an offset beyond every resource's range
@@ -137,127 +102,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, RSRC_FLAGS);
 }
 
-template <int FMT>
-__device__ __forceinline__ Operands make_operands(const GemmArgs& g, int64_t m0, int64_t n0) {
-    using F = Fmt<FMT>;
-    const int64_t rowbytes = g.ld / F::EPB, sstride = g.ld / F::BLK;
-    Operands o;
-    const int64_t ra = tile_rows(g.M - m0, GBM), rb = tile_rows(g.N - n0, GBN);
-    o.a = make_rsrc(g.a_codes + m0 * rowbytes, ra * rowbytes);
-    o.b = make_rsrc(g.b_codes + n0 * rowbytes, rb * rowbytes);
-    o.as = make_rsrc(g.a_scales + m0 * sstride, ra * sstride);
-    o.bs = make_rsrc(g.b_scales + n0 * sstride, rb * sstride);
-    return o;
-}
-
-template <int FMT>
-__device__ __forceinline__ void stage_load(const GemmArgs& g, const Operands& o, int64_t k0, Stage& st) {
-    using F = Fmt<FMT>;
-    const int tid = threadIdx.x;
-    const uint32_t rowbytes = (uint32_t)(g.ld / F::EPB);
-    const int soff = (int)(k0 / F::EPB);
-    const bool tail = k0 + F::BK > g.K;   // uniform
-#pragma unroll
-    for (int p = 0; p < GBM * 4 / F::THREADS; ++p) {
-        const int idx = tid + F::THREADS * p;
-        const int r = idx >> 2, c = idx & 3;
-        uint32_t off = (uint32_t)r * rowbytes + 16u * c;
-        if (tail && k0 + (int64_t)c * 16 * F::EPB >= g.K) off = OOB;
-        st.a[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(o.a, off, soff, 0));
-        st.b[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(o.b, off, soff, 0));
-    }
-    // scales: the first half of the threads own A rows (two rows each with 256 threads, one
-    // with 512), the second half the same B rows.  The operand choice is wave-uniform;
-    // reading it through readfirstlane lets the resource stay in scalar registers.
-    constexpr int HT = F::THREADS / 2, RPT = GBM / HT;
-    const int op = __builtin_amdgcn_readfirstlane(tid / HT), rr = tid % HT;
-    const uint32_t sstride = (uint32_t)(g.ld / F::BLK);
-    const int ssoff = (int)(k0 / F::BLK);
-    const bool aligned = (sstride % F::SPR) == 0 && !tail &&
-                         (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % F::SPR) == 0;   // uniform
-#pragma unroll
-    for (int h = 0; h < RPT; ++h) {
-        const uint32_t off = (uint32_t)(rr + HT * h) * sstride;
-        const __amdgpu_buffer_rsrc_t rs = op ? o.bs : o.as;
-        uint32_t w0 = 0, w1 = 0;
-        if (aligned) {
-            if (F::SPR == 8) {
-                const u32x2v v = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(rs, off, ssoff, 0));
-                w0 = v.x;
-                w1 = v.y;
-            } else {
-                w0 = __builtin_amdgcn_raw_buffer_load_b16(rs, off, ssoff, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < F::SPR; ++i) {
-                const uint32_t o_i = (k0 + (int64_t)i * F::BLK < g.K) ? off + i : OOB;
-                const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(rs, o_i, ssoff, 0);
-                if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
-            }
-        }
-        st.s[h][0] = w0;
-        st.s[h][1] = w1;
-    }
-}
-
-template <int FMT>
-__device__ __forceinline__ void stage_store(uint8_t* buf, const Stage& st) {
-    using F = Fmt<FMT>;
-    const int tid = threadIdx.x;
-    uint8_t* sA = buf;
-    uint8_t* sB = buf + GBM * ROWB;
-    uint8_t* sAs = buf + (GBM + GBN) * ROWB;
-    uint8_t* sBs = sAs + GBM * F::SCB;
-#pragma unroll
-    for (int p = 0; p < GBM * 4 / F::THREADS; ++p) {
-        const int idx = tid + F::THREADS * p;
-        const int r = idx >> 2, c = idx & 3;
-        *(uint4*)(sA + swz(r, c)) = st.a[p];
-        *(uint4*)(sB + swz(r, c)) = st.b[p];
-    }
-    constexpr int HT = F::THREADS / 2, RPT = GBM / HT;
-    const int op = tid / HT, rr = tid % HT;
-    uint8_t* ss = op ? sBs : sAs;
-#pragma unroll
-    for (int h = 0; h < RPT; ++h) {
-        const int r = rr + HT * h;
-        const uint32_t w0 = st.s[h][0], w1 = st.s[h][1];
-        const bool sw = ((r >> 4) & 1) != 0;
-        *(uint2*)(ss + r * 8) = sw ? make_uint2(w1, w0) : make_uint2(w0, w1);
-    }
-}
-
 // ---------------------------------------------------------------- NVFP4 fragments
-
-// Code words of one MFMA step for the wave's 4 A and 4 B fragments: lane (row, kh) of step
-// s (0..7) holds the 8 codes of K elements 64kh + 8s .. +8 of the slice, i.e. dword s%4 of
-// chunk 2kh + s/4 of its row; they belong to block 4kh + s/2 of the slice.
-constexpr int NVTN = Fmt<0>::TN;   // B fragments per NVFP4 wave
-
-struct NvWords {
-    uint32_t a[4], b[NVTN];
-};
-
-template <int S>
-__device__ __forceinline__ void nv_read_words(const uint8_t* buf, int wm, int wn, int frow, int kh, NvWords& w) {
-    const uint8_t* sA = buf;
-    const uint8_t* sB = buf + GBM * ROWB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w.a[i] = *(const uint32_t*)(sA + swz(wm + 32 * i + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
-#pragma unroll
-    for (int j = 0; j < NVTN; ++j) w.b[j] = *(const uint32_t*)(sB + swz(wn + 32 * j + frow, 2 * kh + (S >> 2)) + 4 * (S & 3));
-}
-
-__device__ __forceinline__ void nv_read_scales(const uint8_t* buf, int wm, int wn, int frow, int kh, uint32_t (&sa)[4],
-                                               uint32_t (&sb)[NVTN]) {
-    const uint8_t* sAs = buf + (GBM + GBN) * ROWB;
-    const uint8_t* sBs = sAs + GBM * Fmt<0>::SCB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = *(const uint32_t*)(sAs + sswz(wm + 32 * i + frow, kh));
-#pragma unroll
-    for (int j = 0; j < NVTN; ++j) sb[j] = *(const uint32_t*)(sBs + sswz(wn + 32 * j + frow, kh));
-}
 
 // E2M1 x 2^8 from the hardware conversion (byte `sel` of w, two codes), times the f16 scale
 // s * 2^-8; exact.
@@ -280,45 +125,10 @@ __device__ __forceinline__ half2_t nv_scale(uint32_t w, int b) {
     return (b >> 1) ? half2_t{p[1], p[1]} : half2_t{p[0], p[0]};
 }
 
-// Dequantized operands of one MFMA step for the wave's 4 A and 4 B fragments.
-struct NvOps {
-    half8_t a[4], b[NVTN];
-};
-
-template <int S>
-__device__ __forceinline__ void nv_ops(const NvWords& w, const uint32_t (&sa)[4], const uint32_t (&sb)[NVTN], NvOps& o) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o.a[i] = nv_dequant(w.a[i], nv_scale(sa[i], S >> 1));
-#pragma unroll
-    for (int j = 0; j < NVTN; ++j) o.b[j] = nv_dequant(w.b[j], nv_scale(sb[j], S >> 1));
-}
-
-__device__ __forceinline__ void nv_mfma16(const NvOps& o, floatx16 (&acc)[4][NVTN]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NVTN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
-}
-
-// Scheduling hint for one pipelined step: the LDS reads of the next step's code words first,
-// then 2 MFMAs alone while they land, then the remaining MFMAs each followed by an equal share
-// of the next step's dequantization instructions (8 per fragment).
-__device__ __forceinline__ void nv_interleave() {
-    constexpr int NM = 4 * NVTN;                           // MFMAs per step
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NVTN + 4, 0);  // DS reads of the next step
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMAs while the reads land
-#pragma unroll
-    for (int i = 0; i < NM - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, (8 * (4 + NVTN) + NM - 3) / (NM - 2), 0);  // VALU
-    }
-}
-
 // ---------------------------------------------------------------- MXFP8 slice
 
 constexpr int MXTN = Fmt<1>::TN;   // B fragments per MXFP8 wave
-static_assert(MXTN == 4 && Fmt<1>::NW == 4, "the MXFP8 slice is written for 4 waves of 4 x 4 tiles");
+static_assert(MXTN == 4 && Fmt<1>::THREADS == 256, "the MXFP8 slice is written for 4 waves of 4 x 4 tiles");
 
 struct MxFrag {
     intx8 a[4], b[MXTN];
@@ -979,6 +789,183 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
     wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
 }
 
+// ---------------------------------------------------------------- NVFP4 with per-slice scale DMAs
+
+// Any K that is a multiple of 32 (the C ABI's rule), and K-grouped operands whose groups start
+// at any multiple of 32: the LDS organisation and operand pipeline of nvw_main_loop, with the
+// scales fetched per slice instead of as 16-byte records (which need scale rows 16 bytes
+// apart).  A row's 8 scale bytes of a slice start 0 or 2 bytes into an aligned dword (scale
+// rows lie an even number of bytes apart), so each comes as the 3 aligned dwords that cover
+// it, by dword LDS DMA, into a 12-byte record in the slice's stage; the lane that needs 4 of
+// the bytes (blocks 4kh .. 4kh+3) reads two dwords of the record and shifts.  Stage: A codes
+// [256][64 B], B codes [256][64 B] (as in nvw_main_loop), A records [256][12 B], B records
+// [256][12 B] = 38 KiB.  Per slice each lane issues 8 code DMAs and 6 record DMAs, the same in
+// every slice, so every wait allows the previous slice's 14 in flight.  The records' offsets
+// go into the vector offset (the scalar offset escapes the buffer range check), so a dword
+// past a tile's last scale byte reads as zero.  In a slice that K ends inside (K % 128 != 0)
+// the code DMAs check each 16-byte chunk (K % 32 == 0: a chunk lies entirely inside or
+// outside K) and the scale bytes past K are cleared, so that nothing beyond the operands' K
+// reaches the sums.
+constexpr int NVS_REC = 12;
+constexpr int NVS_STAGE = NV4_CODES + 2 * GBM * NVS_REC;   // 38 KiB
+constexpr int NVS_DS = 6;                                  // record DMAs per lane per slice
+static_assert(4 * NVS_STAGE <= Fmt<3>::LDS, "NVFP4 per-slice scale LDS");
+static_assert(NVS_DS * 64 * 4 == 2 * GBM * 3, "the records of a slice: 4 waves x 6 DMAs of 64 dwords");
+
+__device__ __forceinline__ void dma_b32(const u32x4s& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
+// Code DMAs of part P of the slice whose first code byte per row is b0; in the slice that K
+// ends inside (tail, uniform) every lane checks its chunk and carries the whole offset in the
+// vector offset, so that the range check sees it.
+template <int P>
+__device__ __forceinline__ void nvs_dma_codes(const MxDma& d, uint32_t b0, bool live, bool tail, uint8_t* buf) {
+    const int r0 = 64 * P + 16 * d.wave;
+    const int r = r0 + (d.lane >> 2), c = swzd_chunk(r, d.lane & 3);
+    uint32_t off = (uint32_t)r * d.rowbytes + 16u * c;
+    uint32_t soff = live ? b0 : 0u;
+    if (tail) {
+        off = b0 + 16u * c < d.kbytes ? off + b0 : OOB;
+        soff = 0u;
+    }
+    dma_b128(sized(d.o.a, live), lds_addr(buf + r0 * ROWB), off, soff);
+    dma_b128(sized(d.o.b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off, soff);
+}
+
+// Record DMAs I0 .. I1-1 (of 6) of the slice whose scale bytes start 8k into each row: DMA i
+// of wave w fills dword slots 64 (w + 4i) .. +64 of the slice's records (A's 768, then B's).
+template <int I0, int I1>
+__device__ __forceinline__ void nvs_dma_recs(const u32x4s& rsa, const u32x4s& rsb, const uint32_t (&so)[NVS_DS],
+                                             uint32_t k8, bool live, uint8_t* rec, int wave) {
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        const u32x4s& rs = i >= 3 ? rsb : rsa;   // slot groups w + 4i >= 12 belong to B
+        dma_b32(sized(rs, live), lds_addr(rec + 256 * (wave + 4 * i)), so[i] + k8, 0u);
+    }
+}
+
+// The lane's 4 scale bytes (blocks 4kh .. 4kh+3) of each of its fragments from a slice's
+// records: two dwords at the record's dword oq (0 or 1), shifted right by sh bits (0 or 16,
+// or 8 / 24 for a scale tensor that is not even-aligned), then masked (the bytes past K).
+template <int TN>
+__device__ __forceinline__ void nvs_read_scales(const uint8_t* rec, int wm, int wn, int frow, uint32_t oqa,
+                                                uint32_t sha, uint32_t oqb, uint32_t shb, uint32_t mask,
+                                                uint32_t (&sa)[4], uint32_t (&sb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t* p = (const uint32_t*)(rec + (wm + 32 * i + frow) * NVS_REC) + oqa;
+        sa[i] = __builtin_amdgcn_alignbit(p[1], p[0], sha) & mask;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const uint32_t* p = (const uint32_t*)(rec + GBM * NVS_REC + (wn + 32 * j + frow) * NVS_REC) + oqb;
+        sb[j] = __builtin_amdgcn_alignbit(p[1], p[0], shb) & mask;
+    }
+}
+
+template <int TN>
+__device__ __forceinline__ void nvs_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
+                                              int wm, int wn, int lane, floatx16 (&acc)[4][TN]) {
+    constexpr int NW = 4, DC = 8, PSTEP = 2;
+    static_assert(16 / TN == NW, "4 waves of 128 x 128");
+    if (nk <= 0) return;
+    const MxDma d = make_dma<2, 16>(g, m0, n0, lane);
+    const int frow = lane & 31, kh = lane >> 5;
+    auto buf = [&](int k) { return lds + (k & 3) * NVS_STAGE; };
+    auto rec = [&](int k) { return buf(k) + NV4_CODES; };
+    const int nk32 = (int)nk;   // nk <= 2^20 (host check)
+    const uint32_t kscale = d.kblocks;                           // scale bytes of a row's K
+    const bool ktail = (d.kbytes & 63u) != 0;                    // K % 128 != 0
+    const uint32_t tail_blocks = (kscale & 7u) ? (kscale & 7u) : 8u;   // valid blocks of the last slice
+    // Record resources: from the aligned dword at or below the tile's first scale byte to its
+    // last row's K scale bytes, rounded up to whole dwords (rows past the tile read as zero).
+    const int64_t sbs = g.ld / 16;
+    const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, GBN);
+    const uint8_t* pa = g.a_scales + m0 * sbs;
+    const uint8_t* pb = g.b_scales + n0 * sbs;
+    const uint32_t dla = (uint32_t)((uintptr_t)pa & 3), dlb = (uint32_t)((uintptr_t)pb & 3);
+    const u32x4s rsa = rsrc_words(pa - dla, (dla + (ra - 1) * sbs + kscale + 3) & ~(int64_t)3);
+    const u32x4s rsb = rsrc_words(pb - dlb, (dlb + (rbn - 1) * sbs + kscale + 3) & ~(int64_t)3);
+    uint32_t so[NVS_DS];   // the lane's record DMA offsets for slice 0
+#pragma unroll
+    for (int i = 0; i < NVS_DS; ++i) {
+        const bool opb = i >= 3;
+        const int s = 64 * (d.wave + 4 * i - (opb ? 12 : 0)) + lane, r = s / 3, dw = s - 3 * r;
+        const int64_t rows = opb ? rbn : ra;
+        const uint32_t dl = opb ? dlb : dla;
+        so[i] = r < rows ? (uint32_t)((dl + (uint64_t)r * (uint64_t)sbs) & ~(uint64_t)3) + 4u * dw : OOB;
+    }
+    // where the lane's 4 bytes start in a record: row R's bytes start ((dl + R sbs) mod 4) into
+    // it, and R sbs mod 4 depends only on R's parity (sbs is even), which is frow's
+    const uint32_t par = (uint32_t)(frow & 1) * ((uint32_t)sbs & 2u);
+    const uint32_t oa = ((dla + par) & 3u) + 4u * kh, ob = ((dlb + par) & 3u) + 4u * kh;
+    const uint32_t oqa = oa >> 2, sha = 8u * (oa & 3u), oqb = ob >> 2, shb = 8u * (ob & 3u);
+    // scale bytes of the last slice past K read as zero blocks
+    const int vb = (int)tail_blocks - 4 * kh;   // valid bytes of the lane's 4 in the last slice
+    const uint32_t tmask = vb >= 4 ? ~0u : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+    auto mask_of = [&](int k) { return k == nk32 - 1 ? tmask : ~0u; };
+
+    auto dma_slice = [&](int k) {
+        const bool live = k < nk32, tail = ktail && k == nk32 - 1;
+        static_for<0, 4>([&](auto p_c) { nvs_dma_codes<decltype(p_c)::value>(d, 64u * k, live, tail, buf(k)); });
+        nvs_dma_recs<0, NVS_DS>(rsa, rsb, so, 8u * k, live, rec(k), d.wave);
+    };
+    dma_slice(0);
+    dma_slice(1);
+    dma_slice(2);
+    wait_vm_barrier<2 * (DC + NVS_DS)>();
+
+    NvQuadT<TN> q0, q1;
+    NvWordsT<TN> w;
+    NvOpsT<TN> cur, nxt;
+    uint32_t sa[4], sb[TN], san[4], sbn[TN];
+    nvs_read_scales<TN>(rec(0), wm, wn, frow, oqa, sha, oqb, shb, mask_of(0), sa, sb);
+    nvw_read_quad<0, TN>(buf(0), wm, wn, frow, kh, q0);
+    nvw_words_of<0, TN>(q0, w);
+    nvw_ops<0, TN>(w, sa, sb, cur);
+
+    // Slice kt: the DMAs of slice kt+3 spread over the steps (codes at steps 0, 2, 4, 6,
+    // records at steps 1 and 3), the operand reads as in nvw_main_loop (second half of this
+    // slice at step 2, the next slice's scales at step 5 and first half at step 6).
+    for (int kt = 0; kt < nk32; ++kt) {
+        wait_vm_barrier<DC + NVS_DS>();
+        const int kd = kt + 3;
+        const bool live = kd < nk32, tail = ktail && kd == nk32 - 1;
+        uint8_t* db = buf(kd);
+        uint8_t* dr = rec(kd);
+        const uint8_t* cb = buf(kt);
+        const uint8_t* nb = buf(kt + 1);
+        const uint8_t* nr = rec(kt + 1);
+        const uint32_t nmask = mask_of(kt + 1);
+        static_for<0, 8>([&](auto s_c) {
+            constexpr int S = decltype(s_c)::value;
+            if constexpr (S % PSTEP == 0) nvs_dma_codes<S / PSTEP>(d, 64u * kd, live, tail, db);
+            if constexpr (S == 1) nvs_dma_recs<0, 3>(rsa, rsb, so, 8u * kd, live, dr, d.wave);
+            if constexpr (S == 3) nvs_dma_recs<3, 6>(rsa, rsb, so, 8u * kd, live, dr, d.wave);
+            if constexpr (S == 2) nvw_read_quad<1, TN>(cb, wm, wn, frow, kh, q1);
+            if constexpr (S == 6) nvw_read_quad<0, TN>(nb, wm, wn, frow, kh, q0);
+            if constexpr (S == 5) nvs_read_scales<TN>(nr, wm, wn, frow, oqa, sha, oqb, shb, nmask, san, sbn);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (S + 1 < 4) nvw_words_of<S + 1, TN>(q0, w);
+            else if constexpr (S + 1 < 8) nvw_words_of<S + 1, TN>(q1, w);
+            else nvw_words_of<0, TN>(q0, w);
+            if constexpr (S + 1 < 8) nvw_ops<S + 1, TN>(w, sa, sb, nxt);
+            else nvw_ops<0, TN>(w, san, sbn, nxt);
+            nvw_mfma<TN>(cur, acc);
+            nvw_interleave<TN>();
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+        });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = san[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb[j] = sbn[j];
+    }
+    wait_vm<0>();   // no DMA may still write this workgroup's LDS when the wave ends
+}
+
 // ---------------------------------------------------------------- epilogue
 
 // Epilogue of a tile whose columns lie inside C (4 waves of 128 x 128); rows from m_end on
@@ -1278,75 +1265,14 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     // tile_factors); computed before the main loop so that the epilogue does not wait for the
     // scale loads.
     float alpha_pt = 1.0f;
-    if constexpr (FMT == 2) {
+    if constexpr (FMT == 2 || FMT == 3) {
         if (!g.a_rows && !g.b_rows) alpha_pt = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
 #if __HIP_DEVICE_COMPILE__
         asm volatile("" : "+v"(alpha_pt));
 #endif
     }
     const int frow = lane & 31, kh = lane >> 5;
-    const Operands ops = make_operands<FMT>(g, m0, n0);
-    if constexpr (FMT == 0) {
-        // NVFP4 pipeline over K slices with NSTAGE = 3 LDS buffers.  At the top of iteration kt
-        // a barrier makes slice kt+1 (stored during iteration kt-1) visible and guarantees that
-        // every wave is done with slice kt-1; the staged registers of slice kt+2 then go to
-        // slice kt-1's buffer and the global loads of slice kt+3 are issued, two iterations
-        // ahead of their use.
-        Stage st;
-        if (nk > 0) {
-            stage_load<FMT>(g, ops, 0, st);
-            stage_store<FMT>(lds, st);
-            if (nk > 1) {
-                stage_load<FMT>(g, ops, F::BK, st);
-                stage_store<FMT>(lds + F::STAGE, st);
-            }
-            if (nk > 2) stage_load<FMT>(g, ops, 2 * F::BK, st);
-            __syncthreads();
-        }
-        // NVFP4 software pipeline, one MFMA step (16 MFMAs of K = 16) at a time: while step s
-        // issues its MFMAs, the code words of step s+1 are read from LDS and dequantized into
-        // the next operand set.  The last step of a slice reads and dequantizes step 0 of the
-        // next slice, whose buffer is complete since the barrier at the top of this slice; the
-        // next slice's scale dwords are read at step 6.
-        NvWords w;
-        NvOps cur, nxt;
-        uint32_t sa[4], sb[NVTN], san[4] = {0, 0, 0, 0}, sbn[NVTN] = {};
-        auto bufp = [&](int64_t k) { return lds + (int)(k % F::NSTAGE) * F::STAGE; };
-        if (nk > 0) {
-            nv_read_scales(bufp(0), wm, wn, frow, kh, sa, sb);
-            nv_read_words<0>(bufp(0), wm, wn, frow, kh, w);
-            nv_ops<0>(w, sa, sb, cur);
-        }
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            const uint8_t* cb = bufp(kt);
-            const bool more = kt + 1 < nk;
-            if (kt > 0) __syncthreads();
-            if (kt + 2 < nk) stage_store<FMT>(bufp(kt + 2), st);
-            if (kt + 3 < nk) stage_load<FMT>(g, ops, (kt + 3) * F::BK, st);
-            static_for<0, 8>([&](auto s_c) {
-                constexpr int S = decltype(s_c)::value;
-                if constexpr (S < 7) {
-                    nv_read_words<S + 1>(cb, wm, wn, frow, kh, w);
-                    if constexpr (S == 6) {
-                        if (more) nv_read_scales(bufp(kt + 1), wm, wn, frow, kh, san, sbn);
-                    }
-                    nv_ops<S + 1>(w, sa, sb, nxt);
-                } else {
-                    if (more) {
-                        nv_read_words<0>(bufp(kt + 1), wm, wn, frow, kh, w);
-                        nv_ops<0>(w, san, sbn, nxt);
-                    }
-                }
-                nv_mfma16(cur, acc);
-                nv_interleave();
-                cur = nxt;
-            });
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sa[i] = san[i];
-#pragma unroll
-            for (int j = 0; j < NVTN; ++j) sb[j] = sbn[j];
-        }
-    } else if constexpr (FMT == 1) {
+    if constexpr (FMT == 1) {
         // scale records need rows 16 bytes apart; aligned ones also K a multiple of 512 and
         // 16-byte aligned scale tensors
         const bool rows16 = (g.ld / 32) % 16 == 0;
@@ -1358,13 +1284,14 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         else if (recs) mx_main_loop<MX_RECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (rows16) mx_main_loop<MX_OFFRECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else mx_main_loop<MX_SLOTS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
-    } else {
+    } else if constexpr (FMT == 2) {
         nvw_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+    } else {
+        nvs_main_loop<TN>(g, m0, n0, nk, lds, wm, wn, lane, acc);
     }
     (void)alpha_pt;
 
-    static_assert(FMT == 0 || (F::LDS - FACT_BYTES >= 4 * 128 * (128 * 2 + 16) &&
-                               F::LDS - FACT_BYTES >= 4 * 64 * (128 * 4 + 16)),
+    static_assert(F::LDS - FACT_BYTES >= 4 * 128 * (128 * 2 + 16) && F::LDS - FACT_BYTES >= 4 * 64 * (128 * 4 + 16),
                   "factor tables overlap the epilogue staging");
     // NVFP4 output factors (MXFP8 needs none: its scales are inside the MFMA)
     float* fa = (float*)(lds + F::LDS - FACT_BYTES);
@@ -1374,7 +1301,7 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
     // staged epilogue: every column of the tile inside C (rows past M are skipped there)
     const bool staged = n0 + GBN <= g.N && (g.N * ES) % 16 == 0;   // uniform
     const int64_t m_end = g.M - m0;
-    if constexpr (FMT == 2) {
+    if constexpr (FMT == 2 || FMT == 3) {
         // per-tensor scales on both operands: one uniform factor, no tables
         if (staged && !g.a_rows && !g.b_rows) {
             store_tile_lds<OUT_F32, true>(g, lds, m0, n0, wm, wn, wave, lane, nullptr, nullptr, alpha_pt, m_end, acc);
@@ -1385,21 +1312,19 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         tile_factors<FMT>(g, m0, n0, fa, fb);
         __syncthreads();
     }
-    if constexpr (FMT != 0) {
-        if (staged) {
-            store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, m_end, acc);
-            return;
-        }
+    if (staged) {
+        store_tile_lds<OUT_F32, F::NV>(g, lds, m0, n0, wm, wn, wave, lane, fa, fb, 1.0f, m_end, acc);
+        return;
     }
-    // FMT 1 and 2 accumulators hold C^T tiles (see nvw_mfma): swap the roles of frow and r
-    constexpr bool TR = FMT != 0;
+    // the accumulators hold C^T tiles (see nvw_mfma): lane (frow, kh), register r of tile (i, j)
+    // is row 32i + frow, column 32j + within
     static_for<0, 4 * TN>([&](auto t_c) {
         constexpr int i = decltype(t_c)::value / TN, j = decltype(t_c)::value % TN;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int within = 8 * (r >> 2) + 4 * kh + (r & 3);
-            const int lrow = wm + 32 * i + (TR ? frow : within);
-            const int lcol = wn + 32 * j + (TR ? within : frow);
+            const int lrow = wm + 32 * i + frow;
+            const int lcol = wn + 32 * j + within;
             const int64_t row = m0 + lrow, col = n0 + lcol;
             if (row < g.M && col < g.N) {
                 const float v = F::NV ? acc[i][j][r] * (fa[lrow] * fb[lcol]) : acc[i][j][r];
@@ -1733,13 +1658,13 @@ static int launch_fmt(int fmt, int c_dtype, const GemmArgs& g, const GroupArgs& 
             }
         }
     }
-    // NVFP4: the LDS DMA kernel when every K handled is a multiple of 256 (known on the host
-    // unless K varies per group), the register-staged kernel otherwise
+    // NVFP4: the LDS DMA kernel with scale records when every K handled is a multiple of 256
+    // (known on the host unless K varies per group), with per-slice scale records otherwise
     if constexpr (GM != 2) {
         if (fmt == 0 && g.K % 256 == 0)
             return c_dtype == 1 ? launch_one<2, 1, GM>(g, q, tiles, s) : launch_one<2, 0, GM>(g, q, tiles, s);
     }
-    if (fmt == 0) return c_dtype == 1 ? launch_one<0, 1, GM>(g, q, tiles, s) : launch_one<0, 0, GM>(g, q, tiles, s);
+    if (fmt == 0) return c_dtype == 1 ? launch_one<3, 1, GM>(g, q, tiles, s) : launch_one<3, 0, GM>(g, q, tiles, s);
     return c_dtype == 1 ? launch_one<1, 1, GM>(g, q, tiles, s) : launch_one<1, 0, GM>(g, q, tiles, s);
 }
 

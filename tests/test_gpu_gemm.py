@@ -298,6 +298,20 @@ def test_wgrad_llama3_8b_sampled():
 
 
 @pytest.mark.parametrize("M,N,K,out_dtype", [
+    (1100, 700, 4032, torch.bfloat16),    # K % 256 = 192: a last slice of 64 elements
+    (700, 1100, 4064, torch.float32),     # K % 64 = 32: scale rows 254 bytes apart (alternating alignment)
+    (520, 300, 544, torch.bfloat16),      # 5 slices, the last one of 32 elements
+])
+def test_nvfp4_per_slice_scales(M, N, K, out_dtype):
+    """NVFP4 GEMMs whose K is not a multiple of 256 (the per-slice scale-record kernel): scale
+    rows at any even byte alignment, a last K slice that K ends inside.  Every 256-row and
+    256-column band is sampled."""
+    nv_gemm_check(gaussian_bf16((M, K), 1.0, SEED_X + 20), gaussian_bf16((N, K), STD_W, SEED_W + 20),
+                  out_dtype=out_dtype, rows=stratified(M, 7), cols=stratified(N, 8),
+                  label="per-slice scales %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [
     (4352, 4096, 768, torch.bfloat16),    # 272 tiles: last round split into halves; K / 128 = 6 slices
     (4352, 4160, 512, torch.float32),     # 289 tiles, the last column band 64 wide
     (6144, 4864, 1024, torch.bfloat16),   # 456 tiles: a last round too large to split

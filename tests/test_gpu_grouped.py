@@ -268,12 +268,17 @@ def test_k_grouped_mxfp8_offset_records():
                   offs, M, N, label="mxfp8 offset records")
 
 
-def test_k_grouped_nvfp4_per_group_scales():
+@pytest.mark.parametrize("offs,M,N", [
+    ([0, 256, 288, 288, 800], 288, 160),
+    # groups starting at odd multiples of 32 tokens (scale bytes 2 bytes into a dword), lengths
+    # that end inside a 128-token slice, a 32-token group and one over many slices
+    ([0, 96, 1056, 1088, 2400, 2400, 4064, 4096], 320, 192),
+])
+def test_k_grouped_nvfp4_per_group_scales(offs, M, N):
     """NVFP4 wgrad operands quantized columnwise per group (each group its own tensor scale)
     and laid out along the token dimension."""
     import oracle
-    offs = [0, 256, 288, 288, 800]
-    T, M, N = 800, 288, 160
+    T = offs[-1]
     dy = gaussian_bf16((T, M), 1e-3, 31)
     x = gaussian_bf16((T, N), 1.0, 32)
     G = len(offs) - 1
