@@ -426,12 +426,38 @@ def grouped_figures(step, iters: int):
                                                       mdy["col_scales"], None, mx["col_codes"], mx["col_scales"],
                                                       None, out_dtype=torch.float32, out=dw),
     }
+    # the same wgrad on NVFP4: dY and X quantized columnwise per expert (each expert's tokens
+    # its own tensor scale), codes and scales laid out along all tokens
+    nv = [[bsq.nvfp4_quantize(t[offs_l[g]:offs_l[g + 1]].contiguous(), direction=bsq.COL) for t in (step.dY, step.X)]
+          for g in range(G)]
+    ncat = lambda i, key: torch.cat([q[i][key] for q in nv], dim=1).contiguous()
+    ns = lambda i: torch.cat([q[i]["s_enc"][1:2] for q in nv]).contiguous()
+    na = (ncat(0, "col_codes"), ncat(0, "col_scales"), ns(0))
+    nb = (ncat(1, "col_codes"), ncat(1, "col_scales"), ns(1))
+    del nv
+    launches["wgrad_nvfp4"] = lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_NVFP4, bsq.GROUP_K, offs, *na, *nb,
+                                                                   out_dtype=torch.float32, out=dw)
     out = {"experts": G, "tokens_per_expert": [offs_l[i + 1] - offs_l[i] for i in range(G)]}
     flops = 2.0 * M_TOK * N_OUT * K_IN
     for name, fn in launches.items():
         ms = timed_ms(torch, fn, iters)
         out["grouped_%s_TFLOPs" % name] = round(flops / (ms * 1e-3) / 1e12, 2)
     return out
+
+
+def odd_k_figures(step, iters: int):
+    """Side figure outside the step: the forward NVFP4 GEMM with K = 4032 (the first 4032
+    columns of X and W), whose scale rows are not 16 bytes apart, so that the GEMM takes its
+    per-slice scale path."""
+    bsq, torch = step.bsq, step.torch
+    K = 4032
+    qx = bsq.nvfp4_quantize(step.X[:, :K].contiguous(), direction=bsq.ROW)
+    qw = bsq.nvfp4_quantize(step.W[:, :K].contiguous(), direction=bsq.ROW)
+    y = torch.empty((M_TOK, N_OUT), dtype=torch.bfloat16, device=step.dev)
+    ms = timed_ms(torch, lambda: bsq.blockscaled_gemm(bsq.FMT_NVFP4, qx["row_codes"], qx["row_scales"],
+                                                      qx["s_enc"][0:1], qw["row_codes"], qw["row_scales"],
+                                                      qw["s_enc"][0:1], out=y), iters)
+    return {"shape": [M_TOK, N_OUT, K], "ms": round(ms, 4), "TFLOPs": round(2.0 * M_TOK * N_OUT * K / (ms * 1e-3) / 1e12, 1)}
 
 
 def cpu_baseline(tokens: int):
@@ -547,11 +573,12 @@ def main():
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
     dy_bytes = NVFP4_BYTES_PER_ELT * M_TOK * N_OUT
     peaks = measured_peaks(dev)
-    side = moe = layer = qwen = quant_only = None
+    side = moe = layer = qwen = quant_only = odd_k = None
     if not args.no_side_figures:
         quant_only = quant_only_figures(dev, peaks)
         side = rowscaled_figures(step, max(3, args.steps // 2))
         moe = grouped_figures(step, max(3, args.steps // 2))
+        odd_k = odd_k_figures(step, max(3, args.steps // 2))
         layer = linear_layer_figures(step, max(3, args.steps // 2))
         qwen = qwen3_8b_hybrid_figures(dev, 3, args.mx_row_major)
     tflops = lambda ms: gemm_flops / (ms * 1e-3) / 1e12
@@ -630,6 +657,7 @@ def main():
         "measured_peaks": peaks,
         "quant_only": quant_only,
         "row_scaled": side,
+        "nvfp4_gemm_k4032": odd_k,
         "moe_grouped": moe,
         "nvfp4_linear_layer": layer,
         "qwen3_8b_hybrid": qwen,
