@@ -631,15 +631,30 @@ __device__ __forceinline__ void nvw_words_of(const NvQuadT<TN>& q, NvWordsT<TN>&
     for (int j = 0; j < TN; ++j) w.b[j] = dword_of<S & 3>(q.b[j]);
 }
 
-// The lane's 4 scale bytes (blocks 4kh .. 4kh+3) of slice q (0/1) of a group record.
+// The 16-byte scale records (two slices' bytes) of the wave's fragment rows of a group, one
+// 16-byte read per fragment: 16 lanes read 256 consecutive bytes, which no two of them share
+// a bank in (4-byte reads of one dword of 32 consecutive records put rows r and r + 16 on the
+// same bank: those reads made up nearly all of the kernel's LDS bank-conflict cycles).
 template <int TN>
-__device__ __forceinline__ void nvw_read_scales(const uint8_t* sbuf, int q, int wm, int wn, int frow, int kh,
-                                                uint32_t (&sa)[4], uint32_t (&sb)[TN]) {
+struct NvRecT {
+    uint4 a[4], b[TN];
+};
+
+template <int TN>
+__device__ __forceinline__ void nvw_read_recs(const uint8_t* sbuf, int wm, int wn, int frow, NvRecT<TN>& r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = *(const uint32_t*)(sbuf + (wm + 32 * i + frow) * 16 + 4 * (2 * q + kh));
+    for (int i = 0; i < 4; ++i) r.a[i] = *(const uint4*)(sbuf + (wm + 32 * i + frow) * 16);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-        sb[j] = *(const uint32_t*)(sbuf + GBM * 16 + (wn + 32 * j + frow) * 16 + 4 * (2 * q + kh));
+    for (int j = 0; j < TN; ++j) r.b[j] = *(const uint4*)(sbuf + GBM * 16 + (wn + 32 * j + frow) * 16);
+}
+
+// The lane's 4 scale bytes (blocks 4kh .. 4kh+3) of slice Q (0/1) of the records: dword 2Q + kh.
+template <int Q, int TN>
+__device__ __forceinline__ void nvw_pick_scales(const NvRecT<TN>& r, int kh, uint32_t (&sa)[4], uint32_t (&sb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = kh ? dword_of<2 * Q + 1>(r.a[i]) : dword_of<2 * Q>(r.a[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = kh ? dword_of<2 * Q + 1>(r.b[j]) : dword_of<2 * Q>(r.b[j]);
 }
 
 template <int S, int TN>
@@ -736,8 +751,10 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
     NvQuadT<TN> q0, q1;
     NvWordsT<TN> w;
     NvOpsT<TN> cur, nxt;
+    NvRecT<TN> rec;
     uint32_t sa[4], sb[TN], san[4], sbn[TN];
-    nvw_read_scales<TN>(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
+    nvw_read_recs<TN>(sbuf(0), wm, wn, frow, rec);
+    nvw_pick_scales<0, TN>(rec, kh, sa, sb);
     nvw_read_quad<0, TN>(buf(0), wm, wn, frow, kh, q0);
     nvw_words_of<0, TN>(q0, w);
     nvw_ops<0, TN>(w, sa, sb, cur);
@@ -763,14 +780,18 @@ __device__ __forceinline__ void nvw_main_loop(const GemmArgs& g, int64_t m0, int
             // read after the last slice touches a stale, in-bounds buffer)
             if constexpr (S == 2) nvw_read_quad<1, TN>(cb, wm, wn, frow, kh, q1);
             if constexpr (S == 6) nvw_read_quad<0, TN>(nb, wm, wn, frow, kh, q0);
-            if constexpr (S == 5) nvw_read_scales<TN>(sbuf((kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
+            // an odd slice reads the records of the next group (its own slice's scales are picked)
+            if constexpr (ODD && S == 5) nvw_read_recs<TN>(sbuf((kt + 1) / 2), wm, wn, frow, rec);
             __builtin_amdgcn_sched_barrier(0);
             // dequantize step S+1
             if constexpr (S + 1 < 4) nvw_words_of<S + 1, TN>(q0, w);
             else if constexpr (S + 1 < 8) nvw_words_of<S + 1, TN>(q1, w);
             else nvw_words_of<0, TN>(q0, w);
             if constexpr (S + 1 < 8) nvw_ops<S + 1, TN>(w, sa, sb, nxt);
-            else nvw_ops<0, TN>(w, san, sbn, nxt);
+            else {
+                nvw_pick_scales<ODD ? 0 : 1, TN>(rec, kh, san, sbn);
+                nvw_ops<0, TN>(w, san, sbn, nxt);
+            }
             nvw_mfma<TN>(cur, acc);
             nvw_interleave<TN>();
             __builtin_amdgcn_sched_barrier(0);
@@ -1489,8 +1510,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
     NvQuadT<TN> q0, q1;
     NvWordsT<TN> w;
     NvOpsT<TN> cur, nxt;
+    NvRecT<TN> rec;
     uint32_t sa[4], sb[TN], san[4], sbn[TN];
-    nvw_read_scales<TN>(sbuf(0), 0, wm, wn, frow, kh, sa, sb);
+    nvw_read_recs<TN>(sbuf(0), wm, wn, frow, rec);
+    nvw_pick_scales<0, TN>(rec, kh, sa, sb);
     nvw_read_quad<0, TN>(buf(0), wm, wn, frow, kh, q0);
     nvw_words_of<0, TN>(q0, w);
     nvw_ops<0, TN>(w, sa, sb, cur);
@@ -1526,8 +1549,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
                 if constexpr (ODD && S == 1) nv4_dma_group<NW>(dd, kloc / 2, live, sbuf((gs0 + kd) / 2));
                 if constexpr (S == 2) nvw_read_quad<1, TN>(cb, wm, wn, frow, kh, q1);
                 if constexpr (S == 6 && !LAST) nvw_read_quad<0, TN>(nb, wm, wn, frow, kh, q0);
-                if constexpr (S == 5)
-                    nvw_read_scales<TN>(sbuf((gs0 + kt + 1) / 2), ODD ? 0 : 1, wm, wn, frow, kh, san, sbn);
+                if constexpr (ODD && S == 5) nvw_read_recs<TN>(sbuf((gs0 + kt + 1) / 2), wm, wn, frow, rec);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (S + 1 < 8) {
                     if constexpr (S + 1 < 4) nvw_words_of<S + 1, TN>(q0, w);
@@ -1535,6 +1557,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
                     nvw_ops<S + 1, TN>(w, sa, sb, nxt);
                 } else if constexpr (!LAST) {
                     nvw_words_of<0, TN>(q0, w);
+                    nvw_pick_scales<ODD ? 0 : 1, TN>(rec, kh, san, sbn);
                     nvw_ops<0, TN>(w, san, sbn, nxt);
                 }
                 if constexpr (FIRST && S == 0) nvw_mfma_first<TN>(cur, acc);
@@ -1543,10 +1566,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (S + 1 < 8 || !LAST) cur = nxt;
             });
+            if constexpr (!LAST) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sa[i] = san[i];
+                for (int i = 0; i < 4; ++i) sa[i] = san[i];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) sb[j] = sbn[j];
+                for (int j = 0; j < TN; ++j) sb[j] = sbn[j];
+            }
         };
         using F_ = std::false_type;
         using T_ = std::true_type;
@@ -1561,9 +1586,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
         lds_barrier();   // every wave is done with the stage of the last slice
         nvp_store<OUT_F32, TN>(g, m0, n0, wm, wn, wave, lane, alpha, acc, buf(gs0 + nk - 1));
         // the next tile's first step (its slice 0 landed before the top of this tile's last
-        // slice; sa / sb now hold its scales)
+        // slice, whose step 5 read its first scale records)
         nvw_read_quad<0, TN>(buf(gs0 + nk), wm, wn, frow, kh, q0);
         nvw_words_of<0, TN>(q0, w);
+        nvw_pick_scales<0, TN>(rec, kh, sa, sb);
         nvw_ops<0, TN>(w, sa, sb, cur);
         m0 = m1;
         n0 = n1;
