@@ -71,7 +71,7 @@ QUANT_SOURCES = ("block_scaled_precision_nvfp4_amd/csrc/quantize.hip",
 TRAFFIC = {
     "gemm_fwd_nvfp4": ("profiles/gemm_nvfp4_fwd_llama3_8b_hbm_traffic.md", GEMM_SOURCES),
     "gemm_wgrad_nvfp4": ("profiles/gemm_nvfp4_wgrad_llama3_8b_hbm_traffic.md", GEMM_SOURCES),
-    "quant_dy_col_rht_sr": ("profiles/nvfp4_col_rht_sr_dy_llama3_8b_hbm_traffic.md", QUANT_SOURCES),
+    "quant_dy_hybrid": ("profiles/nvfp4_col_mxfp8_row_dy_llama3_8b_hbm_traffic.md", QUANT_SOURCES),
 }
 
 
@@ -155,8 +155,9 @@ class Step:
         (each pair is a stream barrier, so the throughput loop records only the pairs around
         the two NVFP4 GEMMs):
           q_fwd  NVFP4 rowwise RNE of X and W        g_fwd    forward NVFP4 GEMM
-          q_dy   NVFP4 columnwise RHT + SR of dY      q_xc     the same of X
-          g_wgrad  wgrad NVFP4 GEMM                   q_mx     MXFP8 rowwise dY + requantized W
+          q_dy   dY in one pass: NVFP4 columnwise RHT + SR and MXFP8 rowwise
+          q_xc   NVFP4 columnwise RHT + SR of X       g_wgrad  wgrad NVFP4 GEMM
+          q_mx   MXFP8 columnwise W from its NVFP4 codes
           g_dgrad  dgrad MXFP8 GEMM"""
         bsq, torch = self.bsq, self.torch
         mark = (lambda name: self._ev(name) if name[:-1] in marks else None)
@@ -170,10 +171,13 @@ class Step:
         y = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qx["row_codes"], qx["row_scales"], qx["s_enc"][0:1],
                                  qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], out_dtype=torch.bfloat16)
         mark("g_fwd1")
-        # wgrad
+        # backward operands of dY: NVFP4 columnwise (RHT + SR) for wgrad and MXFP8 rowwise for
+        # dgrad from one pass over dY; MXFP8 codes in the GEMM's slab layout unless the
+        # row-major layout is asked for
+        lay, fmx = (0, bsq.FMT_MXFP8) if self.mx_rows else (bsq.MX_SLAB, bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB)
         mark("q_dy0")
-        qdy = bsq.nvfp4_quantize(self.dY, direction=bsq.COL, rounding=bsq.SR, sr_seed=self.seed, sr_stream=0,
-                                 rht_signs=self.signs, workspace=ws)
+        qdy = bsq.nvfp4_col_mxfp8_row_quantize(self.dY, rounding=bsq.SR, sr_seed=self.seed, sr_stream=0,
+                                               rht_signs=self.signs, mx_slab=not self.mx_rows, workspace=ws)
         mark("q_dy1")
         mark("q_xc0")
         qxc = bsq.nvfp4_quantize(self.X, direction=bsq.COL, rounding=bsq.SR, sr_seed=self.seed, sr_stream=1,
@@ -183,15 +187,12 @@ class Step:
         dw = bsq.blockscaled_gemm(bsq.FMT_NVFP4, qdy["col_codes"], qdy["col_scales"], qdy["s_enc"][1:2],
                                   qxc["col_codes"], qxc["col_scales"], qxc["s_enc"][1:2], out_dtype=torch.float32)
         mark("g_wgrad1")
-        # dgrad (MXFP8 backward operands; W from its rowwise-dequantized NVFP4 value), codes in
-        # the GEMM's slab layout unless the row-major layout is asked for
-        lay, fmx = (0, bsq.FMT_MXFP8) if self.mx_rows else (bsq.MX_SLAB, bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB)
+        # dgrad (MXFP8 operands; W from its rowwise-dequantized NVFP4 value)
         mark("q_mx0")
-        mdy = bsq.mxfp8_quantize(self.dY, direction=bsq.ROW | lay)
         mw = bsq.mxfp8_requantize_nvfp4(qw["row_codes"], qw["row_scales"], qw["s_enc"][0:1], direction=bsq.COL | lay)
         mark("q_mx1")
         mark("g_dgrad0")
-        dx = bsq.blockscaled_gemm(fmx, mdy["row_codes"], mdy["row_scales"], None,
+        dx = bsq.blockscaled_gemm(fmx, qdy["mx_row_codes"], qdy["mx_row_scales"], None,
                                   mw["col_codes"], mw["col_scales"], None, out_dtype=torch.bfloat16)
         mark("g_dgrad1")
         return y, dw, dx
@@ -571,7 +572,8 @@ def main():
     g_dgrad = step.avg_ms("g_dgrad")
     q_fwd, q_dy, q_xc, q_mx = (step.avg_ms(k) for k in ("q_fwd", "q_dy", "q_xc", "q_mx"))
     q_bytes = NVFP4_BYTES_PER_ELT * (M_TOK * K_IN + N_OUT * K_IN)
-    dy_bytes = NVFP4_BYTES_PER_ELT * M_TOK * N_OUT
+    # dY's one-pass cast: dY read once, NVFP4 columnwise and MXFP8 rowwise written
+    dy_bytes = (NVFP4_BYTES_PER_ELT + 1.03125) * M_TOK * N_OUT
     peaks = measured_peaks(dev)
     side = moe = layer = qwen = quant_only = odd_k = None
     if not args.no_side_figures:
@@ -611,11 +613,12 @@ def main():
     # fraction of what two reads + one write allow at 8 TB/s
     two_pass = lambda bpe_write: (2.0 + bpe_write) / (4.0 + bpe_write)
     quant = {
-        "dy_col_rht_sr": roofline_entry(
+        "dy_col_rht_sr_mx_row": roofline_entry(
             "hbm", gbps(dy_bytes, q_dy), HBM_PEAK_GBPS, "GB/s",
-            "nvfp4_amax_rht_kernel<2> + nvfp4_encode_kernel<2,true,true>: NVFP4 columnwise RHT16 + Philox SR of "
-            "dY[16384,14336]", dy_bytes, "quant_dy_col_rht_sr", us=round(q_dy * 1e3, 2),
-            two_pass_bound_frac=round(gbps(dy_bytes, q_dy) / (HBM_PEAK_GBPS * two_pass(0.5625)), 4)),
+            "nvfp4_amax_rht_kernel<2> + nvfp4_encode_kernel<2,true,true,true>: dY[16384,14336] in one encode "
+            "pass, NVFP4 columnwise RHT16 + Philox SR and MXFP8 rowwise", dy_bytes, "quant_dy_hybrid",
+            us=round(q_dy * 1e3, 2),
+            two_pass_bound_frac=round(gbps(dy_bytes, q_dy) / (HBM_PEAK_GBPS * two_pass(0.5625 + 1.03125)), 4)),
         "x_col_rht_sr": roofline_entry(
             "hbm", gbps(NVFP4_BYTES_PER_ELT * M_TOK * K_IN, q_xc), HBM_PEAK_GBPS, "GB/s",
             "NVFP4 columnwise RHT16 + Philox SR of X[16384,4096]", NVFP4_BYTES_PER_ELT * M_TOK * K_IN,
@@ -624,10 +627,10 @@ def main():
             "hbm", gbps(q_bytes, q_fwd), HBM_PEAK_GBPS, "GB/s", "NVFP4 rowwise RNE of X and W (two passes each)",
             q_bytes, us=round(q_fwd * 1e3, 2),
             two_pass_bound_frac=round(gbps(q_bytes, q_fwd) / (HBM_PEAK_GBPS * two_pass(0.5625)), 4)),
-        "mx_dgrad_operands": roofline_entry(
-            "hbm", gbps(M_TOK * N_OUT * 3.03125 + N_OUT * K_IN * (0.5625 + 1.03125), q_mx), HBM_PEAK_GBPS, "GB/s",
-            "MXFP8 rowwise of dY + MXFP8 columnwise of W from its NVFP4 codes (one pass each)",
-            M_TOK * N_OUT * 3.03125 + N_OUT * K_IN * (0.5625 + 1.03125), us=round(q_mx * 1e3, 2)),
+        "mx_w_requant": roofline_entry(
+            "hbm", gbps(N_OUT * K_IN * (0.5625 + 1.03125), q_mx), HBM_PEAK_GBPS, "GB/s",
+            "MXFP8 columnwise of W from its NVFP4 rowwise codes (one pass)",
+            N_OUT * K_IN * (0.5625 + 1.03125), us=round(q_mx * 1e3, 2)),
     }
     if quant_only is not None:
         for name, e in quant_only.items():
@@ -647,8 +650,8 @@ def main():
         "nvfp4_quant_frac": {"of_peak_8TBps": round(gbps(q_bytes, q_fwd) / HBM_PEAK_GBPS, 4),
                              "of_measured_copy": round(gbps(q_bytes, q_fwd) / peaks["copy_GBps"], 4)},
         "nvfp4_gemm_TFLOPs": round(tflops(g_fwd), 2),
-        "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "nvfp4_quant_dy_col": round(q_dy, 4),
-                      "nvfp4_quant_x_col": round(q_xc, 4), "mxfp8_casts_dgrad": round(q_mx, 4),
+        "kernel_ms": {"nvfp4_quant_fwd_XW": round(q_fwd, 4), "dy_nvfp4_col_mxfp8_row": round(q_dy, 4),
+                      "nvfp4_quant_x_col": round(q_xc, 4), "mxfp8_requant_w": round(q_mx, 4),
                       "gemm_fwd_nvfp4": round(g_fwd, 4), "gemm_wgrad_nvfp4": round(g_wgrad, 4),
                       "gemm_dgrad_mxfp8": round(g_dgrad, 4)},
         "mxfp8_gemm_TFLOPs": round(tflops(g_dgrad), 2),

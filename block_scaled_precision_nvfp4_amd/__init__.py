@@ -52,6 +52,8 @@ def lib():
         vp, i64, i32, u32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_noalloc.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_col_mxfp8_row_quantize.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp, i32,
+                                                   vp, vp, vp]
         L.nvfp4_quantize_rowscaled.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp]
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
@@ -66,7 +68,7 @@ def lib():
         L.nvfp4_linear_forward.argtypes = [vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_backward.argtypes = [vp, vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
         for f in ("nvfp4_linear_forward", "nvfp4_linear_backward", "nvfp4_quantize", "nvfp4_quantize_noalloc",
-                  "nvfp4_quantize_rowscaled",
+                  "nvfp4_col_mxfp8_row_quantize", "nvfp4_quantize_rowscaled",
                   "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
                   "blockscaled_gemm", "blockscaled_grouped_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int
@@ -148,6 +150,31 @@ def nvfp4_quantize(x: torch.Tensor, direction: int = ROW, rounding: int = RNE, s
         x.data_ptr(), R, Cc, direction, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg),
         _ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
         _ptr(out.get("col_scales")), out["amax"].data_ptr(), out["s_enc"].data_ptr(), ws.data_ptr(), _stream(dev)))
+    return out
+
+
+def nvfp4_col_mxfp8_row_quantize(x: torch.Tensor, rounding: int = RNE, sr_seed: int = 0, sr_stream: int = 0,
+                                 rht_signs=None, mx_slab: bool = False,
+                                 workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """One pass over a bf16 [rows, cols] device tensor that writes NVFP4 columnwise (as
+    ``nvfp4_quantize(x, COL, ...)``: ``col_codes``, ``col_scales``, ``amax``, ``s_enc``) and
+    MXFP8 rowwise (as ``mxfp8_quantize(x, ROW | (MX_SLAB if mx_slab else 0))``:
+    ``mx_row_codes``, ``mx_row_scales``).  RHT and SR apply to the NVFP4 part only."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    R, Cc = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {"col_codes": torch.empty((Cc, R // 2), **u8), "col_scales": torch.empty((Cc, R // 16), **u8),
+           "amax": torch.empty(2, dtype=torch.float32, device=dev),
+           "s_enc": torch.empty(2, dtype=torch.float32, device=dev),
+           "mx_row_codes": torch.empty((R, Cc), **u8), "mx_row_scales": torch.empty((R, Cc // 32), **u8)}
+    ws = _workspace(workspace, NVFP4_QUANTIZE_WORKSPACE_BYTES, dev)
+    sg = _signs(rht_signs, dev)
+    _check("nvfp4_col_mxfp8_row_quantize", lib().nvfp4_col_mxfp8_row_quantize(
+        x.data_ptr(), R, Cc, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg), out["col_codes"].data_ptr(),
+        out["col_scales"].data_ptr(), out["amax"].data_ptr(), out["s_enc"].data_ptr(), ws.data_ptr(),
+        MX_SLAB if mx_slab else 0, out["mx_row_codes"].data_ptr(), out["mx_row_scales"].data_ptr(),
+        _stream(dev)))
     return out
 
 

@@ -101,6 +101,28 @@ int nvfp4_quantize_noalloc(const void* x, int64_t rows, int64_t cols, int direct
                                                        amax_out, s_enc_out, hip_stream), fn);
 }
 
+int nvfp4_col_mxfp8_row_quantize(const void* x, int64_t rows, int64_t cols, int rounding, uint64_t sr_seed,
+                                 uint32_t sr_stream, const int8_t* rht_signs, uint8_t* col_codes,
+                                 uint8_t* col_scales, float* amax_out, float* s_enc_out, void* workspace,
+                                 int mx_layout, uint8_t* mx_row_codes, uint8_t* mx_row_scales, void* hip_stream) {
+    static const char* fn = "nvfp4_col_mxfp8_row_quantize";
+    if (mx_layout != 0 && mx_layout != BSQ_MX_SLAB)
+        return fail(BSQ_ERR_ARG, "%s: mx_layout must be 0 or BSQ_MX_SLAB, got %d", fn, mx_layout);
+    if (const int st = nvfp4_quantize_check(fn, x, rows, cols, BSQ_COL, rounding, rht_signs, nullptr, nullptr,
+                                            col_codes, col_scales, amax_out, s_enc_out, true, workspace))
+        return st;
+    if (cols % 32 != 0) return fail(BSQ_ERR_SHAPE, "%s: MXFP8 rowwise needs cols %% 32 == 0, got %lld", fn, (long long)cols);
+    if (mx_layout && cols % 64 != 0)
+        return fail(BSQ_ERR_SHAPE, "%s: rowwise slab codes need cols %% 64 == 0, got %lld", fn, (long long)cols);
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty && (!mx_row_codes || !mx_row_scales)) return fail(BSQ_ERR_NULL, "%s: MXFP8 rowwise outputs are NULL", fn);
+    if (misaligned(mx_row_codes)) return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    return launched(bsq::launch_nvfp4_quantize(x, rows, cols, BSQ_COL, rounding, sr_seed, sr_stream, rht_signs, nullptr,
+                                               nullptr, col_codes, col_scales, amax_out, s_enc_out,
+                                               static_cast<float*>(workspace), hip_stream, mx_row_codes,
+                                               mx_row_scales, mx_layout ? 1 : 0), fn);
+}
+
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_enc, int64_t rows, int64_t cols,
                      void* out, void* hip_stream) {
     static const char* fn = "nvfp4_dequantize";

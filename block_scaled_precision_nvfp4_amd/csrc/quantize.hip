@@ -264,6 +264,55 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t
 
 // ------------------------------------------------------------------ NVFP4 encode
 
+// Scale byte of a 32-block with amax m: X = floor(log2 m) - 8 clamped at -127, byte X+127;
+// for a normal binary32 m that is max(exponent_field - 8, 0), and 0 for subnormal or zero m.
+__device__ __forceinline__ uint32_t mx_scale_byte(float m) {
+    const int e = (int)(__float_as_uint(m) >> 23);
+    return (uint32_t)(e > 8 ? e - 8 : 0);
+}
+
+// 2^-X for scale byte b (X = b - 127): binary32 with exponent field 254 - b (b <= 246).
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
+
+// Byte offset of code (r, k) of a [rows][K] code matrix in the slab layout: rows in bands of
+// 256 (the last band holds the rest), band b at byte 256 b K, holding its n rows as K/64
+// consecutive slabs of n x 64 bytes (K a multiple of 64).  A GEMM tile's rows are one band,
+// and each 64-element K slice of them one contiguous block.
+__device__ __forceinline__ int64_t slab_offset(int64_t r, int64_t k, int64_t rows, int64_t K) {
+    const int64_t b = r >> 8, left = rows - (b << 8), n = left < 256 ? left : 256;
+    return (b << 8) * K + (k >> 6) * n * 64 + (r & 255) * 64 + (k & 63);
+}
+
+// MXFP8 rowwise cast of a thread's 16 x 8 sub-tile: 32-blocks along the row span the 4
+// lanes cc .. cc+3; codes (8 bytes per row) go to the row-major or slab-layout code matrix and
+// each block's scale byte to its row of the scale matrix.
+__device__ __forceinline__ void mx_row_tile(const SubTile& q, const TileCoord& t, int64_t R, int64_t C,
+                                            uint8_t* row_codes, uint8_t* row_scales, int slab) {
+    const bool colok = t.c0 < C;
+    static_for<0, 16>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        const int64_t r = t.r0 + j;
+        float v[8];
+        row_of(q, j, v);
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+        m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+        m = __builtin_fmaxf(m, __shfl_xor(m, 2));
+        uint32_t lo = 0, hi = 0, sb = 0;
+        if (m != 0.0f) {
+            sb = mx_scale_byte(m);
+            const float inv = mx_inv_scale(sb);
+            lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        }
+        if (colok && r < R) {
+            *(uint2*)(row_codes + (slab ? slab_offset(r, t.c0, R, C) : r * C + t.c0)) = make_uint2(lo, hi);
+            if ((t.cc & 3) == 0) row_scales[r * (C / 32) + t.c0 / 32] = (uint8_t)sb;
+        }
+    });
+}
+
 struct NvEncodeArgs {
     const uint16_t* x;
     int64_t R, C;
@@ -278,6 +327,9 @@ struct NvEncodeArgs {
     float* s_enc_out;
     uint64_t seed;
     uint32_t stream;
+    uint8_t* mx_codes;    // MXFP8 rowwise output of the same input (hybrid calls; else unused)
+    uint8_t* mx_scales;
+    int mx_slab;
 };
 
 // The encode multiplier S / fp32(s_b) of every nonzero scale code s_b (codes 1..126) for tensor
@@ -372,12 +424,16 @@ __device__ __forceinline__ void store_col_scales(const uint8_t* sc, uint8_t* out
     }
 }
 
-template <int DIRS, bool RHT, bool SR>
+// MXROW: also the MXFP8 rowwise cast of the same tile (from the untransformed values), so that
+// the per-direction recipe's backward operand (MXFP8 rowwise, NVFP4 columnwise) reads its
+// input once.
+template <int DIRS, bool RHT, bool SR, bool MXROW = false>
 __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) {
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
     SubTile q;
     load_subtile(a.x, R, C, t, q);
+    if constexpr (MXROW) mx_row_tile(q, t, R, C, a.mx_codes, a.mx_scales, a.mx_slab);
     const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
     const float2 am = parts_max<NTHREADS, DIRS>(a.parts, a.nparts);
     const float Srow = nvfp4_tensor_scale(am.x);
@@ -465,15 +521,6 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
 
 // ------------------------------------------------------------------ MXFP8 cast
 
-// Scale byte of a 32-block with amax m: X = floor(log2 m) - 8 clamped at -127, byte X+127;
-// for a normal binary32 m that is max(exponent_field - 8, 0), and 0 for subnormal or zero m.
-__device__ __forceinline__ uint32_t mx_scale_byte(float m) {
-    const int e = (int)(__float_as_uint(m) >> 23);
-    return (uint32_t)(e > 8 ? e - 8 : 0);
-}
-
-// 2^-X for scale byte b (X = b - 127): binary32 with exponent field 254 - b (b <= 246).
-__device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
 
 // bf16 bits of the dequantized NVFP4 element with code c (4 bits) in a block with scale value
 // sc: bf16_RNE((E2M1(c) * sc) / S).  The product is exact; one rounded division, then RNE.
@@ -544,14 +591,6 @@ struct MxArgs {
     int slab;   // codes in the slab layout (see slab_offset)
 };
 
-// Byte offset of code (r, k) of a [rows][K] code matrix in the slab layout: rows in bands of
-// 256 (the last band holds the rest), band b at byte 256 b K, holding its n rows as K/64
-// consecutive slabs of n x 64 bytes (K a multiple of 64).  A GEMM tile's rows are one band,
-// and each 64-element K slice of them one contiguous block.
-__device__ __forceinline__ int64_t slab_offset(int64_t r, int64_t k, int64_t rows, int64_t K) {
-    const int64_t b = r >> 8, left = rows - (b << 8), n = left < 256 ? left : 256;
-    return (b << 8) * K + (k >> 6) * n * 64 + (r & 255) * 64 + (k & 63);
-}
 
 // SRC 0: bf16 input; SRC 1: the rowwise-dequantized value of an NVFP4 tensor.
 template <int DIRS, int SRC = 0>
@@ -561,32 +600,8 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
     SubTile q;
     if constexpr (SRC == 0) load_subtile(a.x, R, C, t, q);
     else load_subtile_nvfp4(a.nv_codes, a.nv_scales, a.nv_s_enc[0], R, C, t, q);
-    const bool colok = t.c0 < C;
 
-    if (DIRS & 1) {
-        static_for<0, 16>([&](auto j_c) {
-            constexpr int j = decltype(j_c)::value;
-            const int64_t r = t.r0 + j;
-            float v[8];
-            row_of(q, j, v);
-            float m = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 2));
-            uint32_t lo = 0, hi = 0, sb = 0;
-            if (m != 0.0f) {
-                sb = mx_scale_byte(m);
-                const float inv = mx_inv_scale(sb);
-                lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-                hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-            }
-            if (colok && r < R) {
-                *(uint2*)(a.row_codes + (a.slab ? slab_offset(r, t.c0, R, C) : r * C + t.c0)) = make_uint2(lo, hi);
-                if ((t.cc & 3) == 0) a.row_scales[r * (C / 32) + t.c0 / 32] = (uint8_t)sb;
-            }
-        });
-    }
+    if (DIRS & 1) mx_row_tile(q, t, R, C, a.row_codes, a.row_scales, a.slab);
 
     if (DIRS & 2) {
         // same placement as the NVFP4 columnwise transpose: block rb of column 8cc + k at
@@ -1040,7 +1055,9 @@ static inline int launch_status() { return (int)hipGetLastError(); }
 
 template <int DIRS, bool RHT, bool SR>
 static int launch_encode_tiles(const NvEncodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR>), tile_grid(a.R, a.C), dim3(NTHREADS), 0, s, a);
+    if (DIRS == 2 && a.mx_codes != nullptr)
+        hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR, true>), tile_grid(a.R, a.C), dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((nvfp4_encode_kernel<DIRS, RHT, SR>), tile_grid(a.R, a.C), dim3(NTHREADS), 0, s, a);
     return launch_status();
 }
 
@@ -1052,7 +1069,7 @@ static int launch_encode_tiles(const NvEncodeArgs& a, bool sr, hipStream_t s) {
 int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
                           uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
                           uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, float* parts,
-                          void* hip_stream) {
+                          void* hip_stream, uint8_t* mx_codes, uint8_t* mx_scales, int mx_slab) {
     hipStream_t s = (hipStream_t)hip_stream;
     if (R == 0 || C == 0) {
         hipLaunchKernelGGL(empty_tensor_scales_kernel, dim3(1), dim3(64), 0, s, amax, s_enc);
@@ -1090,7 +1107,7 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
     }
     // columnwise, alone or with rowwise: the 256 x 128 tile kernels
     const NvEncodeArgs a{(const uint16_t*)x, R, C, signs, row_codes, row_scales, col_codes, col_scales,
-                         parts, nparts, amax, s_enc, seed, stream};
+                         parts, nparts, amax, s_enc, seed, stream, mx_codes, mx_scales, mx_slab};
     if (direction == 2) return rht ? launch_encode_tiles<2, true>(a, sr, s) : launch_encode_tiles<2, false>(a, sr, s);
     return rht ? launch_encode_tiles<3, true>(a, sr, s) : launch_encode_tiles<3, false>(a, sr, s);
 }

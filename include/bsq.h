@@ -140,6 +140,34 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
                    void* hip_stream);
 
 /*
+ * nvfp4_col_mxfp8_row_quantize -- one bf16 tensor quantized to two formats, one per direction,
+ * in one pass over it: NVFP4 columnwise (exactly nvfp4_quantize with direction BSQ_COL) and
+ * MXFP8 rowwise (exactly mxfp8_quantize with direction BSQ_ROW).
+ *
+ * Defines: hybrid (per-direction) quantization, page "[Pytorch][Common] Hybrid quantization"
+ * (Description: rowwise and columnwise operands of one tensor may use different formats).
+ * This pairing serves the backward operand dY in the per-direction recipe of this library:
+ * rowwise MXFP8 for the dgrad GEMM, columnwise NVFP4 (with RHT and SR) for the wgrad GEMM.  The NVFP4 part's
+ * amax pass still reads x; the MXFP8 codes come from the encode pass's read, so x is read twice
+ * in all instead of three times.
+ *
+ * Arguments: x, rows, cols, rounding, sr_seed, sr_stream, rht_signs, col_codes, col_scales,
+ * amax_out, s_enc_out and workspace as for nvfp4_quantize with direction BSQ_COL (rows % 16 ==
+ * 0; amax_out / s_enc_out slots as nvfp4_quantize writes them for BSQ_COL); the RHT and
+ * SR apply to the NVFP4 part only.  mx_layout 0 (row-major codes) or BSQ_MX_SLAB;
+ * mx_row_codes [rows][cols] E4M3 bytes (row-major, or the slab layout, which needs cols % 64
+ * == 0) and mx_row_scales [rows][cols/32] E8M0 bytes as mxfp8_quantize writes them (cols % 32
+ * == 0); required unless the tensor is empty.
+ * Errors: those of nvfp4_quantize and mxfp8_quantize for these arguments; BSQ_ERR_ARG for
+ * another mx_layout.
+ */
+int nvfp4_col_mxfp8_row_quantize(const void* x, int64_t rows, int64_t cols, int rounding,
+                                 uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
+                                 uint8_t* col_codes, uint8_t* col_scales, float* amax_out,
+                                 float* s_enc_out, void* workspace, int mx_layout,
+                                 uint8_t* mx_row_codes, uint8_t* mx_row_scales, void* hip_stream);
+
+/*
  * nvfp4_quantize_noalloc -- nvfp4_quantize without the workspace argument, for callers that
  * cannot allocate device memory or pass scratch: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Arguments, numerics, outputs and errors are those

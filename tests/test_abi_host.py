@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     for f in ["nvfp4_quantize", "nvfp4_quantize_rowscaled", "nvfp4_dequantize", "mxfp8_quantize",
               "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "blockscaled_grouped_gemm",
               "nvfp4_linear_workspace_bytes", "nvfp4_linear_saved_bytes", "nvfp4_linear_forward",
-              "nvfp4_linear_backward", "bsq_last_error", "bsq_version", "nvfp4_quantize_noalloc"]:
+              "nvfp4_linear_backward", "bsq_last_error", "bsq_version", "nvfp4_quantize_noalloc",
+              "nvfp4_col_mxfp8_row_quantize"]:
         assert f in names
 
 
@@ -89,6 +90,37 @@ def test_nvfp4_quantize_workspace_size(L):
     # validation must accept a NULL workspace and NULL outputs: a zero-row columnwise call with
     # misaligned outputs still fails on alignment, proving it got past the NULL checks
     assert q(L, rows=0, rc=None, rs=None, cc=None, cs=None, ws=None, x=FAKE + 8) == 6
+
+
+def hyb(L, x=FAKE, rows=256, cols=256, rounding=1, signs=None, cc=FAKE, cs=FAKE, amax=FAKE, senc=FAKE, ws=FAKE,
+        layout=0, mc=FAKE, ms=FAKE):
+    return L.nvfp4_col_mxfp8_row_quantize(x, rows, cols, rounding, 0, 0, signs, cc, cs, amax, senc, ws, layout,
+                                          mc, ms, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(layout=1), 3, "mx_layout"),
+    (dict(layout=4 | 1), 3, "mx_layout"),
+    (dict(rounding=3), 3, "rounding"),
+    (dict(rows=24), 2, "rows % 16"),
+    (dict(cols=48), 2, "cols % 32"),
+    (dict(cols=96, layout=4), 2, "cols % 64"),
+    (dict(cc=None), 1, "columnwise outputs"),
+    (dict(ws=None), 1, "workspace"),
+    (dict(mc=None), 1, "MXFP8 rowwise outputs"),
+    (dict(ms=None), 1, "MXFP8 rowwise outputs"),
+    (dict(mc=FAKE + 8), 6, "aligned"),
+    (dict(x=FAKE + 8), 6, "aligned"),
+])
+def test_hybrid_quantize_validation(L, kw, status, needle):
+    assert hyb(L, **kw) == status
+    assert needle in last(L)
+
+
+def test_hybrid_quantize_empty_needs_no_outputs(L):
+    # a zero-row call accepts NULL outputs and workspace: misaligned x still fails on alignment,
+    # which proves the call got past the NULL checks without launching anything
+    assert hyb(L, rows=0, cc=None, cs=None, ws=None, mc=None, ms=None, x=FAKE + 8) == 6
 
 
 def test_mxfp8_quantize_validation(L):

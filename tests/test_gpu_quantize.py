@@ -51,6 +51,31 @@ def check_mxfp8(x_cpu, direction, label=""):
             assert_bytes_equal(got[key + "_codes"], ref[key + "_codes"], label + " " + key + "_codes")
 
 
+def check_hybrid(x_cpu, rounding=0, seed=0, stream=0, signs=None, slab=False, label=""):
+    """One-pass NVFP4 columnwise + MXFP8 rowwise against the oracle's two casts of the same
+    input: each half bit-exact to its own format's oracle."""
+    import oracle
+    from tests.gpu_common import from_slab
+    R, Cc = x_cpu.shape
+    note("hybrid %s shape=%s rnd=%d rht=%s slab=%s" % (label, (R, Cc), rounding, signs is not None, slab))
+    got = bsq.nvfp4_col_mxfp8_row_quantize(x_cpu.to(DEV), rounding=rounding, sr_seed=seed, sr_stream=stream,
+                                           rht_signs=signs, mx_slab=slab)
+    torch.cuda.synchronize()
+    ref = oracle.nvfp4_quantize(x_cpu, direction=2, rounding=rounding, sr_seed=seed, sr_stream=stream,
+                                signs=None if signs is None else signs.numpy())
+    assert_f32_equal(got["amax"][1:2], ref["amax"][1:2], label + " amax col")
+    assert_f32_equal(got["s_enc"][1:2], ref["s_enc"][1:2], label + " s_enc col")
+    assert_bytes_equal(got["col_scales"], ref["col_scales"], label + " col_scales")
+    assert_bytes_equal(got["col_codes"], ref["col_codes"], label + " col_codes")
+    del ref
+    mref = oracle.mxfp8_quantize(x_cpu, direction=1)
+    codes = got["mx_row_codes"]
+    if slab:
+        codes = torch.from_numpy(from_slab(codes, R, Cc))
+    assert_bytes_equal(got["mx_row_scales"], mref["row_scales"], label + " mxfp8 row_scales")
+    assert_bytes_equal(codes, mref["row_codes"], label + " mxfp8 row_codes")
+
+
 # ----------------------------------------------------------------- small and ragged
 
 @pytest.mark.parametrize("shape", [(128, 256), (256, 128), (272, 144), (16, 16), (48, 400), (528, 16)])
@@ -107,6 +132,24 @@ def test_nvfp4_zero_and_empty():
     got = bsq.nvfp4_quantize(x, direction=3)
     torch.cuda.synchronize()
     assert got["amax"].cpu().tolist() == [0.0, 0.0] and got["s_enc"].cpu().tolist() == [1.0, 1.0]
+
+
+@pytest.mark.parametrize("shape,slab", [((256, 256), False), ((256, 256), True), ((272, 160), False),
+                                         ((272, 192), True), ((32, 32), False), ((48, 448), True),
+                                         ((528, 64), True)])
+@pytest.mark.parametrize("rounding,use_rht", [(0, False), (1, True), (0, True)])
+def test_hybrid_small(shape, slab, rounding, use_rht):
+    x = outlier_bf16(shape, seed=31, mask_seed=32)
+    check_hybrid(x, rounding=rounding, seed=SEED_SR_KEY, stream=3, signs=rht_signs(SEED_SIGNS) if use_rht else None,
+                 slab=slab, label="small")
+
+
+def test_hybrid_zero_and_empty():
+    check_hybrid(torch.zeros((64, 64), dtype=torch.bfloat16), label="zeros")
+    got = bsq.nvfp4_col_mxfp8_row_quantize(torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV), rounding=1)
+    torch.cuda.synchronize()
+    assert got["amax"][1].item() == 0.0 and got["s_enc"][1].item() == 1.0
+    assert got["mx_row_codes"].shape == (0, 64) and got["col_codes"].shape == (64, 0)
 
 
 def test_calls_share_no_state():
@@ -314,6 +357,13 @@ def test_fwd_operands_llama3_8b():
     """Forward operands of the Llama-3-8B FFN up-projection, NVFP4 rowwise RNE."""
     check_nvfp4(gaussian_bf16((16384, 4096), 1.0, SEED_X), 1, label="fwd X")
     check_nvfp4(gaussian_bf16((14336, 4096), STD_W, SEED_W), 1, label="fwd W")
+
+
+def test_dy_hybrid_llama3_8b():
+    """The backward's dY [16384, 14336] in one pass: NVFP4 columnwise with RHT + SR (stream 0)
+    for wgrad and MXFP8 rowwise in the slab layout for dgrad."""
+    check_hybrid(gaussian_bf16((16384, 14336), STD_DY, SEED_DY), rounding=1, seed=SEED_SR_KEY, stream=0,
+                 signs=rht_signs(SEED_SIGNS), slab=True, label="dY")
 
 
 def test_wgrad_operands_llama3_8b():
