@@ -411,8 +411,12 @@ def grouped_figures(step, iters: int):
         m = bsq.mxfp8_requantize_nvfp4(q["row_codes"], q["row_scales"], q["s_enc"][0:1],
                                        direction=bsq.COL | (0 if step.mx_rows else bsq.MX_SLAB))
         mw_codes[g], mw_scales[g] = m["col_codes"], m["col_scales"]
-    mdy = bsq.mxfp8_quantize(step.dY, direction=bsq.ROW | bsq.COL)
-    mx = bsq.mxfp8_quantize(step.X, direction=bsq.COL)
+    # wgrad operands: columnwise casts over all tokens, slab-layout codes unless the row-major
+    # layout is asked for; dgrad's token operand is M-grouped, so row-major
+    lay = 0 if step.mx_rows else bsq.MX_SLAB
+    mdy = bsq.mxfp8_quantize(step.dY, direction=bsq.ROW)
+    mdy.update(bsq.mxfp8_quantize(step.dY, direction=bsq.COL | lay))
+    mx = bsq.mxfp8_quantize(step.X, direction=bsq.COL | lay)
     fwd_fmt = bsq.FMT_NVFP4 | bsq.FMT_A_ROWSCALED
     y = torch.empty((M_TOK, N_OUT), dtype=torch.bfloat16, device=step.dev)
     dx = torch.empty((M_TOK, K_IN), dtype=torch.bfloat16, device=step.dev)
@@ -423,7 +427,8 @@ def grouped_figures(step, iters: int):
         "dgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8 | (0 if step.mx_rows else bsq.FMT_MX_SLAB_B),
                                                       bsq.GROUP_M, offs, mdy["row_codes"],
                                                       mdy["row_scales"], None, mw_codes, mw_scales, None, out=dx),
-        "wgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8, bsq.GROUP_K, offs, mdy["col_codes"],
+        "wgrad": lambda: bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8 | (0 if step.mx_rows else bsq.FMT_MX_SLAB),
+                                                      bsq.GROUP_K, offs, mdy["col_codes"],
                                                       mdy["col_scales"], None, mx["col_codes"], mx["col_scales"],
                                                       None, out_dtype=torch.float32, out=dw),
     }

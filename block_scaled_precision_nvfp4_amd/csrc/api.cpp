@@ -249,12 +249,13 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
                              int c_dtype, void* hip_stream) {
     static const char* fn = "blockscaled_grouped_gemm";
     const int a_rows = (fmt & BSQ_FMT_A_ROWSCALED) != 0, b_rows = (fmt & BSQ_FMT_B_ROWSCALED) != 0;
-    const int slab_b = (fmt & BSQ_FMT_MX_SLAB_B) != 0;
+    const int slab = ((fmt & BSQ_FMT_MX_SLAB_A) ? 1 : 0) | ((fmt & BSQ_FMT_MX_SLAB_B) ? 2 : 0);
     const int flags = fmt & (BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED);
-    fmt &= ~(BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED | BSQ_FMT_MX_SLAB_B);
-    if (slab_b && (fmt != BSQ_FMT_MXFP8 || mode != BSQ_GROUP_M))
-        return fail(BSQ_ERR_ARG, "%s: BSQ_FMT_MX_SLAB_B applies to MXFP8 with BSQ_GROUP_M only", fn);
-    if (slab_b && K % 512 != 0) return fail(BSQ_ERR_SHAPE, "%s: slab operands need K %% 512 == 0, got %lld", fn, (long long)K);
+    fmt &= ~(BSQ_FMT_A_ROWSCALED | BSQ_FMT_B_ROWSCALED | BSQ_FMT_MX_SLAB);
+    if (slab && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: the slab flags apply to MXFP8 only", fn);
+    if ((slab & 1) && mode != BSQ_GROUP_K)
+        return fail(BSQ_ERR_ARG, "%s: BSQ_FMT_MX_SLAB_A applies with BSQ_GROUP_K only (M-grouped A is cut by the groups)", fn);
+    if (slab && K % 512 != 0) return fail(BSQ_ERR_SHAPE, "%s: slab operands need K %% 512 == 0, got %lld", fn, (long long)K);
     if (fmt != BSQ_FMT_NVFP4 && fmt != BSQ_FMT_MXFP8) return fail(BSQ_ERR_ARG, "%s: fmt must be 0 (NVFP4) or 1 (MXFP8), optionally with the row-scaled flags, got %d", fn, fmt | flags);
     if (flags && fmt != BSQ_FMT_NVFP4) return fail(BSQ_ERR_ARG, "%s: the row-scaled flags apply to NVFP4 operands only", fn);
     if (mode != BSQ_GROUP_M && mode != BSQ_GROUP_K) return fail(BSQ_ERR_ARG, "%s: mode must be 1 (BSQ_GROUP_M) or 2 (BSQ_GROUP_K), got %d", fn, mode);
@@ -276,7 +277,7 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
         return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     return launched(bsq::launch_blockscaled_grouped_gemm(fmt, mode, groups, offsets, M, N, K, a_codes, a_scales,
                                                          a_s_enc, b_codes, b_scales, b_s_enc, a_rows, b_rows, c,
-                                                         c_dtype, hip_stream, slab_b ? 2 : 0), fn);
+                                                         c_dtype, hip_stream, slab), fn);
 }
 
 }  // extern "C"

@@ -60,6 +60,7 @@ struct GemmArgs {
     int a_rows, b_rows;   // the operand's tensor scale is per row (float[M] / float[N])
     int64_t ld;           // elements between consecutive rows of A and of B (K unless grouped along K)
     int slab;             // MXFP8 codes in the slab layout (K a multiple of 512): bit 0 A, bit 1 B
+    int64_t k0;           // K-grouped: the group's first element along the rows of a slab operand
 };
 
 // FMT 1: MXFP8; FMT 2: NVFP4 with grouped scale records (K a multiple of 256); FMT 3: NVFP4
@@ -154,8 +155,10 @@ struct MxFrag {
 // each slice of the band is one contiguous block that the DMAs read whole (row-major codes
 // come as 64-byte pieces of rows 2 KiB and more apart, which fill LDS at about 60 % of the
 // rate).  The API admits slab operands only where K % 512 == 0, so they always meet the
-// aligned-record conditions.
-constexpr int MX_SLOTS = 0, MX_RECS = 1, MX_OFFRECS = 2, MX_SLAB = 3;
+// aligned-record conditions.  MX_GSLAB is the K-grouped launch with slab operands: a group's
+// K range starts at any multiple of 32, so its scales take offset records and its codes are
+// addressed from the whole band (mx_gslab_codes).
+constexpr int MX_SLOTS = 0, MX_RECS = 1, MX_OFFRECS = 2, MX_SLAB = 3, MX_GSLAB = 4;
 constexpr int MX_CODES = 2 * GBM * ROWB;                  // 32 KiB
 constexpr int MX_STAGE_SLOTS = MX_CODES + 2 * GBM * 2 * 4;  // 36 KiB
 constexpr int MX_GROUP = 8;                                // slices per grouped scale record
@@ -218,6 +221,7 @@ struct MxDma {
     uint32_t rowbytes, sstride;   // code and scale bytes between consecutive rows
     uint32_t kbytes, kblocks;     // code and scale bytes of a row's K elements
     uint32_t slab_a, slab_b;      // slab layout: bytes of one slice of the tile's A / B rows
+    uint32_t gslab, gchunk;       // K-grouped slab operands: slab and chunk of the group's first element
     int wave, lane;
 };
 
@@ -314,6 +318,34 @@ __device__ __forceinline__ void mx_slab_codes(const MxDma& d, uint32_t k, bool l
     else dma_b128(sized(d.o.b, live), lds_addr(buf + GBM * ROWB + r0 * ROWB), off_r, soff);
 }
 
+// Slice k's codes in a K-grouped launch with at least one operand in the slab layout (SL as in
+// mx_slab_codes).  The group starts gchunk 16-byte chunks into slab gslab (gchunk 0 or 2: group
+// boundaries are multiples of 32), so the lane's local chunk c of slice k is chunk
+// (gchunk + c) % 4 of slab gslab + k + (gchunk + c) / 4.  The resource spans the tile's band
+// (n rows, slabs of n x 64 bytes); rows past n and chunks past the group's K are sent out of
+// range, and the whole offset is in the vector offset, which the range check covers.
+template <int P, int SL>
+__device__ __forceinline__ void mx_gslab_codes(const MxDma& d, uint32_t k, bool live, uint8_t* buf) {
+    const int r0 = 64 * P + 16 * d.wave;
+    const int r = r0 + (d.lane >> 2), c = swzd_chunk(r, d.lane & 3);
+    const bool in = live && 64u * k + 16u * (uint32_t)c < d.kbytes;
+    const uint32_t gc = d.gchunk + (uint32_t)c;
+    const uint32_t sl = d.gslab + k + (gc >> 2), within = (uint32_t)r * 64u + 16u * (gc & 3u);
+    const uint32_t off_r = in ? (uint32_t)r * d.rowbytes + 16u * c + 64u * k : OOB;
+    if constexpr (SL & 1) {
+        const uint32_t off = (in && within < d.slab_a) ? sl * d.slab_a + within : OOB;
+        dma_b128(d.o.a, lds_addr(buf + r0 * ROWB), off, 0u);
+    } else {
+        dma_b128(d.o.a, lds_addr(buf + r0 * ROWB), off_r, 0u);
+    }
+    if constexpr (SL & 2) {
+        const uint32_t off = (in && within < d.slab_b) ? sl * d.slab_b + within : OOB;
+        dma_b128(d.o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off, 0u);
+    } else {
+        dma_b128(d.o.b, lds_addr(buf + GBM * ROWB + r0 * ROWB), off_r, 0u);
+    }
+}
+
 // DMA plan of the tile at (m0, n0); its B rows are the first `brows` (GBN, or 128 for the
 // persistent kernel's half tiles) -- the DMAs of B rows past them read nothing and write zeros.
 template <int EPB, int BLK>
@@ -331,6 +363,8 @@ __device__ __forceinline__ MxDma make_dma(const GemmArgs& g, int64_t m0, int64_t
     d.kblocks = (uint32_t)(g.K / BLK);
     d.slab_a = (uint32_t)ra * 64u;
     d.slab_b = (uint32_t)rbn * 64u;
+    d.gslab = (uint32_t)(g.k0 / 64);
+    d.gchunk = (uint32_t)((g.k0 / 16) & 3);
     d.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     d.lane = lane;
     return d;
@@ -362,7 +396,7 @@ __device__ __forceinline__ void mx_read_part(const uint8_t* buf, const uint8_t* 
     if constexpr (MODE == MX_RECS || MODE == MX_SLAB) {
         f.as[P] = sbuf[ra * 16 + 2 * q + kh];
         f.bs[P] = sbuf[GBM * 16 + rb * 16 + 2 * q + kh];
-    } else if constexpr (MODE == MX_OFFRECS) {
+    } else if constexpr (MODE == MX_OFFRECS || MODE == MX_GSLAB) {
         f.as[P] = sp.a[512 * P];
         f.bs[P] = sp.b[512 * P];
     } else {
@@ -405,43 +439,105 @@ __device__ __forceinline__ void mx_mfma_row(const MxFrag& f, floatx16 (&acc)[4][
 // schedule one record later: records 0 and 1 come with the first slices, record G+2 is
 // fetched during slice 8G+1 into the buffer of record G-1 (last read for slice 8G-1) and is
 // first read for slice 8G+8.
-template <int MODE, int SL = 0>
-__device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
-                                             int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
-    constexpr bool REC = MODE != MX_SLOTS;
-    constexpr bool ALIGNED = MODE == MX_RECS || MODE == MX_SLAB;   // aligned records, nk % MX_GROUP == 0
-    constexpr int DC = 8;                    // code DMAs per slice per lane
-    constexpr int DS = REC ? 0 : 4;          // per-slice scale DMAs
-    constexpr int DG = 2;                    // scale-record DMAs (every MX_GROUP slices)
-    constexpr int STRIDE = REC ? MX_CODES : MX_STAGE_SLOTS;
-    if (nk <= 0) return;
-    MxDma d = make_dma<1, 32>(g, m0, n0, lane);
-    auto buf = [&](int64_t k) { return lds + (int)(k & 3) * STRIDE; };
-    auto sbuf = [&](int64_t grp) { return lds + 4 * MX_CODES + (int)(grp & 1) * MX_SREC; };
-    auto rbuf = [&](int j3) { return lds + 4 * MX_CODES + j3 * MX_SREC; };   // offset record j, j3 = j mod 3
-    const int nk32 = (int)nk;   // nk <= 2^17 (K <= 2^23)
-    const int kbl = (int)d.kblocks;
+template <int MODE>
+struct MxLds {
+    static constexpr bool REC = MODE != MX_SLOTS;
+    static constexpr int STRIDE = REC ? MX_CODES : MX_STAGE_SLOTS;
+    static __device__ __forceinline__ uint8_t* buf(uint8_t* lds, int64_t k) { return lds + (int)(k & 3) * STRIDE; }
+    static __device__ __forceinline__ uint8_t* sbuf(uint8_t* lds, int64_t grp) {
+        return lds + 4 * MX_CODES + (int)(grp & 1) * MX_SREC;
+    }
+    // offset record j, j3 = j mod 3
+    static __device__ __forceinline__ uint8_t* rbuf(uint8_t* lds, int j3) { return lds + 4 * MX_CODES + j3 * MX_SREC; }
+};
 
+// A tile's DMA plan and, for offset records, where its scale bytes sit in their records.
+struct MxPlan {
+    MxDma d;
+    int dla, dlb;         // offset records: bytes into its first record where every A / B row starts
+    uint32_t offa, offb;  // offset records: the lane's row offset from the resource base
+    int nk32, kbl;        // slices; K-blocks (scale bytes) per row
+};
+
+template <int MODE>
+__device__ __forceinline__ MxPlan mx_plan(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, int lane) {
+    MxPlan p;
+    p.d = make_dma<1, 32>(g, m0, n0, lane);
+    p.nk32 = (int)nk;   // nk <= 2^17 (K <= 2^23)
+    p.kbl = (int)p.d.kblocks;
+    p.dla = p.dlb = 0;
+    p.offa = p.offb = OOB;
     // Offset records: the resources span the aligned records that hold the tile's scale bytes,
     // from the one holding its first byte through the one holding its last (whole records:
     // the range check drops a dword that reaches past the range; the bytes past the tensor's
     // end share the last byte's 16 aligned bytes, so its page).  Every row of an operand
     // starts dl bytes into its first record.
-    int dla = 0, dlb = 0;
-    uint32_t offa = OOB, offb = OOB;
-    if constexpr (MODE == MX_OFFRECS) {
+    if constexpr (MODE == MX_OFFRECS || MODE == MX_GSLAB) {
         const int64_t sb = g.ld / 32;
         const int64_t ra = tile_rows(g.M - m0, GBM), rbn = tile_rows(g.N - n0, GBN);
         const uint8_t* pa = g.a_scales + m0 * sb;
         const uint8_t* pb = g.b_scales + n0 * sb;
-        dla = (int)((uintptr_t)pa & 15);
-        dlb = (int)((uintptr_t)pb & 15);
-        d.o.as = rsrc_words(pa - dla, (dla + (ra - 1) * sb + kbl + 15) & ~(int64_t)15);
-        d.o.bs = rsrc_words(pb - dlb, (dlb + (rbn - 1) * sb + kbl + 15) & ~(int64_t)15);
-        const int row = 64 * d.wave + lane;
-        offa = row < ra ? (uint32_t)(row * sb) : OOB;
-        offb = row < rbn ? (uint32_t)(row * sb) : OOB;
+        p.dla = (int)((uintptr_t)pa & 15);
+        p.dlb = (int)((uintptr_t)pb & 15);
+        p.d.o.as = rsrc_words(pa - p.dla, (p.dla + (ra - 1) * sb + p.kbl + 15) & ~(int64_t)15);
+        p.d.o.bs = rsrc_words(pb - p.dlb, (p.dlb + (rbn - 1) * sb + p.kbl + 15) & ~(int64_t)15);
+        const int row = 64 * p.d.wave + lane;
+        p.offa = row < ra ? (uint32_t)(row * sb) : OOB;
+        p.offb = row < rbn ? (uint32_t)(row * sb) : OOB;
     }
+    return p;
+}
+
+// Slice k's code DMAs, part P (K a multiple of 512 with grouped records: the scalar form).
+template <int MODE, int SL, int P>
+__device__ __forceinline__ void mx_dma_part(const MxDma& d, int64_t k, bool live, uint8_t* b) {
+    if constexpr (MODE == MX_RECS) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
+    else if constexpr (MODE == MX_SLAB) mx_slab_codes<P, SL>(d, (uint32_t)k, live, b);
+    else if constexpr (MODE == MX_GSLAB) mx_gslab_codes<P, SL>(d, (uint32_t)k, live, b);
+    else mx_dma_codes<P>(d, k * 64, live, b);
+}
+
+// All DMAs of slice k (codes, and per-slice scales in the slot layout).
+template <int MODE, int SL>
+__device__ __forceinline__ void mx_dma_slice(const MxPlan& p, int64_t k, uint8_t* lds) {
+    const bool live = (int)k < p.nk32;
+    uint8_t* b = MxLds<MODE>::buf(lds, k);
+    static_for<0, 4>([&](auto p_c) { mx_dma_part<MODE, SL, decltype(p_c)::value>(p.d, k, live, b); });
+    if constexpr (MODE == MX_SLOTS) {
+        mx_dma_slots<0>(p.d, k * 64, live, b);
+        mx_dma_slots<1>(p.d, k * 64, live, b);
+    }
+}
+
+// The DMAs that precede a tile's first slice: its first scale record(s) and slices 0-2.  Per
+// lane: 2 + 24 (grouped records), 4 + 24 (offset records) or 32 (slots) operations, of which
+// slices 1 and 2 (16 or 24) come last.
+template <int MODE, int SL>
+__device__ __forceinline__ void mx_prologue(const MxPlan& p, uint8_t* lds) {
+    if constexpr (MODE == MX_RECS || MODE == MX_SLAB) nv4_dma_group<4>(p.d, 0, true, MxLds<MODE>::sbuf(lds, 0));
+    if constexpr (MODE == MX_OFFRECS || MODE == MX_GSLAB) {
+        mx_dma_offrec(p.d, p.offa, p.offb, 0, true, MxLds<MODE>::rbuf(lds, 0));
+        mx_dma_offrec(p.d, p.offa, p.offb, 1, 16 < 15 + p.kbl, MxLds<MODE>::rbuf(lds, 1));
+    }
+    mx_dma_slice<MODE, SL>(p, 0, lds);
+    mx_dma_slice<MODE, SL>(p, 1, lds);
+    mx_dma_slice<MODE, SL>(p, 2, lds);
+}
+
+template <int MODE, int SL = 0>
+__device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int64_t n0, int64_t nk, uint8_t* lds,
+                                             int wm, int wn, int lane, floatx16 (&acc)[4][MXTN]) {
+    using L = MxLds<MODE>;
+    constexpr bool REC = L::REC;
+    constexpr bool ALIGNED = MODE == MX_RECS || MODE == MX_SLAB;   // aligned records, nk % MX_GROUP == 0
+    constexpr bool OFFR = MODE == MX_OFFRECS || MODE == MX_GSLAB;  // offset records
+    constexpr int DC = 8;                    // code DMAs per slice per lane
+    constexpr int DS = REC ? 0 : 4;          // per-slice scale DMAs
+    constexpr int DG = 2;                    // scale-record DMAs (every MX_GROUP slices)
+    if (nk <= 0) return;
+    const MxPlan pl = mx_plan<MODE>(g, m0, n0, nk, lane);
+    const MxDma& d = pl.d;
+    const int nk32 = pl.nk32, kbl = pl.kbl;
     // The lane's scale bytes of slice q of a group whose first record is in buffer c3: byte
     // dl + 2q + kh of the group's two records (below 32).  Where K ends inside a slice (an odd
     // number of K-blocks) the last slice's second K-block has zero codes but its scale bytes
@@ -450,12 +546,12 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     // scale is NaN.
     const bool hi = lane >= 32;
     const int lrow_a = (wm + (lane & 31)) * 16, lrow_b = GBM * 16 + (wn + (lane & 31)) * 16;
-    const int last_odd = (MODE == MX_OFFRECS && (kbl & 1)) ? nk32 - 1 : -1;
+    const int last_odd = (OFFR && (kbl & 1)) ? nk32 - 1 : -1;
     auto rec_ptrs = [&](int c3, int q, int64_t k) {
-        const uint8_t* cur = rbuf(c3);
-        const uint8_t* nxt = rbuf(c3 == 2 ? 0 : c3 + 1);
+        const uint8_t* cur = L::rbuf(lds, c3);
+        const uint8_t* nxt = L::rbuf(lds, c3 == 2 ? 0 : c3 + 1);
         auto at = [&](int t) { return t < 16 ? cur + t : nxt + (t - 16); };
-        const int ta = dla + 2 * q, tb = dlb + 2 * q, up = (int)k == last_odd ? 0 : 1;
+        const int ta = pl.dla + 2 * q, tb = pl.dlb + 2 * q, up = (int)k == last_odd ? 0 : 1;
         MxSPtr sp;
         sp.a = (hi ? at(ta + up) : at(ta)) + lrow_a;
         sp.b = (hi ? at(tb + up) : at(tb)) + lrow_b;
@@ -463,35 +559,12 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
     };
     int g3 = 0;   // offset records: the current group's index mod 3
 
-    // slice k's code DMAs, part P (K a multiple of 512 with grouped records: the scalar form)
-    auto dma_part = [&](auto p_c, int64_t k, bool live, uint8_t* b) {
-        constexpr int P = decltype(p_c)::value;
-        if constexpr (MODE == MX_RECS) nv4_dma_codes<P, 4>(d, 64u * (uint32_t)k, live, b);
-        else if constexpr (MODE == MX_SLAB) mx_slab_codes<P, SL>(d, (uint32_t)k, live, b);
-        else mx_dma_codes<P>(d, k * 64, live, b);
-    };
-    auto dma_slice = [&](int64_t k) {
-        const bool live = (int)k < nk32;
-        uint8_t* b = buf(k);
-        static_for<0, 4>([&](auto p_c) { dma_part(p_c, k, live, b); });
-        if constexpr (!REC) {
-            mx_dma_slots<0>(d, k * 64, live, b);
-            mx_dma_slots<1>(d, k * 64, live, b);
-        }
-    };
-    if constexpr (ALIGNED) nv4_dma_group<4>(d, 0, true, sbuf(0));
-    if constexpr (MODE == MX_OFFRECS) {
-        mx_dma_offrec(d, offa, offb, 0, true, rbuf(0));
-        mx_dma_offrec(d, offa, offb, 1, 16 < 15 + kbl, rbuf(1));
-    }
-    dma_slice(0);
-    dma_slice(1);
-    dma_slice(2);
+    mx_prologue<MODE, SL>(pl, lds);
     wait_vm_barrier<2 * (DC + DS)>();
     MxFrag f0, f1;
     MxSPtr sp0{nullptr, nullptr};
-    if constexpr (MODE == MX_OFFRECS) sp0 = rec_ptrs(0, 0, 0);
-    mx_read<MODE>(buf(0), sbuf(0), 0, sp0, wm, wn, lane, f0);
+    if constexpr (OFFR) sp0 = rec_ptrs(0, 0, 0);
+    mx_read<MODE>(L::buf(lds, 0), L::sbuf(lds, 0), 0, sp0, wm, wn, lane, f0);
 
     // One slice.  Grouped records: Q = kt mod MX_GROUP (the loop is unrolled by MX_GROUP).
     // Offset records: the slice's place in its group is a run-time value, so that one loop
@@ -500,7 +573,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
         constexpr int Q = decltype(q_c)::value;
         [[maybe_unused]] const int qr = (int)(kt & (MX_GROUP - 1));   // offset records
         [[maybe_unused]] const int g3n = g3 == 2 ? 0 : g3 + 1;
-        if constexpr (MODE == MX_OFFRECS) {
+        if constexpr (OFFR) {
             if (qr == 2) wait_vm_barrier<DC + DG>();   // slice kt-1 also issued a record
             else wait_vm_barrier<DC>();
         } else if constexpr (REC && Q == 2) {
@@ -510,25 +583,25 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
         }
         const int64_t kd = kt + 3;
         const bool live = (int)kd < nk32;
-        uint8_t* db = buf(kd);
+        uint8_t* db = L::buf(lds, kd);
         const int64_t kn = kt + 1;                   // fragments read for the next slice
-        const uint8_t* nb = buf(kn);
-        const uint8_t* ns = sbuf(kn / MX_GROUP);
+        const uint8_t* nb = L::buf(lds, kn);
+        const uint8_t* ns = L::sbuf(lds, kn / MX_GROUP);
         const int qn = REC ? (Q + 1) % MX_GROUP : 0;
         MxSPtr spn{nullptr, nullptr};
-        if constexpr (MODE == MX_OFFRECS) spn = rec_ptrs(qr == MX_GROUP - 1 ? g3n : g3, (qr + 1) & (MX_GROUP - 1), kn);
+        if constexpr (OFFR) spn = rec_ptrs(qr == MX_GROUP - 1 ? g3n : g3, (qr + 1) & (MX_GROUP - 1), kn);
         static_for<0, 4>([&](auto p_c) {
             constexpr int P = decltype(p_c)::value;
-            dma_part(p_c, kd, live, db);
+            mx_dma_part<MODE, SL, P>(d, kd, live, db);
             if constexpr (!REC && P < 2) mx_dma_slots<P>(d, kd * 64, live, db);
             if constexpr (ALIGNED && Q == 1 && P == 0) {
                 const int grp = (int)(kt / MX_GROUP) + 1;
-                nv4_dma_group<4>(d, (uint32_t)grp, grp * MX_GROUP < nk32, sbuf(grp));
+                nv4_dma_group<4>(d, (uint32_t)grp, grp * MX_GROUP < nk32, L::sbuf(lds, grp));
             }
-            if constexpr (MODE == MX_OFFRECS && P == 0) {
+            if constexpr (OFFR && P == 0) {
                 if (qr == 1) {
                     const int j = (int)(kt / MX_GROUP) + 2;
-                    mx_dma_offrec(d, offa, offb, (uint32_t)j, 16 * j < 15 + kbl, rbuf(g3 == 0 ? 2 : g3 - 1));
+                    mx_dma_offrec(d, pl.offa, pl.offb, (uint32_t)j, 16 * j < 15 + kbl, L::rbuf(lds, g3 == 0 ? 2 : g3 - 1));
                 }
             }
             mx_mfma_row<P>(fc, acc);
@@ -543,7 +616,7 @@ __device__ __forceinline__ void mx_main_loop(const GemmArgs& g, int64_t m0, int6
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
-        if constexpr (MODE == MX_OFFRECS) g3 = qr == MX_GROUP - 1 ? g3n : g3;
+        if constexpr (OFFR) g3 = qr == MX_GROUP - 1 ? g3n : g3;
     };
     using Q0 = std::integral_constant<int, 0>;
     using Q1 = std::integral_constant<int, 1>;
@@ -1211,6 +1284,30 @@ __device__ __forceinline__ bool group_of_m(const GroupArgs& q, int64_t nbn, int6
     return found >= 0;
 }
 
+// The GEMM of K-group grp folded into g: its K range, operand and output bases and tensor
+// scales.
+template <int FMT, int OUT_F32>
+__device__ __forceinline__ void k_group_args(GemmArgs& g, const GroupArgs& q, int64_t grp) {
+    using F = Fmt<FMT>;
+    constexpr int ES = OUT_F32 ? 4 : 2;
+    int64_t o0, o1;
+    group_bounds(q, grp, o0, o1);
+    if (o0 % 32 != 0 || (o1 - o0) % 32 != 0) o1 = o0 = 0;
+    g.K = o1 - o0;
+    // a slab operand's group is addressed from its band (mx_gslab_codes); a row-major one
+    // from the group's first code byte of each row
+    if (!(g.slab & 1)) g.a_codes += o0 / F::EPB;
+    if (!(g.slab & 2)) g.b_codes += o0 / F::EPB;
+    g.k0 = o0;
+    g.a_scales += o0 / F::BLK;
+    g.b_scales += o0 / F::BLK;
+    g.c = (uint8_t*)g.c + grp * g.M * g.N * ES;
+    if constexpr (F::NV) {
+        g.a_s_enc += grp;
+        g.b_s_enc += grp;
+    }
+}
+
 // Fold group bookkeeping into g; bid becomes the workgroup's index within its group's tiles.
 // Returns false for a workgroup with no tile.
 template <int FMT, int OUT_F32, int GM>
@@ -1239,23 +1336,14 @@ __device__ __forceinline__ bool enter_group(GemmArgs& g, const GroupArgs& q, int
         grp = bid / share;
         local = bid - grp * share;
         if (grp >= q.groups) return false;
-        group_bounds(q, grp, o0, o1);
-        if (o0 % 32 != 0 || (o1 - o0) % 32 != 0) o1 = o0 = 0;
-        g.K = o1 - o0;
-        g.a_codes += o0 / F::EPB;
-        g.a_scales += o0 / F::BLK;
-        g.b_codes += o0 / F::EPB;
-        g.b_scales += o0 / F::BLK;
-        g.c = (uint8_t*)g.c + grp * g.M * g.N * ES;
-        if constexpr (F::NV) {
-            g.a_s_enc += grp;
-            g.b_s_enc += grp;
-        }
+        k_group_args<FMT, OUT_F32>(g, q, grp);
     }
     bid = local;
     return bid < ((g.M + GBM - 1) / GBM) * nbn;
 }
 
+// One output tile per workgroup.  GM 0: a plain launch; 1: M-grouped; 2: K-grouped; 3:
+// K-grouped MXFP8 with slab-layout operands.
 template <int FMT, int OUT_F32, int GM>
 __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, GroupArgs q) {
     using F = Fmt<FMT>;
@@ -1299,7 +1387,15 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
         const bool rows16 = (g.ld / 32) % 16 == 0;
         const bool recs = rows16 && g.K % (MX_GROUP * 64) == 0 &&
                           (((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) == 0;
-        if (recs && g.slab == 3) mx_main_loop<MX_SLAB, 3>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        if constexpr (GM == 3) {
+            // K-grouped slab operands (a kernel of its own: with the other main loops in one
+            // function the register allocation spills): group starts are multiples of 32, not
+            // of a slice, so offset records for the scales (their rows are 16 bytes apart: the
+            // API asks for K % 512 == 0 here) and band-wide addressing for the codes
+            if (g.slab == 3) mx_main_loop<MX_GSLAB, 3>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+            else if (g.slab == 2) mx_main_loop<MX_GSLAB, 2>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+            else mx_main_loop<MX_GSLAB, 1>(g, m0, n0, nk, lds, wm, wn, lane, acc);
+        } else if (recs && g.slab == 3) mx_main_loop<MX_SLAB, 3>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (recs && g.slab == 2) mx_main_loop<MX_SLAB, 2>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (recs && g.slab == 1) mx_main_loop<MX_SLAB, 1>(g, m0, n0, nk, lds, wm, wn, lane, acc);
         else if (recs) mx_main_loop<MX_RECS>(g, m0, n0, nk, lds, wm, wn, lane, acc);
@@ -1635,14 +1731,15 @@ static int launch_one(const GemmArgs& g, const GroupArgs& q, int64_t tiles, hipS
     return (int)hipGetLastError();
 }
 
-// Slab-layout MXFP8 codes are read only by the aligned-record main loop; any other scale path
-// would address them as row-major.  The C ABI admits slab operands only where that loop
-// applies; this check keeps every launch path to the same rule.
+// Slab-layout MXFP8 codes are read only by the aligned-record main loop and, in K-grouped
+// launches, by the offset-record loop with band-wide code addressing; any other path would
+// address them as row-major.  The C ABI admits slab operands only where those loops apply;
+// this check keeps every launch path to the same rule.
 static bool slab_ok(const GemmArgs& g, int fmt, int mode) {
     if (g.slab == 0) return true;
     if (fmt != 1 || g.K % (MX_GROUP * 64) != 0) return false;
     if ((((uintptr_t)g.a_scales | (uintptr_t)g.b_scales) % 16) != 0) return false;
-    if (mode == 2) return false;                    // K-grouped: group starts are not aligned records
+    if (mode == 2) return (int64_t)GBM * g.K <= 0x7FFFFFFF;   // K-grouped: a band within one resource
     if (mode == 1 && (g.slab & 1)) return false;    // M-grouped: group bands cut the token operand
     return true;
 }
@@ -1722,6 +1819,8 @@ int launch_blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int
     const int64_t tiles = grouped_gemm_workgroups(mode, groups, M, N);
     hipStream_t s = (hipStream_t)hip_stream;
     if (mode == 1) return launch_fmt<1>(fmt, c_dtype, g, q, tiles, s);
+    if (g.slab != 0)   // MXFP8 (slab_ok): the K-grouped kernel for slab-layout operands
+        return c_dtype == 1 ? launch_one<1, 1, 3>(g, q, tiles, s) : launch_one<1, 0, 3>(g, q, tiles, s);
     return launch_fmt<2>(fmt, c_dtype, g, q, tiles, s);
 }
 

@@ -293,8 +293,10 @@ int rht_apply(const void* x, int64_t rows, int64_t cols, int axis, const int8_t*
  *   fmt BSQ_FMT_MXFP8 | BSQ_FMT_MX_SLAB_A and/or BSQ_FMT_MX_SLAB_B (BSQ_FMT_MX_SLAB: both):
  *       that operand's codes are in the slab layout (as an MXFP8 cast with BSQ_MX_SLAB
  *       writes them), scales as for BSQ_FMT_MXFP8; K % 512 == 0, else BSQ_ERR_SHAPE.
- *       blockscaled_grouped_gemm accepts BSQ_FMT_MX_SLAB_B with BSQ_GROUP_M only, B being
- *       G slab-layout matrices [N][K] one after the other.
+ *       blockscaled_grouped_gemm accepts BSQ_FMT_MX_SLAB_B with BSQ_GROUP_M, B being G
+ *       slab-layout matrices [N][K] one after the other, and either flag with BSQ_GROUP_K,
+ *       where A [M][K] and B [N][K] are whole slab-layout matrices over all groups (K the
+ *       grouped extent, e.g. the columnwise casts of dY and X with BSQ_MX_SLAB).
  *   c [M][N], c_dtype BSQ_OUT_BF16 (RNE) or BSQ_OUT_F32.
  *   M, N >= 0 arbitrary; M, N or K == 0 are valid (K == 0 writes zeros).  K is below 2^24
  *   (NVFP4) or 2^23 (MXFP8), so that a 256-row operand tile stays below 2 GiB.

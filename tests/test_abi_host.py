@@ -205,13 +205,18 @@ def test_gemm_slab_flag_validation(L):
     assert f(1 | 0x40, 0, 128, 512, *args, 0, None) == 0
     assert f(1 | 0xC0, 128, 128, 1056, *args, 0, None) == 2 and "K % 512" in last(L)
     assert f(1 | 0x80, 0, 128, 512, *args, 0, None) == 0
-    # grouped: only B (stacked per-group matrices) may be slab, with BSQ_GROUP_M
+    # grouped: B (stacked per-group matrices) may be slab with BSQ_GROUP_M; A and B (whole
+    # matrices over the grouped extent) with BSQ_GROUP_K; MXFP8 only, K % 512 == 0
     gg_ = L.blockscaled_grouped_gemm
-    assert gg_(1 | 0x40, 1, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3
-    assert gg_(1 | 0x80, 2, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3 and "GROUP_M only" in last(L)
-    assert gg_(0 | 0x80, 1, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3
+    assert gg_(1 | 0x40, 1, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3 and "GROUP_K only" in last(L)
+    assert gg_(1 | 0xC0, 1, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3 and "GROUP_K only" in last(L)
+    assert gg_(0 | 0x80, 1, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3 and "MXFP8 only" in last(L)
+    assert gg_(0 | 0x40, 2, 4, FAKE, 256, 256, 512, *[FAKE] * 7, 0, None) == 3 and "MXFP8 only" in last(L)
     assert gg_(1 | 0x80, 1, 4, FAKE, 256, 256, 1056, *[FAKE] * 7, 0, None) == 2 and "K % 512" in last(L)
+    assert gg_(1 | 0xC0, 2, 4, FAKE, 256, 256, 1056, *[FAKE] * 7, 0, None) == 2 and "K % 512" in last(L)
     assert gg_(1 | 0x80, 1, 4, None, 256, 256, 512, *[FAKE] * 7, 0, None) == 1
+    for fl in (0x40, 0x80, 0xC0):   # accepted: the call gets as far as the NULL offsets
+        assert gg_(1 | fl, 2, 4, None, 256, 256, 512, *[FAKE] * 7, 0, None) == 1 and "offsets" in last(L)
 
 
 def gg(L, fmt=0, mode=1, groups=4, offs=FAKE, M=256, N=256, K=256, ac=FAKE, as_=FAKE, sa=FAKE, bc=FAKE, bs=FAKE,

@@ -328,6 +328,27 @@ def test_persistent_tiles(M, N, K, out_dtype):
                   label="persistent %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K,out_dtype", [
+    (4352, 4104, 512, torch.bfloat16),   # 289 tiles, the last column band 8 wide
+    (4100, 4160, 1024, torch.float32),   # 17 x 17 tiles, a ragged last row band
+])
+def test_mxfp8_ragged_bands_sampled(M, N, K, out_dtype):
+    """MXFP8 launches of more tiles than a 256-CU device has CUs with narrow or ragged last
+    bands (aligned scale records: K a multiple of 512).  Every 256-row and 128-column band is
+    sampled."""
+    mx_gemm_check(gaussian_bf16((M, K), 1.0, SEED_X + 30), gaussian_bf16((N, K), STD_W, SEED_W + 30), 1, 1,
+                  out_dtype=out_dtype, rows=stratified(M, 13), cols=stratified(N, 14, band=128),
+                  label="ragged bands %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mxfp8_slab_ragged_bands_sampled(out_dtype):
+    """Slab-layout MXFP8 codes for a 4352 x 4160 output (289 tiles, ragged last column band),
+    K = 1024."""
+    slab_dgrad_check(4352, 1024, 4160, out_dtype, rows=stratified(4352, 15), cols=stratified(4160, 16, band=128),
+                     label="slab ragged bands")
+
+
 def test_hybrid_qwen3_8b_sampled():
     """Per-direction recipe at the Qwen3-8B FFN shape: NVFP4 rowwise forward GEMM; MXFP8
     dgrad dX = dY W (dY rowwise, W columnwise) and wgrad dW = dY^T X (both columnwise);

@@ -2,10 +2,11 @@
 boundaries read on the device) against the CPU oracle, through the C ABI.
 
 M-grouped (per-expert fprop / dgrad): ragged group sizes including empty groups, rows before
-the first and after the last group (which must stay untouched), K a multiple of 256 (LDS-DMA
-NVFP4 kernel) and not (register-staged kernel), per-group and per-row (row-scaled) NVFP4
+the first and after the last group (which must stay untouched), K a multiple of 256 (NVFP4
+kernel with scale records) and not (per-slice scales), per-group and per-row (row-scaled) NVFP4
 tensor scales, MXFP8, and more than 64 groups (the device-side scan takes several chunks).
-K-grouped (per-expert wgrad): MXFP8 operands quantized columnwise over all tokens, NVFP4
+K-grouped (per-expert wgrad): MXFP8 operands quantized columnwise over all tokens (row-major
+or slab-layout codes, and the full-size mixture-of-experts wgrad sampled), NVFP4
 operands quantized per group, empty and misaligned groups (computed as empty).  Operands
 are quantized on the GPU and by the oracle from the same bf16 inputs and must agree bit for
 bit before the GEMMs are compared (relative Frobenius error <= 2e-3 against the oracle
@@ -191,11 +192,11 @@ def test_m_grouped_many_groups():
     run_m_grouped(bsq.FMT_NVFP4, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, torch.bfloat16, label="100 groups")
 
 
-def run_k_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, label=""):
+def run_k_grouped(fmt, a_gpu, a_ref, b_gpu, b_ref, offs, M, N, label="", layout=0):
     import oracle
-    note("grouped K %s fmt=%d M=%d N=%d groups=%d" % (label, fmt, M, N, len(offs) - 1))
+    note("grouped K %s fmt=%d M=%d N=%d groups=%d layout=%#x" % (label, fmt, M, N, len(offs) - 1, layout))
     o = torch.tensor(offs, dtype=torch.int64, device=DEV)
-    out = bsq.blockscaled_grouped_gemm(fmt, bsq.GROUP_K, o, *a_gpu, *b_gpu, out_dtype=torch.float32)
+    out = bsq.blockscaled_grouped_gemm(fmt | layout, bsq.GROUP_K, o, *a_gpu, *b_gpu, out_dtype=torch.float32)
     torch.cuda.synchronize()
     ref, sabs = oracle.blockscaled_grouped_gemm(fmt, oracle.GROUP_K, offs, *a_ref, *b_ref, with_abs=True)
     got = out.cpu().numpy().astype(np.float64)
@@ -233,12 +234,15 @@ def test_k_grouped_mxfp8_wgrad():
                   offs, M, N, label="mxfp8 wgrad")
 
 
-def test_k_grouped_mxfp8_offset_records():
+@pytest.mark.parametrize("layout", [0, bsq.FMT_MX_SLAB_A, bsq.FMT_MX_SLAB_B, bsq.FMT_MX_SLAB])
+def test_k_grouped_mxfp8_offset_records(layout):
     """K-grouped MXFP8 wgrad whose groups start at many byte offsets inside a 16-byte scale
     record (starts at multiples of 32 tokens), with odd numbers of K-blocks (the last K slice
     half outside the group), one group spanning several 8-slice record groups, and NaN scale
     bytes in the two columns after the last group (a misaligned group, computed as empty),
-    which must not reach the last group's sums."""
+    which must not reach the last group's sums.  With the slab flags the operands' codes come
+    from casts with MX_SLAB (groups starting half-way into a 64-token slab take its second
+    half and the next slab's first; ragged last bands: M = 320, N = 192)."""
     import oracle
     kblocks = [3, 17, 1, 37, 5, 2, 41]
     offs = [0]
@@ -249,13 +253,16 @@ def test_k_grouped_mxfp8_offset_records():
     T, M, N = 4096, 320, 192
     dy = gaussian_bf16((T, M), 1e-3, 81)
     x = outlier_bf16((T, N), seed=82, mask_seed=83)
-    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.COL)
-    qb = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.COL)
+    slab_a = bsq.MX_SLAB if layout & bsq.FMT_MX_SLAB_A else 0
+    slab_b = bsq.MX_SLAB if layout & bsq.FMT_MX_SLAB_B else 0
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.COL | slab_a)
+    qb = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.COL | slab_b)
     ra = oracle.mxfp8_quantize(dy, direction=oracle.COL)
     rb = oracle.mxfp8_quantize(x, direction=oracle.COL)
     torch.cuda.synchronize()
-    for q, r, nm in ((qa, ra, "dY"), (qb, rb, "X")):
-        assert_bytes_equal(q["col_codes"], r["col_codes"], nm + " col codes")
+    for q, r, nm, sl, rows in ((qa, ra, "dY", slab_a, M), (qb, rb, "X", slab_b, N)):
+        codes = torch.from_numpy(from_slab(q["col_codes"], rows, T)) if sl else q["col_codes"]
+        assert_bytes_equal(codes, r["col_codes"], nm + " col codes")
         assert_bytes_equal(q["col_scales"], r["col_scales"], nm + " col scales")
     nan_cols = slice(end // 32, end // 32 + 2)
     for t in (qa["col_scales"], qb["col_scales"]):
@@ -265,7 +272,40 @@ def test_k_grouped_mxfp8_offset_records():
         r["col_scales"][:, nan_cols] = 255
     run_k_grouped(bsq.FMT_MXFP8, (qa["col_codes"], qa["col_scales"], None), (ra["col_codes"], ra["col_scales"], None),
                   (qb["col_codes"], qb["col_scales"], None), (rb["col_codes"], rb["col_scales"], None),
-                  offs, M, N, label="mxfp8 offset records")
+                  offs, M, N, label="mxfp8 offset records", layout=layout)
+
+
+@pytest.mark.parametrize("layout", [0, bsq.FMT_MX_SLAB, bsq.FMT_MX_SLAB_B])
+def test_k_grouped_mxfp8_many_groups(layout):
+    """40 groups of a [520, 264] wgrad output (3 x 2 tiles, ragged in both dimensions; 320
+    workgroups with the padding to 8 per group): group lengths at random multiples of 32
+    including empty groups and one that is not a multiple of 32 (it and the next group are
+    computed as empty), on row-major, both-slab or B-only slab codes."""
+    import oracle
+    rng = np.random.default_rng(91)
+    sizes = list(rng.integers(0, 7, 40) * 32)
+    sizes[5] = 0
+    sizes[17] = 48   # misaligned: this group and the next (which realigns) are empty
+    sizes[18] = 80
+    offs = splits_to_offsets(0, sizes)
+    T = 4096
+    assert offs[-1] <= T
+    M, N = 520, 264
+    dy = gaussian_bf16((T, M), 1e-3, 92)
+    x = outlier_bf16((T, N), seed=93, mask_seed=94)
+    slab_a = bsq.MX_SLAB if layout & bsq.FMT_MX_SLAB_A else 0
+    slab_b = bsq.MX_SLAB if layout & bsq.FMT_MX_SLAB_B else 0
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.COL | slab_a)
+    qb = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.COL | slab_b)
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.COL)
+    rb = oracle.mxfp8_quantize(x, direction=oracle.COL)
+    torch.cuda.synchronize()
+    for q, r, nm, sl, rows in ((qa, ra, "dY", slab_a, M), (qb, rb, "X", slab_b, N)):
+        codes = torch.from_numpy(from_slab(q["col_codes"], rows, T)) if sl else q["col_codes"]
+        assert_bytes_equal(codes, r["col_codes"], nm + " col codes")
+    run_k_grouped(bsq.FMT_MXFP8, (qa["col_codes"], qa["col_scales"], None), (ra["col_codes"], ra["col_scales"], None),
+                  (qb["col_codes"], qb["col_scales"], None), (rb["col_codes"], rb["col_scales"], None),
+                  offs, M, N, label="mxfp8 many groups", layout=layout)
 
 
 @pytest.mark.parametrize("offs,M,N", [
@@ -343,3 +383,43 @@ def test_grouped_moe_fprop_sampled():
                                             r["s_enc"][o0:o1], b_ref[0][g], b_ref[1][g], float(b_ref[2][g]),
                                             rows=rows - o0, cols=cols, with_abs=True)
         check_close(yc.astype(np.float64), ref, torch.bfloat16, "expert %d" % g, sabs, K)
+
+
+def test_grouped_moe_wgrad_mxfp8_slab_sampled():
+    """The mixture-of-experts wgrad at full size: 8 experts over 16384 tokens (boundaries at
+    random multiples of 32), dW_g [14336, 4096] = dY_g^T X_g from MXFP8 columnwise casts of dY
+    [16384, 14336] and X [16384, 4096] with slab-layout codes, fp32 out; the casts are checked
+    whole against the oracle, the GEMM on rows x columns that include the first and last of
+    every 256-wide band of each group's output (every output tile of every group)."""
+    import oracle
+    G, T, M, N = 8, 16384, 14336, 4096
+    rng = np.random.default_rng(2024)
+    cuts = np.sort(rng.choice(np.arange(1, T // 32), G - 1, replace=False)) * 32
+    offs = [0] + [int(c) for c in cuts] + [T]
+    note("grouped K moe wgrad slab sampled offs=%s" % offs)
+    dy = gaussian_bf16((T, M), 1e-4, 61)
+    x = gaussian_bf16((T, N), 1.0, 62)
+    qa = bsq.mxfp8_quantize(dy.to(DEV), direction=bsq.COL | bsq.MX_SLAB)
+    qb = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.COL | bsq.MX_SLAB)
+    o = torch.tensor(offs, dtype=torch.int64, device=DEV)
+    dw = bsq.blockscaled_grouped_gemm(bsq.FMT_MXFP8 | bsq.FMT_MX_SLAB, bsq.GROUP_K, o, qa["col_codes"],
+                                      qa["col_scales"], None, qb["col_codes"], qb["col_scales"], None,
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ra = oracle.mxfp8_quantize(dy, direction=oracle.COL)
+    rb = oracle.mxfp8_quantize(x, direction=oracle.COL)
+    del dy, x
+    assert np.array_equal(from_slab(qa["col_codes"], M, T), ra["col_codes"]), "dY slab codes"
+    assert np.array_equal(from_slab(qb["col_codes"], N, T), rb["col_codes"]), "X slab codes"
+    assert_bytes_equal(qa["col_scales"], ra["col_scales"], "dY col scales")
+    assert_bytes_equal(qb["col_scales"], rb["col_scales"], "X col scales")
+    del qa, qb
+    for g in range(G):
+        o0, o1 = offs[g], offs[g + 1]
+        rows, cols = stratified(M, 70 + g), stratified(N, 80 + g)
+        got = dw[g][torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
+        a = (np.ascontiguousarray(ra["col_codes"][rows, o0:o1]), np.ascontiguousarray(ra["col_scales"][rows, o0 // 32:o1 // 32]))
+        b = (np.ascontiguousarray(rb["col_codes"][cols, o0:o1]), np.ascontiguousarray(rb["col_scales"][cols, o0 // 32:o1 // 32]))
+        ref, sabs = oracle.blockscaled_gemm(oracle.FMT_MXFP8, a[0], a[1], 1.0, b[0], b[1], 1.0, with_abs=True)
+        model = mxfp8_mfma_model(a[0], a[1], b[0], b[1])
+        check_close(got.astype(np.float64), ref, torch.float32, "expert %d" % g, sabs, o1 - o0, model=model)
