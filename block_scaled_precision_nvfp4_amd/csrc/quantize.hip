@@ -578,6 +578,100 @@ __device__ __forceinline__ void load_subtile_nvfp4(const uint8_t* __restrict__ c
     }
 }
 
+// The workgroup's 256 x 128 tile of an NVFP4 rowwise tensor staged in LDS: codes (64 bytes a
+// row; row r at LDS row r ^ ((r >> 4) & 3), so that the four rows a wave reads together, 16
+// apart, fall on different banks), scale bytes (8 a row), and the two dequantization
+// quotients of every scale byte (load_subtile_nvfp4's qa, qb as bf16, and whether the
+// exponent-step shortcut holds), computed once per workgroup instead of once per thread row.
+struct NvTileLds {
+    uint4 codes[TILE_R][4];
+    uint2 scales[TILE_R];
+    uint32_t ab[128];   // bf16(qa) | bf16(qb) << 16 for scale byte s (bit 7 ignored)
+    uint32_t ok[4];     // bit s: qa and qb both in the shortcut's exponent range
+};
+
+// Stage the tile (tr0, tc0) of codes [R][C/2] and scales [R][C/16] (C % 32 == 0, so each
+// 16-byte code chunk lies inside or outside the tensor and rows are 16-byte aligned); rows and
+// chunks outside read as zero.  Ends with a barrier.
+__device__ __forceinline__ void stage_nvfp4_tile(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales, float S, int64_t R,
+                                                 int64_t C, int64_t tr0, int64_t tc0, NvTileLds& L) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int id = tid + NTHREADS * p, row = id >> 2, part = id & 3;
+        const int64_t r = tr0 + row;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < R && tc0 + 32 * part + 32 <= C) v = *(const uint4*)(codes + r * (C / 2) + tc0 / 2 + 16 * part);
+        L.codes[row ^ ((row >> 4) & 3)][part] = v;
+    }
+    {
+        const int64_t r = tr0 + tid;
+        uint32_t lo = 0u, hi = 0u;
+        if (r < R) {
+            const uint8_t* src = scales + r * (C / 16) + tc0 / 16;
+            const int64_t nb = (C - tc0) / 16;   // scale bytes of the row inside the tile
+            if (nb >= 8 && ((uintptr_t)src & 7u) == 0) {
+                const uint2 w = *(const uint2*)src;
+                lo = w.x;
+                hi = w.y;
+            } else {
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const uint32_t v = b < nb ? (uint32_t)src[b] : 0u;
+                    if (b < 4) lo |= v << (8 * b); else hi |= v << (8 * (b - 4));
+                }
+            }
+        }
+        L.scales[tid] = make_uint2(lo, hi);
+    }
+    if (tid < 128) {
+        const float sc = e4m3_decode_nonneg((uint32_t)tid);
+        const float qa = (0.5f * sc) / S, qb = (1.5f * sc) / S;
+        const uint32_t ea = __float_as_uint(qa) >> 23, eb = __float_as_uint(qb) >> 23;
+        const bool ok = ea - 1u < 250u && eb - 1u < 250u;
+        L.ab[tid] = f32_to_bf16_rne(qa) | (f32_to_bf16_rne(qb) << 16);
+        const uint64_t m = __ballot(ok);
+        if ((tid & 63) == 0) {
+            L.ok[2 * (tid >> 6)] = (uint32_t)m;
+            L.ok[2 * (tid >> 6) + 1] = (uint32_t)(m >> 32);
+        }
+    }
+    __syncthreads();
+}
+
+// load_subtile_nvfp4 from the staged tile: the same values, bit for bit.
+__device__ __forceinline__ void load_subtile_nvfp4_lds(const NvTileLds& L, float S, const TileCoord& t,
+                                                       SubTile q) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int lr = 16 * t.rb + j;
+        const uint32_t cw = ((const uint32_t*)&L.codes[lr ^ ((lr >> 4) & 3)][0])[t.cc];
+        const uint32_t sbyte = (((t.cc >> 1) < 4 ? L.scales[lr].x : L.scales[lr].y) >> (8 * ((t.cc >> 1) & 3))) & 0x7Fu;
+        if ((L.ok[sbyte >> 5] >> (sbyte & 31)) & 1u) {
+            const uint32_t ab = L.ab[sbyte];
+            const uint32_t ba = ab & 0xFFFFu, bb = ab >> 16;
+            auto deq = [&](uint32_t c) {
+                const uint32_t m = c & 7u;
+                const uint32_t k = (0x23120100u >> (4u * m)) & 0xFu;
+                const uint32_t base = ((0xA8u >> m) & 1u) ? bb : ba;
+                const uint32_t mag = m ? base + (k << 7) : 0u;
+                return mag | ((c & 8u) << 12);
+            };
+#pragma unroll
+            for (int w = 0; w < 4; ++w) q[j][w] = deq((cw >> (8 * w)) & 0xFu) | (deq((cw >> (8 * w + 4)) & 0xFu) << 16);
+        } else {
+            const float sc = e4m3_decode_nonneg(sbyte);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t lo = nvfp4_dequant_bf16((cw >> (8 * w)) & 0xFu, sc, S);
+                const uint32_t hi = nvfp4_dequant_bf16((cw >> (8 * w + 4)) & 0xFu, sc, S);
+                q[j][w] = lo | (hi << 16);
+            }
+        }
+    }
+}
+
 struct MxArgs {
     const uint16_t* x;         // bf16 source, or
     const uint8_t* nv_codes;   // NVFP4 rowwise source (codes, scales, tensor scale)
@@ -598,8 +692,19 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
     SubTile q;
-    if constexpr (SRC == 0) load_subtile(a.x, R, C, t, q);
-    else load_subtile_nvfp4(a.nv_codes, a.nv_scales, a.nv_s_enc[0], R, C, t, q);
+    if constexpr (SRC == 0) {
+        load_subtile(a.x, R, C, t, q);
+    } else {
+        const float S = a.nv_s_enc[0];
+        if (C % 32 == 0) {   // uniform: 16-byte code chunks, staged through LDS
+            __shared__ NvTileLds stage;
+            stage_nvfp4_tile(a.nv_codes, a.nv_scales, S, R, C, (int64_t)blockIdx.y * TILE_R,
+                             (int64_t)blockIdx.x * TILE_C, stage);
+            load_subtile_nvfp4_lds(stage, S, t, q);
+        } else {
+            load_subtile_nvfp4(a.nv_codes, a.nv_scales, S, R, C, t, q);
+        }
+    }
 
     if (DIRS & 1) mx_row_tile(q, t, R, C, a.row_codes, a.row_scales, a.slab);
 

@@ -363,11 +363,14 @@ def test_hybrid_qwen3_8b_sampled():
 
 
 @pytest.mark.parametrize("shape,direction", [((4096, 1024), 2), ((256, 512), 3), ((96, 160), 1), ((200, 64), 1),
-                                             ((320, 448), 1 | 4), ((320, 448), 3 | 4), ((1088, 128), 1 | 4)])
+                                             ((320, 448), 1 | 4), ((320, 448), 3 | 4), ((1088, 128), 1 | 4),
+                                             ((64, 144), 2), ((288, 416), 3)])
 def test_fused_requantize_matches_chain(shape, direction):
     """mxfp8_requantize_nvfp4 = mxfp8_quantize(nvfp4_dequantize(.)) bit for bit, against the
     oracle's chain and the library's own two-call chain (ragged row counts for rowwise); with
-    MX_SLAB (direction | 4) the codes are compared in the slab layout (ragged last bands)."""
+    MX_SLAB (direction | 4) the codes are compared in the slab layout (ragged last bands).
+    Column counts that are multiples of 32 stage the NVFP4 tile through LDS (416: a last tile
+    with one of its four 16-byte code chunks per row inside), 144 takes the per-thread loads."""
     import oracle
     X = outlier_bf16(shape, seed=shape[0] + 3, mask_seed=shape[1] + 5)
     note("fused requantize %s dir=%d" % (shape, direction))
