@@ -52,6 +52,7 @@ def lib():
         vp, i64, i32, u32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_noalloc.argtypes = [vp, i64, i64, i32, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize_fprop_wgrad.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_col_mxfp8_row_quantize.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp, i32,
                                                    vp, vp, vp]
         L.nvfp4_quantize_rowscaled.argtypes = [vp, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp, vp]
@@ -68,7 +69,7 @@ def lib():
         L.nvfp4_linear_forward.argtypes = [vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_backward.argtypes = [vp, vp, vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
         for f in ("nvfp4_linear_forward", "nvfp4_linear_backward", "nvfp4_quantize", "nvfp4_quantize_noalloc",
-                  "nvfp4_col_mxfp8_row_quantize", "nvfp4_quantize_rowscaled",
+                  "nvfp4_col_mxfp8_row_quantize", "nvfp4_quantize_fprop_wgrad", "nvfp4_quantize_rowscaled",
                   "nvfp4_dequantize", "mxfp8_quantize", "mxfp8_requantize_nvfp4", "rht_apply",
                   "blockscaled_gemm", "blockscaled_grouped_gemm", "bsq_version"):
             getattr(L, f).restype = C.c_int
@@ -150,6 +151,29 @@ def nvfp4_quantize(x: torch.Tensor, direction: int = ROW, rounding: int = RNE, s
         x.data_ptr(), R, Cc, direction, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg),
         _ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
         _ptr(out.get("col_scales")), out["amax"].data_ptr(), out["s_enc"].data_ptr(), ws.data_ptr(), _stream(dev)))
+    return out
+
+
+def nvfp4_quantize_fprop_wgrad(x: torch.Tensor, rounding: int = RNE, sr_seed: int = 0, sr_stream: int = 0,
+                               rht_signs=None, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """One pass over a bf16 [rows, cols] activation that writes its rowwise forward operand (RNE,
+    no transform: ``row_codes``, ``row_scales``) and its columnwise wgrad operand (the given
+    rounding and transform: ``col_codes``, ``col_scales``); ``amax`` / ``s_enc`` as for
+    ``nvfp4_quantize`` (index 0 rowwise, 1 columnwise)."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    R, Cc = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {"row_codes": torch.empty((R, Cc // 2), **u8), "row_scales": torch.empty((R, Cc // 16), **u8),
+           "col_codes": torch.empty((Cc, R // 2), **u8), "col_scales": torch.empty((Cc, R // 16), **u8),
+           "amax": torch.empty(2, dtype=torch.float32, device=dev),
+           "s_enc": torch.empty(2, dtype=torch.float32, device=dev)}
+    ws = _workspace(workspace, NVFP4_QUANTIZE_WORKSPACE_BYTES, dev)
+    sg = _signs(rht_signs, dev)
+    _check("nvfp4_quantize_fprop_wgrad", lib().nvfp4_quantize_fprop_wgrad(
+        x.data_ptr(), R, Cc, rounding, sr_seed & (2 ** 64 - 1), sr_stream, _ptr(sg), out["row_codes"].data_ptr(),
+        out["row_scales"].data_ptr(), out["col_codes"].data_ptr(), out["col_scales"].data_ptr(),
+        out["amax"].data_ptr(), out["s_enc"].data_ptr(), ws.data_ptr(), _stream(dev)))
     return out
 
 

@@ -88,6 +88,20 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
                                                static_cast<float*>(workspace), hip_stream), fn);
 }
 
+int nvfp4_quantize_fprop_wgrad(const void* x, int64_t rows, int64_t cols, int rounding, uint64_t sr_seed,
+                               uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
+                               uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out,
+                               void* workspace, void* hip_stream) {
+    static const char* fn = "nvfp4_quantize_fprop_wgrad";
+    if (const int st = nvfp4_quantize_check(fn, x, rows, cols, BSQ_ROW | BSQ_COL, rounding, rht_signs, row_codes,
+                                            row_scales, col_codes, col_scales, amax_out, s_enc_out, true, workspace))
+        return st;
+    return launched(bsq::launch_nvfp4_quantize_fprop_wgrad(x, rows, cols, rounding, sr_seed, sr_stream, rht_signs,
+                                                           row_codes, row_scales, col_codes, col_scales, amax_out,
+                                                           s_enc_out, static_cast<float*>(workspace), hip_stream),
+                    fn);
+}
+
 int nvfp4_quantize_noalloc(const void* x, int64_t rows, int64_t cols, int direction, int rounding, uint64_t sr_seed,
                            uint32_t sr_stream, const int8_t* rht_signs, uint8_t* row_codes, uint8_t* row_scales,
                            uint8_t* col_codes, uint8_t* col_scales, float* amax_out, float* s_enc_out,
@@ -376,25 +390,23 @@ int nvfp4_linear_forward(const void* x, const void* w, int64_t tokens, int64_t i
         return fail(BSQ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     const LinearLayout L = linear_layout(T, K, N);
     void* ws = workspace;
-    // fprop operands: rowwise NVFP4, RNE
-    st = bsq::launch_nvfp4_quantize(x, T, K, BSQ_ROW, BSQ_RNE, 0, 0, nullptr, at<uint8_t>(ws, L.x_row.codes),
-                                    at<uint8_t>(ws, L.x_row.scales), nullptr, nullptr, at<float>(ws, L.x_row.amax),
-                                    at<float>(ws, L.x_row.s_enc), at<float>(ws, L.qws), hip_stream);
+    // X for both of its GEMMs in one pass: rowwise RNE (the fprop operand, in the workspace) and
+    // columnwise along tokens with RHT + SR (the saved activation for wgrad); slot 0 of the saved
+    // tensor scales holds the rowwise one
+    st = bsq::launch_nvfp4_quantize_fprop_wgrad(x, T, K, BSQ_SR, sr_seed, 1, rht_signs, at<uint8_t>(ws, L.x_row.codes),
+                                                at<uint8_t>(ws, L.x_row.scales), at<uint8_t>(saved, L.x_col.codes),
+                                                at<uint8_t>(saved, L.x_col.scales), at<float>(saved, L.x_col.amax),
+                                                at<float>(saved, L.x_col.s_enc), at<float>(ws, L.qws), hip_stream);
     if (st) return launched(st, fn);
+    // W rowwise, RNE
     st = bsq::launch_nvfp4_quantize(w, N, K, BSQ_ROW, BSQ_RNE, 0, 0, nullptr, at<uint8_t>(ws, L.w_row.codes),
                                     at<uint8_t>(ws, L.w_row.scales), nullptr, nullptr, at<float>(ws, L.w_row.amax),
                                     at<float>(ws, L.w_row.s_enc), at<float>(ws, L.qws), hip_stream);
     if (st) return launched(st, fn);
     st = bsq::launch_blockscaled_gemm(BSQ_FMT_NVFP4, T, N, K, at<uint8_t>(ws, L.x_row.codes),
-                                      at<uint8_t>(ws, L.x_row.scales), at<float>(ws, L.x_row.s_enc),
+                                      at<uint8_t>(ws, L.x_row.scales), at<float>(saved, L.x_col.s_enc),
                                       at<uint8_t>(ws, L.w_row.codes), at<uint8_t>(ws, L.w_row.scales),
                                       at<float>(ws, L.w_row.s_enc), 0, 0, y, BSQ_OUT_BF16, hip_stream);
-    if (st) return launched(st, fn);
-    // the saved activation: X columnwise along tokens (the wgrad contraction), RHT + SR
-    st = bsq::launch_nvfp4_quantize(x, T, K, BSQ_COL, BSQ_SR, sr_seed, 1, rht_signs, nullptr, nullptr,
-                                    at<uint8_t>(saved, L.x_col.codes), at<uint8_t>(saved, L.x_col.scales),
-                                    at<float>(saved, L.x_col.amax), at<float>(saved, L.x_col.s_enc), at<float>(ws, L.qws),
-                                    hip_stream);
     return launched(st, fn);
 }
 

@@ -15,6 +15,10 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
                           uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc, float* workspace,
                           void* hip_stream, uint8_t* mx_codes = nullptr, uint8_t* mx_scales = nullptr,
                           int mx_slab = 0);
+int launch_nvfp4_quantize_fprop_wgrad(const void* x, int64_t R, int64_t C, int rounding, uint64_t seed,
+                                      uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
+                                      uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc,
+                                      float* workspace, void* hip_stream);
 int launch_nvfp4_quantize_noalloc(const void* x, int64_t R, int64_t C, int direction, int rounding, uint64_t seed,
                                   uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
                                   uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc,

@@ -217,7 +217,9 @@ __device__ __forceinline__ void publish_scales(float2 am, float* amax_out, float
 // grid of at most AMAX_PARTS workgroups, workgroup w taking tiles w, w + grid, ...  The
 // butterfly's outputs h are four times the transform's values, exactly, so the maxima of |h|
 // are taken and quartered once at the end.
-template <int DIRS>
+// ROWPLAIN (DIRS 3): the rowwise maximum over the untransformed values (a rowwise direction
+// cast without the transform, beside a transformed columnwise one).
+template <int DIRS, bool ROWPLAIN = false>
 __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t* __restrict__ x, int64_t R,
                                                                   int64_t C, const int8_t* __restrict__ signs,
                                                                   float* __restrict__ parts) {
@@ -233,13 +235,17 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t
             static_for<0, 16>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 float v[8];
+                if constexpr (ROWPLAIN) {
+                    row_of(q, j, v);
+                } else {
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t word = q[j][w] ^ row_sign_word(neg, upper, w);
-                    v[2 * w] = bf16_lo(word);
-                    v[2 * w + 1] = bf16_hi(word);
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t word = q[j][w] ^ row_sign_word(neg, upper, w);
+                        v[2 * w] = bf16_lo(word);
+                        v[2 * w + 1] = bf16_hi(word);
+                    }
+                    rht16_pair_core(v, upper);
                 }
-                rht16_pair_core(v, upper);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) mrow = __builtin_fmaxf(mrow, __builtin_fabsf(v[k]));
             });
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_amax_rht_kernel(const uint16_t
             });
         }
     }
-    store_parts<NTHREADS, DIRS>(mrow * 0.25f, mcol * 0.25f, parts);
+    store_parts<NTHREADS, DIRS>(ROWPLAIN ? mrow : mrow * 0.25f, mcol * 0.25f, parts);
 }
 
 // ------------------------------------------------------------------ NVFP4 encode
@@ -426,9 +432,11 @@ __device__ __forceinline__ void store_col_scales(const uint8_t* sc, uint8_t* out
 
 // MXROW: also the MXFP8 rowwise cast of the same tile (from the untransformed values), so that
 // the per-direction recipe's backward operand (MXFP8 rowwise, NVFP4 columnwise) reads its
-// input once.
-template <int DIRS, bool RHT, bool SR, bool MXROW = false>
+// input once.  ROWPLAIN (DIRS 3): the rowwise direction without the transform and with RNE
+// (the forward operand), the columnwise one with RHT and SR as given (the wgrad operand).
+template <int DIRS, bool RHT, bool SR, bool MXROW = false, bool ROWPLAIN = false>
 __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) {
+    constexpr bool RHT_ROW = RHT && !ROWPLAIN, SR_ROW = SR && !ROWPLAIN;
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
     SubTile q;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             constexpr int j = decltype(j_c)::value;
             const int64_t r = t.r0 + j;
             float v[8];
-            if (RHT) {
+            if (RHT_ROW) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t word = q[j][w] ^ row_sign_word(neg, upper, w);
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
             m = __builtin_fmaxf(m, __shfl_xor(m, 1));
             uint32_t w;
-            const uint32_t sb = encode_block<8, SR, RHT>(v, m, Srow, enc_tab[0],
+            const uint32_t sb = encode_block<8, SR_ROW, RHT_ROW>(v, m, Srow, enc_tab[0],
                                                          (uint64_t)r * (uint64_t)C + (uint64_t)t.c0, a.seed, a.stream,
                                                          0u, &w);
             if (colok && r < R) {
@@ -1215,6 +1223,42 @@ int launch_nvfp4_quantize(const void* x, int64_t R, int64_t C, int direction, in
                          parts, nparts, amax, s_enc, seed, stream, mx_codes, mx_scales, mx_slab};
     if (direction == 2) return rht ? launch_encode_tiles<2, true>(a, sr, s) : launch_encode_tiles<2, false>(a, sr, s);
     return rht ? launch_encode_tiles<3, true>(a, sr, s) : launch_encode_tiles<3, false>(a, sr, s);
+}
+
+// The rowwise forward operand (RNE, no transform) and the columnwise wgrad operand (RHT and SR
+// as given) of one tensor from one amax pass and one encode pass.  Without RHT and SR both
+// directions are the plain cast, which nvfp4_quantize already does in one pass.
+int launch_nvfp4_quantize_fprop_wgrad(const void* x, int64_t R, int64_t C, int rounding, uint64_t seed,
+                                      uint32_t stream, const int8_t* signs, uint8_t* row_codes, uint8_t* row_scales,
+                                      uint8_t* col_codes, uint8_t* col_scales, float* amax, float* s_enc,
+                                      float* parts, void* hip_stream) {
+    const bool rht = signs != nullptr, sr = rounding == 1;
+    if (!rht && !sr)
+        return launch_nvfp4_quantize(x, R, C, 3, 0, seed, stream, nullptr, row_codes, row_scales, col_codes,
+                                     col_scales, amax, s_enc, parts, hip_stream);
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (R == 0 || C == 0) {
+        hipLaunchKernelGGL(empty_tensor_scales_kernel, dim3(1), dim3(64), 0, s, amax, s_enc);
+        return launch_status();
+    }
+    unsigned np;
+    if (rht) {
+        np = amax_grid(((R + TILE_R - 1) / TILE_R) * ((C + TILE_C - 1) / TILE_C), 1);
+        hipLaunchKernelGGL((nvfp4_amax_rht_kernel<3, true>), dim3(np), dim3(NTHREADS), 0, s, (const uint16_t*)x, R, C,
+                           signs, parts);
+    } else {
+        const int64_t n16 = R * C / 8;
+        np = amax_grid(n16, (int64_t)LIN_THREADS * LIN_UNITS);
+        hipLaunchKernelGGL(amax_linear_kernel<3>, dim3(np), dim3(LIN_THREADS), 0, s, (const uint4*)x, n16, parts);
+    }
+    if (const int e = launch_status()) return e;
+    const NvEncodeArgs a{(const uint16_t*)x, R, C, signs, row_codes, row_scales, col_codes, col_scales,
+                         parts, (int)np, amax, s_enc, seed, stream, nullptr, nullptr, 0};
+    const dim3 g = tile_grid(R, C);
+    if (rht && sr) hipLaunchKernelGGL((nvfp4_encode_kernel<3, true, true, false, true>), g, dim3(NTHREADS), 0, s, a);
+    else if (rht) hipLaunchKernelGGL((nvfp4_encode_kernel<3, true, false, false, true>), g, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((nvfp4_encode_kernel<3, false, true, false, true>), g, dim3(NTHREADS), 0, s, a);
+    return launch_status();
 }
 
 // ------------------------------------------------------------------ allocation-free variant

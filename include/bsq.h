@@ -140,6 +140,29 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int direction, int
                    void* hip_stream);
 
 /*
+ * nvfp4_quantize_fprop_wgrad -- one bf16 activation quantized for both of its GEMMs in one
+ * amax pass and one encode pass: rowwise NVFP4 with RNE and no transform (the forward operand,
+ * exactly nvfp4_quantize with direction BSQ_ROW, rounding BSQ_RNE, rht_signs NULL) and
+ * columnwise NVFP4 with the given rounding and transform (the wgrad operand, exactly
+ * nvfp4_quantize with direction BSQ_COL and these rounding, sr_seed, sr_stream and rht_signs).
+ *
+ * Defines: the recipe of the page "Add an NVFP4 quantization converter" (Summary: the random
+ * Hadamard transform and stochastic rounding apply to the backward operands only) applied to
+ * the activation X, whose columnwise quantization is made in the forward pass and saved for
+ * wgrad (Table 1 takeaway: quantized activations are what is saved).
+ *
+ * Arguments: as for nvfp4_quantize with direction BSQ_ROW | BSQ_COL (rows % 16 == 0,
+ * cols % 16 == 0); amax_out[0] / s_enc_out[0] are the rowwise amax and tensor scale of the
+ * untransformed values, [1] the columnwise ones (of the transformed values with RHT).
+ * Errors: those of nvfp4_quantize for these arguments.
+ */
+int nvfp4_quantize_fprop_wgrad(const void* x, int64_t rows, int64_t cols, int rounding,
+                               uint64_t sr_seed, uint32_t sr_stream, const int8_t* rht_signs,
+                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                               uint8_t* col_scales, float* amax_out, float* s_enc_out,
+                               void* workspace, void* hip_stream);
+
+/*
  * nvfp4_col_mxfp8_row_quantize -- one bf16 tensor quantized to two formats, one per direction,
  * in one pass over it: NVFP4 columnwise (exactly nvfp4_quantize with direction BSQ_COL) and
  * MXFP8 rowwise (exactly mxfp8_quantize with direction BSQ_ROW).
@@ -361,8 +384,9 @@ int blockscaled_grouped_gemm(int fmt, int mode, int64_t groups, const int64_t* o
  *             RHT + SR (SR stream 2);
  *             dW[N][K] (fp32) = dY_col * X_col^T  (contraction over tokens, X from `saved`),
  *             dX[T][K] (bf16) = dY_row * W_col^T  (contraction over N).
- * Each step is exactly the corresponding nvfp4_quantize / blockscaled_gemm call; the
- * intermediate quantized operands live in `workspace`.
+ * Each step is exactly the corresponding nvfp4_quantize / blockscaled_gemm call (X's two
+ * casts are one nvfp4_quantize_fprop_wgrad call); the intermediate quantized operands live in
+ * `workspace`.
  *
  *   x [T][K], w [N][K], dy [T][N] bf16 (device); T = tokens, K = in_features,
  *   N = out_features, all multiples of 32, non-zero and below 2^24 (each is the contraction

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
               "mxfp8_requantize_nvfp4", "rht_apply", "blockscaled_gemm", "blockscaled_grouped_gemm",
               "nvfp4_linear_workspace_bytes", "nvfp4_linear_saved_bytes", "nvfp4_linear_forward",
               "nvfp4_linear_backward", "bsq_last_error", "bsq_version", "nvfp4_quantize_noalloc",
-              "nvfp4_col_mxfp8_row_quantize"]:
+              "nvfp4_col_mxfp8_row_quantize", "nvfp4_quantize_fprop_wgrad"]:
         assert f in names
 
 
@@ -121,6 +121,28 @@ def test_hybrid_quantize_empty_needs_no_outputs(L):
     # a zero-row call accepts NULL outputs and workspace: misaligned x still fails on alignment,
     # which proves the call got past the NULL checks without launching anything
     assert hyb(L, rows=0, cc=None, cs=None, ws=None, mc=None, ms=None, x=FAKE + 8) == 6
+
+
+def fw(L, x=FAKE, rows=256, cols=256, rounding=1, signs=None, rc=FAKE, rs=FAKE, cc=FAKE, cs=FAKE, amax=FAKE,
+       senc=FAKE, ws=FAKE):
+    return L.nvfp4_quantize_fprop_wgrad(x, rows, cols, rounding, 0, 0, signs, rc, rs, cc, cs, amax, senc, ws, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(rounding=2), 3, "rounding"),
+    (dict(rows=24), 2, "rows % 16"),
+    (dict(cols=24), 2, "cols % 16"),
+    (dict(rows=-16), 2, "negative"),
+    (dict(rc=None), 1, "rowwise outputs"),
+    (dict(cs=None), 1, "columnwise outputs"),
+    (dict(amax=None), 1, "amax_out"),
+    (dict(ws=None), 1, "workspace"),
+    (dict(x=FAKE + 8), 6, "aligned"),
+    (dict(signs=FAKE + 2), 6, "aligned"),
+])
+def test_fprop_wgrad_quantize_validation(L, kw, status, needle):
+    assert fw(L, **kw) == status
+    assert needle in last(L)
 
 
 def test_mxfp8_quantize_validation(L):

@@ -76,6 +76,28 @@ def check_hybrid(x_cpu, rounding=0, seed=0, stream=0, signs=None, slab=False, la
     assert_bytes_equal(codes, mref["row_codes"], label + " mxfp8 row_codes")
 
 
+def check_fprop_wgrad(x_cpu, rounding=0, seed=0, stream=0, signs=None, label=""):
+    """One-pass rowwise RNE (no transform) + columnwise (given rounding and transform) against
+    the oracle's two casts of the same input."""
+    import oracle
+    note("fprop+wgrad %s shape=%s rnd=%d rht=%s" % (label, tuple(x_cpu.shape), rounding, signs is not None))
+    got = bsq.nvfp4_quantize_fprop_wgrad(x_cpu.to(DEV), rounding=rounding, sr_seed=seed, sr_stream=stream,
+                                         rht_signs=signs)
+    torch.cuda.synchronize()
+    rr = oracle.nvfp4_quantize(x_cpu, direction=1)
+    assert_f32_equal(got["amax"][0:1], rr["amax"][0:1], label + " amax row")
+    assert_f32_equal(got["s_enc"][0:1], rr["s_enc"][0:1], label + " s_enc row")
+    assert_bytes_equal(got["row_scales"], rr["row_scales"], label + " row_scales")
+    assert_bytes_equal(got["row_codes"], rr["row_codes"], label + " row_codes")
+    del rr
+    rc = oracle.nvfp4_quantize(x_cpu, direction=2, rounding=rounding, sr_seed=seed, sr_stream=stream,
+                               signs=None if signs is None else signs.numpy())
+    assert_f32_equal(got["amax"][1:2], rc["amax"][1:2], label + " amax col")
+    assert_f32_equal(got["s_enc"][1:2], rc["s_enc"][1:2], label + " s_enc col")
+    assert_bytes_equal(got["col_scales"], rc["col_scales"], label + " col_scales")
+    assert_bytes_equal(got["col_codes"], rc["col_codes"], label + " col_codes")
+
+
 # ----------------------------------------------------------------- small and ragged
 
 @pytest.mark.parametrize("shape", [(128, 256), (256, 128), (272, 144), (16, 16), (48, 400), (528, 16)])
@@ -150,6 +172,23 @@ def test_hybrid_zero_and_empty():
     torch.cuda.synchronize()
     assert got["amax"][1].item() == 0.0 and got["s_enc"][1].item() == 1.0
     assert got["mx_row_codes"].shape == (0, 64) and got["col_codes"].shape == (64, 0)
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (272, 144), (32, 16), (48, 400), (528, 16)])
+@pytest.mark.parametrize("rounding,use_rht", [(1, True), (0, True), (1, False), (0, False)])
+def test_fprop_wgrad_small(shape, rounding, use_rht):
+    x = outlier_bf16(shape, seed=41, mask_seed=42)
+    check_fprop_wgrad(x, rounding=rounding, seed=SEED_SR_KEY, stream=5, signs=rht_signs(SEED_SIGNS) if use_rht else None,
+                      label="small")
+
+
+def test_fprop_wgrad_zero_and_empty():
+    check_fprop_wgrad(torch.zeros((64, 64), dtype=torch.bfloat16), rounding=1, signs=rht_signs(SEED_SIGNS),
+                      label="zeros")
+    got = bsq.nvfp4_quantize_fprop_wgrad(torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV), rounding=1,
+                                         rht_signs=rht_signs(SEED_SIGNS))
+    torch.cuda.synchronize()
+    assert got["amax"].cpu().tolist() == [0.0, 0.0] and got["s_enc"].cpu().tolist() == [1.0, 1.0]
 
 
 def test_calls_share_no_state():
@@ -357,6 +396,13 @@ def test_fwd_operands_llama3_8b():
     """Forward operands of the Llama-3-8B FFN up-projection, NVFP4 rowwise RNE."""
     check_nvfp4(gaussian_bf16((16384, 4096), 1.0, SEED_X), 1, label="fwd X")
     check_nvfp4(gaussian_bf16((14336, 4096), STD_W, SEED_W), 1, label="fwd W")
+
+
+def test_x_fprop_wgrad_llama3_8b():
+    """The layer input X [16384, 4096] in one pass: rowwise RNE for the forward GEMM and
+    columnwise RHT + SR (stream 1) for wgrad."""
+    check_fprop_wgrad(gaussian_bf16((16384, 4096), 1.0, SEED_X), rounding=1, seed=SEED_SR_KEY, stream=1,
+                      signs=rht_signs(SEED_SIGNS), label="X")
 
 
 def test_dy_hybrid_llama3_8b():
