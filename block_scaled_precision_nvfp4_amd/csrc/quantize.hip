@@ -295,6 +295,11 @@ __device__ __forceinline__ int64_t slab_offset(int64_t r, int64_t k, int64_t row
 __device__ __forceinline__ void mx_row_tile(const SubTile& q, const TileCoord& t, int64_t R, int64_t C,
                                             uint8_t* row_codes, uint8_t* row_scales, int slab) {
     const bool colok = t.c0 < C;
+    // the sub-tile's 16 rows lie in one 256-row band (r0 is a multiple of 16), so in either
+    // layout row r0 + j's codes sit j row pitches (64 bytes in a slab, C row-major) after row r0's
+    uint8_t* code0 = row_codes + (slab ? slab_offset(t.r0, t.c0, R, C) : t.r0 * C + t.c0);
+    const int64_t pitch = slab ? 64 : C;
+    uint8_t* scale0 = row_scales + t.r0 * (C / 32) + t.c0 / 32;
     static_for<0, 16>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         const int64_t r = t.r0 + j;
@@ -313,8 +318,8 @@ __device__ __forceinline__ void mx_row_tile(const SubTile& q, const TileCoord& t
             hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
         }
         if (colok && r < R) {
-            *(uint2*)(row_codes + (slab ? slab_offset(r, t.c0, R, C) : r * C + t.c0)) = make_uint2(lo, hi);
-            if ((t.cc & 3) == 0) row_scales[r * (C / 32) + t.c0 / 32] = (uint8_t)sb;
+            *(uint2*)(code0 + j * pitch) = make_uint2(lo, hi);
+            if ((t.cc & 3) == 0) scale0[j * (C / 32)] = (uint8_t)sb;
         }
     });
 }
