@@ -460,6 +460,9 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
 
     if (DIRS & 1) {
         const bool upper = (t.cc & 1) != 0;
+        // row r0 + j's code word and scale byte, j row pitches after row r0's
+        uint8_t* code0 = a.row_codes + t.r0 * (C / 2) + t.c0 / 2;
+        uint8_t* scale0 = a.row_scales + t.r0 * (C / 16) + t.c0 / 16;
         static_for<0, 16>([&](auto j_c) {
             constexpr int j = decltype(j_c)::value;
             const int64_t r = t.r0 + j;
@@ -484,8 +487,8 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
                                                          (uint64_t)r * (uint64_t)C + (uint64_t)t.c0, a.seed, a.stream,
                                                          0u, &w);
             if (colok && r < R) {
-                *(uint32_t*)(a.row_codes + r * (C / 2) + t.c0 / 2) = w;
-                if (!upper) a.row_scales[r * (C / 16) + t.c0 / 16] = (uint8_t)sb;
+                *(uint32_t*)(code0 + j * (C / 2)) = w;
+                if (!upper) scale0[j * (C / 16)] = (uint8_t)sb;
             }
         });
     }
