@@ -332,8 +332,9 @@ def test_quant_only_workload():
 
 def test_beyond_2g_elements():
     """A [131088, 16384] tensor (2^31 + 2^18 elements, input byte offsets past 2^32): NVFP4
-    rowwise RNE, MXFP8 rowwise, row-scaled NVFP4 and NVFP4 columnwise RNE with RHT.  The tensor maximum (100,
-    above every N(0,1) draw) is planted at row 0, column 5, so any set of rows containing row 0
+    rowwise RNE, MXFP8 rowwise, row-scaled NVFP4, NVFP4 columnwise RNE with RHT, and the
+    two one-pass casts (NVFP4 columnwise + MXFP8 rowwise; NVFP4 rowwise + columnwise).
+    The tensor maximum (100, above every N(0,1) draw) is planted at row 0, column 5, so any set of rows containing row 0
     (or of columns containing column 5) has the tensor's scale; rowwise codes depend only on
     their row and that scale, columnwise codes only on their column, so the oracle quantizes
     sampled rows (the first and last, the middle, a random spread) or sampled columns on
@@ -369,8 +370,22 @@ def test_beyond_2g_elements():
     cidx = torch.from_numpy(cols).to(DEV)
     c_codes, c_scales = col["col_codes"][cidx].contiguous(), col["col_scales"][cidx].contiguous()
     c_amax, c_senc = col["amax"][1:2].clone(), col["s_enc"][1:2].clone()
+    # the one-pass casts on the same tensor (RNE, so that sampled rows and columns are
+    # independent of the element indices SR would draw with): dY's NVFP4 columnwise (RHT) +
+    # MXFP8 rowwise, and an activation's rowwise RNE + columnwise RHT
+    note("rowwise beyond 2^31 elements: one-pass casts")
+    del col
+    hy = bsq.nvfp4_col_mxfp8_row_quantize(xd, rht_signs=signs)
+    h_codes, h_scales = hy["col_codes"][cidx].contiguous(), hy["col_scales"][cidx].contiguous()
+    h_mc, h_ms = hy["mx_row_codes"][idx].contiguous(), hy["mx_row_scales"][idx].contiguous()
+    del hy
+    fw = bsq.nvfp4_quantize_fprop_wgrad(xd, rht_signs=signs)
+    f_rc, f_rs = fw["row_codes"][idx].contiguous(), fw["row_scales"][idx].contiguous()
+    f_cc, f_cs = fw["col_codes"][cidx].contiguous(), fw["col_scales"][cidx].contiguous()
+    f_senc = fw["s_enc"].clone()
+    del fw
     sub_c = xd[:, cidx].cpu().contiguous()
-    del col, xd
+    del xd
     torch.cuda.synchronize()
     ref = oracle.nvfp4_quantize(sub, direction=1)
     assert_f32_equal(g_amax, ref["amax"][0:1], "amax")
@@ -390,6 +405,16 @@ def test_beyond_2g_elements():
     assert_f32_equal(c_senc, cref["s_enc"][1:2], "col s_enc")
     assert_bytes_equal(c_scales, cref["col_scales"], "col_scales")
     assert_bytes_equal(c_codes, cref["col_codes"], "col_codes")
+    assert_bytes_equal(h_scales, cref["col_scales"], "one-pass col_scales")
+    assert_bytes_equal(h_codes, cref["col_codes"], "one-pass col_codes")
+    assert_bytes_equal(h_ms, mref["row_scales"], "one-pass mxfp8 row_scales")
+    assert_bytes_equal(h_mc, mref["row_codes"], "one-pass mxfp8 row_codes")
+    assert_f32_equal(f_senc[0:1], ref["s_enc"][0:1], "fprop+wgrad s_enc row")
+    assert_f32_equal(f_senc[1:2], cref["s_enc"][1:2], "fprop+wgrad s_enc col")
+    assert_bytes_equal(f_rs, ref["row_scales"], "fprop+wgrad row_scales")
+    assert_bytes_equal(f_rc, ref["row_codes"], "fprop+wgrad row_codes")
+    assert_bytes_equal(f_cs, cref["col_scales"], "fprop+wgrad col_scales")
+    assert_bytes_equal(f_cc, cref["col_codes"], "fprop+wgrad col_codes")
 
 
 def test_fwd_operands_llama3_8b():
