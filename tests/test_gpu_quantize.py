@@ -271,6 +271,53 @@ def test_graph_replay(direction, rounding, use_rht):
                 assert torch.equal(out[key + "_codes"], eager[key + "_codes"]), "replay %d vs eager" % i
 
 
+def test_graph_replay_one_pass_casts():
+    """The two one-pass casts (an activation's rowwise RNE + columnwise RHT + SR; dY's NVFP4
+    columnwise RHT + SR + MXFP8 rowwise) captured in one HIP graph and replayed on a large-amax,
+    a small-amax and again the large-amax input: every replay matches the oracle bit for bit."""
+    import oracle
+    shape = (512, 384)
+    inputs = [outlier_bf16(shape, seed=95, mask_seed=96), gaussian_bf16(shape, 1e-4, 97),
+              outlier_bf16(shape, seed=95, mask_seed=96)]
+    signs = rht_signs(SEED_SIGNS)
+    sn = signs.numpy()
+    refs = [(oracle.nvfp4_quantize(t, direction=1),
+             oracle.nvfp4_quantize(t, direction=2, rounding=1, sr_seed=SEED_SR_KEY, sr_stream=1, signs=sn),
+             oracle.nvfp4_quantize(t, direction=2, rounding=1, sr_seed=SEED_SR_KEY, sr_stream=0, signs=sn),
+             oracle.mxfp8_quantize(t, direction=1)) for t in inputs]
+    xin = inputs[2].to(DEV)
+    sg = signs.to(DEV)
+    note("graph capture of the one-pass casts")
+    calls = lambda: (bsq.nvfp4_quantize_fprop_wgrad(xin, rounding=1, sr_seed=SEED_SR_KEY, sr_stream=1, rht_signs=sg),
+                     bsq.nvfp4_col_mxfp8_row_quantize(xin, rounding=1, sr_seed=SEED_SR_KEY, sr_stream=0, rht_signs=sg))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fw, hy = calls()
+    for i, (t, (rrow, rcol1, rcol0, rmx)) in enumerate(zip(inputs, refs)):
+        note("graph replay %d" % i)
+        xin.copy_(t.to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_f32_equal(fw["s_enc"][0:1], rrow["s_enc"][0:1], "replay %d fprop s_enc" % i)
+        assert_bytes_equal(fw["row_scales"], rrow["row_scales"], "replay %d fprop row_scales" % i)
+        assert_bytes_equal(fw["row_codes"], rrow["row_codes"], "replay %d fprop row_codes" % i)
+        assert_f32_equal(fw["s_enc"][1:2], rcol1["s_enc"][1:2], "replay %d wgrad s_enc" % i)
+        assert_bytes_equal(fw["col_scales"], rcol1["col_scales"], "replay %d wgrad col_scales" % i)
+        assert_bytes_equal(fw["col_codes"], rcol1["col_codes"], "replay %d wgrad col_codes" % i)
+        assert_f32_equal(hy["s_enc"][1:2], rcol0["s_enc"][1:2], "replay %d dY s_enc" % i)
+        assert_bytes_equal(hy["col_scales"], rcol0["col_scales"], "replay %d dY col_scales" % i)
+        assert_bytes_equal(hy["col_codes"], rcol0["col_codes"], "replay %d dY col_codes" % i)
+        assert_bytes_equal(hy["mx_row_scales"], rmx["row_scales"], "replay %d dY mxfp8 scales" % i)
+        assert_bytes_equal(hy["mx_row_codes"], rmx["row_codes"], "replay %d dY mxfp8 codes" % i)
+
+
 def test_nvfp4_extreme_values():
     """Subnormal bf16, huge values and signed zeros in one tensor."""
     v = torch.tensor([0.0, -0.0, 1e-40, -1e-39, 3.0e38, -2.5e38, 1.0, -6.0] * 64, dtype=torch.float32)
