@@ -1463,8 +1463,8 @@ __global__ __launch_bounds__(Fmt<FMT>::THREADS, 1) void gemm_kernel(GemmArgs g, 
 
 // ---------------------------------------------------------------- persistent NVFP4 kernel
 //
-// Plain NVFP4 launches with per-tensor scales on both operands and K a multiple of 256 (at
-// least 512).  At most one workgroup per CU: workgroup b computes the output tiles b, b + P,
+// Plain NVFP4 launches with a per-tensor scale on B and on A (or, with bf16 output, one per
+// row of A) and K a multiple of 256 (at least 512).  At most one workgroup per CU: workgroup b computes the output tiles b, b + P,
 // b + 2P, ... (P = gridDim.x, a multiple of 8 whenever it is below the tile count, so that all
 // tiles of a workgroup have the XCD phase tile_of assumes).  The LDS ring and the operand
 // pipeline of nvw_main_loop run on from one tile to the next: the next tile's slices 0-2 and
@@ -1515,9 +1515,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // until the next barrier.  A pass stages 32 rows (one accumulator row group i) by JS x 32
 // columns of the wave's block in the wave's 8 KiB, row-major with the 16-byte chunk index
 // XORed with the row, then each lane stores CPL chunks.  Every lane takes part in every pass.
+// With rowf, row r of the tile takes the factor rowf[r] instead of alpha (a row-scaled A).
 template <bool OUT_F32, int TN>
 __device__ __forceinline__ void nvp_store(const GemmArgs& g, int64_t m0, int64_t n0, int wm, int wn, int wave,
-                                          int lane, float alpha, const floatx16 (&acc)[4][TN], uint8_t* stage) {
+                                          int lane, float alpha, const floatx16 (&acc)[4][TN], uint8_t* stage,
+                                          const float* rowf = nullptr) {
     constexpr int ES = OUT_F32 ? 4 : 2;
     constexpr int JS = 8 / ES < TN ? 8 / ES : TN;   // 32-column groups per pass (8 KiB / 32 rows / 32 / ES)
     constexpr int RB = 32 * JS * ES;                // staged bytes per row
@@ -1533,13 +1535,14 @@ __device__ __forceinline__ void nvp_store(const GemmArgs& g, int64_t m0, int64_t
     const uint32_t cbase = (uint32_t)(n0 + wn) * ES;
     static_for<0, 4 * (TN / JS)>([&](auto p_c) {
         constexpr int I = decltype(p_c)::value / (TN / JS), J0 = (decltype(p_c)::value % (TN / JS)) * JS;
+        const float f = rowf ? rowf[wm + 32 * I + frow] : alpha;   // the lane's row in this pass
 #pragma unroll
         for (int jj = 0; jj < JS; ++jj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int j = J0 + jj;
-                const float x = acc_read(acc[I][j][4 * q]) * alpha, y = acc_read(acc[I][j][4 * q + 1]) * alpha;
-                const float z = acc_read(acc[I][j][4 * q + 2]) * alpha, w = acc_read(acc[I][j][4 * q + 3]) * alpha;
+                const float x = acc_read(acc[I][j][4 * q]) * f, y = acc_read(acc[I][j][4 * q + 1]) * f;
+                const float z = acc_read(acc[I][j][4 * q + 2]) * f, w = acc_read(acc[I][j][4 * q + 3]) * f;
                 const int col = 32 * jj + 8 * q + 4 * kh;   // first of the 4 columns, within the pass
                 uint8_t* dst = reg + frow * RB + (((col * ES / 16) ^ (frow & (CPR - 1))) << 4) + (col * ES) % 16;
                 if constexpr (OUT_F32) *(float4*)dst = make_float4(x, y, z, w);
@@ -1556,10 +1559,15 @@ __device__ __forceinline__ void nvp_store(const GemmArgs& g, int64_t m0, int64_t
     });
 }
 
-template <bool OUT_F32>
+// AROWS: A is row-scaled (one tensor scale per row of A, B per-tensor): each tile's rows take
+// fp32(1 / (S_a[m] S_b)) (product and quotient in binary64, as tile_factors), the row's scale
+// loaded at the top of the tile and the factors put in LDS between the last slice and the
+// stores.
+template <bool OUT_F32, bool AROWS = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_full, int64_t halves) {
     constexpr int TN = 4, NW = 4, DC = 8, DG = 2, PSTEP = 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds[Fmt<2>::LDS];
+    __shared__ float rowf[AROWS ? GBM : 1];   // a row-scaled A's factors of the tile being stored
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int frow = lane & 31, kh = lane >> 5;
     const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
@@ -1568,10 +1576,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
     const int items = (int)((t_full - 1 - (int64_t)blockIdx.x) / P) + 1;   // t_full >= P
     const int nk = (int)(g.K / 128);   // even, >= 4
     // alpha = fp32(1 / (S_a S_b)), product and quotient in binary64 (as in tile_factors)
-    float alpha = (float)(1.0 / ((double)g.a_s_enc[0] * (double)g.b_s_enc[0]));
+    const double sbd = (double)g.b_s_enc[0];
+    float alpha = AROWS ? 1.0f : (float)(1.0 / ((double)g.a_s_enc[0] * sbd));
 #if __HIP_DEVICE_COMPILE__
     asm volatile("" : "+v"(alpha));
 #endif
+    // thread t's row of the tile (t < 256 = GBM): its A tensor scale and output factor
+    auto row_scale = [&](int64_t tm0) { return g.a_s_enc[tm0 + threadIdx.x < g.M ? tm0 + threadIdx.x : g.M - 1]; };
+    auto put_factors = [&](int64_t tm0, float sa) {
+        rowf[threadIdx.x] = tm0 + threadIdx.x < g.M ? (float)(1.0 / ((double)sa * sbd)) : 1.0f;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
     auto origin = [&](int it, int64_t& m0, int64_t& n0) {   // tiles < 2^31 (host check)
         uint32_t tm, tn;
         tile_of32((uint32_t)nbm, (uint32_t)nbn, blockIdx.x + (uint32_t)it * (uint32_t)P, tm, tn);
@@ -1616,6 +1631,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
 
     for (int it = 0; it < items; ++it) {
         const int gs0 = it * nk;
+        [[maybe_unused]] float sa_row = 0.0f;
+        if constexpr (AROWS) sa_row = row_scale(m0);   // used by the stores at the tile's end
         // slice kt of this tile; in the tile's last slice (LAST) the last step neither reads nor
         // dequantizes the next tile's first step: that happens after the stores, so that those
         // operands are not live across the epilogue
@@ -1680,7 +1697,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
         slice(nk - 2, F_{}, F_{}, F_{});
         slice(nk - 1, T_{}, T_{}, F_{});
         lds_barrier();   // every wave is done with the stage of the last slice
-        nvp_store<OUT_F32, TN>(g, m0, n0, wm, wn, wave, lane, alpha, acc, buf(gs0 + nk - 1));
+        if constexpr (AROWS) {
+            put_factors(m0, sa_row);
+            nvp_store<OUT_F32, TN>(g, m0, n0, wm, wn, wave, lane, alpha, acc, buf(gs0 + nk - 1), rowf);
+        } else {
+            nvp_store<OUT_F32, TN>(g, m0, n0, wm, wn, wave, lane, alpha, acc, buf(gs0 + nk - 1));
+        }
         // the next tile's first step (its slice 0 landed before the top of this tile's last
         // slice, whose step 5 read its first scale records)
         nvw_read_quad<0, TN>(buf(gs0 + nk), wm, wn, frow, kh, q0);
@@ -1719,7 +1741,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nvp_kernel(GemmArgs g, int64_t t_
                     for (int r = 0; r < 16; ++r) hacc[i][j][r] = 0.0f;
             nvw_main_loop<2, 4>(g, hm0, hn0, nk, lds, hwm, hwn, lane, hacc, 128);
             lds_barrier();   // every wave is done with the ring
-            nvp_store<OUT_F32, 2>(g, hm0, hn0, hwm, hwn, wave, lane, alpha, hacc, lds);
+            if constexpr (AROWS) {
+                put_factors(hm0, row_scale(hm0));
+                nvp_store<OUT_F32, 2>(g, hm0, hn0, hwm, hwn, wave, lane, alpha, hacc, lds, rowf);
+            } else {
+                nvp_store<OUT_F32, 2>(g, hm0, hn0, hwm, hwn, wave, lane, alpha, hacc, lds);
+            }
         }
     }
 }
@@ -1745,14 +1772,15 @@ static bool slab_ok(const GemmArgs& g, int fmt, int mode) {
 }
 
 // Workgroups of a persistent NVFP4 launch over `tiles` output tiles, or 0 where that kernel does
-// not apply: per-tensor scales on both operands, K a multiple of 256 and at least 512, N a
+// not apply: a per-tensor scale on B and on A (or one per row of A, bf16 output only: with fp32
+// output that variant spills), K a multiple of 256 and at least 512, N a
 // multiple of 8 (every 16-byte chunk of a row of C lies inside C or outside it), C 16-byte aligned, a
 // tile's rows of C within a 2^31-byte resource, and the global slice count of a workgroup
 // within int range.
 static int64_t persistent_workgroups(const GemmArgs& g, int c_dtype, int64_t tiles) {
     if (tiles >= ((int64_t)1 << 31) || g.N >= ((int64_t)1 << 34)) return 0;   // 32-bit tile arithmetic
     const int64_t es = c_dtype == 1 ? 4 : 2;
-    if (g.a_rows || g.b_rows || g.K % 256 != 0 || g.K < 512 || g.N % 8 != 0) return 0;
+    if (g.b_rows || (g.a_rows && c_dtype == 1) || g.K % 256 != 0 || g.K < 512 || g.N % 8 != 0) return 0;
     if ((uintptr_t)g.c % 16 != 0 || (int64_t)GBM * g.N * es > 0x7FFFFFFF) return 0;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -1774,9 +1802,14 @@ static int launch_fmt(int fmt, int c_dtype, const GemmArgs& g, const GroupArgs& 
                 const int64_t r = tiles % p;
                 const int64_t t_full = (r != 0 && 2 * r <= p) ? tiles - r : tiles;
                 const int64_t halves = t_full < tiles ? 2 * r : 0;
-                if (c_dtype == 1)
-                    hipLaunchKernelGGL(gemm_nvp_kernel<true>, dim3((unsigned)p), dim3(256), 0, s, g, t_full, halves);
-                else hipLaunchKernelGGL(gemm_nvp_kernel<false>, dim3((unsigned)p), dim3(256), 0, s, g, t_full, halves);
+                const dim3 grid((unsigned)p), block(256);
+                if (g.a_rows) {   // bf16 output (persistent_workgroups)
+                    hipLaunchKernelGGL((gemm_nvp_kernel<false, true>), grid, block, 0, s, g, t_full, halves);
+                } else if (c_dtype == 1) {
+                    hipLaunchKernelGGL((gemm_nvp_kernel<true>), grid, block, 0, s, g, t_full, halves);
+                } else {
+                    hipLaunchKernelGGL((gemm_nvp_kernel<false>), grid, block, 0, s, g, t_full, halves);
+                }
                 return (int)hipGetLastError();
             }
         }

@@ -163,6 +163,17 @@ def test_rowscaled_gemm_f32_out(a_rows, b_rows):
     rowscaled_gemm_check(260, 100, 288, a_rows, b_rows, out_dtype=torch.float32, label="f32-ragged")
 
 
+@pytest.mark.parametrize("M,N,K", [(4352, 4160, 512), (8192, 8192, 768)])
+def test_rowscaled_gemm_persistent(M, N, K):
+    """Row-scaled A with per-tensor B and bf16 out on the persistent kernel: several tiles per
+    workgroup, each tile's per-row factors put in LDS before its stores, a last round split
+    into halves (289 tiles) or whole (1024 tiles), a ragged last column band.  Every 256-row
+    and 128-column band is sampled."""
+    from tests.gpu_common import stratified
+    rowscaled_gemm_check(M, N, K, 1, 0, rows=stratified(M, 78), cols=stratified(N, 79, band=128),
+                         label="persistent")
+
+
 def test_rowscaled_gemm_equal_scales_is_bitwise_per_tensor():
     """Per-row scales that all equal the tensor scale give the per-tensor GEMM bit for bit
     when one operand is row-scaled (the factor is the same binary64 quotient rounded once)."""
