@@ -600,11 +600,11 @@ def main():
             "dgrad": (M_TOK + K_IN) * N_OUT * 1.03125 + 2.0 * M_TOK * K_IN}
     gemms = {
         "fwd_nvfp4": roofline_entry("mfma", tflops(g_fwd), F16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-                                    "gemm_nvp_kernel<false>: NVFP4 fwd Y = X W^T, persistent, f16 MFMA with in-register dequant",
+                                    "gemm_nvp_kernel<false, false>: NVFP4 fwd Y = X W^T, persistent, f16 MFMA with in-register dequant",
                                     algo["fwd"], "gemm_fwd_nvfp4", ms=round(g_fwd, 4),
                                     frac_of_measured=round(tflops(g_fwd) / peaks["mfma_f16_32x32x16_TFLOPs"], 4)),
         "wgrad_nvfp4": roofline_entry("mfma", tflops(g_wgrad), F16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-                                      "gemm_nvp_kernel<true>: NVFP4 wgrad dW = dY^T X (fp32 out), persistent, f16 MFMA",
+                                      "gemm_nvp_kernel<true, false>: NVFP4 wgrad dW = dY^T X (fp32 out), persistent, f16 MFMA",
                                       algo["wgrad"], "gemm_wgrad_nvfp4", ms=round(g_wgrad, 4),
                                       frac_of_measured=round(tflops(g_wgrad) / peaks["mfma_f16_32x32x16_TFLOPs"], 4)),
         "dgrad_mxfp8": roofline_entry("mfma", tflops(g_dgrad), FP8_MFMA_PEAK_TFLOPS, "TFLOP/s",
@@ -623,7 +623,7 @@ def main():
     quant = {
         "dy_col_rht_sr_mx_row": roofline_entry(
             "hbm", gbps(dy_bytes, q_dy), HBM_PEAK_GBPS, "GB/s",
-            "nvfp4_amax_rht_kernel<2> + nvfp4_encode_kernel<2,true,true,true>: dY[16384,14336] in one encode "
+            "nvfp4_amax_rht_kernel<2,false> + nvfp4_encode_kernel<2,true,true,true,false>: dY[16384,14336] in one encode "
             "pass, NVFP4 columnwise RHT16 + Philox SR and MXFP8 rowwise", dy_bytes, "quant_dy_hybrid",
             us=round(q_dy * 1e3, 2),
             two_pass_bound_frac=round(gbps(dy_bytes, q_dy) / (HBM_PEAK_GBPS * two_pass(0.5625 + 1.03125)), 4)),
