@@ -39,13 +39,15 @@ struct TileCoord {
     int rb, cc;       // sub-tile coordinates inside the workgroup tile
 };
 
-// The thread's sub-tile in tile (ty, tx) of the 256 x 128 tile grid.
+// The thread's sub-tile in tile (ty, tx) of the TR x TC tile grid (TC / 8 threads per row of
+// sub-tiles; 256 x 128 unless a kernel says otherwise).
+template <int TR = TILE_R, int TC = TILE_C>
 __device__ __forceinline__ TileCoord tile_coord_at(int64_t ty, int64_t tx) {
     TileCoord t;
-    t.rb = threadIdx.x >> 4;
-    t.cc = threadIdx.x & 15;
-    t.r0 = ty * TILE_R + 16 * t.rb;
-    t.c0 = tx * TILE_C + 8 * t.cc;
+    t.rb = threadIdx.x / (TC / 8);
+    t.cc = threadIdx.x % (TC / 8);
+    t.r0 = ty * TR + 16 * t.rb;
+    t.c0 = tx * TC + 8 * t.cc;
     return t;
 }
 
@@ -59,15 +61,16 @@ __device__ __forceinline__ TileCoord tile_coord() { return tile_coord_at(blockId
 // The loads go through a buffer resource over the tile's rows that exist (rows past R read
 // as zero through its range check, a column chunk past C through an offset beyond it), so a
 // row costs one 32-bit offset add instead of 64-bit address arithmetic and a branch; tensors
-// whose 256-row tile spans 2^31 bytes or more (C >= 2^22) take 64-bit addresses instead.
+// whose TR-row tile spans 2^31 bytes or more (C TR >= 2^30) take 64-bit addresses instead.
 typedef uint32_t SubTile[16][4];
 
+template <int TR = TILE_R>
 __device__ __forceinline__ void load_subtile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                              const TileCoord& t, SubTile q) {
     const bool colok = t.c0 < C;
-    if (C < ((int64_t)1 << 22)) {   // uniform
+    if (C * TR < ((int64_t)1 << 30)) {   // uniform
         const int64_t row0 = t.r0 - 16 * t.rb;   // the tile's first row
-        const int64_t rows = (R - row0) < TILE_R ? (R - row0) : TILE_R;
+        const int64_t rows = (R - row0) < TR ? (R - row0) : TR;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(x + row0 * C), (short)0, (int)(rows * C * 2), 0x00020000);
         const uint32_t stride = (uint32_t)C * 2u;
@@ -280,6 +283,32 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float m) {
 // 2^-X for scale byte b (X = b - 127): binary32 with exponent field 254 - b (b <= 246).
 __device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
 
+// Two 16-bit lanes of a 32-bit word, unsigned or signed: packed minima and maxima
+// (v_pk_max_u16, v_pk_min_u16, v_pk_min_i16).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_i16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(i16x2_t, a), __builtin_bit_cast(i16x2_t, b)));
+}
+
+// Four E4M3 codes (bytes 0..3: a.lo, a.hi, b.lo, b.hi) of bf16 pairs a and b divided by the
+// binary32 power of two s, rounded to nearest even (v_cvt_scalef32_pk_fp8_bf16: exact for a
+// normal s and quotients below 464 in magnitude; larger ones give the NaN code, so callers clamp).
+__device__ __forceinline__ uint32_t fp8x4_scaled(uint32_t a, uint32_t b, float s) {
+    typedef short s16x2_t __attribute__((ext_vector_type(2)));
+    // the first conversion replaces the low word of a's own register; the second the high one
+    s16x2_t o = __builtin_bit_cast(s16x2_t, a);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, __builtin_bit_cast(bf16x2_t, a), s, false);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, __builtin_bit_cast(bf16x2_t, b), s, true);
+    return __builtin_bit_cast(uint32_t, o);
+}
+
 // Byte offset of code (r, k) of a [rows][K] code matrix in the slab layout: rows in bands of
 // 256 (the last band holds the rest), band b at byte 256 b K, holding its n rows as K/64
 // consecutive slabs of n x 64 bytes (K a multiple of 64).  A GEMM tile's rows are one band,
@@ -403,23 +432,23 @@ __device__ __forceinline__ uint32_t encode_block(float* v, float vmax, float S, 
     return sb;
 }
 
-// The columnwise scales of a tile: column col's BN = 256 / BLK scale bytes sit in LDS at
+// The columnwise scales of a TR x TC tile: column col's BN = TR / BLK scale bytes sit in LDS at
 // sc[col][b ^ x(col)] (the placement the encode writes them in: x = (col >> 3) mod BN) and
 // are contiguous in the output row of column tc0 + col.  One thread per column gathers them
 // and, where the tile's rows are all inside R and the output row's bytes are aligned for it,
-// writes them with one BN-byte store (16 for NVFP4, 8 for MXFP8) instead of BN byte stores
-// spread over the workgroup.
-template <int BLK>
+// writes them with one BN-byte store (16 for NVFP4 and the 512-row MXFP8 tile, 8 for the
+// 256-row MXFP8 tile) instead of BN byte stores spread over the workgroup.
+template <int BLK, int TR = TILE_R, int TC = TILE_C>
 __device__ __forceinline__ void store_col_scales(const uint8_t* sc, uint8_t* out, int64_t R, int64_t C, int64_t tr0,
                                                  int64_t tc0) {
-    constexpr int BN = TILE_R / BLK;
+    constexpr int BN = TR / BLK;
     const int col = threadIdx.x;
-    if (col >= TILE_C) return;
+    if (col >= TC) return;
     const int64_t c = tc0 + col;
     if (c >= C) return;
     const int x = (col >> 3) & (BN - 1);
     uint8_t* dst = out + c * (R / BLK) + tr0 / BLK;
-    if (tr0 + TILE_R <= R && ((uintptr_t)dst % BN) == 0) {
+    if (tr0 + TR <= R && ((uintptr_t)dst % BN) == 0) {
         uint32_t w[BN / 4];
 #pragma unroll
         for (int i = 0; i < BN / 4; ++i) {
@@ -702,20 +731,50 @@ struct MxArgs {
 };
 
 
-// SRC 0: bf16 input; SRC 1: the rowwise-dequantized value of an NVFP4 tensor.
-template <int DIRS, int SRC = 0>
-__global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
-    const TileCoord t = tile_coord();
+// Tile of workgroup id among G tiles in an XCD-aware order: workgroups are dispatched to the
+// chip's 8 XCDs in turn (id mod 8), so XCD x is given the x-th contiguous run of tiles in row-major
+// tile order and streams one band of the tensor through its own L2 instead of every eighth tile.
+__device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t G) {
+    const int64_t q = G / 8, rmd = G % 8, x = id % 8;
+    return x * q + (x < rmd ? x : rmd) + id / 8;
+}
+
+// Maximum of the packed 16-bit lanes of m and of lane t ^ CCS's m (the other half of a 32-row
+// block, CCS = 16 or 32 sub-tiles per tile row): v_permlane16_swap / v_permlane32_swap leave a
+// lane's own value and its partner's in the two results.
+template <int CCS>
+__device__ __forceinline__ uint32_t pk_max_u16_block_pair(uint32_t m) {
+    static_assert(CCS == 16 || CCS == 32, "partner lane within the wave");
+    if constexpr (CCS == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+        return pk_max_u16(r[0], r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+        return pk_max_u16(r[0], r[1]);
+    }
+}
+
+// MXFP8 cast of TR x TC tiles (TR TC / 128 threads of 16 x 8 sub-tiles; a 1-D grid of tiles in
+// XCD-aware order).  SRC 0: bf16 input, 512 x 256 tiles (16 waves; a wave reads two 512-byte row
+// segments per load and the columnwise transpose leaves as 512-byte pieces of each output row).
+// SRC 1: the rowwise-dequantized value of an NVFP4 tensor, 256 x 128 tiles staged through LDS.
+template <int DIRS, int SRC, int TR, int TC>
+__global__ __launch_bounds__(TR * TC / 128) void mxfp8_kernel(MxArgs a) {
+    constexpr int CCS = TC / 8, RBS = TR / 16, BN = TR / 32;
+    static_assert(SRC == 0 || (TR == TILE_R && TC == TILE_C), "the NVFP4 staging is 256 x 128");
     const int64_t R = a.R, C = a.C;
+    const int64_t ntx = (C + TC - 1) / TC, ntile = ntx * ((R + TR - 1) / TR);
+    const int64_t tile = xcd_tile(blockIdx.x, ntile);
+    const int64_t tr0 = tile / ntx * TR, tc0 = tile % ntx * TC;
+    const TileCoord t = tile_coord_at<TR, TC>(tile / ntx, tile % ntx);
     SubTile q;
     if constexpr (SRC == 0) {
-        load_subtile(a.x, R, C, t, q);
+        load_subtile<TR>(a.x, R, C, t, q);
     } else {
         const float S = a.nv_s_enc[0];
         if (C % 32 == 0) {   // uniform: 16-byte code chunks, staged through LDS
             __shared__ NvTileLds stage;
-            stage_nvfp4_tile(a.nv_codes, a.nv_scales, S, R, C, (int64_t)blockIdx.y * TILE_R,
-                             (int64_t)blockIdx.x * TILE_C, stage);
+            stage_nvfp4_tile(a.nv_codes, a.nv_scales, S, R, C, tr0, tc0, stage);
             load_subtile_nvfp4_lds(stage, S, t, q);
         } else {
             load_subtile_nvfp4(a.nv_codes, a.nv_scales, S, R, C, t, q);
@@ -725,19 +784,22 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
     if (DIRS & 1) mx_row_tile(q, t, R, C, a.row_codes, a.row_scales, a.slab);
 
     if (DIRS & 2) {
-        // same placement as the NVFP4 columnwise transpose: block rb of column 8cc + k at
-        // [8cc + k][rb ^ cc] (scales at [8cc + k][(rb >> 1) ^ (cc & 7)])
-        __shared__ uint4 lds_codes[TILE_C][TILE_R / 16];
-        __shared__ uint8_t lds_sc[TILE_C][TILE_R / 32];
+        // the NVFP4 columnwise transpose's placement: block rb of column 8cc + k at
+        // [8cc + k][rb ^ cc] (scales at [8cc + k][(rb >> 1) ^ (cc mod BN)])
+        __shared__ uint4 lds_codes[TC][RBS];
+        __shared__ uint8_t lds_sc[TC][BN];
+        static_assert(CCS <= RBS, "swizzle stays inside a column's slots");
         const bool upper = (t.rb & 1) != 0;
-        static_for<0, 8>([&](auto k_c) {
+        const int slot = t.rb ^ t.cc, sslot = (t.rb >> 1) ^ (t.cc & (BN - 1));
+        // binary32 form of column k: amax, scale byte, x * 2^-X clamped to +-448, E4M3 codes
+        auto col_f32 = [&](auto k_c) {
             constexpr int k = decltype(k_c)::value;
             float v[16];
             col_of(q, k, v);
             float m = 0.0f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+            m = __builtin_fmaxf(m, __shfl_xor(m, CCS));
             uint32_t w[4] = {0, 0, 0, 0}, sb = 0;
             if (m != 0.0f) {
                 sb = mx_scale_byte(m);
@@ -746,16 +808,56 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
                 for (int q = 0; q < 4; ++q)
                     w[q] = e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
             }
-            lds_codes[8 * t.cc + k][t.rb ^ t.cc] = make_uint4(w[0], w[1], w[2], w[3]);
-            if (!upper) lds_sc[8 * t.cc + k][(t.rb >> 1) ^ (t.cc & 7)] = (uint8_t)sb;
+            lds_codes[8 * t.cc + k][slot] = make_uint4(w[0], w[1], w[2], w[3]);
+            if (!upper) lds_sc[8 * t.cc + k][sslot] = (uint8_t)sb;
+        };
+        // Packed form of the column pair (2w, 2w + 1) held in word w of every row: the same codes
+        // and scale bytes.  For finite bf16 the magnitude bits order like the values, so one
+        // 16-bit unsigned maximum per row gives both columns' amax; the amax exponent field E
+        // gives the scale byte E - 8 (X = E - 135).  Each element is clamped to 448 * 2^X (bf16
+        // exponent E, mantissa 1.75), the largest value whose code is finite, by a signed and an
+        // unsigned 16-bit minimum; v_cvt_scalef32_pk_fp8_bf16 then divides two elements of one
+        // column by 2^X (exact) and rounds them to nearest even E4M3.  The conversion neither
+        // saturates nor takes a zero scale operand, so a wave in which some block has E <= 8
+        // (all zero, or amax below 2^-118: scale byte 0) takes the binary32 form.
+        static_for<0, 4>([&](auto w_c) {
+            constexpr int w = decltype(w_c)::value;
+            uint32_t M = 0u;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) M = pk_max_u16(M, q[j][w] & 0x7FFF7FFFu);
+            M = pk_max_u16_block_pair<CCS>(M);
+            const bool fast = (M & 0xFFFFu) >= 0x480u && M >= 0x04800000u;   // both E >= 9
+            if (__builtin_amdgcn_ballot_w64(!fast) == 0) {   // wave-uniform
+                const uint32_t T = (M & 0x7F807F80u) | 0x00600060u;
+                const uint32_t sb = ((M >> 7) & 0x00FF00FFu) - 0x00080008u;
+                const float s_lo = __uint_as_float((sb & 0xFFu) << 23), s_hi = __uint_as_float((sb >> 16) << 23);
+                uint32_t z[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) z[j] = pk_min_u16(pk_min_i16(q[j][w], T), T | 0x80008000u);
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    lo[d] = fp8x4_scaled(__builtin_amdgcn_perm(z[4 * d + 1], z[4 * d], 0x05040100u),
+                                         __builtin_amdgcn_perm(z[4 * d + 3], z[4 * d + 2], 0x05040100u), s_lo);
+                    hi[d] = fp8x4_scaled(__builtin_amdgcn_perm(z[4 * d + 1], z[4 * d], 0x07060302u),
+                                         __builtin_amdgcn_perm(z[4 * d + 3], z[4 * d + 2], 0x07060302u), s_hi);
+                }
+                lds_codes[8 * t.cc + 2 * w][slot] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                lds_codes[8 * t.cc + 2 * w + 1][slot] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                if (!upper) {
+                    lds_sc[8 * t.cc + 2 * w][sslot] = (uint8_t)(sb & 0xFFu);
+                    lds_sc[8 * t.cc + 2 * w + 1][sslot] = (uint8_t)(sb >> 16);
+                }
+            } else {
+                col_f32(std::integral_constant<int, 2 * w>{});
+                col_f32(std::integral_constant<int, 2 * w + 1>{});
+            }
         });
         __syncthreads();
-        const int64_t tr0 = (int64_t)blockIdx.y * TILE_R;
-        const int64_t tc0 = (int64_t)blockIdx.x * TILE_C;
 #pragma unroll
-        for (int p = 0; p < (TILE_C * TILE_R / 16) / NTHREADS; ++p) {
-            const int idx = threadIdx.x + NTHREADS * p;
-            const int col = idx >> 4, rbk = idx & 15;
+        for (int p = 0; p < 8; ++p) {   // TC x RBS 16-byte pieces, 8 per thread
+            const int idx = threadIdx.x + (TR * TC / 128) * p;
+            const int col = idx / RBS, rbk = idx % RBS;
             const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
             if (c < C && r < R) {
                 // non-temporal: the codes are not read again by this pass (21.9 against 22.4 us)
@@ -764,7 +866,7 @@ __global__ __launch_bounds__(NTHREADS) void mxfp8_kernel(MxArgs a) {
                                             (u32v4*)(a.col_codes + (a.slab ? slab_offset(c, r, C, R) : c * R + r)));
             }
         }
-        store_col_scales<32>(&lds_sc[0][0], a.col_scales, R, C, tr0, tc0);
+        store_col_scales<32, TR, TC>(&lds_sc[0][0], a.col_scales, R, C, tr0, tc0);
     }
 }
 
@@ -1153,6 +1255,14 @@ static inline unsigned lin_grid(int64_t n16) {
 
 // ------------------------------------------------------------------ launchers
 
+// MXFP8 cast tiles from bf16: columnwise alone 512 x 256 (1024 threads), rowwise + columnwise
+// MX_TR3 x MX_TC3; a 1-D grid of one workgroup per tile.
+constexpr int MX_TR = 512, MX_TC = 256, MX_TR3 = 512, MX_TC3 = 256;
+template <int TR, int TC>
+static inline unsigned mx_tiles(int64_t R, int64_t C) {
+    return (unsigned)(((C + TC - 1) / TC) * ((R + TR - 1) / TR));
+}
+
 static inline dim3 tile_grid(int64_t R, int64_t C) {
     return dim3((unsigned)((C + TILE_C - 1) / TILE_C), (unsigned)((R + TILE_R - 1) / TILE_R), 1);
 }
@@ -1341,7 +1451,6 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
     const int slab = (direction & 4) != 0;
     direction &= 3;
     MxArgs a{(const uint16_t*)x, nullptr, nullptr, nullptr, R, C, row_codes, row_scales, col_codes, col_scales, slab};
-    const dim3 g = tile_grid(R, C);
     if (direction == 1) {
         const int64_t n16 = R * C / 8;
         const double inv_c8 = 8.0 / (double)C;
@@ -1351,8 +1460,12 @@ int launch_mxfp8_quantize(const void* x, int64_t R, int64_t C, int direction, ui
         else
             hipLaunchKernelGGL(mxfp8_row_linear_kernel<false>, dim3(lin_grid(n16)), dim3(LIN_THREADS), 0, s,
                                (const uint4*)x, n16, (uint2*)row_codes, row_scales, R, C, inv_c8);
-    } else if (direction == 2) hipLaunchKernelGGL(mxfp8_kernel<2>, g, dim3(NTHREADS), 0, s, a);
-    else hipLaunchKernelGGL(mxfp8_kernel<3>, g, dim3(NTHREADS), 0, s, a);
+    } else {
+        const dim3 g(mx_tiles<MX_TR, MX_TC>(R, C));
+        if (direction == 2) hipLaunchKernelGGL((mxfp8_kernel<2, 0, MX_TR, MX_TC>), g, dim3(MX_TR * MX_TC / 128), 0, s, a);
+        else hipLaunchKernelGGL((mxfp8_kernel<3, 0, MX_TR3, MX_TC3>), dim3(mx_tiles<MX_TR3, MX_TC3>(R, C)),
+                                dim3(MX_TR3 * MX_TC3 / 128), 0, s, a);
+    }
     return (int)hipGetLastError();
 }
 
@@ -1364,10 +1477,10 @@ int launch_mxfp8_requantize_nvfp4(const uint8_t* codes, const uint8_t* scales, c
     const int slab = (direction & 4) != 0;
     direction &= 3;
     MxArgs a{nullptr, codes, scales, s_enc, R, C, row_codes, row_scales, col_codes, col_scales, slab};
-    const dim3 g = tile_grid(R, C);
-    if (direction == 1) hipLaunchKernelGGL((mxfp8_kernel<1, 1>), g, dim3(NTHREADS), 0, s, a);
-    else if (direction == 2) hipLaunchKernelGGL((mxfp8_kernel<2, 1>), g, dim3(NTHREADS), 0, s, a);
-    else hipLaunchKernelGGL((mxfp8_kernel<3, 1>), g, dim3(NTHREADS), 0, s, a);
+    const dim3 g(mx_tiles<TILE_R, TILE_C>(R, C));
+    if (direction == 1) hipLaunchKernelGGL((mxfp8_kernel<1, 1, TILE_R, TILE_C>), g, dim3(NTHREADS), 0, s, a);
+    else if (direction == 2) hipLaunchKernelGGL((mxfp8_kernel<2, 1, TILE_R, TILE_C>), g, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((mxfp8_kernel<3, 1, TILE_R, TILE_C>), g, dim3(NTHREADS), 0, s, a);
     return (int)hipGetLastError();
 }
 

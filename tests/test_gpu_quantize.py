@@ -343,6 +343,43 @@ def test_mxfp8_extreme_and_zero_blocks():
     check_mxfp8(v.to(torch.bfloat16), 3, label="extreme")
 
 
+def block_edge_bf16(R, C, seed):
+    """bf16 [R, C] whose columnwise 32-blocks sit on the MXFP8 encoder's edges: each block's amax
+    has a random exponent field in 9..254 and a mantissa that is random or one of the saturation
+    edges (448, just below / at / above 464, and 511 after scaling); the other elements are bit
+    patterns at most the amax (half uniform, so bf16 subnormals and zeros occur, half within 40
+    patterns of it), with random signs.  The first 64 rows of columns 128..255 also hold blocks
+    whose scale byte is 0 (all zero with -0 entries, or amax exponent 0..8), so that waves with
+    and without such blocks meet in one launch."""
+    g = np.random.default_rng(seed)
+    nb = R // 32
+    exp = g.integers(9, 255, size=(nb, C))
+    mant = g.integers(0, 128, size=(nb, C))
+    pick = g.random((nb, C)) < 0.5
+    mant[pick] = g.choice([0x60, 0x67, 0x68, 0x69, 0x7F], size=int(pick.sum()))
+    amax = (exp << 7) | mant
+    if C > 128:
+        amax[0, 130:132] = 0
+        amax[1, 140:144] = g.integers(0, 9, size=4) << 7 | g.integers(0, 128, size=4)
+    amax3 = amax[:, None, :]
+    u = g.random((nb, 32, C))
+    near = g.random((nb, 32, C)) < 0.5
+    mag = np.where(near, amax3 - np.floor(u * 41), np.floor(u * (amax3 + 1))).astype(np.int64)
+    mag = np.clip(mag, 0, amax3)
+    at = g.integers(0, 32, size=(nb, C))
+    mag[np.arange(nb)[:, None], at, np.arange(C)[None, :]] = amax
+    sign = (g.random((nb, 32, C)) < 0.5).astype(np.int64)
+    bits = (mag | (sign << 15)).astype(np.uint16).reshape(R, C)
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("shape", [(512, 256), (288, 160)])
+def test_mxfp8_block_edges(shape):
+    x = block_edge_bf16(*shape, seed=61)
+    for direction in (2, 3):
+        check_mxfp8(x, direction, label="block-edges")
+
+
 def test_rht_apply_matches_oracle():
     import oracle
     for axis in (0, 1):
