@@ -309,6 +309,32 @@ __device__ __forceinline__ uint32_t fp8x4_scaled(uint32_t a, uint32_t b, float s
     return __builtin_bit_cast(uint32_t, o);
 }
 
+// Packed MXFP8 rowwise encode of an 8-element unit w[0..3] (bf16 pairs of one row) whose 32-block
+// spans the 4 lanes of an aligned quad: the same codes and scale byte as the binary32 form.  The
+// block amax is a 16-bit unsigned maximum over magnitude bits (within the unit, across its two
+// halves, then across the quad by DPP); the clamp to 448 * 2^X and the scaled conversion are the
+// columnwise encoder's.  Returns false, for every lane of the wave, when some block of the wave
+// has scale byte 0 (amax exponent field <= 8, all-zero blocks included): the caller then takes the
+// binary32 form.  The lanes of a quad are all active or all inactive (an inactive lane adds
+// nothing: DPP reads from it return 0 and the ballot skips it).
+__device__ __forceinline__ bool mx_row_unit_packed(const uint32_t w[4], uint32_t& lo, uint32_t& hi, uint32_t& sb) {
+    uint32_t M = pk_max_u16(pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
+                            pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
+    M = pk_max_u16(M, __builtin_amdgcn_alignbit(M, M, 16));   // both halves: the unit's amax
+    M = pk_max_u16(M, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)M, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    M = pk_max_u16(M, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)M, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    if (__builtin_amdgcn_ballot_w64((M & 0xFFFFu) < 0x480u) != 0) return false;   // wave-uniform
+    const uint32_t T = (M & 0x7F807F80u) | 0x00600060u, T2 = T | 0x80008000u;
+    sb = ((M >> 7) & 0xFFu) - 8u;
+    const float s = __uint_as_float(sb << 23);
+    uint32_t z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = pk_min_u16(pk_min_i16(w[i], T), T2);
+    lo = fp8x4_scaled(z[0], z[1], s);
+    hi = fp8x4_scaled(z[2], z[3], s);
+    return true;
+}
+
 // Byte offset of code (r, k) of a [rows][K] code matrix in the slab layout: rows in bands of
 // 256 (the last band holds the rest), band b at byte 256 b K, holding its n rows as K/64
 // consecutive slabs of n x 64 bytes (K a multiple of 64).  A GEMM tile's rows are one band,
@@ -332,19 +358,22 @@ __device__ __forceinline__ void mx_row_tile(const SubTile& q, const TileCoord& t
     static_for<0, 16>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         const int64_t r = t.r0 + j;
-        float v[8];
-        row_of(q, j, v);
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
-        m = __builtin_fmaxf(m, __shfl_xor(m, 1));
-        m = __builtin_fmaxf(m, __shfl_xor(m, 2));
         uint32_t lo = 0, hi = 0, sb = 0;
-        if (m != 0.0f) {
-            sb = mx_scale_byte(m);
-            const float inv = mx_inv_scale(sb);
-            lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-            hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        if (!mx_row_unit_packed(q[j], lo, hi, sb)) {
+            float v[8];
+            row_of(q, j, v);
+            float m = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            m = __builtin_fmaxf(m, __shfl_xor(m, 2));
+            lo = hi = sb = 0;
+            if (m != 0.0f) {
+                sb = mx_scale_byte(m);
+                const float inv = mx_inv_scale(sb);
+                lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+                hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+            }
         }
         if (colok && r < R) {
             *(uint2*)(code0 + j * pitch) = make_uint2(lo, hi);
@@ -1215,19 +1244,23 @@ __global__ __launch_bounds__(LIN_THREADS) void mxfp8_row_linear_kernel(const uin
 #pragma unroll
         for (int k = 0; k < LIN_UNITS; ++k) {
             const int64_t u = base + (int64_t)k * LIN_THREADS;
-            float v[8];
-            unpack_bf16x8(q[k], v);
-            float m = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 2));
             uint32_t lo = 0, hi = 0, sb = 0;
-            if (m != 0.0f) {
-                sb = mx_scale_byte(m);
-                const float inv = mx_inv_scale(sb);
-                lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-                hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+            const uint32_t wk[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+            if (!mx_row_unit_packed(wk, lo, hi, sb)) {
+                float v[8];
+                unpack_bf16x8(q[k], v);
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+                m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+                m = __builtin_fmaxf(m, __shfl_xor(m, 2));
+                lo = hi = sb = 0;
+                if (m != 0.0f) {
+                    sb = mx_scale_byte(m);
+                    const float inv = mx_inv_scale(sb);
+                    lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+                    hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+                }
             }
             if (u < n16) {
                 int64_t at = u;
