@@ -654,14 +654,15 @@ __device__ __forceinline__ void load_subtile_nvfp4(const uint8_t* __restrict__ c
 
 // The workgroup's 256 x 128 tile of an NVFP4 rowwise tensor staged in LDS: codes (64 bytes a
 // row; row r at LDS row r ^ ((r >> 4) & 3), so that the four rows a wave reads together, 16
-// apart, fall on different banks), scale bytes (8 a row), and the two dequantization
-// quotients of every scale byte (load_subtile_nvfp4's qa, qb as bf16, and whether the
-// exponent-step shortcut holds), computed once per workgroup instead of once per thread row.
+// apart, fall on different banks), scale bytes (8 a row), and for every scale byte s the bf16
+// bits of the eight non-negative codes' dequantized values, nvfp4_dequant_bf16(m, fp32(s), S)
+// for m = 0..7, as byte tables (lut[s] = low bytes of m = 0..3, of m = 4..7, high bytes of
+// m = 0..3, of m = 4..7), built once per workgroup.  A negative code's value is the same bits
+// with the sign set (the rounding is symmetric; code 8 gives -0).
 struct NvTileLds {
     uint4 codes[TILE_R][4];
     uint2 scales[TILE_R];
-    uint32_t ab[128];   // bf16(qa) | bf16(qb) << 16 for scale byte s (bit 7 ignored)
-    uint32_t ok[4];     // bit s: qa and qb both in the shortcut's exponent range
+    uint4 lut[128];   // scale byte s (bit 7 ignored)
 };
 
 // Stage the tile (tr0, tc0) of codes [R][C/2] and scales [R][C/16] (C % 32 == 0, so each
@@ -699,49 +700,43 @@ __device__ __forceinline__ void stage_nvfp4_tile(const uint8_t* __restrict__ cod
         }
         L.scales[tid] = make_uint2(lo, hi);
     }
-    if (tid < 128) {
-        const float sc = e4m3_decode_nonneg((uint32_t)tid);
-        const float qa = (0.5f * sc) / S, qb = (1.5f * sc) / S;
-        const uint32_t ea = __float_as_uint(qa) >> 23, eb = __float_as_uint(qb) >> 23;
-        const bool ok = ea - 1u < 250u && eb - 1u < 250u;
-        L.ab[tid] = f32_to_bf16_rne(qa) | (f32_to_bf16_rne(qb) << 16);
-        const uint64_t m = __ballot(ok);
-        if ((tid & 63) == 0) {
-            L.ok[2 * (tid >> 6)] = (uint32_t)m;
-            L.ok[2 * (tid >> 6) + 1] = (uint32_t)(m >> 32);
+    {   // thread (s, half): codes 4 half .. 4 half + 3 of scale byte s
+        static_assert(NTHREADS == 256, "two threads per scale byte");
+        const int sbyte = tid >> 1, half = tid & 1;
+        const float sc = e4m3_decode_nonneg((uint32_t)sbyte);
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = nvfp4_dequant_bf16((uint32_t)(4 * half + i), sc, S);
+            lo |= (v & 0xFFu) << (8 * i);
+            hi |= (v >> 8) << (8 * i);
         }
+        uint32_t* w = (uint32_t*)&L.lut[sbyte];
+        w[half] = lo;
+        w[2 + half] = hi;
     }
     __syncthreads();
 }
 
-// load_subtile_nvfp4 from the staged tile: the same values, bit for bit.
-__device__ __forceinline__ void load_subtile_nvfp4_lds(const NvTileLds& L, float S, const TileCoord& t,
-                                                       SubTile q) {
+// load_subtile_nvfp4 from the staged tile: the same values, bit for bit.  Per row, the code word
+// is split into its even and odd codes; per bf16 pair, v_perm_b32 gathers the pair's codes into
+// the two halves, two more look up the low and high bytes of their magnitudes in the row's
+// scale table, a fourth interleaves them, and the code's sign bit is moved to bit 15.
+__device__ __forceinline__ void load_subtile_nvfp4_lds(const NvTileLds& L, const TileCoord& t, SubTile q) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int lr = 16 * t.rb + j;
         const uint32_t cw = ((const uint32_t*)&L.codes[lr ^ ((lr >> 4) & 3)][0])[t.cc];
         const uint32_t sbyte = (((t.cc >> 1) < 4 ? L.scales[lr].x : L.scales[lr].y) >> (8 * ((t.cc >> 1) & 3))) & 0x7Fu;
-        if ((L.ok[sbyte >> 5] >> (sbyte & 31)) & 1u) {
-            const uint32_t ab = L.ab[sbyte];
-            const uint32_t ba = ab & 0xFFFFu, bb = ab >> 16;
-            auto deq = [&](uint32_t c) {
-                const uint32_t m = c & 7u;
-                const uint32_t k = (0x23120100u >> (4u * m)) & 0xFu;
-                const uint32_t base = ((0xA8u >> m) & 1u) ? bb : ba;
-                const uint32_t mag = m ? base + (k << 7) : 0u;
-                return mag | ((c & 8u) << 12);
-            };
+        const uint4 T = L.lut[sbyte];
+        const uint32_t even = cw & 0x0F0F0F0Fu, odd = (cw >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) q[j][w] = deq((cw >> (8 * w)) & 0xFu) | (deq((cw >> (8 * w + 4)) & 0xFu) << 16);
-        } else {
-            const float sc = e4m3_decode_nonneg(sbyte);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t lo = nvfp4_dequant_bf16((cw >> (8 * w)) & 0xFu, sc, S);
-                const uint32_t hi = nvfp4_dequant_bf16((cw >> (8 * w + 4)) & 0xFu, sc, S);
-                q[j][w] = lo | (hi << 16);
-            }
+        for (int w = 0; w < 4; ++w) {
+            // halves: code 2w (byte w of even), code 2w + 1 (byte w of odd); selector 12 gives 0
+            const uint32_t c = __builtin_amdgcn_perm(odd, even, 0x0C000C00u | ((4u + w) << 16) | (uint32_t)w);
+            const uint32_t sel = c & 0x00070007u;
+            const uint32_t lo = __builtin_amdgcn_perm(T.y, T.x, sel), hi = __builtin_amdgcn_perm(T.w, T.z, sel);
+            q[j][w] = __builtin_amdgcn_perm(hi, lo, 0x06020400u) | ((c << 12) & 0x80008000u);
         }
     }
 }
@@ -804,7 +799,7 @@ __global__ __launch_bounds__(TR * TC / 128) void mxfp8_kernel(MxArgs a) {
         if (C % 32 == 0) {   // uniform: 16-byte code chunks, staged through LDS
             __shared__ NvTileLds stage;
             stage_nvfp4_tile(a.nv_codes, a.nv_scales, S, R, C, tr0, tc0, stage);
-            load_subtile_nvfp4_lds(stage, S, t, q);
+            load_subtile_nvfp4_lds(stage, t, q);
         } else {
             load_subtile_nvfp4(a.nv_codes, a.nv_scales, S, R, C, t, q);
         }
