@@ -344,37 +344,69 @@ __device__ __forceinline__ int64_t slab_offset(int64_t r, int64_t k, int64_t row
     return (b << 8) * K + (k >> 6) * n * 64 + (r & 255) * 64 + (k & 63);
 }
 
-// MXFP8 rowwise cast of a thread's 16 x 8 sub-tile: 32-blocks along the row span the 4
-// lanes cc .. cc+3; codes (8 bytes per row) go to the row-major or slab-layout code matrix and
-// each block's scale byte to its row of the scale matrix.
+// MXFP8 rowwise cast of a thread's 16 x 8 sub-tile of a TR-row tile: 32-blocks along the row
+// span the 4 lanes cc .. cc+3; codes (8 bytes per row) go to the row-major or slab-layout code
+// matrix and each block's scale byte to its row of the scale matrix.  The tile's rows of either
+// matrix are one contiguous range (slab bands are 256 rows and tiles start on a band), so the
+// stores go through buffer resources over it: a thread steps a 32-bit offset by the row pitch,
+// and rows past R fall outside the range and are dropped -- except slab rows in a partial last
+// band, whose offsets would land in the band's next slab and are dropped explicitly.  Tensors
+// whose tile spans 2^31 bytes or more (C TR >= 2^31) take 64-bit addresses instead.
+template <int TR>
 __device__ __forceinline__ void mx_row_tile(const SubTile& q, const TileCoord& t, int64_t R, int64_t C,
                                             uint8_t* row_codes, uint8_t* row_scales, int slab) {
     const bool colok = t.c0 < C;
+    auto encode_row = [&](int j, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
+        if (mx_row_unit_packed(q[j], lo, hi, sb)) return;
+        float v[8];
+        row_of(q, j, v);
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+        m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+        m = __builtin_fmaxf(m, __shfl_xor(m, 2));
+        lo = hi = sb = 0;
+        if (m != 0.0f) {
+            sb = mx_scale_byte(m);
+            const float inv = mx_inv_scale(sb);
+            lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        }
+    };
     // the sub-tile's 16 rows lie in one 256-row band (r0 is a multiple of 16), so in either
     // layout row r0 + j's codes sit j row pitches (64 bytes in a slab, C row-major) after row r0's
-    uint8_t* code0 = row_codes + (slab ? slab_offset(t.r0, t.c0, R, C) : t.r0 * C + t.c0);
+    const int64_t code_at = slab ? slab_offset(t.r0, t.c0, R, C) : t.r0 * C + t.c0;
+    if (C * TR < ((int64_t)1 << 31)) {   // uniform
+        typedef unsigned int u32v2_t __attribute__((ext_vector_type(2)));
+        const int64_t row0 = t.r0 - 16 * t.rb;   // the tile's first row
+        const int64_t rows = (R - row0) < TR ? (R - row0) : TR;
+        const __amdgpu_buffer_rsrc_t rc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(row_codes + row0 * C), (short)0, (int)(rows * C), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(row_scales + row0 * (C / 32)), (short)0, (int)(rows * (C / 32)), 0x00020000);
+        const uint32_t oc = colok ? (uint32_t)(code_at - row0 * C) : 0x80000000u;
+        const uint32_t os = (colok && (t.cc & 3) == 0) ? (uint32_t)((t.r0 - row0) * (C / 32) + t.c0 / 32) : 0x80000000u;
+        const uint32_t pc = slab ? 64u : (uint32_t)C, ps = (uint32_t)(C / 32);
+        const bool cut = slab && rows < TR;   // uniform
+        static_for<0, 16>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            uint32_t lo, hi, sb;
+            encode_row(j, lo, hi, sb);
+            uint32_t ocj = oc + (uint32_t)j * pc;
+            if (cut && t.r0 + j >= R) ocj = 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b64(u32v2_t{lo, hi}, rc, (int)ocj, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sb, rs, (int)(os + (uint32_t)j * ps), 0, 0);
+        });
+        return;
+    }
+    uint8_t* code0 = row_codes + code_at;
     const int64_t pitch = slab ? 64 : C;
     uint8_t* scale0 = row_scales + t.r0 * (C / 32) + t.c0 / 32;
     static_for<0, 16>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         const int64_t r = t.r0 + j;
-        uint32_t lo = 0, hi = 0, sb = 0;
-        if (!mx_row_unit_packed(q[j], lo, hi, sb)) {
-            float v[8];
-            row_of(q, j, v);
-            float m = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 2));
-            lo = hi = sb = 0;
-            if (m != 0.0f) {
-                sb = mx_scale_byte(m);
-                const float inv = mx_inv_scale(sb);
-                lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-                hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-            }
-        }
+        uint32_t lo, hi, sb;
+        encode_row(j, lo, hi, sb);
         if (colok && r < R) {
             *(uint2*)(code0 + j * pitch) = make_uint2(lo, hi);
             if ((t.cc & 3) == 0) scale0[j * (C / 32)] = (uint8_t)sb;
@@ -504,7 +536,7 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     const int64_t R = a.R, C = a.C;
     SubTile q;
     load_subtile(a.x, R, C, t, q);
-    if constexpr (MXROW) mx_row_tile(q, t, R, C, a.mx_codes, a.mx_scales, a.mx_slab);
+    if constexpr (MXROW) mx_row_tile<TILE_R>(q, t, R, C, a.mx_codes, a.mx_scales, a.mx_slab);
     const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
     const float2 am = parts_max<NTHREADS, DIRS>(a.parts, a.nparts);
     const float Srow = nvfp4_tensor_scale(am.x);
@@ -805,7 +837,7 @@ __global__ __launch_bounds__(TR * TC / 128) void mxfp8_kernel(MxArgs a) {
         }
     }
 
-    if (DIRS & 1) mx_row_tile(q, t, R, C, a.row_codes, a.row_scales, a.slab);
+    if (DIRS & 1) mx_row_tile<TR>(q, t, R, C, a.row_codes, a.row_scales, a.slab);
 
     if (DIRS & 2) {
         // the NVFP4 columnwise transpose's placement: block rb of column 8cc + k at

@@ -380,6 +380,25 @@ def test_mxfp8_block_edges(shape):
         check_mxfp8(x, direction, label="block-edges")
 
 
+@pytest.mark.parametrize("shape", [(576, 64), (832, 128), (1088, 192), (320, 320), (64, 128)])
+def test_mxfp8_both_slab_ragged_bands(shape):
+    """Rowwise + columnwise MXFP8 with both code matrices in the slab layout, on row counts whose
+    512-row tiles end inside a band or span a full band and a partial one (rows past the tensor
+    must not land in the band's next slab), against the oracle's row-major codes."""
+    import oracle
+    from tests.gpu_common import from_slab
+    R, Cc = shape
+    x = outlier_bf16(shape, seed=71, mask_seed=72)
+    note("mxfp8 both slab shape=%s" % (shape,))
+    got = bsq.mxfp8_quantize(x.to(DEV), direction=bsq.ROW | bsq.COL | bsq.MX_SLAB)
+    torch.cuda.synchronize()
+    ref = oracle.mxfp8_quantize(x, direction=3)
+    assert_bytes_equal(got["row_scales"], ref["row_scales"], "row_scales")
+    assert_bytes_equal(got["col_scales"], ref["col_scales"], "col_scales")
+    assert np.array_equal(from_slab(got["row_codes"], R, Cc), ref["row_codes"]), "row codes"
+    assert np.array_equal(from_slab(got["col_codes"], Cc, R), ref["col_codes"]), "col codes"
+
+
 def test_rht_apply_matches_oracle():
     import oracle
     for axis in (0, 1):
