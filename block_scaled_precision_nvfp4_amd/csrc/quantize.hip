@@ -169,10 +169,10 @@ __device__ __forceinline__ void store_parts(float a, float b, float* __restrict_
 
 // Encode pass prologue: the tensor amax of the directions in DIRS, reduced by the whole
 // workgroup (NT threads) from the nparts partial maxima the amax pass stored, returned to
-// every thread.  Contains barriers: every thread must call it.
+// every thread.  parts_load gives a thread's share (so that a kernel can issue its own loads
+// before the reduction waits on it); parts_reduce contains barriers: every thread must call it.
 template <int NT, int DIRS>
-__device__ __forceinline__ float2 parts_max(const float* __restrict__ parts, int nparts) {
-    __shared__ float red[2][NT / 64];
+__device__ __forceinline__ float2 parts_load(const float* __restrict__ parts, int nparts) {
     float a = 0.0f, b = 0.0f;
 #pragma unroll
     for (int k = 0; k < (AMAX_PARTS + NT - 1) / NT; ++k) {
@@ -182,6 +182,13 @@ __device__ __forceinline__ float2 parts_max(const float* __restrict__ parts, int
             if (DIRS & 2) b = __builtin_fmaxf(b, parts[AMAX_PARTS + i]);
         }
     }
+    return make_float2(a, b);
+}
+
+template <int NT, int DIRS>
+__device__ __forceinline__ float2 parts_reduce(float2 mine) {
+    __shared__ float red[2][NT / 64];
+    float a = mine.x, b = mine.y;
     a = wave_max(a);
     b = wave_max(b);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -198,6 +205,18 @@ __device__ __forceinline__ float2 parts_max(const float* __restrict__ parts, int
         b = __builtin_fmaxf(b, red[1][w]);
     }
     return make_float2(a, b);
+}
+
+template <int NT, int DIRS>
+__device__ __forceinline__ float2 parts_max(const float* __restrict__ parts, int nparts) {
+    return parts_reduce<NT, DIRS>(parts_load<NT, DIRS>(parts, nparts));
+}
+
+// max(m, m of lane ^ 1), the other half of a 16-block, by a DPP quad move (a lane whose
+// partner is inactive keeps its own m).
+__device__ __forceinline__ float pair_max(float m) {
+    const int b = __builtin_bit_cast(int, m);
+    return __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));
 }
 
 // Workgroup 0 of an encode pass publishes amax and S of the directions in DIRS.
@@ -571,7 +590,7 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             float m = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            m = pair_max(m);
             uint32_t w;
             const uint32_t sb = encode_block<8, SR_ROW, RHT_ROW>(v, m, Srow, enc_tab[0],
                                                          (uint64_t)r * (uint64_t)C + (uint64_t)t.c0, a.seed, a.stream,
@@ -1091,7 +1110,19 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
                                                                        uint32_t stream) {
     int64_t first, stride;
     lin_range(n16, first, stride);
-    const float2 am = parts_max<LIN_THREADS, 1>(parts, nparts);
+    uint4 q[LIN_UNITS];
+    auto load_sweep = [&](int64_t base) {
+#pragma unroll
+        for (int k = 0; k < LIN_UNITS; ++k) {
+            const int64_t u = base + (int64_t)k * LIN_THREADS;
+            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    // the partial maxima, then the first sweep's units: the prologue's reduction and table
+    // build run while the units are in flight
+    const float2 mine = parts_load<LIN_THREADS, 1>(parts, nparts);
+    load_sweep(first);
+    const float2 am = parts_reduce<LIN_THREADS, 1>(mine);
     const float S = nvfp4_tensor_scale(am.x);
     publish_scales<1>(am, amax_out, s_enc_out);
     __shared__ float enc_tab[128];
@@ -1103,12 +1134,7 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
 #pragma unroll
     for (int w = 0; w < 4; ++w) sw[w] = RHT ? row_sign_word(neg, upper, w) : 0u;
     for (int64_t base = first; base < n16; base += stride) {
-        uint4 q[LIN_UNITS];
-#pragma unroll
-        for (int k = 0; k < LIN_UNITS; ++k) {
-            const int64_t u = base + (int64_t)k * LIN_THREADS;
-            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
-        }
+        if (base != first) load_sweep(base);
 #pragma unroll
         for (int k = 0; k < LIN_UNITS; ++k) {
             const int64_t u = base + (int64_t)k * LIN_THREADS;
@@ -1122,7 +1148,7 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
             float m = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
-            m = __builtin_fmaxf(m, __shfl_xor(m, 1));
+            m = pair_max(m);
             uint32_t w;
             const uint32_t sb = encode_block<8, SR, RHT>(v, m, S, enc_tab, (uint64_t)u * 8u, seed, stream, 0u, &w);
             if (u < n16) {
