@@ -1053,7 +1053,11 @@ __global__ __launch_bounds__(LIN_THREADS) void amax_linear_kernel(const uint4* _
 #pragma unroll
         for (int k = 0; k < LIN_UNITS; ++k) {
             const int64_t u = base + (int64_t)k * LIN_THREADS;
-            q[k] = u < n16 ? load16_stream(x + u) : make_uint4(0, 0, 0, 0);
+            // Before a columnwise (tile) encode the loads are temporal, so that the tensor can
+            // stay in the memory-side cache for the encode's second read (measured: that encode
+            // 13-15 % faster on 64-134 MB tensors, this pass ~4 % slower); before the streaming
+            // rowwise encode, which gained nothing from it, they stay non-temporal.
+            q[k] = u < n16 ? (DIRS == 1 ? load16_stream(x + u) : x[u]) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < LIN_UNITS; ++k) {
