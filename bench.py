@@ -268,32 +268,41 @@ def quant_only_figures(dev, peaks, iters: int = 10):
         "mxfp8_col": (lambda x: bsq.mxfp8_quantize(x, direction=bsq.COL), 2.0 + 1.03125),
     }
     out = {"shape": [R, C]}
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # A cast of this size runs ~20-30 us, less than the binding's host work per call (output
-    # allocation and argument marshalling), so back-to-back calls would time the host.  A spin
-    # kernel queued first holds the stream until every timed launch is enqueued: the events
-    # then bracket the kernels alone.
-    torch.cuda._sleep(1 << 20)
-    e0.record()
-    torch.cuda._sleep(1 << 24)
-    e1.record()
-    torch.cuda.synchronize()
-    cycles_per_ms = (1 << 24) / max(e0.elapsed_time(e1), 1e-3)
-    backlog = int(cycles_per_ms * max(5.0, 0.25 * iters))
     for name, (fn, bpe) in cases.items():
-        fn(xs[0])
-        torch.cuda.synchronize()
-        torch.cuda._sleep(backlog)
-        e0.record()
-        for i in range(iters):
-            fn(xs[i % 4])
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / iters * 1e3
+        us = spin_timed_us(torch, lambda i: fn(xs[i % 4]), iters)
         gbps = bpe * n / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "GBps": round(gbps, 1), "of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
                      "of_measured_copy": round(gbps / peaks["copy_GBps"], 4)}
     return out
+
+
+_SPIN_CYCLES_PER_MS = []
+
+
+def spin_timed_us(torch, fn, iters: int) -> float:
+    """Mean us per launch of ``fn(i)``, i = 0 .. iters-1, with the host's work kept out of the
+    timed region.  A cast of ~20-50 us runs shorter than the binding's host work per call (output
+    allocation and argument marshalling), so back-to-back calls would time the host: a spin
+    kernel queued first holds the stream until every timed launch is enqueued, and the events
+    then bracket the kernels alone."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not _SPIN_CYCLES_PER_MS:
+        torch.cuda._sleep(1 << 20)
+        e0.record()
+        torch.cuda._sleep(1 << 24)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS.append((1 << 24) / max(e0.elapsed_time(e1), 1e-3))
+    backlog = int(_SPIN_CYCLES_PER_MS[0] * max(5.0, 0.25 * iters))
+    fn(0)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(backlog)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e3
 
 
 def timed_ms(torch, fn, iters: int) -> float:
@@ -313,15 +322,21 @@ def timed_ms(torch, fn, iters: int) -> float:
 
 
 def rowscaled_figures(step, iters: int):
-    """Side figures outside the step: row-scaled NVFP4 (one outer scale per row) of X and the
-    forward GEMM with row-scaled X, each timed over ``iters`` back-to-back launches."""
+    """Side figures outside the step: row-scaled NVFP4 (one outer scale per row) of X, timed
+    behind a spin kernel over ``iters`` launches rotating over 4 copies of X (as the
+    quantize-only casts), and the forward GEMM with row-scaled X over ``iters`` back-to-back
+    launches."""
     bsq, torch = step.bsq, step.torch
     qw = bsq.nvfp4_quantize(step.W, direction=bsq.ROW)
     qx = bsq.nvfp4_quantize_rowscaled(step.X)
     fmt = bsq.FMT_NVFP4 | bsq.FMT_A_ROWSCALED
     y = bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"], qw["row_scales"],
                              qw["s_enc"][0:1])
-    q_ms = timed_ms(torch, lambda: bsq.nvfp4_quantize_rowscaled(step.X), iters)
+    xs = [step.X] + [step.X.clone() for _ in range(3)]
+    for i in range(iters):   # bring the shader clock up, as timed_ms does
+        bsq.nvfp4_quantize_rowscaled(xs[i % 4])
+    q_ms = spin_timed_us(torch, lambda i: bsq.nvfp4_quantize_rowscaled(xs[i % 4]), iters) * 1e-3
+    del xs
     g_ms = timed_ms(torch, lambda: bsq.blockscaled_gemm(fmt, qx["codes"], qx["scales"], qx["s_enc"], qw["row_codes"],
                                                         qw["row_scales"], qw["s_enc"][0:1], out=y), iters)
     q_bytes = M_TOK * K_IN * NVFP4_BYTES_PER_ELT + 8.0 * M_TOK   # + amax and S per row

@@ -219,6 +219,35 @@ __device__ __forceinline__ float pair_max(float m) {
     return __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));
 }
 
+// Maximum of m over aligned groups of 2^lg lanes (1 <= lg <= 6, uniform), returned to every lane
+// of the group, without LDS traffic: DPP quad moves (lane ^ 1, lane ^ 2), the half-row and row
+// mirrors (which, once quads agree, pair each quad with the other quad of its 8 and each 8 with
+// the other 8 of its row of 16), then v_permlane16_swap and v_permlane32_swap across rows.
+// Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float m) {
+    const int b = __builtin_bit_cast(int, m);
+    return __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ float group_max_dpp(float m, int lg) {
+    m = dpp_max_step<0xB1>(m);                 // quad_perm [1, 0, 3, 2]
+    if (lg >= 2) m = dpp_max_step<0x4E>(m);    // quad_perm [2, 3, 0, 1]
+    if (lg >= 3) m = dpp_max_step<0x141>(m);   // row_half_mirror
+    if (lg >= 4) m = dpp_max_step<0x140>(m);   // row_mirror
+    if (lg >= 5) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, m);
+        const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+    }
+    if (lg >= 6) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, m);
+        const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+    }
+    return m;
+}
+
 // Workgroup 0 of an encode pass publishes amax and S of the directions in DIRS.
 template <int DIRS>
 __device__ __forceinline__ void publish_scales(float2 am, float* amax_out, float* s_enc_out) {
@@ -1243,7 +1272,7 @@ __global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4
             }
         }
         // row amax: across the group's lanes, then across its waves
-        for (int o = 1; o < T && o < 64; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+        m = group_max_dpp(m, lgt < 6 ? lgt : 6);
         if (T > 64) {
             if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
             __syncthreads();
@@ -1268,7 +1297,7 @@ __global__ __launch_bounds__(RS_THREADS) void nvfp4_rowscaled_kernel(const uint4
                 const int64_t u = c0 + sub + (int64_t)T * k;
                 float v[8];
                 float bm = values(k, v);
-                bm = __builtin_fmaxf(bm, __shfl_xor(bm, 1));
+                bm = pair_max(bm);
                 uint32_t w;
                 const uint32_t sb = encode_block<8, SR, false>(v, bm, S, nullptr, (uint64_t)(base + u) * 8u, seed, stream,
                                                                0u, &w);
