@@ -599,10 +599,12 @@ def main():
     dy_bytes = (NVFP4_BYTES_PER_ELT + 1.03125) * M_TOK * N_OUT
     # the metric's quantization half: the forward operands alone, NVFP4 rowwise RNE of X and W
     # as two plain calls (the step makes X's rowwise operand together with its columnwise one)
+    # (timed behind a spin kernel: two binding calls cost about as much host time as their ~90 us
+    # of kernels, so back-to-back timing could measure the host)
     ws = step.qws
-    rne_ms = timed_ms(torch, lambda: (bsq.nvfp4_quantize(step.X, direction=bsq.ROW, workspace=ws),
-                                      bsq.nvfp4_quantize(step.W, direction=bsq.ROW, workspace=ws)),
-                      max(4, args.steps))
+    rne_ms = spin_timed_us(torch, lambda i: (bsq.nvfp4_quantize(step.X, direction=bsq.ROW, workspace=ws),
+                                             bsq.nvfp4_quantize(step.W, direction=bsq.ROW, workspace=ws)),
+                           max(4, args.steps)) * 1e-3
     rne_bytes = NVFP4_BYTES_PER_ELT * (M_TOK + N_OUT) * K_IN
     peaks = measured_peaks(dev)
     side = moe = layer = qwen = quant_only = odd_k = None
