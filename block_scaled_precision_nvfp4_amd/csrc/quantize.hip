@@ -598,9 +598,20 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
 
     if (DIRS & 1) {
         const bool upper = (t.cc & 1) != 0;
-        // row r0 + j's code word and scale byte, j row pitches after row r0's
+        // row r0 + j's code word and scale byte, j row pitches after row r0's.  Where the tile's
+        // rows of codes span less than 2^31 bytes they are stored through buffer resources over
+        // those rows: a 32-bit offset per row, rows past R dropped by the range check.
         uint8_t* code0 = a.row_codes + t.r0 * (C / 2) + t.c0 / 2;
         uint8_t* scale0 = a.row_scales + t.r0 * (C / 16) + t.c0 / 16;
+        const bool rsrc_ok = C * TILE_R < ((int64_t)1 << 32);   // uniform
+        const int64_t row0 = t.r0 - 16 * t.rb;                  // the tile's first row
+        const int64_t rows = (R - row0) < TILE_R ? (R - row0) : TILE_R;
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.row_codes + row0 * (C / 2)), (short)0, rsrc_ok ? (int)(rows * (C / 2)) : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.row_scales + row0 * (C / 16)), (short)0, rsrc_ok ? (int)(rows * (C / 16)) : 0, 0x00020000);
+        const uint32_t oc = colok ? (uint32_t)(16 * t.rb * (C / 2) + t.c0 / 2) : 0x80000000u;
+        const uint32_t os = (colok && !upper) ? (uint32_t)(16 * t.rb * (C / 16) + t.c0 / 16) : 0x80000000u;
         static_for<0, 16>([&](auto j_c) {
             constexpr int j = decltype(j_c)::value;
             const int64_t r = t.r0 + j;
@@ -624,7 +635,10 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
             const uint32_t sb = encode_block<8, SR_ROW, RHT_ROW>(v, m, Srow, enc_tab[0],
                                                          (uint64_t)r * (uint64_t)C + (uint64_t)t.c0, a.seed, a.stream,
                                                          0u, &w);
-            if (colok && r < R) {
+            if (rsrc_ok) {
+                __builtin_amdgcn_raw_buffer_store_b32(w, rc, (int)(oc + (uint32_t)j * (uint32_t)(C / 2)), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sb, rs, (int)(os + (uint32_t)j * (uint32_t)(C / 16)), 0, 0);
+            } else if (colok && r < R) {
                 *(uint32_t*)(code0 + j * (C / 2)) = w;
                 if (!upper) scale0[j * (C / 16)] = (uint8_t)sb;
             }
