@@ -435,8 +435,9 @@ def test_quant_only_workload():
 
 def test_beyond_2g_elements():
     """A [131088, 16384] tensor (2^31 + 2^18 elements, input byte offsets past 2^32): NVFP4
-    rowwise RNE, MXFP8 rowwise, row-scaled NVFP4, NVFP4 columnwise RNE with RHT, and the
-    two one-pass casts (NVFP4 columnwise + MXFP8 rowwise; NVFP4 rowwise + columnwise).
+    rowwise RNE, MXFP8 rowwise, row-scaled NVFP4, NVFP4 columnwise RNE with RHT, the two
+    one-pass casts (NVFP4 columnwise + MXFP8 rowwise; NVFP4 rowwise + columnwise), and MXFP8
+    columnwise of its first 131072 rows (2^31 elements; MXFP8 columns need rows % 32 == 0).
     The tensor maximum (100, above every N(0,1) draw) is planted at row 0, column 5, so any set of rows containing row 0
     (or of columns containing column 5) has the tensor's scale; rowwise codes depend only on
     their row and that scale, columnwise codes only on their column, so the oracle quantizes
@@ -487,6 +488,10 @@ def test_beyond_2g_elements():
     f_cc, f_cs = fw["col_codes"][cidx].contiguous(), fw["col_scales"][cidx].contiguous()
     f_senc = fw["s_enc"].clone()
     del fw
+    note("rowwise beyond 2^31 elements: MXFP8 columnwise")
+    mc = bsq.mxfp8_quantize(xd[:131072], direction=2)
+    mc_codes, mc_scales = mc["col_codes"][cidx].contiguous(), mc["col_scales"][cidx].contiguous()
+    del mc
     sub_c = xd[:, cidx].cpu().contiguous()
     del xd
     torch.cuda.synchronize()
@@ -518,6 +523,9 @@ def test_beyond_2g_elements():
     assert_bytes_equal(f_rc, ref["row_codes"], "fprop+wgrad row_codes")
     assert_bytes_equal(f_cs, cref["col_scales"], "fprop+wgrad col_scales")
     assert_bytes_equal(f_cc, cref["col_codes"], "fprop+wgrad col_codes")
+    mcref = oracle.mxfp8_quantize(sub_c[:131072].contiguous(), direction=2)   # columns are independent
+    assert_bytes_equal(mc_scales, mcref["col_scales"], "mxfp8 col_scales")
+    assert_bytes_equal(mc_codes, mcref["col_codes"], "mxfp8 col_codes")
 
 
 def test_fwd_operands_llama3_8b():
