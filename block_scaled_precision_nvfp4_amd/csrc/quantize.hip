@@ -676,12 +676,33 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
         __syncthreads();
         const int64_t tr0 = (int64_t)blockIdx.y * TILE_R;
         const int64_t tc0 = (int64_t)blockIdx.x * TILE_C;
+        if (R * TILE_C < ((int64_t)1 << 32)) {   // uniform
+            // the tile's output rows tc0 .. tc0 + 127 of the codes [C][R/2] through a buffer
+            // resource over them: a thread's 8 pieces lie 16 output rows apart (one 32-bit add
+            // each), output rows past C fall outside the range, and a thread whose input rows
+            // lie past R (the same for all 8) stores nothing
+            const int64_t ncols = (C - tc0) < TILE_C ? (C - tc0) : TILE_C;
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a.col_codes + tc0 * (R / 2)), (short)0, (int)(ncols * (R / 2)), 0x00020000);
+            const int col0 = threadIdx.x >> 4, rbk = threadIdx.x & 15;
+            const int64_t r = tr0 + 16 * rbk;
+            const uint32_t off0 = r < R ? (uint32_t)(col0 * (R / 2) + r / 2) : 0x80000000u;
+            const uint32_t step = (uint32_t)(16 * (R / 2));
 #pragma unroll
-        for (int p = 0; p < (TILE_C * TILE_R / 16) / NTHREADS; ++p) {
-            const int idx = threadIdx.x + NTHREADS * p;
-            const int col = idx >> 4, rbk = idx & 15;
-            const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
-            if (c < C && r < R) *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk ^ (col >> 3)];
+            for (int p = 0; p < 8; ++p) {
+                const int col = col0 + 16 * p;
+                const uint2 v = lds_codes[col][rbk ^ (col >> 3)];
+                typedef unsigned int u32v2_t __attribute__((ext_vector_type(2)));
+                __builtin_amdgcn_raw_buffer_store_b64(u32v2_t{v.x, v.y}, rc, (int)(off0 + (uint32_t)p * step), 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < (TILE_C * TILE_R / 16) / NTHREADS; ++p) {
+                const int idx = threadIdx.x + NTHREADS * p;
+                const int col = idx >> 4, rbk = idx & 15;
+                const int64_t c = tc0 + col, r = tr0 + 16 * rbk;
+                if (c < C && r < R) *(uint2*)(a.col_codes + c * (R / 2) + r / 2) = lds_codes[col][rbk ^ (col >> 3)];
+            }
         }
         store_col_scales<16>(&lds_sc[0][0], a.col_scales, R, C, tr0, tc0);
     }
