@@ -122,11 +122,37 @@ __device__ __forceinline__ uint32_t sign_mask16(const int8_t* __restrict__ signs
     return m;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
-    return v;
+// Maximum of m over aligned groups of 2^lg lanes (1 <= lg <= 6, uniform), returned to every lane
+// of the group, without LDS traffic: DPP quad moves (lane ^ 1, lane ^ 2), the half-row and row
+// mirrors (which, once quads agree, pair each quad with the other quad of its 8 and each 8 with
+// the other 8 of its row of 16), then v_permlane16_swap and v_permlane32_swap across rows.
+// Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float m) {
+    const int b = __builtin_bit_cast(int, m);
+    return __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false)));
 }
+
+__device__ __forceinline__ float group_max_dpp(float m, int lg) {
+    m = dpp_max_step<0xB1>(m);                 // quad_perm [1, 0, 3, 2]
+    if (lg >= 2) m = dpp_max_step<0x4E>(m);    // quad_perm [2, 3, 0, 1]
+    if (lg >= 3) m = dpp_max_step<0x141>(m);   // row_half_mirror
+    if (lg >= 4) m = dpp_max_step<0x140>(m);   // row_mirror
+    if (lg >= 5) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, m);
+        const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+    }
+    if (lg >= 6) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, m);
+        const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+    }
+    return m;
+}
+
+// Maximum of v over the wave, returned to every lane (DPP and lane swaps: no LDS round trips).
+__device__ __forceinline__ float wave_max(float v) { return group_max_dpp(v, 6); }
 
 // ------------------------------------------------------------------ per-tensor amax
 
@@ -169,26 +195,42 @@ __device__ __forceinline__ void store_parts(float a, float b, float* __restrict_
 
 // Encode pass prologue: the tensor amax of the directions in DIRS, reduced by the whole
 // workgroup (NT threads) from the nparts partial maxima the amax pass stored, returned to
-// every thread.  parts_load gives a thread's share (so that a kernel can issue its own loads
-// before the reduction waits on it); parts_reduce contains barriers: every thread must call it.
+// every thread.  parts_load issues a thread's share of the loads (slots threadIdx.x + NT k)
+// and returns them unreduced, so that a kernel can issue its own loads behind them before
+// parts_reduce waits; parts_reduce contains barriers: every thread must call it.  The slots
+// are read through buffer resources whose range ends at slot nparts: a slot past it reads as
+// 0, neutral for a maximum of non-negative values, so every load is unconditional and all of
+// them are in flight together (with a branch per slot each load waited for the previous one).
+template <int NT>
+struct PartsShare {
+    uint32_t a[(AMAX_PARTS + NT - 1) / NT], b[(AMAX_PARTS + NT - 1) / NT];
+};
+
 template <int NT, int DIRS>
-__device__ __forceinline__ float2 parts_load(const float* __restrict__ parts, int nparts) {
-    float a = 0.0f, b = 0.0f;
+__device__ __forceinline__ PartsShare<NT> parts_load(const float* __restrict__ parts, int nparts) {
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)parts, (short)0, nparts * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(parts + AMAX_PARTS), (short)0, nparts * 4, 0x00020000);
+    PartsShare<NT> sh;
 #pragma unroll
     for (int k = 0; k < (AMAX_PARTS + NT - 1) / NT; ++k) {
-        const int i = threadIdx.x + NT * k;
-        if (i < nparts) {
-            if (DIRS & 1) a = __builtin_fmaxf(a, parts[i]);
-            if (DIRS & 2) b = __builtin_fmaxf(b, parts[AMAX_PARTS + i]);
-        }
+        const int off = 4 * ((int)threadIdx.x + NT * k);
+        sh.a[k] = (DIRS & 1) ? __builtin_amdgcn_raw_buffer_load_b32(ra, off, 0, 0) : 0u;
+        sh.b[k] = (DIRS & 2) ? __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0) : 0u;
     }
-    return make_float2(a, b);
+    return sh;
 }
 
 template <int NT, int DIRS>
-__device__ __forceinline__ float2 parts_reduce(float2 mine) {
+__device__ __forceinline__ float2 parts_reduce(const PartsShare<NT>& sh) {
     __shared__ float red[2][NT / 64];
-    float a = mine.x, b = mine.y;
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < (AMAX_PARTS + NT - 1) / NT; ++k) {
+        a = __builtin_fmaxf(a, __builtin_bit_cast(float, sh.a[k]));
+        b = __builtin_fmaxf(b, __builtin_bit_cast(float, sh.b[k]));
+    }
     a = wave_max(a);
     b = wave_max(b);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -207,45 +249,11 @@ __device__ __forceinline__ float2 parts_reduce(float2 mine) {
     return make_float2(a, b);
 }
 
-template <int NT, int DIRS>
-__device__ __forceinline__ float2 parts_max(const float* __restrict__ parts, int nparts) {
-    return parts_reduce<NT, DIRS>(parts_load<NT, DIRS>(parts, nparts));
-}
-
 // max(m, m of lane ^ 1), the other half of a 16-block, by a DPP quad move (a lane whose
 // partner is inactive keeps its own m).
 __device__ __forceinline__ float pair_max(float m) {
     const int b = __builtin_bit_cast(int, m);
     return __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));
-}
-
-// Maximum of m over aligned groups of 2^lg lanes (1 <= lg <= 6, uniform), returned to every lane
-// of the group, without LDS traffic: DPP quad moves (lane ^ 1, lane ^ 2), the half-row and row
-// mirrors (which, once quads agree, pair each quad with the other quad of its 8 and each 8 with
-// the other 8 of its row of 16), then v_permlane16_swap and v_permlane32_swap across rows.
-// Every lane of the wave must be active.
-template <int CTRL>
-__device__ __forceinline__ float dpp_max_step(float m) {
-    const int b = __builtin_bit_cast(int, m);
-    return __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false)));
-}
-
-__device__ __forceinline__ float group_max_dpp(float m, int lg) {
-    m = dpp_max_step<0xB1>(m);                 // quad_perm [1, 0, 3, 2]
-    if (lg >= 2) m = dpp_max_step<0x4E>(m);    // quad_perm [2, 3, 0, 1]
-    if (lg >= 3) m = dpp_max_step<0x141>(m);   // row_half_mirror
-    if (lg >= 4) m = dpp_max_step<0x140>(m);   // row_mirror
-    if (lg >= 5) {
-        const uint32_t b = __builtin_bit_cast(uint32_t, m);
-        const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-        m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-    }
-    if (lg >= 6) {
-        const uint32_t b = __builtin_bit_cast(uint32_t, m);
-        const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-        m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-    }
-    return m;
 }
 
 // Workgroup 0 of an encode pass publishes amax and S of the directions in DIRS.
@@ -582,11 +590,13 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     constexpr bool RHT_ROW = RHT && !ROWPLAIN, SR_ROW = SR && !ROWPLAIN;
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
+    // the partial maxima first, then the tile: the prologue's reduction waits for the former only
+    const PartsShare<NTHREADS> parts = parts_load<NTHREADS, DIRS>(a.parts, a.nparts);
     SubTile q;
     load_subtile(a.x, R, C, t, q);
     if constexpr (MXROW) mx_row_tile<TILE_R>(q, t, R, C, a.mx_codes, a.mx_scales, a.mx_slab);
     const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
-    const float2 am = parts_max<NTHREADS, DIRS>(a.parts, a.nparts);
+    const float2 am = parts_reduce<NTHREADS, DIRS>(parts);
     const float Srow = nvfp4_tensor_scale(am.x);
     const float Scol = nvfp4_tensor_scale(am.y);
     publish_scales<DIRS>(am, a.amax_out, a.s_enc_out);
@@ -1226,7 +1236,7 @@ __global__ __launch_bounds__(LIN_THREADS) void nvfp4_row_linear_kernel(const uin
     };
     // the partial maxima, then the first sweep's units: the prologue's reduction and table
     // build run while the units are in flight
-    const float2 mine = parts_load<LIN_THREADS, 1>(parts, nparts);
+    const PartsShare<LIN_THREADS> mine = parts_load<LIN_THREADS, 1>(parts, nparts);
     load_sweep(first);
     const float2 am = parts_reduce<LIN_THREADS, 1>(mine);
     const float S = nvfp4_tensor_scale(am.x);
