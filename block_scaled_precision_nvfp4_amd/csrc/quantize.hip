@@ -590,7 +590,7 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     constexpr bool RHT_ROW = RHT && !ROWPLAIN, SR_ROW = SR && !ROWPLAIN;
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
-    // the partial maxima first, then the tile: the prologue's reduction waits for the former only
+    // the partial maxima are loaded ahead of the tile, so that their reduction needs none of its loads
     const PartsShare<NTHREADS> parts = parts_load<NTHREADS, DIRS>(a.parts, a.nparts);
     SubTile q;
     load_subtile(a.x, R, C, t, q);
