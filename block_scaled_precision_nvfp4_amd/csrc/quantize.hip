@@ -590,10 +590,10 @@ __global__ __launch_bounds__(NTHREADS) void nvfp4_encode_kernel(NvEncodeArgs a) 
     constexpr bool RHT_ROW = RHT && !ROWPLAIN, SR_ROW = SR && !ROWPLAIN;
     const TileCoord t = tile_coord();
     const int64_t R = a.R, C = a.C;
-    // the partial maxima are loaded ahead of the tile, so that their reduction needs none of its loads
-    const PartsShare<NTHREADS> parts = parts_load<NTHREADS, DIRS>(a.parts, a.nparts);
+    // the tile's loads, then the partial maxima's, all in flight together before the first wait
     SubTile q;
     load_subtile(a.x, R, C, t, q);
+    const PartsShare<NTHREADS> parts = parts_load<NTHREADS, DIRS>(a.parts, a.nparts);
     if constexpr (MXROW) mx_row_tile<TILE_R>(q, t, R, C, a.mx_codes, a.mx_scales, a.mx_slab);
     const uint32_t neg = RHT ? sign_mask16(a.signs) : 0u;
     const float2 am = parts_reduce<NTHREADS, DIRS>(parts);
