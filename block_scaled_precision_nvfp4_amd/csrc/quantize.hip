@@ -797,49 +797,73 @@ __device__ __forceinline__ void stage_nvfp4_tile(const uint8_t* __restrict__ cod
                                                  const uint8_t* __restrict__ scales, float S, int64_t R,
                                                  int64_t C, int64_t tr0, int64_t tc0, NvTileLds& L) {
     const int tid = threadIdx.x;
+    // every load of the tile first (four 16-byte code chunks and a row of scale bytes per
+    // thread), so that their latencies overlap; the lookup table is computed while the code
+    // chunks are in flight, and the LDS stores come last
+    uint4 v[4];
+    if (C < ((int64_t)1 << 24)) {   // uniform: the tile's rows of codes span less than 2^31 bytes
+        // through a buffer resource over those rows, with no branch: rows past R lie past its
+        // range and a chunk past C gets an offset beyond it, and both read as zero
+        const int64_t rows = (R - tr0) < TILE_R ? (R - tr0) : TILE_R;
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(codes + tr0 * (C / 2)), (short)0, (int)(rows * (C / 2)), 0x00020000);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int id = tid + NTHREADS * p, row = id >> 2, part = id & 3;
-        const int64_t r = tr0 + row;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < R && tc0 + 32 * part + 32 <= C) v = *(const uint4*)(codes + r * (C / 2) + tc0 / 2 + 16 * part);
-        L.codes[row ^ ((row >> 4) & 3)][part] = v;
+        for (int p = 0; p < 4; ++p) {
+            const int id = tid + NTHREADS * p, row = id >> 2, part = id & 3;
+            const uint32_t off = tc0 + 32 * part + 32 <= C ? (uint32_t)(row * (C / 2) + tc0 / 2 + 16 * part)
+                                                           : 0x80000000u;
+            v[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)off, 0, 0));
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int id = tid + NTHREADS * p, row = id >> 2, part = id & 3;
+            const int64_t r = tr0 + row;
+            v[p] = make_uint4(0u, 0u, 0u, 0u);
+            if (r < R && tc0 + 32 * part + 32 <= C) v[p] = *(const uint4*)(codes + r * (C / 2) + tc0 / 2 + 16 * part);
+        }
     }
+    // thread (s, half): codes 4 half .. 4 half + 3 of scale byte s
+    static_assert(NTHREADS == 256, "two threads per scale byte");
+    const int sbyte = tid >> 1, half = tid & 1;
+    uint32_t llo = 0u, lhi = 0u;
+    {
+        const float sc = e4m3_decode_nonneg((uint32_t)sbyte);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t x = nvfp4_dequant_bf16((uint32_t)(4 * half + i), sc, S);
+            llo |= (x & 0xFFu) << (8 * i);
+            lhi |= (x >> 8) << (8 * i);
+        }
+    }
+    uint32_t slo = 0u, shi = 0u;
     {
         const int64_t r = tr0 + tid;
-        uint32_t lo = 0u, hi = 0u;
         if (r < R) {
             const uint8_t* src = scales + r * (C / 16) + tc0 / 16;
             const int64_t nb = (C - tc0) / 16;   // scale bytes of the row inside the tile
             if (nb >= 8 && ((uintptr_t)src & 7u) == 0) {
                 const uint2 w = *(const uint2*)src;
-                lo = w.x;
-                hi = w.y;
+                slo = w.x;
+                shi = w.y;
             } else {
 #pragma unroll
                 for (int b = 0; b < 8; ++b) {
-                    const uint32_t v = b < nb ? (uint32_t)src[b] : 0u;
-                    if (b < 4) lo |= v << (8 * b); else hi |= v << (8 * (b - 4));
+                    const uint32_t x = b < nb ? (uint32_t)src[b] : 0u;
+                    if (b < 4) slo |= x << (8 * b); else shi |= x << (8 * (b - 4));
                 }
             }
         }
-        L.scales[tid] = make_uint2(lo, hi);
     }
-    {   // thread (s, half): codes 4 half .. 4 half + 3 of scale byte s
-        static_assert(NTHREADS == 256, "two threads per scale byte");
-        const int sbyte = tid >> 1, half = tid & 1;
-        const float sc = e4m3_decode_nonneg((uint32_t)sbyte);
-        uint32_t lo = 0u, hi = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t v = nvfp4_dequant_bf16((uint32_t)(4 * half + i), sc, S);
-            lo |= (v & 0xFFu) << (8 * i);
-            hi |= (v >> 8) << (8 * i);
-        }
-        uint32_t* w = (uint32_t*)&L.lut[sbyte];
-        w[half] = lo;
-        w[2 + half] = hi;
+    for (int p = 0; p < 4; ++p) {
+        const int id = tid + NTHREADS * p, row = id >> 2, part = id & 3;
+        L.codes[row ^ ((row >> 4) & 3)][part] = v[p];
     }
+    L.scales[tid] = make_uint2(slo, shi);
+    uint32_t* w = (uint32_t*)&L.lut[sbyte];
+    w[half] = llo;
+    w[2 + half] = lhi;
     __syncthreads();
 }
 
